@@ -1,0 +1,385 @@
+"""Pins of the CPU oracle to what the pages and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a worked
+example printed on the pages (fixtures under tests/golden/, each citing its
+page and section), a closed form, an invariant, a special case that reduces
+to a library routine, or an independent brute-force evaluation.
+"""
+import math
+
+import numpy as np
+import pytest
+import scipy.special
+import torch
+
+import oracle
+import synthetic
+from conftest import read_golden
+
+
+def f32cfg(**kw):
+    cfg = dict(d=4, L=0, n=4, k=2, F=4, kind="relu2", act="f32", weights="f32", router_w="f32",
+               in_norm="none", expert_norm="none", res_gate="none", eps_in=0.0, eps_expert=0.0,
+               bias_in_weights=0)
+    cfg.update(kw)
+    return cfg
+
+
+# ---------------------------------------------------------------------------
+# Norms: worked example of C_gamma vs I_gamma (normalization-orders section)
+# ---------------------------------------------------------------------------
+
+def test_rmsnorm_orders_worked_example():
+    g = read_golden("rmsnorm_orders.txt")
+    x, gamma = np.array(g["x"]), np.array(g["gamma"], np.float32)
+    C = oracle.rms_centered(x, gamma, 0.0)
+    np.testing.assert_allclose(C, g["C"], rtol=0, atol=1e-15)
+    I_ = oracle.rms_input_scaled(x, gamma, 0.0)
+    expect = np.array(g["I_num"]) / math.sqrt(g["I_den_sq"][0])
+    np.testing.assert_allclose(I_, expect, rtol=0, atol=1e-15)
+    # rounding the scaled vector (2,1) to bf16 is exact, so the bf16 form agrees
+    np.testing.assert_allclose(oracle.rms_input_scaled(x, gamma, 0.0, act="bf16"), expect, atol=1e-15)
+    # collinear but not equal
+    assert abs(C[0] / C[1] - I_[0] / I_[1]) < 1e-12 and not np.allclose(C, I_)
+
+
+def test_rmsnorm_closed_forms():
+    rng = np.random.default_rng(0)
+    x = rng.standard_normal(37)
+    # gamma = 0 and eps = 0: both orders reduce to x / rms(x), with mean square 1 afterwards
+    for f in (lambda v: oracle.rms_centered(v, None, 0.0), lambda v: oracle.rms_input_scaled(v, None, 0.0)):
+        r = f(x)
+        assert abs(np.mean(r * r) - 1.0) < 1e-14
+        np.testing.assert_allclose(r, x / np.sqrt(np.mean(x * x)), rtol=1e-14)
+    # epsilon enters under the root: a constant vector c gives c / sqrt(c^2 + eps)
+    c = np.full(8, 0.3)
+    np.testing.assert_allclose(oracle.rms_centered(c, None, 0.5), c / math.sqrt(0.09 + 0.5), rtol=1e-15)
+    # C scales after normalising: output of a gain g is (1+g) times the gain-free output
+    gam = rng.standard_normal(37).astype(np.float32) * 0.1
+    np.testing.assert_allclose(oracle.rms_centered(x, gam, 1e-3),
+                               (1 + gam.astype(np.float64)) * oracle.rms_centered(x, None, 1e-3), rtol=1e-14)
+
+
+def test_input_scaled_rounds_scaled_vector_to_input_dtype():
+    # The scaled vector is rounded to bf16 before the reduction: pick values where that matters.
+    x = np.array([1.0 + 2 ** -8, 1.0, 3.0, -2.0])   # 1+2^-8 is a bf16 tie: rounds to 1.0 (even)
+    gamma = np.zeros(4, np.float32)
+    r = oracle.rms_input_scaled(x, gamma, 0.0, act="bf16")
+    s = np.array([1.0, 1.0, 3.0, -2.0])
+    np.testing.assert_allclose(r, s / np.sqrt(np.mean(s * s)), rtol=1e-15)
+
+
+# ---------------------------------------------------------------------------
+# bf16 rounding used by the oracle vs torch's conversion (a library routine)
+# ---------------------------------------------------------------------------
+
+def test_round_bf16_matches_library_and_ties():
+    rng = np.random.default_rng(1)
+    vals = np.concatenate([rng.standard_normal(2000) * 10.0 ** rng.integers(-30, 30, 2000),
+                           [1.0 + 2 ** -8, 1.0 + 3 * 2 ** -8, -(1.0 + 2 ** -8), 2 ** -130, 3.0e-39]])
+    ours = np.array([oracle.round_bf16(v) for v in vals])
+    ref = torch.tensor(vals.astype(np.float32)).to(torch.bfloat16).to(torch.float64).numpy()
+    # torch rounds via float32 first; for these values that first step is exact or harmless
+    np.testing.assert_array_equal(ours, ref)
+    assert oracle.round_bf16(1.0 + 2 ** -8) == 1.0            # tie to even (down)
+    assert oracle.round_bf16(1.0 + 3 * 2 ** -8) == 1.0 + 2 ** -6  # tie to even (up)
+
+
+# ---------------------------------------------------------------------------
+# Gate: worked example, invariants and special cases ("The gate")
+# ---------------------------------------------------------------------------
+
+def _router_layer(H):
+    """A layer whose router logits equal H for the input x = e_0."""
+    n = len(H)
+    x = np.zeros((1, n), np.float32)
+    x[0, 0] = 1.0
+    W = np.zeros((n, n), np.float32)
+    W[:, 0] = H
+    return x, W
+
+
+def test_topk_softmax_worked_example():
+    g = read_golden("topk_softmax.txt")
+    H, k = np.array(g["H"]), int(g["k"][0])
+    G = oracle.gate_dense(H, k)
+    np.testing.assert_allclose(G, g["G_printed"], atol=5e-4)          # the page's three places
+    np.testing.assert_allclose(G[:2], [1 / (1 + math.exp(-1)), 1 / (1 + math.exp(1))], rtol=1e-15)
+    assert G[2] == 0.0 and G[3] == 0.0
+    # the same numbers through the full forward: a router whose logits are H
+    x, W = _router_layer(H)
+    n = len(H)
+    cfg = f32cfg(d=n, n=n, k=k, F=2)
+    t = {"x": x, "router_w": W, "w1": np.zeros((n, 2, n), np.float32), "w2": np.zeros((n, n, 2), np.float32)}
+    r = oracle.forward(cfg, t)
+    assert list(r["idx"][0]) == [0, 1]
+    np.testing.assert_allclose(r["w"][0], G[:2], rtol=1e-15)
+
+
+@pytest.mark.parametrize("n,k", [(8, 2), (256, 8), (5, 5), (7, 1)])
+def test_gate_invariants(n, k):
+    rng = np.random.default_rng(n * 100 + k)
+    for _ in range(20):
+        H = rng.standard_normal(n) * 3
+        G = oracle.gate_dense(H, k)
+        assert (G >= 0).all()
+        assert abs(G.sum() - 1.0) < k * 2.0 ** -52 * 4
+        assert (G > 0).sum() == k
+        # the kept entries are exactly the k largest
+        kept = set(np.flatnonzero(G))
+        assert kept == set(np.argsort(-H, kind="stable")[:k])
+
+
+def test_gate_special_cases():
+    rng = np.random.default_rng(3)
+    H = rng.standard_normal(9)
+    # k = 1: the single survivor gets weight exactly 1
+    G = oracle.gate_dense(H, 1)
+    assert G.max() == 1.0 and G.argmax() == np.argmax(H)
+    # k = n: the ordinary softmax
+    np.testing.assert_allclose(oracle.gate_dense(H, 9), scipy.special.softmax(H), rtol=1e-14)
+    # exact ties: lower expert id first, equal weights 1/k
+    idx, margin = oracle.topk(np.zeros(16), 4)
+    assert list(idx) == [0, 1, 2, 3] and margin == 0.0
+    np.testing.assert_allclose(oracle.gate_dense(np.zeros(16), 4)[:4], 0.25, rtol=0)
+    # selection order is by score, largest first
+    idx, margin = oracle.topk(np.array([0.1, 0.5, 0.5, 0.9, -1.0]), 3)
+    assert list(idx) == [3, 1, 2] and abs(margin - 0.4) < 1e-15
+
+
+# ---------------------------------------------------------------------------
+# Per-expert norm before mixing: the page's counterexample, through forward()
+# ---------------------------------------------------------------------------
+
+def test_norm_before_mix_counterexample():
+    g = read_golden("norm_before_mix.txt")
+    e1, e2 = np.array(g["e1"]), np.array(g["e2"])
+    # Two ReLU experts whose outputs on x = (1,1) are e1 and e2; router weights zero -> tie -> weights 1/2.
+    cfg = f32cfg(d=2, n=2, k=2, F=2, expert_norm="input_scaled")
+    w1 = np.stack([np.eye(2), np.eye(2)]).astype(np.float32)
+    w2 = np.stack([np.diag(e1), np.diag(e2)]).astype(np.float32)  # W2 @ relu(x) with x = (1,1)
+    t = {"x": np.ones((1, 2), np.float32), "router_w": np.zeros((2, 2), np.float32), "w1": w1, "w2": w2,
+         "gamma_ex": np.zeros(2, np.float32)}
+    r = oracle.forward(cfg, t)
+    np.testing.assert_allclose(r["w"][0], [0.5, 0.5])
+    np.testing.assert_allclose(r["y"][0] ** 2, g["individual_sq"], rtol=1e-15)
+    mixed = oracle.rms_centered(0.5 * e1 + 0.5 * e2, None, 0.0)
+    np.testing.assert_allclose(mixed, np.array(g["mixed_num"]) / math.sqrt(g["mixed_den_sq"][0]), rtol=1e-15)
+    assert np.abs(r["y"][0] - mixed).max() > 0.5   # the orders differ
+
+
+# ---------------------------------------------------------------------------
+# Experts: closed forms of SwiGLU wiring (gate rows first, then up rows)
+# ---------------------------------------------------------------------------
+
+def test_swiglu_identity_closed_form():
+    # L = F = 4, no latent scaling: down = up = I, gate rows = I, up rows = 2I, W2 = I.
+    D = 4
+    cfg = dict(d=D, L=D, n=2, k=1, F=D, kind="swiglu3", act="f32", weights="f32", router_w="f32",
+               in_norm="none", expert_norm="none", res_gate="linear", eps_in=0.0, eps_expert=0.0)
+    I = np.eye(D, dtype=np.float32)
+    w1 = np.stack([np.concatenate([I, 2 * I]), np.concatenate([I, 2 * I])])
+    w2 = np.stack([I, I])
+    x = np.array([[0.5, -1.25, 2.0, 0.0]], np.float32)
+    gate = np.array([1.0, 0.5, 0.0, 0.25], np.float32)
+    t = {"x": x, "router_w": np.zeros((2, D), np.float32), "down_w": I, "w1": w1, "w2": w2, "up_w": I, "gate": gate}
+    r = oracle.forward(cfg, t)
+    z = x[0].astype(np.float64)
+    silu = z / (1 + np.exp(-z))
+    np.testing.assert_allclose(r["y"][0], silu * (2 * z), rtol=1e-15, atol=1e-300)
+    np.testing.assert_allclose(r["out"][0], z + gate * silu * (2 * z), rtol=1e-15)
+
+
+def test_identical_experts_make_routing_irrelevant():
+    # All experts equal and sum of weights 1: y equals that expert's normalised output for every routing.
+    p = synthetic.small(T=6, d=32, L=16, F=16, n=6, k=3)
+    prm = synthetic.layer_params(p)
+    prm["w1"] = np.broadcast_to(prm["w1"][0], prm["w1"].shape).copy()
+    prm["w2"] = np.broadcast_to(prm["w2"][0], prm["w2"].shape).copy()
+    x = synthetic.inputs(p)
+    cfg = p.cfg()
+    r = oracle.forward(cfg, dict(prm, x=x))
+    forced = np.tile(np.array([[5, 0, 2]], np.int32), (p.T, 1))
+    r2 = oracle.forward(cfg, dict(prm, x=x), forced=forced)
+    np.testing.assert_allclose(r["y"], r2["y"], rtol=1e-12, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# Brute force: an independent numpy evaluation of the whole layer
+# ---------------------------------------------------------------------------
+
+def _numpy_layer(cfg, t, act_round):
+    """Plain numpy matmuls over all experts with the dense gate vector."""
+    x = t["x"].astype(np.float64)
+    T = x.shape[0]
+    if cfg["in_norm"] == "centered":
+        u = (1 + t["gamma_in"].astype(np.float64)) * x / np.sqrt((x * x).mean(1, keepdims=True) + cfg["eps_in"])
+        u = act_round(u)
+    elif cfg["in_norm"] == "input_scaled":
+        s = act_round((1 + t["gamma_in"].astype(np.float64)) * x)
+        u = act_round(s / np.sqrt((s * s).mean(1, keepdims=True) + cfg["eps_in"]))
+    else:
+        u = x
+    logits = (u @ t["router_w"].astype(np.float64).T).astype(np.float32)
+    score = logits + t["bias"] if "bias" in t else logits
+    n, k, F = cfg["n"], cfg["k"], cfg["F"]
+    G = np.zeros((T, n))
+    for i in range(T):
+        order = sorted(range(n), key=lambda e: (-float(score[i, e]), e))[:k]
+        H = logits[i, order].astype(np.float64)
+        G[i, order] = scipy.special.softmax(H)
+    z = u @ t["down_w"].astype(np.float64).T if cfg["L"] else u
+    m = np.zeros_like(z)
+    for e in range(n):
+        W1 = t["w1"][e].astype(np.float64)
+        if cfg["kind"] == "swiglu3":
+            gg, vv = z @ W1[:F].T, z @ W1[F:].T
+            a = gg * scipy.special.expit(gg) * vv
+        else:
+            a = np.maximum(z @ W1.T, 0)
+        o = a @ t["w2"][e].astype(np.float64).T
+        if cfg["expert_norm"] == "input_scaled":
+            s = act_round((1 + t["gamma_ex"].astype(np.float64)) * o)
+            o = s / np.sqrt((s * s).mean(1, keepdims=True) + cfg["eps_expert"])
+        m += G[:, e:e + 1] * o
+    y = m @ t["up_w"].astype(np.float64).T if cfg["L"] else m
+    out = x + t["gate"].astype(np.float64) * y if cfg["res_gate"] == "linear" else y
+    return G, y, out
+
+
+@pytest.mark.parametrize("in_norm", ["none", "centered", "input_scaled"])
+@pytest.mark.parametrize("bias", [False, True])
+def test_bruteforce_latent_layer_f32(in_norm, bias):
+    rng = np.random.default_rng(7)
+    d, L, F, n, k, T = 24, 12, 10, 7, 3, 9
+    cfg = dict(d=d, L=L, n=n, k=k, F=F, kind="swiglu3", act="f32", weights="f32", router_w="f32",
+               in_norm=in_norm, expert_norm="input_scaled", res_gate="linear", eps_in=1e-5, eps_expert=1e-6)
+    f = lambda *s: (rng.standard_normal(s) * 0.4).astype(np.float32)
+    t = {"x": f(T, d) * 2, "router_w": f(n, d), "down_w": f(L, d), "w1": f(n, 2 * F, L), "w2": f(n, L, F),
+         "up_w": f(d, L), "gamma_ex": f(L) * 0.1, "gamma_in": f(d) * 0.1,
+         "gate": rng.uniform(0, 1, d).astype(np.float32)}
+    if bias:
+        t["bias"] = f(n)
+    r = oracle.forward(cfg, t)
+    rd = oracle.forward(cfg, t, dense=True)
+    G, y, out = _numpy_layer(cfg, t, lambda v: v.astype(np.float32).astype(np.float64))
+    for i in range(T):
+        np.testing.assert_allclose(G[i, r["idx"][i]], r["w"][i], rtol=1e-13)
+        assert (G[i] > 0).sum() == k
+    np.testing.assert_allclose(r["y"], y, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(r["out"], out, rtol=1e-10, atol=1e-12)
+    # sparse dispatch equals the dense sum over all n experts
+    np.testing.assert_allclose(r["y"], rd["y"], rtol=1e-12, atol=1e-13)
+
+
+def test_bruteforce_relu_layer_c0_shape():
+    p = synthetic.PRESETS["c0"]
+    prm = synthetic.layer_params(p)
+    x = synthetic.inputs(p)[:16]
+    t = dict(prm, x=x)
+    cfg = p.cfg()
+    r = oracle.forward(cfg, t)
+    G, y, out = _numpy_layer(cfg, t, None)
+    np.testing.assert_allclose(r["y"], y, rtol=1e-11, atol=1e-12)
+    np.testing.assert_array_equal(r["out"], r["y"])   # out = y: no residual gate
+    rd = oracle.forward(cfg, t, dense=True)
+    np.testing.assert_allclose(r["y"], rd["y"], rtol=1e-12, atol=1e-13)
+
+
+def test_bruteforce_bf16_small_layer():
+    # bf16 stored weights and activations; the rounding of I_gamma's scaled vector via torch.
+    p = synthetic.small(T=5, d=64, L=32, F=32, n=8, k=2)
+    t = dict(synthetic.layer_params(p), x=synthetic.inputs(p))
+    cfg = p.cfg()
+    r = oracle.forward(cfg, t)
+    tf = {kk: (synthetic.bf16_to_f32(v) if v.dtype == np.uint16 else v) for kk, v in t.items()}
+    bf = lambda v: torch.from_numpy(np.asarray(v, np.float64)).to(torch.bfloat16).to(torch.float64).numpy()
+    G, y, out = _numpy_layer(cfg, tf, bf)
+    np.testing.assert_allclose(r["y"], y, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(r["out"], out, rtol=1e-9, atol=1e-12)
+
+
+def test_rows_are_independent():
+    p = synthetic.small(T=10, d=64, L=32, F=32, n=8, k=2)
+    t = dict(synthetic.layer_params(p), x=synthetic.inputs(p))
+    cfg = p.cfg()
+    full = oracle.forward(cfg, t)
+    part = oracle.forward(cfg, t, tokens=np.array([7, 2, 9]))
+    np.testing.assert_array_equal(part["y"], full["y"][[7, 2, 9]])
+    np.testing.assert_array_equal(part["idx"], full["idx"][[7, 2, 9]])
+
+
+# ---------------------------------------------------------------------------
+# Permutation: invariants and a library sort
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("T,k,n", [(1, 1, 1), (37, 4, 16), (300, 8, 256), (64, 2, 8)])
+def test_permutation_invariants(T, k, n):
+    rng = np.random.default_rng(T + k + n)
+    idx = np.stack([rng.choice(n, size=k, replace=False) for _ in range(T)]).astype(np.int32)
+    r = oracle.permute(idx, n)
+    assert r["counts"].sum() == T * k
+    np.testing.assert_array_equal(r["offsets"], np.concatenate([[0], np.cumsum(r["counts"])]))
+    # a library stable sort by (expert, token)
+    tt = np.repeat(np.arange(T), k)
+    jj = np.tile(np.arange(k), T)
+    order = np.lexsort((tt, idx.reshape(-1)))
+    np.testing.assert_array_equal(r["perm_tok"], tt[order])
+    np.testing.assert_array_equal(r["perm_slot"], jj[order])
+    # inverse: pos[t, j] points back to (t, j)
+    np.testing.assert_array_equal(r["perm_tok"][r["pos"]], np.repeat(np.arange(T)[:, None], k, 1))
+    np.testing.assert_array_equal(r["perm_slot"][r["pos"]], np.tile(np.arange(k)[None, :], (T, 1)))
+
+
+# ---------------------------------------------------------------------------
+# MXFP4 decode: exhaustive against the OCP MX v1.0 E2M1 table
+# ---------------------------------------------------------------------------
+
+E2M1 = [0.0, 0.5, 1.0, 1.5, 2.0, 3.0, 4.0, 6.0, -0.0, -0.5, -1.0, -1.5, -2.0, -3.0, -4.0, -6.0]
+
+
+@pytest.mark.parametrize("E", [0, 1, 100, 120, 127, 130, 200, 254])
+def test_mxfp4_decode_exhaustive(E):
+    K = 32
+    codes = np.array([c for c in range(16)] * 2, np.uint8)
+    packed = (codes[0::2] | (codes[1::2] << 4)).astype(np.uint8)
+    buf = np.concatenate([packed, np.array([E], np.uint8)])
+    dec = oracle.decode_matrix(buf, "mxfp4", 1, K)[0]
+    expect = np.array([E2M1[c] for c in codes]) * 2.0 ** (E - 127)
+    np.testing.assert_array_equal(dec, expect)
+
+
+def test_mxfp4_quantiser_round_trip_and_rne():
+    # values on the grid times a power of two come back exactly; amax decides the scale
+    rng = np.random.default_rng(5)
+    rows = []
+    for s in (-7, 0, 3):
+        v = np.array([E2M1[c] for c in rng.integers(0, 16, 32)], np.float32)
+        v[0] = 6.0  # amax 6 -> floor(log2 6) - 2 = 0 -> scale 2^0 relative
+        rows.append(v * np.float32(2.0 ** s))
+    v = np.stack(rows)
+    buf = synthetic.mxfp4_quantize(v)
+    np.testing.assert_array_equal(oracle.decode_matrix(buf, "mxfp4", 3, 32), v.astype(np.float64))
+    # ties go to the even code: amax 4 -> scale 1 (floor(log2 4) - 2 = 0)
+    w = np.zeros((1, 32), np.float32)
+    w[0, :8] = [4.0, 0.25, 0.75, 1.25, 1.75, 2.5, 3.5, 5.0]
+    dec = oracle.decode_matrix(synthetic.mxfp4_quantize(w), "mxfp4", 1, 32)[0]
+    np.testing.assert_array_equal(dec[:8], [4.0, 0.0, 1.0, 1.0, 2.0, 2.0, 4.0, 4.0])
+    # saturation: amax 7 -> scale 2^0 -> 7 saturates to 6
+    w[0, 0] = 7.0
+    assert oracle.decode_matrix(synthetic.mxfp4_quantize(w), "mxfp4", 1, 32)[0, 0] == 6.0
+
+
+# ---------------------------------------------------------------------------
+# Shapes: the parameter arithmetic of the 816B-A42B layer
+# ---------------------------------------------------------------------------
+
+def test_latent_layer_parameter_counts():
+    p = synthetic.PRESETS["c1"]
+    per_expert = 2 * p.F * p.L + p.L * p.F
+    assert per_expert == 3 * 4096 ** 2 == 50_331_648
+    total_experts = per_expert * p.n * 62
+    assert abs(total_experts / 816e9 - 0.979) < 0.001          # "about 97%" of 816B
+    assert abs(p.k * per_expert * 62 / 1e9 - 24.96) < 0.01    # about 25B active expert parameters
+    # the two-matrix 8192->4096->8192 reading would exceed the total
+    assert 2 * 8192 * 4096 * 256 * 62 > 816e9
