@@ -1,0 +1,206 @@
+"""Benchmark of one latent MoE layer forward on one MI355X.
+
+A step is one pass of the whole layer (input norm when configured, router,
+top-k, permutation, down-projection, grouped GEMM1 + SwiGLU, grouped GEMM2 +
+per-expert norm, combine, up-projection + residual gate) over one batch of
+seeded synthetic input of the 816B-A42B layer shape (d=8192, latent 4096,
+256 SwiGLU experts 4096->4096->4096, top-8 softmax gating, bf16 weights),
+with every input already resident in HBM.
+
+Default workload: decode, T=64 tokens.  A secondary line item times the
+prefill regime, T=8192.  Prints one JSON line.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
+BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def layer_bytes(p, counts) -> dict:
+    """Algorithmic HBM bytes of one forward: every weight byte of the touched
+    experts, the router and both projections read once, x read, out written."""
+    touched = int((counts > 0).sum())
+    per_expert_w1 = 2 * p.F * p.L * 2
+    per_expert_w2 = p.L * p.F * 2
+    dense = (p.n * p.d + p.L * p.d + p.d * p.L) * 2
+    TK = p.chunk_T * p.k
+    act = p.chunk_T * p.d * 2 + p.chunk_T * p.d * 4
+    gemm1 = touched * per_expert_w1 + TK * p.L * 2 + TK * p.F * 2   # W1 + gathered z rows + act rows
+    return {"touched": touched, "total": touched * (per_expert_w1 + per_expert_w2) + dense + act, "gemm1": gemm1}
+
+
+def layer_flops(p) -> dict:
+    T = p.chunk_T
+    per_tok = 2 * p.d * p.n + 2 * p.d * p.L + p.k * (2 * p.L * 2 * p.F + 2 * p.F * p.L) + 2 * p.L * p.d
+    return {"total": T * per_tok, "gemm1": T * p.k * 2 * p.L * 2 * p.F}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--prefill-steps", type=int, default=10)
+    ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import sparse_mixture_experts_router_amd as moe
+    import synthetic
+
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    moe.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+
+    def to_dev(a):
+        if a.dtype == np.uint16:
+            a = a.view(np.int16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    p = synthetic.PRESETS["c1"]
+    t0 = time.time()
+    host = synthetic.layer_params(p)
+    log("layer generated in %.1f s" % (time.time() - t0))
+    W = {k: to_dev(v) for k, v in host.items()}
+    gains = {"router_bias": None, "gamma_in": None, "gamma_expert": W["gamma_ex"], "res_gate": W["gate"]}
+
+    def make_desc(T):
+        return moe.make_desc(T, p.d, p.L, p.n, p.k, p.F, expert_kind=p.kind, act=p.act, router=p.router_w,
+                             weights=p.weights, in_norm=p.in_norm, expert_norm=p.expert_norm, res_gate=p.res_gate,
+                             eps_in=p.eps_in, eps_expert=p.eps_expert)
+
+    stream = torch.cuda.current_stream()
+
+    def run_workload(pr, steps, warmup):
+        T = pr.chunk_T
+        desc = make_desc(T)
+        x_host = synthetic.inputs(pr)
+        x = to_dev(x_host)
+        out = torch.empty((T, p.d), dtype=torch.float32, device=dev)
+        ws = torch.empty(moe.moe_workspace_bytes(desc), dtype=torch.uint8, device=dev)
+        counts = torch.empty(p.n, dtype=torch.int32, device=dev)
+        fwd = lambda dbg=None: moe.moe_layer_forward(desc, x, W["router_w"], W["down_w"], W["w1"], W["w2"],
+                                                     W["up_w"], gains, out, workspace=ws, dbg=dbg, stream=stream)
+        fwd({"expert_counts": counts})
+        torch.cuda.synchronize()
+        for _ in range(warmup):
+            fwd()
+        evs = [moe.StageEvents() for _ in range(steps)]
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for i in range(steps):
+            fwd({"stage_events": evs[i].address})
+        torch.cuda.synchronize()
+        wall = time.perf_counter() - t_start
+        stages = {}
+        for s in moe.STAGES:
+            v = [e.elapsed_ms(s) for e in evs]
+            v = [q for q in v if q is not None]
+            if v:
+                stages[s] = sum(v) / len(v)
+        for e in evs:
+            e.close()
+        return {"T": T, "ms": wall * 1e3 / steps, "stages": stages, "counts": counts.cpu().numpy(), "x": x_host}
+
+    # ---- decode (headline) ----
+    r = run_workload(p, args.steps, args.warmup)
+    by = layer_bytes(p, r["counts"])
+    fl = layer_flops(p)
+    tok_s = p.chunk_T / (r["ms"] * 1e-3)
+    g1_ms = r["stages"]["gemm1"]
+    g1_gbs = by["gemm1"] / (g1_ms * 1e-3) / 1e9
+    log("decode T=%d: %.3f ms/step, %.0f tok/s, layer %.0f GB/s; stages %s" % (
+        p.chunk_T, r["ms"], tok_s, by["total"] / (r["ms"] * 1e-3) / 1e9,
+        {k: round(v, 4) for k, v in r["stages"].items()}))
+
+    result = {
+        "metric": "MoE-layer tokens/s at T=64 (decode; T=8192 prefill under secondary)",
+        "value": round(tok_s, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(r["ms"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic (seeded Philox normals, random-init weights of the 816B-A42B layer shape)",
+        "config": {"workload": "latent MoE layer, decode T=64", "T": p.chunk_T, "d_model": p.d, "d_latent": p.L,
+                   "d_ff": p.F, "n_experts": p.n, "top_k": p.k, "weights": p.weights,
+                   "touched_experts": by["touched"], "layer_bytes": by["total"],
+                   "layer_GBps": round(by["total"] / (r["ms"] * 1e-3) / 1e9, 1),
+                   "layer_frac_hbm": round(by["total"] / (r["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "stage_ms": {k: round(v, 4) for k, v in r["stages"].items()}},
+        "roofline": {"kernel": "gemm_stream_kernel (grouped GEMM1 + SwiGLU)", "bound": "hbm",
+                     "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(g1_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "bytes_per_launch": by["gemm1"], "avg_launch_ms": round(g1_ms, 4)},
+    }
+
+    # ---- prefill (secondary) ----
+    if not args.no_prefill:
+        p2 = synthetic.PRESETS["c2"]
+        r2 = run_workload(p2, args.prefill_steps, 2)
+        fl2 = layer_flops(p2)
+        tf = fl2["total"] / (r2["ms"] * 1e-3) / 1e12
+        g1 = r2["stages"]["gemm1"]
+        g1_tf = fl2["gemm1"] / (g1 * 1e-3) / 1e12
+        log("prefill T=%d: %.3f ms/step, %.0f tok/s, %.1f TFLOP/s; stages %s" % (
+            p2.chunk_T, r2["ms"], p2.chunk_T / (r2["ms"] * 1e-3), tf, {k: round(v, 4) for k, v in r2["stages"].items()}))
+        result["secondary"] = {
+            "workload": "latent MoE layer, prefill T=8192", "value": round(p2.chunk_T / (r2["ms"] * 1e-3), 1),
+            "unit": "tokens/s", "ms_per_step": round(r2["ms"], 4), "steps": args.prefill_steps,
+            "layer_TFLOPs": round(tf, 1), "layer_frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
+            "stage_ms": {k: round(v, 4) for k, v in r2["stages"].items()},
+            "roofline": {"kernel": "gemm_tile_kernel (grouped GEMM1 + SwiGLU)", "bound": "mfma",
+                         "achieved": round(g1_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                         "frac": round(g1_tf / BF16_PEAK_TFLOPS, 4), "flops_per_launch": fl2["gemm1"],
+                         "avg_launch_ms": round(g1, 4)}}
+
+    # ---- CPU oracle baseline on a bounded sample of the decode workload ----
+    if not args.no_cpu_baseline:
+        import oracle
+        cfg = p.cfg()
+        t = dict(host)
+        t["x"] = r["x"]
+        t1 = time.perf_counter()
+        oracle.forward(cfg, t, tokens=np.array([0]))
+        one = time.perf_counter() - t1
+        m = int(max(1, min(p.chunk_T - 1, args.cpu_seconds // max(one, 1e-3))))
+        toks = np.arange(1, 1 + m)
+        t1 = time.perf_counter()
+        oracle.forward(cfg, t, tokens=toks)
+        el = time.perf_counter() - t1
+        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        result["cpu_baseline"] = {"value": round(m / el, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                                  "sample": "%d tokens of the T=64 decode batch (rows are independent), fp64 "
+                                            "oracle, %.1f s" % (m, el)}
+        log("cpu oracle: %d tokens in %.1f s on %d threads" % (m, el, cores))
+
+    print(json.dumps(result))
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,211 @@
+/*
+ * moe.h -- C ABI of the MI355X latent sparse mixture-of-experts layer.
+ *
+ * One forward pass of the layer
+ *     y   = P_up( sum_{j<k} w_j * N( E_{idx_j}( P_down u ) ) )
+ *     out = h + g * y          (or out = y)
+ * where u is the branch input (x, or an RMS norm of x), the gate
+ * (idx, w) = Softmax(KeepTopK(u W_r^T, k)), E_e is expert e and N the
+ * per-expert output norm.  Sources, cited by page title and section:
+ *   - bobbyburns.tech, "816 billion parameters, and only 42 billion show up
+ *     for each token", section "The math": "Setup" (y = sum_i G(x)_i E_i(x),
+ *     experts with G_i = 0 are never evaluated) and "The gate"
+ *     (G = Softmax(KeepTopK(H, k)), noise-free at inference);
+ *   - flozi.net, "Muse Spark Open: Norm-Preserving Gates Are Not a Norm
+ *     Guarantee": "Two normalization orders implement different functions"
+ *     (R_eps, C_gamma, I_gamma with gain 1+gamma), "Latent experts:
+ *     normalization happens before the weighted sum" (router on the
+ *     full-width input, 8192 -> 4096 latent projection, SwiGLU experts with
+ *     packed gate/up [n, 2F, L] and down [n, L, F] weights, one shared norm
+ *     gain applied to every expert output before its routing weight) and
+ *     "What this means for serving and kernel work" (FP32 router and gates,
+ *     norms reduce in FP32 and return the input dtype);
+ *   - archdb.vladsavinov.com, "Muse-Spark-Open-816B-A42B" fact sheet (SwiGLU,
+ *     no GLU clamp, no FFN bias, no shared expert, routed scaling 1, latent
+ *     width 4,096).
+ *
+ * Conventions for every entry point:
+ *   - all tensor pointers are DEVICE pointers (hipMalloc'd or from a
+ *     framework allocator) owned by the caller; the library allocates
+ *     nothing, keeps no global mutable state and is re-entrant;
+ *   - all matrices are row-major with the reduction dimension contiguous;
+ *   - `stream` is a hipStream_t (NULL = default stream); work is enqueued
+ *     asynchronously and no call synchronises with the host;
+ *   - the descriptor is validated on the host before any launch; on error
+ *     nothing is enqueued and a negative moe_status is returned;
+ *   - inputs are assumed finite; there are no device-side checks.
+ */
+#ifndef MOE_MI355X_H
+#define MOE_MI355X_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    MOE_OK = 0,
+    MOE_ERR_INVALID_ARG = -1,          /* malformed descriptor or NULL required pointer */
+    MOE_ERR_UNSUPPORTED = -2,          /* well-formed, but a combination this build does not run */
+    MOE_ERR_WORKSPACE_TOO_SMALL = -3,  /* workspace_bytes < moe_workspace_bytes(desc) */
+    MOE_ERR_HIP = -4                   /* a HIP launch or event call failed */
+} moe_status;
+
+enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1, MOE_DT_MXFP4 = 2 };
+enum { MOE_NORM_NONE = 0, MOE_NORM_CENTERED = 1, MOE_NORM_INPUT_SCALED = 2 };
+enum { MOE_EXPERT_RELU2 = 0, MOE_EXPERT_SWIGLU3 = 1 };
+enum { MOE_RES_NONE = 0, MOE_RES_LINEAR = 1 };
+
+/* Number of timed stages; stage s is bracketed by stage_events[2s], [2s+1]. */
+enum {
+    MOE_STAGE_IN_NORM = 0, MOE_STAGE_ROUTER = 1, MOE_STAGE_TOPK = 2, MOE_STAGE_PERMUTE = 3,
+    MOE_STAGE_DOWN = 4, MOE_STAGE_GEMM1 = 5, MOE_STAGE_GEMM2 = 6, MOE_STAGE_COMBINE = 7,
+    MOE_STAGE_UP = 8, MOE_NUM_STAGES = 9
+};
+
+/*
+ * Layer descriptor (host memory, read during the call only).
+ *   T            tokens (rows of x); 0 is valid and enqueues nothing
+ *   d_model      width d of x and out
+ *   d_latent     latent width L of the expert space; 0 = experts read u
+ *   n_experts    n (1..256); top_k: k (1..min(n,16))
+ *   d_ff         expert hidden width F
+ *   expert_kind  MOE_EXPERT_SWIGLU3: E(z) = W2 (silu(Wg z) * (Wu z)),
+ *                expert_w1 = [n][2F][L] (rows 0..F-1 gate, F..2F-1 up),
+ *                expert_w2 = [n][L][F];
+ *                MOE_EXPERT_RELU2: E(u) = W2 relu(W1 u), expert_w1 =
+ *                [n][F][d], expert_w2 = [n][d][F] (no latent)
+ *   act_dtype    dtype of x: MOE_DT_BF16 or MOE_DT_F32
+ *   router_dtype dtype of router_w [n][d]; logits are always fp32
+ *   weight_dtype dtype of down_w, expert_w1, expert_w2, up_w:
+ *                F32, BF16 or MXFP4.  An MXFP4 matrix [R][K] is one buffer:
+ *                R*K/2 bytes of E2M1 codes (row-major, low nibble = even
+ *                element) followed by R*K/32 E8M0 scale bytes ([R][K/32]),
+ *                one per 32 consecutive elements along K (OCP MX v1.0);
+ *                an expert tensor is the [n*rows][K] matrix.
+ *   in_norm      norm of x before router and down-projection (u = x if NONE)
+ *   expert_norm  norm of each expert output before its routing weight
+ *                (gain gamma_expert, one vector shared by all experts)
+ *   res_gate     MOE_RES_LINEAR: out = x + res_gate * y; NONE: out = y
+ *   bias_in_weights  0: router_bias only changes which experts are selected
+ *                (weights use the unbiased logits); 1: it also enters the
+ *                softmax
+ *   eps_in, eps_expert  RMS epsilons: R(v) = v * (mean(v^2) + eps)^-1/2
+ */
+typedef struct {
+    int64_t T;
+    int64_t d_model;
+    int64_t d_latent;
+    int64_t n_experts;
+    int64_t top_k;
+    int64_t d_ff;
+    int32_t expert_kind;
+    int32_t act_dtype;
+    int32_t router_dtype;
+    int32_t weight_dtype;
+    int32_t in_norm;
+    int32_t expert_norm;
+    int32_t res_gate;
+    int32_t bias_in_weights;
+    float eps_in;
+    float eps_expert;
+} moe_desc;
+
+/* FP32 parameter vectors (device pointers; NULL where the stage is off).
+ *   router_bias  [n]  selection bias (may be NULL even when routing)
+ *   gamma_in     [d]  input-norm gain (gain applied as 1 + gamma)
+ *   gamma_expert [L]  per-expert output-norm gain, shared by all experts
+ *   res_gate     [d]  residual gate vector g */
+typedef struct {
+    const float *router_bias;
+    const float *gamma_in;
+    const float *gamma_expert;
+    const float *res_gate;
+} moe_gains;
+
+/* Optional outputs for inspection (device pointers, each may be NULL).
+ *   topk_idx [T][k] int32  selected experts, largest score first, ties to
+ *                          the lower expert id
+ *   topk_w   [T][k] fp32   their gate weights
+ *   expert_counts [n], expert_offsets [n+1] int32  tokens per expert and
+ *                          the exclusive prefix sum
+ *   perm_tok, perm_slot [T*k] int32  the (token, slot) pairs sorted by
+ *                          (expert, token)
+ *   y        [T][d] fp32   branch output before the residual gate
+ *   stage_events  NULL or an array of 2*MOE_NUM_STAGES hipEvent_t created
+ *                 by the caller; stage s records [2s] before and [2s+1]
+ *                 after its kernels on `stream` (skipped stages record
+ *                 nothing) */
+typedef struct {
+    int32_t *topk_idx;
+    float *topk_w;
+    int32_t *expert_counts;
+    int32_t *expert_offsets;
+    int32_t *perm_tok;
+    int32_t *perm_slot;
+    float *y;
+    void **stage_events;
+} moe_debug;
+
+/* Human-readable text of a moe_status (static storage). */
+const char *moe_error_string(int status);
+
+/* Host-only check of a descriptor: MOE_OK, MOE_ERR_INVALID_ARG or
+ * MOE_ERR_UNSUPPORTED.  Needs no GPU. */
+int moe_validate(const moe_desc *desc);
+
+/* Device workspace bytes moe_layer_forward needs for this descriptor
+ * (0 if the descriptor is invalid).  Host-only; needs no GPU. */
+size_t moe_workspace_bytes(const moe_desc *desc);
+
+/*
+ * The layer forward pass.
+ *   x          [T][d]   act_dtype
+ *   router_w   [n][d]   router_dtype
+ *   down_w     [L][d]   weight_dtype (NULL when d_latent == 0)
+ *   expert_w1, expert_w2  see moe_desc.expert_kind
+ *   up_w       [d][L]   weight_dtype (NULL when d_latent == 0)
+ *   gains      host struct of device vectors (may be NULL if none needed)
+ *   out        [T][d]   fp32
+ *   workspace  device scratch of at least moe_workspace_bytes(desc) bytes,
+ *              256-byte aligned; contents on entry are ignored
+ *   dbg        optional inspection outputs (NULL for none)
+ * Returns MOE_OK once everything is enqueued on `stream`.
+ */
+int moe_layer_forward(const moe_desc *desc, const void *x, const void *router_w, const void *down_w,
+                      const void *expert_w1, const void *expert_w2, const void *up_w,
+                      const moe_gains *gains, void *out, void *workspace, size_t workspace_bytes,
+                      moe_debug *dbg, void *stream);
+
+/*
+ * Router stage alone: fp32 logits l = u W_r^T, selection on s = l + bias
+ * (fp32), top-k by (s descending, expert id ascending), softmax of the kept
+ * logits ("The gate", Softmax(KeepTopK)).  u is [T][d] of desc->act_dtype
+ * (the branch input: no input norm is applied here).
+ *   topk_idx [T][k] int32, topk_w [T][k] fp32 (outputs)
+ *   logits   [T][n] fp32 (optional output, may be NULL)
+ *   workspace >= moe_router_workspace_bytes(desc)
+ */
+size_t moe_router_workspace_bytes(const moe_desc *desc);
+int moe_router_topk(const moe_desc *desc, const void *u, const void *router_w, const float *router_bias,
+                    int32_t *topk_idx, float *topk_w, float *logits, void *workspace,
+                    size_t workspace_bytes, void *stream);
+
+/*
+ * Permutation stage alone: from topk_idx [T][k] (values in [0, n)) writes
+ *   counts [n], offsets [n+1]  tokens per expert, exclusive prefix sum
+ *   perm_tok, perm_slot [T*k]  pairs sorted by (expert, token): within
+ *                              expert e's segment [offsets[e], offsets[e+1])
+ *                              the tokens ascend
+ *   pos [T][k]                 inverse: perm position of (t, j)
+ * Deterministic (no atomics decide an order).  T*k < 2^31.
+ */
+int moe_permute(int64_t T, int64_t k, int64_t n, const int32_t *topk_idx, int32_t *counts, int32_t *offsets,
+                int32_t *perm_tok, int32_t *perm_slot, int32_t *pos, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* MOE_MI355X_H */

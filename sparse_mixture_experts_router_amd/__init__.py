@@ -1,0 +1,247 @@
+"""MI355X latent sparse mixture-of-experts layer: Python binding.
+
+Thin ctypes marshalling over the C ABI of ``include/moe.h`` (library
+``libmoe_mi355x.so`` built from ``csrc/`` for gfx950).  Every step of the
+layer runs in that library's HIP kernels; this module only checks tensors and
+passes device pointers.  There is no fallback: if the library is missing the
+import of any entry point raises.
+
+Names follow the C ABI: ``moe_layer_forward``, ``moe_workspace_bytes``,
+``moe_validate``, ``moe_error_string``, ``moe_router_topk``,
+``moe_router_workspace_bytes``, ``moe_permute``.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
+
+MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = 0, -1, -2, -3, -4
+DT = {"f32": 0, "bf16": 1, "mxfp4": 2}
+NORM = {"none": 0, "centered": 1, "input_scaled": 2}
+KIND = {"relu2": 0, "swiglu3": 1}
+RES = {"none": 0, "linear": 1}
+STAGES = ["in_norm", "router", "topk", "permute", "down", "gemm1", "gemm2", "combine", "up"]
+
+
+class MoeError(RuntimeError):
+    def __init__(self, code: int, what: str = ""):
+        super().__init__("%s: %s (%d)" % (what or "moe", moe_error_string(code), code))
+        self.code = code
+
+
+class moe_desc(ctypes.Structure):
+    _fields_ = [("T", ctypes.c_int64), ("d_model", ctypes.c_int64), ("d_latent", ctypes.c_int64),
+                ("n_experts", ctypes.c_int64), ("top_k", ctypes.c_int64), ("d_ff", ctypes.c_int64),
+                ("expert_kind", ctypes.c_int32), ("act_dtype", ctypes.c_int32), ("router_dtype", ctypes.c_int32),
+                ("weight_dtype", ctypes.c_int32), ("in_norm", ctypes.c_int32), ("expert_norm", ctypes.c_int32),
+                ("res_gate", ctypes.c_int32), ("bias_in_weights", ctypes.c_int32), ("eps_in", ctypes.c_float),
+                ("eps_expert", ctypes.c_float)]
+
+
+class moe_gains(ctypes.Structure):
+    _fields_ = [("router_bias", ctypes.c_void_p), ("gamma_in", ctypes.c_void_p),
+                ("gamma_expert", ctypes.c_void_p), ("res_gate", ctypes.c_void_p)]
+
+
+class moe_debug(ctypes.Structure):
+    _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("expert_counts", ctypes.c_void_p),
+                ("expert_offsets", ctypes.c_void_p), ("perm_tok", ctypes.c_void_p), ("perm_slot", ctypes.c_void_p),
+                ("y", ctypes.c_void_p), ("stage_events", ctypes.c_void_p)]
+
+
+_lib = None
+
+
+def lib() -> ctypes.CDLL:
+    """The loaded HIP library (raises if it has not been built)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError("libmoe_mi355x.so is not built; run __graft_entry__.build() "
+                              "(hipcc --offload-arch=gfx950)")
+        L = ctypes.CDLL(LIB_PATH)
+        vp, i64, sz = ctypes.c_void_p, ctypes.c_int64, ctypes.c_size_t
+        L.moe_error_string.argtypes = [ctypes.c_int]
+        L.moe_error_string.restype = ctypes.c_char_p
+        L.moe_validate.argtypes = [ctypes.POINTER(moe_desc)]
+        L.moe_workspace_bytes.argtypes = [ctypes.POINTER(moe_desc)]
+        L.moe_workspace_bytes.restype = sz
+        L.moe_layer_forward.argtypes = [ctypes.POINTER(moe_desc), vp, vp, vp, vp, vp, vp, ctypes.POINTER(moe_gains),
+                                        vp, vp, sz, ctypes.POINTER(moe_debug), vp]
+        L.moe_router_workspace_bytes.argtypes = [ctypes.POINTER(moe_desc)]
+        L.moe_router_workspace_bytes.restype = sz
+        L.moe_router_topk.argtypes = [ctypes.POINTER(moe_desc), vp, vp, vp, vp, vp, vp, vp, sz, vp]
+        L.moe_permute.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
+        _lib = L
+    return _lib
+
+
+EXPORTED = ["moe_error_string", "moe_validate", "moe_workspace_bytes", "moe_layer_forward",
+            "moe_router_workspace_bytes", "moe_router_topk", "moe_permute"]
+
+
+def make_desc(T, d_model, d_latent, n_experts, top_k, d_ff, expert_kind="swiglu3", act="bf16", router="bf16",
+              weights="bf16", in_norm="none", expert_norm="none", res_gate="none", bias_in_weights=0,
+              eps_in=1e-5, eps_expert=1e-6) -> moe_desc:
+    return moe_desc(T=T, d_model=d_model, d_latent=d_latent, n_experts=n_experts, top_k=top_k, d_ff=d_ff,
+                    expert_kind=KIND[expert_kind], act_dtype=DT[act], router_dtype=DT[router],
+                    weight_dtype=DT[weights], in_norm=NORM[in_norm], expert_norm=NORM[expert_norm],
+                    res_gate=RES[res_gate], bias_in_weights=int(bias_in_weights), eps_in=eps_in,
+                    eps_expert=eps_expert)
+
+
+def moe_error_string(code: int) -> str:
+    return lib().moe_error_string(int(code)).decode()
+
+
+def moe_validate(desc: moe_desc) -> int:
+    return lib().moe_validate(ctypes.byref(desc))
+
+
+def moe_workspace_bytes(desc: moe_desc) -> int:
+    return lib().moe_workspace_bytes(ctypes.byref(desc))
+
+
+def moe_router_workspace_bytes(desc: moe_desc) -> int:
+    return lib().moe_router_workspace_bytes(ctypes.byref(desc))
+
+
+def _ptr(t, what: str, nbytes: int | None = None):
+    """Device pointer of a contiguous CUDA tensor (or None / a raw int)."""
+    if t is None:
+        return None
+    if isinstance(t, int):
+        return t
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % what)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % what)
+    if nbytes is not None and t.numel() * t.element_size() < nbytes:
+        raise ValueError("%s holds %d bytes, needs %d" % (what, t.numel() * t.element_size(), nbytes))
+    return t.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _wbytes(desc: moe_desc, rows: int, K: int) -> int:
+    if desc.weight_dtype == DT["mxfp4"]:
+        return rows * K // 2 + rows * K // 32
+    return rows * K * (4 if desc.weight_dtype == DT["f32"] else 2)
+
+
+def moe_layer_forward(desc: moe_desc, x, router_w, down_w, expert_w1, expert_w2, up_w, gains: dict | None, out,
+                      workspace=None, dbg: dict | None = None, stream=None):
+    """Enqueue one layer forward on `stream` (default: torch's current stream).
+
+    gains: dict of device fp32 tensors under router_bias, gamma_in,
+    gamma_expert, res_gate (absent = NULL).  dbg: dict of device tensors under
+    the moe_debug field names, plus optionally "stage_events" (an int
+    address of 2*9 hipEvent_t).  workspace: uint8 device tensor of at least
+    moe_workspace_bytes(desc) bytes (allocated here when None).
+    """
+    import torch
+    T, d, L, n, k, F = desc.T, desc.d_model, desc.d_latent, desc.n_experts, desc.top_k, desc.d_ff
+    ab = 4 if desc.act_dtype == DT["f32"] else 2
+    rb = 4 if desc.router_dtype == DT["f32"] else 2
+    Din = L if L else d
+    rows1 = n * (2 * F if desc.expert_kind == KIND["swiglu3"] else F)
+    need = moe_workspace_bytes(desc)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+    g = moe_gains()
+    for nm in ("router_bias", "gamma_in", "gamma_expert", "res_gate"):
+        v = (gains or {}).get(nm)
+        if v is not None and v.dtype != torch.float32:
+            raise ValueError("gain %s must be float32" % nm)
+        setattr(g, nm, _ptr(v, nm))
+    dd = None
+    if dbg:
+        dd = moe_debug()
+        for nm, _ in moe_debug._fields_:
+            v = dbg.get(nm)
+            setattr(dd, nm, _ptr(v, nm) if nm != "stage_events" else v)
+    rc = lib().moe_layer_forward(
+        ctypes.byref(desc), _ptr(x, "x", T * d * ab), _ptr(router_w, "router_w", n * d * rb),
+        _ptr(down_w, "down_w", _wbytes(desc, L, d) if L else None), _ptr(expert_w1, "expert_w1", _wbytes(desc, rows1, Din)),
+        _ptr(expert_w2, "expert_w2", _wbytes(desc, n * Din, F)), _ptr(up_w, "up_w", _wbytes(desc, d, L) if L else None),
+        ctypes.byref(g), _ptr(out, "out", T * d * 4), _ptr(workspace, "workspace"),
+        workspace.numel() if not isinstance(workspace, int) else need, ctypes.byref(dd) if dd else None,
+        _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_layer_forward")
+    return out
+
+
+def moe_router_topk(desc: moe_desc, u, router_w, router_bias, topk_idx, topk_w, logits=None, workspace=None,
+                    stream=None):
+    import torch
+    if logits is None and workspace is None:
+        workspace = torch.empty(max(moe_router_workspace_bytes(desc), 1), dtype=torch.uint8, device=u.device)
+    rc = lib().moe_router_topk(ctypes.byref(desc), _ptr(u, "u"), _ptr(router_w, "router_w"),
+                               _ptr(router_bias, "router_bias"), _ptr(topk_idx, "topk_idx"), _ptr(topk_w, "topk_w"),
+                               _ptr(logits, "logits"), _ptr(workspace, "workspace"),
+                               0 if workspace is None else workspace.numel(), _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_router_topk")
+
+
+def moe_permute(T, k, n, topk_idx, counts, offsets, perm_tok, perm_slot, pos, stream=None):
+    rc = lib().moe_permute(T, k, n, _ptr(topk_idx, "topk_idx"), _ptr(counts, "counts"), _ptr(offsets, "offsets"),
+                           _ptr(perm_tok, "perm_tok"), _ptr(perm_slot, "perm_slot"), _ptr(pos, "pos"),
+                           _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_permute")
+
+
+# ---------------------------------------------------------------------------
+# HIP events for per-stage timing on the library's stream
+# ---------------------------------------------------------------------------
+
+class StageEvents:
+    """2 * MOE_NUM_STAGES hipEvent_t, for moe_debug.stage_events."""
+
+    def __init__(self):
+        self.hip = ctypes.CDLL("libamdhip64.so")
+        self.hip.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
+        self.hip.hipEventQuery.argtypes = [ctypes.c_void_p]
+        self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        n = 2 * len(STAGES)
+        self.arr = (ctypes.c_void_p * n)()
+        for i in range(n):
+            ev = ctypes.c_void_p()
+            if self.hip.hipEventCreate(ctypes.byref(ev)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.arr[i] = ev
+        self.recorded = set()
+
+    @property
+    def address(self) -> int:
+        return ctypes.addressof(self.arr)
+
+    def elapsed_ms(self, stage: str):
+        """Milliseconds of a stage of the last recorded call (None if it did not run)."""
+        s = STAGES.index(stage)
+        a, b = self.arr[2 * s], self.arr[2 * s + 1]
+        if self.hip.hipEventQuery(a) != 0 or self.hip.hipEventQuery(b) != 0:
+            return None
+        ms = ctypes.c_float()
+        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+            return None
+        return ms.value
+
+    def close(self):
+        for i in range(len(self.arr)):
+            if self.arr[i]:
+                self.hip.hipEventDestroy(self.arr[i])
+                self.arr[i] = None

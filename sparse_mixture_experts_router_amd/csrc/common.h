@@ -1,0 +1,59 @@
+// Device-side helpers shared by the layer's HIP kernels (gfx950 / CDNA4).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float floatx4_t __attribute__((ext_vector_type(4)));
+
+namespace moe {
+
+constexpr int kWave = 64;
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// fp32 -> bf16 round-to-nearest-even (v_cvt_pk_bf16_f32 on gfx950).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+    __bf16 h = (__bf16)f;
+    return __builtin_bit_cast(uint16_t, h);
+}
+
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+    return (uint32_t)f32_to_bf16(lo) | ((uint32_t)f32_to_bf16(hi) << 16);
+}
+
+__device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
+
+// D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16).
+// Lane l supplies A[l%16][8*(l/16) .. +8) and B[8*(l/16) .. +8)[l%16]
+// (any permutation of k shared by A and B gives the same sum) and receives
+// D[4*(l/16) + r][l%16] in element r.
+__device__ __forceinline__ floatx4_t mfma16x16x32(uint4 a, uint4 b, floatx4_t c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// Eight E2M1 codes (one dword, low nibble first) times 2^(E-127) -> eight
+// bf16 (exact: every product is representable).
+__device__ __forceinline__ uint4 mxfp4x8_to_bf16(uint32_t codes, uint32_t e8m0) {
+    float scale = e8m0 ? __uint_as_float(e8m0 << 23) : __uint_as_float(0x00400000u);
+    bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
+    bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
+    bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
+    bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
+    uint4 r;
+    r.x = __builtin_bit_cast(uint32_t, p0);
+    r.y = __builtin_bit_cast(uint32_t, p1);
+    r.z = __builtin_bit_cast(uint32_t, p2);
+    r.w = __builtin_bit_cast(uint32_t, p3);
+    return r;
+}
+
+__device__ __forceinline__ float silu(float t) { return t / (1.0f + expf(-t)); }
+
+template <typename T>
+__device__ __forceinline__ T wave_shfl_xor(T v, int mask) {
+    return __shfl_xor(v, mask, kWave);
+}
+
+}  // namespace moe

@@ -1,0 +1,464 @@
+// Host side of the C ABI declared in include/moe.h: descriptor validation,
+// workspace carving and the launch chain of one layer forward on one stream.
+//
+// Launch chain (bf16 latent layer), following the layer as described on
+// flozi.net "Muse Spark Open: Norm-Preserving Gates Are Not a Norm
+// Guarantee", section "Latent experts: normalization happens before the
+// weighted sum", and the gate of bobbyburns.tech "816 billion parameters,
+// and only 42 billion show up for each token", section "The gate":
+//   [input norm] -> router GEMM (fp32 logits) -> top-k + softmax ->
+//   permutation (counts, scan, stable scatter, tile lists) ->
+//   down-projection 8192 -> 4096 -> grouped GEMM1 + SwiGLU ->
+//   grouped GEMM2 + per-expert norm partials -> norm + weighted combine ->
+//   up-projection 4096 -> 8192 + residual gate out = x + g * y.
+// The up-projection is linear, so it is applied once to the weighted sum of
+// the normalised expert outputs rather than to each of them.
+#include <hip/hip_runtime.h>
+#include <string.h>
+
+#include "../../include/moe.h"
+#include "gemm.h"
+#include "route.h"
+
+using namespace moe;
+
+namespace {
+
+constexpr int kStreamGrid = 4096;  // persistent grid cap of the streaming GEMM
+constexpr int kTileGrid = 512;     // persistent grid cap of the LDS-tiled GEMM
+
+inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
+
+struct Carve {
+    size_t total = 0;
+    size_t take(size_t bytes) {
+        size_t off = total;
+        total += align256(bytes);
+        return off;
+    }
+};
+
+struct Layout {
+    size_t u, logits, idx, w, counts, offsets, perm_tok, perm_slot, pos, ntiles, tiles_small, tiles_big;
+    size_t z, act, S, ssq, m;
+    int64_t max_small, max_big;
+    size_t total;
+};
+
+int64_t small_tile_cap(int64_t TK, int64_t n) { return TK / kSmallBM + n + 1; }
+int64_t big_tile_cap(int64_t TK, int64_t n) { return TK / kTileBM + n + 1; }
+
+Layout make_layout(const moe_desc *d) {
+    Layout L;
+    memset(&L, 0, sizeof(L));
+    Carve c;
+    const int64_t T = d->T, n = d->n_experts, k = d->top_k, TK = T * k;
+    const bool bf = d->act_dtype == MOE_DT_BF16;
+    const int64_t Dx = d->d_latent ? d->d_latent : d->d_model;  // expert-space width
+    const size_t ab = bf ? 2 : 4;                                 // activation bytes
+    L.u = (bf && d->in_norm != MOE_NORM_NONE) ? c.take((size_t)T * d->d_model * 2) : 0;
+    L.logits = c.take((size_t)T * n * 4);
+    L.idx = c.take((size_t)TK * 4);
+    L.w = c.take((size_t)TK * 4);
+    L.counts = c.take((size_t)n * 4);
+    L.offsets = c.take((size_t)(n + 1) * 4);
+    L.perm_tok = c.take((size_t)TK * 4);
+    L.perm_slot = c.take((size_t)TK * 4);
+    L.pos = c.take((size_t)TK * 4);
+    L.ntiles = c.take(2 * 4);
+    L.max_small = small_tile_cap(TK, n);
+    L.max_big = big_tile_cap(TK, n);
+    L.tiles_small = c.take((size_t)L.max_small * sizeof(TileEntry));
+    L.tiles_big = c.take((size_t)L.max_big * sizeof(TileEntry));
+    L.z = d->d_latent ? c.take((size_t)T * d->d_latent * 2) : 0;
+    L.act = c.take((size_t)TK * d->d_ff * ab);
+    L.S = c.take((size_t)TK * Dx * ab);
+    L.ssq = (bf && d->expert_norm != MOE_NORM_NONE) ? c.take((size_t)TK * (Dx / 16) * 4) : 0;
+    L.m = d->d_latent ? c.take((size_t)T * d->d_latent * 2) : 0;
+    L.total = c.total;
+    return L;
+}
+
+int check_desc(const moe_desc *d) {
+    if (!d) return MOE_ERR_INVALID_ARG;
+    if (d->T < 0 || d->d_model <= 0 || d->d_latent < 0 || d->n_experts < 1 || d->top_k < 1 || d->d_ff <= 0)
+        return MOE_ERR_INVALID_ARG;
+    if (d->n_experts > 256 || d->top_k > d->n_experts || d->top_k > 16) return MOE_ERR_INVALID_ARG;
+    if (d->expert_kind != MOE_EXPERT_RELU2 && d->expert_kind != MOE_EXPERT_SWIGLU3) return MOE_ERR_INVALID_ARG;
+    if (d->act_dtype != MOE_DT_F32 && d->act_dtype != MOE_DT_BF16) return MOE_ERR_INVALID_ARG;
+    if (d->router_dtype != MOE_DT_F32 && d->router_dtype != MOE_DT_BF16) return MOE_ERR_INVALID_ARG;
+    if (d->weight_dtype < MOE_DT_F32 || d->weight_dtype > MOE_DT_MXFP4) return MOE_ERR_INVALID_ARG;
+    if (d->in_norm < MOE_NORM_NONE || d->in_norm > MOE_NORM_INPUT_SCALED) return MOE_ERR_INVALID_ARG;
+    if (d->expert_norm < MOE_NORM_NONE || d->expert_norm > MOE_NORM_INPUT_SCALED) return MOE_ERR_INVALID_ARG;
+    if (d->res_gate != MOE_RES_NONE && d->res_gate != MOE_RES_LINEAR) return MOE_ERR_INVALID_ARG;
+    if (!(d->eps_in >= 0.f) || !(d->eps_expert >= 0.f)) return MOE_ERR_INVALID_ARG;
+    if (d->T * d->top_k >= ((int64_t)1 << 31) || d->T >= ((int64_t)1 << 31)) return MOE_ERR_INVALID_ARG;
+    if (d->expert_kind == MOE_EXPERT_RELU2 && d->d_latent != 0) return MOE_ERR_INVALID_ARG;
+    if (d->act_dtype == MOE_DT_F32) {
+        // fp32 path: the small Shazeer layer shape (no latent, no norms).
+        if (d->router_dtype != MOE_DT_F32 || d->weight_dtype != MOE_DT_F32) return MOE_ERR_UNSUPPORTED;
+        if (d->d_latent != 0 || d->in_norm != MOE_NORM_NONE || d->expert_norm != MOE_NORM_NONE)
+            return MOE_ERR_UNSUPPORTED;
+        return MOE_OK;
+    }
+    // bf16 path: latent SwiGLU layer on MFMA tiles.
+    if (d->router_dtype != MOE_DT_BF16 || d->weight_dtype == MOE_DT_F32) return MOE_ERR_UNSUPPORTED;
+    if (d->d_latent == 0 || d->expert_kind != MOE_EXPERT_SWIGLU3) return MOE_ERR_UNSUPPORTED;
+    if (d->d_model % 512 || d->d_latent % 512 || d->d_ff % 512 || d->n_experts % 16) return MOE_ERR_UNSUPPORTED;
+    return MOE_OK;
+}
+
+inline hipStream_t as_stream(void *s) { return (hipStream_t)s; }
+
+struct Events {
+    hipEvent_t *ev;
+    hipStream_t s;
+    int begin(int stage) { return ev ? (hipEventRecord(ev[2 * stage], s) == hipSuccess ? 0 : MOE_ERR_HIP) : 0; }
+    int end(int stage) { return ev ? (hipEventRecord(ev[2 * stage + 1], s) == hipSuccess ? 0 : MOE_ERR_HIP) : 0; }
+};
+
+#define MOE_TRY(expr)                                \
+    do {                                             \
+        if ((expr) != hipSuccess) return MOE_ERR_HIP; \
+    } while (0)
+#define MOE_TRY_RC(expr)         \
+    do {                         \
+        int rc_ = (expr);        \
+        if (rc_) return rc_;     \
+    } while (0)
+
+// Dense C[T][N] = A[T][K] * B[N][K]^T with the streaming kernel for few rows
+// and the tiled kernel otherwise.
+hipError_t dense_gemm(GemmArgs &g, int epi, bool mx, hipStream_t s) {
+    g.b_group_rows = 0;
+    g.tiles = nullptr;
+    g.ntiles = nullptr;
+    g.counts = nullptr;
+    g.offsets = nullptr;
+    if (g.M <= 128 || g.N % kTileBN != 0) return launch_gemm_stream(g, epi, mx, false, 4, kStreamGrid, s);
+    return launch_gemm_tile(g, epi, mx, false, kTileGrid, s);
+}
+
+int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const void *down_w, const void *w1,
+                 const void *w2, const void *up_w, const moe_gains *gains, void *out, uint8_t *ws, const Layout &L,
+                 moe_debug *dbg, hipStream_t s) {
+    const int64_t T = d->T, D = d->d_model, Lw = d->d_latent, n = d->n_experts, k = d->top_k, F = d->d_ff;
+    const int64_t TK = T * k;
+    const bool mx = d->weight_dtype == MOE_DT_MXFP4;
+    Events ev{dbg ? (hipEvent_t *)dbg->stage_events : nullptr, s};
+
+    const uint16_t *xb = (const uint16_t *)x;
+    const uint16_t *u = xb;
+    if (d->in_norm != MOE_NORM_NONE) {
+        MOE_TRY_RC(ev.begin(MOE_STAGE_IN_NORM));
+        uint16_t *ub = (uint16_t *)(ws + L.u);
+        MOE_TRY(launch_rmsnorm(xb, gains->gamma_in, ub, T, D, d->eps_in,
+                               d->in_norm == MOE_NORM_CENTERED ? 1 : 2, s));
+        MOE_TRY_RC(ev.end(MOE_STAGE_IN_NORM));
+        u = ub;
+    }
+    float *logits = (float *)(ws + L.logits);
+    int32_t *idx = (int32_t *)(ws + L.idx);
+    float *wts = (float *)(ws + L.w);
+    int32_t *counts = (int32_t *)(ws + L.counts), *offsets = (int32_t *)(ws + L.offsets);
+    int32_t *perm_tok = (int32_t *)(ws + L.perm_tok), *perm_slot = (int32_t *)(ws + L.perm_slot);
+    int32_t *pos = (int32_t *)(ws + L.pos), *ntiles = (int32_t *)(ws + L.ntiles);
+    TileEntry *tiles_small = (TileEntry *)(ws + L.tiles_small), *tiles_big = (TileEntry *)(ws + L.tiles_big);
+    uint16_t *z = (uint16_t *)(ws + L.z), *act = (uint16_t *)(ws + L.act), *S = (uint16_t *)(ws + L.S);
+    uint16_t *m = (uint16_t *)(ws + L.m);
+    float *ssq = L.ssq ? (float *)(ws + L.ssq) : nullptr;
+
+    // Router logits (fp32) = u W_r^T.
+    MOE_TRY_RC(ev.begin(MOE_STAGE_ROUTER));
+    {
+        GemmArgs g{};
+        g.A = u;
+        g.lda = D;
+        g.B = router_w;
+        g.b_rows_total = n;
+        g.N = n;
+        g.K = D;
+        g.M = T;
+        g.C = logits;
+        g.ldc = n;
+        MOE_TRY(dense_gemm(g, EPI_F32, false, s));
+    }
+    MOE_TRY_RC(ev.end(MOE_STAGE_ROUTER));
+
+    MOE_TRY_RC(ev.begin(MOE_STAGE_TOPK));
+    MOE_TRY(launch_topk(logits, gains ? gains->router_bias : nullptr, T, (int)n, (int)k, d->bias_in_weights, idx, wts,
+                        s));
+    MOE_TRY_RC(ev.end(MOE_STAGE_TOPK));
+
+    // Experts with up to small_max tokens are streamed (weight-bandwidth
+    // bound); heavier experts use the tiled kernel.
+    const int64_t avg = (TK + n - 1) / n;
+    const int small_max = (avg <= 32) ? (int)(T < 0x7fffffff ? T : 0x7fffffff) : 32;
+    const bool any_big = T > small_max;
+    MOE_TRY_RC(ev.begin(MOE_STAGE_PERMUTE));
+    MOE_TRY(launch_permute(idx, T, (int)k, (int)n, counts, offsets, perm_tok, perm_slot, pos, tiles_small, tiles_big,
+                           ntiles, small_max, s));
+    MOE_TRY_RC(ev.end(MOE_STAGE_PERMUTE));
+
+    // z = u W_d^T (bf16).
+    MOE_TRY_RC(ev.begin(MOE_STAGE_DOWN));
+    {
+        GemmArgs g{};
+        g.A = u;
+        g.lda = D;
+        g.B = down_w;
+        g.b_rows_total = Lw;
+        g.N = Lw;
+        g.K = D;
+        g.M = T;
+        g.C = z;
+        g.ldc = Lw;
+        MOE_TRY(dense_gemm(g, EPI_BF16, mx, s));
+    }
+    MOE_TRY_RC(ev.end(MOE_STAGE_DOWN));
+
+    auto grouped = [&](GemmArgs &g) {
+        g.counts = counts;
+        g.offsets = offsets;
+    };
+    // GEMM1: act[p] = silu(z[tok(p)] Wg_e^T) * (z[tok(p)] Wu_e^T).
+    MOE_TRY_RC(ev.begin(MOE_STAGE_GEMM1));
+    {
+        GemmArgs g{};
+        g.A = z;
+        g.a_gather = perm_tok;
+        g.lda = Lw;
+        g.B = w1;
+        g.b_rows_total = n * 2 * F;
+        g.b_group_rows = 2 * F;
+        g.N = F;
+        g.K = Lw;
+        g.C = act;
+        g.ldc = F;
+        grouped(g);
+        g.tiles = tiles_small;
+        g.ntiles = ntiles;
+        g.max_tiles = (int32_t)L.max_small;
+        MOE_TRY(launch_gemm_stream(g, EPI_SWIGLU, mx, true, 1, kStreamGrid, s));
+        if (any_big) {
+            g.tiles = tiles_big;
+            g.ntiles = ntiles + 1;
+            g.max_tiles = (int32_t)L.max_big;
+            MOE_TRY(launch_gemm_tile(g, EPI_SWIGLU, mx, true, kTileGrid, s));
+        }
+    }
+    MOE_TRY_RC(ev.end(MOE_STAGE_GEMM1));
+
+    // GEMM2: S[p] = bf16((1+gamma) * act[p] W2_e^T) and per-16-column sums of squares.
+    const int epi2 = d->expert_norm != MOE_NORM_NONE ? EPI_NORM : EPI_BF16;
+    MOE_TRY_RC(ev.begin(MOE_STAGE_GEMM2));
+    {
+        GemmArgs g{};
+        g.A = act;
+        g.lda = F;
+        g.B = w2;
+        g.b_rows_total = n * Lw;
+        g.b_group_rows = Lw;
+        g.N = Lw;
+        g.K = F;
+        g.C = S;
+        g.ldc = Lw;
+        g.gamma = gains ? gains->gamma_expert : nullptr;
+        g.ssq = ssq;
+        g.nparts = (int32_t)(Lw / 16);
+        g.norm_round = d->expert_norm == MOE_NORM_INPUT_SCALED ? 1 : 0;
+        grouped(g);
+        g.tiles = tiles_small;
+        g.ntiles = ntiles;
+        g.max_tiles = (int32_t)L.max_small;
+        MOE_TRY(launch_gemm_stream(g, epi2, mx, true, 1, kStreamGrid, s));
+        if (any_big) {
+            g.tiles = tiles_big;
+            g.ntiles = ntiles + 1;
+            g.max_tiles = (int32_t)L.max_big;
+            MOE_TRY(launch_gemm_tile(g, epi2, mx, true, kTileGrid, s));
+        }
+    }
+    MOE_TRY_RC(ev.end(MOE_STAGE_GEMM2));
+
+    MOE_TRY_RC(ev.begin(MOE_STAGE_COMBINE));
+    MOE_TRY(launch_combine(S, ssq, pos, wts, T, Lw, (int)(Lw / 16), d->eps_expert, (int)k, m, s));
+    MOE_TRY_RC(ev.end(MOE_STAGE_COMBINE));
+
+    // out = x + g * (m W_u^T)  (or out = m W_u^T).
+    MOE_TRY_RC(ev.begin(MOE_STAGE_UP));
+    {
+        GemmArgs g{};
+        g.A = m;
+        g.lda = Lw;
+        g.B = up_w;
+        g.b_rows_total = D;
+        g.N = D;
+        g.K = Lw;
+        g.M = T;
+        g.C = out;
+        g.ldc = D;
+        if (d->res_gate == MOE_RES_LINEAR) {
+            g.resid = xb;
+            g.gate = gains->res_gate;
+            g.y = dbg ? dbg->y : nullptr;
+            MOE_TRY(dense_gemm(g, EPI_RESID, mx, s));
+        } else {
+            MOE_TRY(dense_gemm(g, EPI_F32, mx, s));
+            if (dbg && dbg->y) MOE_TRY(hipMemcpyAsync(dbg->y, out, (size_t)T * D * 4, hipMemcpyDeviceToDevice, s));
+        }
+    }
+    MOE_TRY_RC(ev.end(MOE_STAGE_UP));
+
+    if (dbg) {
+        if (dbg->topk_idx) MOE_TRY(hipMemcpyAsync(dbg->topk_idx, idx, TK * 4, hipMemcpyDeviceToDevice, s));
+        if (dbg->topk_w) MOE_TRY(hipMemcpyAsync(dbg->topk_w, wts, TK * 4, hipMemcpyDeviceToDevice, s));
+        if (dbg->expert_counts) MOE_TRY(hipMemcpyAsync(dbg->expert_counts, counts, n * 4, hipMemcpyDeviceToDevice, s));
+        if (dbg->expert_offsets)
+            MOE_TRY(hipMemcpyAsync(dbg->expert_offsets, offsets, (n + 1) * 4, hipMemcpyDeviceToDevice, s));
+        if (dbg->perm_tok) MOE_TRY(hipMemcpyAsync(dbg->perm_tok, perm_tok, TK * 4, hipMemcpyDeviceToDevice, s));
+        if (dbg->perm_slot) MOE_TRY(hipMemcpyAsync(dbg->perm_slot, perm_slot, TK * 4, hipMemcpyDeviceToDevice, s));
+    }
+    return MOE_OK;
+}
+
+int forward_f32(const moe_desc *d, const void *x, const void *router_w, const void *w1, const void *w2,
+                const moe_gains *gains, void *out, uint8_t *ws, const Layout &L, moe_debug *dbg, hipStream_t s) {
+    const int64_t T = d->T, D = d->d_model, n = d->n_experts, k = d->top_k, F = d->d_ff, TK = T * k;
+    Events ev{dbg ? (hipEvent_t *)dbg->stage_events : nullptr, s};
+    float *logits = (float *)(ws + L.logits);
+    int32_t *idx = (int32_t *)(ws + L.idx);
+    float *wts = (float *)(ws + L.w);
+    int32_t *counts = (int32_t *)(ws + L.counts), *offsets = (int32_t *)(ws + L.offsets);
+    int32_t *perm_tok = (int32_t *)(ws + L.perm_tok), *perm_slot = (int32_t *)(ws + L.perm_slot);
+    int32_t *pos = (int32_t *)(ws + L.pos);
+    float *act = (float *)(ws + L.act), *S = (float *)(ws + L.S);
+
+    MOE_TRY_RC(ev.begin(MOE_STAGE_ROUTER));
+    MOE_TRY(launch_router_f32((const float *)x, (const float *)router_w, T, (int)n, D, logits, s));
+    MOE_TRY_RC(ev.end(MOE_STAGE_ROUTER));
+    MOE_TRY_RC(ev.begin(MOE_STAGE_TOPK));
+    MOE_TRY(launch_topk(logits, gains ? gains->router_bias : nullptr, T, (int)n, (int)k, d->bias_in_weights, idx, wts,
+                        s));
+    MOE_TRY_RC(ev.end(MOE_STAGE_TOPK));
+    MOE_TRY_RC(ev.begin(MOE_STAGE_PERMUTE));
+    MOE_TRY(launch_permute(idx, T, (int)k, (int)n, counts, offsets, perm_tok, perm_slot, pos, nullptr, nullptr,
+                           nullptr, 0, s));
+    MOE_TRY_RC(ev.end(MOE_STAGE_PERMUTE));
+    MOE_TRY_RC(ev.begin(MOE_STAGE_GEMM1));
+    MOE_TRY(launch_expert1_f32((const float *)x, (const float *)w1, perm_tok, offsets, (int)n, TK, F, D,
+                               d->expert_kind == MOE_EXPERT_SWIGLU3, act, s));
+    MOE_TRY_RC(ev.end(MOE_STAGE_GEMM1));
+    MOE_TRY_RC(ev.begin(MOE_STAGE_GEMM2));
+    MOE_TRY(launch_expert2_f32(act, (const float *)w2, offsets, (int)n, TK, F, D, S, s));
+    MOE_TRY_RC(ev.end(MOE_STAGE_GEMM2));
+    MOE_TRY_RC(ev.begin(MOE_STAGE_COMBINE));
+    MOE_TRY(launch_combine_f32(S, pos, wts, (const float *)x,
+                               d->res_gate == MOE_RES_LINEAR ? gains->res_gate : nullptr, T, (int)k, D, (float *)out,
+                               dbg ? dbg->y : nullptr, s));
+    MOE_TRY_RC(ev.end(MOE_STAGE_COMBINE));
+    if (dbg) {
+        if (dbg->topk_idx) MOE_TRY(hipMemcpyAsync(dbg->topk_idx, idx, TK * 4, hipMemcpyDeviceToDevice, s));
+        if (dbg->topk_w) MOE_TRY(hipMemcpyAsync(dbg->topk_w, wts, TK * 4, hipMemcpyDeviceToDevice, s));
+        if (dbg->expert_counts) MOE_TRY(hipMemcpyAsync(dbg->expert_counts, counts, n * 4, hipMemcpyDeviceToDevice, s));
+        if (dbg->expert_offsets)
+            MOE_TRY(hipMemcpyAsync(dbg->expert_offsets, offsets, (n + 1) * 4, hipMemcpyDeviceToDevice, s));
+        if (dbg->perm_tok) MOE_TRY(hipMemcpyAsync(dbg->perm_tok, perm_tok, TK * 4, hipMemcpyDeviceToDevice, s));
+        if (dbg->perm_slot) MOE_TRY(hipMemcpyAsync(dbg->perm_slot, perm_slot, TK * 4, hipMemcpyDeviceToDevice, s));
+    }
+    return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *moe_error_string(int status) {
+    switch (status) {
+        case MOE_OK: return "ok";
+        case MOE_ERR_INVALID_ARG: return "invalid argument";
+        case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
+        case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+        case MOE_ERR_HIP: return "HIP error";
+    }
+    return "unknown status";
+}
+
+int moe_validate(const moe_desc *desc) { return check_desc(desc); }
+
+size_t moe_workspace_bytes(const moe_desc *desc) {
+    if (check_desc(desc) != MOE_OK) return 0;
+    return make_layout(desc).total;
+}
+
+int moe_layer_forward(const moe_desc *d, const void *x, const void *router_w, const void *down_w,
+                      const void *expert_w1, const void *expert_w2, const void *up_w, const moe_gains *gains,
+                      void *out, void *workspace, size_t workspace_bytes, moe_debug *dbg, void *stream) {
+    int rc = check_desc(d);
+    if (rc != MOE_OK) return rc;
+    if (!x || !router_w || !expert_w1 || !expert_w2 || !out) return MOE_ERR_INVALID_ARG;
+    if (d->d_latent && (!down_w || !up_w)) return MOE_ERR_INVALID_ARG;
+    if (d->res_gate == MOE_RES_LINEAR && (!gains || !gains->res_gate)) return MOE_ERR_INVALID_ARG;
+    if (d->in_norm != MOE_NORM_NONE && !gains) return MOE_ERR_INVALID_ARG;
+    Layout L = make_layout(d);
+    if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
+    if (!workspace || ((uintptr_t)workspace & 255)) return MOE_ERR_INVALID_ARG;
+    if (d->T == 0) return MOE_OK;
+    hipStream_t s = as_stream(stream);
+    if (d->act_dtype == MOE_DT_BF16)
+        return forward_bf16(d, x, router_w, down_w, expert_w1, expert_w2, up_w, gains, out, (uint8_t *)workspace, L,
+                            dbg, s);
+    return forward_f32(d, x, router_w, expert_w1, expert_w2, gains, out, (uint8_t *)workspace, L, dbg, s);
+}
+
+size_t moe_router_workspace_bytes(const moe_desc *d) {
+    if (check_desc(d) != MOE_OK) return 0;
+    return align256((size_t)d->T * d->n_experts * 4);
+}
+
+int moe_router_topk(const moe_desc *d, const void *u, const void *router_w, const float *router_bias,
+                    int32_t *topk_idx, float *topk_w, float *logits, void *workspace, size_t workspace_bytes,
+                    void *stream) {
+    int rc = check_desc(d);
+    if (rc != MOE_OK) return rc;
+    if (!u || !router_w || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+    float *lg = logits;
+    if (!lg) {
+        if (workspace_bytes < moe_router_workspace_bytes(d)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+        if (!workspace) return MOE_ERR_INVALID_ARG;
+        lg = (float *)workspace;
+    }
+    if (d->T == 0) return MOE_OK;
+    hipStream_t s = as_stream(stream);
+    if (d->router_dtype == MOE_DT_F32) {
+        MOE_TRY(launch_router_f32((const float *)u, (const float *)router_w, d->T, (int)d->n_experts, d->d_model, lg,
+                                  s));
+    } else {
+        GemmArgs g{};
+        g.A = (const uint16_t *)u;
+        g.lda = d->d_model;
+        g.B = router_w;
+        g.b_rows_total = d->n_experts;
+        g.N = d->n_experts;
+        g.K = d->d_model;
+        g.M = d->T;
+        g.C = lg;
+        g.ldc = d->n_experts;
+        MOE_TRY(dense_gemm(g, EPI_F32, false, s));
+    }
+    MOE_TRY(launch_topk(lg, router_bias, d->T, (int)d->n_experts, (int)d->top_k, d->bias_in_weights, topk_idx, topk_w,
+                        s));
+    return MOE_OK;
+}
+
+int moe_permute(int64_t T, int64_t k, int64_t n, const int32_t *topk_idx, int32_t *counts, int32_t *offsets,
+                int32_t *perm_tok, int32_t *perm_slot, int32_t *pos, void *stream) {
+    if (T < 0 || k < 1 || n < 1 || n > 256 || k > n || T * k >= ((int64_t)1 << 31)) return MOE_ERR_INVALID_ARG;
+    if (!topk_idx || !counts || !offsets || !perm_tok || !perm_slot || !pos) return MOE_ERR_INVALID_ARG;
+    hipStream_t s = as_stream(stream);
+    MOE_TRY(launch_permute(topk_idx, T, (int)k, (int)n, counts, offsets, perm_tok, perm_slot, pos, nullptr, nullptr,
+                           nullptr, 0, s));
+    return MOE_OK;
+}
+
+}  // extern "C"

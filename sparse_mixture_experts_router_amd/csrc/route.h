@@ -1,0 +1,32 @@
+// Launchers of the non-GEMM kernels of the MoE layer (see route.hip).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "gemm.h"
+
+namespace moe {
+
+// mode 1: C_gamma (u = (1+g) x / rms(x)); mode 2: I_gamma (s = bf16((1+g) x), u = s / rms(s)).
+hipError_t launch_rmsnorm(const uint16_t *x, const float *gamma, uint16_t *u, int64_t T, int64_t d, float eps,
+                          int mode, hipStream_t s);
+hipError_t launch_topk(const float *logits, const float *bias, int64_t T, int n, int k, int bias_in_weights,
+                       int32_t *idx, float *w, hipStream_t s);
+// Experts with 1..small_max tokens go to the small-tile list (kSmallBM rows
+// per tile), heavier ones to the big-tile list (kTileBM rows per tile).
+hipError_t launch_permute(const int32_t *idx, int64_t T, int k, int n, int32_t *counts, int32_t *offsets,
+                          int32_t *perm_tok, int32_t *perm_slot, int32_t *pos, TileEntry *tiles_small,
+                          TileEntry *tiles_big, int32_t *ntiles, int small_max, hipStream_t s);
+hipError_t launch_combine(const uint16_t *S, const float *ssq, const int32_t *pos, const float *w, int64_t T,
+                          int64_t L, int nparts, float eps, int k, uint16_t *m, hipStream_t s);
+
+hipError_t launch_router_f32(const float *x, const float *W, int64_t T, int n, int64_t d, float *logits,
+                             hipStream_t s);
+hipError_t launch_expert1_f32(const float *x, const float *W1, const int32_t *perm_tok, const int32_t *offsets, int n,
+                              int64_t TK, int64_t F, int64_t din, int swiglu, float *act, hipStream_t s);
+hipError_t launch_expert2_f32(const float *act, const float *W2, const int32_t *offsets, int n, int64_t TK, int64_t F,
+                              int64_t dout, float *S, hipStream_t s);
+hipError_t launch_combine_f32(const float *S, const int32_t *pos, const float *w, const float *x, const float *gate,
+                              int64_t T, int k, int64_t d, float *out, float *y, hipStream_t s);
+
+}  // namespace moe

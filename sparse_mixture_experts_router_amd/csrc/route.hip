@@ -1,0 +1,441 @@
+// Row norms, router top-k, token permutation, norm-and-combine, and the
+// fp32 reference-shape path (small Shazeer layer) of the MoE layer.
+//
+// Sources (page titles and sections):
+//  - gate: bobbyburns.tech "816 billion parameters, and only 42 billion show
+//    up for each token", section "The math" / "The gate": G =
+//    Softmax(KeepTopK(H, k)) -- the k largest logits are kept, every other
+//    entry becomes -inf, so the kept weights sum to one; y = sum_i G_i E_i
+//    ("Setup"), experts with G_i = 0 never run;
+//  - norms: flozi.net "Muse Spark Open: Norm-Preserving Gates Are Not a Norm
+//    Guarantee", "Two normalization orders implement different functions"
+//    (C_gamma = D_gamma R_eps, I_gamma = R_eps D_gamma with the scaled vector
+//    rounded to the input dtype before the FP32 reduction) and "Latent
+//    experts: normalization happens before the weighted sum" (each expert
+//    output is normalised before it is weighted and accumulated);
+//  - router and bias semantics: same page, "Latent experts ..." (FP32
+//    logits; a correction bias changes the selection only).
+#include "common.h"
+#include "route.h"
+
+namespace moe {
+
+// ---------------------------------------------------------------------------
+// Block reductions (fixed order: deterministic)
+// ---------------------------------------------------------------------------
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ float block_sum256(float v, float *lds4) {
+    v = wave_sum(v);
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    __syncthreads();
+    if (lane == 0) lds4[wave] = v;
+    __syncthreads();
+    return ((lds4[0] + lds4[1]) + lds4[2]) + lds4[3];
+}
+
+// ---------------------------------------------------------------------------
+// Input RMS norm: C_gamma or I_gamma of each bf16 row, bf16 out.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t *__restrict__ x, const float *__restrict__ gamma,
+                                                      uint16_t *__restrict__ u, int64_t d, float eps, int mode) {
+    __shared__ float lds4[4];
+    const int64_t row = blockIdx.x;
+    const uint16_t *xr = x + row * d;
+    uint16_t *ur = u + row * d;
+    const int64_t nch = d / 8;
+    float ss = 0.f;
+    for (int64_t c = threadIdx.x; c < nch; c += 256) {
+        uint4 v = *(const uint4 *)(xr + c * 8);
+        const uint16_t *h = (const uint16_t *)&v;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float xv = bf16_to_f32(h[i]);
+            if (mode == 2) {  // input-scaled: square the bf16-rounded scaled value
+                float g = gamma ? 1.0f + gamma[c * 8 + i] : 1.0f;
+                xv = bf16_to_f32(f32_to_bf16(g * xv));
+            }
+            ss += xv * xv;
+        }
+    }
+    ss = block_sum256(ss, lds4);
+    const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+    for (int64_t c = threadIdx.x; c < nch; c += 256) {
+        uint4 v = *(const uint4 *)(xr + c * 8);
+        const uint16_t *h = (const uint16_t *)&v;
+        uint4 o;
+        uint16_t *oh = (uint16_t *)&o;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float g = gamma ? 1.0f + gamma[c * 8 + i] : 1.0f;
+            float xv = bf16_to_f32(h[i]);
+            float r = (mode == 2) ? bf16_to_f32(f32_to_bf16(g * xv)) * inv : g * (xv * inv);
+            oh[i] = f32_to_bf16(r);
+        }
+        *(uint4 *)(ur + c * 8) = o;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Top-k + softmax: one wave per token, lane l holds experts l, l+64, ...
+// Selection order: score descending, expert id ascending on ties.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, const float *__restrict__ bias,
+                                                   int64_t T, int n, int k, int bias_in_weights,
+                                                   int32_t *__restrict__ idx, float *__restrict__ w) {
+    const int lane = threadIdx.x & 63;
+    const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (t >= T) return;
+    float sc[4], hv[4];
+    const float *lr = logits + t * n;
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+        int e = lane + 64 * r;
+        if (e < n) {
+            float l = lr[e];
+            float s = bias ? l + bias[e] : l;
+            sc[r] = s;
+            hv[r] = bias_in_weights ? s : l;
+        } else {
+            sc[r] = -INFINITY;
+            hv[r] = 0.f;
+        }
+    }
+    unsigned taken = 0;  // bit r: expert lane + 64r already selected (or absent)
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        if (lane + 64 * r >= n) taken |= 1u << r;
+    float my_h = 0.f;
+    int my_e = 0;
+    for (int j = 0; j < k; ++j) {
+        float bs = -INFINITY;
+        int be = 0x7fffffff;
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if (!(taken & (1u << r)) && (be == 0x7fffffff || sc[r] > bs)) {
+                bs = sc[r];
+                be = lane + 64 * r;
+            }
+        }
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) {
+            float os = __shfl_xor(bs, o, 64);
+            int oe = __shfl_xor(be, o, 64);
+            bool other = (oe != 0x7fffffff) && (be == 0x7fffffff || os > bs || (os == bs && oe < be));
+            if (other) {
+                bs = os;
+                be = oe;
+            }
+        }
+        const int rsel = be >> 6, src = be & 63;
+        if (lane == src) taken |= 1u << rsel;
+        float hsel = hv[0];
+#pragma unroll
+        for (int r = 1; r < 4; ++r)
+            if (rsel == r) hsel = hv[r];
+        hsel = __shfl(hsel, src, 64);
+        if (lane == j) {
+            my_h = hsel;
+            my_e = be;
+        }
+    }
+    // Softmax over the kept values, held by lanes 0..k-1.
+    float mx = lane < k ? my_h : -INFINITY;
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+    float ex = lane < k ? expf(my_h - mx) : 0.f;
+    float sum = wave_sum(ex);
+    if (lane < k) {
+        idx[t * k + lane] = my_e;
+        w[t * k + lane] = ex / sum;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Permutation: one workgroup of 1024 threads.
+//   counts (LDS histogram) -> exclusive scans (token offsets and the two tile
+//   lists) -> stable scatter: position of (t, j) with expert e is
+//   offsets[e] + #{t' < t : e in idx[t']}, counted with per-chunk LDS
+//   bitmaps (bit t of expert e's row) and popcounts, so no atomic decides
+//   an order.
+// ---------------------------------------------------------------------------
+
+constexpr int kPermThreads = 1024;
+constexpr int kPermWords = kPermThreads / 32;
+
+__device__ __forceinline__ void scan256_excl(int *a, int n) {  // in-place exclusive scan, a[n] = total
+    // Hillis-Steele on n <= 256 entries by the first 256 threads.
+    const int tid = threadIdx.x;
+    int v = (tid < n) ? a[tid] : 0;
+    __syncthreads();
+    for (int off = 1; off < 256; off <<= 1) {
+        int add = (tid < 256 && tid >= off && tid < n) ? a[tid - off] : 0;
+        __syncthreads();
+        if (tid < n) a[tid] += add;
+        __syncthreads();
+    }
+    int incl = (tid < n) ? a[tid] : 0;
+    __syncthreads();
+    if (tid < n) a[tid] = incl - v;
+    if (tid == n - 1) a[n] = incl;
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__restrict__ idx, int64_t T, int k, int n,
+                                                               int32_t *__restrict__ counts,
+                                                               int32_t *__restrict__ offsets,
+                                                               int32_t *__restrict__ perm_tok,
+                                                               int32_t *__restrict__ perm_slot,
+                                                               int32_t *__restrict__ pos, TileEntry *tiles_small,
+                                                               TileEntry *tiles_big, int32_t *ntiles, int small_max) {
+    __shared__ int cnt[257], off[257], ts[257], tb[257], base[256];
+    __shared__ unsigned mask[256][kPermWords];
+    const int tid = threadIdx.x;
+    if (tid < 257) cnt[tid] = 0;
+    __syncthreads();
+    const int64_t TK = T * k;
+    for (int64_t i = tid; i < TK; i += kPermThreads) atomicAdd(&cnt[idx[i]], 1);
+    __syncthreads();
+    if (tid < n) {
+        int c = cnt[tid];
+        off[tid] = c;
+        ts[tid] = (c > 0 && c <= small_max) ? (c + kSmallBM - 1) / kSmallBM : 0;
+        tb[tid] = (c > small_max) ? (c + kTileBM - 1) / kTileBM : 0;
+        base[tid] = 0;
+    }
+    scan256_excl(off, n);
+    scan256_excl(ts, n);
+    scan256_excl(tb, n);
+    if (tid < n) {
+        const int c = cnt[tid];
+        counts[tid] = c;
+        offsets[tid] = off[tid];
+        if (tiles_small && c > 0 && c <= small_max)
+            for (int q = 0; q < ts[tid + 1] - ts[tid]; ++q) tiles_small[ts[tid] + q] = TileEntry{tid, q * kSmallBM};
+        if (tiles_big && c > small_max)
+            for (int q = 0; q < tb[tid + 1] - tb[tid]; ++q) tiles_big[tb[tid] + q] = TileEntry{tid, q * kTileBM};
+    }
+    if (tid == 0) {
+        offsets[n] = off[n];
+        if (ntiles) {
+            ntiles[0] = ts[n];
+            ntiles[1] = tb[n];
+        }
+    }
+    for (int64_t c0 = 0; c0 < T; c0 += kPermThreads) {
+        for (int i = tid; i < 256 * kPermWords; i += kPermThreads) (&mask[0][0])[i] = 0u;
+        __syncthreads();
+        const int64_t t = c0 + tid;
+        const bool live = t < T;
+        const int word = tid >> 5, bit = tid & 31;
+        if (live)
+            for (int j = 0; j < k; ++j) atomicOr(&mask[idx[t * k + j]][word], 1u << bit);
+        __syncthreads();
+        if (live) {
+            for (int j = 0; j < k; ++j) {
+                const int e = idx[t * k + j];
+                int rank = __popc(mask[e][word] & ((1u << bit) - 1u));
+                for (int q = 0; q < word; ++q) rank += __popc(mask[e][q]);
+                const int p = off[e] + base[e] + rank;
+                perm_tok[p] = (int32_t)t;
+                perm_slot[p] = j;
+                pos[t * k + j] = p;
+            }
+        }
+        __syncthreads();
+        if (tid < n) {
+            int add = 0;
+            for (int q = 0; q < kPermWords; ++q) add += __popc(mask[tid][q]);
+            base[tid] += add;
+        }
+        __syncthreads();
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Norm part 2 and weighted combine (bf16 latent path):
+//   r_p = (sum_q ssq[p][q] / L + eps)^-1/2   (partials summed in index order)
+//   m_t = sum_j w_tj * r_{p_tj} * S[p_tj]     (slots in order, fp32) -> bf16
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ S, const float *__restrict__ ssq,
+                                                      const int32_t *__restrict__ pos, const float *__restrict__ w,
+                                                      int64_t L, int nparts, float eps, int k,
+                                                      uint16_t *__restrict__ m) {
+    __shared__ float coef[16];
+    __shared__ int32_t prow[16];
+    const int64_t t = blockIdx.x;
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    for (int j = wave; j < k; j += 4) {
+        const int32_t p = pos[t * k + j];
+        float c = w[t * k + j];
+        if (ssq) {
+            float s = 0.f;
+            for (int q = lane; q < nparts; q += 64) s += ssq[(int64_t)p * nparts + q];
+            s = wave_sum(s);
+            c *= 1.0f / sqrtf(s / (float)L + eps);
+        }
+        if (lane == 0) {
+            coef[j] = c;
+            prow[j] = p;
+        }
+    }
+    __syncthreads();
+    for (int64_t ch = threadIdx.x; ch < L / 8; ch += 256) {
+        float acc[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) acc[i] = 0.f;
+        for (int j = 0; j < k; ++j) {
+            uint4 v = *(const uint4 *)(S + (int64_t)prow[j] * L + ch * 8);
+            const uint16_t *h = (const uint16_t *)&v;
+            const float c = coef[j];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) acc[i] += c * bf16_to_f32(h[i]);
+        }
+        uint4 o;
+        o.x = pack_bf16x2(acc[0], acc[1]);
+        o.y = pack_bf16x2(acc[2], acc[3]);
+        o.z = pack_bf16x2(acc[4], acc[5]);
+        o.w = pack_bf16x2(acc[6], acc[7]);
+        *(uint4 *)(m + t * L + ch * 8) = o;
+    }
+}
+
+// ---------------------------------------------------------------------------
+// fp32 path (no latent projection, fp32 everything): plain per-output
+// threads; the layer is tiny and latency bound.
+// ---------------------------------------------------------------------------
+
+__global__ void router_f32_kernel(const float *__restrict__ x, const float *__restrict__ W, int64_t T, int n, int64_t d,
+                                  float *__restrict__ logits) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= T * n) return;
+    const int64_t t = i / n, e = i % n;
+    float s = 0.f;
+    for (int64_t c = 0; c < d; ++c) s = fmaf(x[t * d + c], W[e * d + c], s);
+    logits[i] = s;
+}
+
+__device__ __forceinline__ int expert_of(const int32_t *offsets, int n, int64_t p) {
+    int lo = 0, hi = n;
+    while (hi - lo > 1) {
+        int mid = (lo + hi) >> 1;
+        if (offsets[mid] <= p) lo = mid;
+        else hi = mid;
+    }
+    return lo;
+}
+
+__global__ void expert1_f32_kernel(const float *__restrict__ x, const float *__restrict__ W1,
+                                   const int32_t *__restrict__ perm_tok, const int32_t *__restrict__ offsets, int n,
+                                   int64_t TK, int64_t F, int64_t din, int swiglu, float *__restrict__ act) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= TK * F) return;
+    const int64_t p = i / F, f = i % F;
+    const int e = expert_of(offsets, n, p);
+    const float *u = x + (int64_t)perm_tok[p] * din;
+    const int64_t rows = swiglu ? 2 * F : F;
+    const float *wg = W1 + ((int64_t)e * rows + f) * din;
+    float g = 0.f;
+    for (int64_t c = 0; c < din; ++c) g = fmaf(wg[c], u[c], g);
+    if (swiglu) {
+        const float *wu = W1 + ((int64_t)e * rows + F + f) * din;
+        float v = 0.f;
+        for (int64_t c = 0; c < din; ++c) v = fmaf(wu[c], u[c], v);
+        act[i] = silu(g) * v;
+    } else {
+        act[i] = fmaxf(g, 0.f);
+    }
+}
+
+__global__ void expert2_f32_kernel(const float *__restrict__ act, const float *__restrict__ W2,
+                                   const int32_t *__restrict__ offsets, int n, int64_t TK, int64_t F, int64_t dout,
+                                   float *__restrict__ S) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= TK * dout) return;
+    const int64_t p = i / dout, c = i % dout;
+    const int e = expert_of(offsets, n, p);
+    const float *wr = W2 + ((int64_t)e * dout + c) * F;
+    const float *ar = act + p * F;
+    float s = 0.f;
+    for (int64_t f = 0; f < F; ++f) s = fmaf(wr[f], ar[f], s);
+    S[i] = s;
+}
+
+__global__ void combine_f32_kernel(const float *__restrict__ S, const int32_t *__restrict__ pos,
+                                   const float *__restrict__ w, const float *__restrict__ x,
+                                   const float *__restrict__ gate, int64_t T, int k, int64_t d,
+                                   float *__restrict__ out, float *__restrict__ y) {
+    const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+    if (i >= T * d) return;
+    const int64_t t = i / d, c = i % d;
+    float s = 0.f;
+    for (int j = 0; j < k; ++j) s = fmaf(w[t * k + j], S[(int64_t)pos[t * k + j] * d + c], s);
+    if (y) y[i] = s;
+    out[i] = gate ? x[i] + gate[c] * s : s;
+}
+
+// ---------------------------------------------------------------------------
+// Launchers
+// ---------------------------------------------------------------------------
+
+static inline unsigned blocks_for(int64_t n, int b) { return (unsigned)((n + b - 1) / b); }
+
+hipError_t launch_rmsnorm(const uint16_t *x, const float *gamma, uint16_t *u, int64_t T, int64_t d, float eps,
+                          int mode, hipStream_t s) {
+    rmsnorm_kernel<<<(unsigned)T, 256, 0, s>>>(x, gamma, u, d, eps, mode);
+    return hipGetLastError();
+}
+
+hipError_t launch_topk(const float *logits, const float *bias, int64_t T, int n, int k, int bias_in_weights,
+                       int32_t *idx, float *w, hipStream_t s) {
+    topk_kernel<<<blocks_for(T, 4), 256, 0, s>>>(logits, bias, T, n, k, bias_in_weights, idx, w);
+    return hipGetLastError();
+}
+
+hipError_t launch_permute(const int32_t *idx, int64_t T, int k, int n, int32_t *counts, int32_t *offsets,
+                          int32_t *perm_tok, int32_t *perm_slot, int32_t *pos, TileEntry *tiles_small,
+                          TileEntry *tiles_big, int32_t *ntiles, int small_max, hipStream_t s) {
+    permute_kernel<<<1, kPermThreads, 0, s>>>(idx, T, k, n, counts, offsets, perm_tok, perm_slot, pos, tiles_small,
+                                              tiles_big, ntiles, small_max);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine(const uint16_t *S, const float *ssq, const int32_t *pos, const float *w, int64_t T,
+                          int64_t L, int nparts, float eps, int k, uint16_t *m, hipStream_t s) {
+    combine_kernel<<<(unsigned)T, 256, 0, s>>>(S, ssq, pos, w, L, nparts, eps, k, m);
+    return hipGetLastError();
+}
+
+hipError_t launch_router_f32(const float *x, const float *W, int64_t T, int n, int64_t d, float *logits,
+                             hipStream_t s) {
+    router_f32_kernel<<<blocks_for(T * n, 256), 256, 0, s>>>(x, W, T, n, d, logits);
+    return hipGetLastError();
+}
+
+hipError_t launch_expert1_f32(const float *x, const float *W1, const int32_t *perm_tok, const int32_t *offsets, int n,
+                              int64_t TK, int64_t F, int64_t din, int swiglu, float *act, hipStream_t s) {
+    expert1_f32_kernel<<<blocks_for(TK * F, 256), 256, 0, s>>>(x, W1, perm_tok, offsets, n, TK, F, din, swiglu, act);
+    return hipGetLastError();
+}
+
+hipError_t launch_expert2_f32(const float *act, const float *W2, const int32_t *offsets, int n, int64_t TK, int64_t F,
+                              int64_t dout, float *S, hipStream_t s) {
+    expert2_f32_kernel<<<blocks_for(TK * dout, 256), 256, 0, s>>>(act, W2, offsets, n, TK, F, dout, S);
+    return hipGetLastError();
+}
+
+hipError_t launch_combine_f32(const float *S, const int32_t *pos, const float *w, const float *x, const float *gate,
+                              int64_t T, int k, int64_t d, float *out, float *y, hipStream_t s) {
+    combine_f32_kernel<<<blocks_for(T * d, 256), 256, 0, s>>>(S, pos, w, x, gate, T, k, d, out, y);
+    return hipGetLastError();
+}
+
+}  // namespace moe

@@ -1,0 +1,90 @@
+"""GPU parity at the 816B-A42B layer's real shape (d=8192, L=F=4096, n=256,
+k=8), in the launch configuration the benchmark times: routing on all or a
+seeded sample of tokens, outputs on sampled tokens the oracle evaluates one
+by one (rows are independent), permutation bit-exact on every token."""
+import numpy as np
+import pytest
+import torch
+
+import synthetic
+from gpu_helpers import DeviceLayer, compare, run, say, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def layer_host():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    say("generating the seed-1 layer (bf16 and MXFP4 forms)")
+    return synthetic.layer_params(synthetic.PRESETS["c1"], formats=("bf16", "mxfp4"))
+
+
+@pytest.fixture(scope="module")
+def bf16_layer(layer_host):
+    say("uploading bf16 layer")
+    return DeviceLayer(synthetic.PRESETS["c1"], host={k: v for k, v in layer_host.items() if "@" not in k})
+
+
+def preset_layer(p, layer_host, base: DeviceLayer):
+    """A DeviceLayer for preset p sharing the seed-1 device weights of `base`
+    (MXFP4 presets get the MXFP4 forms of the same draws)."""
+    host = {k: v for k, v in layer_host.items() if "@" not in k}
+    lay = DeviceLayer.__new__(DeviceLayer)
+    lay.p, lay.host, lay.dev = p, host, dict(base.dev)
+    if p.weights == "mxfp4":
+        for k in ("down_w", "w1", "w2", "up_w"):
+            host[k] = layer_host[k + "@mxfp4"]
+            lay.dev[k] = to_dev(host[k])
+    if p.router_bias == "zipf":
+        host["bias"] = synthetic.zipf_bias(p.n)
+        lay.dev["bias"] = to_dev(host["bias"])
+    if p.in_norm != "none":
+        host["gamma_in"] = synthetic.normal_f32(p.layer_seed, "gamma_in", p.d, 0.02)
+        lay.dev["gamma_in"] = to_dev(host["gamma_in"])
+    return lay
+
+
+def test_c1_decode_T64(bf16_layer):
+    p = synthetic.PRESETS["c1"]
+    x = synthetic.inputs(p)
+    gpu = run(bf16_layer, x)
+    touched = int((gpu["expert_counts"] > 0).sum())
+    say("c1 touched experts: %d" % touched)
+    compare(p, bf16_layer.host, x, gpu, label="c1")
+
+
+def test_c2_prefill_T8192(layer_host, bf16_layer):
+    p = synthetic.PRESETS["c2"]
+    x = synthetic.inputs(p)
+    gpu = run(bf16_layer, x)
+    c = gpu["expert_counts"]
+    say("c2 tokens/expert min %d max %d" % (c.min(), c.max()))
+    compare(p, bf16_layer.host, x, gpu, tokens=synthetic.sample_tokens(p.T, 32, seed=21),
+            route_tokens=synthetic.sample_tokens(p.T, 1024, seed=22), label="c2")
+
+
+def test_c3_skewed_T16384(layer_host, bf16_layer):
+    p = synthetic.PRESETS["c3"]
+    lay = preset_layer(p, layer_host, bf16_layer)
+    x = synthetic.inputs(p)
+    gpu = run(lay, x)
+    c = gpu["expert_counts"]
+    say("c3 hottest expert %d tokens (%.1f%% of tokens), empty experts %d, experts with <=5 tokens %d" % (
+        c.max(), 100.0 * c.max() / p.T, int((c == 0).sum()), int((c <= 5).sum())))
+    assert (c == 0).any() and c.max() > 0.5 * p.T
+    # sample includes tokens routed to cold experts
+    tok = synthetic.sample_tokens(p.T, 32, seed=31)
+    compare(p, lay.host, x, gpu, tokens=tok, route_tokens=synthetic.sample_tokens(p.T, 1024, seed=32), label="c3")
+
+
+@pytest.mark.parametrize("name", ["c4c", "c4i"])
+def test_c4_mxfp4_chunks(name, layer_host, bf16_layer):
+    p = synthetic.PRESETS[name]
+    lay = preset_layer(p, layer_host, bf16_layer)
+    for chunk in (0, p.chunks - 1):
+        x = synthetic.inputs(p, chunk=chunk)
+        gpu = run(lay, x)
+        compare(p, lay.host, x, gpu, tokens=synthetic.sample_tokens(p.chunk_T, 24, seed=40 + chunk),
+                route_tokens=synthetic.sample_tokens(p.chunk_T, 512, seed=50 + chunk),
+                label="%s chunk %d" % (name, chunk))
