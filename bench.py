@@ -114,7 +114,8 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_start
         stages = {}
-        for s in moe.STAGES:
+        ran = [s for s in moe.STAGES if s != "in_norm" or pr.in_norm != "none"]
+        for s in ran:
             v = [e.elapsed_ms(s) for e in evs]
             v = [q for q in v if q is not None]
             if v:
@@ -145,7 +146,7 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": "bf16 weights, fp16 activations, fp32 accumulate",
         "data": "synthetic (seeded Philox normals, random-init weights of the 816B-A42B layer shape)",
         "config": {"workload": "latent MoE layer, decode T=64", "T": p.chunk_T, "d_model": p.d, "d_latent": p.L,
                    "d_ff": p.F, "n_experts": p.n, "top_k": p.k, "weights": p.weights,

@@ -53,7 +53,7 @@ typedef enum {
     MOE_ERR_HIP = -4                   /* a HIP launch or event call failed */
 } moe_status;
 
-enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1, MOE_DT_MXFP4 = 2 };
+enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1, MOE_DT_MXFP4 = 2, MOE_DT_F16 = 3 };
 enum { MOE_NORM_NONE = 0, MOE_NORM_CENTERED = 1, MOE_NORM_INPUT_SCALED = 2 };
 enum { MOE_EXPERT_RELU2 = 0, MOE_EXPERT_SWIGLU3 = 1 };
 enum { MOE_RES_NONE = 0, MOE_RES_LINEAR = 1 };
@@ -67,7 +67,8 @@ enum {
 
 /*
  * Layer descriptor (host memory, read during the call only).
- *   T            tokens (rows of x); 0 is valid and enqueues nothing
+ *   T            tokens (rows of x); 0 is valid, enqueues nothing and
+ *                accepts NULL tensor and workspace pointers
  *   d_model      width d of x and out
  *   d_latent     latent width L of the expert space; 0 = experts read u
  *   n_experts    n (1..256); top_k: k (1..min(n,16))
@@ -93,6 +94,16 @@ enum {
  *                (weights use the unbiased logits); 1: it also enters the
  *                softmax
  *   eps_in, eps_expert  RMS epsilons: R(v) = v * (mean(v^2) + eps)^-1/2
+ *   interm_dtype dtype of the activations the latent path stores between
+ *                its GEMMs and feeds to MFMA: the latent z, the SwiGLU
+ *                output and the weighted sum m (the normalised expert
+ *                outputs S stay bf16, the input dtype of that norm).
+ *                MOE_DT_F16 (also selected by 0): 3 more mantissa bits than
+ *                bf16; bf16/MXFP4 weights are converted to fp16 in registers
+ *                (exact for 2^-17 <= |w| < 65504); a z or SwiGLU value of
+ *                magnitude >= 65504 becomes +-inf and poisons its outputs.
+ *                MOE_DT_BF16: bf16 everywhere (no range limit beyond bf16).
+ *                Ignored on the fp32 path.
  */
 typedef struct {
     int64_t T;
@@ -111,6 +122,8 @@ typedef struct {
     int32_t bias_in_weights;
     float eps_in;
     float eps_expert;
+    int32_t interm_dtype;
+    int32_t reserved;
 } moe_desc;
 
 /* FP32 parameter vectors (device pointers; NULL where the stage is off).
@@ -134,6 +147,14 @@ typedef struct {
  *   perm_tok, perm_slot [T*k] int32  the (token, slot) pairs sorted by
  *                          (expert, token)
  *   y        [T][d] fp32   branch output before the residual gate
+ *   pos      [T][k] int32  perm position of (t, j)
+ *   Intermediates of the bf16 latent path (ignored on the fp32 path):
+ *   z        [T][L]  bf16  down-projection output
+ *   act      [T*k][F] bf16 SwiGLU output, rows in perm order
+ *   S        [T*k][L] bf16 bf16((1+gamma) * expert output), perm order
+ *   ssq      [T*k][L/16] fp32  per-16-column sums of squares of S (of the
+ *                          unrounded expert output for the centered norm)
+ *   m        [T][L]  bf16  weighted sum of the normalised expert outputs
  *   stage_events  NULL or an array of 2*MOE_NUM_STAGES hipEvent_t created
  *                 by the caller; stage s records [2s] before and [2s+1]
  *                 after its kernels on `stream` (skipped stages record
@@ -146,6 +167,12 @@ typedef struct {
     int32_t *perm_tok;
     int32_t *perm_slot;
     float *y;
+    int32_t *pos;
+    void *z;
+    void *act;
+    void *S;
+    float *ssq;
+    void *m;
     void **stage_events;
 } moe_debug;
 

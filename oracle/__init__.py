@@ -18,11 +18,11 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "libmoe_oracle.so")
 
-F32, BF16, MXFP4 = 0, 1, 2
+F32, BF16, MXFP4, F16 = 0, 1, 2, 3
 NORM_NONE, NORM_CENTERED, NORM_INPUT_SCALED = 0, 1, 2
 RELU, SWIGLU = 0, 1
 
-_DT = {"f32": F32, "bf16": BF16, "mxfp4": MXFP4}
+_DT = {"f32": F32, "bf16": BF16, "mxfp4": MXFP4, "f16": F16}
 _NORM = {"none": NORM_NONE, "centered": NORM_CENTERED, "input_scaled": NORM_INPUT_SCALED}
 _KIND = {"relu2": RELU, "swiglu3": SWIGLU}
 
@@ -44,7 +44,7 @@ class _Desc(ctypes.Structure):
                 ("rdt", ctypes.c_int32), ("in_norm", ctypes.c_int32), ("ex_norm", ctypes.c_int32),
                 ("res_gate", ctypes.c_int32), ("bias_in_weights", ctypes.c_int32),
                 ("eps_in", ctypes.c_double), ("eps_ex", ctypes.c_double),
-                ("mirror", ctypes.c_int32), ("pad_", ctypes.c_int32)]
+                ("mirror", ctypes.c_int32), ("interm", ctypes.c_int32)]
 
 
 class _Tensors(ctypes.Structure):
@@ -58,8 +58,7 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build()
+        build()  # compiles only when the library is missing or older than its source
         _lib = ctypes.CDLL(_LIB)
         vp, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
         _lib.orc_forward.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Tensors), vp, i64, vp, i32,
@@ -73,6 +72,8 @@ def lib():
         _lib.orc_decode_matrix.argtypes = [vp, i32, i64, i64, vp]
         _lib.orc_round_bf16.argtypes = [dbl]
         _lib.orc_round_bf16.restype = dbl
+        _lib.orc_round_f16.argtypes = [dbl]
+        _lib.orc_round_f16.restype = dbl
     return _lib
 
 
@@ -93,7 +94,7 @@ def make_desc(cfg: dict, mirror: bool = False) -> _Desc:
                  ex_norm=_NORM[cfg["expert_norm"]], res_gate=1 if cfg["res_gate"] == "linear" else 0,
                  bias_in_weights=int(cfg.get("bias_in_weights", 0)),
                  eps_in=float(cfg["eps_in"]), eps_ex=float(cfg["eps_expert"]),
-                 mirror=int(mirror), pad_=0)
+                 mirror=int(mirror), interm=_DT[cfg.get("interm", "bf16")] if cfg["act"] == "bf16" else F32)
 
 
 _KEEP = []
@@ -201,3 +202,7 @@ def decode_matrix(buf: np.ndarray, dt: str, rows: int, K: int) -> np.ndarray:
 
 def round_bf16(v: float) -> float:
     return lib().orc_round_bf16(float(v))
+
+
+def round_f16(v: float) -> float:
+    return lib().orc_round_f16(float(v))

@@ -29,7 +29,8 @@
  *    input-scaled norm rounds the scaled vector to the input dtype before
  *    its reduction ([Gates], normalization-orders section);
  *  - optional "mirror" mode additionally rounds the latent z, the SwiGLU
- *    output and the mixture m to the activation dtype (debug aid only).
+ *    output and the mixture m to an intermediate dtype (bf16 or fp16), the
+ *    way a device stores them between GEMMs (a diagnostic, not a bar).
  *
  * Parity pins: see the oracle's tests.  Unpinned readings (each also listed
  * in the design notes): the epsilon placement x*(mean(x^2)+eps)^-1/2, the
@@ -41,7 +42,7 @@
 #include <stdlib.h>
 #include <string.h>
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_MXFP4 = 2 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_MXFP4 = 2, ORC_F16 = 3 };
 enum { ORC_NORM_NONE = 0, ORC_NORM_CENTERED = 1, ORC_NORM_INPUT_SCALED = 2 };
 enum { ORC_RELU = 0, ORC_SWIGLU = 1 };
 
@@ -56,8 +57,8 @@ typedef struct {
     int32_t res_gate;      /* 0: out = y; 1: out = h + g*y (h = x) */
     int32_t bias_in_weights; /* 0: bias only changes selection */
     double eps_in, eps_ex;
-    int32_t mirror;        /* 1: round z, a and m to the activation dtype */
-    int32_t pad_;
+    int32_t mirror;        /* 1: round z, a and m to the intermediate dtype (debug aid) */
+    int32_t interm;        /* intermediate dtype of mirror mode: ORC_BF16 or ORC_F16 */
 } orc_desc;
 
 typedef struct {
@@ -107,7 +108,29 @@ static double round_to_bf16(double v) {
 
 static double round_to_f32(double v) { return (double)(float)v; }
 
-static double round_act(int act, double v) { return act == ORC_BF16 ? round_to_bf16(v) : round_to_f32(v); }
+/* Round a double to the nearest IEEE half value (ties to even): 11
+ * significant bits, spacing 2^-24 below 2^-14, overflow to infinity past
+ * the largest finite value 65504. */
+static double round_to_f16(double v) {
+    if (v == 0.0 || !isfinite(v)) return v;
+    int e;
+    frexp(v, &e);
+    if (e - 1 < -14) e = -13;
+    double q = ldexp(1.0, e - 1 - 10);
+    double r = v / q, fl = floor(r), diff = r - fl, res;
+    if (diff > 0.5) res = fl + 1.0;
+    else if (diff < 0.5) res = fl;
+    else res = (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
+    res *= q;
+    if (fabs(res) > 65504.0) return res > 0 ? INFINITY : -INFINITY;
+    return res;
+}
+
+static double round_act(int act, double v) {
+    if (act == ORC_BF16) return round_to_bf16(v);
+    if (act == ORC_F16) return round_to_f16(v);
+    return round_to_f32(v);
+}
 
 /* OCP MX v1.0: E2M1 element = (-1)^s * 2^(E-1) * (1 + m/2), E in 1..3; E=0: m/2. */
 static double e2m1_value(unsigned code) {
@@ -313,7 +336,7 @@ static void expert(const orc_desc *d, const orc_tensors *w, int64_t e, const dou
         for (int64_t i = 0; i < F; ++i) {
             double silu = g[i] / (1.0 + exp(-g[i])); /* silu(t) = t * sigmoid(t) */
             a[i] = silu * up[i];
-            if (d->mirror) a[i] = round_act(d->act, a[i]);
+            if (d->mirror) a[i] = round_act(d->interm, a[i]);
         }
         free(g);
         free(up);
@@ -321,7 +344,7 @@ static void expert(const orc_desc *d, const orc_tensors *w, int64_t e, const dou
         matvec(w->w1, d->wdt, d->n * F, Kin, e * F, F, v, a);
         for (int64_t i = 0; i < F; ++i) {
             a[i] = a[i] > 0.0 ? a[i] : 0.0;
-            if (d->mirror) a[i] = round_act(d->act, a[i]);
+            if (d->mirror) a[i] = round_act(d->interm, a[i]);
         }
     }
     matvec(w->w2, d->wdt, d->n * Dout, F, e * Dout, Dout, a, o);
@@ -375,7 +398,7 @@ int orc_forward(const orc_desc *d, const orc_tensors *w, const int64_t *tok, int
         /* expert-space input */
         if (L) {
             matvec(w->down_w, d->wdt, L, D, 0, L, u, z);
-            if (d->mirror) for (int64_t i = 0; i < L; ++i) z[i] = round_act(d->act, z[i]);
+            if (d->mirror) for (int64_t i = 0; i < L; ++i) z[i] = round_act(d->interm, z[i]);
         } else {
             memcpy(z, u, sizeof(double) * (size_t)D);
         }
@@ -395,7 +418,7 @@ int orc_forward(const orc_desc *d, const orc_tensors *w, const int64_t *tok, int
                 for (int64_t i = 0; i < Dx; ++i) m[i] += wt[j] * nr[i];
             }
         }
-        if (d->mirror) for (int64_t i = 0; i < Dx; ++i) m[i] = round_act(d->act, m[i]);
+        if (d->mirror) for (int64_t i = 0; i < Dx; ++i) m[i] = round_act(d->interm, m[i]);
         if (L) matvec(w->up_w, d->wdt, D, L, 0, D, m, yy);
         else memcpy(yy, m, sizeof(double) * (size_t)D);
         if (y) memcpy(y + q * D, yy, sizeof(double) * (size_t)D);
@@ -440,3 +463,4 @@ void orc_decode_matrix(const void *base, int32_t dt, int64_t rows, int64_t K, do
 }
 
 double orc_round_bf16(double v) { return round_to_bf16(v); }
+double orc_round_f16(double v) { return round_to_f16(v); }

@@ -19,7 +19,7 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = 0, -1, -2, -3, -4
-DT = {"f32": 0, "bf16": 1, "mxfp4": 2}
+DT = {"f32": 0, "bf16": 1, "mxfp4": 2, "f16": 3}
 NORM = {"none": 0, "centered": 1, "input_scaled": 2}
 KIND = {"relu2": 0, "swiglu3": 1}
 RES = {"none": 0, "linear": 1}
@@ -38,7 +38,7 @@ class moe_desc(ctypes.Structure):
                 ("expert_kind", ctypes.c_int32), ("act_dtype", ctypes.c_int32), ("router_dtype", ctypes.c_int32),
                 ("weight_dtype", ctypes.c_int32), ("in_norm", ctypes.c_int32), ("expert_norm", ctypes.c_int32),
                 ("res_gate", ctypes.c_int32), ("bias_in_weights", ctypes.c_int32), ("eps_in", ctypes.c_float),
-                ("eps_expert", ctypes.c_float)]
+                ("eps_expert", ctypes.c_float), ("interm_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class moe_gains(ctypes.Structure):
@@ -49,7 +49,9 @@ class moe_gains(ctypes.Structure):
 class moe_debug(ctypes.Structure):
     _fields_ = [("topk_idx", ctypes.c_void_p), ("topk_w", ctypes.c_void_p), ("expert_counts", ctypes.c_void_p),
                 ("expert_offsets", ctypes.c_void_p), ("perm_tok", ctypes.c_void_p), ("perm_slot", ctypes.c_void_p),
-                ("y", ctypes.c_void_p), ("stage_events", ctypes.c_void_p)]
+                ("y", ctypes.c_void_p), ("pos", ctypes.c_void_p), ("z", ctypes.c_void_p), ("act", ctypes.c_void_p),
+                ("S", ctypes.c_void_p), ("ssq", ctypes.c_void_p), ("m", ctypes.c_void_p),
+                ("stage_events", ctypes.c_void_p)]
 
 
 _lib = None
@@ -85,12 +87,12 @@ EXPORTED = ["moe_error_string", "moe_validate", "moe_workspace_bytes", "moe_laye
 
 def make_desc(T, d_model, d_latent, n_experts, top_k, d_ff, expert_kind="swiglu3", act="bf16", router="bf16",
               weights="bf16", in_norm="none", expert_norm="none", res_gate="none", bias_in_weights=0,
-              eps_in=1e-5, eps_expert=1e-6) -> moe_desc:
+              eps_in=1e-5, eps_expert=1e-6, interm="f16") -> moe_desc:
     return moe_desc(T=T, d_model=d_model, d_latent=d_latent, n_experts=n_experts, top_k=top_k, d_ff=d_ff,
                     expert_kind=KIND[expert_kind], act_dtype=DT[act], router_dtype=DT[router],
                     weight_dtype=DT[weights], in_norm=NORM[in_norm], expert_norm=NORM[expert_norm],
                     res_gate=RES[res_gate], bias_in_weights=int(bias_in_weights), eps_in=eps_in,
-                    eps_expert=eps_expert)
+                    eps_expert=eps_expert, interm_dtype=DT[interm], reserved=0)
 
 
 def moe_error_string(code: int) -> str:
@@ -216,6 +218,7 @@ class StageEvents:
         self.hip.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p, ctypes.c_void_p]
         self.hip.hipEventQuery.argtypes = [ctypes.c_void_p]
         self.hip.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.hip.hipGetLastError.restype = ctypes.c_int
         n = 2 * len(STAGES)
         self.arr = (ctypes.c_void_p * n)()
         for i in range(n):
@@ -230,13 +233,16 @@ class StageEvents:
         return ctypes.addressof(self.arr)
 
     def elapsed_ms(self, stage: str):
-        """Milliseconds of a stage of the last recorded call (None if it did not run)."""
+        """Milliseconds of a stage of the last recorded call (None if it did
+        not run).  A failed query leaves HIP's last-error state set, which the
+        next framework call would report as its own failure, so it is cleared
+        here."""
         s = STAGES.index(stage)
         a, b = self.arr[2 * s], self.arr[2 * s + 1]
-        if self.hip.hipEventQuery(a) != 0 or self.hip.hipEventQuery(b) != 0:
-            return None
         ms = ctypes.c_float()
-        if self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0:
+        if (self.hip.hipEventQuery(a) != 0 or self.hip.hipEventQuery(b) != 0
+                or self.hip.hipEventElapsedTime(ctypes.byref(ms), a, b) != 0):
+            self.hip.hipGetLastError()
             return None
         return ms.value
 

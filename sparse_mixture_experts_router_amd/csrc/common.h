@@ -3,8 +3,13 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "gemm.h"  // ActType
+
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef __fp16 fp16x2_t __attribute__((ext_vector_type(2)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
 
 namespace moe {
@@ -25,27 +30,67 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
 
 __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8_t, v); }
 
-// D(16x16, fp32) += A(16x32, bf16) * B(32x16, bf16).
+// D(16x16, fp32) += A(16x32) * B(32x16), bf16 or fp16 inputs.
 // Lane l supplies A[l%16][8*(l/16) .. +8) and B[8*(l/16) .. +8)[l%16]
 // (any permutation of k shared by A and B gives the same sum) and receives
 // D[4*(l/16) + r][l%16] in element r.
+template <int AT>
 __device__ __forceinline__ floatx4_t mfma16x16x32(uint4 a, uint4 b, floatx4_t c) {
-    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+    if constexpr (AT == ACT_F16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
+                                                      c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// fp32 -> activation bits (round to nearest even; fp16 overflows to inf).
+template <int AT>
+__device__ __forceinline__ uint16_t f32_to_act(float f) {
+    if constexpr (AT == ACT_F16) return __builtin_bit_cast(uint16_t, (_Float16)f);
+    else return f32_to_bf16(f);
+}
+
+template <int AT>
+__device__ __forceinline__ float act_to_f32(uint16_t b) {
+    if constexpr (AT == ACT_F16) return (float)__builtin_bit_cast(_Float16, b);
+    else return bf16_to_f32(b);
+}
+
+// Eight bf16 -> eight fp16.  Exact for |w| in [2^-17, 65504]: a bf16 value
+// has 8 significant bits and fp16 11, so nothing is rounded in that range.
+__device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v) {
+    float lo = __uint_as_float(v << 16), hi = __uint_as_float(v & 0xffff0000u);
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+}
+__device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 v) {
+    return make_uint4(bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w));
+}
+
+// Weight operand in the activation type: bf16 weights pass through or are
+// converted to fp16.
+template <int AT>
+__device__ __forceinline__ uint4 weight_bf16_as(uint4 v) {
+    if constexpr (AT == ACT_F16) return bf16x8_to_f16x8(v);
+    else return v;
 }
 
 // Eight E2M1 codes (one dword, low nibble first) times 2^(E-127) -> eight
-// bf16 (exact: every product is representable).
-__device__ __forceinline__ uint4 mxfp4x8_to_bf16(uint32_t codes, uint32_t e8m0) {
+// bf16 or fp16 (exact whenever the product is representable).
+template <int AT>
+__device__ __forceinline__ uint4 mxfp4x8_to_act(uint32_t codes, uint32_t e8m0) {
     float scale = e8m0 ? __uint_as_float(e8m0 << 23) : __uint_as_float(0x00400000u);
-    bf16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0);
-    bf16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1);
-    bf16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2);
-    bf16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3);
     uint4 r;
-    r.x = __builtin_bit_cast(uint32_t, p0);
-    r.y = __builtin_bit_cast(uint32_t, p1);
-    r.z = __builtin_bit_cast(uint32_t, p2);
-    r.w = __builtin_bit_cast(uint32_t, p3);
+    if constexpr (AT == ACT_F16) {
+        r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scale, 0));
+        r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scale, 1));
+        r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scale, 2));
+        r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, scale, 3));
+    } else {
+        r.x = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 0));
+        r.y = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 1));
+        r.z = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 2));
+        r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3));
+    }
     return r;
 }
 

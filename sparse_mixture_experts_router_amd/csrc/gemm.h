@@ -1,17 +1,21 @@
 // Arguments and launchers of the layer's MFMA GEMMs: C = A * B^T with A rows
-// of bf16 activations and B rows of bf16 or MXFP4 weights (both with the
-// reduction dimension K contiguous), fp32 accumulation, fused epilogues.
+// of activations (bf16 or fp16) and B rows of bf16 or MXFP4 weights (both
+// with the reduction dimension K contiguous), fp32 accumulation, fused
+// epilogues.
 #pragma once
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
 namespace moe {
 
+// Activation (MFMA input) types of the layer's GEMMs.
+enum ActType : int { ACT_BF16 = 0, ACT_F16 = 1 };
+
 enum Epi : int {
     EPI_F32 = 0,     // C[p][n] = acc (fp32)
-    EPI_BF16 = 1,    // C[p][n] = bf16(acc)
-    EPI_SWIGLU = 2,  // C[p][j] = bf16(silu(acc[j]) * acc[F + j]); B holds gate rows then up rows
-    EPI_NORM = 3,    // C[p][n] = s = bf16((1 + gamma[n]) * acc); ssq[p][nb] = sum over the block of s^2
+    EPI_ACT = 1,     // C[p][n] = act(acc), in the output activation type
+    EPI_SWIGLU = 2,  // C[p][j] = act(silu(acc[j]) * acc[F + j]); B holds gate rows then up rows
+    EPI_NORM = 3,    // C[p][n] = s = bf16((1 + gamma[n]) * acc); ssq[p][n/16] = sums of squares per 16 columns
     EPI_RESID = 4    // out[p][n] = x[p][n] + gate[n] * acc (fp32); y[p][n] = acc when y != NULL
 };
 
@@ -21,8 +25,8 @@ struct TileEntry {  // one M-tile of a grouped GEMM: expert e, rows m0 .. of its
 };
 
 struct GemmArgs {
-    // A: bf16 rows with leading dimension lda.  Grouped GEMMs index rows by
-    // permuted position p; a_gather (may be NULL) maps p to the A row.
+    // A: activation rows with leading dimension lda.  Grouped GEMMs index rows
+    // by permuted position p; a_gather (may be NULL) maps p to the A row.
     const uint16_t *A;
     const int32_t *a_gather;
     int64_t lda;
@@ -45,25 +49,29 @@ struct GemmArgs {
     const float *gamma;    // EPI_NORM gain (NULL = 1)
     float *ssq;            // EPI_NORM partial sums of squares [rows][nparts]
     int32_t nparts;
-    int32_t norm_round;    // EPI_NORM: 1 rounds the scaled vector to bf16 before squaring
+    int32_t norm_round;    // EPI_NORM: 1 squares the bf16-rounded scaled value (input-scaled norm)
     const uint16_t *resid; // EPI_RESID: x rows (bf16), leading dimension N
     const float *gate;     // EPI_RESID: g [N]
     float *y;              // EPI_RESID: optional y [rows][N]
 };
 
-// Columns of output that one work item of each kernel covers.
-constexpr int kStreamCols = 16;   // per 16-column block; SWIGLU items cover 16 outputs (32 B rows)
 constexpr int kTileBM = 128;
 constexpr int kTileBN = 128;      // B rows per tile (SWIGLU: 64 gate + 64 up -> 64 outputs)
 constexpr int kTileBK = 64;
 constexpr int kSmallBM = 16;      // rows per tile of the streaming kernel's grouped lists
 
-// Launchers (return hipError_t of the launch).
-// Streaming kernel: weights streamed straight into MFMA registers, K split
-// over the 4 waves of a workgroup.  mb: 16-row blocks per tile (1..4).
-hipError_t launch_gemm_stream(const GemmArgs &a, int epi, bool mx, bool grouped, int mb, int grid_cap,
-                              hipStream_t s);
-// LDS-tiled kernel: 128x128x64 tiles, double-buffered LDS, 4 waves of 64x64.
-hipError_t launch_gemm_tile(const GemmArgs &a, int epi, bool mx, bool grouped, int grid_cap, hipStream_t s);
+// Kernel choice for a launch.
+enum GemmPath : int { PATH_STREAM = 0, PATH_TILE = 1 };
+
+// Router logits: dense, A = u (bf16), B = router weight (bf16), fp32 out.
+hipError_t launch_router_gemm(const GemmArgs &a, int path, hipStream_t s);
+// Down-projection: dense, A = u (bf16), output z in activation type `ot`.
+hipError_t launch_down_gemm(const GemmArgs &a, int path, bool mx, int ot, hipStream_t s);
+// Expert GEMM1 + SwiGLU: grouped, A = z in activation type `at`, output in `at`.
+hipError_t launch_gemm1(const GemmArgs &a, int path, bool mx, int at, hipStream_t s);
+// Expert GEMM2: grouped, A = act in `at`; EPI_NORM (bf16 S + partial sums) or EPI_ACT with bf16 S.
+hipError_t launch_gemm2(const GemmArgs &a, int path, bool mx, int at, bool norm, hipStream_t s);
+// Up-projection: dense, A = m in `at`, EPI_RESID or EPI_F32.
+hipError_t launch_up_gemm(const GemmArgs &a, int path, bool mx, int at, bool resid, hipStream_t s);
 
 }  // namespace moe

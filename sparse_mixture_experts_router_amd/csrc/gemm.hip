@@ -50,13 +50,13 @@ __device__ __forceinline__ bool load_tile(const GemmArgs &a, bool grouped, int b
 
 // Store one accumulator element of a non-SwiGLU epilogue.  Returns the value
 // whose square feeds the norm's partial sum (EPI_NORM), else 0.
-template <int EPI>
+template <int EPI, int OT>
 __device__ __forceinline__ float store_elem(const GemmArgs &a, int64_t p, int64_t n, float v) {
     if constexpr (EPI == EPI_F32) {
         ((float *)a.C)[p * a.ldc + n] = v;
         return 0.f;
-    } else if constexpr (EPI == EPI_BF16) {
-        ((uint16_t *)a.C)[p * a.ldc + n] = f32_to_bf16(v);
+    } else if constexpr (EPI == EPI_ACT) {
+        ((uint16_t *)a.C)[p * a.ldc + n] = f32_to_act<OT>(v);
         return 0.f;
     } else if constexpr (EPI == EPI_NORM) {
         float gsc = a.gamma ? 1.0f + a.gamma[n] : 1.0f;
@@ -95,14 +95,14 @@ __device__ __forceinline__ float sum16(float v) {
 // same 64 bytes of its A row.  Partial sums of the waves meet in LDS and
 // wave 0 applies the epilogue.
 
-template <int MB, int NB, bool MX>
+template <int MB, int NB>
 struct StreamFrag {
     uint4 b[NB][4];
     uint4 a[MB][4];
 };
 
-template <int MB, int NB, bool MX>
-__device__ __forceinline__ void stream_load(StreamFrag<MB, NB, MX> &f, const uint8_t *const bptr[NB],
+template <int MB, int NB, bool MX, int AT>
+__device__ __forceinline__ void stream_load(StreamFrag<MB, NB> &f, const uint8_t *const bptr[NB],
                                             const uint8_t *const bscale[NB], const uint16_t *const aptr[MB],
                                             int64_t kk) {
 #pragma unroll
@@ -110,14 +110,14 @@ __device__ __forceinline__ void stream_load(StreamFrag<MB, NB, MX> &f, const uin
         if constexpr (MX) {
             uint4 codes = *(const uint4 *)(bptr[c] + (kk >> 1));
             uint32_t sc = bscale[c][kk >> 5];
-            f.b[c][0] = mxfp4x8_to_bf16(codes.x, sc);
-            f.b[c][1] = mxfp4x8_to_bf16(codes.y, sc);
-            f.b[c][2] = mxfp4x8_to_bf16(codes.z, sc);
-            f.b[c][3] = mxfp4x8_to_bf16(codes.w, sc);
+            f.b[c][0] = mxfp4x8_to_act<AT>(codes.x, sc);
+            f.b[c][1] = mxfp4x8_to_act<AT>(codes.y, sc);
+            f.b[c][2] = mxfp4x8_to_act<AT>(codes.z, sc);
+            f.b[c][3] = mxfp4x8_to_act<AT>(codes.w, sc);
         } else {
             const uint4 *p = (const uint4 *)(bptr[c] + kk * 2);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) f.b[c][s] = p[s];
+            for (int s = 0; s < 4; ++s) f.b[c][s] = weight_bf16_as<AT>(p[s]);
         }
     }
 #pragma unroll
@@ -133,7 +133,7 @@ __device__ __forceinline__ void stream_load(StreamFrag<MB, NB, MX> &f, const uin
     }
 }
 
-template <int MB, int NB, int EPI, bool MX, bool GROUPED>
+template <int MB, int NB, int EPI, bool MX, bool GROUPED, int AT, int OT>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
     constexpr int BM = 16 * MB;
     __shared__ floatx4_t red[3][MB][NB][64];
@@ -196,16 +196,17 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
             for (int c = 0; c < NB; ++c) acc[m][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-        StreamFrag<MB, NB, MX> cur, nxt;
-        stream_load<MB, NB, MX>(cur, bptr, bscale, aptr, kbeg);
+        StreamFrag<MB, NB> cur, nxt;
+        stream_load<MB, NB, MX, AT>(cur, bptr, bscale, aptr, kbeg);
         for (int64_t kk = kbeg; kk < kend; kk += 128) {
-            if (kk + 128 < kend) stream_load<MB, NB, MX>(nxt, bptr, bscale, aptr, kk + 128);
+            if (kk + 128 < kend) stream_load<MB, NB, MX, AT>(nxt, bptr, bscale, aptr, kk + 128);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
                 for (int m = 0; m < MB; ++m)
 #pragma unroll
-                    for (int c = 0; c < NB; ++c) acc[m][c] = mfma16x16x32(cur.a[m][s], cur.b[c][s], acc[m][c]);
+                    for (int c = 0; c < NB; ++c)
+                        acc[m][c] = mfma16x16x32<AT>(cur.a[m][s], cur.b[c][s], acc[m][c]);
             cur = nxt;
         }
 
@@ -237,13 +238,13 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
                     if constexpr (EPI == EPI_SWIGLU) {
                         if (ok) {
                             float g = acc[m][0][q], u = acc[m][NB - 1][q];
-                            ((uint16_t *)a.C)[p * a.ldc + nb * 16 + li] = f32_to_bf16(silu(g) * u);
+                            ((uint16_t *)a.C)[p * a.ldc + nb * 16 + li] = f32_to_act<OT>(silu(g) * u);
                         }
                     } else {
 #pragma unroll
                         for (int c = 0; c < NB; ++c) {
                             int64_t n = (nb * NB + c) * 16 + li;
-                            if (ok) rowsq[q] += store_elem<EPI>(a, p, n, acc[m][c][q]);
+                            if (ok) rowsq[q] += store_elem<EPI, OT>(a, p, n, acc[m][c][q]);
                         }
                     }
                 }
@@ -276,7 +277,7 @@ constexpr int kLdsTile = kTileBM * kTileBK;  // bf16 elements per operand stage
 
 __device__ __forceinline__ int swz(int row, int chunk) { return row * kTileBK + ((chunk ^ (row & 7)) << 3); }
 
-template <int EPI, bool MX, bool GROUPED>
+template <int EPI, bool MX, bool GROUPED, int AT, int OT>
 __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kLdsTile];  // [stage][A/B]
 
@@ -343,10 +344,10 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs a) {
             if constexpr (MX) {
                 uint4 codes = *(const uint4 *)(bcode + k0 / 2);
                 uint32_t sc = bsc[k0 / 32];
-                rb[0] = mxfp4x8_to_bf16(codes.x, sc);
-                rb[1] = mxfp4x8_to_bf16(codes.y, sc);
-                rb[2] = mxfp4x8_to_bf16(codes.z, sc);
-                rb[3] = mxfp4x8_to_bf16(codes.w, sc);
+                rb[0] = mxfp4x8_to_act<AT>(codes.x, sc);
+                rb[1] = mxfp4x8_to_act<AT>(codes.y, sc);
+                rb[2] = mxfp4x8_to_act<AT>(codes.z, sc);
+                rb[3] = mxfp4x8_to_act<AT>(codes.w, sc);
             } else {
 #pragma unroll
                 for (int r = 0; r < 4; ++r) rb[r] = *(const uint4 *)(bsrc[r] + k0);
@@ -382,6 +383,10 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs a) {
             for (int c = 0; c < 4; ++c) acc[m][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
         gload(0);
+        if constexpr (!MX && AT == ACT_F16) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) rb[r] = bf16x8_to_f16x8(rb[r]);
+        }
         lstore(0);
         __syncthreads();
         for (int kt = 0; kt < nk; ++kt) {
@@ -398,9 +403,15 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs a) {
 #pragma unroll
                 for (int m = 0; m < 4; ++m)
 #pragma unroll
-                    for (int c = 0; c < 4; ++c) acc[m][c] = mfma16x16x32(fa[m], fb[c], acc[m][c]);
+                    for (int c = 0; c < 4; ++c) acc[m][c] = mfma16x16x32<AT>(fa[m], fb[c], acc[m][c]);
             }
-            if (kt + 1 < nk) lstore(st ^ 1);
+            if (kt + 1 < nk) {
+                if constexpr (!MX && AT == ACT_F16) {
+#pragma unroll
+                    for (int r = 0; r < 4; ++r) rb[r] = bf16x8_to_f16x8(rb[r]);
+                }
+                lstore(st ^ 1);
+            }
             __syncthreads();
         }
 
@@ -419,14 +430,14 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs a) {
                         if (ok) {
                             float g = acc[m][c][q], u = acc[m][c + 2][q];
                             int64_t j = nb * 64 + wn * 32 + c * 16 + li;
-                            ((uint16_t *)a.C)[p * a.ldc + j] = f32_to_bf16(silu(g) * u);
+                            ((uint16_t *)a.C)[p * a.ldc + j] = f32_to_act<OT>(silu(g) * u);
                         }
                     }
                 } else {
 #pragma unroll
                     for (int c = 0; c < 4; ++c) {
                         int64_t n = nb * kTileBN + wn * 64 + c * 16 + li;
-                        float sq = ok ? store_elem<EPI>(a, p, n, acc[m][c][q]) : 0.f;
+                        float sq = ok ? store_elem<EPI, OT>(a, p, n, acc[m][c][q]) : 0.f;
                         if constexpr (EPI == EPI_NORM) {
                             sq = sum16(sq);
                             if (li == 0 && ok) a.ssq[p * a.nparts + nb * 8 + wn * 4 + c] = sq;
@@ -441,71 +452,93 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs a) {
 // Launchers
 // ---------------------------------------------------------------------------
 
-template <int MB, int NB, int EPI>
-static hipError_t stream_dispatch(const GemmArgs &a, bool mx, bool grouped, int grid, hipStream_t s) {
-    if (mx) {
-        if (grouped) gemm_stream_kernel<MB, NB, EPI, true, true><<<grid, 256, 0, s>>>(a);
-        else gemm_stream_kernel<MB, NB, EPI, true, false><<<grid, 256, 0, s>>>(a);
-    } else {
-        if (grouped) gemm_stream_kernel<MB, NB, EPI, false, true><<<grid, 256, 0, s>>>(a);
-        else gemm_stream_kernel<MB, NB, EPI, false, false><<<grid, 256, 0, s>>>(a);
-    }
+constexpr int kStreamGrid = 4096;  // persistent grid cap of the streaming kernel
+constexpr int kTileGrid = 512;     // persistent grid cap of the tiled kernel
+
+template <int MB, int NB, int EPI, bool MX, bool GROUPED, int AT, int OT>
+static hipError_t run_stream(const GemmArgs &a, hipStream_t s) {
+    const int64_t nblocks = (EPI == EPI_SWIGLU) ? a.N / 16 : a.N / (16 * NB);
+    const int64_t tiles = GROUPED ? a.max_tiles : (a.M + 16 * MB - 1) / (16 * MB);
+    const int64_t items = tiles * nblocks;
+    if (items <= 0) return hipSuccess;
+    const int grid = (int)(items < kStreamGrid ? items : kStreamGrid);
+    gemm_stream_kernel<MB, NB, EPI, MX, GROUPED, AT, OT><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
 }
 
-template <int MB>
-static hipError_t stream_epi(const GemmArgs &a, int epi, bool mx, bool grouped, int grid, hipStream_t s) {
-    switch (epi) {
-        case EPI_F32: return stream_dispatch<MB, 1, EPI_F32>(a, mx, grouped, grid, s);
-        case EPI_BF16: return stream_dispatch<MB, 1, EPI_BF16>(a, mx, grouped, grid, s);
-        case EPI_SWIGLU: return stream_dispatch<MB, 2, EPI_SWIGLU>(a, mx, grouped, grid, s);
-        case EPI_NORM: return stream_dispatch<MB, 1, EPI_NORM>(a, mx, grouped, grid, s);
-        case EPI_RESID: return stream_dispatch<MB, 1, EPI_RESID>(a, mx, grouped, grid, s);
-    }
-    return hipErrorInvalidValue;
-}
-
-hipError_t launch_gemm_stream(const GemmArgs &a, int epi, bool mx, bool grouped, int mb, int grid_cap,
-                              hipStream_t s) {
-    int64_t nblocks = (epi == EPI_SWIGLU) ? a.N / 16 : a.N / 16;
-    int64_t tiles = grouped ? a.max_tiles : (a.M + 16 * mb - 1) / (16 * mb);
-    int64_t items = tiles * nblocks;
+template <int EPI, bool MX, bool GROUPED, int AT, int OT>
+static hipError_t run_tile(const GemmArgs &a, hipStream_t s) {
+    const int64_t nblocks = (EPI == EPI_SWIGLU) ? a.N / 64 : a.N / kTileBN;
+    const int64_t tiles = GROUPED ? a.max_tiles : (a.M + kTileBM - 1) / kTileBM;
+    const int64_t items = tiles * nblocks;
     if (items <= 0) return hipSuccess;
-    int grid = (int)(items < grid_cap ? items : grid_cap);
-    switch (mb) {
-        case 1: return stream_epi<1>(a, epi, mx, grouped, grid, s);
-        case 2: return stream_epi<2>(a, epi, mx, grouped, grid, s);
-        case 4: return stream_epi<4>(a, epi, mx, grouped, grid, s);
-    }
-    return hipErrorInvalidValue;
-}
-
-template <int EPI>
-static hipError_t tile_dispatch(const GemmArgs &a, bool mx, bool grouped, int grid, hipStream_t s) {
-    if (mx) {
-        if (grouped) gemm_tile_kernel<EPI, true, true><<<grid, 256, 0, s>>>(a);
-        else gemm_tile_kernel<EPI, true, false><<<grid, 256, 0, s>>>(a);
-    } else {
-        if (grouped) gemm_tile_kernel<EPI, false, true><<<grid, 256, 0, s>>>(a);
-        else gemm_tile_kernel<EPI, false, false><<<grid, 256, 0, s>>>(a);
-    }
+    const int grid = (int)(items < kTileGrid ? items : kTileGrid);
+    gemm_tile_kernel<EPI, MX, GROUPED, AT, OT><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
 }
 
-hipError_t launch_gemm_tile(const GemmArgs &a, int epi, bool mx, bool grouped, int grid_cap, hipStream_t s) {
-    int64_t nblocks = (epi == EPI_SWIGLU) ? a.N / 64 : a.N / kTileBN;
-    int64_t tiles = grouped ? a.max_tiles : (a.M + kTileBM - 1) / kTileBM;
-    int64_t items = tiles * nblocks;
-    if (items <= 0) return hipSuccess;
-    int grid = (int)(items < grid_cap ? items : grid_cap);
-    switch (epi) {
-        case EPI_F32: return tile_dispatch<EPI_F32>(a, mx, grouped, grid, s);
-        case EPI_BF16: return tile_dispatch<EPI_BF16>(a, mx, grouped, grid, s);
-        case EPI_SWIGLU: return tile_dispatch<EPI_SWIGLU>(a, mx, grouped, grid, s);
-        case EPI_NORM: return tile_dispatch<EPI_NORM>(a, mx, grouped, grid, s);
-        case EPI_RESID: return tile_dispatch<EPI_RESID>(a, mx, grouped, grid, s);
+// Dense launches use 64-row tiles on the streaming kernel, grouped ones 16-row tiles.
+template <int EPI, int NB, bool MX, bool GROUPED, int AT, int OT>
+static hipError_t run_path(const GemmArgs &a, int path, hipStream_t s) {
+    if (path == PATH_TILE) return run_tile<EPI, MX, GROUPED, AT, OT>(a, s);
+    if constexpr (GROUPED) return run_stream<1, NB, EPI, MX, GROUPED, AT, OT>(a, s);
+    else return run_stream<4, NB, EPI, MX, GROUPED, AT, OT>(a, s);
+}
+
+hipError_t launch_router_gemm(const GemmArgs &a, int path, hipStream_t s) {
+    return run_path<EPI_F32, 1, false, false, ACT_BF16, ACT_BF16>(a, path, s);
+}
+
+hipError_t launch_down_gemm(const GemmArgs &a, int path, bool mx, int ot, hipStream_t s) {
+    if (mx) {
+        if (ot == ACT_F16) return run_path<EPI_ACT, 1, true, false, ACT_BF16, ACT_F16>(a, path, s);
+        return run_path<EPI_ACT, 1, true, false, ACT_BF16, ACT_BF16>(a, path, s);
     }
-    return hipErrorInvalidValue;
+    if (ot == ACT_F16) return run_path<EPI_ACT, 1, false, false, ACT_BF16, ACT_F16>(a, path, s);
+    return run_path<EPI_ACT, 1, false, false, ACT_BF16, ACT_BF16>(a, path, s);
+}
+
+hipError_t launch_gemm1(const GemmArgs &a, int path, bool mx, int at, hipStream_t s) {
+    if (mx) {
+        if (at == ACT_F16) return run_path<EPI_SWIGLU, 2, true, true, ACT_F16, ACT_F16>(a, path, s);
+        return run_path<EPI_SWIGLU, 2, true, true, ACT_BF16, ACT_BF16>(a, path, s);
+    }
+    if (at == ACT_F16) return run_path<EPI_SWIGLU, 2, false, true, ACT_F16, ACT_F16>(a, path, s);
+    return run_path<EPI_SWIGLU, 2, false, true, ACT_BF16, ACT_BF16>(a, path, s);
+}
+
+hipError_t launch_gemm2(const GemmArgs &a, int path, bool mx, int at, bool norm, hipStream_t s) {
+    if (norm) {
+        if (mx) {
+            if (at == ACT_F16) return run_path<EPI_NORM, 1, true, true, ACT_F16, ACT_BF16>(a, path, s);
+            return run_path<EPI_NORM, 1, true, true, ACT_BF16, ACT_BF16>(a, path, s);
+        }
+        if (at == ACT_F16) return run_path<EPI_NORM, 1, false, true, ACT_F16, ACT_BF16>(a, path, s);
+        return run_path<EPI_NORM, 1, false, true, ACT_BF16, ACT_BF16>(a, path, s);
+    }
+    if (mx) {
+        if (at == ACT_F16) return run_path<EPI_ACT, 1, true, true, ACT_F16, ACT_BF16>(a, path, s);
+        return run_path<EPI_ACT, 1, true, true, ACT_BF16, ACT_BF16>(a, path, s);
+    }
+    if (at == ACT_F16) return run_path<EPI_ACT, 1, false, true, ACT_F16, ACT_BF16>(a, path, s);
+    return run_path<EPI_ACT, 1, false, true, ACT_BF16, ACT_BF16>(a, path, s);
+}
+
+hipError_t launch_up_gemm(const GemmArgs &a, int path, bool mx, int at, bool resid, hipStream_t s) {
+    if (resid) {
+        if (mx) {
+            if (at == ACT_F16) return run_path<EPI_RESID, 1, true, false, ACT_F16, ACT_BF16>(a, path, s);
+            return run_path<EPI_RESID, 1, true, false, ACT_BF16, ACT_BF16>(a, path, s);
+        }
+        if (at == ACT_F16) return run_path<EPI_RESID, 1, false, false, ACT_F16, ACT_BF16>(a, path, s);
+        return run_path<EPI_RESID, 1, false, false, ACT_BF16, ACT_BF16>(a, path, s);
+    }
+    if (mx) {
+        if (at == ACT_F16) return run_path<EPI_F32, 1, true, false, ACT_F16, ACT_BF16>(a, path, s);
+        return run_path<EPI_F32, 1, true, false, ACT_BF16, ACT_BF16>(a, path, s);
+    }
+    if (at == ACT_F16) return run_path<EPI_F32, 1, false, false, ACT_F16, ACT_BF16>(a, path, s);
+    return run_path<EPI_F32, 1, false, false, ACT_BF16, ACT_BF16>(a, path, s);
 }
 
 }  // namespace moe

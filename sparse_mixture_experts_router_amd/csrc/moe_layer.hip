@@ -24,9 +24,6 @@ using namespace moe;
 
 namespace {
 
-constexpr int kStreamGrid = 4096;  // persistent grid cap of the streaming GEMM
-constexpr int kTileGrid = 512;     // persistent grid cap of the LDS-tiled GEMM
-
 inline size_t align256(size_t v) { return (v + 255) & ~(size_t)255; }
 
 struct Carve {
@@ -92,6 +89,8 @@ int check_desc(const moe_desc *d) {
     if (d->expert_norm < MOE_NORM_NONE || d->expert_norm > MOE_NORM_INPUT_SCALED) return MOE_ERR_INVALID_ARG;
     if (d->res_gate != MOE_RES_NONE && d->res_gate != MOE_RES_LINEAR) return MOE_ERR_INVALID_ARG;
     if (!(d->eps_in >= 0.f) || !(d->eps_expert >= 0.f)) return MOE_ERR_INVALID_ARG;
+    if (d->interm_dtype != MOE_DT_F32 && d->interm_dtype != MOE_DT_BF16 && d->interm_dtype != MOE_DT_F16)
+        return MOE_ERR_INVALID_ARG;
     if (d->T * d->top_k >= ((int64_t)1 << 31) || d->T >= ((int64_t)1 << 31)) return MOE_ERR_INVALID_ARG;
     if (d->expert_kind == MOE_EXPERT_RELU2 && d->d_latent != 0) return MOE_ERR_INVALID_ARG;
     if (d->act_dtype == MOE_DT_F32) {
@@ -127,17 +126,11 @@ struct Events {
         if (rc_) return rc_;     \
     } while (0)
 
-// Dense C[T][N] = A[T][K] * B[N][K]^T with the streaming kernel for few rows
-// and the tiled kernel otherwise.
-hipError_t dense_gemm(GemmArgs &g, int epi, bool mx, hipStream_t s) {
-    g.b_group_rows = 0;
-    g.tiles = nullptr;
-    g.ntiles = nullptr;
-    g.counts = nullptr;
-    g.offsets = nullptr;
-    if (g.M <= 128 || g.N % kTileBN != 0) return launch_gemm_stream(g, epi, mx, false, 4, kStreamGrid, s);
-    return launch_gemm_tile(g, epi, mx, false, kTileGrid, s);
-}
+// Dense C[T][N] = A[T][K] * B[N][K]^T: the streaming kernel for few rows,
+// the tiled kernel otherwise.
+int dense_path(const GemmArgs &g) { return (g.M <= 128 || g.N % kTileBN != 0) ? PATH_STREAM : PATH_TILE; }
+
+int interm_act(const moe_desc *d) { return d->interm_dtype == MOE_DT_BF16 ? ACT_BF16 : ACT_F16; }
 
 int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const void *down_w, const void *w1,
                  const void *w2, const void *up_w, const moe_gains *gains, void *out, uint8_t *ws, const Layout &L,
@@ -145,6 +138,7 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
     const int64_t T = d->T, D = d->d_model, Lw = d->d_latent, n = d->n_experts, k = d->top_k, F = d->d_ff;
     const int64_t TK = T * k;
     const bool mx = d->weight_dtype == MOE_DT_MXFP4;
+    const int at = interm_act(d);
     Events ev{dbg ? (hipEvent_t *)dbg->stage_events : nullptr, s};
 
     const uint16_t *xb = (const uint16_t *)x;
@@ -181,7 +175,7 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
         g.M = T;
         g.C = logits;
         g.ldc = n;
-        MOE_TRY(dense_gemm(g, EPI_F32, false, s));
+        MOE_TRY(launch_router_gemm(g, dense_path(g), s));
     }
     MOE_TRY_RC(ev.end(MOE_STAGE_ROUTER));
 
@@ -213,7 +207,7 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
         g.M = T;
         g.C = z;
         g.ldc = Lw;
-        MOE_TRY(dense_gemm(g, EPI_BF16, mx, s));
+        MOE_TRY(launch_down_gemm(g, dense_path(g), mx, at, s));
     }
     MOE_TRY_RC(ev.end(MOE_STAGE_DOWN));
 
@@ -239,18 +233,18 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
         g.tiles = tiles_small;
         g.ntiles = ntiles;
         g.max_tiles = (int32_t)L.max_small;
-        MOE_TRY(launch_gemm_stream(g, EPI_SWIGLU, mx, true, 1, kStreamGrid, s));
+        MOE_TRY(launch_gemm1(g, PATH_STREAM, mx, at, s));
         if (any_big) {
             g.tiles = tiles_big;
             g.ntiles = ntiles + 1;
             g.max_tiles = (int32_t)L.max_big;
-            MOE_TRY(launch_gemm_tile(g, EPI_SWIGLU, mx, true, kTileGrid, s));
+            MOE_TRY(launch_gemm1(g, PATH_TILE, mx, at, s));
         }
     }
     MOE_TRY_RC(ev.end(MOE_STAGE_GEMM1));
 
     // GEMM2: S[p] = bf16((1+gamma) * act[p] W2_e^T) and per-16-column sums of squares.
-    const int epi2 = d->expert_norm != MOE_NORM_NONE ? EPI_NORM : EPI_BF16;
+    const bool norm2 = d->expert_norm != MOE_NORM_NONE;
     MOE_TRY_RC(ev.begin(MOE_STAGE_GEMM2));
     {
         GemmArgs g{};
@@ -271,18 +265,18 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
         g.tiles = tiles_small;
         g.ntiles = ntiles;
         g.max_tiles = (int32_t)L.max_small;
-        MOE_TRY(launch_gemm_stream(g, epi2, mx, true, 1, kStreamGrid, s));
+        MOE_TRY(launch_gemm2(g, PATH_STREAM, mx, at, norm2, s));
         if (any_big) {
             g.tiles = tiles_big;
             g.ntiles = ntiles + 1;
             g.max_tiles = (int32_t)L.max_big;
-            MOE_TRY(launch_gemm_tile(g, epi2, mx, true, kTileGrid, s));
+            MOE_TRY(launch_gemm2(g, PATH_TILE, mx, at, norm2, s));
         }
     }
     MOE_TRY_RC(ev.end(MOE_STAGE_GEMM2));
 
     MOE_TRY_RC(ev.begin(MOE_STAGE_COMBINE));
-    MOE_TRY(launch_combine(S, ssq, pos, wts, T, Lw, (int)(Lw / 16), d->eps_expert, (int)k, m, s));
+    MOE_TRY(launch_combine(S, ssq, pos, wts, T, Lw, (int)(Lw / 16), d->eps_expert, (int)k, at, m, s));
     MOE_TRY_RC(ev.end(MOE_STAGE_COMBINE));
 
     // out = x + g * (m W_u^T)  (or out = m W_u^T).
@@ -302,9 +296,9 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
             g.resid = xb;
             g.gate = gains->res_gate;
             g.y = dbg ? dbg->y : nullptr;
-            MOE_TRY(dense_gemm(g, EPI_RESID, mx, s));
+            MOE_TRY(launch_up_gemm(g, dense_path(g), mx, at, true, s));
         } else {
-            MOE_TRY(dense_gemm(g, EPI_F32, mx, s));
+            MOE_TRY(launch_up_gemm(g, dense_path(g), mx, at, false, s));
             if (dbg && dbg->y) MOE_TRY(hipMemcpyAsync(dbg->y, out, (size_t)T * D * 4, hipMemcpyDeviceToDevice, s));
         }
     }
@@ -318,6 +312,13 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
             MOE_TRY(hipMemcpyAsync(dbg->expert_offsets, offsets, (n + 1) * 4, hipMemcpyDeviceToDevice, s));
         if (dbg->perm_tok) MOE_TRY(hipMemcpyAsync(dbg->perm_tok, perm_tok, TK * 4, hipMemcpyDeviceToDevice, s));
         if (dbg->perm_slot) MOE_TRY(hipMemcpyAsync(dbg->perm_slot, perm_slot, TK * 4, hipMemcpyDeviceToDevice, s));
+        if (dbg->pos) MOE_TRY(hipMemcpyAsync(dbg->pos, pos, TK * 4, hipMemcpyDeviceToDevice, s));
+        if (dbg->z) MOE_TRY(hipMemcpyAsync(dbg->z, z, (size_t)T * Lw * 2, hipMemcpyDeviceToDevice, s));
+        if (dbg->act) MOE_TRY(hipMemcpyAsync(dbg->act, act, (size_t)TK * F * 2, hipMemcpyDeviceToDevice, s));
+        if (dbg->S) MOE_TRY(hipMemcpyAsync(dbg->S, S, (size_t)TK * Lw * 2, hipMemcpyDeviceToDevice, s));
+        if (dbg->ssq && ssq)
+            MOE_TRY(hipMemcpyAsync(dbg->ssq, ssq, (size_t)TK * (Lw / 16) * 4, hipMemcpyDeviceToDevice, s));
+        if (dbg->m) MOE_TRY(hipMemcpyAsync(dbg->m, m, (size_t)T * Lw * 2, hipMemcpyDeviceToDevice, s));
     }
     return MOE_OK;
 }
@@ -365,6 +366,7 @@ int forward_f32(const moe_desc *d, const void *x, const void *router_w, const vo
             MOE_TRY(hipMemcpyAsync(dbg->expert_offsets, offsets, (n + 1) * 4, hipMemcpyDeviceToDevice, s));
         if (dbg->perm_tok) MOE_TRY(hipMemcpyAsync(dbg->perm_tok, perm_tok, TK * 4, hipMemcpyDeviceToDevice, s));
         if (dbg->perm_slot) MOE_TRY(hipMemcpyAsync(dbg->perm_slot, perm_slot, TK * 4, hipMemcpyDeviceToDevice, s));
+        if (dbg->pos) MOE_TRY(hipMemcpyAsync(dbg->pos, pos, TK * 4, hipMemcpyDeviceToDevice, s));
     }
     return MOE_OK;
 }
@@ -396,6 +398,7 @@ int moe_layer_forward(const moe_desc *d, const void *x, const void *router_w, co
                       void *out, void *workspace, size_t workspace_bytes, moe_debug *dbg, void *stream) {
     int rc = check_desc(d);
     if (rc != MOE_OK) return rc;
+    if (d->T == 0) return MOE_OK;  // nothing to read or write: pointers may be NULL
     if (!x || !router_w || !expert_w1 || !expert_w2 || !out) return MOE_ERR_INVALID_ARG;
     if (d->d_latent && (!down_w || !up_w)) return MOE_ERR_INVALID_ARG;
     if (d->res_gate == MOE_RES_LINEAR && (!gains || !gains->res_gate)) return MOE_ERR_INVALID_ARG;
@@ -444,7 +447,7 @@ int moe_router_topk(const moe_desc *d, const void *u, const void *router_w, cons
         g.M = d->T;
         g.C = lg;
         g.ldc = d->n_experts;
-        MOE_TRY(dense_gemm(g, EPI_F32, false, s));
+        MOE_TRY(launch_router_gemm(g, dense_path(g), s));
     }
     MOE_TRY(launch_topk(lg, router_bias, d->T, (int)d->n_experts, (int)d->top_k, d->bias_in_weights, topk_idx, topk_w,
                         s));

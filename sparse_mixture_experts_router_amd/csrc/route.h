@@ -17,8 +17,9 @@ hipError_t launch_topk(const float *logits, const float *bias, int64_t T, int n,
 hipError_t launch_permute(const int32_t *idx, int64_t T, int k, int n, int32_t *counts, int32_t *offsets,
                           int32_t *perm_tok, int32_t *perm_slot, int32_t *pos, TileEntry *tiles_small,
                           TileEntry *tiles_big, int32_t *ntiles, int small_max, hipStream_t s);
+// m in activation type `ot` (ACT_BF16 / ACT_F16).
 hipError_t launch_combine(const uint16_t *S, const float *ssq, const int32_t *pos, const float *w, int64_t T,
-                          int64_t L, int nparts, float eps, int k, uint16_t *m, hipStream_t s);
+                          int64_t L, int nparts, float eps, int k, int ot, uint16_t *m, hipStream_t s);
 
 hipError_t launch_router_f32(const float *x, const float *W, int64_t T, int n, int64_t d, float *logits,
                              hipStream_t s);

@@ -260,11 +260,16 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__
 }
 
 // ---------------------------------------------------------------------------
-// Norm part 2 and weighted combine (bf16 latent path):
+// Norm part 2 and weighted combine (latent path):
 //   r_p = (sum_q ssq[p][q] / L + eps)^-1/2   (partials summed in index order)
-//   m_t = sum_j w_tj * r_{p_tj} * S[p_tj]     (slots in order, fp32) -> bf16
+//   m_t = sum_j w_tj * r_{p_tj} * S[p_tj]     (slots in order, fp32)
+// m is stored in the activation type of the up-projection.  With the
+// input-scaled norm every normalised expert output has |n_i| <= sqrt(L) and
+// the weights sum to one, so |m_i| <= sqrt(L) (64 at L = 4096): fp16 cannot
+// overflow there.
 // ---------------------------------------------------------------------------
 
+template <int OT>
 __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict__ S, const float *__restrict__ ssq,
                                                       const int32_t *__restrict__ pos, const float *__restrict__ w,
                                                       int64_t L, int nparts, float eps, int k,
@@ -300,10 +305,9 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
             for (int i = 0; i < 8; ++i) acc[i] += c * bf16_to_f32(h[i]);
         }
         uint4 o;
-        o.x = pack_bf16x2(acc[0], acc[1]);
-        o.y = pack_bf16x2(acc[2], acc[3]);
-        o.z = pack_bf16x2(acc[4], acc[5]);
-        o.w = pack_bf16x2(acc[6], acc[7]);
+        uint16_t *oh = (uint16_t *)&o;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) oh[i] = f32_to_act<OT>(acc[i]);
         *(uint4 *)(m + t * L + ch * 8) = o;
     }
 }
@@ -409,8 +413,9 @@ hipError_t launch_permute(const int32_t *idx, int64_t T, int k, int n, int32_t *
 }
 
 hipError_t launch_combine(const uint16_t *S, const float *ssq, const int32_t *pos, const float *w, int64_t T,
-                          int64_t L, int nparts, float eps, int k, uint16_t *m, hipStream_t s) {
-    combine_kernel<<<(unsigned)T, 256, 0, s>>>(S, ssq, pos, w, L, nparts, eps, k, m);
+                          int64_t L, int nparts, float eps, int k, int ot, uint16_t *m, hipStream_t s) {
+    if (ot == ACT_F16) combine_kernel<ACT_F16><<<(unsigned)T, 256, 0, s>>>(S, ssq, pos, w, L, nparts, eps, k, m);
+    else combine_kernel<ACT_BF16><<<(unsigned)T, 256, 0, s>>>(S, ssq, pos, w, L, nparts, eps, k, m);
     return hipGetLastError();
 }
 

@@ -43,8 +43,7 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        if not os.path.exists(_LIB):
-            build()
+        build()  # compiles only when the library is missing or older than its source
         _lib = ctypes.CDLL(_LIB)
         vp, u64, i64, f32, cp = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int64, ctypes.c_float, ctypes.c_char_p
         _lib.synth_philox4x32_10.argtypes = [vp, vp, vp]
@@ -158,6 +157,7 @@ class Preset:
     chunks: int = 1
     w_std: float = 0.02            # latent layers; c0 uses 1/sqrt(fan_in)
     bias_in_weights: int = 0
+    interm: str = "f16"            # dtype a device keeps z, SwiGLU output and m in: "f16" | "bf16"
 
     @property
     def chunk_T(self) -> int:

@@ -30,7 +30,7 @@ def desc_of(p: synthetic.Preset, T: int | None = None):
     return moe.make_desc(p.chunk_T if T is None else T, p.d, p.L, p.n, p.k, p.F, expert_kind=p.kind, act=p.act,
                          router=p.router_w, weights=p.weights, in_norm=p.in_norm, expert_norm=p.expert_norm,
                          res_gate=p.res_gate, bias_in_weights=p.bias_in_weights, eps_in=p.eps_in,
-                         eps_expert=p.eps_expert)
+                         eps_expert=p.eps_expert, interm=p.interm)
 
 
 class DeviceLayer:
@@ -50,7 +50,7 @@ class DeviceLayer:
                 "gamma_expert": self.dev.get("gamma_ex"), "res_gate": self.dev.get("gate")}
 
 
-def run(layer: DeviceLayer, x: np.ndarray, dbg: bool = True, workspace=None):
+def run(layer: DeviceLayer, x: np.ndarray, dbg: bool = True, workspace=None, stages: bool = True):
     p = layer.p
     T = x.shape[0]
     desc = desc_of(p, T)
@@ -64,7 +64,15 @@ def run(layer: DeviceLayer, x: np.ndarray, dbg: bool = True, workspace=None):
              "expert_offsets": torch.empty(p.n + 1, dtype=torch.int32, device="cuda"),
              "perm_tok": torch.empty(T * p.k, dtype=torch.int32, device="cuda"),
              "perm_slot": torch.empty(T * p.k, dtype=torch.int32, device="cuda"),
-             "y": torch.empty((T, p.d), dtype=torch.float32, device="cuda")}
+             "y": torch.empty((T, p.d), dtype=torch.float32, device="cuda"),
+             "pos": torch.empty((T, p.k), dtype=torch.int32, device="cuda")}
+        if stages and p.act == "bf16":
+            TK = T * p.k
+            D.update({"z": torch.empty((T, p.L), dtype=torch.int16, device="cuda"),
+                      "act": torch.empty((TK, p.F), dtype=torch.int16, device="cuda"),
+                      "S": torch.empty((TK, p.L), dtype=torch.int16, device="cuda"),
+                      "ssq": torch.empty((TK, p.L // 16), dtype=torch.float32, device="cuda"),
+                      "m": torch.empty((T, p.L), dtype=torch.int16, device="cuda")})
     dv = layer.dev
     moe.moe_layer_forward(desc, xd, dv["router_w"], dv.get("down_w"), dv["w1"], dv["w2"], dv.get("up_w"),
                           layer.gains(), out, workspace=workspace, dbg=D)
@@ -72,12 +80,25 @@ def run(layer: DeviceLayer, x: np.ndarray, dbg: bool = True, workspace=None):
     res = {"out": out.cpu().numpy()}
     if dbg:
         for k_, v in D.items():
-            res[k_] = v.cpu().numpy()
+            a = v.cpu().numpy()
+            res[k_] = a.view(np.uint16) if a.dtype == np.int16 else a
     return res
 
 
 def oracle_cfg(p: synthetic.Preset) -> dict:
     return p.cfg()
+
+
+def gate_weight_atol(p) -> float:
+    """Tolerance of the gate weights.  Without an input norm both sides see
+    the same stored u and their fp32 logits differ only by accumulation
+    order (~1e-6), so 2e-5.  With an input norm, u is itself a bf16 rounding
+    of a value the GPU computes in fp32 and the oracle in fp64: a few
+    elements land one bf16 ulp (2^-8 relative) apart, shifting a logit by
+    about sqrt(#flips) * 2^-8 * |u| * std(W) (~3e-4 for 1% flips at the
+    tested shapes, 5 sigma ~1.5e-3 at d=8192) and a softmax weight by at most
+    half of that, so 1e-3."""
+    return 1e-3 if (p.act == "bf16" and p.in_norm != "none") else 2e-5
 
 
 def check_routing(p, host, x, gpu, tokens, label=""):
@@ -103,9 +124,20 @@ def check_routing(p, host, x, gpu, tokens, label=""):
     order_bad = np.flatnonzero(ordered & ~(gidx == r["idx"]).all(axis=1))
     assert order_bad.size == 0, "%s routing order differs at tokens %s" % (label, tokens[order_bad][:10])
     same = (gidx == r["idx"]).all(axis=1)
-    np.testing.assert_allclose(gpu["topk_w"][tokens][same], r["w"][same], rtol=0, atol=2e-5,
+    np.testing.assert_allclose(gpu["topk_w"][tokens][same], r["w"][same], rtol=0, atol=gate_weight_atol(p),
                                err_msg=label + " gate weights")
     return int((~clean).sum())
+
+
+# The oracle's bf16-dataflow mode (z, the SwiGLU output and m rounded to
+# bf16 where the device stores them) is reported beside the exact oracle.  It
+# is not a tighter bar: a single one-ulp flip upstream (an fp32 and an fp64
+# sum of the same products straddling a bf16 boundary) shifts every later
+# value of that token slightly and re-draws a few percent of its later
+# roundings, so whole-layer agreement with the dataflow oracle is of the order
+# of the bf16 rounding noise itself.  The per-stage checks below (check_stages)
+# are the tight ones.
+TOL_DATAFLOW = {"f32": 1e-5, "bf16": 2e-2, "mxfp4": 5e-2}
 
 
 def compare(p: synthetic.Preset, host: dict, x: np.ndarray, gpu: dict, tokens=None, route_tokens=None,
@@ -113,13 +145,15 @@ def compare(p: synthetic.Preset, host: dict, x: np.ndarray, gpu: dict, tokens=No
     """Compare GPU results with the oracle.
 
     Routing on rows `route_tokens` (all rows if None), see check_routing.
-    Outputs on rows `tokens` (all if None): max |out_gpu - out_oracle| and
-    max |y_gpu - y_oracle| within tol * RMS(y_oracle), where tokens whose GPU
-    experts differ from the oracle's (only near-ties can) are evaluated by the
-    oracle with the GPU's experts.  Permutation: bit-exact against the
-    oracle's permutation of the GPU's own top-k indices.
-    weights_key: which stored form of the big weights the GPU ran (the
-    oracle decodes the same bits), e.g. "mxfp4".
+    Layer outputs on rows `tokens` (all if None):
+      graded:  max |out_gpu - out_oracle| <= tol * RMS(y_oracle) against the
+               exact (fp64) oracle, tol = 1e-5 (fp32), 2e-2 (bf16), 5e-2
+               (MXFP4, on the same dequantised bits);
+      reported: the same against the oracle's bf16-dataflow mode.
+    Tokens whose GPU experts differ from the oracle's (only near-ties can)
+    are evaluated by the oracle with the GPU's experts.  Permutation:
+    bit-exact against the oracle's permutation of the GPU's own indices.
+    weights_key: which stored form of the big weights the GPU ran, e.g. "mxfp4".
     """
     T = x.shape[0]
     tok = np.arange(T, dtype=np.int64) if tokens is None else np.asarray(tokens, np.int64)
@@ -132,25 +166,176 @@ def compare(p: synthetic.Preset, host: dict, x: np.ndarray, gpu: dict, tokens=No
     excluded = check_routing(p, t, x, gpu, rtok, label)
     t["x"] = x
     cfg = oracle_cfg(p)
-    r = oracle.forward(cfg, t, tokens=tok)
     gidx = gpu["topk_idx"][tok]
-    y_ref, out_ref = r["y"].copy(), r["out"].copy()
-    diff = np.flatnonzero(~(gidx == r["idx"]).all(axis=1))
-    if diff.size:
-        rf = oracle.forward(cfg, t, tokens=tok[diff], forced=gidx[diff])
-        y_ref[diff], out_ref[diff] = rf["y"], rf["out"]
-    rms = float(np.sqrt(np.mean(y_ref ** 2)))
-    tol = TOL[p.weights if p.act == "bf16" else "f32"]
-    err_out = float(np.abs(gpu["out"][tok] - out_ref).max())
-    err_y = float(np.abs(gpu["y"][tok] - y_ref).max())
-    say("%s: routed=%d (excluded %d) compared=%d forced=%d rms(y)=%.4g max|dout|/rms=%.3g max|dy|/rms=%.3g "
-        "(tol %.0e)" % (label, len(rtok), excluded, len(tok), diff.size, rms, err_out / rms, err_y / rms, tol))
-    assert err_out <= tol * rms, "%s out error %.3g > %.3g" % (label, err_out, tol * rms)
-    assert err_y <= tol * rms, "%s y error %.3g > %.3g" % (label, err_y, tol * rms)
+    refs = {}
+    for mode, mirror in (("exact", False), ("dataflow", True)):
+        r = oracle.forward(cfg, t, tokens=tok, mirror=mirror)
+        y_ref, out_ref = r["y"].copy(), r["out"].copy()
+        diff = np.flatnonzero(~(gidx == r["idx"]).all(axis=1))
+        if diff.size:
+            rf = oracle.forward(cfg, t, tokens=tok[diff], forced=gidx[diff], mirror=mirror)
+            y_ref[diff], out_ref[diff] = rf["y"], rf["out"]
+        refs[mode] = (y_ref, out_ref, diff.size)
+    y_ex, out_ex, nforced = refs["exact"]
+    y_df, out_df, _ = refs["dataflow"]
+    rms = float(np.sqrt(np.mean(y_ex ** 2)))
+    kind = p.weights if p.act == "bf16" else "f32"
+    tol, tol_df = TOL[kind], TOL_DATAFLOW[kind]
+    e_out = float(np.abs(gpu["out"][tok] - out_ex).max()) / rms
+    e_y = float(np.abs(gpu["y"][tok] - y_ex).max()) / rms
+    e_out_df = float(np.abs(gpu["out"][tok] - out_df).max()) / rms
+    e_y_df = float(np.abs(gpu["y"][tok] - y_df).max()) / rms
+    say("%s: routed=%d (excluded %d) compared=%d forced=%d rms(y)=%.4g | exact: max|dout|/rms=%.3g (tol %.0e) "
+        "max|dy|/rms=%.3g | bf16-dataflow: max|dout|/rms=%.3g max|dy|/rms=%.3g (tol %.0e)" % (
+            label, len(rtok), excluded, len(tok), nforced, rms, e_out, tol, e_y, e_out_df, e_y_df, tol_df))
+    assert e_out <= tol, "%s out error %.3g * RMS(y) > %.0e" % (label, e_out, tol)
+    if kind == "f32":
+        assert e_y <= tol, "%s y error %.3g * RMS(y) > %.0e" % (label, e_y, tol)
     if check_perm:
         pr = oracle.permute(gpu["topk_idx"], p.n)
         np.testing.assert_array_equal(gpu["expert_counts"], pr["counts"], err_msg=label + " counts")
         np.testing.assert_array_equal(gpu["expert_offsets"], pr["offsets"], err_msg=label + " offsets")
         np.testing.assert_array_equal(gpu["perm_tok"], pr["perm_tok"], err_msg=label + " perm_tok")
         np.testing.assert_array_equal(gpu["perm_slot"], pr["perm_slot"], err_msg=label + " perm_slot")
-    return {"err_out": err_out / rms, "err_y": err_y / rms, "excluded": excluded}
+    return {"err_out": e_out, "err_y": e_y, "err_out_df": e_out_df, "err_y_df": e_y_df, "excluded": excluded}
+
+
+# ---------------------------------------------------------------------------
+# Stage checks: each device stage against the exact function of the device's
+# own stage input, rounded where the device stores the result.  Agreement is
+# to one bf16 ulp on a small fraction of elements: an fp32 (device) and an
+# fp64 sum of the same products can straddle a bf16 rounding boundary.
+# ---------------------------------------------------------------------------
+
+FLIP_FRACTION = 5e-3
+
+
+def bf16f(a: np.ndarray) -> np.ndarray:
+    return synthetic.bf16_to_f32(np.ascontiguousarray(a).view(np.uint16)).astype(np.float64)
+
+
+def round_bf16(v: np.ndarray) -> np.ndarray:
+    """bf16 RNE of float64 values (torch's conversion, a library routine)."""
+    return torch.from_numpy(np.asarray(v, np.float64)).to(torch.bfloat16).to(torch.float64).numpy()
+
+
+def round_f16(v: np.ndarray) -> np.ndarray:
+    return torch.from_numpy(np.asarray(v, np.float64)).to(torch.float16).to(torch.float64).numpy()
+
+
+def f16f(a: np.ndarray) -> np.ndarray:
+    return np.ascontiguousarray(a).view(np.uint16).view(np.float16).astype(np.float64)
+
+
+def ulp_bf16(v: np.ndarray) -> np.ndarray:
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -126)))
+    return 2.0 ** (e - 7)
+
+
+def ulp_f16(v: np.ndarray) -> np.ndarray:
+    e = np.floor(np.log2(np.maximum(np.abs(v), 2.0 ** -14)))
+    return 2.0 ** (e - 10)
+
+
+def interm_ops(p):
+    """(decode, round, ulp) of the dtype the device keeps z, act and m in."""
+    if p.interm == "bf16":
+        return bf16f, round_bf16, ulp_bf16
+    return f16f, round_f16, ulp_f16
+
+
+def weight_rows(host: dict, key: str, fmt: str, rows_total: int, K: int, row0: int, nrows: int) -> np.ndarray:
+    """Rows [row0, row0+nrows) of a stored [rows_total][K] weight, as float64."""
+    w = host[key]
+    if fmt == "mxfp4":
+        codes = w[:rows_total * K // 2].reshape(rows_total, K // 2)[row0:row0 + nrows]
+        sc = w[rows_total * K // 2:].reshape(rows_total, K // 32)[row0:row0 + nrows]
+        buf = np.concatenate([codes.reshape(-1), sc.reshape(-1)])
+        return oracle.decode_matrix(buf, "mxfp4", nrows, K)
+    flat = w.reshape(-1, K)[row0:row0 + nrows]
+    return bf16f(flat) if flat.dtype == np.uint16 else flat.astype(np.float64)
+
+
+def _flips(name, got, ref, label, ulp=ulp_bf16, floor=None):
+    """got vs ref: equal except one-ulp flips; `floor` (per row) admits the
+    absolute error of an fp32 sum where the result nearly cancels."""
+    d = np.abs(got - ref)
+    lim = 1.01 * ulp(ref)
+    if floor is not None:
+        lim = np.maximum(lim, floor[:, None])
+    bad = d > lim
+    frac = float((d > 0).mean())
+    say("  stage %-4s %s: differing %.4f%%, beyond 1 ulp %d" % (name, label, 100 * frac, int(bad.sum())))
+    assert not bad.any(), "%s stage %s: %d elements beyond one bf16 ulp" % (label, name, int(bad.sum()))
+    assert frac <= FLIP_FRACTION, "%s stage %s: %.3g of elements differ" % (label, name, frac)
+
+
+def check_stages(p: synthetic.Preset, host: dict, x: np.ndarray, gpu: dict, tokens, label: str = ""):
+    """Stage checks on tokens `tokens` and their (token, slot) rows."""
+    tok = np.asarray(tokens, np.int64)
+    fmt = p.weights
+    dec, rnd, ulp = interm_ops(p)
+    rowfloor = lambda a: 3e-5 * np.sqrt(np.mean(a ** 2, axis=1))
+    d, L, F, n, k = p.d, p.L, p.F, p.n, p.k
+    xf = bf16f(x[tok])
+    # input norm (exact, fp64) and down-projection
+    if p.in_norm != "none":
+        gam = 1.0 + host["gamma_in"].astype(np.float64)
+        if p.in_norm == "centered":
+            u = gam * xf / np.sqrt((xf * xf).mean(1, keepdims=True) + p.eps_in)
+        else:
+            s_ = round_bf16(gam * xf)
+            u = s_ / np.sqrt((s_ * s_).mean(1, keepdims=True) + p.eps_in)
+        u = round_bf16(u)
+    else:
+        u = xf
+    Wd = weight_rows(host, "down_w", fmt, L, d, 0, L)
+    zexact = u @ Wd.T
+    zref = rnd(zexact)
+    zg = dec(gpu["z"][tok])
+    if p.in_norm != "none":
+        # u itself may differ by one bf16 ulp in a few elements: z within 1e-3 relative of the row
+        dz = np.abs(zg - zexact)
+        assert (dz <= 1e-3 * np.sqrt(np.mean(zexact ** 2, axis=1))[:, None] + ulp(zexact)).all(), label + " stage z"
+    else:
+        _flips("z", zg, zref, label, ulp, rowfloor(zexact))
+    del Wd
+    pos = gpu["pos"][tok]
+    rows = pos.reshape(-1)
+    offs = gpu["expert_offsets"]
+    eid = np.searchsorted(offs, rows, side="right") - 1
+    zfull = dec(gpu["z"])
+    ptok = gpu["perm_tok"]
+    actg = dec(gpu["act"][rows])
+    Sg = bf16f(gpu["S"][rows])
+    act_ref = np.zeros_like(actg)
+    o_ref = np.zeros_like(Sg)
+    for e in np.unique(eid):
+        sel = np.flatnonzero(eid == e)
+        W1 = weight_rows(host, "w1", fmt, n * 2 * F, L, e * 2 * F, 2 * F)
+        zin = zfull[ptok[rows[sel]]]
+        g_, v_ = zin @ W1[:F].T, zin @ W1[F:].T
+        act_ref[sel] = g_ / (1 + np.exp(-g_)) * v_
+        W2 = weight_rows(host, "w2", fmt, n * L, F, e * L, L)
+        o_ref[sel] = actg[sel] @ W2.T
+    _flips("act", actg, rnd(act_ref), label, ulp, rowfloor(act_ref))
+    gam = 1.0 + (host["gamma_ex"].astype(np.float64) if "gamma_ex" in host else 0.0)
+    S_ref = round_bf16(gam * o_ref)
+    _flips("S", Sg, S_ref, label, ulp_bf16, rowfloor(gam * o_ref))
+    if p.expert_norm != "none":
+        sq = (Sg if p.expert_norm == "input_scaled" else o_ref) ** 2
+        ssq_ref = sq.reshape(len(rows), L // 16, 16).sum(2)
+        np.testing.assert_allclose(gpu["ssq"][rows], ssq_ref, rtol=2e-5, atol=1e-30, err_msg=label + " ssq")
+        r = 1.0 / np.sqrt(gpu["ssq"][rows].astype(np.float64).sum(1) / L + p.eps_expert)
+    else:
+        r = np.ones(len(rows))
+    coef = (gpu["topk_w"][tok].reshape(-1).astype(np.float64) * r).reshape(len(tok), k)
+    m_exact = np.einsum("tj,tjl->tl", coef, Sg.reshape(len(tok), k, L))
+    mg = dec(gpu["m"][tok])
+    _flips("m", mg, rnd(m_exact), label, ulp, rowfloor(m_exact))
+    Wu = weight_rows(host, "up_w", fmt, d, L, 0, d)
+    y_ref = mg @ Wu.T
+    rms = float(np.sqrt(np.mean(y_ref ** 2)))
+    assert np.abs(gpu["y"][tok] - y_ref).max() <= 1e-5 * rms, label + " stage up (y)"
+    out_ref = xf + host["gate"].astype(np.float64) * y_ref if p.res_gate == "linear" else y_ref
+    assert np.abs(gpu["out"][tok] - out_ref).max() <= 1e-5 * max(rms, 1.0), label + " stage up (out)"

@@ -7,7 +7,7 @@ import pytest
 import torch
 
 import synthetic
-from gpu_helpers import DeviceLayer, compare, run, say, to_dev
+from gpu_helpers import DeviceLayer, check_stages, compare, run, say, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -52,6 +52,7 @@ def test_c1_decode_T64(bf16_layer):
     touched = int((gpu["expert_counts"] > 0).sum())
     say("c1 touched experts: %d" % touched)
     compare(p, bf16_layer.host, x, gpu, label="c1")
+    check_stages(p, bf16_layer.host, x, gpu, synthetic.sample_tokens(p.T, 4, seed=11), label="c1")
 
 
 def test_c2_prefill_T8192(layer_host, bf16_layer):
@@ -62,6 +63,7 @@ def test_c2_prefill_T8192(layer_host, bf16_layer):
     say("c2 tokens/expert min %d max %d" % (c.min(), c.max()))
     compare(p, bf16_layer.host, x, gpu, tokens=synthetic.sample_tokens(p.T, 32, seed=21),
             route_tokens=synthetic.sample_tokens(p.T, 1024, seed=22), label="c2")
+    check_stages(p, bf16_layer.host, x, gpu, synthetic.sample_tokens(p.T, 4, seed=23), label="c2")
 
 
 def test_c3_skewed_T16384(layer_host, bf16_layer):
@@ -76,6 +78,7 @@ def test_c3_skewed_T16384(layer_host, bf16_layer):
     # sample includes tokens routed to cold experts
     tok = synthetic.sample_tokens(p.T, 32, seed=31)
     compare(p, lay.host, x, gpu, tokens=tok, route_tokens=synthetic.sample_tokens(p.T, 1024, seed=32), label="c3")
+    check_stages(p, lay.host, x, gpu, tok[:4], label="c3")
 
 
 @pytest.mark.parametrize("name", ["c4c", "c4i"])
@@ -88,3 +91,5 @@ def test_c4_mxfp4_chunks(name, layer_host, bf16_layer):
         compare(p, lay.host, x, gpu, tokens=synthetic.sample_tokens(p.chunk_T, 24, seed=40 + chunk),
                 route_tokens=synthetic.sample_tokens(p.chunk_T, 512, seed=50 + chunk),
                 label="%s chunk %d" % (name, chunk))
+        check_stages(p, lay.host, x, gpu, synthetic.sample_tokens(p.chunk_T, 3, seed=60 + chunk),
+                     label="%s chunk %d" % (name, chunk))

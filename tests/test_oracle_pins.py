@@ -383,3 +383,13 @@ def test_latent_layer_parameter_counts():
     assert abs(p.k * per_expert * 62 / 1e9 - 24.96) < 0.01    # about 25B active expert parameters
     # the two-matrix 8192->4096->8192 reading would exceed the total
     assert 2 * 8192 * 4096 * 256 * 62 > 816e9
+
+
+def test_round_f16_matches_library_and_ties():
+    rng = np.random.default_rng(2)
+    vals = np.concatenate([rng.standard_normal(2000) * 10.0 ** rng.integers(-9, 5, 2000),
+                           [1.0 + 2 ** -11, 1.0 + 3 * 2 ** -11, 65504.0, 65519.0, 65520.0, 2 ** -25, 3 * 2 ** -25]])
+    ours = np.array([oracle.round_f16(v) for v in vals])
+    ref = torch.tensor(vals).to(torch.float16).to(torch.float64).numpy()
+    np.testing.assert_array_equal(ours, ref)
+    assert oracle.round_f16(1.0 + 2 ** -11) == 1.0 and oracle.round_f16(65520.0) == np.inf
