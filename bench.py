@@ -48,6 +48,23 @@ def layer_flops(p) -> dict:
     return {"total": T * per_tok, "gemm1": T * p.k * 2 * p.L * 2 * p.F}
 
 
+def recorded_traffic(name: str):
+    """HBM bytes per launch of a kernel from a committed rocprofv3 counter
+    record under profiles/, or None when the kernel sources changed since
+    the counters were taken."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", name)
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    h = hashlib.sha256()
+    for f in ("gemm.hip", "gemm.h", "common.h"):
+        h.update(open(os.path.join(ROOT, "sparse_mixture_experts_router_amd", "csrc", f), "rb").read())
+    if h.hexdigest()[:16] != rec.get("source_sha256_16"):
+        return None
+    return rec["traffic_bytes"]
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -57,6 +74,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
+                    help="only run the library's plain 16-byte copy of MIB MiB (5 times), to calibrate HBM counters")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
@@ -70,6 +89,19 @@ def main():
     import synthetic
 
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        n = args.copy_calibration << 20
+        a = torch.rand(n // 4, dtype=torch.float32, device="cuda")  # random bits: constant data reads as far fewer bytes
+        b = torch.empty_like(a)
+        moe.moe_hbm_copy(b, a, n)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(5):
+            moe.moe_hbm_copy(b, a, n)
+        torch.cuda.synchronize()
+        dt = (time.perf_counter() - t0) / 5
+        print(json.dumps({"copy_bytes": n, "copy_GBps": round(2 * n / dt / 1e9, 1)}))
+        return
     moe.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
 
@@ -156,7 +188,8 @@ def main():
                    "stage_ms": {k: round(v, 4) for k, v in r["stages"].items()}},
         "roofline": {"kernel": "gemm_stream_kernel (grouped GEMM1 + SwiGLU)", "bound": "hbm",
                      "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(g1_gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                     "frac": round(g1_gbs / HBM_PEAK_GBS, 4),
+                     "traffic": recorded_traffic("decode_T64_gemm1_traffic.json"),
                      "bytes_per_launch": by["gemm1"], "avg_launch_ms": round(g1_ms, 4)},
     }
 

@@ -232,6 +232,15 @@ int moe_router_topk(const moe_desc *desc, const void *u, const void *router_w, c
 int moe_permute(int64_t T, int64_t k, int64_t n, const int32_t *topk_idx, int32_t *counts, int32_t *offsets,
                 int32_t *perm_tok, int32_t *perm_slot, int32_t *pos, void *stream);
 
+/*
+ * Plain device copy dst = src of `bytes` bytes (a multiple of 16; both
+ * pointers 16-byte aligned; the ranges must not overlap), with 16-byte
+ * loads and stores: the reference kernel for the HBM byte counters
+ * (FETCH_SIZE / WRITE_SIZE) and the achievable copy bandwidth that the
+ * layer's bandwidth-bound kernels are measured against.
+ */
+int moe_hbm_copy(void *dst, const void *src, size_t bytes, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -77,12 +77,13 @@ def lib() -> ctypes.CDLL:
         L.moe_router_workspace_bytes.restype = sz
         L.moe_router_topk.argtypes = [ctypes.POINTER(moe_desc), vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_permute.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
+        L.moe_hbm_copy.argtypes = [vp, vp, sz, vp]
         _lib = L
     return _lib
 
 
 EXPORTED = ["moe_error_string", "moe_validate", "moe_workspace_bytes", "moe_layer_forward",
-            "moe_router_workspace_bytes", "moe_router_topk", "moe_permute"]
+            "moe_router_workspace_bytes", "moe_router_topk", "moe_permute", "moe_hbm_copy"]
 
 
 def make_desc(T, d_model, d_latent, n_experts, top_k, d_ff, expert_kind="swiglu3", act="bf16", router="bf16",
@@ -203,6 +204,12 @@ def moe_permute(T, k, n, topk_idx, counts, offsets, perm_tok, perm_slot, pos, st
                            _stream(stream))
     if rc != MOE_OK:
         raise MoeError(rc, "moe_permute")
+
+
+def moe_hbm_copy(dst, src, nbytes: int, stream=None):
+    rc = lib().moe_hbm_copy(_ptr(dst, "dst", nbytes), _ptr(src, "src", nbytes), nbytes, _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_hbm_copy")
 
 
 # ---------------------------------------------------------------------------

@@ -464,4 +464,10 @@ int moe_permute(int64_t T, int64_t k, int64_t n, const int32_t *topk_idx, int32_
     return MOE_OK;
 }
 
+int moe_hbm_copy(void *dst, const void *src, size_t bytes, void *stream) {
+    if ((bytes & 15) || (bytes && (!dst || !src)) || (((uintptr_t)dst | (uintptr_t)src) & 15)) return MOE_ERR_INVALID_ARG;
+    MOE_TRY(launch_copy16(src, dst, (int64_t)bytes, as_stream(stream)));
+    return MOE_OK;
+}
+
 }  // extern "C"

@@ -21,6 +21,9 @@ hipError_t launch_permute(const int32_t *idx, int64_t T, int k, int n, int32_t *
 hipError_t launch_combine(const uint16_t *S, const float *ssq, const int32_t *pos, const float *w, int64_t T,
                           int64_t L, int nparts, float eps, int k, int ot, uint16_t *m, hipStream_t s);
 
+// dst = src, 16 bytes per lane per access (bytes: multiple of 16).
+hipError_t launch_copy16(const void *src, void *dst, int64_t bytes, hipStream_t s);
+
 hipError_t launch_router_f32(const float *x, const float *W, int64_t T, int n, int64_t d, float *logits,
                              hipStream_t s);
 hipError_t launch_expert1_f32(const float *x, const float *W1, const int32_t *perm_tok, const int32_t *offsets, int n,

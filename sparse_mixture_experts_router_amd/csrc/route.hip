@@ -387,8 +387,27 @@ __global__ void combine_f32_kernel(const float *__restrict__ S, const int32_t *_
 }
 
 // ---------------------------------------------------------------------------
+// Plain copy with 16-byte loads and stores: the reference point for HBM
+// counters and for the achievable copy bandwidth.
+// ---------------------------------------------------------------------------
+
+__global__ __launch_bounds__(256) void copy16_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst,
+                                                     int64_t n16) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
+}
+
+// ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+
+hipError_t launch_copy16(const void *src, void *dst, int64_t bytes, hipStream_t s) {
+    const int64_t n16 = bytes / 16;
+    if (n16 <= 0) return hipSuccess;
+    const int64_t blocks = (n16 + 255) / 256;
+    copy16_kernel<<<(unsigned)(blocks < 8192 ? blocks : 8192), 256, 0, s>>>((const uint4 *)src, (uint4 *)dst, n16);
+    return hipGetLastError();
+}
 
 static inline unsigned blocks_for(int64_t n, int b) { return (unsigned)((n + b - 1) / b); }
 
