@@ -72,6 +72,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-prefill", action="store_true")
+    ap.add_argument("--only-prefill", action="store_true", help="skip the decode workload (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
@@ -155,6 +156,14 @@ def main():
         for e in evs:
             e.close()
         return {"T": T, "ms": wall * 1e3 / steps, "stages": stages, "counts": counts.cpu().numpy(), "x": x_host}
+
+    if args.only_prefill:
+        p2 = synthetic.PRESETS["c2"]
+        r2 = run_workload(p2, args.prefill_steps, 2)
+        tf = layer_flops(p2)["total"] / (r2["ms"] * 1e-3) / 1e12
+        log("prefill T=%d: %.3f ms/step, %.1f TFLOP/s; stages %s" % (
+            p2.chunk_T, r2["ms"], tf, {k: round(v, 4) for k, v in r2["stages"].items()}))
+        return
 
     # ---- decode (headline) ----
     r = run_workload(p, args.steps, args.warmup)

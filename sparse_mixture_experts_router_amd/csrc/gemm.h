@@ -55,9 +55,8 @@ struct GemmArgs {
     float *y;              // EPI_RESID: optional y [rows][N]
 };
 
-constexpr int kTileBM = 128;
-constexpr int kTileBN = 128;      // B rows per tile (SWIGLU: 64 gate + 64 up -> 64 outputs)
-constexpr int kTileBK = 64;
+constexpr int kTileBM = 256;      // rows per tile of the large-tile kernel (and of its grouped lists)
+constexpr int kTileBN = 256;      // B rows per tile (SWIGLU: 128 gate + 128 up -> 128 outputs)
 constexpr int kSmallBM = 16;      // rows per tile of the streaming kernel's grouped lists
 
 // Kernel choice for a launch.

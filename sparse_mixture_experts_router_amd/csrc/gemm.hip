@@ -263,188 +263,306 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 }
 
 // ---------------------------------------------------------------------------
-// LDS-tiled kernel (many rows per expert: MFMA bound)
+// Large-tile kernel (many rows per expert; dense projections at large T)
 // ---------------------------------------------------------------------------
 //
-// Tile 128 (rows of A) x 128 (rows of B) x 64 (K), 256 threads as 2 x 2
-// waves of 64 x 64.  Each stage holds A and B as [128][64] bf16 with the
-// 16-byte chunk index XOR-swizzled by (row & 7), double-buffered; the next
-// stage is fetched into registers while the current one is multiplied.
-// EPI_SWIGLU tiles hold 64 gate rows then the 64 matching up rows, and each
-// wave's four column blocks are two gate blocks and their two up blocks.
+// Tile 256 (A rows) x 256 (B rows) x 32 (K) per stage, 256 threads as 2 x 2
+// waves of 128 x 128, so a wave reads 16 KiB of LDS per stage for 64 MFMAs
+// (64 FLOP per LDS byte).  Operands move global -> LDS with gfx950's
+// direct-to-LDS loads (global_load_lds): a wave instruction fills LDS in lane
+// order, so each lane fetches the global chunk that belongs at its LDS slot,
+// which realises the XOR swizzle.  Four stage buffers rotate with a prefetch
+// distance of three K-tiles (96 KiB in flight per CU, what the HBM latency
+// asks for): a stage's fragments are read into registers, then the loads of
+// the K-tile three ahead are issued, then the MFMAs run; each wave waits for
+// its own loads of the next K-tile and a barrier publishes it.  MXFP4 weights
+// are moved as codes and scales and dequantised per fragment.
+// The MFMA operands are swapped (B first), so a lane's four accumulator
+// elements are four consecutive output columns of one row: epilogue stores
+// are 8 or 16 bytes wide.  EPI_SWIGLU tiles hold 128 gate rows then the 128
+// matching up rows; wave column block c < 4 (gate) pairs with c + 4 (up).
+// Row blocks of 16 past the tile's valid rows skip their MFMAs; their A rows
+// are clamped to a valid row and their results are never stored.
 
-constexpr int kLdsTile = kTileBM * kTileBK;  // bf16 elements per operand stage
+constexpr int kBigBM = kTileBM, kBigBN = kTileBN, kBigBK = 32;
+static_assert(kBigBM == 256 && kBigBN == 256, "the wave layout below assumes 256x256 tiles");
+constexpr int kBigOpBytes = kBigBM * kBigBK * 2;      // one operand stage (A, or bf16 B): 16 KiB
+constexpr int kBigMxCodeBytes = kBigBN * kBigBK / 2;  // MXFP4 B codes per stage: 4 KiB
+constexpr int kBigStageBytes = 2 * kBigOpBytes;       // 32 KiB; 4 stages = 128 KiB
 
-__device__ __forceinline__ int swz(int row, int chunk) { return row * kTileBK + ((chunk ^ (row & 7)) << 3); }
+__shared__ __attribute__((aligned(16))) uint8_t big_lds0[kBigStageBytes];
+__shared__ __attribute__((aligned(16))) uint8_t big_lds1[kBigStageBytes];
+__shared__ __attribute__((aligned(16))) uint8_t big_lds2[kBigStageBytes];
+__shared__ __attribute__((aligned(16))) uint8_t big_lds3[kBigStageBytes];
+
+// Separate LDS objects per stage let the compiler see that a read of one
+// stage does not depend on the loads still landing in the others.
+template <int ST>
+__device__ __forceinline__ uint8_t *big_buf() {
+    if constexpr (ST == 0) return big_lds0;
+    else if constexpr (ST == 1) return big_lds1;
+    else if constexpr (ST == 2) return big_lds2;
+    else return big_lds3;
+}
+
+#define MOE_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
+// 64-byte rows (32 x 16-bit): 16-byte chunk c of row r lives at chunk
+// c ^ ((r >> 1) & 3), so the 8 rows a ds_read_b128 serves at once hit 8
+// distinct 16-byte bank groups.
+__device__ __forceinline__ int bswz(int row, int chunk) {
+    return row * (kBigBK * 2) + ((chunk ^ ((row >> 1) & 3)) << 4);
+}
+
+struct BigCtx {
+    const uint16_t *A;      // activation base
+    uint32_t aoff[4];       // element offset of this lane's 4 A rows (+ its chunk)
+    const uint8_t *B;       // bf16: this lane's first B row (+ chunk); MXFP4: its code row
+    int64_t bstep;          // bf16: elements between this lane's B rows (16 rows)
+    const uint8_t *bsc;     // MXFP4: scale row of this lane
+    int64_t K;
+};
+
+// Direct-to-LDS loads of K-tile kt into stage buffer ST.  A wave instruction
+// fills 1 KiB of LDS in lane order (16 bytes per lane for dwordx4, 4 per lane
+// for dword): 16 rows x 4 chunks of A or bf16 B, 64 rows x 16 bytes of MXFP4
+// codes, or 64 rows' scale words.
+template <int ST, bool MX>
+__device__ __forceinline__ void big_issue(const BigCtx &c, int kt, int wave) {
+    uint8_t *buf = big_buf<ST>();
+    const int64_t k0 = (int64_t)kt * kBigBK;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+        __builtin_amdgcn_global_load_lds(c.A + c.aoff[i] + k0, MOE_LDS(buf + (wave * 4 + i) * 1024), 16, 0, 0);
+    uint8_t *bb = buf + kBigOpBytes;
+    if constexpr (MX) {
+        __builtin_amdgcn_global_load_lds(c.B + k0 / 2, MOE_LDS(bb + wave * 1024), 16, 0, 0);
+        // the 4-byte-aligned word holding this stage's scale byte of the lane's row
+        __builtin_amdgcn_global_load_lds(c.bsc + ((k0 / 32) & ~(int64_t)3),
+                                         MOE_LDS(bb + kBigMxCodeBytes + wave * 256), 4, 0, 0);
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+            __builtin_amdgcn_global_load_lds((const uint16_t *)c.B + i * c.bstep + k0,
+                                             MOE_LDS(bb + (wave * 4 + i) * 1024), 16, 0, 0);
+    }
+}
+
+// Fragments of one stage: A rows wm*128 + 16m + li, B rows bcol[c] + li, chunk lg.
+template <int ST, bool MX, int AT>
+__device__ __forceinline__ void big_read(uint4 (&fa)[8], uint4 (&fb)[8], const int (&bcol)[8], int wm, int li, int lg,
+                                         int mlive, int kt) {
+    const uint8_t *buf = big_buf<ST>();
+    const uint8_t *bb = buf + kBigOpBytes;
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+        if (m < mlive) fa[m] = *(const uint4 *)(buf + bswz(wm * 128 + m * 16 + li, lg));
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        const int r = bcol[c] + li;
+        if constexpr (MX) {
+            const uint32_t codes = *(const uint32_t *)(bb + r * 16 + lg * 4);
+            const uint32_t sc = bb[kBigMxCodeBytes + r * 4 + (kt & 3)];
+            fb[c] = mxfp4x8_to_act<AT>(codes, sc);
+        } else {
+            fb[c] = weight_bf16_as<AT>(*(const uint4 *)(bb + bswz(r, lg)));
+        }
+    }
+}
+
+template <int AT>
+__device__ __forceinline__ void big_mma(floatx4_t (&acc)[8][8], const uint4 (&fa)[8], const uint4 (&fb)[8], int mlive) {
+#pragma unroll
+    for (int m = 0; m < 8; ++m)
+        if (m < mlive) {
+#pragma unroll
+            for (int c = 0; c < 8; ++c) acc[m][c] = mfma16x16x32<AT>(fb[c], fa[m], acc[m][c]);
+        }
+}
+
+// Load instructions per wave per stage, and the vmcnt waits that leave 2, 1
+// or 0 later stages in flight.
+template <bool MX> struct BigWait;
+template <> struct BigWait<false> {
+    static __device__ __forceinline__ void keep2() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
+    static __device__ __forceinline__ void keep1() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
+};
+template <> struct BigWait<true> {
+    static __device__ __forceinline__ void keep2() { asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); }
+    static __device__ __forceinline__ void keep1() { asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); }
+};
+
+// One K step on stage ST: read its fragments, prefetch K-tile kt+3 into the
+// stage three ahead, multiply, then wait until K-tile kt+1 has landed (the
+// two later ones may stay in flight) and publish it.
+template <int ST, bool MX, int AT>
+__device__ __forceinline__ void big_step(const BigCtx &c, floatx4_t (&acc)[8][8], const int (&bcol)[8], int kt,
+                                         int nk, int wave, int wm, int li, int lg, int mlive) {
+    uint4 fa[8], fb[8];
+    big_read<ST, MX, AT>(fa, fb, bcol, wm, li, lg, mlive, kt);
+    asm volatile("" ::: "memory");  // keep the LDS reads ahead of the next loads
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 3 < nk) big_issue<(ST + 3) & 3, MX>(c, kt + 3, wave);
+    __builtin_amdgcn_sched_barrier(0);
+    big_mma<AT>(acc, fa, fb, mlive);
+    __builtin_amdgcn_sched_barrier(0);
+    if (kt + 3 < nk) BigWait<MX>::keep2();
+    else if (kt + 2 < nk) BigWait<MX>::keep1();
+    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+}
 
 template <int EPI, bool MX, bool GROUPED, int AT, int OT>
-__global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs a) {
-    __shared__ __attribute__((aligned(16))) uint16_t lds[2][2][kLdsTile];  // [stage][A/B]
-
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_big_kernel(GemmArgs a) {
     const int tid = threadIdx.x;
-    const int lane = tid & 63;
-    const int wave = tid >> 6;
+    const int lane = tid & 63, wave = tid >> 6;
     const int wm = wave >> 1, wn = wave & 1;
     const int li = lane & 15, lg = lane >> 4;
 
     const int64_t K = a.K;
-    const int64_t nblocks = (EPI == EPI_SWIGLU) ? a.N / 64 : a.N / kTileBN;
-    const int ntiles = GROUPED ? *a.ntiles : (int)((a.M + kTileBM - 1) / kTileBM);
+    const int64_t nblocks = (EPI == EPI_SWIGLU) ? a.N / (kBigBN / 2) : a.N / kBigBN;
+    const int ntiles = GROUPED ? *a.ntiles : (int)((a.M + kBigBM - 1) / kBigBM);
     const int64_t items = (int64_t)ntiles * nblocks;
-    const int nk = (int)(K / kTileBK);
+    const int nk = (int)(K / kBigBK);  // a multiple of 8
+    // Direct-load lane mapping of 64-byte rows: lane l fills row 16q + (l >> 2),
+    // physical chunk l & 3, i.e. logical chunk (l & 3) ^ ((l >> 3) & 3).
+    const int drow = lane >> 2, dchunk = (lane & 3) ^ ((lane >> 3) & 3);
 
-    // Global->LDS assignment: bf16 operands: thread loads rows (tid>>3) + 32r, chunk tid&7.
-    const int lrow = tid >> 3, lchunk = tid & 7;
-    // MXFP4 B: thread handles row tid>>1, 32-element half (tid&1).
-    const int mrow = tid >> 1, mhalf = tid & 1;
+    int bcol[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+        if constexpr (EPI == EPI_SWIGLU)
+            bcol[c] = (c < 4) ? wn * 64 + c * 16 : 128 + wn * 64 + (c - 4) * 16;
+        else
+            bcol[c] = wn * 128 + c * 16;
+    }
 
     for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
-        const int t = (int)(item % ntiles);
-        const int64_t nb = item / ntiles;
+        // Tile-major order: the column blocks of one row tile run side by side
+        // (its A rows stay in L2) and so do the row tiles of one expert.
+        const int t = (int)(item / nblocks);
+        const int64_t nb = item - (int64_t)t * nblocks;
         RowTile rt;
-        load_tile(a, GROUPED, kTileBM, t, rt);
+        load_tile(a, GROUPED, kBigBM, t, rt);
         const int64_t brow0 = GROUPED ? (int64_t)rt.e * a.b_group_rows : 0;
 
-        // A source rows for this thread's 4 load slots.
-        const uint16_t *asrc[4];
+        BigCtx c;
+        c.A = a.A;
+        c.K = K;
 #pragma unroll
-        for (int r = 0; r < 4; ++r) {
-            int row = lrow + 32 * r;
-            if (row < rt.mcount) {
-                int64_t p = rt.p0 + row;
-                int64_t arow = a.a_gather ? (int64_t)a.a_gather[p] : p;
-                asrc[r] = a.A + arow * a.lda + lchunk * 8;
-            } else {
-                asrc[r] = nullptr;
-            }
+        for (int i = 0; i < 4; ++i) {
+            const int row = min(wave * 64 + i * 16 + drow, rt.mcount - 1);
+            const int64_t p = rt.p0 + row;
+            const int64_t arow = a.a_gather ? (int64_t)a.a_gather[p] : p;
+            c.aoff[i] = (uint32_t)(arow * a.lda + dchunk * 8);
         }
-        // B source rows.
+        // This lane's B rows: tile rows 64*wave + 16i + drow (bf16) or
+        // 64*wave + lane (MXFP4); SWIGLU waves 0-1 load gate rows, waves 2-3
+        // the matching up rows.
         auto brow_of = [&](int row) -> int64_t {
             if constexpr (EPI == EPI_SWIGLU)
-                return brow0 + (row < 64 ? nb * 64 + row : a.N + nb * 64 + (row - 64));
+                return brow0 + (row < 128 ? nb * 128 + row : a.N + nb * 128 + (row - 128));
             else
-                return brow0 + nb * kTileBN + row;
+                return brow0 + nb * kBigBN + row;
         };
-        const uint16_t *bsrc[4];
-        const uint8_t *bcode = nullptr, *bsc = nullptr;
         if constexpr (MX) {
-            int64_t r = brow_of(mrow);
-            bcode = (const uint8_t *)a.B + r * (K / 2) + mhalf * 16;
-            bsc = (const uint8_t *)a.B + a.b_rows_total * (K / 2) + r * (K / 32) + mhalf;
+            const int64_t r = brow_of(wave * 64 + lane);
+            c.B = (const uint8_t *)a.B + r * (K / 2);
+            c.bstep = 0;
+            c.bsc = (const uint8_t *)a.B + a.b_rows_total * (K / 2) + r * (K / 32);
         } else {
+            const int64_t r = brow_of(wave * 64 + drow);
+            c.B = (const uint8_t *)((const uint16_t *)a.B + r * K + dchunk * 8);
+            c.bstep = 16 * K;
+            c.bsc = nullptr;
+        }
+        const int mlive = min(8, max(0, (rt.mcount - wm * 128 + 15) / 16));  // live 16-row blocks of this wave
+
+        floatx4_t acc[8][8];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) bsrc[r] = (const uint16_t *)a.B + brow_of(lrow + 32 * r) * K + lchunk * 8;
+        for (int m = 0; m < 8; ++m)
+#pragma unroll
+            for (int cc = 0; cc < 8; ++cc) acc[m][cc] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+        big_issue<0, MX>(c, 0, wave);
+        big_issue<1, MX>(c, 1, wave);
+        big_issue<2, MX>(c, 2, wave);
+        BigWait<MX>::keep2();
+        __builtin_amdgcn_s_barrier();
+        for (int kt = 0; kt < nk; kt += 8) {
+            big_step<0, MX, AT>(c, acc, bcol, kt + 0, nk, wave, wm, li, lg, mlive);
+            big_step<1, MX, AT>(c, acc, bcol, kt + 1, nk, wave, wm, li, lg, mlive);
+            big_step<2, MX, AT>(c, acc, bcol, kt + 2, nk, wave, wm, li, lg, mlive);
+            big_step<3, MX, AT>(c, acc, bcol, kt + 3, nk, wave, wm, li, lg, mlive);
+            big_step<0, MX, AT>(c, acc, bcol, kt + 4, nk, wave, wm, li, lg, mlive);
+            big_step<1, MX, AT>(c, acc, bcol, kt + 5, nk, wave, wm, li, lg, mlive);
+            big_step<2, MX, AT>(c, acc, bcol, kt + 6, nk, wave, wm, li, lg, mlive);
+            big_step<3, MX, AT>(c, acc, bcol, kt + 7, nk, wave, wm, li, lg, mlive);
         }
 
-        uint4 ra[4], rb[4];
-        auto gload = [&](int kt) {
-            int64_t k0 = (int64_t)kt * kTileBK;
+        // Epilogue: lane (li, lg) holds row wm*128 + 16m + li, columns
+        // bcol[c] + 4lg + q (q = 0..3) of every block.
 #pragma unroll
-            for (int r = 0; r < 4; ++r) ra[r] = asrc[r] ? *(const uint4 *)(asrc[r] + k0) : make_uint4(0, 0, 0, 0);
-            if constexpr (MX) {
-                uint4 codes = *(const uint4 *)(bcode + k0 / 2);
-                uint32_t sc = bsc[k0 / 32];
-                rb[0] = mxfp4x8_to_act<AT>(codes.x, sc);
-                rb[1] = mxfp4x8_to_act<AT>(codes.y, sc);
-                rb[2] = mxfp4x8_to_act<AT>(codes.z, sc);
-                rb[3] = mxfp4x8_to_act<AT>(codes.w, sc);
-            } else {
+        for (int m = 0; m < 8; ++m) {
+            const int row = wm * 128 + m * 16 + li;
+            const bool ok = row < rt.mcount;
+            const int64_t p = rt.p0 + row;
+            if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) rb[r] = *(const uint4 *)(bsrc[r] + k0);
-            }
-        };
-        auto lstore = [&](int st) {
-            uint16_t *la = lds[st][0], *lb = lds[st][1];
+                for (int cc = 0; cc < 4; ++cc) {
+                    if (ok) {
+                        uint16_t h[4];
 #pragma unroll
-            for (int r = 0; r < 4; ++r) *(uint4 *)(la + swz(lrow + 32 * r, lchunk)) = ra[r];
-            if constexpr (MX) {
-#pragma unroll
-                for (int c = 0; c < 4; ++c) *(uint4 *)(lb + swz(mrow, mhalf * 4 + c)) = rb[c];
-            } else {
-#pragma unroll
-                for (int r = 0; r < 4; ++r) *(uint4 *)(lb + swz(lrow + 32 * r, lchunk)) = rb[r];
-            }
-        };
-
-        // Wave's B-tile rows of its 4 column blocks.
-        int bcol[4];
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-            if constexpr (EPI == EPI_SWIGLU)
-                bcol[c] = (c < 2) ? wn * 32 + c * 16 : 64 + wn * 32 + (c - 2) * 16;
-            else
-                bcol[c] = wn * 64 + c * 16;
-        }
-
-        floatx4_t acc[4][4];
-#pragma unroll
-        for (int m = 0; m < 4; ++m)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) acc[m][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-
-        gload(0);
-        if constexpr (!MX && AT == ACT_F16) {
-#pragma unroll
-            for (int r = 0; r < 4; ++r) rb[r] = bf16x8_to_f16x8(rb[r]);
-        }
-        lstore(0);
-        __syncthreads();
-        for (int kt = 0; kt < nk; ++kt) {
-            const int st = kt & 1;
-            if (kt + 1 < nk) gload(kt + 1);
-            const uint16_t *la = lds[st][0], *lb = lds[st][1];
-#pragma unroll
-            for (int s = 0; s < 2; ++s) {
-                uint4 fa[4], fb[4];
-#pragma unroll
-                for (int m = 0; m < 4; ++m) fa[m] = *(const uint4 *)(la + swz(wm * 64 + m * 16 + li, s * 4 + lg));
-#pragma unroll
-                for (int c = 0; c < 4; ++c) fb[c] = *(const uint4 *)(lb + swz(bcol[c] + li, s * 4 + lg));
-#pragma unroll
-                for (int m = 0; m < 4; ++m)
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) acc[m][c] = mfma16x16x32<AT>(fa[m], fb[c], acc[m][c]);
-            }
-            if (kt + 1 < nk) {
-                if constexpr (!MX && AT == ACT_F16) {
-#pragma unroll
-                    for (int r = 0; r < 4; ++r) rb[r] = bf16x8_to_f16x8(rb[r]);
+                        for (int q = 0; q < 4; ++q) h[q] = f32_to_act<OT>(silu(acc[m][cc][q]) * acc[m][cc + 4][q]);
+                        const int64_t j = nb * 128 + wn * 64 + cc * 16 + lg * 4;
+                        *(uint2 *)((uint16_t *)a.C + p * a.ldc + j) =
+                            make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+                    }
                 }
-                lstore(st ^ 1);
-            }
-            __syncthreads();
-        }
-
-        // Epilogue.  EPI_NORM partial sums are per 16-column block, the same
-        // layout the streaming kernel writes (nparts = N / 16 per row).
+            } else {
 #pragma unroll
-        for (int m = 0; m < 4; ++m)
+                for (int cc = 0; cc < 8; ++cc) {
+                    const int64_t n = nb * kBigBN + wn * 128 + cc * 16 + lg * 4;
+                    const floatx4_t v = acc[m][cc];
+                    if constexpr (EPI == EPI_F32) {
+                        if (ok) *(floatx4_t *)((float *)a.C + p * a.ldc + n) = v;
+                    } else if constexpr (EPI == EPI_ACT) {
+                        if (ok)
+                            *(uint2 *)((uint16_t *)a.C + p * a.ldc + n) =
+                                make_uint2(f32_to_act<OT>(v[0]) | ((uint32_t)f32_to_act<OT>(v[1]) << 16),
+                                           f32_to_act<OT>(v[2]) | ((uint32_t)f32_to_act<OT>(v[3]) << 16));
+                    } else if constexpr (EPI == EPI_NORM) {
+                        uint16_t h[4];
+                        float sq = 0.f;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                int row = wm * 64 + m * 16 + lg * 4 + q;
-                bool ok = row < rt.mcount;
-                int64_t p = rt.p0 + row;
-                if constexpr (EPI == EPI_SWIGLU) {
-#pragma unroll
-                    for (int c = 0; c < 2; ++c) {
+                        for (int q = 0; q < 4; ++q) {
+                            const float gsc = a.gamma ? 1.0f + a.gamma[n + q] : 1.0f;
+                            h[q] = f32_to_bf16(gsc * v[q]);
+                            const float e = a.norm_round ? bf16_to_f32(h[q]) : v[q];
+                            sq += e * e;
+                        }
+                        if (ok)
+                            *(uint2 *)((uint16_t *)a.C + p * a.ldc + n) =
+                                make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+                        sq += __shfl_xor(sq, 16, 64);
+                        sq += __shfl_xor(sq, 32, 64);
+                        if (ok && lg == 0) a.ssq[p * a.nparts + nb * 16 + wn * 8 + cc] = sq;
+                    } else {  // EPI_RESID
                         if (ok) {
-                            float g = acc[m][c][q], u = acc[m][c + 2][q];
-                            int64_t j = nb * 64 + wn * 32 + c * 16 + li;
-                            ((uint16_t *)a.C)[p * a.ldc + j] = f32_to_act<OT>(silu(g) * u);
-                        }
-                    }
-                } else {
-#pragma unroll
-                    for (int c = 0; c < 4; ++c) {
-                        int64_t n = nb * kTileBN + wn * 64 + c * 16 + li;
-                        float sq = ok ? store_elem<EPI, OT>(a, p, n, acc[m][c][q]) : 0.f;
-                        if constexpr (EPI == EPI_NORM) {
-                            sq = sum16(sq);
-                            if (li == 0 && ok) a.ssq[p * a.nparts + nb * 8 + wn * 4 + c] = sq;
+                            const uint2 hx = *(const uint2 *)(a.resid + p * a.N + n);
+                            const float4 g = *(const float4 *)(a.gate + n);
+                            floatx4_t o;
+                            o[0] = bf16_to_f32((uint16_t)hx.x) + g.x * v[0];
+                            o[1] = bf16_to_f32((uint16_t)(hx.x >> 16)) + g.y * v[1];
+                            o[2] = bf16_to_f32((uint16_t)hx.y) + g.z * v[2];
+                            o[3] = bf16_to_f32((uint16_t)(hx.y >> 16)) + g.w * v[3];
+                            *(floatx4_t *)((float *)a.C + p * a.ldc + n) = o;
+                            if (a.y) *(floatx4_t *)(a.y + p * a.N + n) = v;
                         }
                     }
                 }
             }
+        }
     }
 }
 
@@ -453,7 +571,7 @@ __global__ __launch_bounds__(256) void gemm_tile_kernel(GemmArgs a) {
 // ---------------------------------------------------------------------------
 
 constexpr int kStreamGrid = 4096;  // persistent grid cap of the streaming kernel
-constexpr int kTileGrid = 512;     // persistent grid cap of the tiled kernel
+constexpr int kBigGrid = 256;      // persistent grid cap of the large-tile kernel (one per CU)
 
 template <int MB, int NB, int EPI, bool MX, bool GROUPED, int AT, int OT>
 static hipError_t run_stream(const GemmArgs &a, hipStream_t s) {
@@ -468,12 +586,12 @@ static hipError_t run_stream(const GemmArgs &a, hipStream_t s) {
 
 template <int EPI, bool MX, bool GROUPED, int AT, int OT>
 static hipError_t run_tile(const GemmArgs &a, hipStream_t s) {
-    const int64_t nblocks = (EPI == EPI_SWIGLU) ? a.N / 64 : a.N / kTileBN;
-    const int64_t tiles = GROUPED ? a.max_tiles : (a.M + kTileBM - 1) / kTileBM;
+    const int64_t nblocks = (EPI == EPI_SWIGLU) ? a.N / (kBigBN / 2) : a.N / kBigBN;
+    const int64_t tiles = GROUPED ? a.max_tiles : (a.M + kBigBM - 1) / kBigBM;
     const int64_t items = tiles * nblocks;
     if (items <= 0) return hipSuccess;
-    const int grid = (int)(items < kTileGrid ? items : kTileGrid);
-    gemm_tile_kernel<EPI, MX, GROUPED, AT, OT><<<grid, 256, 0, s>>>(a);
+    const int grid = (int)(items < kBigGrid ? items : kBigGrid);
+    gemm_big_kernel<EPI, MX, GROUPED, AT, OT><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
 }
 
