@@ -25,6 +25,12 @@ COMMON = ["--offload-arch=" + ARCH, "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wno
           "-I", os.path.join(os.path.dirname(HERE), "include")]
 
 
+# Extra hipcc flags per source file.
+PER_FILE = {
+    "gemm.hip": os.environ.get("MOE_GEMM_FLAGS", "-mllvm -amdgpu-sched-strategy=iterative-minreg").split(),
+}
+
+
 def sources():
     return sorted(glob.glob(os.path.join(CSRC, "*.hip")))
 
@@ -36,7 +42,7 @@ def headers():
 
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC] + COMMON + ["-c", src, "-o", obj]
+    cmd = [HIPCC] + COMMON + PER_FILE.get(os.path.basename(src), []) + ["-c", src, "-o", obj]
     r = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in r.stdout.splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:

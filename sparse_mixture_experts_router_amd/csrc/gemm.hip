@@ -271,24 +271,31 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 // (64 FLOP per LDS byte).  Operands move global -> LDS with gfx950's
 // direct-to-LDS loads (global_load_lds): a wave instruction fills LDS in lane
 // order, so each lane fetches the global chunk that belongs at its LDS slot,
-// which realises the XOR swizzle.  Four stage buffers rotate with a prefetch
-// distance of three K-tiles (96 KiB in flight per CU, what the HBM latency
-// asks for): a stage's fragments are read into registers, then the loads of
-// the K-tile three ahead are issued, then the MFMAs run; each wave waits for
-// its own loads of the next K-tile and a barrier publishes it.  MXFP4 weights
-// are moved as codes and scales and dequantised per fragment.
+// which realises the XOR swizzle.  Four stage buffers rotate; the loads of
+// K-tile kt+4 are issued at step kt, so three K-tiles (96 KiB per CU) are in
+// flight while the MFMAs of one run.  Fragments are double-buffered in
+// registers: the MFMAs on K-tile kt overlap the LDS reads of kt+1.
+// When the MFMA type differs from the stored weights (bf16 weights with fp16
+// activations, or MXFP4), each wave converts the share of the B stage that
+// its own loads brought in, in LDS, two K-tiles ahead (bf16 -> fp16 in place;
+// MXFP4 codes and block scales -> the activation type into the B operand
+// area), so the MFMA operands always come straight from LDS reads.
 // The MFMA operands are swapped (B first), so a lane's four accumulator
 // elements are four consecutive output columns of one row: epilogue stores
 // are 8 or 16 bytes wide.  EPI_SWIGLU tiles hold 128 gate rows then the 128
 // matching up rows; wave column block c < 4 (gate) pairs with c + 4 (up).
-// Row blocks of 16 past the tile's valid rows skip their MFMAs; their A rows
-// are clamped to a valid row and their results are never stored.
+// Rows past the tile's valid rows load a clamped valid A row; their results
+// are never stored.  The half-height variant (HM) serves grouped tiles of at
+// most 128 rows (an expert's remainder): its four waves share the 128 A rows
+// and each takes 64 of the 256 B rows, so no wave idles on empty rows.
 
 constexpr int kBigBM = kTileBM, kBigBN = kTileBN, kBigBK = 32;
 static_assert(kBigBM == 256 && kBigBN == 256, "the wave layout below assumes 256x256 tiles");
-constexpr int kBigOpBytes = kBigBM * kBigBK * 2;      // one operand stage (A, or bf16 B): 16 KiB
+constexpr int kBigOpBytes = kBigBM * kBigBK * 2;      // one operand area (A, or B in the MFMA type): 16 KiB
 constexpr int kBigMxCodeBytes = kBigBN * kBigBK / 2;  // MXFP4 B codes per stage: 4 KiB
-constexpr int kBigStageBytes = 2 * kBigOpBytes;       // 32 KiB; 4 stages = 128 KiB
+constexpr int kBigMxCodeOff = 2 * kBigOpBytes;        // MXFP4 codes, then 1 KiB of scale words
+constexpr int kBigMxScaleOff = kBigMxCodeOff + kBigMxCodeBytes;
+constexpr int kBigStageBytes = kBigMxScaleOff + kBigBN * 4;  // 37 KiB; 4 stages = 148 KiB
 
 __shared__ __attribute__((aligned(16))) uint8_t big_lds0[kBigStageBytes];
 __shared__ __attribute__((aligned(16))) uint8_t big_lds1[kBigStageBytes];
@@ -314,127 +321,172 @@ __device__ __forceinline__ int bswz(int row, int chunk) {
     return row * (kBigBK * 2) + ((chunk ^ ((row >> 1) & 3)) << 4);
 }
 
+// Load addresses: a wave-uniform base plus a 32-bit byte offset per lane, so
+// the loads take the scalar-base form and the per-lane state stays small.
 struct BigCtx {
-    const uint16_t *A;      // activation base
-    uint32_t aoff[4];       // element offset of this lane's 4 A rows (+ its chunk)
-    const uint8_t *B;       // bf16: this lane's first B row (+ chunk); MXFP4: its code row
-    int64_t bstep;          // bf16: elements between this lane's B rows (16 rows)
-    const uint8_t *bsc;     // MXFP4: scale row of this lane
-    int64_t K;
+    const uint8_t *A;       // activation base (uniform)
+    uint32_t aoff[4];       // byte offsets of this lane's 4 A chunks at k = 0
+    const uint8_t *B;       // first B row of the tile (bf16) or its code row (MXFP4) (uniform)
+    uint32_t boff[4];       // bf16: byte offsets of this lane's 4 B chunks; MXFP4: [0] codes, [1] scales
+    const uint8_t *bsc;     // MXFP4: scale base of the tile (uniform)
 };
 
 // Direct-to-LDS loads of K-tile kt into stage buffer ST.  A wave instruction
 // fills 1 KiB of LDS in lane order (16 bytes per lane for dwordx4, 4 per lane
 // for dword): 16 rows x 4 chunks of A or bf16 B, 64 rows x 16 bytes of MXFP4
 // codes, or 64 rows' scale words.
-template <int ST, bool MX>
+template <int ST, bool MX, int HM>
 __device__ __forceinline__ void big_issue(const BigCtx &c, int kt, int wave) {
+    constexpr int NA = HM ? 2 : 4;  // A loads per wave (16 rows each)
     uint8_t *buf = big_buf<ST>();
-    const int64_t k0 = (int64_t)kt * kBigBK;
+    const uint8_t *Ak = c.A + (int64_t)kt * (kBigBK * 2);
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-        __builtin_amdgcn_global_load_lds(c.A + c.aoff[i] + k0, MOE_LDS(buf + (wave * 4 + i) * 1024), 16, 0, 0);
-    uint8_t *bb = buf + kBigOpBytes;
+    for (int i = 0; i < NA; ++i)
+        __builtin_amdgcn_global_load_lds(Ak + c.aoff[i], MOE_LDS(buf + (wave * NA + i) * 1024), 16, 0, 0);
     if constexpr (MX) {
-        __builtin_amdgcn_global_load_lds(c.B + k0 / 2, MOE_LDS(bb + wave * 1024), 16, 0, 0);
-        // the 4-byte-aligned word holding this stage's scale byte of the lane's row
-        __builtin_amdgcn_global_load_lds(c.bsc + ((k0 / 32) & ~(int64_t)3),
-                                         MOE_LDS(bb + kBigMxCodeBytes + wave * 256), 4, 0, 0);
+        __builtin_amdgcn_global_load_lds(c.B + (int64_t)kt * (kBigBK / 2) + c.boff[0],
+                                         MOE_LDS(buf + kBigMxCodeOff + wave * 1024), 16, 0, 0);
+        // the 4-byte-aligned word holding this K-tile's scale byte of the lane's row
+        __builtin_amdgcn_global_load_lds(c.bsc + (int64_t)(kt & ~3) + c.boff[1],
+                                         MOE_LDS(buf + kBigMxScaleOff + wave * 256), 4, 0, 0);
     } else {
+        uint8_t *bb = buf + kBigOpBytes;
+        const uint8_t *Bk = c.B + (int64_t)kt * (kBigBK * 2);
 #pragma unroll
         for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds((const uint16_t *)c.B + i * c.bstep + k0,
-                                             MOE_LDS(bb + (wave * 4 + i) * 1024), 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(Bk + c.boff[i], MOE_LDS(bb + (wave * 4 + i) * 1024), 16, 0, 0);
+    }
+}
+
+template <bool MX, int AT> constexpr bool kBigConvert = MX || AT == ACT_F16;
+
+// Convert the B data that this wave's own loads put into stage ST (K-tile kt)
+// into the MFMA type: bf16 -> fp16 in place (the lane's own four chunks), or
+// the 32 MXFP4 codes of row 64*wave + lane times its block scale -> four
+// swizzled chunks of the B operand area.
+template <int ST, bool MX, int AT>
+__device__ __forceinline__ void big_convert(int kt, int wave, int lane) {
+    uint8_t *buf = big_buf<ST>();
+    uint8_t *bb = buf + kBigOpBytes;
+    if constexpr (MX) {
+        const int r = wave * 64 + lane;
+        const uint4 codes = *(const uint4 *)(buf + kBigMxCodeOff + r * 16);
+        const uint32_t sc = buf[kBigMxScaleOff + r * 4 + (kt & 3)];
+        *(uint4 *)(bb + bswz(r, 0)) = mxfp4x8_to_act<AT>(codes.x, sc);
+        *(uint4 *)(bb + bswz(r, 1)) = mxfp4x8_to_act<AT>(codes.y, sc);
+        *(uint4 *)(bb + bswz(r, 2)) = mxfp4x8_to_act<AT>(codes.z, sc);
+        *(uint4 *)(bb + bswz(r, 3)) = mxfp4x8_to_act<AT>(codes.w, sc);
+    } else {
+        uint4 v[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) v[i] = *(const uint4 *)(bb + (wave * 4 + i) * 1024 + lane * 16);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) *(uint4 *)(bb + (wave * 4 + i) * 1024 + lane * 16) = bf16x8_to_f16x8(v[i]);
     }
 }
 
 // Fragments of one stage: A rows wm*128 + 16m + li, B rows bcol[c] + li, chunk lg.
-template <int ST, bool MX, int AT>
-__device__ __forceinline__ void big_read(uint4 (&fa)[8], uint4 (&fb)[8], const int (&bcol)[8], int wm, int li, int lg,
-                                         int mlive, int kt) {
+template <int ST, int NBK>
+__device__ __forceinline__ void big_read(uint4 (&fa)[8], uint4 (&fb)[NBK], const int (&bcol)[NBK], int wm, int li,
+                                         int lg) {
     const uint8_t *buf = big_buf<ST>();
     const uint8_t *bb = buf + kBigOpBytes;
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
-        if (m < mlive) fa[m] = *(const uint4 *)(buf + bswz(wm * 128 + m * 16 + li, lg));
+    for (int c = 0; c < NBK; ++c) fb[c] = *(const uint4 *)(bb + bswz(bcol[c] + li, lg));
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
-        const int r = bcol[c] + li;
-        if constexpr (MX) {
-            const uint32_t codes = *(const uint32_t *)(bb + r * 16 + lg * 4);
-            const uint32_t sc = bb[kBigMxCodeBytes + r * 4 + (kt & 3)];
-            fb[c] = mxfp4x8_to_act<AT>(codes, sc);
-        } else {
-            fb[c] = weight_bf16_as<AT>(*(const uint4 *)(bb + bswz(r, lg)));
-        }
-    }
+    for (int m = 0; m < 8; ++m) fa[m] = *(const uint4 *)(buf + bswz(wm * 128 + m * 16 + li, lg));
 }
 
-template <int AT>
-__device__ __forceinline__ void big_mma(floatx4_t (&acc)[8][8], const uint4 (&fa)[8], const uint4 (&fb)[8], int mlive) {
+template <int AT, int NBK>
+__device__ __forceinline__ void big_mma(floatx4_t (&acc)[8][NBK], const uint4 (&fa)[8], const uint4 (&fb)[NBK]) {
 #pragma unroll
     for (int m = 0; m < 8; ++m)
-        if (m < mlive) {
 #pragma unroll
-            for (int c = 0; c < 8; ++c) acc[m][c] = mfma16x16x32<AT>(fb[c], fa[m], acc[m][c]);
-        }
+        for (int c = 0; c < NBK; ++c) acc[m][c] = mfma16x16x32<AT>(fb[c], fa[m], acc[m][c]);
 }
 
-// Load instructions per wave per stage, and the vmcnt waits that leave 2, 1
-// or 0 later stages in flight.
-template <bool MX> struct BigWait;
-template <> struct BigWait<false> {
-    static __device__ __forceinline__ void keep2() { asm volatile("s_waitcnt vmcnt(16)" ::: "memory"); }
-    static __device__ __forceinline__ void keep1() { asm volatile("s_waitcnt vmcnt(8)" ::: "memory"); }
-};
-template <> struct BigWait<true> {
-    static __device__ __forceinline__ void keep2() { asm volatile("s_waitcnt vmcnt(12)" ::: "memory"); }
-    static __device__ __forceinline__ void keep1() { asm volatile("s_waitcnt vmcnt(6)" ::: "memory"); }
+// Load instructions per wave per stage, and the vmcnt waits that leave 3 or
+// 2 later stages in flight.  The waits go through the s_waitcnt builtin (not
+// inline asm) so the compiler's own wait insertion knows of them.  gfx9
+// s_waitcnt fields: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+template <bool MX, int HM> struct BigWait {
+    static constexpr int kPerStage = (HM ? 2 : 4) + (MX ? 2 : 4);
+    static __device__ __forceinline__ void keep3() { __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * kPerStage)); }
+    static __device__ __forceinline__ void keep2() { __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kPerStage)); }
+    static __device__ __forceinline__ void all() { __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); }
 };
 
-// One K step on stage ST: read its fragments, prefetch K-tile kt+3 into the
-// stage three ahead, multiply, then wait until K-tile kt+1 has landed (the
-// two later ones may stay in flight) and publish it.
-template <int ST, bool MX, int AT>
-__device__ __forceinline__ void big_step(const BigCtx &c, floatx4_t (&acc)[8][8], const int (&bcol)[8], int kt,
-                                         int nk, int wave, int wm, int li, int lg, int mlive) {
-    uint4 fa[8], fb[8];
-    big_read<ST, MX, AT>(fa, fb, bcol, wm, li, lg, mlive, kt);
-    asm volatile("" ::: "memory");  // keep the LDS reads ahead of the next loads
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 3 < nk) big_issue<(ST + 3) & 3, MX>(c, kt + 3, wave);
-    __builtin_amdgcn_sched_barrier(0);
-    big_mma<AT>(acc, fa, fb, mlive);
-    __builtin_amdgcn_sched_barrier(0);
-    if (kt + 3 < nk) BigWait<MX>::keep2();
-    else if (kt + 2 < nk) BigWait<MX>::keep1();
-    else asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-}
-
-template <int EPI, bool MX, bool GROUPED, int AT, int OT>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_big_kernel(GemmArgs a) {
-    const int tid = threadIdx.x;
-    const int lane = tid & 63, wave = tid >> 6;
-    const int wm = wave >> 1, wn = wave & 1;
+// One K step j of a group of eight, on K-tile kt (stage ST = kt & 3).  On
+// entry this wave holds the fragments of kt (cur) and has finished all its
+// LDS work on earlier steps.  The barrier then guarantees for every wave that
+// K-tile kt+1 is complete in its stage (landed, and converted where needed)
+// and that nobody still reads stage ST, which receives K-tile kt+4 (clamped
+// to the last K-tile near the end: those loads are never read).  The MFMAs on
+// cur overlap the reads of kt+1 into nxt, except in the group's last step:
+// fragments are not carried across the loop's back edge, which keeps the
+// accumulators in place in the register allocation.  With conversion, the
+// wave waits for its own loads of kt+2 and converts them halfway through the
+// MFMAs, so the next barrier publishes kt+2 ready for use.
+template <int J, bool MX, int AT, int HM, int NBK>
+__device__ __forceinline__ void big_step(const BigCtx &c, floatx4_t (&acc)[8][NBK], const uint4 (&cur_a)[8],
+                                         const uint4 (&cur_b)[NBK], uint4 (&nxt_a)[8], uint4 (&nxt_b)[NBK],
+                                         const int (&bcol)[NBK], int kt, int nk, int wave, int wm, int lane) {
+    constexpr int ST = J & 3;
     const int li = lane & 15, lg = lane >> 4;
+    if constexpr (!kBigConvert<MX, AT>) BigWait<MX, HM>::keep2();
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    big_issue<ST, MX, HM>(c, min(kt + 4, nk - 1), wave);
+    if constexpr (J < 7) big_read<(ST + 1) & 3, NBK>(nxt_a, nxt_b, bcol, wm, li, lg);
+    if constexpr (kBigConvert<MX, AT>) {
+        // first half of the MFMAs (rows 0-3), then the conversion, then the rest
+#pragma unroll
+        for (int m = 0; m < 4; ++m)
+#pragma unroll
+            for (int cc = 0; cc < NBK; ++cc) acc[m][cc] = mfma16x16x32<AT>(cur_b[cc], cur_a[m], acc[m][cc]);
+        __builtin_amdgcn_sched_barrier(0);
+        BigWait<MX, HM>::keep2();
+        big_convert<(ST + 2) & 3, MX, AT>(kt + 2, wave, lane);
+#pragma unroll
+        for (int m = 4; m < 8; ++m)
+#pragma unroll
+            for (int cc = 0; cc < NBK; ++cc) acc[m][cc] = mfma16x16x32<AT>(cur_b[cc], cur_a[m], acc[m][cc]);
+    } else {
+        big_mma<AT, NBK>(acc, cur_a, cur_b);
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+}
+
+template <int EPI, bool MX, bool GROUPED, int AT, int OT, int HM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_big_kernel(GemmArgs a) {
+    constexpr int NBK = HM ? 4 : 8;      // 16-column blocks per wave
+    constexpr int NA = HM ? 2 : 4;       // A loads per wave per stage
+    constexpr int BM = HM ? kHalfBM : kBigBM;
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = HM ? 0 : wave >> 1, wn = HM ? wave : wave & 1;
+    const int li = lane & 15, lg = lane >> 4;
+    constexpr int WCOLS = HM ? 64 : 128;  // output-space B rows per wave (SWIGLU: half gate, half up)
 
     const int64_t K = a.K;
     const int64_t nblocks = (EPI == EPI_SWIGLU) ? a.N / (kBigBN / 2) : a.N / kBigBN;
-    const int ntiles = GROUPED ? *a.ntiles : (int)((a.M + kBigBM - 1) / kBigBM);
+    const int ntiles = GROUPED ? *a.ntiles : (int)((a.M + BM - 1) / BM);
     const int64_t items = (int64_t)ntiles * nblocks;
     const int nk = (int)(K / kBigBK);  // a multiple of 8
     // Direct-load lane mapping of 64-byte rows: lane l fills row 16q + (l >> 2),
     // physical chunk l & 3, i.e. logical chunk (l & 3) ^ ((l >> 3) & 3).
     const int drow = lane >> 2, dchunk = (lane & 3) ^ ((lane >> 3) & 3);
 
-    int bcol[8];
+    int bcol[NBK];
 #pragma unroll
-    for (int c = 0; c < 8; ++c) {
+    for (int c = 0; c < NBK; ++c) {
         if constexpr (EPI == EPI_SWIGLU)
-            bcol[c] = (c < 4) ? wn * 64 + c * 16 : 128 + wn * 64 + (c - 4) * 16;
+            bcol[c] = (c < NBK / 2) ? wn * (WCOLS / 2) + c * 16 : 128 + wn * (WCOLS / 2) + (c - NBK / 2) * 16;
         else
-            bcol[c] = wn * 128 + c * 16;
+            bcol[c] = wn * WCOLS + c * 16;
     }
 
     for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
@@ -443,62 +495,74 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         const int t = (int)(item / nblocks);
         const int64_t nb = item - (int64_t)t * nblocks;
         RowTile rt;
-        load_tile(a, GROUPED, kBigBM, t, rt);
+        load_tile(a, GROUPED, BM, t, rt);
         const int64_t brow0 = GROUPED ? (int64_t)rt.e * a.b_group_rows : 0;
 
         BigCtx c;
-        c.A = a.A;
-        c.K = K;
+        c.A = (const uint8_t *)a.A;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int row = min(wave * 64 + i * 16 + drow, rt.mcount - 1);
+        for (int i = 0; i < NA; ++i) {
+            const int row = min(wave * (NA * 16) + i * 16 + drow, rt.mcount - 1);
             const int64_t p = rt.p0 + row;
             const int64_t arow = a.a_gather ? (int64_t)a.a_gather[p] : p;
-            c.aoff[i] = (uint32_t)(arow * a.lda + dchunk * 8);
+            c.aoff[i] = (uint32_t)((arow * a.lda + dchunk * 8) * 2);
         }
-        // This lane's B rows: tile rows 64*wave + 16i + drow (bf16) or
-        // 64*wave + lane (MXFP4); SWIGLU waves 0-1 load gate rows, waves 2-3
-        // the matching up rows.
-        auto brow_of = [&](int row) -> int64_t {
-            if constexpr (EPI == EPI_SWIGLU)
-                return brow0 + (row < 128 ? nb * 128 + row : a.N + nb * 128 + (row - 128));
-            else
-                return brow0 + nb * kBigBN + row;
-        };
+        // The tile's B rows 0..255: SWIGLU rows 0-127 are gate rows nb*128.., rows
+        // 128-255 the matching up rows N + nb*128..; a lane loads tile rows
+        // 64*wave + 16i + drow (bf16) or 64*wave + lane (MXFP4).
+        const int64_t bfirst = brow0 + ((EPI == EPI_SWIGLU) ? nb * 128 : nb * kBigBN);
+        const int64_t upskip = (EPI == EPI_SWIGLU) ? a.N - 128 : 0;  // rows 128.. sit this far further on
+        auto brel = [&](int row) -> int64_t { return row + (row >= 128 ? upskip : 0); };
         if constexpr (MX) {
-            const int64_t r = brow_of(wave * 64 + lane);
-            c.B = (const uint8_t *)a.B + r * (K / 2);
-            c.bstep = 0;
-            c.bsc = (const uint8_t *)a.B + a.b_rows_total * (K / 2) + r * (K / 32);
+            const int row = wave * 64 + lane;
+            c.B = (const uint8_t *)a.B + bfirst * (K / 2);
+            c.bsc = (const uint8_t *)a.B + a.b_rows_total * (K / 2) + bfirst * (K / 32);
+            c.boff[0] = (uint32_t)(brel(row) * (K / 2));
+            c.boff[1] = (uint32_t)(brel(row) * (K / 32));
+            c.boff[2] = c.boff[3] = 0;
         } else {
-            const int64_t r = brow_of(wave * 64 + drow);
-            c.B = (const uint8_t *)((const uint16_t *)a.B + r * K + dchunk * 8);
-            c.bstep = 16 * K;
+            c.B = (const uint8_t *)((const uint16_t *)a.B + bfirst * K);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) c.boff[i] = (uint32_t)((brel(wave * 64 + i * 16 + drow) * K + dchunk * 8) * 2);
             c.bsc = nullptr;
         }
-        const int mlive = min(8, max(0, (rt.mcount - wm * 128 + 15) / 16));  // live 16-row blocks of this wave
 
-        floatx4_t acc[8][8];
+        floatx4_t acc[8][NBK];
 #pragma unroll
         for (int m = 0; m < 8; ++m)
 #pragma unroll
-            for (int cc = 0; cc < 8; ++cc) acc[m][cc] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+            for (int cc = 0; cc < NBK; ++cc) acc[m][cc] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-        big_issue<0, MX>(c, 0, wave);
-        big_issue<1, MX>(c, 1, wave);
-        big_issue<2, MX>(c, 2, wave);
-        BigWait<MX>::keep2();
+        big_issue<0, MX, HM>(c, 0, wave);
+        big_issue<1, MX, HM>(c, 1, wave);
+        big_issue<2, MX, HM>(c, 2, wave);
+        big_issue<3, MX, HM>(c, 3, wave);
+        if constexpr (kBigConvert<MX, AT>) {
+            BigWait<MX, HM>::keep2();
+            big_convert<0, MX, AT>(0, wave, lane);
+            big_convert<1, MX, AT>(1, wave, lane);
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        } else {
+            BigWait<MX, HM>::keep3();
+        }
         __builtin_amdgcn_s_barrier();
         for (int kt = 0; kt < nk; kt += 8) {
-            big_step<0, MX, AT>(c, acc, bcol, kt + 0, nk, wave, wm, li, lg, mlive);
-            big_step<1, MX, AT>(c, acc, bcol, kt + 1, nk, wave, wm, li, lg, mlive);
-            big_step<2, MX, AT>(c, acc, bcol, kt + 2, nk, wave, wm, li, lg, mlive);
-            big_step<3, MX, AT>(c, acc, bcol, kt + 3, nk, wave, wm, li, lg, mlive);
-            big_step<0, MX, AT>(c, acc, bcol, kt + 4, nk, wave, wm, li, lg, mlive);
-            big_step<1, MX, AT>(c, acc, bcol, kt + 5, nk, wave, wm, li, lg, mlive);
-            big_step<2, MX, AT>(c, acc, bcol, kt + 6, nk, wave, wm, li, lg, mlive);
-            big_step<3, MX, AT>(c, acc, bcol, kt + 7, nk, wave, wm, li, lg, mlive);
+            // K-tile kt is complete for every wave (barrier above or step 7 below).
+            uint4 fa0[8], fb0[NBK], fa1[8], fb1[NBK];
+            big_read<0, NBK>(fa0, fb0, bcol, wm, li, lg);
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            big_step<0, MX, AT, HM, NBK>(c, acc, fa0, fb0, fa1, fb1, bcol, kt + 0, nk, wave, wm, lane);
+            big_step<1, MX, AT, HM, NBK>(c, acc, fa1, fb1, fa0, fb0, bcol, kt + 1, nk, wave, wm, lane);
+            big_step<2, MX, AT, HM, NBK>(c, acc, fa0, fb0, fa1, fb1, bcol, kt + 2, nk, wave, wm, lane);
+            big_step<3, MX, AT, HM, NBK>(c, acc, fa1, fb1, fa0, fb0, bcol, kt + 3, nk, wave, wm, lane);
+            big_step<4, MX, AT, HM, NBK>(c, acc, fa0, fb0, fa1, fb1, bcol, kt + 4, nk, wave, wm, lane);
+            big_step<5, MX, AT, HM, NBK>(c, acc, fa1, fb1, fa0, fb0, bcol, kt + 5, nk, wave, wm, lane);
+            big_step<6, MX, AT, HM, NBK>(c, acc, fa0, fb0, fa1, fb1, bcol, kt + 6, nk, wave, wm, lane);
+            big_step<7, MX, AT, HM, NBK>(c, acc, fa1, fb1, fa0, fb0, bcol, kt + 7, nk, wave, wm, lane);
         }
+        // Drain the clamped tail loads before the stages are refilled.
+        BigWait<MX, HM>::all();
+        __builtin_amdgcn_s_barrier();
 
         // Epilogue: lane (li, lg) holds row wm*128 + 16m + li, columns
         // bcol[c] + 4lg + q (q = 0..3) of every block.
@@ -509,20 +573,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const int64_t p = rt.p0 + row;
             if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
-                for (int cc = 0; cc < 4; ++cc) {
+                for (int cc = 0; cc < NBK / 2; ++cc) {
                     if (ok) {
                         uint16_t h[4];
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) h[q] = f32_to_act<OT>(silu(acc[m][cc][q]) * acc[m][cc + 4][q]);
-                        const int64_t j = nb * 128 + wn * 64 + cc * 16 + lg * 4;
+                        for (int q = 0; q < 4; ++q)
+                            h[q] = f32_to_act<OT>(silu(acc[m][cc][q]) * acc[m][cc + NBK / 2][q]);
+                        const int64_t j = nb * 128 + wn * (WCOLS / 2) + cc * 16 + lg * 4;
                         *(uint2 *)((uint16_t *)a.C + p * a.ldc + j) =
                             make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
                     }
                 }
             } else {
 #pragma unroll
-                for (int cc = 0; cc < 8; ++cc) {
-                    const int64_t n = nb * kBigBN + wn * 128 + cc * 16 + lg * 4;
+                for (int cc = 0; cc < NBK; ++cc) {
+                    const int64_t n = nb * kBigBN + wn * WCOLS + cc * 16 + lg * 4;
                     const floatx4_t v = acc[m][cc];
                     if constexpr (EPI == EPI_F32) {
                         if (ok) *(floatx4_t *)((float *)a.C + p * a.ldc + n) = v;
@@ -546,7 +611,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
                                 make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
                         sq += __shfl_xor(sq, 16, 64);
                         sq += __shfl_xor(sq, 32, 64);
-                        if (ok && lg == 0) a.ssq[p * a.nparts + nb * 16 + wn * 8 + cc] = sq;
+                        if (ok && lg == 0) a.ssq[p * a.nparts + nb * 16 + wn * (WCOLS / 16) + cc] = sq;
                     } else {  // EPI_RESID
                         if (ok) {
                             const uint2 hx = *(const uint2 *)(a.resid + p * a.N + n);
@@ -584,21 +649,25 @@ static hipError_t run_stream(const GemmArgs &a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int EPI, bool MX, bool GROUPED, int AT, int OT>
+template <int EPI, bool MX, bool GROUPED, int AT, int OT, int HM>
 static hipError_t run_tile(const GemmArgs &a, hipStream_t s) {
     const int64_t nblocks = (EPI == EPI_SWIGLU) ? a.N / (kBigBN / 2) : a.N / kBigBN;
     const int64_t tiles = GROUPED ? a.max_tiles : (a.M + kBigBM - 1) / kBigBM;
     const int64_t items = tiles * nblocks;
     if (items <= 0) return hipSuccess;
     const int grid = (int)(items < kBigGrid ? items : kBigGrid);
-    gemm_big_kernel<EPI, MX, GROUPED, AT, OT><<<grid, 256, 0, s>>>(a);
+    gemm_big_kernel<EPI, MX, GROUPED, AT, OT, HM><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
 }
 
 // Dense launches use 64-row tiles on the streaming kernel, grouped ones 16-row tiles.
 template <int EPI, int NB, bool MX, bool GROUPED, int AT, int OT>
 static hipError_t run_path(const GemmArgs &a, int path, hipStream_t s) {
-    if (path == PATH_TILE) return run_tile<EPI, MX, GROUPED, AT, OT>(a, s);
+    if (path == PATH_TILE) return run_tile<EPI, MX, GROUPED, AT, OT, 0>(a, s);
+    if (path == PATH_HALF) {
+        if constexpr (GROUPED) return run_tile<EPI, MX, GROUPED, AT, OT, 1>(a, s);
+        else return hipErrorInvalidValue;
+    }
     if constexpr (GROUPED) return run_stream<1, NB, EPI, MX, GROUPED, AT, OT>(a, s);
     else return run_stream<4, NB, EPI, MX, GROUPED, AT, OT>(a, s);
 }

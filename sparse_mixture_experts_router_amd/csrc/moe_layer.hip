@@ -36,14 +36,15 @@ struct Carve {
 };
 
 struct Layout {
-    size_t u, logits, idx, w, counts, offsets, perm_tok, perm_slot, pos, ntiles, tiles_small, tiles_big;
-    size_t z, act, S, ssq, m;
-    int64_t max_small, max_big;
+    size_t u, logits, idx, w, counts, offsets, perm_tok, perm_slot, pos, ntiles, tiles_small, tiles_big, tiles_half;
+    size_t perm_scratch, z, act, S, ssq, m;
+    int64_t max_small, max_big, max_half;
     size_t total;
 };
 
 int64_t small_tile_cap(int64_t TK, int64_t n) { return TK / kSmallBM + n + 1; }
 int64_t big_tile_cap(int64_t TK, int64_t n) { return TK / kTileBM + n + 1; }
+int64_t half_tile_cap(int64_t n) { return n; }  // at most one per expert
 
 Layout make_layout(const moe_desc *d) {
     Layout L;
@@ -62,11 +63,14 @@ Layout make_layout(const moe_desc *d) {
     L.perm_tok = c.take((size_t)TK * 4);
     L.perm_slot = c.take((size_t)TK * 4);
     L.pos = c.take((size_t)TK * 4);
-    L.ntiles = c.take(2 * 4);
+    L.ntiles = c.take(3 * 4);
     L.max_small = small_tile_cap(TK, n);
     L.max_big = big_tile_cap(TK, n);
+    L.max_half = half_tile_cap(n);
     L.tiles_small = c.take((size_t)L.max_small * sizeof(TileEntry));
     L.tiles_big = c.take((size_t)L.max_big * sizeof(TileEntry));
+    L.tiles_half = c.take((size_t)L.max_half * sizeof(TileEntry));
+    L.perm_scratch = c.take((size_t)permute_scratch_ints(T, (int)n) * 4);
     L.z = d->d_latent ? c.take((size_t)T * d->d_latent * 2) : 0;
     L.act = c.take((size_t)TK * d->d_ff * ab);
     L.S = c.take((size_t)TK * Dx * ab);
@@ -158,6 +162,8 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
     int32_t *perm_tok = (int32_t *)(ws + L.perm_tok), *perm_slot = (int32_t *)(ws + L.perm_slot);
     int32_t *pos = (int32_t *)(ws + L.pos), *ntiles = (int32_t *)(ws + L.ntiles);
     TileEntry *tiles_small = (TileEntry *)(ws + L.tiles_small), *tiles_big = (TileEntry *)(ws + L.tiles_big);
+    TileEntry *tiles_half = (TileEntry *)(ws + L.tiles_half);
+    int32_t *perm_scratch = (int32_t *)(ws + L.perm_scratch);
     uint16_t *z = (uint16_t *)(ws + L.z), *act = (uint16_t *)(ws + L.act), *S = (uint16_t *)(ws + L.S);
     uint16_t *m = (uint16_t *)(ws + L.m);
     float *ssq = L.ssq ? (float *)(ws + L.ssq) : nullptr;
@@ -191,7 +197,7 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
     const bool any_big = T > small_max;
     MOE_TRY_RC(ev.begin(MOE_STAGE_PERMUTE));
     MOE_TRY(launch_permute(idx, T, (int)k, (int)n, counts, offsets, perm_tok, perm_slot, pos, tiles_small, tiles_big,
-                           ntiles, small_max, s));
+                           tiles_half, ntiles, small_max, perm_scratch, s));
     MOE_TRY_RC(ev.end(MOE_STAGE_PERMUTE));
 
     // z = u W_d^T (bf16).
@@ -239,6 +245,10 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
             g.ntiles = ntiles + 1;
             g.max_tiles = (int32_t)L.max_big;
             MOE_TRY(launch_gemm1(g, PATH_TILE, mx, at, s));
+            g.tiles = tiles_half;
+            g.ntiles = ntiles + 2;
+            g.max_tiles = (int32_t)L.max_half;
+            MOE_TRY(launch_gemm1(g, PATH_HALF, mx, at, s));
         }
     }
     MOE_TRY_RC(ev.end(MOE_STAGE_GEMM1));
@@ -271,6 +281,10 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
             g.ntiles = ntiles + 1;
             g.max_tiles = (int32_t)L.max_big;
             MOE_TRY(launch_gemm2(g, PATH_TILE, mx, at, norm2, s));
+            g.tiles = tiles_half;
+            g.ntiles = ntiles + 2;
+            g.max_tiles = (int32_t)L.max_half;
+            MOE_TRY(launch_gemm2(g, PATH_HALF, mx, at, norm2, s));
         }
     }
     MOE_TRY_RC(ev.end(MOE_STAGE_GEMM2));
@@ -344,7 +358,7 @@ int forward_f32(const moe_desc *d, const void *x, const void *router_w, const vo
     MOE_TRY_RC(ev.end(MOE_STAGE_TOPK));
     MOE_TRY_RC(ev.begin(MOE_STAGE_PERMUTE));
     MOE_TRY(launch_permute(idx, T, (int)k, (int)n, counts, offsets, perm_tok, perm_slot, pos, nullptr, nullptr,
-                           nullptr, 0, s));
+                           nullptr, nullptr, 0, (int32_t *)(ws + L.perm_scratch), s));
     MOE_TRY_RC(ev.end(MOE_STAGE_PERMUTE));
     MOE_TRY_RC(ev.begin(MOE_STAGE_GEMM1));
     MOE_TRY(launch_expert1_f32((const float *)x, (const float *)w1, perm_tok, offsets, (int)n, TK, F, D,
@@ -460,7 +474,7 @@ int moe_permute(int64_t T, int64_t k, int64_t n, const int32_t *topk_idx, int32_
     if (!topk_idx || !counts || !offsets || !perm_tok || !perm_slot || !pos) return MOE_ERR_INVALID_ARG;
     hipStream_t s = as_stream(stream);
     MOE_TRY(launch_permute(topk_idx, T, (int)k, (int)n, counts, offsets, perm_tok, perm_slot, pos, nullptr, nullptr,
-                           nullptr, 0, s));
+                           nullptr, nullptr, 0, nullptr, s));
     return MOE_OK;
 }
 

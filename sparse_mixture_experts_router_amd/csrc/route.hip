@@ -159,12 +159,14 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
 }
 
 // ---------------------------------------------------------------------------
-// Permutation: one workgroup of 1024 threads.
-//   counts (LDS histogram) -> exclusive scans (token offsets and the two tile
-//   lists) -> stable scatter: position of (t, j) with expert e is
-//   offsets[e] + #{t' < t : e in idx[t']}, counted with per-chunk LDS
-//   bitmaps (bit t of expert e's row) and popcounts, so no atomic decides
-//   an order.
+// Permutation.  The position of (t, j) with expert e is
+// offsets[e] + #{t' < t : e in idx[t']}: expert-major, token order inside an
+// expert (top-k experts of a token are distinct).  Ranks are counted with LDS
+// bitmaps (bit t of expert e's row) and popcounts, so no atomic decides an
+// order.  Small batches use one workgroup of 1024 threads (histogram ->
+// scans -> scatter in chunks of 1024 tokens); large ones use three kernels
+// over chunks of 256 tokens: per-chunk histograms, one scan workgroup
+// (per-expert chunk bases, offsets, tile lists), and a per-chunk scatter.
 // ---------------------------------------------------------------------------
 
 constexpr int kPermThreads = 1024;
@@ -188,47 +190,78 @@ __device__ __forceinline__ void scan256_excl(int *a, int n) {  // in-place exclu
     __syncthreads();
 }
 
-__global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__restrict__ idx, int64_t T, int k, int n,
-                                                               int32_t *__restrict__ counts,
-                                                               int32_t *__restrict__ offsets,
-                                                               int32_t *__restrict__ perm_tok,
-                                                               int32_t *__restrict__ perm_slot,
-                                                               int32_t *__restrict__ pos, TileEntry *tiles_small,
-                                                               TileEntry *tiles_big, int32_t *ntiles, int small_max) {
-    __shared__ int cnt[257], off[257], ts[257], tb[257], base[256];
-    __shared__ unsigned mask[256][kPermWords];
+// Tile lists of the grouped GEMMs for an expert with c rows: 1..small_max
+// rows -> small tiles of kSmallBM rows; more -> c / kTileBM full tiles, and
+// for a remainder r one more full tile when r > kHalfBM or one half-height
+// tile when 0 < r <= kHalfBM.
+__device__ __forceinline__ void tile_counts(int c, int small_max, int &ns, int &nb, int &nh) {
+    ns = (c > 0 && c <= small_max) ? (c + kSmallBM - 1) / kSmallBM : 0;
+    nb = nh = 0;
+    if (c > small_max) {
+        const int full = c / kTileBM, r = c - full * kTileBM;
+        nb = full + (r > kHalfBM ? 1 : 0);
+        nh = (r > 0 && r <= kHalfBM) ? 1 : 0;
+    }
+}
+
+// Counts, offsets and the three tile lists from per-expert counts cnt[0..n)
+// in LDS.  off/ts/tb/th: LDS scratch of 257 entries.  Every thread of the
+// workgroup (>= 256) must call it.
+__device__ void publish_counts(const int *cnt, int *off, int *ts, int *tb, int *th, int n, int small_max,
+                               int32_t *counts, int32_t *offsets, TileEntry *tiles_small, TileEntry *tiles_big,
+                               TileEntry *tiles_half, int32_t *ntiles) {
     const int tid = threadIdx.x;
-    if (tid < 257) cnt[tid] = 0;
-    __syncthreads();
-    const int64_t TK = T * k;
-    for (int64_t i = tid; i < TK; i += kPermThreads) atomicAdd(&cnt[idx[i]], 1);
-    __syncthreads();
     if (tid < n) {
-        int c = cnt[tid];
-        off[tid] = c;
-        ts[tid] = (c > 0 && c <= small_max) ? (c + kSmallBM - 1) / kSmallBM : 0;
-        tb[tid] = (c > small_max) ? (c + kTileBM - 1) / kTileBM : 0;
-        base[tid] = 0;
+        int ns, nb, nh;
+        tile_counts(cnt[tid], small_max, ns, nb, nh);
+        off[tid] = cnt[tid];
+        ts[tid] = ns;
+        tb[tid] = nb;
+        th[tid] = nh;
     }
     scan256_excl(off, n);
     scan256_excl(ts, n);
     scan256_excl(tb, n);
+    scan256_excl(th, n);
     if (tid < n) {
         const int c = cnt[tid];
         counts[tid] = c;
         offsets[tid] = off[tid];
-        if (tiles_small && c > 0 && c <= small_max)
+        if (tiles_small)
             for (int q = 0; q < ts[tid + 1] - ts[tid]; ++q) tiles_small[ts[tid] + q] = TileEntry{tid, q * kSmallBM};
-        if (tiles_big && c > small_max)
+        if (tiles_big)
             for (int q = 0; q < tb[tid + 1] - tb[tid]; ++q) tiles_big[tb[tid] + q] = TileEntry{tid, q * kTileBM};
+        if (tiles_half && th[tid + 1] > th[tid]) tiles_half[th[tid]] = TileEntry{tid, (c / kTileBM) * kTileBM};
     }
     if (tid == 0) {
         offsets[n] = off[n];
         if (ntiles) {
             ntiles[0] = ts[n];
             ntiles[1] = tb[n];
+            ntiles[2] = th[n];
         }
     }
+    __syncthreads();
+}
+
+__global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__restrict__ idx, int64_t T, int k, int n,
+                                                               int32_t *__restrict__ counts,
+                                                               int32_t *__restrict__ offsets,
+                                                               int32_t *__restrict__ perm_tok,
+                                                               int32_t *__restrict__ perm_slot,
+                                                               int32_t *__restrict__ pos, TileEntry *tiles_small,
+                                                               TileEntry *tiles_big, TileEntry *tiles_half,
+                                                               int32_t *ntiles, int small_max) {
+    __shared__ int cnt[257], off[257], ts[257], tb[257], th[257], base[256];
+    __shared__ unsigned mask[256][kPermWords];
+    const int tid = threadIdx.x;
+    if (tid < 257) cnt[tid] = 0;
+    if (tid < 256) base[tid] = 0;
+    __syncthreads();
+    const int64_t TK = T * k;
+    for (int64_t i = tid; i < TK; i += kPermThreads) atomicAdd(&cnt[idx[i]], 1);
+    __syncthreads();
+    publish_counts(cnt, off, ts, tb, th, n, small_max, counts, offsets, tiles_small, tiles_big, tiles_half, ntiles);
     for (int64_t c0 = 0; c0 < T; c0 += kPermThreads) {
         for (int i = tid; i < 256 * kPermWords; i += kPermThreads) (&mask[0][0])[i] = 0u;
         __syncthreads();
@@ -256,6 +289,80 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__
             base[tid] += add;
         }
         __syncthreads();
+    }
+}
+
+constexpr int kChunkTok = 256;                 // tokens per chunk of the multi-workgroup permutation
+constexpr int kChunkWords = kChunkTok / 32;
+
+// Per-chunk expert histograms: wg_counts[g][e].
+__global__ __launch_bounds__(kChunkTok) void perm_count_kernel(const int32_t *__restrict__ idx, int64_t T, int k, int n,
+                                                              int32_t *__restrict__ wg_counts) {
+    __shared__ int cnt[256];
+    const int tid = threadIdx.x;
+    cnt[tid] = 0;
+    __syncthreads();
+    const int64_t t = (int64_t)blockIdx.x * kChunkTok + tid;
+    if (t < T)
+        for (int j = 0; j < k; ++j) atomicAdd(&cnt[idx[t * k + j]], 1);
+    __syncthreads();
+    if (tid < n) wg_counts[(int64_t)blockIdx.x * n + tid] = cnt[tid];
+}
+
+// One workgroup: per-expert totals, the chunk bases wg_base[g][e] =
+// offsets[e] + sum_{g' < g} wg_counts[g'][e], offsets and tile lists.
+__global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t *__restrict__ wg_counts, int G, int n,
+                                                        int32_t *__restrict__ wg_base, int32_t *__restrict__ counts,
+                                                        int32_t *__restrict__ offsets, TileEntry *tiles_small,
+                                                        TileEntry *tiles_big, TileEntry *tiles_half, int32_t *ntiles,
+                                                        int small_max) {
+    __shared__ int cnt[257], off[257], ts[257], tb[257], th[257];
+    const int tid = threadIdx.x;
+    if (tid < n) {
+        int run = 0;
+        for (int g = 0; g < G; ++g) {
+            const int c = wg_counts[(int64_t)g * n + tid];
+            wg_base[(int64_t)g * n + tid] = run;
+            run += c;
+        }
+        cnt[tid] = run;
+    }
+    __syncthreads();
+    publish_counts(cnt, off, ts, tb, th, n, small_max, counts, offsets, tiles_small, tiles_big, tiles_half, ntiles);
+    if (tid < n) {
+        const int o = off[tid];
+        for (int g = 0; g < G; ++g) wg_base[(int64_t)g * n + tid] += o;
+    }
+}
+
+// Stable scatter of one chunk: rank of token t among the chunk's tokens of
+// expert e from the LDS bitmap, plus the chunk's base for e.
+__global__ __launch_bounds__(kChunkTok) void perm_scatter_kernel(const int32_t *__restrict__ idx, int64_t T, int k,
+                                                                int n, const int32_t *__restrict__ wg_base,
+                                                                int32_t *__restrict__ perm_tok,
+                                                                int32_t *__restrict__ perm_slot,
+                                                                int32_t *__restrict__ pos) {
+    __shared__ unsigned mask[256][kChunkWords];
+    const int tid = threadIdx.x;
+    for (int i = tid; i < 256 * kChunkWords; i += kChunkTok) (&mask[0][0])[i] = 0u;
+    __syncthreads();
+    const int64_t t = (int64_t)blockIdx.x * kChunkTok + tid;
+    const bool live = t < T;
+    const int word = tid >> 5, bit = tid & 31;
+    if (live)
+        for (int j = 0; j < k; ++j) atomicOr(&mask[idx[t * k + j]][word], 1u << bit);
+    __syncthreads();
+    if (live) {
+        const int32_t *base = wg_base + (int64_t)blockIdx.x * n;
+        for (int j = 0; j < k; ++j) {
+            const int e = idx[t * k + j];
+            int rank = __popc(mask[e][word] & ((1u << bit) - 1u));
+            for (int q = 0; q < word; ++q) rank += __popc(mask[e][q]);
+            const int p = base[e] + rank;
+            perm_tok[p] = (int32_t)t;
+            perm_slot[p] = j;
+            pos[t * k + j] = p;
+        }
     }
 }
 
@@ -423,11 +530,23 @@ hipError_t launch_topk(const float *logits, const float *bias, int64_t T, int n,
     return hipGetLastError();
 }
 
+int64_t permute_scratch_ints(int64_t T, int n) { return 2 * ((T + kChunkTok - 1) / kChunkTok) * n; }
+
 hipError_t launch_permute(const int32_t *idx, int64_t T, int k, int n, int32_t *counts, int32_t *offsets,
                           int32_t *perm_tok, int32_t *perm_slot, int32_t *pos, TileEntry *tiles_small,
-                          TileEntry *tiles_big, int32_t *ntiles, int small_max, hipStream_t s) {
-    permute_kernel<<<1, kPermThreads, 0, s>>>(idx, T, k, n, counts, offsets, perm_tok, perm_slot, pos, tiles_small,
-                                              tiles_big, ntiles, small_max);
+                          TileEntry *tiles_big, TileEntry *tiles_half, int32_t *ntiles, int small_max,
+                          int32_t *scratch, hipStream_t s) {
+    if (!scratch || T < kPermMultiMinT) {
+        permute_kernel<<<1, kPermThreads, 0, s>>>(idx, T, k, n, counts, offsets, perm_tok, perm_slot, pos,
+                                                  tiles_small, tiles_big, tiles_half, ntiles, small_max);
+        return hipGetLastError();
+    }
+    const int G = (int)((T + kChunkTok - 1) / kChunkTok);
+    int32_t *wg_counts = scratch, *wg_base = scratch + (int64_t)G * n;
+    perm_count_kernel<<<G, kChunkTok, 0, s>>>(idx, T, k, n, wg_counts);
+    perm_scan_kernel<<<1, 256, 0, s>>>(wg_counts, G, n, wg_base, counts, offsets, tiles_small, tiles_big, tiles_half,
+                                       ntiles, small_max);
+    perm_scatter_kernel<<<G, kChunkTok, 0, s>>>(idx, T, k, n, wg_base, perm_tok, perm_slot, pos);
     return hipGetLastError();
 }
 
