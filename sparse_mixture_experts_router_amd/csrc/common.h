@@ -11,6 +11,7 @@ typedef _Float16 f16x8_t __attribute__((ext_vector_type(8)));
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 typedef __fp16 fp16x2_t __attribute__((ext_vector_type(2)));
 typedef float floatx4_t __attribute__((ext_vector_type(4)));
+typedef float floatx16_t __attribute__((ext_vector_type(16)));
 
 namespace moe {
 
@@ -41,6 +42,19 @@ __device__ __forceinline__ floatx4_t mfma16x16x32(uint4 a, uint4 b, floatx4_t c)
                                                       c, 0, 0, 0);
     else
         return __builtin_amdgcn_mfma_f32_16x16x32_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
+}
+
+// 32x32x16 MFMA: lane l supplies row l%32 of A and column l%32 of B at
+// k = 8*(l/32) .. +7; it receives D[8*(r/4) + 4*(l/32) + r%4][l%32] in
+// register r.  One wave per SIMD sustains close to the peak rate with this
+// shape (the 16x16x32 one needs two waves per SIMD for that).
+template <int AT>
+__device__ __forceinline__ floatx16_t mfma32x32x16(uint4 a, uint4 b, floatx16_t c) {
+    if constexpr (AT == ACT_F16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
+                                                      c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(as_bf16x8(a), as_bf16x8(b), c, 0, 0, 0);
 }
 
 // fp32 -> activation bits (round to nearest even; fp16 overflows to inf).

@@ -266,227 +266,254 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 // Large-tile kernel (many rows per expert; dense projections at large T)
 // ---------------------------------------------------------------------------
 //
-// Tile 256 (A rows) x 256 (B rows) x 32 (K) per stage, 256 threads as 2 x 2
-// waves of 128 x 128, so a wave reads 16 KiB of LDS per stage for 64 MFMAs
-// (64 FLOP per LDS byte).  Operands move global -> LDS with gfx950's
-// direct-to-LDS loads (global_load_lds): a wave instruction fills LDS in lane
-// order, so each lane fetches the global chunk that belongs at its LDS slot,
-// which realises the XOR swizzle.  Four stage buffers rotate; the loads of
-// K-tile kt+4 are issued at step kt, so three K-tiles (96 KiB per CU) are in
-// flight while the MFMAs of one run.  Fragments are double-buffered in
-// registers: the MFMAs on K-tile kt overlap the LDS reads of kt+1.
+// Tile 256 (A rows) x 256 (B rows), 256 threads as 2 x 2 waves of 128 x 128,
+// each a 4 x 4 grid of 32 x 32 x 16 MFMA blocks (one wave per SIMD keeps this
+// MFMA shape close to its peak issue rate; the 16 x 16 x 32 shape would need
+// two waves per SIMD).  K advances in pairs of 64: a pair buffer holds the A
+// and B rows of one pair as 128-byte rows, and two buffers alternate.
+// Operands move global -> LDS with direct-to-LDS loads (global_load_lds): a
+// wave instruction fills 8 rows x 128 bytes of LDS in lane order, so each lane
+// fetches the global chunk that belongs at its XOR-swizzled LDS slot, and
+// every L2 request is a whole 128-byte row segment.  A pair runs as two 32-K
+// sub-steps.  Fragments are double-buffered in registers: the MFMAs of one
+// sub-step overlap the LDS reads of the next, and the loads of pair p+2 are
+// spread between the MFMAs of pair p's second sub-step; the only barrier of a
+// pair sits in front of it.
 // When the MFMA type differs from the stored weights (bf16 weights with fp16
-// activations, or MXFP4), each wave converts the share of the B stage that
-// its own loads brought in, in LDS, two K-tiles ahead (bf16 -> fp16 in place;
-// MXFP4 codes and block scales -> the activation type into the B operand
-// area), so the MFMA operands always come straight from LDS reads.
-// The MFMA operands are swapped (B first), so a lane's four accumulator
-// elements are four consecutive output columns of one row: epilogue stores
-// are 8 or 16 bytes wide.  EPI_SWIGLU tiles hold 128 gate rows then the 128
-// matching up rows; wave column block c < 4 (gate) pairs with c + 4 (up).
+// activations, or MXFP4), each wave converts the share of a pair's B that its
+// own loads brought in, in LDS, before the barrier that publishes the pair
+// (bf16 -> fp16 in place; MXFP4 codes and block scales -> the activation type
+// into the B operand area), so MFMA operands always come straight from LDS.
+// The MFMA operands are swapped (B first), so a lane's accumulator registers
+// hold runs of four adjacent output columns of one row: epilogue stores are 8
+// or 16 bytes wide.  EPI_SWIGLU tiles hold 128 gate rows then the 128 matching
+// up rows; a wave's gate column blocks pair with its up column blocks.
 // Rows past the tile's valid rows load a clamped valid A row; their results
 // are never stored.  The half-height variant (HM) serves grouped tiles of at
 // most 128 rows (an expert's remainder): its four waves share the 128 A rows
 // and each takes 64 of the 256 B rows, so no wave idles on empty rows.
 
-constexpr int kBigBM = kTileBM, kBigBN = kTileBN, kBigBK = 32;
+constexpr int kBigBM = kTileBM, kBigBN = kTileBN, kBigBK = 64;  // K per pair
 static_assert(kBigBM == 256 && kBigBN == 256, "the wave layout below assumes 256x256 tiles");
-constexpr int kBigOpBytes = kBigBM * kBigBK * 2;      // one operand area (A, or B in the MFMA type): 16 KiB
-constexpr int kBigMxCodeBytes = kBigBN * kBigBK / 2;  // MXFP4 B codes per stage: 4 KiB
-constexpr int kBigMxCodeOff = 2 * kBigOpBytes;        // MXFP4 codes, then 1 KiB of scale words
-constexpr int kBigMxScaleOff = kBigMxCodeOff + kBigMxCodeBytes;
-constexpr int kBigStageBytes = kBigMxScaleOff + kBigBN * 4;  // 37 KiB; 4 stages = 148 KiB
+constexpr int kBigRow = kBigBK * 2;                             // bytes per LDS row (128)
+constexpr int kBigOpBytes = kBigBM * kBigRow;                   // A area, or B area in the MFMA type: 32 KiB
+constexpr int kBigMxCodeOff = 2 * kBigOpBytes;                  // MXFP4: 256 rows x 32 bytes of codes,
+constexpr int kBigMxScaleOff = kBigMxCodeOff + kBigBN * 32;     // then 256 scale words
+constexpr int kBigPairBytes = kBigMxScaleOff + kBigBN * 4;      // 73 KiB; two buffers = 146 KiB
 
-__shared__ __attribute__((aligned(16))) uint8_t big_lds0[kBigStageBytes];
-__shared__ __attribute__((aligned(16))) uint8_t big_lds1[kBigStageBytes];
-__shared__ __attribute__((aligned(16))) uint8_t big_lds2[kBigStageBytes];
-__shared__ __attribute__((aligned(16))) uint8_t big_lds3[kBigStageBytes];
+__shared__ __attribute__((aligned(16))) uint8_t big_lds0[kBigPairBytes];
+__shared__ __attribute__((aligned(16))) uint8_t big_lds1[kBigPairBytes];
 
-// Separate LDS objects per stage let the compiler see that a read of one
-// stage does not depend on the loads still landing in the others.
-template <int ST>
+// Separate LDS objects per buffer let the compiler see that a read of one
+// buffer does not depend on the loads still landing in the other.
+template <int P>
 __device__ __forceinline__ uint8_t *big_buf() {
-    if constexpr (ST == 0) return big_lds0;
-    else if constexpr (ST == 1) return big_lds1;
-    else if constexpr (ST == 2) return big_lds2;
-    else return big_lds3;
+    if constexpr (P == 0) return big_lds0;
+    else return big_lds1;
 }
 
 #define MOE_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
-// 64-byte rows (32 x 16-bit): 16-byte chunk c of row r lives at chunk
-// c ^ ((r >> 1) & 3), so the 8 rows a ds_read_b128 serves at once hit 8
-// distinct 16-byte bank groups.
+// 128-byte rows (64 x 16-bit): 16-byte chunk c of row r lives at chunk
+// c ^ ((r >> 1) & 3), so the 8 rows a ds_read_b128 phase serves at one
+// logical chunk hit 8 distinct 16-byte bank groups.
 __device__ __forceinline__ int bswz(int row, int chunk) {
-    return row * (kBigBK * 2) + ((chunk ^ ((row >> 1) & 3)) << 4);
+    return row * kBigRow + ((chunk ^ ((row >> 1) & 3)) << 4);
 }
 
 // Load addresses: a wave-uniform base plus a 32-bit byte offset per lane, so
 // the loads take the scalar-base form and the per-lane state stays small.
 struct BigCtx {
     const uint8_t *A;       // activation base (uniform)
-    uint32_t aoff[4];       // byte offsets of this lane's 4 A chunks at k = 0
+    uint32_t aoff[8];       // byte offsets of this lane's A chunks at k = 0
     const uint8_t *B;       // first B row of the tile (bf16) or its code row (MXFP4) (uniform)
-    uint32_t boff[4];       // bf16: byte offsets of this lane's 4 B chunks; MXFP4: [0] codes, [1] scales
+    uint32_t boff[8];       // bf16: this lane's B chunks; MXFP4: [0..1] codes, [2] scale word
     const uint8_t *bsc;     // MXFP4: scale base of the tile (uniform)
 };
 
-// Direct-to-LDS loads of K-tile kt into stage buffer ST.  A wave instruction
-// fills 1 KiB of LDS in lane order (16 bytes per lane for dwordx4, 4 per lane
-// for dword): 16 rows x 4 chunks of A or bf16 B, 64 rows x 16 bytes of MXFP4
-// codes, or 64 rows' scale words.
-template <int ST, bool MX, int HM>
-__device__ __forceinline__ void big_issue(const BigCtx &c, int kt, int wave) {
-    constexpr int NA = HM ? 2 : 4;  // A loads per wave (16 rows each)
-    uint8_t *buf = big_buf<ST>();
-    const uint8_t *Ak = c.A + (int64_t)kt * (kBigBK * 2);
+template <bool MX, int HM> struct BigShape {
+    static constexpr int NA = HM ? 4 : 8;         // A loads per wave per pair (8 rows each)
+    static constexpr int NB = MX ? 3 : 8;         // B loads per wave per pair
+    static constexpr int kPerPair = NA + NB;
+};
+
+// Direct-to-LDS loads of K pair pr into buffer P.
+template <int P, bool MX, int HM>
+__device__ __forceinline__ void big_issue(const BigCtx &c, int pr, int wave) {
+    constexpr int NA = BigShape<MX, HM>::NA;
+    uint8_t *buf = big_buf<P>();
+    const uint8_t *Ak = c.A + (int64_t)pr * kBigRow;
 #pragma unroll
     for (int i = 0; i < NA; ++i)
         __builtin_amdgcn_global_load_lds(Ak + c.aoff[i], MOE_LDS(buf + (wave * NA + i) * 1024), 16, 0, 0);
     if constexpr (MX) {
-        __builtin_amdgcn_global_load_lds(c.B + (int64_t)kt * (kBigBK / 2) + c.boff[0],
-                                         MOE_LDS(buf + kBigMxCodeOff + wave * 1024), 16, 0, 0);
-        // the 4-byte-aligned word holding this K-tile's scale byte of the lane's row
-        __builtin_amdgcn_global_load_lds(c.bsc + (int64_t)(kt & ~3) + c.boff[1],
+        const uint8_t *Bk = c.B + (int64_t)pr * 32;
+#pragma unroll
+        for (int i = 0; i < 2; ++i)
+            __builtin_amdgcn_global_load_lds(Bk + c.boff[i], MOE_LDS(buf + kBigMxCodeOff + (wave * 2 + i) * 1024), 16, 0,
+                                             0);
+        // the 4-byte-aligned word holding the scale bytes of K-tiles 2pr, 2pr+1
+        __builtin_amdgcn_global_load_lds(c.bsc + (int64_t)((2 * pr) & ~3) + c.boff[2],
                                          MOE_LDS(buf + kBigMxScaleOff + wave * 256), 4, 0, 0);
     } else {
         uint8_t *bb = buf + kBigOpBytes;
-        const uint8_t *Bk = c.B + (int64_t)kt * (kBigBK * 2);
+        const uint8_t *Bk = c.B + (int64_t)pr * kBigRow;
 #pragma unroll
-        for (int i = 0; i < 4; ++i)
-            __builtin_amdgcn_global_load_lds(Bk + c.boff[i], MOE_LDS(bb + (wave * 4 + i) * 1024), 16, 0, 0);
+        for (int i = 0; i < 8; ++i)
+            __builtin_amdgcn_global_load_lds(Bk + c.boff[i], MOE_LDS(bb + (wave * 8 + i) * 1024), 16, 0, 0);
     }
 }
 
-template <bool MX, int AT> constexpr bool kBigConvert = MX || AT == ACT_F16;
+// MXFP4 weights are dequantised in LDS, once per wave share; bf16 weights
+// with fp16 activations are converted per fragment in registers, between
+// the MFMAs.
+template <bool MX, int AT> constexpr bool kBigConvert = MX;
+template <bool MX, int AT> constexpr bool kBigRegConvert = !MX && AT == ACT_F16;
 
-// Convert the B data that this wave's own loads put into stage ST (K-tile kt)
-// into the MFMA type: bf16 -> fp16 in place (the lane's own four chunks), or
-// the 32 MXFP4 codes of row 64*wave + lane times its block scale -> four
-// swizzled chunks of the B operand area.
-template <int ST, bool MX, int AT>
-__device__ __forceinline__ void big_convert(int kt, int wave, int lane) {
-    uint8_t *buf = big_buf<ST>();
+// Convert the B data that this wave's own loads put into buffer P (pair pr)
+// into the MFMA type: bf16 -> fp16 in place (the lane's own eight chunks), or
+// the 64 MXFP4 codes of row 64*wave + lane times the block scales of K-tiles
+// 2pr and 2pr+1 -> eight swizzled chunks of the B operand area.
+template <int P, bool MX, int AT>
+__device__ __forceinline__ void big_convert(int pr, int wave, int lane) {
+    uint8_t *buf = big_buf<P>();
     uint8_t *bb = buf + kBigOpBytes;
     if constexpr (MX) {
         const int r = wave * 64 + lane;
-        const uint4 codes = *(const uint4 *)(buf + kBigMxCodeOff + r * 16);
-        const uint32_t sc = buf[kBigMxScaleOff + r * 4 + (kt & 3)];
-        *(uint4 *)(bb + bswz(r, 0)) = mxfp4x8_to_act<AT>(codes.x, sc);
-        *(uint4 *)(bb + bswz(r, 1)) = mxfp4x8_to_act<AT>(codes.y, sc);
-        *(uint4 *)(bb + bswz(r, 2)) = mxfp4x8_to_act<AT>(codes.z, sc);
-        *(uint4 *)(bb + bswz(r, 3)) = mxfp4x8_to_act<AT>(codes.w, sc);
+        const uint4 c0 = *(const uint4 *)(buf + kBigMxCodeOff + r * 32);
+        const uint4 c1 = *(const uint4 *)(buf + kBigMxCodeOff + r * 32 + 16);
+        const uint32_t sw = *(const uint32_t *)(buf + kBigMxScaleOff + r * 4);
+        const uint32_t s0 = (sw >> (8 * ((2 * pr) & 3))) & 255u, s1 = (sw >> (8 * ((2 * pr + 1) & 3))) & 255u;
+        *(uint4 *)(bb + bswz(r, 0)) = mxfp4x8_to_act<AT>(c0.x, s0);
+        *(uint4 *)(bb + bswz(r, 1)) = mxfp4x8_to_act<AT>(c0.y, s0);
+        *(uint4 *)(bb + bswz(r, 2)) = mxfp4x8_to_act<AT>(c0.z, s0);
+        *(uint4 *)(bb + bswz(r, 3)) = mxfp4x8_to_act<AT>(c0.w, s0);
+        *(uint4 *)(bb + bswz(r, 4)) = mxfp4x8_to_act<AT>(c1.x, s1);
+        *(uint4 *)(bb + bswz(r, 5)) = mxfp4x8_to_act<AT>(c1.y, s1);
+        *(uint4 *)(bb + bswz(r, 6)) = mxfp4x8_to_act<AT>(c1.z, s1);
+        *(uint4 *)(bb + bswz(r, 7)) = mxfp4x8_to_act<AT>(c1.w, s1);
     } else {
-        uint4 v[4];
+        uint4 v[8];
 #pragma unroll
-        for (int i = 0; i < 4; ++i) v[i] = *(const uint4 *)(bb + (wave * 4 + i) * 1024 + lane * 16);
+        for (int i = 0; i < 8; ++i) v[i] = *(const uint4 *)(bb + (wave * 8 + i) * 1024 + lane * 16);
 #pragma unroll
-        for (int i = 0; i < 4; ++i) *(uint4 *)(bb + (wave * 4 + i) * 1024 + lane * 16) = bf16x8_to_f16x8(v[i]);
+        for (int i = 0; i < 8; ++i) *(uint4 *)(bb + (wave * 8 + i) * 1024 + lane * 16) = bf16x8_to_f16x8(v[i]);
     }
 }
 
-// Fragments of one stage: A rows wm*128 + 16m + li, B rows bcol[c] + li, chunk lg.
-template <int ST, int NBK>
-__device__ __forceinline__ void big_read(uint4 (&fa)[8], uint4 (&fb)[NBK], const int (&bcol)[NBK], int wm, int li,
-                                         int lg) {
-    const uint8_t *buf = big_buf<ST>();
+// Fragments of sub-step HS (K 32*HS .. +31 of the pair in buffer P) for the
+// 32x32x16 MFMA: lane (lr = l%32, lh = l/32) reads row lr of each 32-row
+// block at K half h, i.e. logical chunk 4*HS + 2h + lh.
+// fa[2m + h]: A rows wm*128 + 32m + lr; fb[2c + h]: B rows bcol[c] + lr.
+template <int P, int HS, int NBK, bool CVT>
+__device__ __forceinline__ void big_read(uint4 (&fa)[8], uint4 (&fb)[2 * NBK], const int (&bcol)[NBK], int wm, int lr,
+                                         int lh) {
+    const uint8_t *buf = big_buf<P>();
     const uint8_t *bb = buf + kBigOpBytes;
 #pragma unroll
-    for (int c = 0; c < NBK; ++c) fb[c] = *(const uint4 *)(bb + bswz(bcol[c] + li, lg));
+    for (int c = 0; c < NBK; ++c)
 #pragma unroll
-    for (int m = 0; m < 8; ++m) fa[m] = *(const uint4 *)(buf + bswz(wm * 128 + m * 16 + li, lg));
+        for (int h = 0; h < 2; ++h) {
+            const uint4 v = *(const uint4 *)(bb + bswz(bcol[c] + lr, 4 * HS + 2 * h + lh));
+            fb[2 * c + h] = CVT ? bf16x8_to_f16x8(v) : v;
+        }
+#pragma unroll
+    for (int m = 0; m < 4; ++m)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            fa[2 * m + h] = *(const uint4 *)(buf + bswz(wm * 128 + m * 32 + lr, 4 * HS + 2 * h + lh));
 }
 
+// The MFMAs of one sub-step, K half by K half, so two MFMAs on one
+// accumulator are 4 * NBK instructions apart.
 template <int AT, int NBK>
-__device__ __forceinline__ void big_mma(floatx4_t (&acc)[8][NBK], const uint4 (&fa)[8], const uint4 (&fb)[NBK]) {
+__device__ __forceinline__ void big_mma(floatx16_t (&acc)[4][NBK], const uint4 (&fa)[8], const uint4 (&fb)[2 * NBK]) {
 #pragma unroll
-    for (int m = 0; m < 8; ++m)
-#pragma unroll
-        for (int c = 0; c < NBK; ++c) acc[m][c] = mfma16x16x32<AT>(fb[c], fa[m], acc[m][c]);
-}
-
-// Load instructions per wave per stage, and the vmcnt waits that leave 3 or
-// 2 later stages in flight.  The waits go through the s_waitcnt builtin (not
-// inline asm) so the compiler's own wait insertion knows of them.  gfx9
-// s_waitcnt fields: vmcnt bits 3:0 and 15:14, expcnt 6:4, lgkmcnt 11:8.
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
-template <bool MX, int HM> struct BigWait {
-    static constexpr int kPerStage = (HM ? 2 : 4) + (MX ? 2 : 4);
-    static __device__ __forceinline__ void keep3() { __builtin_amdgcn_s_waitcnt(waitcnt_vm(3 * kPerStage)); }
-    static __device__ __forceinline__ void keep2() { __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * kPerStage)); }
-    static __device__ __forceinline__ void all() { __builtin_amdgcn_s_waitcnt(waitcnt_vm(0)); }
-};
-
-// One K step j of a group of eight, on K-tile kt (stage ST = kt & 3).  On
-// entry this wave holds the fragments of kt (cur) and has finished all its
-// LDS work on earlier steps.  The barrier then guarantees for every wave that
-// K-tile kt+1 is complete in its stage (landed, and converted where needed)
-// and that nobody still reads stage ST, which receives K-tile kt+4 (clamped
-// to the last K-tile near the end: those loads are never read).  The MFMAs on
-// cur overlap the reads of kt+1 into nxt, except in the group's last step:
-// fragments are not carried across the loop's back edge, which keeps the
-// accumulators in place in the register allocation.  With conversion, the
-// wave waits for its own loads of kt+2 and converts them halfway through the
-// MFMAs, so the next barrier publishes kt+2 ready for use.
-template <int J, bool MX, int AT, int HM, int NBK>
-__device__ __forceinline__ void big_step(const BigCtx &c, floatx4_t (&acc)[8][NBK], const uint4 (&cur_a)[8],
-                                         const uint4 (&cur_b)[NBK], uint4 (&nxt_a)[8], uint4 (&nxt_b)[NBK],
-                                         const int (&bcol)[NBK], int kt, int nk, int wave, int wm, int lane) {
-    constexpr int ST = J & 3;
-    const int li = lane & 15, lg = lane >> 4;
-    if constexpr (!kBigConvert<MX, AT>) BigWait<MX, HM>::keep2();
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    big_issue<ST, MX, HM>(c, min(kt + 4, nk - 1), wave);
-    if constexpr (J < 7) big_read<(ST + 1) & 3, NBK>(nxt_a, nxt_b, bcol, wm, li, lg);
-    if constexpr (kBigConvert<MX, AT>) {
-        // first half of the MFMAs (rows 0-3), then the conversion, then the rest
+    for (int h = 0; h < 2; ++h)
 #pragma unroll
         for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int cc = 0; cc < NBK; ++cc) acc[m][cc] = mfma16x16x32<AT>(cur_b[cc], cur_a[m], acc[m][cc]);
-        __builtin_amdgcn_sched_barrier(0);
-        BigWait<MX, HM>::keep2();
-        big_convert<(ST + 2) & 3, MX, AT>(kt + 2, wave, lane);
+            for (int c = 0; c < NBK; ++c) acc[m][c] = mfma32x32x16<AT>(fb[2 * c + h], fa[2 * m + h], acc[m][c]);
+}
+
+// Waits go through the s_waitcnt builtin (not inline asm) so the compiler's
+// own wait insertion knows of them.  gfx9 s_waitcnt fields: vmcnt bits 3:0
+// and 15:14, expcnt 6:4, lgkmcnt 11:8.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+
+// Pair pr (buffer P) in two sub-steps.  On entry the wave holds the
+// fragments of sub-step 2pr (f0), buffer P is complete everywhere, and the
+// loads of pair pr+1 (buffer P^1) are in flight.
+//   first:  read sub-step 2pr+1 (buffer P) into f1; MFMAs on f0.
+//   second: wait for the own loads of pair pr+1, convert them if needed,
+//           barrier (pair pr+1 complete everywhere, every read of buffer P
+//           done), loads of pair pr+2 into buffer P (clamped to the last pair
+//           near the end: those loads are never read), read sub-step 2pr+2
+//           (buffer P^1) into f0, MFMAs on f1 with the loads and reads spread
+//           between them.
+template <int P, bool MX, int AT, int HM, int NBK>
+__device__ __forceinline__ void big_pair(const BigCtx &c, floatx16_t (&acc)[4][NBK], uint4 (&fa0)[8],
+                                         uint4 (&fb0)[2 * NBK], uint4 (&fa1)[8], uint4 (&fb1)[2 * NBK],
+                                         const int (&bcol)[NBK], int pr, int npair, int wave, int wm, int lane) {
+    const int lr = lane & 31, lh = lane >> 5;
+    constexpr bool CVT = kBigRegConvert<MX, AT>;
+    big_read<P, 1, NBK, CVT>(fa1, fb1, bcol, wm, lr, lh);
+    big_mma<AT, NBK>(acc, fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    if constexpr (kBigConvert<MX, AT>) big_convert<P ^ 1, MX, AT>(pr + 1, wave, lane);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    big_issue<P, MX, HM>(c, min(pr + 2, npair - 1), wave);
+    big_read<P ^ 1, 0, NBK, CVT>(fa0, fb0, bcol, wm, lr, lh);
+    big_mma<AT, NBK>(acc, fa1, fb1);
+    constexpr int NL = BigShape<MX, HM>::kPerPair, NR = 8 + 2 * NBK, NM = 8 * NBK;
 #pragma unroll
-        for (int m = 4; m < 8; ++m)
-#pragma unroll
-            for (int cc = 0; cc < NBK; ++cc) acc[m][cc] = mfma16x16x32<AT>(cur_b[cc], cur_a[m], acc[m][cc]);
-    } else {
-        big_mma<AT, NBK>(acc, cur_a, cur_b);
+    for (int i = 0; i < NL; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // direct-to-LDS load
     }
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - NL - NR > 0 ? NM - NL - NR : 0, 0);
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
 }
 
 template <int EPI, bool MX, bool GROUPED, int AT, int OT, int HM>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_big_kernel(GemmArgs a) {
-    constexpr int NBK = HM ? 4 : 8;      // 16-column blocks per wave
-    constexpr int NA = HM ? 2 : 4;       // A loads per wave per stage
+    constexpr int NBK = HM ? 2 : 4;       // 32-column blocks per wave
+    constexpr int NA = BigShape<MX, HM>::NA;
     constexpr int BM = HM ? kHalfBM : kBigBM;
+    constexpr int WCOLS = 32 * NBK;       // B rows per wave (SWIGLU: half gate, half up)
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = HM ? 0 : wave >> 1, wn = HM ? wave : wave & 1;
-    const int li = lane & 15, lg = lane >> 4;
-    constexpr int WCOLS = HM ? 64 : 128;  // output-space B rows per wave (SWIGLU: half gate, half up)
+    const int lr = lane & 31, lh = lane >> 5;
 
     const int64_t K = a.K;
     const int64_t nblocks = (EPI == EPI_SWIGLU) ? a.N / (kBigBN / 2) : a.N / kBigBN;
     const int ntiles = GROUPED ? *a.ntiles : (int)((a.M + BM - 1) / BM);
     const int64_t items = (int64_t)ntiles * nblocks;
-    const int nk = (int)(K / kBigBK);  // a multiple of 8
-    // Direct-load lane mapping of 64-byte rows: lane l fills row 16q + (l >> 2),
-    // physical chunk l & 3, i.e. logical chunk (l & 3) ^ ((l >> 3) & 3).
-    const int drow = lane >> 2, dchunk = (lane & 3) ^ ((lane >> 3) & 3);
+    const int npair = (int)(K / kBigBK);  // a multiple of 8
+    // Direct-load lane mapping of 128-byte rows: lane l fills row 8q + (l >> 3),
+    // physical chunk l & 7, i.e. logical chunk (l & 7) ^ ((l >> 4) & 3).
+    const int drow = lane >> 3, dchunk = (lane & 7) ^ ((lane >> 4) & 3);
 
+    // Tile B rows of this wave's column blocks.  SWIGLU: blocks c < NBK/2 are
+    // gate rows (0..127 of the tile), block c + NBK/2 the matching up rows.
     int bcol[NBK];
 #pragma unroll
     for (int c = 0; c < NBK; ++c) {
         if constexpr (EPI == EPI_SWIGLU)
-            bcol[c] = (c < NBK / 2) ? wn * (WCOLS / 2) + c * 16 : 128 + wn * (WCOLS / 2) + (c - NBK / 2) * 16;
+            bcol[c] = (c < NBK / 2) ? wn * (WCOLS / 2) + c * 32 : 128 + wn * (WCOLS / 2) + (c - NBK / 2) * 32;
         else
-            bcol[c] = wn * WCOLS + c * 16;
+            bcol[c] = wn * WCOLS + c * 32;
     }
 
     for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
@@ -502,127 +529,138 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
         c.A = (const uint8_t *)a.A;
 #pragma unroll
         for (int i = 0; i < NA; ++i) {
-            const int row = min(wave * (NA * 16) + i * 16 + drow, rt.mcount - 1);
+            const int row = min(wave * (NA * 8) + i * 8 + drow, rt.mcount - 1);
             const int64_t p = rt.p0 + row;
             const int64_t arow = a.a_gather ? (int64_t)a.a_gather[p] : p;
             c.aoff[i] = (uint32_t)((arow * a.lda + dchunk * 8) * 2);
         }
         // The tile's B rows 0..255: SWIGLU rows 0-127 are gate rows nb*128.., rows
         // 128-255 the matching up rows N + nb*128..; a lane loads tile rows
-        // 64*wave + 16i + drow (bf16) or 64*wave + lane (MXFP4).
+        // 64*wave + 8i + drow (bf16), codes of rows 64*wave + 32i + lane/2 and
+        // the scale word of row 64*wave + lane (MXFP4).
         const int64_t bfirst = brow0 + ((EPI == EPI_SWIGLU) ? nb * 128 : nb * kBigBN);
         const int64_t upskip = (EPI == EPI_SWIGLU) ? a.N - 128 : 0;  // rows 128.. sit this far further on
         auto brel = [&](int row) -> int64_t { return row + (row >= 128 ? upskip : 0); };
         if constexpr (MX) {
-            const int row = wave * 64 + lane;
             c.B = (const uint8_t *)a.B + bfirst * (K / 2);
             c.bsc = (const uint8_t *)a.B + a.b_rows_total * (K / 2) + bfirst * (K / 32);
-            c.boff[0] = (uint32_t)(brel(row) * (K / 2));
-            c.boff[1] = (uint32_t)(brel(row) * (K / 32));
-            c.boff[2] = c.boff[3] = 0;
+#pragma unroll
+            for (int i = 0; i < 2; ++i)
+                c.boff[i] = (uint32_t)(brel(wave * 64 + i * 32 + (lane >> 1)) * (K / 2) + (lane & 1) * 16);
+            c.boff[2] = (uint32_t)(brel(wave * 64 + lane) * (K / 32));
+#pragma unroll
+            for (int i = 3; i < 8; ++i) c.boff[i] = 0;
         } else {
             c.B = (const uint8_t *)((const uint16_t *)a.B + bfirst * K);
 #pragma unroll
-            for (int i = 0; i < 4; ++i) c.boff[i] = (uint32_t)((brel(wave * 64 + i * 16 + drow) * K + dchunk * 8) * 2);
+            for (int i = 0; i < 8; ++i) c.boff[i] = (uint32_t)((brel(wave * 64 + i * 8 + drow) * K + dchunk * 8) * 2);
             c.bsc = nullptr;
         }
+#pragma unroll
+        for (int i = NA; i < 8; ++i) c.aoff[i] = 0;
 
-        floatx4_t acc[8][NBK];
+        floatx16_t acc[4][NBK];
 #pragma unroll
-        for (int m = 0; m < 8; ++m)
+        for (int m = 0; m < 4; ++m)
 #pragma unroll
-            for (int cc = 0; cc < NBK; ++cc) acc[m][cc] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+            for (int cc = 0; cc < NBK; ++cc)
+#pragma unroll
+                for (int r = 0; r < 16; ++r) acc[m][cc][r] = 0.f;
 
         big_issue<0, MX, HM>(c, 0, wave);
         big_issue<1, MX, HM>(c, 1, wave);
-        big_issue<2, MX, HM>(c, 2, wave);
-        big_issue<3, MX, HM>(c, 3, wave);
-        if constexpr (kBigConvert<MX, AT>) {
-            BigWait<MX, HM>::keep2();
-            big_convert<0, MX, AT>(0, wave, lane);
-            big_convert<1, MX, AT>(1, wave, lane);
-            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        } else {
-            BigWait<MX, HM>::keep3();
-        }
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(BigShape<MX, HM>::kPerPair));
+        if constexpr (kBigConvert<MX, AT>) big_convert<0, MX, AT>(0, wave, lane);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         __builtin_amdgcn_s_barrier();
-        for (int kt = 0; kt < nk; kt += 8) {
-            // K-tile kt is complete for every wave (barrier above or step 7 below).
-            uint4 fa0[8], fb0[NBK], fa1[8], fb1[NBK];
-            big_read<0, NBK>(fa0, fb0, bcol, wm, li, lg);
+        {
+            uint4 fa0[8], fb0[2 * NBK], fa1[8], fb1[2 * NBK];
+            big_read<0, 0, NBK, kBigRegConvert<MX, AT>>(fa0, fb0, bcol, wm, lr, lh);
             __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-            big_step<0, MX, AT, HM, NBK>(c, acc, fa0, fb0, fa1, fb1, bcol, kt + 0, nk, wave, wm, lane);
-            big_step<1, MX, AT, HM, NBK>(c, acc, fa1, fb1, fa0, fb0, bcol, kt + 1, nk, wave, wm, lane);
-            big_step<2, MX, AT, HM, NBK>(c, acc, fa0, fb0, fa1, fb1, bcol, kt + 2, nk, wave, wm, lane);
-            big_step<3, MX, AT, HM, NBK>(c, acc, fa1, fb1, fa0, fb0, bcol, kt + 3, nk, wave, wm, lane);
-            big_step<4, MX, AT, HM, NBK>(c, acc, fa0, fb0, fa1, fb1, bcol, kt + 4, nk, wave, wm, lane);
-            big_step<5, MX, AT, HM, NBK>(c, acc, fa1, fb1, fa0, fb0, bcol, kt + 5, nk, wave, wm, lane);
-            big_step<6, MX, AT, HM, NBK>(c, acc, fa0, fb0, fa1, fb1, bcol, kt + 6, nk, wave, wm, lane);
-            big_step<7, MX, AT, HM, NBK>(c, acc, fa1, fb1, fa0, fb0, bcol, kt + 7, nk, wave, wm, lane);
+            for (int pr = 0; pr < npair; pr += 2) {
+                big_pair<0, MX, AT, HM, NBK>(c, acc, fa0, fb0, fa1, fb1, bcol, pr, npair, wave, wm, lane);
+                big_pair<1, MX, AT, HM, NBK>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 1, npair, wave, wm, lane);
+            }
         }
-        // Drain the clamped tail loads before the stages are refilled.
-        BigWait<MX, HM>::all();
+        // Drain the clamped tail loads before the buffers are refilled.
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
         __builtin_amdgcn_s_barrier();
 
-        // Epilogue: lane (li, lg) holds row wm*128 + 16m + li, columns
-        // bcol[c] + 4lg + q (q = 0..3) of every block.
+        // Epilogue: lane (lr, lh) holds, in block (m, c), output row
+        // wm*128 + 32m + lr and the tile columns bcol[c] + 8g + 4lh + q in
+        // register 4g + q (g, q = 0..3): four runs of four adjacent columns.
 #pragma unroll
-        for (int m = 0; m < 8; ++m) {
-            const int row = wm * 128 + m * 16 + li;
+        for (int m = 0; m < 4; ++m) {
+            const int row = wm * 128 + m * 32 + lr;
             const bool ok = row < rt.mcount;
             const int64_t p = rt.p0 + row;
             if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
                 for (int cc = 0; cc < NBK / 2; ++cc) {
-                    if (ok) {
-                        uint16_t h[4];
 #pragma unroll
-                        for (int q = 0; q < 4; ++q)
-                            h[q] = f32_to_act<OT>(silu(acc[m][cc][q]) * acc[m][cc + NBK / 2][q]);
-                        const int64_t j = nb * 128 + wn * (WCOLS / 2) + cc * 16 + lg * 4;
-                        *(uint2 *)((uint16_t *)a.C + p * a.ldc + j) =
-                            make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+                    for (int g = 0; g < 4; ++g) {
+                        if (ok) {
+                            uint16_t h[4];
+#pragma unroll
+                            for (int q = 0; q < 4; ++q)
+                                h[q] = f32_to_act<OT>(silu(acc[m][cc][4 * g + q]) * acc[m][cc + NBK / 2][4 * g + q]);
+                            const int64_t j = nb * 128 + bcol[cc] + 8 * g + 4 * lh;
+                            *(uint2 *)((uint16_t *)a.C + p * a.ldc + j) =
+                                make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+                        }
                     }
                 }
             } else {
 #pragma unroll
                 for (int cc = 0; cc < NBK; ++cc) {
-                    const int64_t n = nb * kBigBN + wn * WCOLS + cc * 16 + lg * 4;
-                    const floatx4_t v = acc[m][cc];
-                    if constexpr (EPI == EPI_F32) {
-                        if (ok) *(floatx4_t *)((float *)a.C + p * a.ldc + n) = v;
-                    } else if constexpr (EPI == EPI_ACT) {
-                        if (ok)
-                            *(uint2 *)((uint16_t *)a.C + p * a.ldc + n) =
-                                make_uint2(f32_to_act<OT>(v[0]) | ((uint32_t)f32_to_act<OT>(v[1]) << 16),
-                                           f32_to_act<OT>(v[2]) | ((uint32_t)f32_to_act<OT>(v[3]) << 16));
-                    } else if constexpr (EPI == EPI_NORM) {
-                        uint16_t h[4];
-                        float sq = 0.f;
+                    const int64_t n0 = nb * kBigBN + bcol[cc];
+                    float sq[2] = {0.f, 0.f};  // EPI_NORM: sums of squares of the two 16-column halves
 #pragma unroll
-                        for (int q = 0; q < 4; ++q) {
-                            const float gsc = a.gamma ? 1.0f + a.gamma[n + q] : 1.0f;
-                            h[q] = f32_to_bf16(gsc * v[q]);
-                            const float e = a.norm_round ? bf16_to_f32(h[q]) : v[q];
-                            sq += e * e;
+                    for (int g = 0; g < 4; ++g) {
+                        const int64_t n = n0 + 8 * g + 4 * lh;
+                        floatx4_t v;
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) v[q] = acc[m][cc][4 * g + q];
+                        if constexpr (EPI == EPI_F32) {
+                            if (ok) *(floatx4_t *)((float *)a.C + p * a.ldc + n) = v;
+                        } else if constexpr (EPI == EPI_ACT) {
+                            if (ok)
+                                *(uint2 *)((uint16_t *)a.C + p * a.ldc + n) =
+                                    make_uint2(f32_to_act<OT>(v[0]) | ((uint32_t)f32_to_act<OT>(v[1]) << 16),
+                                               f32_to_act<OT>(v[2]) | ((uint32_t)f32_to_act<OT>(v[3]) << 16));
+                        } else if constexpr (EPI == EPI_NORM) {
+                            uint16_t h[4];
+#pragma unroll
+                            for (int q = 0; q < 4; ++q) {
+                                const float gsc = a.gamma ? 1.0f + a.gamma[n + q] : 1.0f;
+                                h[q] = f32_to_bf16(gsc * v[q]);
+                                const float e = a.norm_round ? bf16_to_f32(h[q]) : v[q];
+                                sq[g >> 1] += e * e;
+                            }
+                            if (ok)
+                                *(uint2 *)((uint16_t *)a.C + p * a.ldc + n) =
+                                    make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
+                        } else {  // EPI_RESID
+                            if (ok) {
+                                const uint2 hx = *(const uint2 *)(a.resid + p * a.N + n);
+                                const float4 gt = *(const float4 *)(a.gate + n);
+                                floatx4_t o;
+                                o[0] = bf16_to_f32((uint16_t)hx.x) + gt.x * v[0];
+                                o[1] = bf16_to_f32((uint16_t)(hx.x >> 16)) + gt.y * v[1];
+                                o[2] = bf16_to_f32((uint16_t)hx.y) + gt.z * v[2];
+                                o[3] = bf16_to_f32((uint16_t)(hx.y >> 16)) + gt.w * v[3];
+                                *(floatx4_t *)((float *)a.C + p * a.ldc + n) = o;
+                                if (a.y) *(floatx4_t *)(a.y + p * a.N + n) = v;
+                            }
                         }
-                        if (ok)
-                            *(uint2 *)((uint16_t *)a.C + p * a.ldc + n) =
-                                make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
-                        sq += __shfl_xor(sq, 16, 64);
-                        sq += __shfl_xor(sq, 32, 64);
-                        if (ok && lg == 0) a.ssq[p * a.nparts + nb * 16 + wn * (WCOLS / 16) + cc] = sq;
-                    } else {  // EPI_RESID
-                        if (ok) {
-                            const uint2 hx = *(const uint2 *)(a.resid + p * a.N + n);
-                            const float4 g = *(const float4 *)(a.gate + n);
-                            floatx4_t o;
-                            o[0] = bf16_to_f32((uint16_t)hx.x) + g.x * v[0];
-                            o[1] = bf16_to_f32((uint16_t)(hx.x >> 16)) + g.y * v[1];
-                            o[2] = bf16_to_f32((uint16_t)hx.y) + g.z * v[2];
-                            o[3] = bf16_to_f32((uint16_t)(hx.y >> 16)) + g.w * v[3];
-                            *(floatx4_t *)((float *)a.C + p * a.ldc + n) = o;
-                            if (a.y) *(floatx4_t *)(a.y + p * a.N + n) = v;
+                    }
+                    if constexpr (EPI == EPI_NORM) {
+                        // lanes lr and lr + 32 hold the other columns of each 16-column half
+                        sq[0] += __shfl_xor(sq[0], 32, 64);
+                        sq[1] += __shfl_xor(sq[1], 32, 64);
+                        if (ok && lh == 0) {
+                            a.ssq[p * a.nparts + n0 / 16] = sq[0];
+                            a.ssq[p * a.nparts + n0 / 16 + 1] = sq[1];
                         }
                     }
                 }
