@@ -52,17 +52,24 @@ def recorded_traffic(name: str):
     """HBM bytes per launch of a kernel from a committed rocprofv3 counter
     record under profiles/, or None when the kernel sources changed since
     the counters were taken."""
-    import hashlib
     path = os.path.join(ROOT, "profiles", name)
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
-    h = hashlib.sha256()
-    for f in ("gemm.hip", "gemm.h", "common.h"):
-        h.update(open(os.path.join(ROOT, "sparse_mixture_experts_router_amd", "csrc", f), "rb").read())
-    if h.hexdigest()[:16] != rec.get("source_sha256_16"):
+    if csrc_hash() != rec.get("source_sha256_16"):
         return None
     return rec["traffic_bytes"]
+
+
+def csrc_hash() -> str:
+    """Digest of the kernel sources (all of csrc/, in name order)."""
+    import glob
+    import hashlib
+    h = hashlib.sha256()
+    for f in sorted(glob.glob(os.path.join(ROOT, "sparse_mixture_experts_router_amd", "csrc", "*"))):
+        if f.endswith((".hip", ".h")):
+            h.update(open(f, "rb").read())
+    return h.hexdigest()[:16]
 
 
 def main():
@@ -210,6 +217,7 @@ def main():
         tf = fl2["total"] / (r2["ms"] * 1e-3) / 1e12
         g1 = r2["stages"]["gemm1"]
         g1_tf = fl2["gemm1"] / (g1 * 1e-3) / 1e12
+        by2 = layer_bytes(p2, r2["counts"])
         log("prefill T=%d: %.3f ms/step, %.0f tok/s, %.1f TFLOP/s; stages %s" % (
             p2.chunk_T, r2["ms"], p2.chunk_T / (r2["ms"] * 1e-3), tf, {k: round(v, 4) for k, v in r2["stages"].items()}))
         result["secondary"] = {
@@ -217,10 +225,16 @@ def main():
             "unit": "tokens/s", "ms_per_step": round(r2["ms"], 4), "steps": args.prefill_steps,
             "layer_TFLOPs": round(tf, 1), "layer_frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
             "stage_ms": {k: round(v, 4) for k, v in r2["stages"].items()},
-            "roofline": {"kernel": "gemm_tile_kernel (grouped GEMM1 + SwiGLU)", "bound": "mfma",
-                         "achieved": round(g1_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "roofline": {"kernel": "gemm_big_kernel (grouped GEMM1 + SwiGLU; full- and half-height tile launches)",
+                         "bound": "mfma", "achieved": round(g1_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
                          "frac": round(g1_tf / BF16_PEAK_TFLOPS, 4), "flops_per_launch": fl2["gemm1"],
-                         "avg_launch_ms": round(g1, 4)}}
+                         "avg_launch_ms": round(g1, 4),
+                         "traffic": recorded_traffic("prefill_T8192_gemm1_traffic.json"),
+                         # at ~256 rows per expert GEMM1 does ~256 FLOP per weight byte, below the
+                         # chip's ~312 FLOP/B balance: the weight stream bounds it as well
+                         "hbm_view": {"weight_and_row_bytes": by2["gemm1"],
+                                      "achieved_GBps": round(by2["gemm1"] / (g1 * 1e-3) / 1e9, 1),
+                                      "frac": round(by2["gemm1"] / (g1 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}}
 
     # ---- CPU oracle baseline on a bounded sample of the decode workload ----
     if not args.no_cpu_baseline:
