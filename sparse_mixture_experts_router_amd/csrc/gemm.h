@@ -57,11 +57,12 @@ struct GemmArgs {
 
 constexpr int kTileBM = 256;      // rows per tile of the large-tile kernel (and of its grouped lists)
 constexpr int kHalfBM = 128;      // rows per tile of its half-height variant (expert remainders)
+constexpr int kTallBM = 384;      // rows of its tall variant (one tile for an expert with 257..384 rows)
 constexpr int kTileBN = 256;      // B rows per tile (SWIGLU: 128 gate + 128 up -> 128 outputs)
 constexpr int kSmallBM = 16;      // rows per tile of the streaming kernel's grouped lists
 
 // Kernel choice for a launch.
-enum GemmPath : int { PATH_STREAM = 0, PATH_TILE = 1, PATH_HALF = 2 };
+enum GemmPath : int { PATH_STREAM = 0, PATH_TILE = 1, PATH_HALF = 2, PATH_TALL = 3 };
 
 // Router logits: dense, A = u (bf16), B = router weight (bf16), fp32 out.
 hipError_t launch_router_gemm(const GemmArgs &a, int path, hipStream_t s);

@@ -37,14 +37,15 @@ struct Carve {
 
 struct Layout {
     size_t u, logits, idx, w, counts, offsets, perm_tok, perm_slot, pos, ntiles, tiles_small, tiles_big, tiles_half;
-    size_t perm_scratch, z, act, S, ssq, m;
-    int64_t max_small, max_big, max_half;
+    size_t tiles_tall, perm_scratch, z, act, S, ssq, m;
+    int64_t max_small, max_big, max_half, max_tall;
     size_t total;
 };
 
 int64_t small_tile_cap(int64_t TK, int64_t n) { return TK / kSmallBM + n + 1; }
 int64_t big_tile_cap(int64_t TK, int64_t n) { return TK / kTileBM + n + 1; }
 int64_t half_tile_cap(int64_t n) { return n; }  // at most one per expert
+int64_t tall_tile_cap(int64_t n) { return n; }  // at most one per expert
 
 Layout make_layout(const moe_desc *d) {
     Layout L;
@@ -63,13 +64,15 @@ Layout make_layout(const moe_desc *d) {
     L.perm_tok = c.take((size_t)TK * 4);
     L.perm_slot = c.take((size_t)TK * 4);
     L.pos = c.take((size_t)TK * 4);
-    L.ntiles = c.take(3 * 4);
+    L.ntiles = c.take(4 * 4);
     L.max_small = small_tile_cap(TK, n);
     L.max_big = big_tile_cap(TK, n);
     L.max_half = half_tile_cap(n);
+    L.max_tall = tall_tile_cap(n);
     L.tiles_small = c.take((size_t)L.max_small * sizeof(TileEntry));
     L.tiles_big = c.take((size_t)L.max_big * sizeof(TileEntry));
     L.tiles_half = c.take((size_t)L.max_half * sizeof(TileEntry));
+    L.tiles_tall = c.take((size_t)L.max_tall * sizeof(TileEntry));
     L.perm_scratch = c.take((size_t)permute_scratch_ints(T, (int)n) * 4);
     L.z = d->d_latent ? c.take((size_t)T * d->d_latent * 2) : 0;
     L.act = c.take((size_t)TK * d->d_ff * ab);
@@ -162,7 +165,7 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
     int32_t *perm_tok = (int32_t *)(ws + L.perm_tok), *perm_slot = (int32_t *)(ws + L.perm_slot);
     int32_t *pos = (int32_t *)(ws + L.pos), *ntiles = (int32_t *)(ws + L.ntiles);
     TileEntry *tiles_small = (TileEntry *)(ws + L.tiles_small), *tiles_big = (TileEntry *)(ws + L.tiles_big);
-    TileEntry *tiles_half = (TileEntry *)(ws + L.tiles_half);
+    TileEntry *tiles_half = (TileEntry *)(ws + L.tiles_half), *tiles_tall = (TileEntry *)(ws + L.tiles_tall);
     int32_t *perm_scratch = (int32_t *)(ws + L.perm_scratch);
     uint16_t *z = (uint16_t *)(ws + L.z), *act = (uint16_t *)(ws + L.act), *S = (uint16_t *)(ws + L.S);
     uint16_t *m = (uint16_t *)(ws + L.m);
@@ -197,7 +200,7 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
     const bool any_big = T > small_max;
     MOE_TRY_RC(ev.begin(MOE_STAGE_PERMUTE));
     MOE_TRY(launch_permute(idx, T, (int)k, (int)n, counts, offsets, perm_tok, perm_slot, pos, tiles_small, tiles_big,
-                           tiles_half, ntiles, small_max, perm_scratch, s));
+                           tiles_half, tiles_tall, ntiles, small_max, perm_scratch, s));
     MOE_TRY_RC(ev.end(MOE_STAGE_PERMUTE));
 
     // z = u W_d^T (bf16).
@@ -249,6 +252,10 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
             g.ntiles = ntiles + 2;
             g.max_tiles = (int32_t)L.max_half;
             MOE_TRY(launch_gemm1(g, PATH_HALF, mx, at, s));
+            g.tiles = tiles_tall;
+            g.ntiles = ntiles + 3;
+            g.max_tiles = (int32_t)L.max_tall;
+            MOE_TRY(launch_gemm1(g, PATH_TALL, mx, at, s));
         }
     }
     MOE_TRY_RC(ev.end(MOE_STAGE_GEMM1));
@@ -285,6 +292,10 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
             g.ntiles = ntiles + 2;
             g.max_tiles = (int32_t)L.max_half;
             MOE_TRY(launch_gemm2(g, PATH_HALF, mx, at, norm2, s));
+            g.tiles = tiles_tall;
+            g.ntiles = ntiles + 3;
+            g.max_tiles = (int32_t)L.max_tall;
+            MOE_TRY(launch_gemm2(g, PATH_TALL, mx, at, norm2, s));
         }
     }
     MOE_TRY_RC(ev.end(MOE_STAGE_GEMM2));
@@ -358,7 +369,7 @@ int forward_f32(const moe_desc *d, const void *x, const void *router_w, const vo
     MOE_TRY_RC(ev.end(MOE_STAGE_TOPK));
     MOE_TRY_RC(ev.begin(MOE_STAGE_PERMUTE));
     MOE_TRY(launch_permute(idx, T, (int)k, (int)n, counts, offsets, perm_tok, perm_slot, pos, nullptr, nullptr,
-                           nullptr, nullptr, 0, (int32_t *)(ws + L.perm_scratch), s));
+                           nullptr, nullptr, nullptr, 0, (int32_t *)(ws + L.perm_scratch), s));
     MOE_TRY_RC(ev.end(MOE_STAGE_PERMUTE));
     MOE_TRY_RC(ev.begin(MOE_STAGE_GEMM1));
     MOE_TRY(launch_expert1_f32((const float *)x, (const float *)w1, perm_tok, offsets, (int)n, TK, F, D,
@@ -474,7 +485,7 @@ int moe_permute(int64_t T, int64_t k, int64_t n, const int32_t *topk_idx, int32_
     if (!topk_idx || !counts || !offsets || !perm_tok || !perm_slot || !pos) return MOE_ERR_INVALID_ARG;
     hipStream_t s = as_stream(stream);
     MOE_TRY(launch_permute(topk_idx, T, (int)k, (int)n, counts, offsets, perm_tok, perm_slot, pos, nullptr, nullptr,
-                           nullptr, nullptr, 0, nullptr, s));
+                           nullptr, nullptr, nullptr, 0, nullptr, s));
     return MOE_OK;
 }
 

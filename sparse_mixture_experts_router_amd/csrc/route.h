@@ -13,17 +13,18 @@ hipError_t launch_rmsnorm(const uint16_t *x, const float *gamma, uint16_t *u, in
 hipError_t launch_topk(const float *logits, const float *bias, int64_t T, int n, int k, int bias_in_weights,
                        int32_t *idx, float *w, hipStream_t s);
 // Experts with 1..small_max tokens go to the small-tile list (kSmallBM rows
-// per tile), heavier ones to the big-tile list (kTileBM rows per tile) and,
-// for a remainder of at most kHalfBM rows, the half-tile list.  ntiles[0..2]
-// receive the three list lengths.  With scratch (permute_scratch_ints(T, n)
+// per tile).  Heavier ones get one tile when it holds them (half-height list
+// up to kHalfBM rows, full list up to kTileBM, tall list up to kTallBM), else
+// full tiles of kTileBM rows plus, for a remainder of at most kHalfBM rows,
+// a half-height tile.  ntiles[0..3] receive the four list lengths.  With scratch (permute_scratch_ints(T, n)
 // ints) and T >= kPermMultiMinT the work spreads over chunks of tokens;
 // otherwise one workgroup does it.
 constexpr int64_t kPermMultiMinT = 1024;
 int64_t permute_scratch_ints(int64_t T, int n);
 hipError_t launch_permute(const int32_t *idx, int64_t T, int k, int n, int32_t *counts, int32_t *offsets,
                           int32_t *perm_tok, int32_t *perm_slot, int32_t *pos, TileEntry *tiles_small,
-                          TileEntry *tiles_big, TileEntry *tiles_half, int32_t *ntiles, int small_max,
-                          int32_t *scratch, hipStream_t s);
+                          TileEntry *tiles_big, TileEntry *tiles_half, TileEntry *tiles_tall, int32_t *ntiles,
+                          int small_max, int32_t *scratch, hipStream_t s);
 // m in activation type `ot` (ACT_BF16 / ACT_F16).
 hipError_t launch_combine(const uint16_t *S, const float *ssq, const int32_t *pos, const float *w, int64_t T,
                           int64_t L, int nparts, float eps, int k, int ot, uint16_t *m, hipStream_t s);

@@ -191,38 +191,50 @@ __device__ __forceinline__ void scan256_excl(int *a, int n) {  // in-place exclu
 }
 
 // Tile lists of the grouped GEMMs for an expert with c rows: 1..small_max
-// rows -> small tiles of kSmallBM rows; more -> c / kTileBM full tiles, and
-// for a remainder r one more full tile when r > kHalfBM or one half-height
-// tile when 0 < r <= kHalfBM.
-__device__ __forceinline__ void tile_counts(int c, int small_max, int &ns, int &nb, int &nh) {
+// rows -> small tiles of kSmallBM rows.  More rows -> a single tile when it
+// holds them (half-height up to kHalfBM rows, full up to kTileBM, tall up to
+// kTallBM), so the expert's weights stream once; beyond that c / kTileBM
+// full tiles, and for a remainder r one more full tile when r > kHalfBM or
+// one half-height tile when 0 < r <= kHalfBM.
+__device__ __forceinline__ void tile_counts(int c, int small_max, int &ns, int &nb, int &nh, int &nt) {
     ns = (c > 0 && c <= small_max) ? (c + kSmallBM - 1) / kSmallBM : 0;
-    nb = nh = 0;
+    nb = nh = nt = 0;
     if (c > small_max) {
-        const int full = c / kTileBM, r = c - full * kTileBM;
-        nb = full + (r > kHalfBM ? 1 : 0);
-        nh = (r > 0 && r <= kHalfBM) ? 1 : 0;
+        if (c <= kHalfBM) {
+            nh = 1;
+        } else if (c <= kTileBM) {
+            nb = 1;
+        } else if (c <= kTallBM) {
+            nt = 1;
+        } else {
+            const int full = c / kTileBM, r = c - full * kTileBM;
+            nb = full + (r > kHalfBM ? 1 : 0);
+            nh = (r > 0 && r <= kHalfBM) ? 1 : 0;
+        }
     }
 }
 
 // Counts, offsets and the three tile lists from per-expert counts cnt[0..n)
 // in LDS.  off/ts/tb/th: LDS scratch of 257 entries.  Every thread of the
 // workgroup (>= 256) must call it.
-__device__ void publish_counts(const int *cnt, int *off, int *ts, int *tb, int *th, int n, int small_max,
+__device__ void publish_counts(const int *cnt, int *off, int *ts, int *tb, int *th, int *tt, int n, int small_max,
                                int32_t *counts, int32_t *offsets, TileEntry *tiles_small, TileEntry *tiles_big,
-                               TileEntry *tiles_half, int32_t *ntiles) {
+                               TileEntry *tiles_half, TileEntry *tiles_tall, int32_t *ntiles) {
     const int tid = threadIdx.x;
     if (tid < n) {
-        int ns, nb, nh;
-        tile_counts(cnt[tid], small_max, ns, nb, nh);
+        int ns, nb, nh, nt;
+        tile_counts(cnt[tid], small_max, ns, nb, nh, nt);
         off[tid] = cnt[tid];
         ts[tid] = ns;
         tb[tid] = nb;
         th[tid] = nh;
+        tt[tid] = nt;
     }
     scan256_excl(off, n);
     scan256_excl(ts, n);
     scan256_excl(tb, n);
     scan256_excl(th, n);
+    scan256_excl(tt, n);
     if (tid < n) {
         const int c = cnt[tid];
         counts[tid] = c;
@@ -231,7 +243,10 @@ __device__ void publish_counts(const int *cnt, int *off, int *ts, int *tb, int *
             for (int q = 0; q < ts[tid + 1] - ts[tid]; ++q) tiles_small[ts[tid] + q] = TileEntry{tid, q * kSmallBM};
         if (tiles_big)
             for (int q = 0; q < tb[tid + 1] - tb[tid]; ++q) tiles_big[tb[tid] + q] = TileEntry{tid, q * kTileBM};
-        if (tiles_half && th[tid + 1] > th[tid]) tiles_half[th[tid]] = TileEntry{tid, (c / kTileBM) * kTileBM};
+        // a half-height tile holds either the whole expert or its remainder after the full tiles
+        if (tiles_half && th[tid + 1] > th[tid])
+            tiles_half[th[tid]] = TileEntry{tid, c <= kHalfBM ? 0 : (c / kTileBM) * kTileBM};
+        if (tiles_tall && tt[tid + 1] > tt[tid]) tiles_tall[tt[tid]] = TileEntry{tid, 0};
     }
     if (tid == 0) {
         offsets[n] = off[n];
@@ -239,6 +254,7 @@ __device__ void publish_counts(const int *cnt, int *off, int *ts, int *tb, int *
             ntiles[0] = ts[n];
             ntiles[1] = tb[n];
             ntiles[2] = th[n];
+            ntiles[3] = tt[n];
         }
     }
     __syncthreads();
@@ -251,8 +267,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__
                                                                int32_t *__restrict__ perm_slot,
                                                                int32_t *__restrict__ pos, TileEntry *tiles_small,
                                                                TileEntry *tiles_big, TileEntry *tiles_half,
-                                                               int32_t *ntiles, int small_max) {
-    __shared__ int cnt[257], off[257], ts[257], tb[257], th[257], base[256];
+                                                               TileEntry *tiles_tall, int32_t *ntiles, int small_max) {
+    __shared__ int cnt[257], off[257], ts[257], tb[257], th[257], tt[257], base[256];
     __shared__ unsigned mask[256][kPermWords];
     const int tid = threadIdx.x;
     if (tid < 257) cnt[tid] = 0;
@@ -261,7 +277,8 @@ __global__ __launch_bounds__(kPermThreads) void permute_kernel(const int32_t *__
     const int64_t TK = T * k;
     for (int64_t i = tid; i < TK; i += kPermThreads) atomicAdd(&cnt[idx[i]], 1);
     __syncthreads();
-    publish_counts(cnt, off, ts, tb, th, n, small_max, counts, offsets, tiles_small, tiles_big, tiles_half, ntiles);
+    publish_counts(cnt, off, ts, tb, th, tt, n, small_max, counts, offsets, tiles_small, tiles_big, tiles_half,
+                   tiles_tall, ntiles);
     for (int64_t c0 = 0; c0 < T; c0 += kPermThreads) {
         for (int i = tid; i < 256 * kPermWords; i += kPermThreads) (&mask[0][0])[i] = 0u;
         __syncthreads();
@@ -314,9 +331,9 @@ __global__ __launch_bounds__(kChunkTok) void perm_count_kernel(const int32_t *__
 __global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t *__restrict__ wg_counts, int G, int n,
                                                         int32_t *__restrict__ wg_base, int32_t *__restrict__ counts,
                                                         int32_t *__restrict__ offsets, TileEntry *tiles_small,
-                                                        TileEntry *tiles_big, TileEntry *tiles_half, int32_t *ntiles,
-                                                        int small_max) {
-    __shared__ int cnt[257], off[257], ts[257], tb[257], th[257];
+                                                        TileEntry *tiles_big, TileEntry *tiles_half,
+                                                        TileEntry *tiles_tall, int32_t *ntiles, int small_max) {
+    __shared__ int cnt[257], off[257], ts[257], tb[257], th[257], tt[257];
     const int tid = threadIdx.x;
     if (tid < n) {
         int run = 0;
@@ -328,7 +345,8 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t *__restric
         cnt[tid] = run;
     }
     __syncthreads();
-    publish_counts(cnt, off, ts, tb, th, n, small_max, counts, offsets, tiles_small, tiles_big, tiles_half, ntiles);
+    publish_counts(cnt, off, ts, tb, th, tt, n, small_max, counts, offsets, tiles_small, tiles_big, tiles_half,
+                   tiles_tall, ntiles);
     if (tid < n) {
         const int o = off[tid];
         for (int g = 0; g < G; ++g) wg_base[(int64_t)g * n + tid] += o;
@@ -534,18 +552,18 @@ int64_t permute_scratch_ints(int64_t T, int n) { return 2 * ((T + kChunkTok - 1)
 
 hipError_t launch_permute(const int32_t *idx, int64_t T, int k, int n, int32_t *counts, int32_t *offsets,
                           int32_t *perm_tok, int32_t *perm_slot, int32_t *pos, TileEntry *tiles_small,
-                          TileEntry *tiles_big, TileEntry *tiles_half, int32_t *ntiles, int small_max,
-                          int32_t *scratch, hipStream_t s) {
+                          TileEntry *tiles_big, TileEntry *tiles_half, TileEntry *tiles_tall, int32_t *ntiles,
+                          int small_max, int32_t *scratch, hipStream_t s) {
     if (!scratch || T < kPermMultiMinT) {
         permute_kernel<<<1, kPermThreads, 0, s>>>(idx, T, k, n, counts, offsets, perm_tok, perm_slot, pos,
-                                                  tiles_small, tiles_big, tiles_half, ntiles, small_max);
+                                                  tiles_small, tiles_big, tiles_half, tiles_tall, ntiles, small_max);
         return hipGetLastError();
     }
     const int G = (int)((T + kChunkTok - 1) / kChunkTok);
     int32_t *wg_counts = scratch, *wg_base = scratch + (int64_t)G * n;
     perm_count_kernel<<<G, kChunkTok, 0, s>>>(idx, T, k, n, wg_counts);
     perm_scan_kernel<<<1, 256, 0, s>>>(wg_counts, G, n, wg_base, counts, offsets, tiles_small, tiles_big, tiles_half,
-                                       ntiles, small_max);
+                                       tiles_tall, ntiles, small_max);
     perm_scatter_kernel<<<G, kChunkTok, 0, s>>>(idx, T, k, n, wg_base, perm_tok, perm_slot, pos);
     return hipGetLastError();
 }
