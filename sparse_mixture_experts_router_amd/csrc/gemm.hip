@@ -351,9 +351,9 @@ struct BigCtx {
 };
 
 // Cache policy of the weight loads: every weight block is read once, and
-// the sc1 (streaming) policy moves them measurably faster (7.0 vs 6.2 TB/s
+// the non-temporal (nt) policy moves them measurably faster (7.0 vs 6.2 TB/s
 // for a pure weight stream on this chip).
-constexpr int kStreamPolicy = 2;
+constexpr int kStreamPolicy = 2;  // nt
 
 // Direct-to-LDS loads of K pair pr into buffer P.
 template <int P, bool MX, int TM>
