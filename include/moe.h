@@ -81,7 +81,13 @@ enum {
  *   act_dtype    dtype of x: MOE_DT_BF16 or MOE_DT_F32
  *   router_dtype dtype of router_w [n][d]; logits are always fp32
  *   weight_dtype dtype of down_w, expert_w1, expert_w2, up_w:
- *                F32, BF16 or MXFP4.  An MXFP4 matrix [R][K] is one buffer:
+ *                F32, BF16, MXFP4, or F16: expert_w1, expert_w2 and up_w
+ *                stored as IEEE fp16 and down_w as bf16 (the fp16 GEMMs
+ *                then read their weights without converting them; a bf16
+ *                checkpoint converts with moe_convert_bf16_to_f16, which
+ *                changes no value in [2^-17, 65504], so the layer's results
+ *                equal those of the BF16 format; needs fp16 intermediates).
+ *                An MXFP4 matrix [R][K] is one buffer:
  *                R*K/2 bytes of E2M1 codes (row-major, low nibble = even
  *                element) followed by R*K/32 E8M0 scale bytes ([R][K/32]),
  *                one per 32 consecutive elements along K (OCP MX v1.0);
@@ -231,6 +237,18 @@ int moe_router_topk(const moe_desc *desc, const void *u, const void *router_w, c
  */
 int moe_permute(int64_t T, int64_t k, int64_t n, const int32_t *topk_idx, int32_t *counts, int32_t *offsets,
                 int32_t *perm_tok, int32_t *perm_slot, int32_t *pos, void *stream);
+
+/*
+ * Weight conversion for weight_dtype MOE_DT_F16: count bf16 values at src
+ * become IEEE fp16 values at dst, rounded to nearest even: exact for
+ * magnitudes in [2^-17, 65504] (a bf16 value has 8 significant bits),
+ * smaller ones round to an fp16 subnormal or zero, larger ones overflow to
+ * +-inf, NaN stays NaN.  This is the conversion the fp16 GEMMs apply to
+ * bf16 weights as they read them.  count is a multiple of 8, both pointers
+ * are 16-byte aligned device pointers, dst == src converts in place (other
+ * overlaps are rejected).  Returns MOE_ERR_INVALID_ARG on a bad argument.
+ */
+int moe_convert_bf16_to_f16(const void *src, void *dst, int64_t count, void *stream);
 
 /*
  * Plain device copy dst = src of `bytes` bytes (a multiple of 16; both

@@ -8,7 +8,8 @@ import of any entry point raises.
 
 Names follow the C ABI: ``moe_layer_forward``, ``moe_workspace_bytes``,
 ``moe_validate``, ``moe_error_string``, ``moe_router_topk``,
-``moe_router_workspace_bytes``, ``moe_permute``.
+``moe_router_workspace_bytes``, ``moe_permute``, ``moe_convert_bf16_to_f16``,
+``moe_hbm_copy``.
 """
 from __future__ import annotations
 
@@ -78,12 +79,13 @@ def lib() -> ctypes.CDLL:
         L.moe_router_topk.argtypes = [ctypes.POINTER(moe_desc), vp, vp, vp, vp, vp, vp, vp, sz, vp]
         L.moe_permute.argtypes = [i64, i64, i64, vp, vp, vp, vp, vp, vp, vp]
         L.moe_hbm_copy.argtypes = [vp, vp, sz, vp]
+        L.moe_convert_bf16_to_f16.argtypes = [vp, vp, i64, vp]
         _lib = L
     return _lib
 
 
 EXPORTED = ["moe_error_string", "moe_validate", "moe_workspace_bytes", "moe_layer_forward",
-            "moe_router_workspace_bytes", "moe_router_topk", "moe_permute", "moe_hbm_copy"]
+            "moe_router_workspace_bytes", "moe_router_topk", "moe_permute", "moe_convert_bf16_to_f16", "moe_hbm_copy"]
 
 
 def make_desc(T, d_model, d_latent, n_experts, top_k, d_ff, expert_kind="swiglu3", act="bf16", router="bf16",
@@ -204,6 +206,14 @@ def moe_permute(T, k, n, topk_idx, counts, offsets, perm_tok, perm_slot, pos, st
                            _stream(stream))
     if rc != MOE_OK:
         raise MoeError(rc, "moe_permute")
+
+
+def moe_convert_bf16_to_f16(src, dst, count: int, stream=None):
+    """bf16 -> fp16 (round to nearest even) of `count` values; dst may be src."""
+    rc = lib().moe_convert_bf16_to_f16(_ptr(src, "src", 2 * count), _ptr(dst, "dst", 2 * count), count,
+                                       _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_convert_bf16_to_f16")
 
 
 def moe_hbm_copy(dst, src, nbytes: int, stream=None):

@@ -37,7 +37,7 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_ca
 // D[4*(l/16) + r][l%16] in element r.
 template <int AT>
 __device__ __forceinline__ floatx4_t mfma16x16x32(uint4 a, uint4 b, floatx4_t c) {
-    if constexpr (AT == ACT_F16)
+    if constexpr (AT != ACT_BF16)
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
                                                       c, 0, 0, 0);
     else
@@ -50,7 +50,7 @@ __device__ __forceinline__ floatx4_t mfma16x16x32(uint4 a, uint4 b, floatx4_t c)
 // shape (the 16x16x32 one needs two waves per SIMD for that).
 template <int AT>
 __device__ __forceinline__ floatx16_t mfma32x32x16(uint4 a, uint4 b, floatx16_t c) {
-    if constexpr (AT == ACT_F16)
+    if constexpr (AT != ACT_BF16)
         return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
                                                       c, 0, 0, 0);
     else
@@ -60,28 +60,33 @@ __device__ __forceinline__ floatx16_t mfma32x32x16(uint4 a, uint4 b, floatx16_t 
 // fp32 -> activation bits (round to nearest even; fp16 overflows to inf).
 template <int AT>
 __device__ __forceinline__ uint16_t f32_to_act(float f) {
+    static_assert(AT == ACT_BF16 || AT == ACT_F16, "a storage type");
     if constexpr (AT == ACT_F16) return __builtin_bit_cast(uint16_t, (_Float16)f);
     else return f32_to_bf16(f);
 }
 
 template <int AT>
 __device__ __forceinline__ float act_to_f32(uint16_t b) {
+    static_assert(AT == ACT_BF16 || AT == ACT_F16, "a storage type");
     if constexpr (AT == ACT_F16) return (float)__builtin_bit_cast(_Float16, b);
     else return bf16_to_f32(b);
 }
 
-// Eight bf16 -> eight fp16.  Exact for |w| in [2^-17, 65504]: a bf16 value
-// has 8 significant bits and fp16 11, so nothing is rounded in that range.
+// Eight bf16 -> eight fp16, rounded to nearest even.  Exact for |w| in
+// [2^-17, 65504]: a bf16 value has 8 significant bits and fp16 11, so
+// nothing is rounded in that range; smaller values round to an fp16
+// subnormal, larger ones overflow to inf.
 __device__ __forceinline__ uint32_t bf16x2_to_f16x2(uint32_t v) {
-    float lo = __uint_as_float(v << 16), hi = __uint_as_float(v & 0xffff0000u);
-    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(lo, hi));
+    const float lo = __uint_as_float(v << 16), hi = __uint_as_float(v & 0xffff0000u);
+    const f16x2_t r = {(_Float16)lo, (_Float16)hi};  // one v_cvt_pk_f16_f32
+    return __builtin_bit_cast(uint32_t, r);
 }
 __device__ __forceinline__ uint4 bf16x8_to_f16x8(uint4 v) {
     return make_uint4(bf16x2_to_f16x2(v.x), bf16x2_to_f16x2(v.y), bf16x2_to_f16x2(v.z), bf16x2_to_f16x2(v.w));
 }
 
-// Weight operand in the activation type: bf16 weights pass through or are
-// converted to fp16.
+// Weight operand in the MFMA type: bf16 weights pass through (bf16 GEMM)
+// or are converted to fp16; fp16 weights pass through.
 template <int AT>
 __device__ __forceinline__ uint4 weight_bf16_as(uint4 v) {
     if constexpr (AT == ACT_F16) return bf16x8_to_f16x8(v);
@@ -92,6 +97,7 @@ __device__ __forceinline__ uint4 weight_bf16_as(uint4 v) {
 // bf16 or fp16 (exact whenever the product is representable).
 template <int AT>
 __device__ __forceinline__ uint4 mxfp4x8_to_act(uint32_t codes, uint32_t e8m0) {
+    static_assert(AT == ACT_BF16 || AT == ACT_F16, "MXFP4 weights are decoded to bf16 or fp16");
     float scale = e8m0 ? __uint_as_float(e8m0 << 23) : __uint_as_float(0x00400000u);
     uint4 r;
     if constexpr (AT == ACT_F16) {

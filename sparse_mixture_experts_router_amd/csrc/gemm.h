@@ -9,7 +9,11 @@
 namespace moe {
 
 // Activation (MFMA input) types of the layer's GEMMs.
-enum ActType : int { ACT_BF16 = 0, ACT_F16 = 1 };
+// Operand types of an MFMA GEMM (template parameter AT) and storage types of
+// activations (OT): bf16 activations with bf16 weights; fp16 activations
+// with bf16 or MXFP4 weights converted to fp16 as they are read; fp16
+// activations with weights already stored as fp16 (AT only).
+enum ActType : int { ACT_BF16 = 0, ACT_F16 = 1, ACT_F16_W16 = 2 };
 
 enum Epi : int {
     EPI_F32 = 0,     // C[p][n] = acc (fp32)

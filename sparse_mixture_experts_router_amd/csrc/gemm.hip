@@ -348,7 +348,15 @@ struct BigCtx {
     const uint8_t *B;       // first B row of the tile (bf16) or its code row (MXFP4) (uniform)
     uint32_t boff[8];       // bf16: this lane's B chunks; MXFP4: [0..1] codes, [2] scale word
     const uint8_t *bsc;     // MXFP4: scale base of the tile (uniform)
+    __amdgpu_buffer_rsrc_t ra, rb;  // bf16 ring: buffer descriptors of A and of the tile's B rows
 };
+
+// A raw buffer descriptor over ptr (stride 0, no range limit in practice):
+// buffer loads take the per-lane 32-bit offset in a VGPR and the pair offset
+// in an SGPR, so the compiler cannot fold them into per-lane 64-bit addresses.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t ring_rsrc(const void *ptr) {
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(ptr), 0, 0x7fffffff, 0x00020000);
+}
 
 // Cache policy of the weight loads: every weight block is read once, and
 // the non-temporal (nt) policy moves them measurably faster (7.0 vs 6.2 TB/s
@@ -505,11 +513,204 @@ __device__ __forceinline__ void big_pair(const BigCtx &c, floatx16_t (&acc)[BigT
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
 }
 
+// ---------------------------------------------------------------------------
+// bf16 weights: a three-slot weight ring.  Every weight byte comes from HBM
+// once, and a CU's loads return in issue order, so the pair time is set by
+// how far ahead of their use the weight loads go out.  The ring keeps A
+// (activations, L2-resident) double-buffered and B (weights) in three slots:
+// after the barrier of pair pr a wave issues A(pr+2) and then B(pr+3), so
+// the wait of pair pr+1 (for A(pr+2), B(pr+2)) leaves only B(pr+3) in
+// flight and the weights get two pair times to arrive instead of one.
+// Each slot is an LDS object of its own, which keeps the compiler's
+// DMA-versus-read dependence tracking exact.
+constexpr int kRingB = 3;  // weight slots
+
+#define MOE_RING_SLOTS(TM, ASZ, BSZ)                                              \
+    __shared__ __attribute__((aligned(16))) uint8_t ring##TM##_a0[ASZ];          \
+    __shared__ __attribute__((aligned(16))) uint8_t ring##TM##_a1[ASZ];          \
+    __shared__ __attribute__((aligned(16))) uint8_t ring##TM##_b0[BSZ];          \
+    __shared__ __attribute__((aligned(16))) uint8_t ring##TM##_b1[BSZ];          \
+    __shared__ __attribute__((aligned(16))) uint8_t ring##TM##_b2[BSZ];
+MOE_RING_SLOTS(0, 256 * kBigRow, 256 * kBigRow)  // full: 160 KiB
+MOE_RING_SLOTS(1, 128 * kBigRow, 256 * kBigRow)  // half: 128 KiB
+MOE_RING_SLOTS(2, 384 * kBigRow, 128 * kBigRow)  // tall: 144 KiB
+#undef MOE_RING_SLOTS
+
+template <int TM, int S>
+__device__ __forceinline__ uint8_t *ring_a() {
+    static_assert(S == 0 || S == 1, "two activation slots");
+    if constexpr (TM == 0) return S ? ring0_a1 : ring0_a0;
+    else if constexpr (TM == 1) return S ? ring1_a1 : ring1_a0;
+    else return S ? ring2_a1 : ring2_a0;
+}
+
+template <int TM, int S>
+__device__ __forceinline__ uint8_t *ring_b() {
+    static_assert(S >= 0 && S < kRingB, "three weight slots");
+    if constexpr (TM == 0) return S == 0 ? ring0_b0 : S == 1 ? ring0_b1 : ring0_b2;
+    else if constexpr (TM == 1) return S == 0 ? ring1_b0 : S == 1 ? ring1_b1 : ring1_b2;
+    else return S == 0 ? ring2_b0 : S == 1 ? ring2_b1 : ring2_b2;
+}
+
+template <int TM, int S>
+__device__ __forceinline__ void ring_issue_a(const BigCtx &c, int pr, int wave) {
+    using T = BigTile<TM>;
+    uint8_t *buf = ring_a<TM, S>();
+#pragma unroll
+    for (int i = 0; i < T::NA; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.ra, MOE_LDS(buf + (wave * T::NA + i) * 1024), 16, c.aoff[i],
+                                                 pr * kBigRow, 0, 0);
+}
+
+template <int TM, int S>
+__device__ __forceinline__ void ring_issue_b(const BigCtx &c, int pr, int wave) {
+    using T = BigTile<TM>;
+    uint8_t *buf = ring_b<TM, S>();
+#pragma unroll
+    for (int i = 0; i < T::NBL; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rb, MOE_LDS(buf + (wave * T::NBL + i) * 1024), 16, c.boff[i],
+                                                 pr * kBigRow, 0, kStreamPolicy);
+}
+
+// Fragments of sub-step HS from activation slot SA and weight slot SB (the
+// same lane mapping as big_read).
+template <int TM, int SA, int SB, int HS, bool CVT>
+__device__ __forceinline__ void ring_read(uint4 (&fa)[2 * BigTile<TM>::MB], uint4 (&fb)[2 * BigTile<TM>::NBK],
+                                          const int (&bcol)[BigTile<TM>::NBK], int arow0, int lr, int lh) {
+    using T = BigTile<TM>;
+    const uint8_t *ab = ring_a<TM, SA>();
+    const uint8_t *bb = ring_b<TM, SB>();
+#pragma unroll
+    for (int c = 0; c < T::NBK; ++c)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint4 v = *(const uint4 *)(bb + bswz(bcol[c] + lr, 4 * HS + 2 * h + lh));
+            fb[2 * c + h] = CVT ? bf16x8_to_f16x8(v) : v;
+        }
+#pragma unroll
+    for (int m = 0; m < T::MB; ++m)
+#pragma unroll
+        for (int h = 0; h < 2; ++h) fa[2 * m + h] = *(const uint4 *)(ab + bswz(arow0 + m * 32 + lr, 4 * HS + 2 * h + lh));
+}
+
+// Pair pr with A in slot SA = pr % 2 and B in slot SB = pr % 3.  On entry
+// the wave holds the fragments of sub-step 2pr (f0), both slots are
+// complete everywhere, and A(pr+1), B(pr+1), B(pr+2) are in flight, issued
+// in the order B(pr+1), A(pr+1), B(pr+2).
+//   first:  read sub-step 2pr+1 into f1; MFMAs on f0.
+//   second: wait for the own A(pr+1) and B(pr+1) (all but the last NBL
+//           loads), barrier (every read of slots SA and SB done), issue
+//           A(pr+2) into SA and B(pr+3) into SB (clamped to the last pair:
+//           clamped loads are never read), read sub-step 2pr+2 into f0,
+//           MFMAs on f1 with the loads and reads spread between them.
+template <int TM, int AT, int SA, int SB>
+__device__ __forceinline__ void ring_pair(const BigCtx &c, floatx16_t (&acc)[BigTile<TM>::MB][BigTile<TM>::NBK],
+                                          uint4 (&fa0)[2 * BigTile<TM>::MB], uint4 (&fb0)[2 * BigTile<TM>::NBK],
+                                          uint4 (&fa1)[2 * BigTile<TM>::MB], uint4 (&fb1)[2 * BigTile<TM>::NBK],
+                                          const int (&bcol)[BigTile<TM>::NBK], int pr, int npair, int wave, int arow0,
+                                          int lane) {
+    using T = BigTile<TM>;
+    constexpr bool CVT = kBigRegConvert<false, AT>;
+    const int lr = lane & 31, lh = lane >> 5;
+    ring_read<TM, SA, SB, 1, CVT>(fa1, fb1, bcol, arow0, lr, lh);
+    big_mma<AT, TM>(acc, fa0, fb0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(T::NBL));
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    ring_issue_a<TM, SA>(c, min(pr + 2, npair - 1), wave);
+    ring_issue_b<TM, SB>(c, min(pr + 3, npair - 1), wave);
+    ring_read<TM, SA ^ 1, (SB + 1) % kRingB, 0, CVT>(fa0, fb0, bcol, arow0, lr, lh);
+    big_mma<AT, TM>(acc, fa1, fb1);
+    constexpr int NL = T::NA + T::NBL, NR = 2 * (T::MB + T::NBK), NM = 2 * T::MB * T::NBK;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // direct-to-LDS load
+    }
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - NL - NR > 0 ? NM - NL - NR : 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+}
+
+// The K loop of a bf16 tile on the ring: prologue, then pairs in groups of
+// six (one full turn of both slot cycles) and a tail of 0, 2 or 4 pairs
+// (npair is a multiple of 8).
+template <int TM, int AT>
+__device__ __forceinline__ void ring_kloop(const BigCtx &c, floatx16_t (&acc)[BigTile<TM>::MB][BigTile<TM>::NBK],
+                                           const int (&bcol)[BigTile<TM>::NBK], int npair, int wave, int arow0,
+                                           int lane) {
+    using T = BigTile<TM>;
+    constexpr int MB = T::MB, NBK = T::NBK;
+    const int lr = lane & 31, lh = lane >> 5;
+    ring_issue_a<TM, 0>(c, 0, wave);
+    ring_issue_b<TM, 0>(c, 0, wave);
+    ring_issue_b<TM, 1>(c, 1, wave);
+    ring_issue_a<TM, 1>(c, 1, wave);
+    ring_issue_b<TM, 2>(c, 2, wave);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * T::NBL + T::NA));  // A(0) and B(0) landed
+    __builtin_amdgcn_s_barrier();
+    uint4 fa0[2 * MB], fb0[2 * NBK], fa1[2 * MB], fb1[2 * NBK];
+    ring_read<TM, 0, 0, 0, kBigRegConvert<false, AT>>(fa0, fb0, bcol, arow0, lr, lh);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    int pr = 0;
+    for (; pr + 6 <= npair; pr += 6) {
+        ring_pair<TM, AT, 0, 0>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 0, npair, wave, arow0, lane);
+        ring_pair<TM, AT, 1, 1>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 1, npair, wave, arow0, lane);
+        ring_pair<TM, AT, 0, 2>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 2, npair, wave, arow0, lane);
+        ring_pair<TM, AT, 1, 0>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 3, npair, wave, arow0, lane);
+        ring_pair<TM, AT, 0, 1>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 4, npair, wave, arow0, lane);
+        ring_pair<TM, AT, 1, 2>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 5, npair, wave, arow0, lane);
+    }
+    // Nested, so the second tail block has one predecessor and the compiler
+    // knows exactly which slots have loads in flight when it starts.
+    if (pr + 2 <= npair) {
+        ring_pair<TM, AT, 0, 0>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 0, npair, wave, arow0, lane);
+        ring_pair<TM, AT, 1, 1>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 1, npair, wave, arow0, lane);
+        if (pr + 4 <= npair) {
+            ring_pair<TM, AT, 0, 2>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 2, npair, wave, arow0, lane);
+            ring_pair<TM, AT, 1, 0>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 3, npair, wave, arow0, lane);
+        }
+    }
+}
+
 // B rows of a tile and how many column blocks a row of C has, per mode.
 template <int EPI, int TM>
 __host__ __device__ constexpr int64_t big_nblocks(int64_t N) {
     return (EPI == EPI_SWIGLU) ? N / (BigTile<TM>::BN / 2) : N / BigTile<TM>::BN;
 }
+
+// An opaque copy of a value: the compiler must recompute whatever derives
+// from it after this point.  Lane-derived addresses and row indices are
+// cheap to recompute but were otherwise hoisted to the kernel entry, held
+// across the K loop and spilled; reloading a spill waits for every earlier
+// memory operation of the wave, the epilogue's stores included.
+__device__ __forceinline__ int opaque(int v) {
+    asm volatile("" : "+v"(v));
+    return v;
+}
+
+// A tile entry read from the device-side list is the same in every lane;
+// saying so keeps the tile's weight base in scalar registers, so the weight
+// loads take the scalar-base form.
+__device__ __forceinline__ void uniform_tile(RowTile &rt) {
+    rt.e = __builtin_amdgcn_readfirstlane(rt.e);
+    rt.mcount = __builtin_amdgcn_readfirstlane(rt.mcount);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)rt.p0);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)rt.p0 >> 32));
+    rt.p0 = (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
+template <int EPI, int OT, int TM>
+__device__ __forceinline__ void big_epilogue(const GemmArgs &a, const RowTile &rt, int64_t nb,
+                                             floatx16_t (&acc)[BigTile<TM>::MB][BigTile<TM>::NBK],
+                                             const int (&bcol)[BigTile<TM>::NBK], int arow0, int lane);
 
 // One output tile (row tile rt, column block nb) in mode TM.
 template <int EPI, bool MX, bool GROUPED, int AT, int OT, int TM>
@@ -520,6 +721,7 @@ __device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, i
     const int wm = TM == 0 ? wave >> 1 : TM == 1 ? 0 : wave;
     const int wn = TM == 0 ? wave & 1 : TM == 1 ? wave : 0;
     const int arow0 = wm * 32 * MB;       // first A row of this wave's row blocks
+    lane = opaque(lane);
     const int lr = lane & 31, lh = lane >> 5;
     const int64_t K = a.K;
     const int npair = (int)(K / kBigBK);  // a multiple of 8
@@ -573,6 +775,8 @@ __device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, i
         for (int i = 0; i < 8; ++i)
             c.boff[i] = i < S::NBL ? (uint32_t)((brel(wave * S::BPW + i * 8 + drow) * K + dchunk * 8) * 2) : 0;
         c.bsc = nullptr;
+        c.ra = ring_rsrc(c.A);
+        c.rb = ring_rsrc(c.B);
     }
 
     floatx16_t acc[MB][NBK];
@@ -583,13 +787,15 @@ __device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, i
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[m][cc][r] = 0.f;
 
-    big_issue<0, MX, TM>(c, 0, wave);
-    big_issue<1, MX, TM>(c, 1, wave);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(S::template kPerPair<MX>));
-    if constexpr (kBigConvert<MX, AT>) big_convert<0, TM, AT>(0, wave, lane);
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();
-    {
+    if constexpr (!MX) {
+        ring_kloop<TM, AT>(c, acc, bcol, npair, wave, arow0, lane);
+    } else {
+        big_issue<0, MX, TM>(c, 0, wave);
+        big_issue<1, MX, TM>(c, 1, wave);
+        __builtin_amdgcn_s_waitcnt(waitcnt_vm(S::template kPerPair<MX>));
+        if constexpr (kBigConvert<MX, AT>) big_convert<0, TM, AT>(0, wave, lane);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_s_barrier();
         uint4 fa0[2 * MB], fb0[2 * NBK], fa1[2 * MB], fb1[2 * NBK];
         big_read<0, 0, TM, kBigRegConvert<MX, AT>>(fa0, fb0, bcol, arow0, lr, lh);
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
@@ -601,15 +807,65 @@ __device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, i
     // Drain the clamped tail loads before the buffers are refilled.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();
+    big_epilogue<EPI, OT, TM>(a, rt, nb, acc, bcol, arow0, opaque(lane));
+}
 
+// Epilogue of one tile (lane id recomputed after the K loop).
+template <int EPI, int OT, int TM>
+__device__ __forceinline__ void big_epilogue(const GemmArgs &a, const RowTile &rt, int64_t nb,
+                                             floatx16_t (&acc)[BigTile<TM>::MB][BigTile<TM>::NBK],
+                                             const int (&bcol)[BigTile<TM>::NBK], int arow0, int lane) {
+    using S = BigTile<TM>;
+    constexpr int MB = S::MB, NBK = S::NBK;
+    const int lr = lane & 31, lh = lane >> 5;
     // Epilogue: lane (lr, lh) holds, in block (m, c), output row arow0 + 32m +
     // lr and the tile columns bcol[c] + 8g + 4lh + q in register 4g + q
     // (g, q = 0..3): four runs of four adjacent columns.
+    //
+    // A load issued after a store waits for that store (one in-order memory
+    // counter), so the loads the epilogue needs go out in batches ahead of
+    // the stores: the norm gain 1 + gamma before the first store, the
+    // residual rows and gate of block m before the stores of block m (one
+    // wait per row block).
+    constexpr bool kCol = EPI == EPI_NORM;
+    float4 colv[kCol ? NBK : 1][4];
+    if constexpr (kCol) {
+#pragma unroll
+        for (int cc = 0; cc < NBK; ++cc)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t n = nb * S::BN + bcol[cc] + 8 * g + 4 * lh;
+                float4 gm = make_float4(0.f, 0.f, 0.f, 0.f);
+                if (a.gamma) gm = *(const float4 *)(a.gamma + n);
+                colv[cc][g] = make_float4(1.0f + gm.x, 1.0f + gm.y, 1.0f + gm.z, 1.0f + gm.w);
+            }
+    }
+    constexpr bool kRes = EPI == EPI_RESID;
+    uint2 resid[kRes ? NBK : 1][4];
+    float4 gate[kRes ? NBK : 1][4];
+    // residual and gate of row block m (rows past the tile's valid rows read its last valid row)
+    auto load_resid = [&](int m) {
+        const int64_t p = rt.p0 + min(arow0 + m * 32 + lr, rt.mcount - 1);
+#pragma unroll
+        for (int cc = 0; cc < NBK; ++cc)
+#pragma unroll
+            for (int g = 0; g < 4; ++g) {
+                const int64_t n = nb * S::BN + bcol[cc] + 8 * g + 4 * lh;
+                resid[cc][g] = *(const uint2 *)(a.resid + p * a.N + n);
+                gate[cc][g] = *(const float4 *)(a.gate + n);
+            }
+    };
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
         const int row = arow0 + m * 32 + lr;
         const bool ok = row < rt.mcount;
         const int64_t p = rt.p0 + row;
+        if constexpr (kRes) {
+            // keeps the compiler from hoisting every block's loads to the top
+            // (the residual and the output have different types)
+            asm volatile("" ::: "memory");
+            load_resid(m);
+        }
         if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
             for (int cc = 0; cc < NBK / 2; ++cc) {
@@ -645,11 +901,12 @@ __device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, i
                                 make_uint2(f32_to_act<OT>(v[0]) | ((uint32_t)f32_to_act<OT>(v[1]) << 16),
                                            f32_to_act<OT>(v[2]) | ((uint32_t)f32_to_act<OT>(v[3]) << 16));
                     } else if constexpr (EPI == EPI_NORM) {
+                        const float4 gs = colv[cc][g];
+                        const float gq[4] = {gs.x, gs.y, gs.z, gs.w};
                         uint16_t h[4];
 #pragma unroll
                         for (int q = 0; q < 4; ++q) {
-                            const float gsc = a.gamma ? 1.0f + a.gamma[n + q] : 1.0f;
-                            h[q] = f32_to_bf16(gsc * v[q]);
+                            h[q] = f32_to_bf16(gq[q] * v[q]);
                             const float e = a.norm_round ? bf16_to_f32(h[q]) : v[q];
                             sq[g >> 1] += e * e;
                         }
@@ -658,8 +915,8 @@ __device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, i
                                 make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
                     } else {  // EPI_RESID
                         if (ok) {
-                            const uint2 hx = *(const uint2 *)(a.resid + p * a.N + n);
-                            const float4 gt = *(const float4 *)(a.gate + n);
+                            const uint2 hx = resid[cc][g];
+                            const float4 gt = gate[cc][g];
                             floatx4_t o;
                             o[0] = bf16_to_f32((uint16_t)hx.x) + gt.x * v[0];
                             o[1] = bf16_to_f32((uint16_t)(hx.x >> 16)) + gt.y * v[1];
@@ -704,6 +961,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             const int64_t nb = i % nblocks;
             RowTile rt;
             load_tile(a, true, BigTile<TM>::BM, t, rt);
+            uniform_tile(rt);
             big_item<EPI, MX, GROUPED, AT, OT, TM>(a, rt, nb, wave, lane);
         }
     } else {
@@ -780,6 +1038,10 @@ hipError_t launch_down_gemm(const GemmArgs &a, int path, bool mx, int ot, hipStr
 }
 
 hipError_t launch_gemm1(const GemmArgs &a, int path, bool mx, int at, hipStream_t s) {
+    if (at == ACT_F16_W16) {
+        if (mx) return hipErrorInvalidValue;
+        return run_path<EPI_SWIGLU, 2, false, true, ACT_F16_W16, ACT_F16>(a, path, s);
+    }
     if (mx) {
         if (at == ACT_F16) return run_path<EPI_SWIGLU, 2, true, true, ACT_F16, ACT_F16>(a, path, s);
         return run_path<EPI_SWIGLU, 2, true, true, ACT_BF16, ACT_BF16>(a, path, s);
@@ -789,6 +1051,11 @@ hipError_t launch_gemm1(const GemmArgs &a, int path, bool mx, int at, hipStream_
 }
 
 hipError_t launch_gemm2(const GemmArgs &a, int path, bool mx, int at, bool norm, hipStream_t s) {
+    if (at == ACT_F16_W16) {
+        if (mx) return hipErrorInvalidValue;
+        if (norm) return run_path<EPI_NORM, 1, false, true, ACT_F16_W16, ACT_BF16>(a, path, s);
+        return run_path<EPI_ACT, 1, false, true, ACT_F16_W16, ACT_BF16>(a, path, s);
+    }
     if (norm) {
         if (mx) {
             if (at == ACT_F16) return run_path<EPI_NORM, 1, true, true, ACT_F16, ACT_BF16>(a, path, s);
@@ -806,6 +1073,11 @@ hipError_t launch_gemm2(const GemmArgs &a, int path, bool mx, int at, bool norm,
 }
 
 hipError_t launch_up_gemm(const GemmArgs &a, int path, bool mx, int at, bool resid, hipStream_t s) {
+    if (at == ACT_F16_W16) {
+        if (mx) return hipErrorInvalidValue;
+        if (resid) return run_path<EPI_RESID, 1, false, false, ACT_F16_W16, ACT_BF16>(a, path, s);
+        return run_path<EPI_F32, 1, false, false, ACT_F16_W16, ACT_BF16>(a, path, s);
+    }
     if (resid) {
         if (mx) {
             if (at == ACT_F16) return run_path<EPI_RESID, 1, true, false, ACT_F16, ACT_BF16>(a, path, s);

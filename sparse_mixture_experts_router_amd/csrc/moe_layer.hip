@@ -91,7 +91,7 @@ int check_desc(const moe_desc *d) {
     if (d->expert_kind != MOE_EXPERT_RELU2 && d->expert_kind != MOE_EXPERT_SWIGLU3) return MOE_ERR_INVALID_ARG;
     if (d->act_dtype != MOE_DT_F32 && d->act_dtype != MOE_DT_BF16) return MOE_ERR_INVALID_ARG;
     if (d->router_dtype != MOE_DT_F32 && d->router_dtype != MOE_DT_BF16) return MOE_ERR_INVALID_ARG;
-    if (d->weight_dtype < MOE_DT_F32 || d->weight_dtype > MOE_DT_MXFP4) return MOE_ERR_INVALID_ARG;
+    if (d->weight_dtype < MOE_DT_F32 || d->weight_dtype > MOE_DT_F16) return MOE_ERR_INVALID_ARG;
     if (d->in_norm < MOE_NORM_NONE || d->in_norm > MOE_NORM_INPUT_SCALED) return MOE_ERR_INVALID_ARG;
     if (d->expert_norm < MOE_NORM_NONE || d->expert_norm > MOE_NORM_INPUT_SCALED) return MOE_ERR_INVALID_ARG;
     if (d->res_gate != MOE_RES_NONE && d->res_gate != MOE_RES_LINEAR) return MOE_ERR_INVALID_ARG;
@@ -109,6 +109,8 @@ int check_desc(const moe_desc *d) {
     }
     // bf16 path: latent SwiGLU layer on MFMA tiles.
     if (d->router_dtype != MOE_DT_BF16 || d->weight_dtype == MOE_DT_F32) return MOE_ERR_UNSUPPORTED;
+    // fp16 weights feed the fp16 GEMMs directly: only with fp16 intermediates
+    if (d->weight_dtype == MOE_DT_F16 && d->interm_dtype == MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
     if (d->d_latent == 0 || d->expert_kind != MOE_EXPERT_SWIGLU3) return MOE_ERR_UNSUPPORTED;
     if (d->d_model % 512 || d->d_latent % 512 || d->d_ff % 512 || d->n_experts % 16) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
@@ -146,6 +148,10 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
     const int64_t TK = T * k;
     const bool mx = d->weight_dtype == MOE_DT_MXFP4;
     const int at = interm_act(d);
+    // operand types of the GEMMs on the fp16 intermediates (expert GEMMs and
+    // the up-projection): fp16 weights need no conversion; down_w is bf16
+    // in every format but MXFP4
+    const int wat = d->weight_dtype == MOE_DT_F16 ? ACT_F16_W16 : at;
     Events ev{dbg ? (hipEvent_t *)dbg->stage_events : nullptr, s};
 
     const uint16_t *xb = (const uint16_t *)x;
@@ -242,20 +248,20 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
         g.tiles = tiles_small;
         g.ntiles = ntiles;
         g.max_tiles = (int32_t)L.max_small;
-        MOE_TRY(launch_gemm1(g, PATH_STREAM, mx, at, s));
+        MOE_TRY(launch_gemm1(g, PATH_STREAM, mx, wat, s));
         if (any_big) {
             g.tiles = tiles_big;
             g.ntiles = ntiles + 1;
             g.max_tiles = (int32_t)L.max_big;
-            MOE_TRY(launch_gemm1(g, PATH_TILE, mx, at, s));
+            MOE_TRY(launch_gemm1(g, PATH_TILE, mx, wat, s));
             g.tiles = tiles_half;
             g.ntiles = ntiles + 2;
             g.max_tiles = (int32_t)L.max_half;
-            MOE_TRY(launch_gemm1(g, PATH_HALF, mx, at, s));
+            MOE_TRY(launch_gemm1(g, PATH_HALF, mx, wat, s));
             g.tiles = tiles_tall;
             g.ntiles = ntiles + 3;
             g.max_tiles = (int32_t)L.max_tall;
-            MOE_TRY(launch_gemm1(g, PATH_TALL, mx, at, s));
+            MOE_TRY(launch_gemm1(g, PATH_TALL, mx, wat, s));
         }
     }
     MOE_TRY_RC(ev.end(MOE_STAGE_GEMM1));
@@ -282,20 +288,20 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
         g.tiles = tiles_small;
         g.ntiles = ntiles;
         g.max_tiles = (int32_t)L.max_small;
-        MOE_TRY(launch_gemm2(g, PATH_STREAM, mx, at, norm2, s));
+        MOE_TRY(launch_gemm2(g, PATH_STREAM, mx, wat, norm2, s));
         if (any_big) {
             g.tiles = tiles_big;
             g.ntiles = ntiles + 1;
             g.max_tiles = (int32_t)L.max_big;
-            MOE_TRY(launch_gemm2(g, PATH_TILE, mx, at, norm2, s));
+            MOE_TRY(launch_gemm2(g, PATH_TILE, mx, wat, norm2, s));
             g.tiles = tiles_half;
             g.ntiles = ntiles + 2;
             g.max_tiles = (int32_t)L.max_half;
-            MOE_TRY(launch_gemm2(g, PATH_HALF, mx, at, norm2, s));
+            MOE_TRY(launch_gemm2(g, PATH_HALF, mx, wat, norm2, s));
             g.tiles = tiles_tall;
             g.ntiles = ntiles + 3;
             g.max_tiles = (int32_t)L.max_tall;
-            MOE_TRY(launch_gemm2(g, PATH_TALL, mx, at, norm2, s));
+            MOE_TRY(launch_gemm2(g, PATH_TALL, mx, wat, norm2, s));
         }
     }
     MOE_TRY_RC(ev.end(MOE_STAGE_GEMM2));
@@ -321,9 +327,9 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
             g.resid = xb;
             g.gate = gains->res_gate;
             g.y = dbg ? dbg->y : nullptr;
-            MOE_TRY(launch_up_gemm(g, dense_path(g), mx, at, true, s));
+            MOE_TRY(launch_up_gemm(g, dense_path(g), mx, wat, true, s));
         } else {
-            MOE_TRY(launch_up_gemm(g, dense_path(g), mx, at, false, s));
+            MOE_TRY(launch_up_gemm(g, dense_path(g), mx, wat, false, s));
             if (dbg && dbg->y) MOE_TRY(hipMemcpyAsync(dbg->y, out, (size_t)T * D * 4, hipMemcpyDeviceToDevice, s));
         }
     }
@@ -486,6 +492,15 @@ int moe_permute(int64_t T, int64_t k, int64_t n, const int32_t *topk_idx, int32_
     hipStream_t s = as_stream(stream);
     MOE_TRY(launch_permute(topk_idx, T, (int)k, (int)n, counts, offsets, perm_tok, perm_slot, pos, nullptr, nullptr,
                            nullptr, nullptr, nullptr, 0, nullptr, s));
+    return MOE_OK;
+}
+
+int moe_convert_bf16_to_f16(const void *src, void *dst, int64_t count, void *stream) {
+    if (count < 0 || (count & 7) || (count && (!dst || !src)) || (((uintptr_t)dst | (uintptr_t)src) & 15))
+        return MOE_ERR_INVALID_ARG;
+    const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst, bytes = (uintptr_t)count * 2;
+    if (a != b && a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARG;  // partial overlap
+    MOE_TRY(launch_bf16_to_f16(src, dst, count, as_stream(stream)));
     return MOE_OK;
 }
 

@@ -31,6 +31,8 @@ hipError_t launch_combine(const uint16_t *S, const float *ssq, const int32_t *po
 
 // dst = src, 16 bytes per lane per access (bytes: multiple of 16).
 hipError_t launch_copy16(const void *src, void *dst, int64_t bytes, hipStream_t s);
+// count bf16 values (a multiple of 8, 16-byte aligned) -> fp16; dst may equal src.
+hipError_t launch_bf16_to_f16(const void *src, void *dst, int64_t count, hipStream_t s);
 
 hipError_t launch_router_f32(const float *x, const float *W, int64_t T, int n, int64_t d, float *logits,
                              hipStream_t s);

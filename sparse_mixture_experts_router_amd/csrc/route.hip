@@ -522,9 +522,26 @@ __global__ __launch_bounds__(256) void copy16_kernel(const uint4 *__restrict__ s
     for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n16; i += stride) dst[i] = src[i];
 }
 
+// bf16 -> fp16, eight values per thread, rounded to nearest even (the same
+// conversion the fp16 GEMMs apply to bf16 weights as they read them).
+__global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint4 *__restrict__ src, uint4 *__restrict__ dst,
+                                                          int64_t n8) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n8; i += stride) dst[i] = bf16x8_to_f16x8(src[i]);
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
+
+hipError_t launch_bf16_to_f16(const void *src, void *dst, int64_t count, hipStream_t s) {
+    const int64_t n8 = count / 8;
+    if (n8 <= 0) return hipSuccess;
+    const int64_t blocks = (n8 + 255) / 256;
+    bf16_to_f16_kernel<<<(unsigned)(blocks < 8192 ? blocks : 8192), 256, 0, s>>>((const uint4 *)src, (uint4 *)dst,
+                                                                                n8);
+    return hipGetLastError();
+}
 
 hipError_t launch_copy16(const void *src, void *dst, int64_t bytes, hipStream_t s) {
     const int64_t n16 = bytes / 16;

@@ -105,3 +105,24 @@ def test_error_strings():
     assert moe.moe_error_string(0) == "ok"
     assert "workspace" in moe.moe_error_string(-3)
     assert moe.moe_error_string(-99) == "unknown status"
+
+
+def test_f16_weight_format_validation():
+    d = desc_of(synthetic.PRESETS["c1"])
+    d.weight_dtype = moe.DT["f16"]
+    assert moe.moe_validate(d) == moe.MOE_OK
+    assert moe.moe_workspace_bytes(d) == moe.moe_workspace_bytes(desc_of(synthetic.PRESETS["c1"]))
+    d.interm_dtype = moe.DT["bf16"]  # fp16 weights feed the fp16 GEMMs only
+    assert moe.moe_validate(d) == moe.MOE_ERR_UNSUPPORTED
+
+
+def test_convert_rejects_before_any_launch():
+    lib = moe.lib()
+    a, b = ctypes.c_void_p(4096), ctypes.c_void_p(1 << 20)  # never dereferenced
+    bad = moe.MOE_ERR_INVALID_ARG
+    assert lib.moe_convert_bf16_to_f16(a, b, 12, None) == bad                    # not a multiple of 8
+    assert lib.moe_convert_bf16_to_f16(a, b, -8, None) == bad
+    assert lib.moe_convert_bf16_to_f16(ctypes.c_void_p(4098), b, 8, None) == bad  # misaligned
+    assert lib.moe_convert_bf16_to_f16(None, b, 8, None) == bad
+    assert lib.moe_convert_bf16_to_f16(a, ctypes.c_void_p(4096 + 16), 64, None) == bad  # partial overlap
+    assert lib.moe_convert_bf16_to_f16(None, None, 0, None) == moe.MOE_OK       # nothing to do

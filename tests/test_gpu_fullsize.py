@@ -2,9 +2,13 @@
 k=8), in the launch configuration the benchmark times: routing on all or a
 seeded sample of tokens, outputs on sampled tokens the oracle evaluates one
 by one (rows are independent), permutation bit-exact on every token."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
+
+import sparse_mixture_experts_router_amd as moe
 
 import synthetic
 from gpu_helpers import DeviceLayer, check_stages, compare, run, say, to_dev
@@ -93,3 +97,24 @@ def test_c4_mxfp4_chunks(name, layer_host, bf16_layer):
                 label="%s chunk %d" % (name, chunk))
         check_stages(p, lay.host, x, gpu, synthetic.sample_tokens(p.chunk_T, 3, seed=60 + chunk),
                      label="%s chunk %d" % (name, chunk))
+
+
+@pytest.mark.parametrize("name", ["c1", "c2"])
+def test_f16_weight_format_full_size(name, bf16_layer):
+    # the fp16 weight format at the real shape: bitwise the bf16 format's results
+    p = synthetic.PRESETS[name]
+    x = synthetic.inputs(p)
+    ref = run(bf16_layer, x)
+    lay = DeviceLayer.__new__(DeviceLayer)
+    lay.p = dataclasses.replace(p, weights="f16")
+    lay.host, lay.dev = bf16_layer.host, dict(bf16_layer.dev)
+    for key in ("w1", "w2", "up_w"):
+        t = bf16_layer.dev[key]
+        c = torch.empty_like(t)
+        moe.moe_convert_bf16_to_f16(t, c, t.numel())
+        lay.dev[key] = c
+    got = run(lay, x)
+    del lay
+    torch.cuda.empty_cache()
+    for key in ref:
+        np.testing.assert_array_equal(got[key], ref[key], err_msg="%s %s" % (name, key))

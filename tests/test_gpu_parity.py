@@ -4,6 +4,8 @@ finishes in seconds (several tiles, ragged tails), through the C ABI.
 Bars: routing indices and permutation bit-exact (near-ties with margin
 < 1e-4 excluded), outputs within 1e-5 * RMS(y) (fp32), 2e-2 * RMS(y) (bf16)
 and 5e-2 * RMS(y) (MXFP4, oracle on the same dequantised bits)."""
+import dataclasses
+
 import numpy as np
 import pytest
 import torch
@@ -179,3 +181,48 @@ def test_fp16_range_overflow_is_loud():
     gpu = run(layer, x, stages=False)
     assert not np.isfinite(gpu["out"][5]).all()
     assert np.isfinite(gpu["out"][[0, 1, 2, 3, 4, 6, 7]]).all()
+
+
+def test_bf16_to_f16_conversion_every_pattern():
+    # every bf16 bit pattern against numpy's round-to-nearest-even float16 cast
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    with np.errstate(over="ignore"):
+        ref = (bits.astype(np.uint32) << 16).view(np.float32).astype(np.float16).view(np.uint16)
+    src = to_dev(bits)
+    dst = torch.empty_like(src)
+    moe.moe_convert_bf16_to_f16(src, dst, bits.size)
+    moe.moe_convert_bf16_to_f16(src, src, bits.size)  # in place
+    torch.cuda.synchronize()
+    nan = np.isnan(ref.view(np.float16))
+    for got in (dst.cpu().numpy().view(np.uint16), src.cpu().numpy().view(np.uint16)):
+        np.testing.assert_array_equal(got[~nan], ref[~nan])
+        assert np.isnan(got[nan].view(np.float16)).all()
+
+
+def f16_weight_layer(layer: DeviceLayer) -> DeviceLayer:
+    """The same layer with expert_w1, expert_w2 and up_w converted on the
+    device to the fp16 weight format (down_w stays bf16)."""
+    lay = DeviceLayer.__new__(DeviceLayer)
+    lay.p = dataclasses.replace(layer.p, name=layer.p.name + "_f16w", weights="f16")
+    lay.host, lay.dev = layer.host, dict(layer.dev)
+    for key in ("w1", "w2", "up_w"):
+        t = layer.dev[key]
+        c = torch.empty_like(t)
+        moe.moe_convert_bf16_to_f16(t, c, t.numel())
+        lay.dev[key] = c
+    return lay
+
+
+@pytest.mark.parametrize("T,n", [(77, 32), (1203, 16)])
+def test_f16_weight_format(T, n):
+    # fp16-stored weights feed the fp16 GEMMs the bits the bf16 format converts
+    # to as it reads them: every output and intermediate is bitwise the same,
+    # and both meet the oracle's bar on the checkpoint's bf16 weights
+    p = small_case("f16w_T%d" % T, T=T, n=n)
+    layer = DeviceLayer(p)
+    x = synthetic.inputs(p)
+    ref = run(layer, x)
+    got = run(f16_weight_layer(layer), x)
+    for key in ref:
+        np.testing.assert_array_equal(got[key], ref[key], err_msg=key)
+    compare(p, layer.host, x, got, tokens=synthetic.sample_tokens(p.T, 120, seed=9), label=p.name + " f16 weights")
