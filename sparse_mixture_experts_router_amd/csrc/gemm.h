@@ -61,7 +61,7 @@ struct GemmArgs {
 
 constexpr int kTileBM = 256;      // rows per tile of the large-tile kernel (and of its grouped lists)
 constexpr int kHalfBM = 128;      // rows per tile of its half-height variant (expert remainders)
-constexpr int kTallBM = 384;      // rows of its tall variant (one tile for an expert with 257..384 rows)
+constexpr int kTallBM = 320;      // rows of its tall variant (one tile for an expert with 257..320 rows)
 constexpr int kTileBN = 256;      // B rows per tile (SWIGLU: 128 gate + 128 up -> 128 outputs)
 constexpr int kSmallBM = 16;      // rows per tile of the streaming kernel's grouped lists
 

@@ -323,18 +323,20 @@ __device__ __forceinline__ int bswz(int row, int chunk) {
 
 // Tile modes: TM 0 = full (256 A rows x 256 B rows; 2 x 2 waves of 128 x 128),
 // TM 1 = half (128 x 256; the four waves share the 128 A rows, each takes 64 B
-// rows), TM 2 = tall (384 x 128; each wave takes 96 A rows and all 128 B rows).
-// A grouped expert with at most 384 rows gets a single tile of the smallest
-// mode that holds it, so its weights stream once.
+// rows), TM 2 = tall (320 x 128; 2 x 2 waves of 160 x 64).  A grouped expert
+// with at most 320 rows gets a single tile of the smallest mode that holds
+// it, so its weights stream once.  (A 320 x 256 tile would re-read its A
+// rows half as often but needs 320 accumulator registers per lane, more
+// than the 256 AGPRs.)
 template <int TM> struct BigTile {
-    static constexpr int BM = TM == 0 ? 256 : TM == 1 ? 128 : 384;  // A rows per tile
+    static constexpr int BM = TM == 0 ? 256 : TM == 1 ? 128 : 320;  // A rows per tile
     static constexpr int BN = TM == 2 ? 128 : 256;                  // B rows per tile
-    static constexpr int MB = TM == 2 ? 3 : 4;                      // 32-row blocks per wave
-    static constexpr int NBK = TM == 1 ? 2 : 4;                     // 32-column blocks per wave
+    static constexpr int MB = TM == 2 ? 5 : 4;                      // 32-row blocks per wave
+    static constexpr int NBK = TM == 0 ? 4 : 2;                     // 32-column blocks per wave
     static constexpr int NA = BM / 32;                              // A loads (8 rows) per wave per pair
     static constexpr int NBL = BN / 32;                             // bf16 B loads per wave per pair
     static constexpr int NBC = BN / 128;                            // MXFP4 code loads per wave per pair
-    static constexpr int BOFF = (TM == 2 ? 384 : 256) * kBigRow;    // byte offset of the B area
+    static constexpr int BOFF = (TM == 2 ? 320 : 256) * kBigRow;    // byte offset of the B area
     static constexpr int BPW = BN / 4;                              // B rows loaded by one wave
     template <bool MX> static constexpr int kPerPair = NA + (MX ? NBC + 1 : NBL);
     static_assert(BOFF + BN * kBigRow <= kBigMxCodeOff, "A and B areas must end before the MXFP4 area");
@@ -533,7 +535,7 @@ constexpr int kRingB = 3;  // weight slots
     __shared__ __attribute__((aligned(16))) uint8_t ring##TM##_b2[BSZ];
 MOE_RING_SLOTS(0, 256 * kBigRow, 256 * kBigRow)  // full: 160 KiB
 MOE_RING_SLOTS(1, 128 * kBigRow, 256 * kBigRow)  // half: 128 KiB
-MOE_RING_SLOTS(2, 384 * kBigRow, 128 * kBigRow)  // tall: 144 KiB
+MOE_RING_SLOTS(2, 320 * kBigRow, 128 * kBigRow)  // tall: 128 KiB
 #undef MOE_RING_SLOTS
 
 template <int TM, int S>
@@ -718,8 +720,8 @@ __device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, i
     using S = BigTile<TM>;
     constexpr int MB = S::MB, NBK = S::NBK, NA = S::NA;
     constexpr int WCOLS = 32 * NBK;       // B rows per wave (SWIGLU: half gate, half up)
-    const int wm = TM == 0 ? wave >> 1 : TM == 1 ? 0 : wave;
-    const int wn = TM == 0 ? wave & 1 : TM == 1 ? wave : 0;
+    const int wm = TM == 1 ? 0 : wave >> 1;
+    const int wn = TM == 1 ? wave : wave & 1;
     const int arow0 = wm * 32 * MB;       // first A row of this wave's row blocks
     lane = opaque(lane);
     const int lr = lane & 31, lh = lane >> 5;
