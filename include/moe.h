@@ -219,7 +219,12 @@ int moe_layer_forward(const moe_desc *desc, const void *x, const void *router_w,
  * (the branch input: no input norm is applied here).
  *   topk_idx [T][k] int32, topk_w [T][k] fp32 (outputs)
  *   logits   [T][n] fp32 (optional output, may be NULL)
- *   workspace >= moe_router_workspace_bytes(desc)
+ *   workspace >= moe_router_workspace_bytes(desc), required when logits is
+ *            NULL.  For a bf16 router on a batch of more than 128 tokens
+ *            and n a multiple of 256 the logits GEMM is split into K slices
+ *            whose fp32 partial sums the workspace holds and the selection
+ *            adds in slice order (deterministic); given logits and no
+ *            workspace it runs unsplit.
  */
 size_t moe_router_workspace_bytes(const moe_desc *desc);
 int moe_router_topk(const moe_desc *desc, const void *u, const void *router_w, const float *router_bias,

@@ -57,6 +57,10 @@ struct GemmArgs {
     const uint16_t *resid; // EPI_RESID: x rows (bf16), leading dimension N
     const float *gate;     // EPI_RESID: g [N]
     float *y;              // EPI_RESID: optional y [rows][N]
+    // dense EPI_F32 tiles on bf16 weights: ksplit > 1 splits K into that many
+    // equal slices (each a multiple of 512), slice s adding its partial sums
+    // into plane s of C ([ksplit][M][ldc]); 0 or 1 = no split
+    int32_t ksplit;
 };
 
 constexpr int kTileBM = 256;      // rows per tile of the large-tile kernel (and of its grouped lists)

@@ -712,11 +712,13 @@ __device__ __forceinline__ void uniform_tile(RowTile &rt) {
 template <int EPI, int OT, int TM>
 __device__ __forceinline__ void big_epilogue(const GemmArgs &a, const RowTile &rt, int64_t nb,
                                              floatx16_t (&acc)[BigTile<TM>::MB][BigTile<TM>::NBK],
-                                             const int (&bcol)[BigTile<TM>::NBK], int arow0, int lane);
+                                             const int (&bcol)[BigTile<TM>::NBK], int arow0, int lane,
+                                             int64_t coff);
 
-// One output tile (row tile rt, column block nb) in mode TM.
+// One output tile (row tile rt, column block nb, K slice ksl) in mode TM.
 template <int EPI, bool MX, bool GROUPED, int AT, int OT, int TM>
-__device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, int64_t nb, int wave, int lane) {
+__device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, int64_t nb, int ksl, int wave,
+                                         int lane) {
     using S = BigTile<TM>;
     constexpr int MB = S::MB, NBK = S::NBK, NA = S::NA;
     constexpr int WCOLS = 32 * NBK;       // B rows per wave (SWIGLU: half gate, half up)
@@ -725,8 +727,10 @@ __device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, i
     const int arow0 = wm * 32 * MB;       // first A row of this wave's row blocks
     lane = opaque(lane);
     const int lr = lane & 31, lh = lane >> 5;
-    const int64_t K = a.K;
-    const int npair = (int)(K / kBigBK);  // a multiple of 8
+    const int64_t K = a.K;                // B row length
+    const int ks = (EPI == EPI_F32 && !MX && !GROUPED && a.ksplit > 1) ? a.ksplit : 1;
+    const int64_t kn = K / ks, k0 = (int64_t)ksl * kn;  // this item's K slice
+    const int npair = (int)(kn / kBigBK);  // a multiple of 8
     // Direct-load lane mapping of 128-byte rows: lane l fills row 8q + (l >> 3),
     // physical chunk l & 7, i.e. logical chunk (l & 7) ^ ((l >> 4) & 3).
     const int drow = lane >> 3, dchunk = (lane & 7) ^ ((lane >> 4) & 3);
@@ -745,7 +749,7 @@ __device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, i
     }
 
     BigCtx c;
-    c.A = (const uint8_t *)a.A;
+    c.A = (const uint8_t *)a.A + k0 * 2;
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
         const int row = min(wave * (NA * 8) + i * 8 + drow, rt.mcount - 1);
@@ -772,7 +776,7 @@ __device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, i
 #pragma unroll
         for (int i = 3; i < 8; ++i) c.boff[i] = 0;
     } else {
-        c.B = (const uint8_t *)((const uint16_t *)a.B + bfirst * K);
+        c.B = (const uint8_t *)((const uint16_t *)a.B + bfirst * K + k0);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
             c.boff[i] = i < S::NBL ? (uint32_t)((brel(wave * S::BPW + i * 8 + drow) * K + dchunk * 8) * 2) : 0;
@@ -809,14 +813,15 @@ __device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, i
     // Drain the clamped tail loads before the buffers are refilled.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();
-    big_epilogue<EPI, OT, TM>(a, rt, nb, acc, bcol, arow0, opaque(lane));
+    big_epilogue<EPI, OT, TM>(a, rt, nb, acc, bcol, arow0, opaque(lane), ksl * a.M * a.ldc);
 }
 
 // Epilogue of one tile (lane id recomputed after the K loop).
 template <int EPI, int OT, int TM>
 __device__ __forceinline__ void big_epilogue(const GemmArgs &a, const RowTile &rt, int64_t nb,
                                              floatx16_t (&acc)[BigTile<TM>::MB][BigTile<TM>::NBK],
-                                             const int (&bcol)[BigTile<TM>::NBK], int arow0, int lane) {
+                                             const int (&bcol)[BigTile<TM>::NBK], int arow0, int lane,
+                                             int64_t coff) {
     using S = BigTile<TM>;
     constexpr int MB = S::MB, NBK = S::NBK;
     const int lr = lane & 31, lh = lane >> 5;
@@ -896,7 +901,7 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs &a, const RowTile &r
 #pragma unroll
                     for (int q = 0; q < 4; ++q) v[q] = acc[m][cc][4 * g + q];
                     if constexpr (EPI == EPI_F32) {
-                        if (ok) *(floatx4_t *)((float *)a.C + p * a.ldc + n) = v;
+                        if (ok) *(floatx4_t *)((float *)a.C + coff + p * a.ldc + n) = v;
                     } else if constexpr (EPI == EPI_ACT) {
                         if (ok)
                             *(uint2 *)((uint16_t *)a.C + p * a.ldc + n) =
@@ -964,17 +969,20 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
             RowTile rt;
             load_tile(a, true, BigTile<TM>::BM, t, rt);
             uniform_tile(rt);
-            big_item<EPI, MX, GROUPED, AT, OT, TM>(a, rt, nb, wave, lane);
+            big_item<EPI, MX, GROUPED, AT, OT, TM>(a, rt, nb, 0, wave, lane);
         }
     } else {
         const int ntiles = (int)((a.M + BigTile<TM>::BM - 1) / BigTile<TM>::BM);
-        const int64_t items = (int64_t)ntiles * nblocks;
+        const int ks = (EPI == EPI_F32 && !MX && a.ksplit > 1) ? a.ksplit : 1;
+        const int64_t items = (int64_t)ntiles * nblocks * ks;
         for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
-            const int t = (int)(item / nblocks);
-            const int64_t nb = item - (int64_t)t * nblocks;
+            const int ksl = (int)(item % ks);
+            const int64_t tb = item / ks;
+            const int t = (int)(tb / nblocks);
+            const int64_t nb = tb - (int64_t)t * nblocks;
             RowTile rt;
             load_tile(a, false, BigTile<TM>::BM, t, rt);
-            big_item<EPI, MX, GROUPED, AT, OT, TM>(a, rt, nb, wave, lane);
+            big_item<EPI, MX, GROUPED, AT, OT, TM>(a, rt, nb, ksl, wave, lane);
         }
     }
 }
@@ -1001,7 +1009,8 @@ template <int EPI, bool MX, bool GROUPED, int AT, int OT, int TM>
 static hipError_t run_tile(const GemmArgs &a, hipStream_t s) {
     const int64_t nblocks = big_nblocks<EPI, TM>(a.N);
     const int64_t tiles = GROUPED ? a.max_tiles : (a.M + BigTile<TM>::BM - 1) / BigTile<TM>::BM;
-    const int64_t items = tiles * nblocks;
+    const int64_t ks = (EPI == EPI_F32 && !MX && !GROUPED && a.ksplit > 1) ? a.ksplit : 1;
+    const int64_t items = tiles * nblocks * ks;
     if (items <= 0) return hipSuccess;
     // grouped launches assign tiles to XCDs and need whole XCD groups
     static_assert(kBigGrid % kXcds == 0, "the grid must cover whole XCD groups");

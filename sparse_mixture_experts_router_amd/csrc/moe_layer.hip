@@ -47,6 +47,20 @@ int64_t big_tile_cap(int64_t TK, int64_t n) { return TK / kTileBM + n + 1; }
 int64_t half_tile_cap(int64_t n) { return n; }  // at most one per expert
 int64_t tall_tile_cap(int64_t n) { return n; }  // at most one per expert
 
+// K slices of the bf16 router GEMM.  It has a single 256-wide column block
+// (n <= 256), so a large batch gives only ceil(T / 256) tiles; slicing K
+// gives every CU work.  Each slice is a multiple of 512 and adds its
+// partial logits into its own fp32 plane; the top-k kernel adds the planes
+// in slice order.  Small batches (streaming kernel) are not sliced.
+int router_splits(const moe_desc *d) {
+    if (d->act_dtype != MOE_DT_BF16 || d->router_dtype != MOE_DT_BF16) return 1;
+    if (d->T <= 128 || d->n_experts % kTileBN) return 1;
+    const int64_t items = (d->T + kTileBM - 1) / kTileBM;
+    int ks = 1;
+    while (items * ks * 2 <= 256 && d->d_model % (ks * 2 * 512) == 0) ks *= 2;
+    return ks;
+}
+
 Layout make_layout(const moe_desc *d) {
     Layout L;
     memset(&L, 0, sizeof(L));
@@ -56,7 +70,7 @@ Layout make_layout(const moe_desc *d) {
     const int64_t Dx = d->d_latent ? d->d_latent : d->d_model;  // expert-space width
     const size_t ab = bf ? 2 : 4;                                 // activation bytes
     L.u = (bf && d->in_norm != MOE_NORM_NONE) ? c.take((size_t)T * d->d_model * 2) : 0;
-    L.logits = c.take((size_t)T * n * 4);
+    L.logits = c.take((size_t)router_splits(d) * T * n * 4);
     L.idx = c.take((size_t)TK * 4);
     L.w = c.take((size_t)TK * 4);
     L.counts = c.take((size_t)n * 4);
@@ -190,13 +204,14 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
         g.M = T;
         g.C = logits;
         g.ldc = n;
+        g.ksplit = router_splits(d);
         MOE_TRY(launch_router_gemm(g, dense_path(g), s));
     }
     MOE_TRY_RC(ev.end(MOE_STAGE_ROUTER));
 
     MOE_TRY_RC(ev.begin(MOE_STAGE_TOPK));
-    MOE_TRY(launch_topk(logits, gains ? gains->router_bias : nullptr, T, (int)n, (int)k, d->bias_in_weights, idx, wts,
-                        s));
+    MOE_TRY(launch_topk(logits, router_splits(d), gains ? gains->router_bias : nullptr, T, (int)n, (int)k,
+                        d->bias_in_weights, idx, wts, nullptr, s));
     MOE_TRY_RC(ev.end(MOE_STAGE_TOPK));
 
     // Experts with up to small_max tokens are streamed (weight-bandwidth
@@ -370,8 +385,8 @@ int forward_f32(const moe_desc *d, const void *x, const void *router_w, const vo
     MOE_TRY(launch_router_f32((const float *)x, (const float *)router_w, T, (int)n, D, logits, s));
     MOE_TRY_RC(ev.end(MOE_STAGE_ROUTER));
     MOE_TRY_RC(ev.begin(MOE_STAGE_TOPK));
-    MOE_TRY(launch_topk(logits, gains ? gains->router_bias : nullptr, T, (int)n, (int)k, d->bias_in_weights, idx, wts,
-                        s));
+    MOE_TRY(launch_topk(logits, 1, gains ? gains->router_bias : nullptr, T, (int)n, (int)k, d->bias_in_weights, idx,
+                        wts, nullptr, s));
     MOE_TRY_RC(ev.end(MOE_STAGE_TOPK));
     MOE_TRY_RC(ev.begin(MOE_STAGE_PERMUTE));
     MOE_TRY(launch_permute(idx, T, (int)k, (int)n, counts, offsets, perm_tok, perm_slot, pos, nullptr, nullptr,
@@ -447,7 +462,7 @@ int moe_layer_forward(const moe_desc *d, const void *x, const void *router_w, co
 
 size_t moe_router_workspace_bytes(const moe_desc *d) {
     if (check_desc(d) != MOE_OK) return 0;
-    return align256((size_t)d->T * d->n_experts * 4);
+    return align256((size_t)router_splits(d) * d->T * d->n_experts * 4);
 }
 
 int moe_router_topk(const moe_desc *d, const void *u, const void *router_w, const float *router_bias,
@@ -456,11 +471,16 @@ int moe_router_topk(const moe_desc *d, const void *u, const void *router_w, cons
     int rc = check_desc(d);
     if (rc != MOE_OK) return rc;
     if (!u || !router_w || !topk_idx || !topk_w) return MOE_ERR_INVALID_ARG;
+    // the K-sliced router needs the workspace for its partial planes; with
+    // logits given and no workspace it runs unsliced straight into them
     float *lg = logits;
-    if (!lg) {
-        if (workspace_bytes < moe_router_workspace_bytes(d)) return MOE_ERR_WORKSPACE_TOO_SMALL;
-        if (!workspace) return MOE_ERR_INVALID_ARG;
+    int ks = 1;
+    if (workspace && workspace_bytes >= moe_router_workspace_bytes(d)) {
         lg = (float *)workspace;
+        ks = router_splits(d);
+    } else if (!lg) {
+        if (workspace_bytes < moe_router_workspace_bytes(d)) return MOE_ERR_WORKSPACE_TOO_SMALL;
+        return MOE_ERR_INVALID_ARG;
     }
     if (d->T == 0) return MOE_OK;
     hipStream_t s = as_stream(stream);
@@ -478,10 +498,11 @@ int moe_router_topk(const moe_desc *d, const void *u, const void *router_w, cons
         g.M = d->T;
         g.C = lg;
         g.ldc = d->n_experts;
+        g.ksplit = ks;
         MOE_TRY(launch_router_gemm(g, dense_path(g), s));
     }
-    MOE_TRY(launch_topk(lg, router_bias, d->T, (int)d->n_experts, (int)d->top_k, d->bias_in_weights, topk_idx, topk_w,
-                        s));
+    MOE_TRY(launch_topk(lg, ks, router_bias, d->T, (int)d->n_experts, (int)d->top_k, d->bias_in_weights, topk_idx,
+                        topk_w, lg == logits ? nullptr : logits, s));
     return MOE_OK;
 }
 

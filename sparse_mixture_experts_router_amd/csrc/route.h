@@ -10,8 +10,10 @@ namespace moe {
 // mode 1: C_gamma (u = (1+g) x / rms(x)); mode 2: I_gamma (s = bf16((1+g) x), u = s / rms(s)).
 hipError_t launch_rmsnorm(const uint16_t *x, const float *gamma, uint16_t *u, int64_t T, int64_t d, float eps,
                           int mode, hipStream_t s);
-hipError_t launch_topk(const float *logits, const float *bias, int64_t T, int n, int k, int bias_in_weights,
-                       int32_t *idx, float *w, hipStream_t s);
+// logits: ks planes of [T][n] fp32 partial sums (over disjoint K slices),
+// added in plane order; lout (may be NULL) receives the summed logits.
+hipError_t launch_topk(const float *logits, int ks, const float *bias, int64_t T, int n, int k, int bias_in_weights,
+                       int32_t *idx, float *w, float *lout, hipStream_t s);
 // Experts with 1..small_max tokens go to the small-tile list (kSmallBM rows
 // per tile).  Heavier ones get one tile when it holds them (half-height list
 // up to kHalfBM rows, full list up to kTileBM, tall list up to kTallBM), else

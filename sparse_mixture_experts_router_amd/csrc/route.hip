@@ -87,19 +87,26 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t *__restrict
 // Selection order: score descending, expert id ascending on ties.
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, const float *__restrict__ bias,
-                                                   int64_t T, int n, int k, int bias_in_weights,
-                                                   int32_t *__restrict__ idx, float *__restrict__ w) {
+// logits: ks planes of [T][n] partial sums over disjoint K slices (ks = 1:
+// the logits themselves), added in plane order, so the sum is the same on
+// every run; lout (may be NULL) receives the summed logits.
+__global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int ks,
+                                                   const float *__restrict__ bias, int64_t T, int n, int k,
+                                                   int bias_in_weights, int32_t *__restrict__ idx,
+                                                   float *__restrict__ w, float *__restrict__ lout) {
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
     float sc[4], hv[4];
     const float *lr = logits + t * n;
+    const int64_t plane = T * n;
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         int e = lane + 64 * r;
         if (e < n) {
             float l = lr[e];
+            for (int q = 1; q < ks; ++q) l += lr[q * plane + e];
+            if (lout) lout[t * n + e] = l;
             float s = bias ? l + bias[e] : l;
             sc[r] = s;
             hv[r] = bias_in_weights ? s : l;
@@ -559,9 +566,9 @@ hipError_t launch_rmsnorm(const uint16_t *x, const float *gamma, uint16_t *u, in
     return hipGetLastError();
 }
 
-hipError_t launch_topk(const float *logits, const float *bias, int64_t T, int n, int k, int bias_in_weights,
-                       int32_t *idx, float *w, hipStream_t s) {
-    topk_kernel<<<blocks_for(T, 4), 256, 0, s>>>(logits, bias, T, n, k, bias_in_weights, idx, w);
+hipError_t launch_topk(const float *logits, int ks, const float *bias, int64_t T, int n, int k, int bias_in_weights,
+                       int32_t *idx, float *w, float *lout, hipStream_t s) {
+    topk_kernel<<<blocks_for(T, 4), 256, 0, s>>>(logits, ks, bias, T, n, k, bias_in_weights, idx, w, lout);
     return hipGetLastError();
 }
 

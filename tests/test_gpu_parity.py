@@ -144,6 +144,31 @@ def test_router_topk_stage_entry_point():
     check_routing(p, prm, x, gpu, np.arange(p.T), "router_stage")
 
 
+def test_router_topk_k_sliced():
+    # n = 256 and T > 128: the router GEMM runs on the tiled kernel with K in
+    # 8 slices of 512, whose partial planes the selection adds in order; the
+    # same call without a workspace runs unsliced into the given logits
+    p = small_case("router_sliced", T=600, d=4096, n=256, k=8, router_bias="zipf")
+    prm = {"router_w": synthetic.normal_bf16(p.layer_seed, "router_w", p.n * p.d, p.w_std).reshape(p.n, p.d),
+           "bias": synthetic.zipf_bias(p.n)}
+    x = synthetic.inputs(p)
+    desc = desc_of(p)
+    ws = torch.empty(moe.moe_router_workspace_bytes(desc), dtype=torch.uint8, device="cuda")
+    assert ws.numel() >= 8 * p.T * p.n * 4
+    r = oracle.forward(p.cfg(), dict(prm, x=x), want_outputs=False)
+    from gpu_helpers import check_routing
+    for label, workspace in (("sliced", ws), ("unsliced", None)):
+        idx = torch.empty((p.T, p.k), dtype=torch.int32, device="cuda")
+        w = torch.empty((p.T, p.k), dtype=torch.float32, device="cuda")
+        lg = torch.full((p.T, p.n), float("nan"), dtype=torch.float32, device="cuda")
+        moe.moe_router_topk(desc, to_dev(x), to_dev(prm["router_w"]), to_dev(prm["bias"]), idx, w, logits=lg,
+                            workspace=workspace)
+        torch.cuda.synchronize()
+        np.testing.assert_allclose(lg.cpu().numpy(), r["logits"], rtol=0, atol=1e-4, err_msg=label)
+        check_routing(p, prm, x, {"topk_idx": idx.cpu().numpy(), "topk_w": w.cpu().numpy()}, np.arange(p.T),
+                      "router " + label)
+
+
 @pytest.mark.parametrize("T,k,n", [(1, 1, 1), (5, 2, 8), (1000, 8, 256), (3000, 4, 16), (2500, 8, 256)])
 def test_permute_stage_entry_point(T, k, n):
     rng = np.random.default_rng(T * 7 + n)
