@@ -234,16 +234,18 @@ def main():
             "unit": "tokens/s", "ms_per_step": round(r2["ms"], 4), "steps": args.prefill_steps,
             "layer_TFLOPs": round(tf, 1), "layer_frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
             "stage_ms": {k: round(v, 4) for k, v in r2["stages"].items()},
-            "roofline": {"kernel": "gemm_big_kernel (grouped GEMM1 + SwiGLU; full- and half-height tile launches)",
-                         "bound": "mfma", "achieved": round(g1_tf, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-                         "frac": round(g1_tf / BF16_PEAK_TFLOPS, 4), "flops_per_launch": fl2["gemm1"],
-                         "avg_launch_ms": round(g1, 4),
+            # at ~256 rows per expert GEMM1 does ~240 FLOP per byte it must move, below the chip's
+            # 2.5 PFLOP/s / 8 TB/s = 312 FLOP/B balance: HBM bounds it (2.3 ms vs 1.8 ms of MFMA)
+            "roofline": {"kernel": "gemm_big_kernel, grouped GEMM1 + SwiGLU (full-tile and tall-tile launches, "
+                                   "timed together by the stage's HIP events)",
+                         "bound": "hbm", "achieved": round(by2["gemm1"] / (g1 * 1e-3) / 1e9, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(by2["gemm1"] / (g1 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "bytes_per_launch": by2["gemm1"], "avg_launch_ms": round(g1, 4),
                          "traffic": recorded_traffic("prefill_T8192_gemm1_traffic.json"),
-                         # at ~256 rows per expert GEMM1 does ~256 FLOP per weight byte, below the
-                         # chip's ~312 FLOP/B balance: the weight stream bounds it as well
-                         "hbm_view": {"weight_and_row_bytes": by2["gemm1"],
-                                      "achieved_GBps": round(by2["gemm1"] / (g1 * 1e-3) / 1e9, 1),
-                                      "frac": round(by2["gemm1"] / (g1 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}}}
+                         "mfma_view": {"flops": fl2["gemm1"], "achieved_TFLOPs": round(g1_tf, 1),
+                                       "peak_TFLOPs": BF16_PEAK_TFLOPS,
+                                       "frac": round(g1_tf / BF16_PEAK_TFLOPS, 4)}}}
 
     # ---- CPU oracle baseline on a bounded sample of the decode workload ----
     if not args.no_cpu_baseline:
