@@ -323,23 +323,25 @@ __device__ __forceinline__ int bswz(int row, int chunk) {
 
 // Tile modes: TM 0 = full (256 A rows x 256 B rows; 2 x 2 waves of 128 x 128),
 // TM 1 = half (128 x 256; the four waves share the 128 A rows, each takes 64 B
-// rows), TM 2 = tall (320 x 128; 2 x 2 waves of 160 x 64).  A grouped expert
-// with at most 320 rows gets a single tile of the smallest mode that holds
-// it, so its weights stream once.  (A 320 x 256 tile would re-read its A
-// rows half as often but needs 320 accumulator registers per lane, more
-// than the 256 AGPRs.)
+// rows), TM 2 = tall (320 x 128; 2 x 2 waves of 160 x 64), TM 3 = wide
+// (320 x 256; eight waves, two per SIMD, in 2 x 4 blocks of 160 x 64).  A
+// grouped expert with at most 320 rows gets a single tile of the smallest
+// mode that holds it, so its weights stream once: wide for bf16 and fp16
+// weights (half the A re-reads of tall: 128 column blocks of GEMM1 instead
+// of 256), tall for MXFP4 (whose dequantisation area leaves no LDS for wide).
 template <int TM> struct BigTile {
+    static constexpr int WAVES = TM == 3 ? 8 : 4;                  // waves per workgroup
     static constexpr int BM = TM == 0 ? 256 : TM == 1 ? 128 : 320;  // A rows per tile
     static constexpr int BN = TM == 2 ? 128 : 256;                  // B rows per tile
-    static constexpr int MB = TM == 2 ? 5 : 4;                      // 32-row blocks per wave
+    static constexpr int MB = TM >= 2 ? 5 : 4;                      // 32-row blocks per wave
     static constexpr int NBK = TM == 0 ? 4 : 2;                     // 32-column blocks per wave
-    static constexpr int NA = BM / 32;                              // A loads (8 rows) per wave per pair
-    static constexpr int NBL = BN / 32;                             // bf16 B loads per wave per pair
+    static constexpr int NA = BM / (8 * WAVES);                     // A loads (8 rows) per wave per pair
+    static constexpr int NBL = BN / (8 * WAVES);                    // bf16 B loads per wave per pair
     static constexpr int NBC = BN / 128;                            // MXFP4 code loads per wave per pair
-    static constexpr int BOFF = (TM == 2 ? 320 : 256) * kBigRow;    // byte offset of the B area
-    static constexpr int BPW = BN / 4;                              // B rows loaded by one wave
+    static constexpr int BOFF = (TM >= 2 ? 320 : 256) * kBigRow;    // MXFP4 buffers: byte offset of the B area
+    static constexpr int BPW = BN / WAVES;                          // B rows loaded by one wave
     template <bool MX> static constexpr int kPerPair = NA + (MX ? NBC + 1 : NBL);
-    static_assert(BOFF + BN * kBigRow <= kBigMxCodeOff, "A and B areas must end before the MXFP4 area");
+    static_assert(TM == 3 || BOFF + BN * kBigRow <= kBigMxCodeOff, "A and B areas must end before the MXFP4 area");
 };
 
 // Load addresses: a wave-uniform base plus a 32-bit byte offset per lane, so
@@ -536,6 +538,7 @@ constexpr int kRingB = 3;  // weight slots
 MOE_RING_SLOTS(0, 256 * kBigRow, 256 * kBigRow)  // full: 160 KiB
 MOE_RING_SLOTS(1, 128 * kBigRow, 256 * kBigRow)  // half: 128 KiB
 MOE_RING_SLOTS(2, 320 * kBigRow, 128 * kBigRow)  // tall: 128 KiB
+MOE_RING_SLOTS(3, 320 * kBigRow, 256 * kBigRow)  // wide: two weight slots used, 144 KiB
 #undef MOE_RING_SLOTS
 
 template <int TM, int S>
@@ -543,15 +546,17 @@ __device__ __forceinline__ uint8_t *ring_a() {
     static_assert(S == 0 || S == 1, "two activation slots");
     if constexpr (TM == 0) return S ? ring0_a1 : ring0_a0;
     else if constexpr (TM == 1) return S ? ring1_a1 : ring1_a0;
-    else return S ? ring2_a1 : ring2_a0;
+    else if constexpr (TM == 2) return S ? ring2_a1 : ring2_a0;
+    else return S ? ring3_a1 : ring3_a0;
 }
 
 template <int TM, int S>
 __device__ __forceinline__ uint8_t *ring_b() {
-    static_assert(S >= 0 && S < kRingB, "three weight slots");
+    static_assert(S >= 0 && S < (TM == 3 ? 2 : kRingB), "weight slot");
     if constexpr (TM == 0) return S == 0 ? ring0_b0 : S == 1 ? ring0_b1 : ring0_b2;
     else if constexpr (TM == 1) return S == 0 ? ring1_b0 : S == 1 ? ring1_b1 : ring1_b2;
-    else return S == 0 ? ring2_b0 : S == 1 ? ring2_b1 : ring2_b2;
+    else if constexpr (TM == 2) return S == 0 ? ring2_b0 : S == 1 ? ring2_b1 : ring2_b2;
+    else return S == 0 ? ring3_b0 : ring3_b1;
 }
 
 template <int TM, int S>
@@ -641,6 +646,96 @@ __device__ __forceinline__ void ring_pair(const BigCtx &c, floatx16_t (&acc)[Big
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
 }
 
+// Wide tiles: eight waves, two per SIMD, so a wave holds 160 accumulators and
+// the fragments of one 16-deep K slice (sub-step HS, half H) at a time; the
+// other wave on its SIMD covers the LDS latency.  A and B are double-buffered
+// in slot S = pr % 2: the pair's four quarters read slot S, then the wave
+// waits for its own loads of pair pr+1, passes the barrier (pair pr+1
+// complete everywhere, every read of slot S done) and issues pair pr+2 into
+// slot S (clamped to the last pair: clamped loads are never read).
+template <int TM, int S, int HS, int H, bool CVT>
+__device__ __forceinline__ void wide_read(uint4 (&fa)[BigTile<TM>::MB], uint4 (&fb)[BigTile<TM>::NBK],
+                                          const int (&bcol)[BigTile<TM>::NBK], int arow0, int lr, int lh) {
+    using T = BigTile<TM>;
+    const uint8_t *ab = ring_a<TM, S>();
+    const uint8_t *bb = ring_b<TM, S>();
+#pragma unroll
+    for (int c = 0; c < T::NBK; ++c) {
+        const uint4 v = *(const uint4 *)(bb + bswz(bcol[c] + lr, 4 * HS + 2 * H + lh));
+        fb[c] = CVT ? bf16x8_to_f16x8(v) : v;
+    }
+#pragma unroll
+    for (int m = 0; m < T::MB; ++m) fa[m] = *(const uint4 *)(ab + bswz(arow0 + m * 32 + lr, 4 * HS + 2 * H + lh));
+}
+
+template <int TM, int AT, int S, int HS, int H>
+__device__ __forceinline__ void wide_quarter(floatx16_t (&acc)[BigTile<TM>::MB][BigTile<TM>::NBK],
+                                             const int (&bcol)[BigTile<TM>::NBK], int arow0, int lr, int lh) {
+    using T = BigTile<TM>;
+    uint4 fa[T::MB], fb[T::NBK];
+    // fenced, so the next quarter's fragments are not read early (one quarter's
+    // fragments live at a time keeps the wave within 256 registers)
+    __builtin_amdgcn_sched_barrier(0);
+    wide_read<TM, S, HS, H, kBigRegConvert<false, AT>>(fa, fb, bcol, arow0, lr, lh);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+#pragma unroll
+    for (int m = 0; m < T::MB; ++m)
+#pragma unroll
+        for (int c = 0; c < T::NBK; ++c) acc[m][c] = mfma32x32x16<AT>(fb[c], fa[m], acc[m][c]);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+// The last quarter reads its fragments, then the wave waits for its loads of
+// pair pr+1 and passes the barrier, and the loads of pair pr+2 go out one
+// between each two of the quarter's MFMAs.
+template <int TM, int AT, int S>
+__device__ __forceinline__ void wide_pair(const BigCtx &c, floatx16_t (&acc)[BigTile<TM>::MB][BigTile<TM>::NBK],
+                                          const int (&bcol)[BigTile<TM>::NBK], int pr, int npair, int wave,
+                                          int arow0, int lr, int lh) {
+    using T = BigTile<TM>;
+    wide_quarter<TM, AT, S, 0, 0>(acc, bcol, arow0, lr, lh);
+    wide_quarter<TM, AT, S, 0, 1>(acc, bcol, arow0, lr, lh);
+    wide_quarter<TM, AT, S, 1, 0>(acc, bcol, arow0, lr, lh);
+    uint4 fa[T::MB], fb[T::NBK];
+    wide_read<TM, S, 1, 1, kBigRegConvert<false, AT>>(fa, fb, bcol, arow0, lr, lh);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    ring_issue_a<TM, S>(c, min(pr + 2, npair - 1), wave);
+    ring_issue_b<TM, S>(c, min(pr + 2, npair - 1), wave);
+#pragma unroll
+    for (int m = 0; m < T::MB; ++m)
+#pragma unroll
+        for (int cc = 0; cc < T::NBK; ++cc) acc[m][cc] = mfma32x32x16<AT>(fb[cc], fa[m], acc[m][cc]);
+    constexpr int NL = T::NA + T::NBL, NM = T::MB * T::NBK;
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // direct-to-LDS load
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - NL > 0 ? NM - NL : 0, 0);
+    __builtin_amdgcn_sched_barrier(0);
+}
+
+template <int TM, int AT>
+__device__ __forceinline__ void wide_kloop(const BigCtx &c, floatx16_t (&acc)[BigTile<TM>::MB][BigTile<TM>::NBK],
+                                           const int (&bcol)[BigTile<TM>::NBK], int npair, int wave, int arow0,
+                                           int lane) {
+    using T = BigTile<TM>;
+    const int lr = lane & 31, lh = lane >> 5;
+    ring_issue_a<TM, 0>(c, 0, wave);
+    ring_issue_b<TM, 0>(c, 0, wave);
+    ring_issue_a<TM, 1>(c, 1, wave);
+    ring_issue_b<TM, 1>(c, 1, wave);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(T::NA + T::NBL));  // A(0) and B(0) landed
+    __builtin_amdgcn_s_barrier();
+    for (int pr = 0; pr < npair; pr += 2) {
+        wide_pair<TM, AT, 0>(c, acc, bcol, pr, npair, wave, arow0, lr, lh);
+        wide_pair<TM, AT, 1>(c, acc, bcol, pr + 1, npair, wave, arow0, lr, lh);
+    }
+}
+
 // The K loop of a bf16 tile on the ring: prologue, then pairs in groups of
 // six (one full turn of both slot cycles) and a tail of 0, 2 or 4 pairs
 // (npair is a multiple of 8).
@@ -722,8 +817,9 @@ __device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, i
     using S = BigTile<TM>;
     constexpr int MB = S::MB, NBK = S::NBK, NA = S::NA;
     constexpr int WCOLS = 32 * NBK;       // B rows per wave (SWIGLU: half gate, half up)
-    const int wm = TM == 1 ? 0 : wave >> 1;
-    const int wn = TM == 1 ? wave : wave & 1;
+    static_assert(!(MX && TM == 3), "MXFP4 grouped tiles use the tall mode");
+    const int wm = TM == 1 ? 0 : TM == 3 ? wave >> 2 : wave >> 1;
+    const int wn = TM == 1 ? wave : TM == 3 ? wave & 3 : wave & 1;
     const int arow0 = wm * 32 * MB;       // first A row of this wave's row blocks
     lane = opaque(lane);
     const int lr = lane & 31, lh = lane >> 5;
@@ -793,7 +889,9 @@ __device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, i
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[m][cc][r] = 0.f;
 
-    if constexpr (!MX) {
+    if constexpr (!MX && TM == 3) {
+        wide_kloop<TM, AT>(c, acc, bcol, npair, wave, arow0, lane);
+    } else if constexpr (!MX) {
         ring_kloop<TM, AT>(c, acc, bcol, npair, wave, arow0, lane);
     } else {
         big_issue<0, MX, TM>(c, 0, wave);
@@ -955,7 +1053,7 @@ constexpr int kXcds = 8;  // workgroup b runs on XCD b % 8 (round-robin dispatch
 // are fetched into the XCD's L2 once and every weight block of the expert
 // is read once.  Dense launches: tile-major order over all workgroups.
 template <int EPI, bool MX, bool GROUPED, int AT, int OT, int TM>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_big_kernel(GemmArgs a) {
+__device__ __forceinline__ void big_kernel_body(const GemmArgs &a) {
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int64_t nblocks = big_nblocks<EPI, TM>(a.N);
     if constexpr (GROUPED) {
@@ -987,6 +1085,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) voi
     }
 }
 
+template <int EPI, bool MX, bool GROUPED, int AT, int OT, int TM>
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(1, 1))) void gemm_big_kernel(GemmArgs a) {
+    big_kernel_body<EPI, MX, GROUPED, AT, OT, TM>(a);
+}
+
+// The wide mode: eight waves, two per SIMD (256 registers each).
+template <int EPI, bool MX, bool GROUPED, int AT, int OT, int TM>
+__global__ __launch_bounds__(512) __attribute__((amdgpu_waves_per_eu(2, 2))) void gemm_wide_kernel(GemmArgs a) {
+    big_kernel_body<EPI, MX, GROUPED, AT, OT, TM>(a);
+}
+
 // ---------------------------------------------------------------------------
 // Launchers
 // ---------------------------------------------------------------------------
@@ -1015,7 +1124,10 @@ static hipError_t run_tile(const GemmArgs &a, hipStream_t s) {
     // grouped launches assign tiles to XCDs and need whole XCD groups
     static_assert(kBigGrid % kXcds == 0, "the grid must cover whole XCD groups");
     const int grid = GROUPED ? kBigGrid : (int)(items < kBigGrid ? items : kBigGrid);
-    gemm_big_kernel<EPI, MX, GROUPED, AT, OT, TM><<<grid, 256, 0, s>>>(a);
+    if constexpr (BigTile<TM>::WAVES == 8)
+        gemm_wide_kernel<EPI, MX, GROUPED, AT, OT, TM><<<grid, 512, 0, s>>>(a);
+    else
+        gemm_big_kernel<EPI, MX, GROUPED, AT, OT, TM><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();
 }
 
@@ -1026,7 +1138,8 @@ static hipError_t run_path(const GemmArgs &a, int path, hipStream_t s) {
     if (path == PATH_HALF || path == PATH_TALL) {
         if constexpr (GROUPED) {
             if (path == PATH_HALF) return run_tile<EPI, MX, GROUPED, AT, OT, 1>(a, s);
-            return run_tile<EPI, MX, GROUPED, AT, OT, 2>(a, s);
+            // the tall list (experts with 257..320 rows): wide tiles, tall ones for MXFP4
+            return run_tile<EPI, MX, GROUPED, AT, OT, MX ? 2 : 3>(a, s);
         } else {
             return hipErrorInvalidValue;
         }
