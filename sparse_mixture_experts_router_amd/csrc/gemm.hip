@@ -668,54 +668,64 @@ __device__ __forceinline__ void wide_read(uint4 (&fa)[BigTile<TM>::MB], uint4 (&
     for (int m = 0; m < T::MB; ++m) fa[m] = *(const uint4 *)(ab + bswz(arow0 + m * 32 + lr, 4 * HS + 2 * H + lh));
 }
 
-template <int TM, int AT, int S, int HS, int H>
-__device__ __forceinline__ void wide_quarter(floatx16_t (&acc)[BigTile<TM>::MB][BigTile<TM>::NBK],
-                                             const int (&bcol)[BigTile<TM>::NBK], int arow0, int lr, int lh) {
-    using T = BigTile<TM>;
-    uint4 fa[T::MB], fb[T::NBK];
-    // fenced, so the next quarter's fragments are not read early (one quarter's
-    // fragments live at a time keeps the wave within 256 registers)
-    __builtin_amdgcn_sched_barrier(0);
-    wide_read<TM, S, HS, H, kBigRegConvert<false, AT>>(fa, fb, bcol, arow0, lr, lh);
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+// Quarters are software-pipelined across two fragment buffers: the reads
+// of quarter q+1 overlap the MFMAs of quarter q.  On entry q0 holds quarter
+// 0 of pair pr.  Before the last quarter the wave waits for its loads of
+// pair pr+1 and passes the barrier (pair pr+1 complete everywhere, every
+// read of slot S done); the loads of pair pr+2 into slot S and the reads of
+// quarter 0 of pair pr+1 then go out between the last quarter's MFMAs.
+template <int TM, int AT>
+__device__ __forceinline__ void wide_mma(floatx16_t (&acc)[BigTile<TM>::MB][BigTile<TM>::NBK],
+                                         const uint4 (&fa)[BigTile<TM>::MB], const uint4 (&fb)[BigTile<TM>::NBK]) {
 #pragma unroll
-    for (int m = 0; m < T::MB; ++m)
+    for (int m = 0; m < BigTile<TM>::MB; ++m)
 #pragma unroll
-        for (int c = 0; c < T::NBK; ++c) acc[m][c] = mfma32x32x16<AT>(fb[c], fa[m], acc[m][c]);
-    __builtin_amdgcn_sched_barrier(0);
+        for (int c = 0; c < BigTile<TM>::NBK; ++c) acc[m][c] = mfma32x32x16<AT>(fb[c], fa[m], acc[m][c]);
 }
 
-// The last quarter reads its fragments, then the wave waits for its loads of
-// pair pr+1 and passes the barrier, and the loads of pair pr+2 go out one
-// between each two of the quarter's MFMAs.
-template <int TM, int AT, int S>
-__device__ __forceinline__ void wide_pair(const BigCtx &c, floatx16_t (&acc)[BigTile<TM>::MB][BigTile<TM>::NBK],
-                                          const int (&bcol)[BigTile<TM>::NBK], int pr, int npair, int wave,
-                                          int arow0, int lr, int lh) {
-    using T = BigTile<TM>;
-    wide_quarter<TM, AT, S, 0, 0>(acc, bcol, arow0, lr, lh);
-    wide_quarter<TM, AT, S, 0, 1>(acc, bcol, arow0, lr, lh);
-    wide_quarter<TM, AT, S, 1, 0>(acc, bcol, arow0, lr, lh);
-    uint4 fa[T::MB], fb[T::NBK];
-    wide_read<TM, S, 1, 1, kBigRegConvert<false, AT>>(fa, fb, bcol, arow0, lr, lh);
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    ring_issue_a<TM, S>(c, min(pr + 2, npair - 1), wave);
-    ring_issue_b<TM, S>(c, min(pr + 2, npair - 1), wave);
-#pragma unroll
-    for (int m = 0; m < T::MB; ++m)
-#pragma unroll
-        for (int cc = 0; cc < T::NBK; ++cc) acc[m][cc] = mfma32x32x16<AT>(fb[cc], fa[m], acc[m][cc]);
-    constexpr int NL = T::NA + T::NBL, NM = T::MB * T::NBK;
+template <int NL, int NR, int NM>
+__device__ __forceinline__ void wide_interleave() {
 #pragma unroll
     for (int i = 0; i < NL; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // direct-to-LDS load
     }
-    __builtin_amdgcn_sched_group_barrier(0x008, NM - NL > 0 ? NM - NL : 0, 0);
+#pragma unroll
+    for (int i = 0; i < NR; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
+    __builtin_amdgcn_sched_group_barrier(0x008, NM - NL - NR > 0 ? NM - NL - NR : 0, 0);
     __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+}
+
+template <int TM, int AT, int S>
+__device__ __forceinline__ void wide_pair(const BigCtx &c, floatx16_t (&acc)[BigTile<TM>::MB][BigTile<TM>::NBK],
+                                          uint4 (&qa0)[BigTile<TM>::MB], uint4 (&qb0)[BigTile<TM>::NBK],
+                                          uint4 (&qa1)[BigTile<TM>::MB], uint4 (&qb1)[BigTile<TM>::NBK],
+                                          const int (&bcol)[BigTile<TM>::NBK], int pr, int npair, int wave,
+                                          int arow0, int lr, int lh) {
+    using T = BigTile<TM>;
+    constexpr bool CVT = kBigRegConvert<false, AT>;
+    constexpr int NR = T::MB + T::NBK, NM = T::MB * T::NBK;
+    wide_read<TM, S, 0, 1, CVT>(qa1, qb1, bcol, arow0, lr, lh);
+    wide_mma<TM, AT>(acc, qa0, qb0);
+    wide_interleave<0, NR, NM>();
+    wide_read<TM, S, 1, 0, CVT>(qa0, qb0, bcol, arow0, lr, lh);
+    wide_mma<TM, AT>(acc, qa1, qb1);
+    wide_interleave<0, NR, NM>();
+    wide_read<TM, S, 1, 1, CVT>(qa1, qb1, bcol, arow0, lr, lh);
+    wide_mma<TM, AT>(acc, qa0, qb0);
+    wide_interleave<0, NR, NM>();
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    ring_issue_a<TM, S>(c, min(pr + 2, npair - 1), wave);
+    ring_issue_b<TM, S>(c, min(pr + 2, npair - 1), wave);
+    wide_read<TM, S ^ 1, 0, 0, CVT>(qa0, qb0, bcol, arow0, lr, lh);
+    wide_mma<TM, AT>(acc, qa1, qb1);
+    wide_interleave<T::NA + T::NBL, NR, NM>();
 }
 
 template <int TM, int AT>
@@ -730,9 +740,12 @@ __device__ __forceinline__ void wide_kloop(const BigCtx &c, floatx16_t (&acc)[Bi
     ring_issue_b<TM, 1>(c, 1, wave);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(T::NA + T::NBL));  // A(0) and B(0) landed
     __builtin_amdgcn_s_barrier();
+    uint4 qa0[T::MB], qb0[T::NBK], qa1[T::MB], qb1[T::NBK];
+    wide_read<TM, 0, 0, 0, kBigRegConvert<false, AT>>(qa0, qb0, bcol, arow0, lr, lh);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     for (int pr = 0; pr < npair; pr += 2) {
-        wide_pair<TM, AT, 0>(c, acc, bcol, pr, npair, wave, arow0, lr, lh);
-        wide_pair<TM, AT, 1>(c, acc, bcol, pr + 1, npair, wave, arow0, lr, lh);
+        wide_pair<TM, AT, 0>(c, acc, qa0, qb0, qa1, qb1, bcol, pr, npair, wave, arow0, lr, lh);
+        wide_pair<TM, AT, 1>(c, acc, qa0, qb0, qa1, qb1, bcol, pr + 1, npair, wave, arow0, lr, lh);
     }
 }
 
