@@ -114,7 +114,13 @@ __device__ __forceinline__ uint4 mxfp4x8_to_act(uint32_t codes, uint32_t e8m0) {
     return r;
 }
 
+// silu(t) = t / (1 + e^-t): `silu` with the accurate exponential and an
+// IEEE division (the fp32 path), `silu_fast` with the hardware exponential
+// (v_exp_f32 on -t log2 e) and reciprocal (v_rcp_f32), relative error about
+// 1e-6, far below the 16-bit rounding of the GEMM epilogues' stored results
+// (2^-11 for fp16); both give -0 as t -> -inf, t as t -> +inf, NaN for NaN.
 __device__ __forceinline__ float silu(float t) { return t / (1.0f + expf(-t)); }
+__device__ __forceinline__ float silu_fast(float t) { return t * __builtin_amdgcn_rcpf(1.0f + __expf(-t)); }
 
 template <typename T>
 __device__ __forceinline__ T wave_shfl_xor(T v, int mask) {

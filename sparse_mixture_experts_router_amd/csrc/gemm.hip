@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
                     if constexpr (EPI == EPI_SWIGLU) {
                         if (ok) {
                             float g = acc[m][0][q], u = acc[m][NB - 1][q];
-                            ((uint16_t *)a.C)[p * a.ldc + nb * 16 + li] = f32_to_act<OT>(silu(g) * u);
+                            ((uint16_t *)a.C)[p * a.ldc + nb * 16 + li] = f32_to_act<OT>(silu_fast(g) * u);
                         }
                     } else {
 #pragma unroll
@@ -993,7 +993,7 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs &a, const RowTile &r
                         uint16_t h[4];
 #pragma unroll
                         for (int q = 0; q < 4; ++q)
-                            h[q] = f32_to_act<OT>(silu(acc[m][cc][4 * g + q]) * acc[m][cc + NBK / 2][4 * g + q]);
+                            h[q] = f32_to_act<OT>(silu_fast(acc[m][cc][4 * g + q]) * acc[m][cc + NBK / 2][4 * g + q]);
                         const int64_t j = nb * (S::BN / 2) + bcol[cc] + 8 * g + 4 * lh;
                         *(uint2 *)((uint16_t *)a.C + p * a.ldc + j) =
                             make_uint2(h[0] | ((uint32_t)h[1] << 16), h[2] | ((uint32_t)h[3] << 16));
