@@ -7,8 +7,10 @@ seeded synthetic input of the 816B-A42B layer shape (d=8192, latent 4096,
 256 SwiGLU experts 4096->4096->4096, top-8 softmax gating, bf16 weights),
 with every input already resident in HBM.
 
-Default workload: decode, T=64 tokens.  A secondary line item times the
-prefill regime, T=8192.  Prints one JSON line.
+Default workload: decode, T=64 tokens (also timed with the Infinity Cache
+flushed between calls).  Further line items time the prefill regime
+(T=8192), skewed routing (T=16384) and MXFP4 weights (4 chunks of 8192).
+Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -30,12 +32,14 @@ def log(*a):
 
 
 def layer_bytes(p, counts) -> dict:
-    """Algorithmic HBM bytes of one forward: every weight byte of the touched
-    experts, the router and both projections read once, x read, out written."""
+    """Algorithmic HBM bytes of one forward (one chunk): every weight byte of
+    the touched experts, the router and both projections read once, x read,
+    out written.  Weights take 2 bytes (bf16, fp16) or 4.25 bits (MXFP4)."""
     touched = int((counts > 0).sum())
-    per_expert_w1 = 2 * p.F * p.L * 2
-    per_expert_w2 = p.L * p.F * 2
-    dense = (p.n * p.d + p.L * p.d + p.d * p.L) * 2
+    wb = 0.53125 if p.weights == "mxfp4" else 2
+    per_expert_w1 = 2 * p.F * p.L * wb
+    per_expert_w2 = p.L * p.F * wb
+    dense = p.n * p.d * 2 + (p.L * p.d + p.d * p.L) * wb
     TK = p.chunk_T * p.k
     act = p.chunk_T * p.d * 2 + p.chunk_T * p.d * 4
     gemm1 = touched * per_expert_w1 + TK * p.L * 2 + TK * p.F * 2   # W1 + gathered z rows + act rows
@@ -43,7 +47,8 @@ def layer_bytes(p, counts) -> dict:
 
 
 def layer_flops(p) -> dict:
-    T = p.chunk_T
+    """FLOPs of one pass over all chunks of preset p."""
+    T = p.chunk_T * p.chunks
     per_tok = 2 * p.d * p.n + 2 * p.d * p.L + p.k * (2 * p.L * 2 * p.F + 2 * p.F * p.L) + 2 * p.L * p.d
     return {"total": T * per_tok, "gemm1": T * p.k * 2 * p.L * 2 * p.F}
 
@@ -81,6 +86,8 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--only-prefill", action="store_true", help="skip the decode workload (profiling runs)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true",
+                    help="skip the cache-flushed decode timing and the skewed (T=16384) and MXFP4 (4 x 8192) workloads")
     ap.add_argument("--weight-format", choices=["bf16", "f16"], default="f16",
                     help="storage of expert_w1, expert_w2, up_w: the bf16 checkpoint as is, or converted once "
                          "(before timing, value-exact) to fp16 so the fp16 GEMMs read it without converting")
@@ -133,44 +140,68 @@ def main():
         torch.cuda.synchronize()
     gains = {"router_bias": None, "gamma_in": None, "gamma_expert": W["gamma_ex"], "res_gate": W["gate"]}
 
-    def make_desc(T):
-        return moe.make_desc(T, p.d, p.L, p.n, p.k, p.F, expert_kind=p.kind, act=p.act, router=p.router_w,
-                             weights=wfmt, in_norm=p.in_norm, expert_norm=p.expert_norm, res_gate=p.res_gate,
-                             eps_in=p.eps_in, eps_expert=p.eps_expert)
+    def make_desc(T, pr, wf):
+        return moe.make_desc(T, pr.d, pr.L, pr.n, pr.k, pr.F, expert_kind=pr.kind, act=pr.act, router=pr.router_w,
+                             weights=wf, in_norm=pr.in_norm, expert_norm=pr.expert_norm, res_gate=pr.res_gate,
+                             eps_in=pr.eps_in, eps_expert=pr.eps_expert)
 
     stream = torch.cuda.current_stream()
 
-    def run_workload(pr, steps, warmup):
+    def run_workload(pr, steps, warmup, Wd=None, gd=None, wf=None):
+        """steps timed passes of preset pr (all of its chunks per pass, chunk_T tokens each)."""
+        Wd, gd, wf = Wd or W, gd or gains, wf or wfmt
         T = pr.chunk_T
-        desc = make_desc(T)
-        x_host = synthetic.inputs(pr)
-        x = to_dev(x_host)
-        out = torch.empty((T, p.d), dtype=torch.float32, device=dev)
+        desc = make_desc(T, pr, wf)
+        x_host = synthetic.inputs(pr, chunk=0) if pr.chunks > 1 else synthetic.inputs(pr)
+        xs = [to_dev(x_host)] + [to_dev(synthetic.inputs(pr, chunk=c)) for c in range(1, pr.chunks)]
+        out = torch.empty((T, pr.d), dtype=torch.float32, device=dev)
         ws = torch.empty(moe.moe_workspace_bytes(desc), dtype=torch.uint8, device=dev)
-        counts = torch.empty(p.n, dtype=torch.int32, device=dev)
-        fwd = lambda dbg=None: moe.moe_layer_forward(desc, x, W["router_w"], W["down_w"], W["w1"], W["w2"],
-                                                     W["up_w"], gains, out, workspace=ws, dbg=dbg, stream=stream)
-        fwd({"expert_counts": counts})
+        counts = torch.empty(pr.n, dtype=torch.int32, device=dev)
+
+        def fwd(c, dbg=None):
+            moe.moe_layer_forward(desc, xs[c], Wd["router_w"], Wd["down_w"], Wd["w1"], Wd["w2"], Wd["up_w"], gd,
+                                  out, workspace=ws, dbg=dbg, stream=stream)
+
+        fwd(0, {"expert_counts": counts})
         torch.cuda.synchronize()
         for _ in range(warmup):
-            fwd()
-        evs = [moe.StageEvents() for _ in range(steps)]
+            for c in range(pr.chunks):
+                fwd(c)
+        evs = [[moe.StageEvents() for _ in range(pr.chunks)] for _ in range(steps)]
         torch.cuda.synchronize()
         t_start = time.perf_counter()
         for i in range(steps):
-            fwd({"stage_events": evs[i].address})
+            for c in range(pr.chunks):
+                fwd(c, {"stage_events": evs[i][c].address})
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_start
         stages = {}
         ran = [s for s in moe.STAGES if s != "in_norm" or pr.in_norm != "none"]
         for s in ran:
-            v = [e.elapsed_ms(s) for e in evs]
-            v = [q for q in v if q is not None]
-            if v:
+            v = [sum(e.elapsed_ms(s) or 0.0 for e in row) for row in evs]
+            if any(v):
                 stages[s] = sum(v) / len(v)
-        for e in evs:
-            e.close()
-        return {"T": T, "ms": wall * 1e3 / steps, "stages": stages, "counts": counts.cpu().numpy(), "x": x_host}
+        for row in evs:
+            for e in row:
+                e.close()
+        return {"T": T * pr.chunks, "ms": wall * 1e3 / steps, "stages": stages, "counts": counts.cpu().numpy(),
+                "x": x_host, "fwd": fwd}
+
+    def flushed_ms(r, steps):
+        """Median event-timed ms of one call after writing 1 GiB of scratch, so no weight, router or
+        projection byte is left in the 256 MB Infinity Cache from the previous call."""
+        scratch = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ms = []
+        for i in range(steps):
+            scratch.fill_(i & 255)
+            e0.record(stream)
+            r["fwd"](0)
+            e1.record(stream)
+            e1.synchronize()
+            ms.append(e0.elapsed_time(e1))
+        del scratch
+        return float(np.median(ms))
 
     if args.only_prefill:
         p2 = synthetic.PRESETS["c2"]
@@ -218,6 +249,15 @@ def main():
                      "bytes_per_launch": by["gemm1"], "avg_launch_ms": round(g1_ms, 4)},
     }
 
+    if not args.no_extra:
+        fm = flushed_ms(r, args.steps)
+        result["decode_cache_flushed"] = {
+            "ms_median": round(fm, 4), "tokens_per_s": round(p.chunk_T / (fm * 1e-3), 1),
+            "layer_GBps": round(by["total"] / (fm * 1e-3) / 1e9, 1),
+            "note": "1 GiB written before each call: nothing of the previous call is left in the 256 MB "
+                    "Infinity Cache (the headline steps run back to back)"}
+        log("decode T=%d, cache flushed between calls: %.3f ms" % (p.chunk_T, fm))
+
     # ---- prefill (secondary) ----
     if not args.no_prefill:
         p2 = synthetic.PRESETS["c2"]
@@ -246,6 +286,38 @@ def main():
                          "mfma_view": {"flops": fl2["gemm1"], "achieved_TFLOPs": round(g1_tf, 1),
                                        "peak_TFLOPs": BF16_PEAK_TFLOPS,
                                        "frac": round(g1_tf / BF16_PEAK_TFLOPS, 4)}}}
+
+    # ---- the skewed and MXFP4 workloads ----
+    def report(pr, rr, label):
+        flx, byx = layer_flops(pr), layer_bytes(pr, rr["counts"])
+        toks = pr.chunk_T * pr.chunks
+        d = {"workload": label, "tokens_per_s": round(toks / (rr["ms"] * 1e-3), 1), "ms_per_step": round(rr["ms"], 4),
+             "TFLOPs": round(flx["total"] / (rr["ms"] * 1e-3) / 1e12, 1),
+             "frac_mfma": round(flx["total"] / (rr["ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
+             "weight_and_io_GBps": round(byx["total"] * pr.chunks / (rr["ms"] * 1e-3) / 1e9, 1),
+             "touched_experts_chunk0": byx["touched"], "stage_ms": {k: round(v, 4) for k, v in rr["stages"].items()}}
+        log("%s: %.3f ms/step, %.0f tok/s, %.1f TFLOP/s" % (label, rr["ms"], d["tokens_per_s"], d["TFLOPs"]))
+        return d
+
+    if not args.no_extra:
+        p3 = synthetic.PRESETS["c3"]
+        g3 = dict(gains)
+        g3["router_bias"] = to_dev(synthetic.zipf_bias(p3.n))
+        result["skewed"] = report(p3, run_workload(p3, 5, 1, gd=g3),
+                                  "T=16384, Zipf(1.2) selection bias (hottest expert most of the tokens)")
+        t0 = time.time()
+        host4 = synthetic.layer_params(synthetic.PRESETS["c4i"])  # MXFP4 forms of the same draws
+        W4 = {k: to_dev(v) for k, v in host4.items()}
+        del host4
+        log("MXFP4 layer generated in %.1f s" % (time.time() - t0))
+        result["mxfp4"] = {}
+        for name in ("c4c", "c4i"):
+            p4 = synthetic.PRESETS[name]
+            g4 = {"router_bias": None, "gamma_in": W4["gamma_in"], "gamma_expert": W4["gamma_ex"], "res_gate": W4["gate"]}
+            result["mxfp4"][p4.in_norm] = report(p4, run_workload(p4, 3, 1, Wd=W4, gd=g4, wf="mxfp4"),
+                                                 "MXFP4 weights, 4 chunks of T=8192, input norm %s" % p4.in_norm)
+        del W4
+        torch.cuda.empty_cache()
 
     # ---- CPU oracle baseline on a bounded sample of the decode workload ----
     if not args.no_cpu_baseline:
