@@ -352,7 +352,8 @@ struct BigCtx {
     const uint8_t *B;       // first B row of the tile (bf16) or its code row (MXFP4) (uniform)
     uint32_t boff[8];       // bf16: this lane's B chunks; MXFP4: [0..1] codes, [2] scale word
     const uint8_t *bsc;     // MXFP4: scale base of the tile (uniform)
-    __amdgpu_buffer_rsrc_t ra, rb;  // bf16 ring: buffer descriptors of A and of the tile's B rows
+    __amdgpu_buffer_rsrc_t ra, rb;  // ring: buffer descriptors of A and of the tile's B rows (bf16, or MXFP4 codes)
+    __amdgpu_buffer_rsrc_t rs;      // ring, MXFP4: descriptor of the tile's scale rows
 };
 
 // A raw buffer descriptor over ptr (stride 0, no range limit in practice):
@@ -541,42 +542,105 @@ MOE_RING_SLOTS(2, 320 * kBigRow, 128 * kBigRow)  // tall: 128 KiB
 MOE_RING_SLOTS(3, 320 * kBigRow, 256 * kBigRow)  // wide: two weight slots used, 144 KiB
 #undef MOE_RING_SLOTS
 
-template <int TM, int S>
+// MXFP4 tiles: the weight slots hold the E2M1 codes (BN rows x 32 bytes per
+// pair) and, after them, the scale words (4 waves x 64 words); the codes are
+// dequantised in registers as the fragments are read.
+#define MOE_MX_SLOTS(TM, ASZ, QSZ)                                                \
+    __shared__ __attribute__((aligned(16))) uint8_t mx##TM##_a0[ASZ];            \
+    __shared__ __attribute__((aligned(16))) uint8_t mx##TM##_a1[ASZ];            \
+    __shared__ __attribute__((aligned(16))) uint8_t mx##TM##_q0[QSZ];            \
+    __shared__ __attribute__((aligned(16))) uint8_t mx##TM##_q1[QSZ];            \
+    __shared__ __attribute__((aligned(16))) uint8_t mx##TM##_q2[QSZ];
+MOE_MX_SLOTS(0, 256 * kBigRow, 256 * 32 + 1024)  // full: 91 KiB
+MOE_MX_SLOTS(1, 128 * kBigRow, 256 * 32 + 1024)  // half: 59 KiB
+MOE_MX_SLOTS(2, 320 * kBigRow, 128 * 32 + 1024)  // tall: 95 KiB
+#undef MOE_MX_SLOTS
+
+template <int TM, int S, bool MX = false>
 __device__ __forceinline__ uint8_t *ring_a() {
     static_assert(S == 0 || S == 1, "two activation slots");
-    if constexpr (TM == 0) return S ? ring0_a1 : ring0_a0;
+    static_assert(!MX || TM <= 2, "MXFP4 tiles: full, half, tall");
+    if constexpr (MX) {
+        if constexpr (TM == 0) return S ? mx0_a1 : mx0_a0;
+        else if constexpr (TM == 1) return S ? mx1_a1 : mx1_a0;
+        else return S ? mx2_a1 : mx2_a0;
+    } else if constexpr (TM == 0) return S ? ring0_a1 : ring0_a0;
     else if constexpr (TM == 1) return S ? ring1_a1 : ring1_a0;
     else if constexpr (TM == 2) return S ? ring2_a1 : ring2_a0;
     else return S ? ring3_a1 : ring3_a0;
 }
 
-template <int TM, int S>
+template <int TM, int S, bool MX = false>
 __device__ __forceinline__ uint8_t *ring_b() {
     static_assert(S >= 0 && S < (TM == 3 ? 2 : kRingB), "weight slot");
-    if constexpr (TM == 0) return S == 0 ? ring0_b0 : S == 1 ? ring0_b1 : ring0_b2;
+    static_assert(!MX || TM <= 2, "MXFP4 tiles: full, half, tall");
+    if constexpr (MX) {
+        if constexpr (TM == 0) return S == 0 ? mx0_q0 : S == 1 ? mx0_q1 : mx0_q2;
+        else if constexpr (TM == 1) return S == 0 ? mx1_q0 : S == 1 ? mx1_q1 : mx1_q2;
+        else return S == 0 ? mx2_q0 : S == 1 ? mx2_q1 : mx2_q2;
+    } else if constexpr (TM == 0) return S == 0 ? ring0_b0 : S == 1 ? ring0_b1 : ring0_b2;
     else if constexpr (TM == 1) return S == 0 ? ring1_b0 : S == 1 ? ring1_b1 : ring1_b2;
     else if constexpr (TM == 2) return S == 0 ? ring2_b0 : S == 1 ? ring2_b1 : ring2_b2;
     else return S == 0 ? ring3_b0 : ring3_b1;
 }
 
-template <int TM, int S>
+template <int TM, int S, bool MX = false>
 __device__ __forceinline__ void ring_issue_a(const BigCtx &c, int pr, int wave) {
     using T = BigTile<TM>;
-    uint8_t *buf = ring_a<TM, S>();
+    uint8_t *buf = ring_a<TM, S, MX>();
 #pragma unroll
     for (int i = 0; i < T::NA; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(c.ra, MOE_LDS(buf + (wave * T::NA + i) * 1024), 16, c.aoff[i],
                                                  pr * kBigRow, 0, 0);
 }
 
-template <int TM, int S>
+template <int TM, int S, bool MX = false>
 __device__ __forceinline__ void ring_issue_b(const BigCtx &c, int pr, int wave) {
     using T = BigTile<TM>;
-    uint8_t *buf = ring_b<TM, S>();
+    uint8_t *buf = ring_b<TM, S, MX>();
+    if constexpr (MX) {
+        // codes: lane l of load i fills row BPW*wave + 32i + l/2, bytes 16(l&1) .. of pair pr
 #pragma unroll
-    for (int i = 0; i < T::NBL; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rb, MOE_LDS(buf + (wave * T::NBL + i) * 1024), 16, c.boff[i],
-                                                 pr * kBigRow, 0, kStreamPolicy);
+        for (int i = 0; i < T::NBC; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rb, MOE_LDS(buf + (wave * T::NBC + i) * 1024), 16, c.boff[i],
+                                                     pr * 32, 0, kStreamPolicy);
+        // the 4-byte-aligned word holding the scale bytes of K-tiles 2pr, 2pr+1
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rs, MOE_LDS(buf + T::BN * 32 + wave * 256), 4, c.boff[2],
+                                                 (2 * pr) & ~3, 0, 0);
+    } else {
+#pragma unroll
+        for (int i = 0; i < T::NBL; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rb, MOE_LDS(buf + (wave * T::NBL + i) * 1024), 16, c.boff[i],
+                                                     pr * kBigRow, 0, kStreamPolicy);
+    }
+}
+
+// Fragments of sub-step HS of pair pr on an MXFP4 tile.  A lane's two 8-value
+// halves h = 0, 1 of the sub-step cover K = 32HS + 16lh + 8h .. +7 (A and B
+// alike, so the sums are unchanged): its 8 code bytes of a B row are
+// contiguous, dequantised here with the row's scale of K-tile 2pr + HS.
+template <int TM, int SA, int SB, int HS, int AT>
+__device__ __forceinline__ void ring_read_mx(uint4 (&fa)[2 * BigTile<TM>::MB], uint4 (&fb)[2 * BigTile<TM>::NBK],
+                                             const int (&bcol)[BigTile<TM>::NBK], int arow0, int lr, int lh,
+                                             int pr) {
+    using T = BigTile<TM>;
+    const uint8_t *ab = ring_a<TM, SA, true>();
+    const uint8_t *qb = ring_b<TM, SB, true>();
+    const int sh = 8 * ((2 * pr + HS) & 3);
+#pragma unroll
+    for (int c = 0; c < T::NBK; ++c) {
+        const int row = bcol[c] + lr;
+        const uint2 cw = *(const uint2 *)(qb + row * 32 + HS * 16 + lh * 8);
+        const uint32_t sw = *(const uint32_t *)(qb + T::BN * 32 + (row / T::BPW) * 256 + (row % T::BPW) * 4);
+        const uint32_t e = (sw >> sh) & 255u;
+        fb[2 * c] = mxfp4x8_to_act<AT>(cw.x, e);
+        fb[2 * c + 1] = mxfp4x8_to_act<AT>(cw.y, e);
+    }
+#pragma unroll
+    for (int m = 0; m < T::MB; ++m)
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+            fa[2 * m + h] = *(const uint4 *)(ab + bswz(arow0 + m * 32 + lr, 4 * HS + 2 * lh + h));
 }
 
 // Fragments of sub-step HS from activation slot SA and weight slot SB (the
@@ -610,7 +674,7 @@ __device__ __forceinline__ void ring_read(uint4 (&fa)[2 * BigTile<TM>::MB], uint
 //           A(pr+2) into SA and B(pr+3) into SB (clamped to the last pair:
 //           clamped loads are never read), read sub-step 2pr+2 into f0,
 //           MFMAs on f1 with the loads and reads spread between them.
-template <int TM, int AT, int SA, int SB>
+template <int TM, int AT, int SA, int SB, bool MX = false>
 __device__ __forceinline__ void ring_pair(const BigCtx &c, floatx16_t (&acc)[BigTile<TM>::MB][BigTile<TM>::NBK],
                                           uint4 (&fa0)[2 * BigTile<TM>::MB], uint4 (&fb0)[2 * BigTile<TM>::NBK],
                                           uint4 (&fa1)[2 * BigTile<TM>::MB], uint4 (&fb1)[2 * BigTile<TM>::NBK],
@@ -618,28 +682,33 @@ __device__ __forceinline__ void ring_pair(const BigCtx &c, floatx16_t (&acc)[Big
                                           int lane) {
     using T = BigTile<TM>;
     constexpr bool CVT = kBigRegConvert<false, AT>;
+    constexpr int NBX = MX ? T::NBC + 1 : T::NBL;  // weight-side loads per wave per pair
     const int lr = lane & 31, lh = lane >> 5;
-    ring_read<TM, SA, SB, 1, CVT>(fa1, fb1, bcol, arow0, lr, lh);
+    if constexpr (MX) ring_read_mx<TM, SA, SB, 1, AT>(fa1, fb1, bcol, arow0, lr, lh, pr);
+    else ring_read<TM, SA, SB, 1, CVT>(fa1, fb1, bcol, arow0, lr, lh);
     big_mma<AT, TM>(acc, fa0, fb0);
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(T::NBL));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(NBX));
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
-    ring_issue_a<TM, SA>(c, min(pr + 2, npair - 1), wave);
-    ring_issue_b<TM, SB>(c, min(pr + 3, npair - 1), wave);
-    ring_read<TM, SA ^ 1, (SB + 1) % kRingB, 0, CVT>(fa0, fb0, bcol, arow0, lr, lh);
+    ring_issue_a<TM, SA, MX>(c, min(pr + 2, npair - 1), wave);
+    ring_issue_b<TM, SB, MX>(c, min(pr + 3, npair - 1), wave);
+    if constexpr (MX) ring_read_mx<TM, SA ^ 1, (SB + 1) % kRingB, 0, AT>(fa0, fb0, bcol, arow0, lr, lh, pr + 1);
+    else ring_read<TM, SA ^ 1, (SB + 1) % kRingB, 0, CVT>(fa0, fb0, bcol, arow0, lr, lh);
     big_mma<AT, TM>(acc, fa1, fb1);
-    constexpr int NL = T::NA + T::NBL, NR = 2 * (T::MB + T::NBK), NM = 2 * T::MB * T::NBK;
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // direct-to-LDS load
-    }
+    // LDS reads first, so they land while the later MFMAs run and the wait
+    // that ends the sub-step does not stall; the loads need not land soon
+    constexpr int NL = T::NA + NBX, NR = 2 * (T::MB + T::NBK), NM = 2 * T::MB * T::NBK;
 #pragma unroll
     for (int i = 0; i < NR; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
         __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+    }
+#pragma unroll
+    for (int i = 0; i < NL; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // direct-to-LDS load
     }
     __builtin_amdgcn_sched_group_barrier(0x008, NM - NL - NR > 0 ? NM - NL - NR : 0, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -686,14 +755,14 @@ __device__ __forceinline__ void wide_mma(floatx16_t (&acc)[BigTile<TM>::MB][BigT
 template <int NL, int NR, int NM>
 __device__ __forceinline__ void wide_interleave() {
 #pragma unroll
-    for (int i = 0; i < NL; ++i) {
+    for (int i = 0; i < NR; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // direct-to-LDS load
+        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
     }
 #pragma unroll
-    for (int i = 0; i < NR; ++i) {
+    for (int i = 0; i < NL; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // direct-to-LDS load
     }
     __builtin_amdgcn_sched_group_barrier(0x008, NM - NL - NR > 0 ? NM - NL - NR : 0, 0);
     __builtin_amdgcn_sched_barrier(0);
@@ -752,40 +821,42 @@ __device__ __forceinline__ void wide_kloop(const BigCtx &c, floatx16_t (&acc)[Bi
 // The K loop of a bf16 tile on the ring: prologue, then pairs in groups of
 // six (one full turn of both slot cycles) and a tail of 0, 2 or 4 pairs
 // (npair is a multiple of 8).
-template <int TM, int AT>
+template <int TM, int AT, bool MX = false>
 __device__ __forceinline__ void ring_kloop(const BigCtx &c, floatx16_t (&acc)[BigTile<TM>::MB][BigTile<TM>::NBK],
                                            const int (&bcol)[BigTile<TM>::NBK], int npair, int wave, int arow0,
                                            int lane) {
     using T = BigTile<TM>;
     constexpr int MB = T::MB, NBK = T::NBK;
     const int lr = lane & 31, lh = lane >> 5;
-    ring_issue_a<TM, 0>(c, 0, wave);
-    ring_issue_b<TM, 0>(c, 0, wave);
-    ring_issue_b<TM, 1>(c, 1, wave);
-    ring_issue_a<TM, 1>(c, 1, wave);
-    ring_issue_b<TM, 2>(c, 2, wave);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * T::NBL + T::NA));  // A(0) and B(0) landed
+    constexpr int NBX = MX ? T::NBC + 1 : T::NBL;  // weight-side loads per wave per pair
+    ring_issue_a<TM, 0, MX>(c, 0, wave);
+    ring_issue_b<TM, 0, MX>(c, 0, wave);
+    ring_issue_b<TM, 1, MX>(c, 1, wave);
+    ring_issue_a<TM, 1, MX>(c, 1, wave);
+    ring_issue_b<TM, 2, MX>(c, 2, wave);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * NBX + T::NA));  // A(0) and B(0) landed
     __builtin_amdgcn_s_barrier();
     uint4 fa0[2 * MB], fb0[2 * NBK], fa1[2 * MB], fb1[2 * NBK];
-    ring_read<TM, 0, 0, 0, kBigRegConvert<false, AT>>(fa0, fb0, bcol, arow0, lr, lh);
+    if constexpr (MX) ring_read_mx<TM, 0, 0, 0, AT>(fa0, fb0, bcol, arow0, lr, lh, 0);
+    else ring_read<TM, 0, 0, 0, kBigRegConvert<false, AT>>(fa0, fb0, bcol, arow0, lr, lh);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     int pr = 0;
     for (; pr + 6 <= npair; pr += 6) {
-        ring_pair<TM, AT, 0, 0>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 0, npair, wave, arow0, lane);
-        ring_pair<TM, AT, 1, 1>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 1, npair, wave, arow0, lane);
-        ring_pair<TM, AT, 0, 2>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 2, npair, wave, arow0, lane);
-        ring_pair<TM, AT, 1, 0>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 3, npair, wave, arow0, lane);
-        ring_pair<TM, AT, 0, 1>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 4, npair, wave, arow0, lane);
-        ring_pair<TM, AT, 1, 2>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 5, npair, wave, arow0, lane);
+        ring_pair<TM, AT, 0, 0, MX>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 0, npair, wave, arow0, lane);
+        ring_pair<TM, AT, 1, 1, MX>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 1, npair, wave, arow0, lane);
+        ring_pair<TM, AT, 0, 2, MX>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 2, npair, wave, arow0, lane);
+        ring_pair<TM, AT, 1, 0, MX>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 3, npair, wave, arow0, lane);
+        ring_pair<TM, AT, 0, 1, MX>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 4, npair, wave, arow0, lane);
+        ring_pair<TM, AT, 1, 2, MX>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 5, npair, wave, arow0, lane);
     }
     // Nested, so the second tail block has one predecessor and the compiler
     // knows exactly which slots have loads in flight when it starts.
     if (pr + 2 <= npair) {
-        ring_pair<TM, AT, 0, 0>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 0, npair, wave, arow0, lane);
-        ring_pair<TM, AT, 1, 1>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 1, npair, wave, arow0, lane);
+        ring_pair<TM, AT, 0, 0, MX>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 0, npair, wave, arow0, lane);
+        ring_pair<TM, AT, 1, 1, MX>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 1, npair, wave, arow0, lane);
         if (pr + 4 <= npair) {
-            ring_pair<TM, AT, 0, 2>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 2, npair, wave, arow0, lane);
-            ring_pair<TM, AT, 1, 0>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 3, npair, wave, arow0, lane);
+            ring_pair<TM, AT, 0, 2, MX>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 2, npair, wave, arow0, lane);
+            ring_pair<TM, AT, 1, 0, MX>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 3, npair, wave, arow0, lane);
         }
     }
 }
@@ -884,6 +955,9 @@ __device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, i
         c.boff[2] = (uint32_t)(brel(wave * S::BPW + lane % S::BPW) * (K / 32));
 #pragma unroll
         for (int i = 3; i < 8; ++i) c.boff[i] = 0;
+        c.ra = ring_rsrc(c.A);
+        c.rb = ring_rsrc(c.B);
+        c.rs = ring_rsrc(c.bsc);
     } else {
         c.B = (const uint8_t *)((const uint16_t *)a.B + bfirst * K + k0);
 #pragma unroll
@@ -902,25 +976,8 @@ __device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, i
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[m][cc][r] = 0.f;
 
-    if constexpr (!MX && TM == 3) {
-        wide_kloop<TM, AT>(c, acc, bcol, npair, wave, arow0, lane);
-    } else if constexpr (!MX) {
-        ring_kloop<TM, AT>(c, acc, bcol, npair, wave, arow0, lane);
-    } else {
-        big_issue<0, MX, TM>(c, 0, wave);
-        big_issue<1, MX, TM>(c, 1, wave);
-        __builtin_amdgcn_s_waitcnt(waitcnt_vm(S::template kPerPair<MX>));
-        if constexpr (kBigConvert<MX, AT>) big_convert<0, TM, AT>(0, wave, lane);
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        __builtin_amdgcn_s_barrier();
-        uint4 fa0[2 * MB], fb0[2 * NBK], fa1[2 * MB], fb1[2 * NBK];
-        big_read<0, 0, TM, kBigRegConvert<MX, AT>>(fa0, fb0, bcol, arow0, lr, lh);
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        for (int pr = 0; pr < npair; pr += 2) {
-            big_pair<0, MX, AT, TM>(c, acc, fa0, fb0, fa1, fb1, bcol, pr, npair, wave, arow0, lane);
-            big_pair<1, MX, AT, TM>(c, acc, fa0, fb0, fa1, fb1, bcol, pr + 1, npair, wave, arow0, lane);
-        }
-    }
+    if constexpr (TM == 3) wide_kloop<TM, AT>(c, acc, bcol, npair, wave, arow0, lane);
+    else ring_kloop<TM, AT, MX>(c, acc, bcol, npair, wave, arow0, lane);
     // Drain the clamped tail loads before the buffers are refilled.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();
