@@ -82,6 +82,70 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t *__restrict
     }
 }
 
+// Rows up to 8192 wide: a workgroup normalises kNormRows rows, each thread
+// keeping its gains (loaded once) and its row chunks in registers between
+// the sum of squares and the scaling.  Per-thread partial sums and the block
+// reduction run in the same order as in rmsnorm_kernel, so the results are
+// the same bits.
+constexpr int kNormRows = 8;
+constexpr int kNormMaxChunks = 4;  // 8-value chunks per thread: d <= 8192
+
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t *__restrict__ x,
+                                                           const float *__restrict__ gamma,
+                                                           uint16_t *__restrict__ u, int64_t T, int64_t d, float eps,
+                                                           int mode) {
+    __shared__ float lds4[4];
+    const int64_t nch = d / 8;
+    float g[kNormMaxChunks][8];
+#pragma unroll
+    for (int j = 0; j < kNormMaxChunks; ++j) {
+        const int64_t c = threadIdx.x + 256 * j;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) g[j][i] = 1.0f;
+        if (c < nch && gamma) {
+            const float4 g0 = *(const float4 *)(gamma + c * 8), g1 = *(const float4 *)(gamma + c * 8 + 4);
+            g[j][0] = 1.0f + g0.x; g[j][1] = 1.0f + g0.y; g[j][2] = 1.0f + g0.z; g[j][3] = 1.0f + g0.w;
+            g[j][4] = 1.0f + g1.x; g[j][5] = 1.0f + g1.y; g[j][6] = 1.0f + g1.z; g[j][7] = 1.0f + g1.w;
+        }
+    }
+    const int64_t r1 = min<int64_t>(T, (int64_t)(blockIdx.x + 1) * kNormRows);
+    for (int64_t row = (int64_t)blockIdx.x * kNormRows; row < r1; ++row) {
+        const uint16_t *xr = x + row * d;
+        uint16_t *ur = u + row * d;
+        uint4 v[kNormMaxChunks];
+        float ss = 0.f;
+#pragma unroll
+        for (int j = 0; j < kNormMaxChunks; ++j) {
+            const int64_t c = threadIdx.x + 256 * j;
+            v[j] = c < nch ? *(const uint4 *)(xr + c * 8) : make_uint4(0, 0, 0, 0);
+            const uint16_t *h = (const uint16_t *)&v[j];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                float xv = bf16_to_f32(h[i]);
+                if (mode == 2) xv = bf16_to_f32(f32_to_bf16(g[j][i] * xv));  // square the bf16-rounded scaled value
+                ss += xv * xv;
+            }
+        }
+        ss = block_sum256(ss, lds4);
+        const float inv = 1.0f / sqrtf(ss / (float)d + eps);
+#pragma unroll
+        for (int j = 0; j < kNormMaxChunks; ++j) {
+            const int64_t c = threadIdx.x + 256 * j;
+            if (c >= nch) continue;
+            const uint16_t *h = (const uint16_t *)&v[j];
+            uint4 o;
+            uint16_t *oh = (uint16_t *)&o;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const float xv = bf16_to_f32(h[i]);
+                const float r = (mode == 2) ? bf16_to_f32(f32_to_bf16(g[j][i] * xv)) * inv : g[j][i] * (xv * inv);
+                oh[i] = f32_to_bf16(r);
+            }
+            *(uint4 *)(ur + c * 8) = o;
+        }
+    }
+}
+
 // ---------------------------------------------------------------------------
 // Top-k + softmax: one wave per token, lane l holds experts l, l+64, ...
 // Selection order: score descending, expert id ascending on ties.
@@ -562,7 +626,10 @@ static inline unsigned blocks_for(int64_t n, int b) { return (unsigned)((n + b -
 
 hipError_t launch_rmsnorm(const uint16_t *x, const float *gamma, uint16_t *u, int64_t T, int64_t d, float eps,
                           int mode, hipStream_t s) {
-    rmsnorm_kernel<<<(unsigned)T, 256, 0, s>>>(x, gamma, u, d, eps, mode);
+    if (d / 8 <= 256 * kNormMaxChunks)
+        rmsnorm_rows_kernel<<<(unsigned)((T + kNormRows - 1) / kNormRows), 256, 0, s>>>(x, gamma, u, T, d, eps, mode);
+    else
+        rmsnorm_kernel<<<(unsigned)T, 256, 0, s>>>(x, gamma, u, d, eps, mode);
     return hipGetLastError();
 }
 
