@@ -21,10 +21,14 @@ _LIB = os.path.join(_HERE, "libmoe_oracle.so")
 F32, BF16, MXFP4, F16 = 0, 1, 2, 3
 NORM_NONE, NORM_CENTERED, NORM_INPUT_SCALED = 0, 1, 2
 RELU, SWIGLU = 0, 1
+RES_NONE, RES_LINEAR, RES_MUSE = 0, 1, 2
+ROUTER_SOFTMAX, ROUTER_SIGMOID = 0, 1
 
 _DT = {"f32": F32, "bf16": BF16, "mxfp4": MXFP4, "f16": F16}
 _NORM = {"none": NORM_NONE, "centered": NORM_CENTERED, "input_scaled": NORM_INPUT_SCALED}
 _KIND = {"relu2": RELU, "swiglu3": SWIGLU}
+_RES = {"none": RES_NONE, "linear": RES_LINEAR, "muse": RES_MUSE}
+_ROUTER = {"softmax": ROUTER_SOFTMAX, "sigmoid": ROUTER_SIGMOID}
 
 
 def build(force: bool = False) -> str:
@@ -44,12 +48,17 @@ class _Desc(ctypes.Structure):
                 ("rdt", ctypes.c_int32), ("in_norm", ctypes.c_int32), ("ex_norm", ctypes.c_int32),
                 ("res_gate", ctypes.c_int32), ("bias_in_weights", ctypes.c_int32),
                 ("eps_in", ctypes.c_double), ("eps_ex", ctypes.c_double),
-                ("mirror", ctypes.c_int32), ("interm", ctypes.c_int32)]
+                ("mirror", ctypes.c_int32), ("interm", ctypes.c_int32),
+                ("router_fn", ctypes.c_int32), ("out_mult", ctypes.c_double), ("rsf", ctypes.c_double),
+                ("lat_norm", ctypes.c_int32), ("out_norm", ctypes.c_int32),
+                ("eps_lat", ctypes.c_double), ("eps_out", ctypes.c_double),
+                ("tau", ctypes.c_double), ("floor_", ctypes.c_double)]
 
 
 class _Tensors(ctypes.Structure):
     _fields_ = [(nm, ctypes.c_void_p) for nm in
-                ("x", "router_w", "down_w", "w1", "w2", "up_w", "bias", "gamma_in", "gamma_ex", "gate")]
+                ("x", "router_w", "down_w", "w1", "w2", "up_w", "bias", "gamma_in", "gamma_ex", "gate",
+                 "gamma_lat", "gamma_out")]
 
 
 _lib = None
@@ -74,6 +83,9 @@ def lib():
         _lib.orc_round_bf16.restype = dbl
         _lib.orc_round_f16.argtypes = [dbl]
         _lib.orc_round_f16.restype = dbl
+        _lib.orc_router_scores.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp]
+        _lib.orc_router_weights.argtypes = [ctypes.POINTER(_Desc), vp, vp, i64, vp]
+        _lib.orc_muse_gate_coeffs.argtypes = [dbl, dbl, dbl, vp, vp]
     return _lib
 
 
@@ -87,14 +99,22 @@ def _c(a, dtype):
 
 def make_desc(cfg: dict, mirror: bool = False) -> _Desc:
     """cfg keys: d, L, n, k, F, kind, act, weights, router_w, in_norm,
-    expert_norm, res_gate, eps_in, eps_expert, bias_in_weights."""
+    expert_norm, res_gate, eps_in, eps_expert, bias_in_weights; optional
+    router_fn ("softmax"), out_mult (1), routed_scale (1), latent_norm
+    ("none"), out_norm ("none"), eps_latent, eps_out (1e-5), res_tau (0.3),
+    res_floor (1e-3)."""
     return _Desc(d=cfg["d"], L=cfg["L"], n=cfg["n"], k=cfg["k"], F=cfg["F"],
                  kind=_KIND[cfg["kind"]], act=_DT[cfg["act"]], wdt=_DT[cfg["weights"]],
                  rdt=_DT[cfg["router_w"]], in_norm=_NORM[cfg["in_norm"]],
-                 ex_norm=_NORM[cfg["expert_norm"]], res_gate=1 if cfg["res_gate"] == "linear" else 0,
+                 ex_norm=_NORM[cfg["expert_norm"]], res_gate=_RES[cfg["res_gate"]],
                  bias_in_weights=int(cfg.get("bias_in_weights", 0)),
                  eps_in=float(cfg["eps_in"]), eps_ex=float(cfg["eps_expert"]),
-                 mirror=int(mirror), interm=_DT[cfg.get("interm", "bf16")] if cfg["act"] == "bf16" else F32)
+                 mirror=int(mirror), interm=_DT[cfg.get("interm", "bf16")] if cfg["act"] == "bf16" else F32,
+                 router_fn=_ROUTER[cfg.get("router_fn", "softmax")], out_mult=float(cfg.get("out_mult", 1.0)),
+                 rsf=float(cfg.get("routed_scale", 1.0)), lat_norm=_NORM[cfg.get("latent_norm", "none")],
+                 out_norm=_NORM[cfg.get("out_norm", "none")], eps_lat=float(cfg.get("eps_latent", 1e-5)),
+                 eps_out=float(cfg.get("eps_out", 1e-5)), tau=float(cfg.get("res_tau", 0.3)),
+                 floor_=float(cfg.get("res_floor", 1e-3)))
 
 
 _KEEP = []
@@ -106,7 +126,7 @@ def forward(cfg: dict, t: dict, tokens=None, forced=None, dense: bool = False, m
 
     t: dict with numpy arrays (raw stored forms: uint16 bf16 bits, float32,
     or uint8 MXFP4 buffers) under keys x, router_w, down_w, w1, w2, up_w and
-    optional float32 bias, gamma_in, gamma_ex, gate.
+    optional float32 bias, gamma_in, gamma_ex, gate, gamma_lat, gamma_out.
     tokens: int64 array of token ids (None: all T rows of x).
     forced: int32 [ntok][k] expert ids (None: route).
     """
@@ -118,7 +138,7 @@ def forward(cfg: dict, t: dict, tokens=None, forced=None, dense: bool = False, m
     for nm in ("x", "router_w", "down_w", "w1", "w2", "up_w"):
         a = t.get(nm)
         arrs[nm] = None if a is None else np.ascontiguousarray(a)
-    for nm in ("bias", "gamma_in", "gamma_ex", "gate"):
+    for nm in ("bias", "gamma_in", "gamma_ex", "gate", "gamma_lat", "gamma_out"):
         a = t.get(nm)
         arrs[nm] = None if a is None else _c(a, np.float32)
     tens = _Tensors(**{nm: _p(a) for nm, a in arrs.items()})
@@ -139,6 +159,42 @@ def forward(cfg: dict, t: dict, tokens=None, forced=None, dense: bool = False, m
     assert rc == 0
     res["tokens"] = tok
     return res
+
+
+def router_scores(cfg: dict, logits, bias=None):
+    """Selection scores and weight basis (float64 [rows][n] each) of fp32
+    logits [rows][n] under the cfg's router function."""
+    desc = make_desc(cfg)
+    lg = np.atleast_2d(_c(logits, np.float32))
+    b = None if bias is None else _c(bias, np.float32)
+    sel = np.zeros(lg.shape, np.float64)
+    H = np.zeros(lg.shape, np.float64)
+    for r in range(lg.shape[0]):
+        lr, sr, hr = lg[r], sel[r], H[r]
+        lib().orc_router_scores(ctypes.byref(desc), _p(lr), _p(b), _p(sr), _p(hr))
+    return sel, H
+
+
+def router_weights(cfg: dict, H, idx) -> np.ndarray:
+    """Weights of the kept experts idx [k] from the weight basis H [n]."""
+    desc = make_desc(cfg)
+    H = _c(H, np.float64)
+    idx = _c(idx, np.int32)
+    w = np.zeros(idx.shape[0], np.float64)
+    lib().orc_router_weights(ctypes.byref(desc), _p(H), _p(idx), idx.shape[0], _p(w))
+    return w
+
+
+def muse_gate_coeffs(g, tau: float = 0.3, floor: float = 1e-3):
+    """(alpha, beta) of the residual gate for each value of g."""
+    g = np.atleast_1d(np.asarray(g, np.float64))
+    al = np.zeros_like(g)
+    be = np.zeros_like(g)
+    a_, b_ = ctypes.c_double(), ctypes.c_double()
+    for i, gv in enumerate(g):
+        lib().orc_muse_gate_coeffs(float(gv), tau, floor, ctypes.byref(a_), ctypes.byref(b_))
+        al[i], be[i] = a_.value, b_.value
+    return al, be
 
 
 def permute(idx: np.ndarray, n: int) -> dict:

@@ -18,7 +18,9 @@
  *             G = Softmax(KeepTopK(H, k)) and its worked example).
  *  [FactSheet] archdb.vladsavinov.com, "Muse-Spark-Open-816B-A42B" (fields
  *             FFN activation SwiGLU, no FFN bias, no GLU clamp,
- *             routed_scaling_factor 1, latent width 4,096).
+ *             routed_scaling_factor 1, latent width 4,096, gating function
+ *             sigmoid, block norm RMSNorm with a 1+w gain and epsilon 1e-5,
+ *             residual design alpha*residual + beta*h).
  *
  * Precision: every sum, product and transcendental is fp64.  Values are
  * rounded only where the method itself stores them in a narrower type:
@@ -45,6 +47,8 @@
 enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_MXFP4 = 2, ORC_F16 = 3 };
 enum { ORC_NORM_NONE = 0, ORC_NORM_CENTERED = 1, ORC_NORM_INPUT_SCALED = 2 };
 enum { ORC_RELU = 0, ORC_SWIGLU = 1 };
+enum { ORC_RES_NONE = 0, ORC_RES_LINEAR = 1, ORC_RES_MUSE = 2 };
+enum { ORC_ROUTER_SOFTMAX = 0, ORC_ROUTER_SIGMOID = 1 };
 
 typedef struct {
     int64_t d, L, n, k, F; /* L == 0: no latent projection, experts read u directly */
@@ -54,11 +58,19 @@ typedef struct {
     int32_t rdt;           /* dtype of the router weight: F32 or BF16 */
     int32_t in_norm;       /* norm applied to x before router and down-projection */
     int32_t ex_norm;       /* norm applied to every expert output before mixing */
-    int32_t res_gate;      /* 0: out = y; 1: out = h + g*y (h = x) */
-    int32_t bias_in_weights; /* 0: bias only changes selection */
+    int32_t res_gate;      /* ORC_RES_NONE: out = b; LINEAR: out = h + g*b; MUSE: alpha*h + beta*b
+                              (h = x, b = the branch output after the optional output norm) */
+    int32_t bias_in_weights; /* softmax router: 0 = bias only changes selection */
     double eps_in, eps_ex;
     int32_t mirror;        /* 1: round z, a and m to the intermediate dtype (debug aid) */
     int32_t interm;        /* intermediate dtype of mirror mode: ORC_BF16 or ORC_F16 */
+    int32_t router_fn;     /* ORC_ROUTER_SOFTMAX or ORC_ROUTER_SIGMOID */
+    double out_mult;       /* sigmoid router: logit multiplier before the sigmoid */
+    double rsf;            /* sigmoid router: routed scaling factor of the weights */
+    int32_t lat_norm;      /* norm of the latent P_down u before the experts (C_pre) */
+    int32_t out_norm;      /* norm of the branch output P_up m (the FFN output norm) */
+    double eps_lat, eps_out;
+    double tau, floor_;    /* ORC_RES_MUSE: temperature and floor of the residual gate */
 } orc_desc;
 
 typedef struct {
@@ -72,6 +84,8 @@ typedef struct {
     const float *gamma_in; /* [d] or NULL */
     const float *gamma_ex; /* [L] (ReLU: [d]) or NULL */
     const float *gate;    /* [d] or NULL */
+    const float *gamma_lat; /* [L] or NULL */
+    const float *gamma_out; /* [d] or NULL */
 } orc_tensors;
 
 /* ------------------------------------------------------------------ */
@@ -290,34 +304,90 @@ static void branch_input(const orc_desc *d, const orc_tensors *w, int64_t t, dou
     for (int64_t i = 0; i < d->d; ++i) u[i] = round_act(d->act, u[i]);
 }
 
-/* Router: FP32 logits l (fp64 dot rounded to fp32); selection score
- * s = fp32(l + b); top-k of s; weights = softmax over the kept logits (with
- * the bias only when bias_in_weights). */
+/* ------------------------------------------------------------------ */
+/* Router scores and weights.                                          */
+/*  softmax ([Shazeer] "The gate"; [Gates] latent-experts section for  */
+/*  the FP32 logits and the selection-only bias): selection score      */
+/*  s = fp32(l + b), weights = softmax over the kept logits (over the  */
+/*  kept s when bias_in_weights).                                      */
+/*  sigmoid ([Gates] latent-experts section; [FactSheet] gating        */
+/*  function): sigma = fp32(sigmoid(fp32(l * output_multiplier))), the */
+/*  router being an FP32 module; selection score s = fp32(sigma + b);  */
+/*  weights = the kept sigma divided by (their sum + 1e-15), times the */
+/*  routed scaling factor.                                             */
+/* ------------------------------------------------------------------ */
+
+/* From fp32 logits l[n] and bias b[n] (or NULL): selection scores sel[n]
+ * and the values H[n] the weights are computed from. */
+void orc_router_scores(const orc_desc *d, const float *l, const float *bias, double *sel, double *H) {
+    for (int64_t e = 0; e < d->n; ++e) {
+        float b = bias ? bias[e] : 0.0f;
+        if (d->router_fn == ORC_ROUTER_SIGMOID) {
+            float v = (float)((double)l[e] * d->out_mult);           /* fp32 product */
+            float sg = (float)(1.0 / (1.0 + exp(-(double)v)));       /* fp32 sigmoid */
+            sel[e] = (double)(bias ? sg + b : sg);                  /* fp32 add */
+            H[e] = (double)sg;
+        } else {
+            float sf = bias ? l[e] + b : l[e];                      /* fp32 add */
+            sel[e] = (double)sf;
+            H[e] = d->bias_in_weights ? (double)sf : (double)l[e];
+        }
+    }
+}
+
+/* Weights of the kept experts idx[0..k) from the values H. */
+void orc_router_weights(const orc_desc *d, const double *H, const int32_t *idx, int64_t k, double *w) {
+    if (d->router_fn == ORC_ROUTER_SIGMOID) {
+        double sum = 0.0;
+        for (int64_t j = 0; j < k; ++j) sum += H[idx[j]];
+        for (int64_t j = 0; j < k; ++j) w[j] = H[idx[j]] / (sum + 1e-15) * d->rsf;
+    } else {
+        orc_softmax_kept(H, idx, k, w);
+    }
+}
+
+/* Router of one token: FP32 logits l (fp64 dot rounded to fp32), scores,
+ * top-k of the selection scores (or the forced experts), weights. */
 static void route(const orc_desc *d, const orc_tensors *w, const double *u, const int32_t *forced,
                   float *logits_out, int32_t *idx, double *wt, double *margin) {
     int64_t n = d->n, k = d->k;
     double *l = (double *)malloc(sizeof(double) * (size_t)n);
+    float *lf = (float *)malloc(sizeof(float) * (size_t)n);
     double *s = (double *)malloc(sizeof(double) * (size_t)n);
     double *H = (double *)malloc(sizeof(double) * (size_t)n);
     matvec(w->router_w, d->rdt, n, d->d, 0, n, u, l);
     for (int64_t e = 0; e < n; ++e) {
-        float lf = (float)l[e];
-        float sf = w->bias ? lf + w->bias[e] : lf; /* fp32 add */
-        l[e] = (double)lf;
-        s[e] = (double)sf;
-        H[e] = d->bias_in_weights ? s[e] : l[e];
-        if (logits_out) logits_out[e] = lf;
+        lf[e] = (float)l[e];
+        if (logits_out) logits_out[e] = lf[e];
     }
+    orc_router_scores(d, lf, w->bias, s, H);
     if (forced) {
         memcpy(idx, forced, sizeof(int32_t) * (size_t)k);
         if (margin) *margin = NAN;
     } else {
         orc_topk(s, n, k, idx, margin);
     }
-    orc_softmax_kept(H, idx, k, wt);
+    orc_router_weights(d, H, idx, k, wt);
     free(l);
+    free(lf);
     free(s);
     free(H);
+}
+
+/* ------------------------------------------------------------------ */
+/* Residual gate ([Gates] "Residual gates: derive the advertised       */
+/* intuition carefully"; [FactSheet] residual design), coordinate-wise */
+/* with w = g / tau: beta = sigmoid(w), alpha = sqrt(max(sigmoid(-w) * */
+/* (1 + beta), floor)); out = alpha * r + beta * b.  The product is    */
+/* evaluated as written, not rewritten as 1 - beta^2.                  */
+/* ------------------------------------------------------------------ */
+void orc_muse_gate_coeffs(double g, double tau, double floor_, double *alpha, double *beta) {
+    double wv = g / tau;
+    double b = 1.0 / (1.0 + exp(-wv));
+    double sn = 1.0 / (1.0 + exp(wv));
+    double a2 = sn * (1.0 + b);
+    *beta = b;
+    *alpha = sqrt(a2 > floor_ ? a2 : floor_);
 }
 
 /* Expert e applied to its input v (z for SwiGLU experts, u for ReLU
@@ -359,10 +429,14 @@ static void expert_norm(const orc_desc *d, const orc_tensors *w, const double *o
 
 /*
  * Forward pass for tokens tok[0..ntok).  Outputs (each may be NULL):
- *   y     [ntok][d]  the MoE branch output, y = P_up( sum_j w_j N(E_j(z)) )
- *                    ([Shazeer] y = sum_i G(x)_i E_i(x); the up-projection
- *                    is linear, so it is applied once after the sum)
- *   out   [ntok][d]  out = h + g * y (res_gate 1) or y
+ *   y     [ntok][d]  the branch output b that enters the residual gate:
+ *                    P_up( sum_j w_j N(E_j(z)) ) ([Shazeer] y = sum_i
+ *                    G(x)_i E_i(x); the up-projection is linear, so it is
+ *                    applied once after the sum), then the FFN output norm
+ *                    when out_norm is set ([Gates] "The complete layer has
+ *                    two separately normalized residual updates")
+ *   out   [ntok][d]  b, h + g * b (linear gate) or alpha * h + beta * b
+ *                    (Muse gate), h = x
  *   logits[ntok][n]  fp32 router logits
  *   idx   [ntok][k]  selected experts, selection order
  *   wts   [ntok][k]  their gate weights
@@ -383,6 +457,8 @@ int orc_forward(const orc_desc *d, const orc_tensors *w, const int64_t *tok, int
     double *nr = (double *)malloc(sizeof(double) * (size_t)Dx);
     double *m = (double *)malloc(sizeof(double) * (size_t)Dx);
     double *yy = (double *)malloc(sizeof(double) * (size_t)D);
+    double *bb = (double *)malloc(sizeof(double) * (size_t)D);
+    double *zn = (double *)malloc(sizeof(double) * (size_t)Dx);
     int32_t *sel = (int32_t *)malloc(sizeof(int32_t) * (size_t)k);
     double *wt = (double *)malloc(sizeof(double) * (size_t)k);
     double *G = (double *)malloc(sizeof(double) * (size_t)n);
@@ -399,6 +475,12 @@ int orc_forward(const orc_desc *d, const orc_tensors *w, const int64_t *tok, int
         if (L) {
             matvec(w->down_w, d->wdt, L, D, 0, L, u, z);
             if (d->mirror) for (int64_t i = 0; i < L; ++i) z[i] = round_act(d->interm, z[i]);
+            if (d->lat_norm != ORC_NORM_NONE) {
+                /* z = C_pre(P_down u) ([Gates] latent-experts section) */
+                apply_norm(d->lat_norm, z, w->gamma_lat, L, d->eps_lat, d->act, zn);
+                memcpy(z, zn, sizeof(double) * (size_t)L);
+                if (d->mirror) for (int64_t i = 0; i < L; ++i) z[i] = round_act(d->interm, z[i]);
+            }
         } else {
             memcpy(z, u, sizeof(double) * (size_t)D);
         }
@@ -421,12 +503,26 @@ int orc_forward(const orc_desc *d, const orc_tensors *w, const int64_t *tok, int
         if (d->mirror) for (int64_t i = 0; i < Dx; ++i) m[i] = round_act(d->interm, m[i]);
         if (L) matvec(w->up_w, d->wdt, D, L, 0, D, m, yy);
         else memcpy(yy, m, sizeof(double) * (size_t)D);
-        if (y) memcpy(y + q * D, yy, sizeof(double) * (size_t)D);
-        if (out)
-            for (int64_t i = 0; i < D; ++i)
-                out[q * D + i] = d->res_gate ? h[i] + (double)w->gate[i] * yy[i] : yy[i];
+        apply_norm(d->out_norm, yy, w->gamma_out, D, d->eps_out, d->act, bb);
+        if (y) memcpy(y + q * D, bb, sizeof(double) * (size_t)D);
+        if (out) {
+            for (int64_t i = 0; i < D; ++i) {
+                double r;
+                if (d->res_gate == ORC_RES_LINEAR) {
+                    r = h[i] + (double)w->gate[i] * bb[i];
+                } else if (d->res_gate == ORC_RES_MUSE) {
+                    double al, be;
+                    orc_muse_gate_coeffs((double)w->gate[i], d->tau, d->floor_, &al, &be);
+                    r = al * h[i] + be * bb[i];
+                } else {
+                    r = bb[i];
+                }
+                out[q * D + i] = r;
+            }
+        }
     }
-    free(h); free(u); free(z); free(o); free(nr); free(m); free(yy); free(sel); free(wt); free(G);
+    free(h); free(u); free(z); free(o); free(nr); free(m); free(yy); free(bb); free(zn); free(sel); free(wt);
+    free(G);
     return 0;
 }
 

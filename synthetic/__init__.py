@@ -148,16 +148,25 @@ class Preset:
     router_w: str       # "f32" | "bf16"
     in_norm: str = "none"          # "none" | "centered" | "input_scaled"
     expert_norm: str = "none"
-    res_gate: str = "none"         # "none" | "linear"
+    res_gate: str = "none"         # "none" | "linear" | "muse"
     eps_in: float = 1e-5
     eps_expert: float = 1e-6
     layer_seed: int = 1
     input_seed: int = 1
-    router_bias: str = "none"      # "none" | "zipf"
+    router_bias: str = "none"      # "none" | "zipf" | "normal" (N(0, 0.05) correction bias)
     chunks: int = 1
     w_std: float = 0.02            # latent layers; c0 uses 1/sqrt(fan_in)
     bias_in_weights: int = 0
     interm: str = "f16"            # dtype a device keeps z, SwiGLU output and m in: "f16" | "bf16"
+    router_fn: str = "softmax"     # "softmax" | "sigmoid"
+    out_mult: float = 1.0          # sigmoid router: logit multiplier
+    routed_scale: float = 1.0      # sigmoid router: routed scaling factor
+    latent_norm: str = "none"      # norm of the latent z before the experts: "none" | "centered"
+    eps_latent: float = 1e-5
+    out_norm: str = "none"         # norm of the branch output: "none" | "centered" | "input_scaled"
+    eps_out: float = 1e-5
+    res_tau: float = 0.3           # Muse residual gate temperature and floor
+    res_floor: float = 1e-3
 
     @property
     def chunk_T(self) -> int:
@@ -182,6 +191,20 @@ PRESETS = {
     "c4c": _latent("c4c", 32768, 4, weights="mxfp4", in_norm="centered", chunks=4),
     "c4i": _latent("c4i", 32768, 4, weights="mxfp4", in_norm="input_scaled", chunks=4),
 }
+
+
+def muse(name: str = "muse", T: int = 8192, input_seed: int = 5, **kw) -> Preset:
+    """The latent layer with the Muse sublayer around it: centered input
+    norm, sigmoid router with a small correction bias, latent pre-norm,
+    input-scaled expert and FFN output norms (block epsilon 1e-5), and the
+    alpha/beta residual gate."""
+    base = dict(weights="bf16", in_norm="centered", eps_in=1e-5, router_fn="sigmoid", router_bias="normal",
+                latent_norm="centered", out_norm="input_scaled", res_gate="muse")
+    base.update(kw)
+    return dataclasses.replace(_latent(name, T, input_seed), eps_expert=1e-5, **base)
+
+
+MUSE_PRESETS = {"m1": muse("m1", 64, 6), "m2": muse("m2", 8192, 5)}
 
 
 def small(name: str = "small", T: int = 77, d: int = 512, L: int = 256, F: int = 256, n: int = 16,
@@ -254,12 +277,21 @@ def layer_params(p: Preset, formats=None) -> dict:
                 out[key + "@" + f] = a
     if p.expert_norm != "none":
         out["gamma_ex"] = normal_f32(s, "gamma_expert", Kin, 0.02)
-    if p.res_gate != "none":
+    if p.res_gate == "linear":
         out["gate"] = uniform_f32(s, "res_gate", p.d, 0.0, 1.0)
+    elif p.res_gate == "muse":
+        # spans the floor: alpha is clamped where g > 2.28 (tau 0.3, floor 1e-3)
+        out["gate"] = uniform_f32(s, "res_gate_muse", p.d, -3.0, 3.0)
     if p.in_norm != "none":
         out["gamma_in"] = normal_f32(s, "gamma_in", p.d, 0.02)
+    if p.latent_norm != "none":
+        out["gamma_lat"] = normal_f32(s, "gamma_latent", p.L, 0.02)
+    if p.out_norm != "none":
+        out["gamma_out"] = normal_f32(s, "gamma_out", p.d, 0.02)
     if p.router_bias == "zipf":
         out["bias"] = zipf_bias(p.n)
+    elif p.router_bias == "normal":
+        out["bias"] = normal_f32(s, "router_bias", p.n, 0.05)
     return out
 
 

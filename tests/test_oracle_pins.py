@@ -221,14 +221,26 @@ def _numpy_layer(cfg, t, act_round):
     else:
         u = x
     logits = (u @ t["router_w"].astype(np.float64).T).astype(np.float32)
-    score = logits + t["bias"] if "bias" in t else logits
+    sigmoid = cfg.get("router_fn", "softmax") == "sigmoid"
+    if sigmoid:
+        v = (logits.astype(np.float64) * cfg.get("out_mult", 1.0)).astype(np.float32)
+        basis = scipy.special.expit(v.astype(np.float64)).astype(np.float32)
+    else:
+        basis = logits
+    score = basis + t["bias"] if "bias" in t else basis
     n, k, F = cfg["n"], cfg["k"], cfg["F"]
     G = np.zeros((T, n))
     for i in range(T):
         order = sorted(range(n), key=lambda e: (-float(score[i, e]), e))[:k]
-        H = logits[i, order].astype(np.float64)
-        G[i, order] = scipy.special.softmax(H)
+        H = basis[i, order].astype(np.float64)
+        if sigmoid:
+            G[i, order] = H / (H.sum() + 1e-15) * cfg.get("routed_scale", 1.0)
+        else:
+            G[i, order] = scipy.special.softmax(H)
     z = u @ t["down_w"].astype(np.float64).T if cfg["L"] else u
+    if cfg.get("latent_norm", "none") == "centered":
+        z = (1 + t["gamma_lat"].astype(np.float64)) * z / np.sqrt((z * z).mean(1, keepdims=True)
+                                                                 + cfg["eps_latent"])
     m = np.zeros_like(z)
     for e in range(n):
         W1 = t["w1"][e].astype(np.float64)
@@ -243,7 +255,19 @@ def _numpy_layer(cfg, t, act_round):
             o = s / np.sqrt((s * s).mean(1, keepdims=True) + cfg["eps_expert"])
         m += G[:, e:e + 1] * o
     y = m @ t["up_w"].astype(np.float64).T if cfg["L"] else m
-    out = x + t["gate"].astype(np.float64) * y if cfg["res_gate"] == "linear" else y
+    if cfg.get("out_norm", "none") == "input_scaled":
+        s = act_round((1 + t["gamma_out"].astype(np.float64)) * y)
+        y = s / np.sqrt((s * s).mean(1, keepdims=True) + cfg["eps_out"])
+    g = t["gate"].astype(np.float64) if "gate" in t else None
+    if cfg["res_gate"] == "linear":
+        out = x + g * y
+    elif cfg["res_gate"] == "muse":
+        w = g / cfg.get("res_tau", 0.3)
+        beta = scipy.special.expit(w)
+        alpha = np.sqrt(np.maximum(scipy.special.expit(-w) * (1 + beta), cfg.get("res_floor", 1e-3)))
+        out = alpha * x + beta * y
+    else:
+        out = y
     return G, y, out
 
 
@@ -393,3 +417,200 @@ def test_round_f16_matches_library_and_ties():
     ref = torch.tensor(vals).to(torch.float16).to(torch.float64).numpy()
     np.testing.assert_array_equal(ours, ref)
     assert oracle.round_f16(1.0 + 2 ** -11) == 1.0 and oracle.round_f16(65520.0) == np.inf
+
+
+# ---------------------------------------------------------------------------
+# Sigmoid router (gates page, "Latent experts: normalization happens before
+# the weighted sum": FP32 logits times output_multiplier, sigmoid, a
+# selection-only correction bias, weights = kept sigmoids / (sum + 1e-15)
+# times routed_scaling_factor; fact sheet: gating function sigmoid)
+# ---------------------------------------------------------------------------
+
+def _sig_layer(logits, k, **kw):
+    n = len(logits)
+    x, W = _router_layer(np.asarray(logits, np.float32))
+    cfg = f32cfg(d=n, n=n, k=k, F=2, router_fn="sigmoid", **kw)
+    t = {"x": x, "router_w": W, "w1": np.zeros((n, 2, n), np.float32), "w2": np.zeros((n, n, 2), np.float32)}
+    return cfg, t
+
+
+def test_sigmoid_router_closed_form():
+    # logits 0, 1, -1, 2 times ln 3: sigmoids 1/2, 3/4, 1/4, 9/10 (sigma(m ln 3) = 3^m / (3^m + 1))
+    cfg, t = _sig_layer([0, 1, -1, 2], 2, out_mult=math.log(3), routed_scale=2.0)
+    sel, H = oracle.router_scores(cfg, [[0, 1, -1, 2]])
+    np.testing.assert_allclose(H[0], [0.5, 0.75, 0.25, 0.9], rtol=1e-7)   # fp32 sigmoids
+    np.testing.assert_array_equal(sel, H)                                  # no bias
+    r = oracle.forward(cfg, t)
+    assert list(r["idx"][0]) == [3, 1]
+    np.testing.assert_allclose(r["w"][0], [2 * 0.9 / 1.65, 2 * 0.75 / 1.65], rtol=1e-7)   # 12/11, 10/11
+    # a bias of +1 on expert 2 moves it into the selection (1.25 > 0.9 > 0.75) but
+    # its weight still uses its own sigmoid 1/4: weights 2 * (1/4, 9/10) / (23/20)
+    t["bias"] = np.array([0, 0, 1, 0], np.float32)
+    r = oracle.forward(cfg, t)
+    assert list(r["idx"][0]) == [2, 3]
+    np.testing.assert_allclose(r["w"][0], [10 / 23, 36 / 23], rtol=1e-7)
+    assert abs(r["margin"][0] - 0.15) < 1e-6   # 0.9 - 0.75
+
+
+def test_sigmoid_router_saturation_and_underflow():
+    # every kept sigmoid rounds to 0 in fp32: the 1e-15 keeps the weights at exactly 0
+    cfg, t = _sig_layer([-200, -300, -150, -180], 2, routed_scale=1.0)
+    r = oracle.forward(cfg, t)
+    assert list(r["idx"][0]) == [0, 1]          # all scores 0: ties to the lower id
+    np.testing.assert_array_equal(r["w"][0], [0.0, 0.0])
+    # every sigmoid rounds to 1: equal weights rsf / (k + 1e-15)
+    cfg, t = _sig_layer([40, 50, 60, 70], 3, routed_scale=2.5)
+    r = oracle.forward(cfg, t)
+    assert list(r["idx"][0]) == [0, 1, 2]
+    np.testing.assert_allclose(r["w"][0], 2.5 / 3, rtol=1e-15)
+
+
+@pytest.mark.parametrize("n,k", [(16, 4), (256, 8)])
+def test_sigmoid_selection_is_monotone_and_weights_renormalise(n, k):
+    rng = np.random.default_rng(n + k)
+    for _ in range(20):
+        lg = (rng.standard_normal(n) * 2).astype(np.float32)
+        cs = f32cfg(n=n, k=k, router_fn="sigmoid", out_mult=0.7, routed_scale=1.5)
+        sel, H = oracle.router_scores(cs, lg)
+        idx, _ = oracle.topk(sel[0], k)
+        # the sigmoid is increasing: without a bias it keeps the k largest logits
+        idx_l, _ = oracle.topk(lg.astype(np.float64), k)
+        assert set(idx) == set(idx_l)
+        w = oracle.router_weights(cs, H[0], idx)
+        assert (w > 0).all() and abs(w.sum() - 1.5) < 1e-12
+        # k = n: every sigmoid, normalised by their total
+        wn = oracle.router_weights(cs, H[0], np.arange(n, dtype=np.int32))
+        np.testing.assert_allclose(wn, 1.5 * H[0] / H[0].sum(), rtol=1e-13)
+
+
+# ---------------------------------------------------------------------------
+# Residual gate (gates page, "Residual gates: derive the advertised
+# intuition carefully"; fact sheet residual design)
+# ---------------------------------------------------------------------------
+
+def test_residual_gate_identity_and_floor():
+    g = np.linspace(-2.2, 2.2, 89)
+    al, be = oracle.muse_gate_coeffs(g, 0.3, 1e-3)
+    # sigma(-w) = 1 - beta, so while the floor is inactive alpha^2 = 1 - beta^2
+    np.testing.assert_allclose(al ** 2 + be ** 2, 1.0, rtol=0, atol=4e-16)
+    assert (np.diff(be) > 0).all() and (np.diff(al) < 0).all()
+    np.testing.assert_allclose(be, 1 / (1 + np.exp(-g / 0.3)), rtol=1e-15)
+    # the floor: sigma(-w)(1 + beta) < 1e-3 once g / 0.3 > ln(2000) (g > 2.28)
+    al, be = oracle.muse_gate_coeffs([2.27, 2.29, 3.0, 30.0], 0.3, 1e-3)
+    assert al[0] > math.sqrt(1e-3)
+    np.testing.assert_array_equal(al[1:], math.sqrt(1e-3))
+    assert al[3] ** 2 + be[3] ** 2 > 1.0009      # clamped: the identity no longer holds
+    # a temperature of 0.3 against 1: the same g gives a sharper beta
+    _, b1 = oracle.muse_gate_coeffs([0.6], 1.0, 1e-3)
+    _, b3 = oracle.muse_gate_coeffs([0.6], 0.3, 1e-3)
+    assert b3[0] > b1[0] > 0.5
+
+
+def _gate_layer(W2, gate_g):
+    """d = 2 ReLU layer, one expert with W1 = I: y = W2 relu(x); Muse gate g."""
+    cfg = f32cfg(d=2, n=1, k=1, F=2, res_gate="muse", res_tau=0.3, res_floor=1e-3)
+    t = {"x": np.array([[1.0, 0.0]], np.float32), "router_w": np.zeros((1, 2), np.float32),
+         "w1": np.eye(2, dtype=np.float32)[None], "w2": np.asarray(W2, np.float32)[None],
+         "gate": np.full(2, gate_g, np.float32)}
+    return oracle.forward(cfg, t)
+
+
+def test_residual_gate_geometry_worked_example():
+    gd = read_golden("residual_gate_geometry.txt")
+    al, be = oracle.muse_gate_coeffs([0.0], gd["tau"][0], gd["floor"][0])
+    assert be[0] == gd["beta"][0]
+    np.testing.assert_allclose(al[0] ** 2, gd["alpha_sq"][0], rtol=1e-15)
+    # equal-norm residual r = (1, 0) and branch b = W2 relu(r): orthogonal, aligned, opposite
+    cases = {"orthogonal": [[0, 0], [1, 0]], "aligned": [[1, 0], [0, 1]], "opposite": [[-1, 0], [0, -1]]}
+    exact = {"orthogonal": 1.0, "aligned": 1 + math.sqrt(3) / 2, "opposite": 1 - math.sqrt(3) / 2}
+    for name, W2 in cases.items():
+        r = _gate_layer(W2, 0.0)
+        f = float((r["out"][0] ** 2).sum())
+        assert abs(f - gd[name][0]) < 5e-4, name          # the page's three places
+        np.testing.assert_allclose(f, exact[name], rtol=1e-14)
+
+
+def test_muse_gate_wiring_against_linear_gate():
+    # g = 0 everywhere: out = (sqrt 3 / 2) x + y / 2, where x + y is the linear gate's output with g = 1
+    p = synthetic.small(T=6, d=64, L=32, F=32, n=8, k=2, out_norm="input_scaled", latent_norm="centered")
+    prm = synthetic.layer_params(p)
+    t = dict(prm, x=synthetic.inputs(p))
+    t["gate"] = np.ones(p.d, np.float32)
+    r_lin = oracle.forward(p.cfg(), t)
+    cfg = dict(p.cfg(), res_gate="muse")
+    t["gate"] = np.zeros(p.d, np.float32)
+    r_m = oracle.forward(cfg, t)
+    x = synthetic.bf16_to_f32(t["x"]).astype(np.float64)
+    np.testing.assert_allclose(r_m["y"], r_lin["y"], rtol=0, atol=0)
+    np.testing.assert_allclose(r_m["out"], math.sqrt(3) / 2 * x + 0.5 * (r_lin["out"] - x), rtol=1e-14, atol=1e-14)
+
+
+# ---------------------------------------------------------------------------
+# Latent pre-norm z = C_pre(P_down u) and the FFN output norm (gates page,
+# "Latent experts ..." and "The complete layer has two separately normalized
+# residual updates")
+# ---------------------------------------------------------------------------
+
+def _f32_latent(**kw):
+    rng = np.random.default_rng(21)
+    d, L, F, n, k, T = 16, 8, 8, 5, 2, 7
+    cfg = dict(d=d, L=L, n=n, k=k, F=F, kind="swiglu3", act="f32", weights="f32", router_w="f32",
+               in_norm="none", expert_norm="input_scaled", res_gate="none", eps_in=0.0, eps_expert=1e-6,
+               eps_latent=0.0, eps_out=0.0)
+    cfg.update(kw)
+    f = lambda *s: (rng.standard_normal(s) * 0.5).astype(np.float32)
+    t = {"x": f(T, d), "router_w": f(n, d), "down_w": f(L, d), "w1": f(n, 2 * F, L), "w2": f(n, L, F),
+         "up_w": f(d, L), "gamma_ex": f(L) * 0.1, "gamma_lat": f(L) * 0.2, "gamma_out": f(d) * 0.2,
+         "gate": rng.uniform(-3, 3, d).astype(np.float32)}
+    return cfg, t
+
+
+def test_latent_prenorm_removes_the_scale_of_the_down_projection():
+    cfg, t = _f32_latent(latent_norm="centered")
+    r = oracle.forward(cfg, t)
+    t4 = dict(t, down_w=t["down_w"] * 4)            # exact in fp32: C(4z) = C(z) with eps = 0
+    np.testing.assert_allclose(oracle.forward(cfg, t4)["y"], r["y"], rtol=1e-13, atol=1e-15)
+    cfg0 = dict(cfg, latent_norm="none")           # without it the SwiGLU sees a 4x larger z
+    assert np.abs(oracle.forward(cfg0, t4)["y"] - oracle.forward(cfg0, t)["y"]).max() > 1e-3
+
+
+def test_output_norm_scale_invariance_and_unit_rms():
+    cfg, t = _f32_latent(out_norm="input_scaled")
+    r = oracle.forward(cfg, t)
+    np.testing.assert_allclose(np.sqrt((r["y"] ** 2).mean(1)), 1.0, rtol=1e-13)   # eps = 0: unit RMS
+    t2 = dict(t, up_w=t["up_w"] * 2)
+    np.testing.assert_array_equal(oracle.forward(cfg, t2)["y"], r["y"])          # powers of two are exact
+    # I_gamma, not C_gamma: the gain enters before the denominator
+    cc = oracle.forward(dict(cfg, out_norm="centered"), t)
+    assert np.abs(cc["y"] - r["y"]).max() > 1e-3
+
+
+@pytest.mark.parametrize("bias", [False, True])
+def test_bruteforce_muse_layer_f32(bias):
+    cfg, t = _f32_latent(in_norm="centered", latent_norm="centered", out_norm="input_scaled", res_gate="muse",
+                         router_fn="sigmoid", out_mult=0.8, routed_scale=1.7, eps_in=1e-5, eps_latent=1e-5,
+                         eps_out=1e-5)
+    t["gamma_in"] = (np.random.default_rng(3).standard_normal(cfg["d"]) * 0.1).astype(np.float32)
+    if bias:
+        t["bias"] = (np.random.default_rng(4).standard_normal(cfg["n"]) * 0.3).astype(np.float32)
+    r = oracle.forward(cfg, t)
+    rd = oracle.forward(cfg, t, dense=True)
+    G, y, out = _numpy_layer(cfg, t, lambda v: v.astype(np.float32).astype(np.float64))
+    for i in range(t["x"].shape[0]):
+        np.testing.assert_allclose(G[i, r["idx"][i]], r["w"][i], rtol=1e-13)
+        assert (G[i] > 0).sum() == cfg["k"]
+    np.testing.assert_allclose(r["y"], y, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(r["out"], out, rtol=1e-10, atol=1e-12)
+    np.testing.assert_allclose(r["y"], rd["y"], rtol=1e-12, atol=1e-13)
+
+
+def test_bruteforce_muse_bf16_small_layer():
+    p = synthetic.muse("mini", T=5, d=64, L=32, F=32, n=8, k=2, layer_seed=11)
+    t = dict(synthetic.layer_params(p), x=synthetic.inputs(p))
+    cfg = p.cfg()
+    r = oracle.forward(cfg, t)
+    tf = {kk: (synthetic.bf16_to_f32(v) if v.dtype == np.uint16 else v) for kk, v in t.items()}
+    bf = lambda v: torch.from_numpy(np.asarray(v, np.float64)).to(torch.bfloat16).to(torch.float64).numpy()
+    G, y, out = _numpy_layer(cfg, tf, bf)
+    np.testing.assert_allclose(r["y"], y, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(r["out"], out, rtol=1e-9, atol=1e-12)
