@@ -56,13 +56,14 @@ typedef enum {
 enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1, MOE_DT_MXFP4 = 2, MOE_DT_F16 = 3 };
 enum { MOE_NORM_NONE = 0, MOE_NORM_CENTERED = 1, MOE_NORM_INPUT_SCALED = 2 };
 enum { MOE_EXPERT_RELU2 = 0, MOE_EXPERT_SWIGLU3 = 1 };
-enum { MOE_RES_NONE = 0, MOE_RES_LINEAR = 1 };
+enum { MOE_RES_NONE = 0, MOE_RES_LINEAR = 1, MOE_RES_MUSE = 2 };
+enum { MOE_ROUTER_SOFTMAX = 0, MOE_ROUTER_SIGMOID = 1 };
 
 /* Number of timed stages; stage s is bracketed by stage_events[2s], [2s+1]. */
 enum {
     MOE_STAGE_IN_NORM = 0, MOE_STAGE_ROUTER = 1, MOE_STAGE_TOPK = 2, MOE_STAGE_PERMUTE = 3,
     MOE_STAGE_DOWN = 4, MOE_STAGE_GEMM1 = 5, MOE_STAGE_GEMM2 = 6, MOE_STAGE_COMBINE = 7,
-    MOE_STAGE_UP = 8, MOE_NUM_STAGES = 9
+    MOE_STAGE_UP = 8, MOE_STAGE_RESGATE = 9, MOE_NUM_STAGES = 10
 };
 
 /*
@@ -95,10 +96,18 @@ enum {
  *   in_norm      norm of x before router and down-projection (u = x if NONE)
  *   expert_norm  norm of each expert output before its routing weight
  *                (gain gamma_expert, one vector shared by all experts)
- *   res_gate     MOE_RES_LINEAR: out = x + res_gate * y; NONE: out = y
- *   bias_in_weights  0: router_bias only changes which experts are selected
- *                (weights use the unbiased logits); 1: it also enters the
- *                softmax
+ *   res_gate     residual update of the branch output b (b = y, or the
+ *                output norm of y when out_norm is set) with the residual x:
+ *                MOE_RES_NONE: out = b; MOE_RES_LINEAR: out = x + g * b;
+ *                MOE_RES_MUSE: out = alpha * x + beta * b, coordinate-wise
+ *                with w = g / res_tau, beta = sigmoid(w), alpha =
+ *                sqrt(max(sigmoid(-w) * (1 + beta), res_floor)) (flozi.net
+ *                "Muse Spark Open: Norm-Preserving Gates Are Not a Norm
+ *                Guarantee", "Residual gates: derive the advertised
+ *                intuition carefully"; g = gains->res_gate, fp32 math)
+ *   bias_in_weights  softmax router: 0 = router_bias only changes which
+ *                experts are selected (weights use the unbiased logits);
+ *                1 = it also enters the softmax.  Must be 0 for sigmoid.
  *   eps_in, eps_expert  RMS epsilons: R(v) = v * (mean(v^2) + eps)^-1/2
  *   interm_dtype dtype of the activations the latent path stores between
  *                its GEMMs and feeds to MFMA: the latent z, the SwiGLU
@@ -110,6 +119,24 @@ enum {
  *                magnitude >= 65504 becomes +-inf and poisons its outputs.
  *                MOE_DT_BF16: bf16 everywhere (no range limit beyond bf16).
  *                Ignored on the fp32 path.
+ *   router_fn    MOE_ROUTER_SOFTMAX (0): Softmax(KeepTopK) of the logits;
+ *                MOE_ROUTER_SIGMOID: s = sigmoid(logit * router_out_mult)
+ *                in fp32, selection on s + router_bias, weights = the kept
+ *                s / (their sum + 1e-15) * routed_scale (same page, "Latent
+ *                experts: normalization happens before the weighted sum").
+ *                router_out_mult and routed_scale are read only for sigmoid.
+ *   latent_norm  MOE_NORM_CENTERED: z = C_pre(P_down u), the output-scaled
+ *                RMS norm of the latent with gain gains->gamma_latent [L]
+ *                and eps_latent, before the experts read it (same page and
+ *                section); MOE_NORM_NONE: z = P_down u.  Latent path only.
+ *   out_norm     norm of the branch output y = P_up m before the residual
+ *                gate (same page, "The complete layer has two separately
+ *                normalized residual updates"): MOE_NORM_INPUT_SCALED,
+ *                CENTERED (gain gains->gamma_out [d], eps_out; the scaled
+ *                vector (1 + gamma) y is stored as bf16) or NONE.  Latent
+ *                path only.
+ *   res_tau, res_floor  MOE_RES_MUSE temperature (> 0; the page's default
+ *                is 0.3) and floor (>= 0; 1e-3 on the page)
  */
 typedef struct {
     int64_t T;
@@ -129,19 +156,32 @@ typedef struct {
     float eps_in;
     float eps_expert;
     int32_t interm_dtype;
-    int32_t reserved;
+    int32_t router_fn;
+    float router_out_mult;
+    float routed_scale;
+    int32_t latent_norm;
+    float eps_latent;
+    int32_t out_norm;
+    float eps_out;
+    float res_tau;
+    float res_floor;
 } moe_desc;
 
 /* FP32 parameter vectors (device pointers; NULL where the stage is off).
  *   router_bias  [n]  selection bias (may be NULL even when routing)
  *   gamma_in     [d]  input-norm gain (gain applied as 1 + gamma)
  *   gamma_expert [L]  per-expert output-norm gain, shared by all experts
- *   res_gate     [d]  residual gate vector g */
+ *   res_gate     [d]  residual gate vector g (required by LINEAR and MUSE)
+ *   gamma_latent [L]  latent pre-norm gain
+ *   gamma_out    [d]  branch output-norm gain
+ * A NULL gain means gamma = 0 (a gain of 1). */
 typedef struct {
     const float *router_bias;
     const float *gamma_in;
     const float *gamma_expert;
     const float *res_gate;
+    const float *gamma_latent;
+    const float *gamma_out;
 } moe_gains;
 
 /* Optional outputs for inspection (device pointers, each may be NULL).
@@ -152,10 +192,11 @@ typedef struct {
  *                          the exclusive prefix sum
  *   perm_tok, perm_slot [T*k] int32  the (token, slot) pairs sorted by
  *                          (expert, token)
- *   y        [T][d] fp32   branch output before the residual gate
+ *   y        [T][d] fp32   branch output b entering the residual gate (after
+ *                          the output norm when out_norm is set)
  *   pos      [T][k] int32  perm position of (t, j)
  *   Intermediates of the bf16 latent path (ignored on the fp32 path):
- *   z        [T][L]  bf16  down-projection output
+ *   z        [T][L]  bf16  down-projection output (after the latent pre-norm)
  *   act      [T*k][F] bf16 SwiGLU output, rows in perm order
  *   S        [T*k][L] bf16 bf16((1+gamma) * expert output), perm order
  *   ssq      [T*k][L/16] fp32  per-16-column sums of squares of S (of the
@@ -213,10 +254,11 @@ int moe_layer_forward(const moe_desc *desc, const void *x, const void *router_w,
                       moe_debug *dbg, void *stream);
 
 /*
- * Router stage alone: fp32 logits l = u W_r^T, selection on s = l + bias
- * (fp32), top-k by (s descending, expert id ascending), softmax of the kept
- * logits ("The gate", Softmax(KeepTopK)).  u is [T][d] of desc->act_dtype
- * (the branch input: no input norm is applied here).
+ * Router stage alone: fp32 logits l = u W_r^T, then desc->router_fn:
+ * softmax: selection on s = l + bias (fp32), top-k by (s descending,
+ * expert id ascending), softmax of the kept logits ("The gate",
+ * Softmax(KeepTopK)); sigmoid: see moe_desc.router_fn.  u is [T][d] of
+ * desc->act_dtype (the branch input: no input norm is applied here).
  *   topk_idx [T][k] int32, topk_w [T][k] fp32 (outputs)
  *   logits   [T][n] fp32 (optional output, may be NULL)
  *   workspace >= moe_router_workspace_bytes(desc), required when logits is

@@ -71,7 +71,7 @@ def lib():
         _lib = ctypes.CDLL(_LIB)
         vp, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
         _lib.orc_forward.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Tensors), vp, i64, vp, i32,
-                                     vp, vp, vp, vp, vp, vp]
+                                     vp, vp, vp, vp, vp, vp, vp]
         _lib.orc_permute.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp]
         _lib.orc_rms_centered.argtypes = [vp, vp, i64, dbl, vp]
         _lib.orc_rms_input_scaled.argtypes = [vp, vp, i64, dbl, ctypes.c_int, vp]
@@ -129,6 +129,9 @@ def forward(cfg: dict, t: dict, tokens=None, forced=None, dense: bool = False, m
     optional float32 bias, gamma_in, gamma_ex, gate, gamma_lat, gamma_out.
     tokens: int64 array of token ids (None: all T rows of x).
     forced: int32 [ntok][k] expert ids (None: route).
+    Outputs: logits, idx, w, margin; with want_outputs also y (the branch
+    output entering the residual gate), out, and ypre (the branch output
+    before the output norm).
     """
     desc = make_desc(cfg, mirror)
     T = t["x"].shape[0]
@@ -152,10 +155,11 @@ def forward(cfg: dict, t: dict, tokens=None, forced=None, dense: bool = False, m
     if want_outputs:
         res["y"] = np.zeros((ntok, d), np.float64)
         res["out"] = np.zeros((ntok, d), np.float64)
+        res["ypre"] = np.zeros((ntok, d), np.float64)
     fz = None if forced is None else _c(forced, np.int32)
     rc = lib().orc_forward(ctypes.byref(desc), ctypes.byref(tens), _p(tok), ntok, _p(fz), int(dense),
                            _p(res.get("y")), _p(res.get("out")), _p(res["logits"]), _p(res["idx"]),
-                           _p(res["w"]), _p(res["margin"]))
+                           _p(res["w"]), _p(res["margin"]), _p(res.get("ypre")))
     assert rc == 0
     res["tokens"] = tok
     return res

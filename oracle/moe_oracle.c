@@ -437,6 +437,7 @@ static void expert_norm(const orc_desc *d, const orc_tensors *w, const double *o
  *                    two separately normalized residual updates")
  *   out   [ntok][d]  b, h + g * b (linear gate) or alpha * h + beta * b
  *                    (Muse gate), h = x
+ *   ypre  [ntok][d]  P_up m, the branch output before the output norm
  *   logits[ntok][n]  fp32 router logits
  *   idx   [ntok][k]  selected experts, selection order
  *   wts   [ntok][k]  their gate weights
@@ -447,7 +448,7 @@ static void expert_norm(const orc_desc *d, const orc_tensors *w, const double *o
  */
 int orc_forward(const orc_desc *d, const orc_tensors *w, const int64_t *tok, int64_t ntok,
                 const int32_t *forced, int32_t dense, double *y, double *out, float *logits,
-                int32_t *idx, double *wts, double *margin) {
+                int32_t *idx, double *wts, double *margin, double *ypre) {
     int64_t D = d->d, L = d->L, k = d->k, n = d->n;
     int64_t Dx = L ? L : D; /* width of the expert space */
     double *h = (double *)malloc(sizeof(double) * (size_t)D);
@@ -470,7 +471,7 @@ int orc_forward(const orc_desc *d, const orc_tensors *w, const int64_t *tok, int
         if (idx) memcpy(idx + q * k, sel, sizeof(int32_t) * (size_t)k);
         if (wts) memcpy(wts + q * k, wt, sizeof(double) * (size_t)k);
         if (margin) margin[q] = mg;
-        if (!y && !out) continue;
+        if (!y && !out && !ypre) continue;
         /* expert-space input */
         if (L) {
             matvec(w->down_w, d->wdt, L, D, 0, L, u, z);
@@ -503,6 +504,7 @@ int orc_forward(const orc_desc *d, const orc_tensors *w, const int64_t *tok, int
         if (d->mirror) for (int64_t i = 0; i < Dx; ++i) m[i] = round_act(d->interm, m[i]);
         if (L) matvec(w->up_w, d->wdt, D, L, 0, D, m, yy);
         else memcpy(yy, m, sizeof(double) * (size_t)D);
+        if (ypre) memcpy(ypre + q * D, yy, sizeof(double) * (size_t)D);
         apply_norm(d->out_norm, yy, w->gamma_out, D, d->eps_out, d->act, bb);
         if (y) memcpy(y + q * D, bb, sizeof(double) * (size_t)D);
         if (out) {

@@ -23,8 +23,10 @@ MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, M
 DT = {"f32": 0, "bf16": 1, "mxfp4": 2, "f16": 3}
 NORM = {"none": 0, "centered": 1, "input_scaled": 2}
 KIND = {"relu2": 0, "swiglu3": 1}
-RES = {"none": 0, "linear": 1}
-STAGES = ["in_norm", "router", "topk", "permute", "down", "gemm1", "gemm2", "combine", "up"]
+RES = {"none": 0, "linear": 1, "muse": 2}
+ROUTER = {"softmax": 0, "sigmoid": 1}
+STAGES = ["in_norm", "router", "topk", "permute", "down", "gemm1", "gemm2", "combine", "up", "resgate"]
+GAINS = ("router_bias", "gamma_in", "gamma_expert", "res_gate", "gamma_latent", "gamma_out")
 
 
 class MoeError(RuntimeError):
@@ -39,12 +41,14 @@ class moe_desc(ctypes.Structure):
                 ("expert_kind", ctypes.c_int32), ("act_dtype", ctypes.c_int32), ("router_dtype", ctypes.c_int32),
                 ("weight_dtype", ctypes.c_int32), ("in_norm", ctypes.c_int32), ("expert_norm", ctypes.c_int32),
                 ("res_gate", ctypes.c_int32), ("bias_in_weights", ctypes.c_int32), ("eps_in", ctypes.c_float),
-                ("eps_expert", ctypes.c_float), ("interm_dtype", ctypes.c_int32), ("reserved", ctypes.c_int32)]
+                ("eps_expert", ctypes.c_float), ("interm_dtype", ctypes.c_int32), ("router_fn", ctypes.c_int32),
+                ("router_out_mult", ctypes.c_float), ("routed_scale", ctypes.c_float),
+                ("latent_norm", ctypes.c_int32), ("eps_latent", ctypes.c_float), ("out_norm", ctypes.c_int32),
+                ("eps_out", ctypes.c_float), ("res_tau", ctypes.c_float), ("res_floor", ctypes.c_float)]
 
 
 class moe_gains(ctypes.Structure):
-    _fields_ = [("router_bias", ctypes.c_void_p), ("gamma_in", ctypes.c_void_p),
-                ("gamma_expert", ctypes.c_void_p), ("res_gate", ctypes.c_void_p)]
+    _fields_ = [(nm, ctypes.c_void_p) for nm in GAINS]
 
 
 class moe_debug(ctypes.Structure):
@@ -90,12 +94,17 @@ EXPORTED = ["moe_error_string", "moe_validate", "moe_workspace_bytes", "moe_laye
 
 def make_desc(T, d_model, d_latent, n_experts, top_k, d_ff, expert_kind="swiglu3", act="bf16", router="bf16",
               weights="bf16", in_norm="none", expert_norm="none", res_gate="none", bias_in_weights=0,
-              eps_in=1e-5, eps_expert=1e-6, interm="f16") -> moe_desc:
+              eps_in=1e-5, eps_expert=1e-6, interm="f16", router_fn="softmax", out_mult=1.0, routed_scale=1.0,
+              latent_norm="none", eps_latent=1e-5, out_norm="none", eps_out=1e-5, res_tau=0.3,
+              res_floor=1e-3) -> moe_desc:
     return moe_desc(T=T, d_model=d_model, d_latent=d_latent, n_experts=n_experts, top_k=top_k, d_ff=d_ff,
                     expert_kind=KIND[expert_kind], act_dtype=DT[act], router_dtype=DT[router],
                     weight_dtype=DT[weights], in_norm=NORM[in_norm], expert_norm=NORM[expert_norm],
                     res_gate=RES[res_gate], bias_in_weights=int(bias_in_weights), eps_in=eps_in,
-                    eps_expert=eps_expert, interm_dtype=DT[interm], reserved=0)
+                    eps_expert=eps_expert, interm_dtype=DT[interm], router_fn=ROUTER[router_fn],
+                    router_out_mult=out_mult, routed_scale=routed_scale, latent_norm=NORM[latent_norm],
+                    eps_latent=eps_latent, out_norm=NORM[out_norm], eps_out=eps_out, res_tau=res_tau,
+                    res_floor=res_floor)
 
 
 def moe_error_string(code: int) -> str:
@@ -149,9 +158,9 @@ def moe_layer_forward(desc: moe_desc, x, router_w, down_w, expert_w1, expert_w2,
     """Enqueue one layer forward on `stream` (default: torch's current stream).
 
     gains: dict of device fp32 tensors under router_bias, gamma_in,
-    gamma_expert, res_gate (absent = NULL).  dbg: dict of device tensors under
-    the moe_debug field names, plus optionally "stage_events" (an int
-    address of 2*9 hipEvent_t).  workspace: uint8 device tensor of at least
+    gamma_expert, res_gate, gamma_latent, gamma_out (absent = NULL).  dbg:
+    dict of device tensors under the moe_debug field names, plus optionally
+    "stage_events" (an int address of 2 * len(STAGES) hipEvent_t).  workspace: uint8 device tensor of at least
     moe_workspace_bytes(desc) bytes (allocated here when None).
     """
     import torch
@@ -164,7 +173,7 @@ def moe_layer_forward(desc: moe_desc, x, router_w, down_w, expert_w1, expert_w2,
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
     g = moe_gains()
-    for nm in ("router_bias", "gamma_in", "gamma_expert", "res_gate"):
+    for nm in GAINS:
         v = (gains or {}).get(nm)
         if v is not None and v.dtype != torch.float32:
             raise ValueError("gain %s must be float32" % nm)

@@ -80,7 +80,8 @@ hipError_t launch_down_gemm(const GemmArgs &a, int path, bool mx, int ot, hipStr
 hipError_t launch_gemm1(const GemmArgs &a, int path, bool mx, int at, hipStream_t s);
 // Expert GEMM2: grouped, A = act in `at`; EPI_NORM (bf16 S + partial sums) or EPI_ACT with bf16 S.
 hipError_t launch_gemm2(const GemmArgs &a, int path, bool mx, int at, bool norm, hipStream_t s);
-// Up-projection: dense, A = m in `at`, EPI_RESID or EPI_F32.
-hipError_t launch_up_gemm(const GemmArgs &a, int path, bool mx, int at, bool resid, hipStream_t s);
+// Up-projection: dense, A = m in `at`; epi = EPI_RESID, EPI_F32, or EPI_NORM
+// (bf16 (1 + gamma) y and per-16-column sums of squares for the output norm).
+hipError_t launch_up_gemm(const GemmArgs &a, int path, bool mx, int at, int epi, hipStream_t s);
 
 }  // namespace moe

@@ -1266,26 +1266,25 @@ hipError_t launch_gemm2(const GemmArgs &a, int path, bool mx, int at, bool norm,
     return run_path<EPI_ACT, 1, false, true, ACT_BF16, ACT_BF16>(a, path, s);
 }
 
-hipError_t launch_up_gemm(const GemmArgs &a, int path, bool mx, int at, bool resid, hipStream_t s) {
+template <int EPI>
+static hipError_t up_gemm(const GemmArgs &a, int path, bool mx, int at, hipStream_t s) {
     if (at == ACT_F16_W16) {
         if (mx) return hipErrorInvalidValue;
-        if (resid) return run_path<EPI_RESID, 1, false, false, ACT_F16_W16, ACT_BF16>(a, path, s);
-        return run_path<EPI_F32, 1, false, false, ACT_F16_W16, ACT_BF16>(a, path, s);
-    }
-    if (resid) {
-        if (mx) {
-            if (at == ACT_F16) return run_path<EPI_RESID, 1, true, false, ACT_F16, ACT_BF16>(a, path, s);
-            return run_path<EPI_RESID, 1, true, false, ACT_BF16, ACT_BF16>(a, path, s);
-        }
-        if (at == ACT_F16) return run_path<EPI_RESID, 1, false, false, ACT_F16, ACT_BF16>(a, path, s);
-        return run_path<EPI_RESID, 1, false, false, ACT_BF16, ACT_BF16>(a, path, s);
+        return run_path<EPI, 1, false, false, ACT_F16_W16, ACT_BF16>(a, path, s);
     }
     if (mx) {
-        if (at == ACT_F16) return run_path<EPI_F32, 1, true, false, ACT_F16, ACT_BF16>(a, path, s);
-        return run_path<EPI_F32, 1, true, false, ACT_BF16, ACT_BF16>(a, path, s);
+        if (at == ACT_F16) return run_path<EPI, 1, true, false, ACT_F16, ACT_BF16>(a, path, s);
+        return run_path<EPI, 1, true, false, ACT_BF16, ACT_BF16>(a, path, s);
     }
-    if (at == ACT_F16) return run_path<EPI_F32, 1, false, false, ACT_F16, ACT_BF16>(a, path, s);
-    return run_path<EPI_F32, 1, false, false, ACT_BF16, ACT_BF16>(a, path, s);
+    if (at == ACT_F16) return run_path<EPI, 1, false, false, ACT_F16, ACT_BF16>(a, path, s);
+    return run_path<EPI, 1, false, false, ACT_BF16, ACT_BF16>(a, path, s);
+}
+
+hipError_t launch_up_gemm(const GemmArgs &a, int path, bool mx, int at, int epi, hipStream_t s) {
+    if (epi == EPI_RESID) return up_gemm<EPI_RESID>(a, path, mx, at, s);
+    if (epi == EPI_NORM) return up_gemm<EPI_NORM>(a, path, mx, at, s);
+    if (epi == EPI_F32) return up_gemm<EPI_F32>(a, path, mx, at, s);
+    return hipErrorInvalidValue;
 }
 
 }  // namespace moe

@@ -6,14 +6,17 @@
 // Guarantee", section "Latent experts: normalization happens before the
 // weighted sum", and the gate of bobbyburns.tech "816 billion parameters,
 // and only 42 billion show up for each token", section "The gate":
-//   [input norm] -> router GEMM (fp32 logits) -> top-k + softmax ->
-//   permutation (counts, scan, stable scatter, tile lists) ->
-//   down-projection 8192 -> 4096 -> grouped GEMM1 + SwiGLU ->
-//   grouped GEMM2 + per-expert norm partials -> norm + weighted combine ->
-//   up-projection 4096 -> 8192 + residual gate out = x + g * y.
+//   [input norm] -> router GEMM (fp32 logits) -> top-k + softmax or
+//   sigmoid weights -> permutation (counts, scan, stable scatter, tile
+//   lists) -> down-projection 8192 -> 4096 [-> latent pre-norm C_pre] ->
+//   grouped GEMM1 + SwiGLU -> grouped GEMM2 + per-expert norm partials ->
+//   norm + weighted combine -> up-projection 4096 -> 8192 with the linear
+//   residual gate out = x + g * y fused into its epilogue, or [output-norm
+//   partials ->] output norm + residual gate (linear or alpha/beta).
 // The up-projection is linear, so it is applied once to the weighted sum of
 // the normalised expert outputs rather than to each of them.
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <string.h>
 
 #include "../../include/moe.h"
@@ -37,7 +40,7 @@ struct Carve {
 
 struct Layout {
     size_t u, logits, idx, w, counts, offsets, perm_tok, perm_slot, pos, ntiles, tiles_small, tiles_big, tiles_half;
-    size_t tiles_tall, perm_scratch, z, act, S, ssq, m;
+    size_t tiles_tall, perm_scratch, z, act, S, ssq, m, S_out, ssq_out;
     int64_t max_small, max_big, max_half, max_tall;
     size_t total;
 };
@@ -93,6 +96,9 @@ Layout make_layout(const moe_desc *d) {
     L.S = c.take((size_t)TK * Dx * ab);
     L.ssq = (bf && d->expert_norm != MOE_NORM_NONE) ? c.take((size_t)TK * (Dx / 16) * 4) : 0;
     L.m = d->d_latent ? c.take((size_t)T * d->d_latent * 2) : 0;
+    const bool onorm = bf && d->out_norm != MOE_NORM_NONE;
+    L.S_out = onorm ? c.take((size_t)T * d->d_model * 2) : 0;
+    L.ssq_out = onorm ? c.take((size_t)T * (d->d_model / 16) * 4) : 0;
     L.total = c.total;
     return L;
 }
@@ -108,8 +114,20 @@ int check_desc(const moe_desc *d) {
     if (d->weight_dtype < MOE_DT_F32 || d->weight_dtype > MOE_DT_F16) return MOE_ERR_INVALID_ARG;
     if (d->in_norm < MOE_NORM_NONE || d->in_norm > MOE_NORM_INPUT_SCALED) return MOE_ERR_INVALID_ARG;
     if (d->expert_norm < MOE_NORM_NONE || d->expert_norm > MOE_NORM_INPUT_SCALED) return MOE_ERR_INVALID_ARG;
-    if (d->res_gate != MOE_RES_NONE && d->res_gate != MOE_RES_LINEAR) return MOE_ERR_INVALID_ARG;
+    if (d->res_gate != MOE_RES_NONE && d->res_gate != MOE_RES_LINEAR && d->res_gate != MOE_RES_MUSE)
+        return MOE_ERR_INVALID_ARG;
     if (!(d->eps_in >= 0.f) || !(d->eps_expert >= 0.f)) return MOE_ERR_INVALID_ARG;
+    if (d->router_fn != MOE_ROUTER_SOFTMAX && d->router_fn != MOE_ROUTER_SIGMOID) return MOE_ERR_INVALID_ARG;
+    if (d->router_fn == MOE_ROUTER_SIGMOID &&
+        (d->bias_in_weights || !isfinite(d->router_out_mult) || !isfinite(d->routed_scale)))
+        return MOE_ERR_INVALID_ARG;
+    if (d->latent_norm < MOE_NORM_NONE || d->latent_norm > MOE_NORM_INPUT_SCALED) return MOE_ERR_INVALID_ARG;
+    if (d->out_norm < MOE_NORM_NONE || d->out_norm > MOE_NORM_INPUT_SCALED) return MOE_ERR_INVALID_ARG;
+    if (d->latent_norm != MOE_NORM_NONE && (d->d_latent == 0 || !(d->eps_latent >= 0.f))) return MOE_ERR_INVALID_ARG;
+    if (d->out_norm != MOE_NORM_NONE && !(d->eps_out >= 0.f)) return MOE_ERR_INVALID_ARG;
+    if (d->res_gate == MOE_RES_MUSE && !(d->res_tau > 0.f && isfinite(d->res_tau) && d->res_floor >= 0.f &&
+                                         isfinite(d->res_floor)))
+        return MOE_ERR_INVALID_ARG;
     if (d->interm_dtype != MOE_DT_F32 && d->interm_dtype != MOE_DT_BF16 && d->interm_dtype != MOE_DT_F16)
         return MOE_ERR_INVALID_ARG;
     if (d->T * d->top_k >= ((int64_t)1 << 31) || d->T >= ((int64_t)1 << 31)) return MOE_ERR_INVALID_ARG;
@@ -119,6 +137,7 @@ int check_desc(const moe_desc *d) {
         if (d->router_dtype != MOE_DT_F32 || d->weight_dtype != MOE_DT_F32) return MOE_ERR_UNSUPPORTED;
         if (d->d_latent != 0 || d->in_norm != MOE_NORM_NONE || d->expert_norm != MOE_NORM_NONE)
             return MOE_ERR_UNSUPPORTED;
+        if (d->out_norm != MOE_NORM_NONE || d->res_gate == MOE_RES_MUSE) return MOE_ERR_UNSUPPORTED;
         return MOE_OK;
     }
     // bf16 path: latent SwiGLU layer on MFMA tiles.
@@ -127,6 +146,10 @@ int check_desc(const moe_desc *d) {
     if (d->weight_dtype == MOE_DT_F16 && d->interm_dtype == MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
     if (d->d_latent == 0 || d->expert_kind != MOE_EXPERT_SWIGLU3) return MOE_ERR_UNSUPPORTED;
     if (d->d_model % 512 || d->d_latent % 512 || d->d_ff % 512 || d->n_experts % 16) return MOE_ERR_UNSUPPORTED;
+    // the latent pre-norm is the output-scaled form; the output norm and the
+    // residual-gate kernel hold a row of at most 8192 values per workgroup
+    if (d->latent_norm == MOE_NORM_INPUT_SCALED) return MOE_ERR_UNSUPPORTED;
+    if ((d->out_norm != MOE_NORM_NONE || d->res_gate == MOE_RES_MUSE) && d->d_model > 8192) return MOE_ERR_UNSUPPORTED;
     return MOE_OK;
 }
 
@@ -155,6 +178,15 @@ int dense_path(const GemmArgs &g) { return (g.M <= 128 || g.N % kTileBN != 0) ? 
 
 int interm_act(const moe_desc *d) { return d->interm_dtype == MOE_DT_BF16 ? ACT_BF16 : ACT_F16; }
 
+RouterFn router_fn_of(const moe_desc *d) {
+    return RouterFn{d->router_fn == MOE_ROUTER_SIGMOID ? kRouterSigmoid : kRouterSoftmax, d->router_out_mult,
+                    d->routed_scale};
+}
+
+int res_mode_of(const moe_desc *d) {
+    return d->res_gate == MOE_RES_MUSE ? kResMuse : d->res_gate == MOE_RES_LINEAR ? kResLinear : kResNone;
+}
+
 int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const void *down_w, const void *w1,
                  const void *w2, const void *up_w, const moe_gains *gains, void *out, uint8_t *ws, const Layout &L,
                  moe_debug *dbg, hipStream_t s) {
@@ -174,7 +206,7 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
         MOE_TRY_RC(ev.begin(MOE_STAGE_IN_NORM));
         uint16_t *ub = (uint16_t *)(ws + L.u);
         MOE_TRY(launch_rmsnorm(xb, gains->gamma_in, ub, T, D, d->eps_in,
-                               d->in_norm == MOE_NORM_CENTERED ? 1 : 2, s));
+                               d->in_norm == MOE_NORM_CENTERED ? 1 : 2, ACT_BF16, s));
         MOE_TRY_RC(ev.end(MOE_STAGE_IN_NORM));
         u = ub;
     }
@@ -211,7 +243,7 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
 
     MOE_TRY_RC(ev.begin(MOE_STAGE_TOPK));
     MOE_TRY(launch_topk(logits, router_splits(d), gains ? gains->router_bias : nullptr, T, (int)n, (int)k,
-                        d->bias_in_weights, idx, wts, nullptr, s));
+                        d->bias_in_weights, router_fn_of(d), idx, wts, nullptr, s));
     MOE_TRY_RC(ev.end(MOE_STAGE_TOPK));
 
     // Experts with up to small_max tokens are streamed (weight-bandwidth
@@ -239,6 +271,8 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
         g.ldc = Lw;
         MOE_TRY(launch_down_gemm(g, dense_path(g), mx, at, s));
     }
+    if (d->latent_norm != MOE_NORM_NONE)  // z = C_pre(z), in place, in the intermediate type
+        MOE_TRY(launch_rmsnorm(z, gains ? gains->gamma_latent : nullptr, z, T, Lw, d->eps_latent, 1, at, s));
     MOE_TRY_RC(ev.end(MOE_STAGE_DOWN));
 
     auto grouped = [&](GemmArgs &g) {
@@ -325,7 +359,11 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
     MOE_TRY(launch_combine(S, ssq, pos, wts, T, Lw, (int)(Lw / 16), d->eps_expert, (int)k, at, m, s));
     MOE_TRY_RC(ev.end(MOE_STAGE_COMBINE));
 
-    // out = x + g * (m W_u^T)  (or out = m W_u^T).
+    // y = m W_u^T.  The linear gate without an output norm is fused into the
+    // epilogue (out = x + g * y); otherwise the epilogue stores y (fp32, in
+    // out) or the output norm's bf16 (1 + gamma) y and partial sums, and the
+    // residual-gate kernel finishes the row.
+    const bool fused = d->out_norm == MOE_NORM_NONE && d->res_gate != MOE_RES_MUSE;
     MOE_TRY_RC(ev.begin(MOE_STAGE_UP));
     {
         GemmArgs g{};
@@ -338,17 +376,34 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
         g.M = T;
         g.C = out;
         g.ldc = D;
-        if (d->res_gate == MOE_RES_LINEAR) {
+        if (fused && d->res_gate == MOE_RES_LINEAR) {
             g.resid = xb;
             g.gate = gains->res_gate;
             g.y = dbg ? dbg->y : nullptr;
-            MOE_TRY(launch_up_gemm(g, dense_path(g), mx, wat, true, s));
+            MOE_TRY(launch_up_gemm(g, dense_path(g), mx, wat, EPI_RESID, s));
+        } else if (d->out_norm != MOE_NORM_NONE) {
+            g.C = ws + L.S_out;
+            g.gamma = gains ? gains->gamma_out : nullptr;
+            g.ssq = (float *)(ws + L.ssq_out);
+            g.nparts = (int32_t)(D / 16);
+            g.norm_round = d->out_norm == MOE_NORM_INPUT_SCALED ? 1 : 0;
+            MOE_TRY(launch_up_gemm(g, dense_path(g), mx, wat, EPI_NORM, s));
         } else {
-            MOE_TRY(launch_up_gemm(g, dense_path(g), mx, wat, false, s));
-            if (dbg && dbg->y) MOE_TRY(hipMemcpyAsync(dbg->y, out, (size_t)T * D * 4, hipMemcpyDeviceToDevice, s));
+            MOE_TRY(launch_up_gemm(g, dense_path(g), mx, wat, EPI_F32, s));
+            if (fused && dbg && dbg->y)
+                MOE_TRY(hipMemcpyAsync(dbg->y, out, (size_t)T * D * 4, hipMemcpyDeviceToDevice, s));
         }
     }
     MOE_TRY_RC(ev.end(MOE_STAGE_UP));
+    if (!fused) {
+        MOE_TRY_RC(ev.begin(MOE_STAGE_RESGATE));
+        const bool onorm = d->out_norm != MOE_NORM_NONE;
+        MOE_TRY(launch_resgate(onorm ? (const uint16_t *)(ws + L.S_out) : nullptr,
+                               onorm ? (const float *)(ws + L.ssq_out) : nullptr, (int)(D / 16), d->eps_out, xb,
+                               gains ? gains->res_gate : nullptr, res_mode_of(d), d->res_tau, d->res_floor, T, D,
+                               (float *)out, dbg ? dbg->y : nullptr, s));
+        MOE_TRY_RC(ev.end(MOE_STAGE_RESGATE));
+    }
 
     if (dbg) {
         if (dbg->topk_idx) MOE_TRY(hipMemcpyAsync(dbg->topk_idx, idx, TK * 4, hipMemcpyDeviceToDevice, s));
@@ -385,8 +440,8 @@ int forward_f32(const moe_desc *d, const void *x, const void *router_w, const vo
     MOE_TRY(launch_router_f32((const float *)x, (const float *)router_w, T, (int)n, D, logits, s));
     MOE_TRY_RC(ev.end(MOE_STAGE_ROUTER));
     MOE_TRY_RC(ev.begin(MOE_STAGE_TOPK));
-    MOE_TRY(launch_topk(logits, 1, gains ? gains->router_bias : nullptr, T, (int)n, (int)k, d->bias_in_weights, idx,
-                        wts, nullptr, s));
+    MOE_TRY(launch_topk(logits, 1, gains ? gains->router_bias : nullptr, T, (int)n, (int)k, d->bias_in_weights,
+                        router_fn_of(d), idx, wts, nullptr, s));
     MOE_TRY_RC(ev.end(MOE_STAGE_TOPK));
     MOE_TRY_RC(ev.begin(MOE_STAGE_PERMUTE));
     MOE_TRY(launch_permute(idx, T, (int)k, (int)n, counts, offsets, perm_tok, perm_slot, pos, nullptr, nullptr,
@@ -447,7 +502,7 @@ int moe_layer_forward(const moe_desc *d, const void *x, const void *router_w, co
     if (d->T == 0) return MOE_OK;  // nothing to read or write: pointers may be NULL
     if (!x || !router_w || !expert_w1 || !expert_w2 || !out) return MOE_ERR_INVALID_ARG;
     if (d->d_latent && (!down_w || !up_w)) return MOE_ERR_INVALID_ARG;
-    if (d->res_gate == MOE_RES_LINEAR && (!gains || !gains->res_gate)) return MOE_ERR_INVALID_ARG;
+    if (d->res_gate != MOE_RES_NONE && (!gains || !gains->res_gate)) return MOE_ERR_INVALID_ARG;
     if (d->in_norm != MOE_NORM_NONE && !gains) return MOE_ERR_INVALID_ARG;
     Layout L = make_layout(d);
     if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
@@ -501,8 +556,8 @@ int moe_router_topk(const moe_desc *d, const void *u, const void *router_w, cons
         g.ksplit = ks;
         MOE_TRY(launch_router_gemm(g, dense_path(g), s));
     }
-    MOE_TRY(launch_topk(lg, ks, router_bias, d->T, (int)d->n_experts, (int)d->top_k, d->bias_in_weights, topk_idx,
-                        topk_w, lg == logits ? nullptr : logits, s));
+    MOE_TRY(launch_topk(lg, ks, router_bias, d->T, (int)d->n_experts, (int)d->top_k, d->bias_in_weights,
+                        router_fn_of(d), topk_idx, topk_w, lg == logits ? nullptr : logits, s));
     return MOE_OK;
 }
 

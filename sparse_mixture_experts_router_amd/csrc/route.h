@@ -7,13 +7,22 @@
 
 namespace moe {
 
-// mode 1: C_gamma (u = (1+g) x / rms(x)); mode 2: I_gamma (s = bf16((1+g) x), u = s / rms(s)).
+// Rows of stored type `it` (ACT_BF16 / ACT_F16), same type out; u may equal x.
+// mode 1: C_gamma (u = (1+g) x / rms(x)); mode 2: I_gamma (s = rnd((1+g) x), u = s / rms(s)).
 hipError_t launch_rmsnorm(const uint16_t *x, const float *gamma, uint16_t *u, int64_t T, int64_t d, float eps,
-                          int mode, hipStream_t s);
+                          int mode, int it, hipStream_t s);
+
+// Router function of the top-k stage.
+constexpr int kRouterSoftmax = 0, kRouterSigmoid = 1;
+struct RouterFn {
+    int fn;          // kRouterSoftmax or kRouterSigmoid
+    float out_mult;  // sigmoid: logit multiplier
+    float rsf;       // sigmoid: routed scaling factor
+};
 // logits: ks planes of [T][n] fp32 partial sums (over disjoint K slices),
 // added in plane order; lout (may be NULL) receives the summed logits.
 hipError_t launch_topk(const float *logits, int ks, const float *bias, int64_t T, int n, int k, int bias_in_weights,
-                       int32_t *idx, float *w, float *lout, hipStream_t s);
+                       const RouterFn &rf, int32_t *idx, float *w, float *lout, hipStream_t s);
 // Experts with 1..small_max tokens go to the small-tile list (kSmallBM rows
 // per tile).  Heavier ones get one tile when it holds them (half-height list
 // up to kHalfBM rows, full list up to kTileBM, tall list up to kTallBM), else
@@ -30,6 +39,16 @@ hipError_t launch_permute(const int32_t *idx, int64_t T, int k, int n, int32_t *
 // m in activation type `ot` (ACT_BF16 / ACT_F16).
 hipError_t launch_combine(const uint16_t *S, const float *ssq, const int32_t *pos, const float *w, int64_t T,
                           int64_t L, int nparts, float eps, int k, int ot, uint16_t *m, hipStream_t s);
+
+// Branch output norm + residual gate.  S != NULL: b = S * rsqrt(sum of the
+// row's nparts partial sums / d + eps) (S bf16 [T][d], ssq [T][nparts]);
+// S == NULL: b = out (fp32 y, overwritten).  out = b, x + g b (kResLinear)
+// or alpha x + beta b (kResMuse, temperature tau, floor floor_); ydbg (may
+// be NULL) receives b.  d % 8 == 0 and d <= 8192.
+constexpr int kResNone = 0, kResLinear = 1, kResMuse = 2;
+hipError_t launch_resgate(const uint16_t *S, const float *ssq, int nparts, float eps, const uint16_t *x,
+                          const float *g, int res, float tau, float floor_, int64_t T, int64_t d, float *out,
+                          float *ydbg, hipStream_t s);
 
 // dst = src, 16 bytes per lane per access (bytes: multiple of 16).
 hipError_t launch_copy16(const void *src, void *dst, int64_t bytes, hipStream_t s);

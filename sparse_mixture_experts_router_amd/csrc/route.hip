@@ -40,11 +40,15 @@ __device__ __forceinline__ float block_sum256(float v, float *lds4) {
 }
 
 // ---------------------------------------------------------------------------
-// Input RMS norm: C_gamma or I_gamma of each bf16 row, bf16 out.
+// Row RMS norms: C_gamma or I_gamma of each row, stored type IT in and out
+// (the input norm on bf16 x; the latent pre-norm in place on z).  u may
+// equal x: every element is read by the thread that writes it, and a row's
+// reads all precede the reduction's barriers.
 // ---------------------------------------------------------------------------
 
-__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t *__restrict__ x, const float *__restrict__ gamma,
-                                                      uint16_t *__restrict__ u, int64_t d, float eps, int mode) {
+template <int IT>
+__global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t *x, const float *__restrict__ gamma,
+                                                      uint16_t *u, int64_t d, float eps, int mode) {
     __shared__ float lds4[4];
     const int64_t row = blockIdx.x;
     const uint16_t *xr = x + row * d;
@@ -56,10 +60,10 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t *__restrict
         const uint16_t *h = (const uint16_t *)&v;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
-            float xv = bf16_to_f32(h[i]);
-            if (mode == 2) {  // input-scaled: square the bf16-rounded scaled value
+            float xv = act_to_f32<IT>(h[i]);
+            if (mode == 2) {  // input-scaled: square the scaled value rounded to the stored type
                 float g = gamma ? 1.0f + gamma[c * 8 + i] : 1.0f;
-                xv = bf16_to_f32(f32_to_bf16(g * xv));
+                xv = act_to_f32<IT>(f32_to_act<IT>(g * xv));
             }
             ss += xv * xv;
         }
@@ -74,9 +78,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t *__restrict
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             float g = gamma ? 1.0f + gamma[c * 8 + i] : 1.0f;
-            float xv = bf16_to_f32(h[i]);
-            float r = (mode == 2) ? bf16_to_f32(f32_to_bf16(g * xv)) * inv : g * (xv * inv);
-            oh[i] = f32_to_bf16(r);
+            float xv = act_to_f32<IT>(h[i]);
+            float r = (mode == 2) ? act_to_f32<IT>(f32_to_act<IT>(g * xv)) * inv : g * (xv * inv);
+            oh[i] = f32_to_act<IT>(r);
         }
         *(uint4 *)(ur + c * 8) = o;
     }
@@ -90,10 +94,9 @@ __global__ __launch_bounds__(256) void rmsnorm_kernel(const uint16_t *__restrict
 constexpr int kNormRows = 8;
 constexpr int kNormMaxChunks = 4;  // 8-value chunks per thread: d <= 8192
 
-__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t *__restrict__ x,
-                                                           const float *__restrict__ gamma,
-                                                           uint16_t *__restrict__ u, int64_t T, int64_t d, float eps,
-                                                           int mode) {
+template <int IT>
+__global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t *x, const float *__restrict__ gamma,
+                                                           uint16_t *u, int64_t T, int64_t d, float eps, int mode) {
     __shared__ float lds4[4];
     const int64_t nch = d / 8;
     float g[kNormMaxChunks][8];
@@ -121,8 +124,8 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t *__res
             const uint16_t *h = (const uint16_t *)&v[j];
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                float xv = bf16_to_f32(h[i]);
-                if (mode == 2) xv = bf16_to_f32(f32_to_bf16(g[j][i] * xv));  // square the bf16-rounded scaled value
+                float xv = act_to_f32<IT>(h[i]);
+                if (mode == 2) xv = act_to_f32<IT>(f32_to_act<IT>(g[j][i] * xv));  // square the rounded scaled value
                 ss += xv * xv;
             }
         }
@@ -137,9 +140,9 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t *__res
             uint16_t *oh = (uint16_t *)&o;
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
-                const float xv = bf16_to_f32(h[i]);
-                const float r = (mode == 2) ? bf16_to_f32(f32_to_bf16(g[j][i] * xv)) * inv : g[j][i] * (xv * inv);
-                oh[i] = f32_to_bf16(r);
+                const float xv = act_to_f32<IT>(h[i]);
+                const float r = (mode == 2) ? act_to_f32<IT>(f32_to_act<IT>(g[j][i] * xv)) * inv : g[j][i] * (xv * inv);
+                oh[i] = f32_to_act<IT>(r);
             }
             *(uint4 *)(ur + c * 8) = o;
         }
@@ -154,10 +157,15 @@ __global__ __launch_bounds__(256) void rmsnorm_rows_kernel(const uint16_t *__res
 // logits: ks planes of [T][n] partial sums over disjoint K slices (ks = 1:
 // the logits themselves), added in plane order, so the sum is the same on
 // every run; lout (may be NULL) receives the summed logits.
+// fn == kRouterSoftmax: selection on s = l + bias (fp32), weights = softmax
+// of the kept logits (of the kept s when bias_in_weights).
+// fn == kRouterSigmoid: sg = sigmoid(l * out_mult) in fp32, selection on
+// sg + bias, weights = kept sg / (their sum + 1e-15) * rsf.
 __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ logits, int ks,
                                                    const float *__restrict__ bias, int64_t T, int n, int k,
-                                                   int bias_in_weights, int32_t *__restrict__ idx,
-                                                   float *__restrict__ w, float *__restrict__ lout) {
+                                                   int bias_in_weights, int fn, float out_mult, float rsf,
+                                                   int32_t *__restrict__ idx, float *__restrict__ w,
+                                                   float *__restrict__ lout) {
     const int lane = threadIdx.x & 63;
     const int64_t t = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (t >= T) return;
@@ -171,9 +179,15 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
             float l = lr[e];
             for (int q = 1; q < ks; ++q) l += lr[q * plane + e];
             if (lout) lout[t * n + e] = l;
-            float s = bias ? l + bias[e] : l;
-            sc[r] = s;
-            hv[r] = bias_in_weights ? s : l;
+            if (fn == kRouterSigmoid) {
+                const float sg = 1.0f / (1.0f + expf(-(l * out_mult)));
+                sc[r] = bias ? sg + bias[e] : sg;
+                hv[r] = sg;
+            } else {
+                float s = bias ? l + bias[e] : l;
+                sc[r] = s;
+                hv[r] = bias_in_weights ? s : l;
+            }
         } else {
             sc[r] = -INFINITY;
             hv[r] = 0.f;
@@ -217,15 +231,23 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
             my_e = be;
         }
     }
-    // Softmax over the kept values, held by lanes 0..k-1.
-    float mx = lane < k ? my_h : -INFINITY;
+    float wt;
+    if (fn == kRouterSigmoid) {
+        // the kept sigmoids (lanes 0..k-1) over their sum plus 1e-15
+        const float sum = wave_sum(lane < k ? my_h : 0.f);
+        wt = my_h / (sum + 1e-15f) * rsf;
+    } else {
+        // softmax over the kept values, held by lanes 0..k-1
+        float mx = lane < k ? my_h : -INFINITY;
 #pragma unroll
-    for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
-    float ex = lane < k ? expf(my_h - mx) : 0.f;
-    float sum = wave_sum(ex);
+        for (int o = 32; o > 0; o >>= 1) mx = fmaxf(mx, __shfl_xor(mx, o, 64));
+        float ex = lane < k ? expf(my_h - mx) : 0.f;
+        float sum = wave_sum(ex);
+        wt = ex / sum;
+    }
     if (lane < k) {
         idx[t * k + lane] = my_e;
-        w[t * k + lane] = ex / sum;
+        w[t * k + lane] = wt;
     }
 }
 
@@ -509,6 +531,98 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
 }
 
 // ---------------------------------------------------------------------------
+// Branch output norm and residual gate (flozi.net "Muse Spark Open: ...",
+// "Residual gates: derive the advertised intuition carefully" and "The
+// complete layer has two separately normalized residual updates"):
+//   b   = S * (sum(ssq) / d + eps)^-1/2 when the output norm is on (S =
+//         bf16((1 + gamma) y) and its per-16-column sums of squares, from the
+//         up-projection's epilogue), else b = y (fp32);
+//   out = b (kResNone), x + g * b (kResLinear), or alpha * x + beta * b
+//         (kResMuse: w = g / tau, beta = sigmoid(w), alpha = sqrt(max(
+//         sigmoid(-w) * (1 + beta), floor)), the product as written).
+// A workgroup takes kNormRows rows; each thread keeps the coefficients of
+// its columns in registers.  Without the norm, y is read from `out` and
+// overwritten element by element by the thread that read it.
+// ---------------------------------------------------------------------------
+
+template <bool NORM>
+__global__ __launch_bounds__(256) void resgate_rows_kernel(const uint16_t *__restrict__ S,
+                                                           const float *__restrict__ ssq, int nparts, float eps,
+                                                           const uint16_t *__restrict__ x,
+                                                           const float *__restrict__ g, int res, float tau,
+                                                           float floor_, int64_t T, int64_t d, float *out,
+                                                           float *__restrict__ ydbg) {
+    __shared__ float lds4[4];
+    const int64_t nch = d / 8;
+    float ca[kNormMaxChunks][8], cb[kNormMaxChunks][8];
+#pragma unroll
+    for (int j = 0; j < kNormMaxChunks; ++j) {
+        const int64_t c = threadIdx.x + 256 * j;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            float a = 0.f, b = 1.f;
+            if (c < nch && res != kResNone) {
+                const float gv = g[c * 8 + i];
+                if (res == kResLinear) {
+                    a = 1.f;
+                    b = gv;
+                } else {
+                    const float wv = gv / tau;
+                    b = 1.0f / (1.0f + expf(-wv));
+                    const float sn = 1.0f / (1.0f + expf(wv));
+                    a = sqrtf(fmaxf(sn * (1.0f + b), floor_));
+                }
+            }
+            ca[j][i] = a;
+            cb[j][i] = b;
+        }
+    }
+    const int64_t r1 = min<int64_t>(T, (int64_t)(blockIdx.x + 1) * kNormRows);
+    for (int64_t row = (int64_t)blockIdx.x * kNormRows; row < r1; ++row) {
+        float inv = 1.f;
+        if constexpr (NORM) {
+            float sq = 0.f;
+            for (int q = threadIdx.x; q < nparts; q += 256) sq += ssq[row * nparts + q];
+            sq = block_sum256(sq, lds4);
+            inv = 1.0f / sqrtf(sq / (float)d + eps);
+        }
+#pragma unroll
+        for (int j = 0; j < kNormMaxChunks; ++j) {
+            const int64_t c = threadIdx.x + 256 * j;
+            if (c >= nch) continue;
+            float bv[8];
+            if constexpr (NORM) {
+                const uint4 v = *(const uint4 *)(S + row * d + c * 8);
+                const uint16_t *h = (const uint16_t *)&v;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) bv[i] = bf16_to_f32(h[i]) * inv;
+            } else {
+                const float4 v0 = *(const float4 *)(out + row * d + c * 8);
+                const float4 v1 = *(const float4 *)(out + row * d + c * 8 + 4);
+                bv[0] = v0.x; bv[1] = v0.y; bv[2] = v0.z; bv[3] = v0.w;
+                bv[4] = v1.x; bv[5] = v1.y; bv[6] = v1.z; bv[7] = v1.w;
+            }
+            float o[8];
+            if (res != kResNone) {
+                const uint4 xv = *(const uint4 *)(x + row * d + c * 8);
+                const uint16_t *xh = (const uint16_t *)&xv;
+#pragma unroll
+                for (int i = 0; i < 8; ++i) o[i] = ca[j][i] * bf16_to_f32(xh[i]) + cb[j][i] * bv[i];
+            } else {
+#pragma unroll
+                for (int i = 0; i < 8; ++i) o[i] = bv[i];
+            }
+            *(float4 *)(out + row * d + c * 8) = make_float4(o[0], o[1], o[2], o[3]);
+            *(float4 *)(out + row * d + c * 8 + 4) = make_float4(o[4], o[5], o[6], o[7]);
+            if (ydbg) {
+                *(float4 *)(ydbg + row * d + c * 8) = make_float4(bv[0], bv[1], bv[2], bv[3]);
+                *(float4 *)(ydbg + row * d + c * 8 + 4) = make_float4(bv[4], bv[5], bv[6], bv[7]);
+            }
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
 // fp32 path (no latent projection, fp32 everything): plain per-output
 // threads; the layer is tiny and latency bound.
 // ---------------------------------------------------------------------------
@@ -624,18 +738,29 @@ hipError_t launch_copy16(const void *src, void *dst, int64_t bytes, hipStream_t 
 
 static inline unsigned blocks_for(int64_t n, int b) { return (unsigned)((n + b - 1) / b); }
 
-hipError_t launch_rmsnorm(const uint16_t *x, const float *gamma, uint16_t *u, int64_t T, int64_t d, float eps,
-                          int mode, hipStream_t s) {
+template <int IT>
+static hipError_t run_rmsnorm(const uint16_t *x, const float *gamma, uint16_t *u, int64_t T, int64_t d, float eps,
+                              int mode, hipStream_t s) {
+    if (T <= 0) return hipSuccess;
     if (d / 8 <= 256 * kNormMaxChunks)
-        rmsnorm_rows_kernel<<<(unsigned)((T + kNormRows - 1) / kNormRows), 256, 0, s>>>(x, gamma, u, T, d, eps, mode);
+        rmsnorm_rows_kernel<IT><<<(unsigned)((T + kNormRows - 1) / kNormRows), 256, 0, s>>>(x, gamma, u, T, d, eps,
+                                                                                             mode);
     else
-        rmsnorm_kernel<<<(unsigned)T, 256, 0, s>>>(x, gamma, u, d, eps, mode);
+        rmsnorm_kernel<IT><<<(unsigned)T, 256, 0, s>>>(x, gamma, u, d, eps, mode);
     return hipGetLastError();
 }
 
+hipError_t launch_rmsnorm(const uint16_t *x, const float *gamma, uint16_t *u, int64_t T, int64_t d, float eps,
+                          int mode, int it, hipStream_t s) {
+    if (it == ACT_F16) return run_rmsnorm<ACT_F16>(x, gamma, u, T, d, eps, mode, s);
+    return run_rmsnorm<ACT_BF16>(x, gamma, u, T, d, eps, mode, s);
+}
+
 hipError_t launch_topk(const float *logits, int ks, const float *bias, int64_t T, int n, int k, int bias_in_weights,
-                       int32_t *idx, float *w, float *lout, hipStream_t s) {
-    topk_kernel<<<blocks_for(T, 4), 256, 0, s>>>(logits, ks, bias, T, n, k, bias_in_weights, idx, w, lout);
+                       const RouterFn &rf, int32_t *idx, float *w, float *lout, hipStream_t s) {
+    if (T <= 0) return hipSuccess;
+    topk_kernel<<<blocks_for(T, 4), 256, 0, s>>>(logits, ks, bias, T, n, k, bias_in_weights, rf.fn, rf.out_mult,
+                                                 rf.rsf, idx, w, lout);
     return hipGetLastError();
 }
 
@@ -663,6 +788,19 @@ hipError_t launch_combine(const uint16_t *S, const float *ssq, const int32_t *po
                           int64_t L, int nparts, float eps, int k, int ot, uint16_t *m, hipStream_t s) {
     if (ot == ACT_F16) combine_kernel<ACT_F16><<<(unsigned)T, 256, 0, s>>>(S, ssq, pos, w, L, nparts, eps, k, m);
     else combine_kernel<ACT_BF16><<<(unsigned)T, 256, 0, s>>>(S, ssq, pos, w, L, nparts, eps, k, m);
+    return hipGetLastError();
+}
+
+hipError_t launch_resgate(const uint16_t *S, const float *ssq, int nparts, float eps, const uint16_t *x,
+                          const float *g, int res, float tau, float floor_, int64_t T, int64_t d, float *out,
+                          float *ydbg, hipStream_t s) {
+    if (T <= 0) return hipSuccess;
+    if (d % 8 || d / 8 > 256 * kNormMaxChunks) return hipErrorInvalidValue;
+    const unsigned grid = (unsigned)((T + kNormRows - 1) / kNormRows);
+    if (S)
+        resgate_rows_kernel<true><<<grid, 256, 0, s>>>(S, ssq, nparts, eps, x, g, res, tau, floor_, T, d, out, ydbg);
+    else
+        resgate_rows_kernel<false><<<grid, 256, 0, s>>>(S, ssq, nparts, eps, x, g, res, tau, floor_, T, d, out, ydbg);
     return hipGetLastError();
 }
 

@@ -204,7 +204,8 @@ def muse(name: str = "muse", T: int = 8192, input_seed: int = 5, **kw) -> Preset
     return dataclasses.replace(_latent(name, T, input_seed), eps_expert=1e-5, **base)
 
 
-MUSE_PRESETS = {"m1": muse("m1", 64, 6), "m2": muse("m2", 8192, 5)}
+PRESETS["m1"] = muse("m1", 64, 6)      # decode batch
+PRESETS["m2"] = muse("m2", 8192, 5)    # prefill batch
 
 
 def small(name: str = "small", T: int = 77, d: int = 512, L: int = 256, F: int = 256, n: int = 16,
@@ -275,6 +276,16 @@ def layer_params(p: Preset, formats=None) -> dict:
                 out[key] = a
             if len(formats) > 1:
                 out[key + "@" + f] = a
+    out.update(gains(p))
+    return out
+
+
+def gains(p: Preset) -> dict:
+    """The layer's small fp32 parameter vectors: gamma_ex, gate, gamma_in,
+    gamma_lat, gamma_out and bias, each present when its stage is on."""
+    s = p.layer_seed
+    Kin = p.L if p.L else p.d
+    out = {}
     if p.expert_norm != "none":
         out["gamma_ex"] = normal_f32(s, "gamma_expert", Kin, 0.02)
     if p.res_gate == "linear":

@@ -10,6 +10,7 @@ import torch
 import oracle
 import sparse_mixture_experts_router_amd as moe
 import synthetic
+from conftest import preset_desc
 
 MARGIN_EXCLUDE = 1e-4
 TOL = {"f32": 1e-5, "bf16": 2e-2, "mxfp4": 5e-2}
@@ -27,10 +28,7 @@ def to_dev(a: np.ndarray) -> torch.Tensor:
 
 
 def desc_of(p: synthetic.Preset, T: int | None = None):
-    return moe.make_desc(p.chunk_T if T is None else T, p.d, p.L, p.n, p.k, p.F, expert_kind=p.kind, act=p.act,
-                         router=p.router_w, weights=p.weights, in_norm=p.in_norm, expert_norm=p.expert_norm,
-                         res_gate=p.res_gate, bias_in_weights=p.bias_in_weights, eps_in=p.eps_in,
-                         eps_expert=p.eps_expert, interm=p.interm)
+    return preset_desc(p, T)
 
 
 class DeviceLayer:
@@ -47,7 +45,8 @@ class DeviceLayer:
 
     def gains(self):
         return {"router_bias": self.dev.get("bias"), "gamma_in": self.dev.get("gamma_in"),
-                "gamma_expert": self.dev.get("gamma_ex"), "res_gate": self.dev.get("gate")}
+                "gamma_expert": self.dev.get("gamma_ex"), "res_gate": self.dev.get("gate"),
+                "gamma_latent": self.dev.get("gamma_lat"), "gamma_out": self.dev.get("gamma_out")}
 
 
 def run(layer: DeviceLayer, x: np.ndarray, dbg: bool = True, workspace=None, stages: bool = True):
@@ -109,9 +108,7 @@ def check_routing(p, host, x, gpu, tokens, label=""):
     t["x"] = x
     r = oracle.forward(oracle_cfg(p), t, tokens=tokens, want_outputs=False)
     gidx = gpu["topk_idx"][tokens]
-    s = r["logits"].astype(np.float32)
-    if "bias" in host:
-        s = (s + host["bias"].astype(np.float32)).astype(np.float32)
+    s = oracle.router_scores(oracle_cfg(p), r["logits"], host.get("bias"))[0]   # selection scores
     clean = r["margin"] >= MARGIN_EXCLUDE
     if p.k < p.n:
         srt = -np.sort(-s.astype(np.float64), axis=1)[:, :p.k + 1]
@@ -138,6 +135,34 @@ def check_routing(p, host, x, gpu, tokens, label=""):
 # of the bf16 rounding noise itself.  The per-stage checks below (check_stages)
 # are the tight ones.
 TOL_DATAFLOW = {"f32": 1e-5, "bf16": 2e-2, "mxfp4": 5e-2}
+
+# The FFN output norm stores s = bf16((1 + gamma) y) (the input-scaled form
+# rounds it there by definition; the output-scaled form is stored that way
+# on the device).  Device and oracle reach y along different fp32 / fp64
+# paths, so an element of s can land one bf16 ulp apart, which moves b by
+# ulp(s) * inv: up to 2^-7 of |b|, about 1.6% of RMS(b) for the largest
+# elements of a row, more than the bf16 tolerance leaves.  Such an element
+# is allowed one ulp of s (times its gate coefficient in out); at most
+# FLIP_OUT_FRACTION of the outputs may exceed the plain tolerance.
+FLIP_OUT_FRACTION = 1e-2
+
+
+def output_norm_allowance(p, host: dict, ypre: np.ndarray):
+    """Per-element allowance (y, out) for the output norm's bf16 step."""
+    if p.out_norm == "none":
+        return 0.0, 0.0
+    gam = 1.0 + host["gamma_out"].astype(np.float64)
+    s_ref = round_bf16(gam * ypre)
+    base = s_ref if p.out_norm == "input_scaled" else ypre
+    inv = 1.0 / np.sqrt((base * base).mean(1, keepdims=True) + p.eps_out)
+    allow_y = 1.01 * ulp_bf16(s_ref) * inv
+    if p.res_gate == "linear":
+        coef = np.abs(host["gate"].astype(np.float64))
+    elif p.res_gate == "muse":
+        coef = 1.0 / (1.0 + np.exp(-host["gate"].astype(np.float64) / p.res_tau))
+    else:
+        coef = 1.0
+    return allow_y, allow_y * coef
 
 
 def compare(p: synthetic.Preset, host: dict, x: np.ndarray, gpu: dict, tokens=None, route_tokens=None,
@@ -170,25 +195,32 @@ def compare(p: synthetic.Preset, host: dict, x: np.ndarray, gpu: dict, tokens=No
     refs = {}
     for mode, mirror in (("exact", False), ("dataflow", True)):
         r = oracle.forward(cfg, t, tokens=tok, mirror=mirror)
-        y_ref, out_ref = r["y"].copy(), r["out"].copy()
+        y_ref, out_ref, ypre = r["y"].copy(), r["out"].copy(), r["ypre"].copy()
         diff = np.flatnonzero(~(gidx == r["idx"]).all(axis=1))
         if diff.size:
             rf = oracle.forward(cfg, t, tokens=tok[diff], forced=gidx[diff], mirror=mirror)
-            y_ref[diff], out_ref[diff] = rf["y"], rf["out"]
-        refs[mode] = (y_ref, out_ref, diff.size)
-    y_ex, out_ex, nforced = refs["exact"]
-    y_df, out_df, _ = refs["dataflow"]
+            y_ref[diff], out_ref[diff], ypre[diff] = rf["y"], rf["out"], rf["ypre"]
+        refs[mode] = (y_ref, out_ref, diff.size, ypre)
+    y_ex, out_ex, nforced, ypre = refs["exact"]
+    y_df, out_df, _, _ = refs["dataflow"]
     rms = float(np.sqrt(np.mean(y_ex ** 2)))
     kind = p.weights if p.act == "bf16" else "f32"
     tol, tol_df = TOL[kind], TOL_DATAFLOW[kind]
-    e_out = float(np.abs(gpu["out"][tok] - out_ex).max()) / rms
-    e_y = float(np.abs(gpu["y"][tok] - y_ex).max()) / rms
-    e_out_df = float(np.abs(gpu["out"][tok] - out_df).max()) / rms
-    e_y_df = float(np.abs(gpu["y"][tok] - y_df).max()) / rms
+    allow_y, allow_out = output_norm_allowance(p, t, ypre)
+    dout, dy = np.abs(gpu["out"][tok] - out_ex), np.abs(gpu["y"][tok] - y_ex)
+    e_out = float(np.maximum(dout - allow_out, 0).max()) / rms
+    e_y = float(np.maximum(dy - allow_y, 0).max()) / rms
+    e_out_df = float(np.maximum(np.abs(gpu["out"][tok] - out_df) - allow_out, 0).max()) / rms
+    e_y_df = float(np.maximum(np.abs(gpu["y"][tok] - y_df) - allow_y, 0).max()) / rms
+    beyond = float((dout > tol * rms).mean())
     say("%s: routed=%d (excluded %d) compared=%d forced=%d rms(y)=%.4g | exact: max|dout|/rms=%.3g (tol %.0e) "
-        "max|dy|/rms=%.3g | bf16-dataflow: max|dout|/rms=%.3g max|dy|/rms=%.3g (tol %.0e)" % (
-            label, len(rtok), excluded, len(tok), nforced, rms, e_out, tol, e_y, e_out_df, e_y_df, tol_df))
+        "max|dy|/rms=%.3g | bf16-dataflow: max|dout|/rms=%.3g max|dy|/rms=%.3g (tol %.0e)%s" % (
+            label, len(rtok), excluded, len(tok), nforced, rms, e_out, tol, e_y, e_out_df, e_y_df, tol_df,
+            " | output-norm flips: raw max|dout|/rms=%.3g, beyond tol %.4f%%" % (float(dout.max()) / rms,
+                                                                           100 * beyond)
+            if p.out_norm != "none" else ""))
     assert e_out <= tol, "%s out error %.3g * RMS(y) > %.0e" % (label, e_out, tol)
+    assert beyond <= FLIP_OUT_FRACTION, "%s: %.3g of the outputs beyond the tolerance" % (label, beyond)
     if kind == "f32":
         assert e_y <= tol, "%s y error %.3g * RMS(y) > %.0e" % (label, e_y, tol)
     if check_perm:
@@ -291,12 +323,21 @@ def check_stages(p: synthetic.Preset, host: dict, x: np.ndarray, gpu: dict, toke
         u = xf
     Wd = weight_rows(host, "down_w", fmt, L, d, 0, L)
     zexact = u @ Wd.T
+    if p.latent_norm == "centered":
+        # the device stores P_down u in the intermediate type, then normalises it
+        zr = rnd(zexact)
+        zexact = (1.0 + host["gamma_lat"].astype(np.float64)) * zr / np.sqrt((zr * zr).mean(1, keepdims=True)
+                                                                            + p.eps_latent)
     zref = rnd(zexact)
     zg = dec(gpu["z"][tok])
-    if p.in_norm != "none":
-        # u itself may differ by one bf16 ulp in a few elements: z within 1e-3 relative of the row
+    if p.in_norm != "none" or p.latent_norm != "none":
+        # u itself may differ by one bf16 ulp in a few elements: z within 1e-3 relative of the row; the
+        # latent pre-norm rounds twice (P_down u, then its normalised value): one more ulp of z
         dz = np.abs(zg - zexact)
-        assert (dz <= 1e-3 * np.sqrt(np.mean(zexact ** 2, axis=1))[:, None] + ulp(zexact)).all(), label + " stage z"
+        nulp = 2 if p.latent_norm != "none" else 1
+        lim = 1e-3 * np.sqrt(np.mean(zexact ** 2, axis=1))[:, None] + nulp * ulp(zexact)
+        say("  stage z    %s: max |dz| / limit %.3f" % (label, float((dz / lim).max())))
+        assert (dz <= lim).all(), label + " stage z"
     else:
         _flips("z", zg, zref, label, ulp, rowfloor(zexact))
     del Wd
@@ -335,7 +376,32 @@ def check_stages(p: synthetic.Preset, host: dict, x: np.ndarray, gpu: dict, toke
     _flips("m", mg, rnd(m_exact), label, ulp, rowfloor(m_exact))
     Wu = weight_rows(host, "up_w", fmt, d, L, 0, d)
     y_ref = mg @ Wu.T
-    rms = float(np.sqrt(np.mean(y_ref ** 2)))
-    assert np.abs(gpu["y"][tok] - y_ref).max() <= 1e-5 * rms, label + " stage up (y)"
-    out_ref = xf + host["gate"].astype(np.float64) * y_ref if p.res_gate == "linear" else y_ref
-    assert np.abs(gpu["out"][tok] - out_ref).max() <= 1e-5 * max(rms, 1.0), label + " stage up (out)"
+    yg = gpu["y"][tok].astype(np.float64)
+    if p.out_norm != "none":
+        # the epilogue stores s = bf16((1 + gamma) y); b = s / rms (of s, or of y for the centered form)
+        gam = 1.0 + host["gamma_out"].astype(np.float64)
+        s_ref = round_bf16(gam * y_ref)
+        base = s_ref if p.out_norm == "input_scaled" else y_ref
+        inv = 1.0 / np.sqrt((base * base).mean(1, keepdims=True) + p.eps_out)
+        b_ref = s_ref * inv
+        rms = float(np.sqrt(np.mean(b_ref ** 2)))
+        # s may sit one bf16 ulp away where y straddles a rounding boundary
+        lim = 1.01 * ulp_bf16(s_ref) * inv + 1e-5 * rms
+        db = np.abs(yg - b_ref)
+        say("  stage outnorm %s: beyond 1e-5 * rms %.4f%%" % (label, 100 * float((db > 1e-5 * rms).mean())))
+        assert (db <= lim).all(), label + " stage output norm"
+        assert float((db > 1e-5 * rms).mean()) <= FLIP_FRACTION, label + " stage output norm flips"
+    else:
+        rms = float(np.sqrt(np.mean(y_ref ** 2)))
+        assert np.abs(yg - y_ref).max() <= 1e-5 * rms, label + " stage up (y)"
+    # residual gate on the device's own branch output
+    if p.res_gate == "linear":
+        out_ref = xf + host["gate"].astype(np.float64) * yg
+    elif p.res_gate == "muse":
+        w = host["gate"].astype(np.float64) / p.res_tau
+        beta = 1.0 / (1.0 + np.exp(-w))
+        alpha = np.sqrt(np.maximum(1.0 / (1.0 + np.exp(w)) * (1.0 + beta), p.res_floor))
+        out_ref = alpha * xf + beta * yg
+    else:
+        out_ref = yg
+    assert np.abs(gpu["out"][tok] - out_ref).max() <= 1e-5 * max(rms, 1.0), label + " stage residual gate (out)"

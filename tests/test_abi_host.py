@@ -2,6 +2,7 @@
 host-only entry points (validation, workspace sizing, error strings) work
 without a GPU.  No compute call is made here."""
 import ctypes
+import dataclasses
 import os
 import re
 
@@ -9,6 +10,7 @@ import pytest
 
 import sparse_mixture_experts_router_amd as moe
 import synthetic
+from conftest import preset_desc
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 
@@ -32,10 +34,7 @@ def test_library_exports_every_declared_symbol():
     assert set(moe.EXPORTED) == set(names)
 
 
-def desc_of(p, T=None):
-    return moe.make_desc(T if T is not None else p.chunk_T, p.d, p.L, p.n, p.k, p.F, expert_kind=p.kind, act=p.act,
-                         router=p.router_w, weights=p.weights, in_norm=p.in_norm, expert_norm=p.expert_norm,
-                         res_gate=p.res_gate, eps_in=p.eps_in, eps_expert=p.eps_expert)
+desc_of = preset_desc
 
 
 @pytest.mark.parametrize("name", list(synthetic.PRESETS))
@@ -62,7 +61,11 @@ def test_workspace_grows_with_T_and_is_aligned():
     ("act_dtype", 7, moe.MOE_ERR_INVALID_ARG),
     ("weight_dtype", 5, moe.MOE_ERR_INVALID_ARG),
     ("in_norm", 3, moe.MOE_ERR_INVALID_ARG),
-    ("res_gate", 2, moe.MOE_ERR_INVALID_ARG),
+    ("res_gate", 3, moe.MOE_ERR_INVALID_ARG),
+    ("router_fn", 2, moe.MOE_ERR_INVALID_ARG),
+    ("latent_norm", 3, moe.MOE_ERR_INVALID_ARG),
+    ("latent_norm", 2, moe.MOE_ERR_UNSUPPORTED),
+    ("out_norm", 3, moe.MOE_ERR_INVALID_ARG),
     ("eps_expert", -1.0, moe.MOE_ERR_INVALID_ARG),
     ("d_model", 8192 + 64, moe.MOE_ERR_UNSUPPORTED),
     ("d_latent", 0, moe.MOE_ERR_UNSUPPORTED),
@@ -99,6 +102,56 @@ def test_forward_rejects_before_any_launch():
     # permute stage argument checks
     assert lib.moe_permute(4, 0, 8, fake, fake, fake, fake, fake, fake, None) == moe.MOE_ERR_INVALID_ARG
     assert lib.moe_permute(4, 2, 8, None, fake, fake, fake, fake, fake, None) == moe.MOE_ERR_INVALID_ARG
+
+
+@pytest.mark.parametrize("changes,code", [
+    ({"bias_in_weights": 1}, moe.MOE_ERR_INVALID_ARG),              # the sigmoid's bias selects only
+    ({"router_out_mult": float("inf")}, moe.MOE_ERR_INVALID_ARG),
+    ({"routed_scale": float("nan")}, moe.MOE_ERR_INVALID_ARG),
+    ({"res_tau": 0.0}, moe.MOE_ERR_INVALID_ARG),
+    ({"res_tau": float("inf")}, moe.MOE_ERR_INVALID_ARG),
+    ({"res_floor": -1e-3}, moe.MOE_ERR_INVALID_ARG),
+    ({"eps_out": -1.0}, moe.MOE_ERR_INVALID_ARG),
+    ({"eps_latent": -1.0}, moe.MOE_ERR_INVALID_ARG),
+    ({"d_model": 8192 + 512}, moe.MOE_ERR_UNSUPPORTED),             # output norm rows hold <= 8192 values
+    ({"router_out_mult": -2.0, "routed_scale": 0.0, "res_floor": 0.0}, moe.MOE_OK),
+])
+def test_muse_descriptor_validation(changes, code):
+    d = desc_of(synthetic.PRESETS["m1"])
+    assert moe.moe_validate(d) == moe.MOE_OK
+    for k_, v in changes.items():
+        setattr(d, k_, v)
+    assert moe.moe_validate(d) == code
+
+
+def test_muse_stages_on_the_fp32_path_and_workspace():
+    c0 = synthetic.PRESETS["c0"]
+    d = desc_of(c0)
+    d.router_fn = moe.ROUTER["sigmoid"]             # the router kernel is shared: allowed
+    assert moe.moe_validate(d) == moe.MOE_OK
+    for field, v in (("out_norm", moe.NORM["input_scaled"]), ("res_gate", moe.RES["muse"])):
+        e = desc_of(c0)
+        setattr(e, field, v)
+        assert moe.moe_validate(e) == moe.MOE_ERR_UNSUPPORTED, field
+    e = desc_of(c0)
+    e.latent_norm = moe.NORM["centered"]            # no latent to normalise
+    assert moe.moe_validate(e) == moe.MOE_ERR_INVALID_ARG
+    # the output norm's bf16 rows and partial sums take T * d * (2 + 4/16) more bytes
+    m1 = synthetic.PRESETS["m1"]
+    a = moe.moe_workspace_bytes(desc_of(m1))
+    b = moe.moe_workspace_bytes(desc_of(dataclasses.replace(m1, out_norm="none")))
+    assert a - b >= m1.T * m1.d * (2 + 4 / 16)
+
+
+def test_muse_forward_needs_its_gate_vector():
+    lib = moe.lib()
+    d = desc_of(synthetic.PRESETS["m1"])
+    g = moe.moe_gains()
+    fake = ctypes.c_void_p(256)  # never dereferenced: validation fails first
+    rc = lib.moe_layer_forward(ctypes.byref(d), fake, fake, fake, fake, fake, fake, ctypes.byref(g), fake, fake,
+                               1 << 40, None, None)
+    assert rc == moe.MOE_ERR_INVALID_ARG
+    assert ctypes.sizeof(moe.moe_desc) == 128 and ctypes.sizeof(moe.moe_gains) == 48
 
 
 def test_error_strings():

@@ -30,22 +30,23 @@ def bf16_layer(layer_host):
     return DeviceLayer(synthetic.PRESETS["c1"], host={k: v for k, v in layer_host.items() if "@" not in k})
 
 
+BIG = ("router_w", "down_w", "w1", "w2", "up_w")
+
+
 def preset_layer(p, layer_host, base: DeviceLayer):
     """A DeviceLayer for preset p sharing the seed-1 device weights of `base`
-    (MXFP4 presets get the MXFP4 forms of the same draws)."""
-    host = {k: v for k, v in layer_host.items() if "@" not in k}
+    (MXFP4 presets get the MXFP4 forms of the same draws), with p's own small
+    parameter vectors (gains, gate, bias)."""
+    host = {k: layer_host[k] for k in BIG}
     lay = DeviceLayer.__new__(DeviceLayer)
-    lay.p, lay.host, lay.dev = p, host, dict(base.dev)
+    lay.p, lay.host, lay.dev = p, host, {k: base.dev[k] for k in BIG}
     if p.weights == "mxfp4":
         for k in ("down_w", "w1", "w2", "up_w"):
             host[k] = layer_host[k + "@mxfp4"]
             lay.dev[k] = to_dev(host[k])
-    if p.router_bias == "zipf":
-        host["bias"] = synthetic.zipf_bias(p.n)
-        lay.dev["bias"] = to_dev(host["bias"])
-    if p.in_norm != "none":
-        host["gamma_in"] = synthetic.normal_f32(p.layer_seed, "gamma_in", p.d, 0.02)
-        lay.dev["gamma_in"] = to_dev(host["gamma_in"])
+    for k, v in synthetic.gains(p).items():
+        host[k] = v
+        lay.dev[k] = to_dev(v)
     return lay
 
 
@@ -118,3 +119,24 @@ def test_f16_weight_format_full_size(name, bf16_layer):
     torch.cuda.empty_cache()
     for key in ref:
         np.testing.assert_array_equal(got[key], ref[key], err_msg="%s %s" % (name, key))
+
+
+@pytest.mark.parametrize("name", ["m1", "m2"])
+def test_muse_sublayer_full_size(name, layer_host, bf16_layer):
+    # sigmoid router with a correction bias, latent pre-norm, input-scaled
+    # output norm and the alpha/beta residual gate around the same layer
+    p = synthetic.PRESETS[name]
+    lay = preset_layer(p, layer_host, bf16_layer)
+    x = synthetic.inputs(p)
+    gpu = run(lay, x)
+    w = gpu["topk_w"]
+    say("%s weight sums: min %.6f max %.6f" % (name, w.sum(1).min(), w.sum(1).max()))
+    np.testing.assert_allclose(w.sum(1), p.routed_scale, rtol=1e-5)
+    if p.T <= 64:
+        compare(p, lay.host, x, gpu, label=name)
+        st = synthetic.sample_tokens(p.T, 4, seed=71)
+    else:
+        compare(p, lay.host, x, gpu, tokens=synthetic.sample_tokens(p.T, 32, seed=72),
+                route_tokens=synthetic.sample_tokens(p.T, 1024, seed=73), label=name)
+        st = synthetic.sample_tokens(p.T, 4, seed=74)
+    check_stages(p, lay.host, x, gpu, st, label=name)
