@@ -9,8 +9,10 @@ with every input already resident in HBM.
 
 Default workload: decode, T=64 tokens (also timed with the Infinity Cache
 flushed between calls).  Further line items time the prefill regime
-(T=8192), skewed routing (T=16384) and MXFP4 weights (4 chunks of 8192).
-Prints one JSON line.
+(T=8192), skewed routing (T=16384), MXFP4 weights (4 chunks of 8192) and
+the Muse sublayer around the same layer (sigmoid router with a correction
+bias, latent pre-norm, input-scaled output norm, alpha/beta residual gate)
+at T=64 and T=8192.  Prints one JSON line.
 """
 from __future__ import annotations
 
@@ -143,7 +145,10 @@ def main():
     def make_desc(T, pr, wf):
         return moe.make_desc(T, pr.d, pr.L, pr.n, pr.k, pr.F, expert_kind=pr.kind, act=pr.act, router=pr.router_w,
                              weights=wf, in_norm=pr.in_norm, expert_norm=pr.expert_norm, res_gate=pr.res_gate,
-                             eps_in=pr.eps_in, eps_expert=pr.eps_expert)
+                             eps_in=pr.eps_in, eps_expert=pr.eps_expert, interm=pr.interm, router_fn=pr.router_fn,
+                             out_mult=pr.out_mult, routed_scale=pr.routed_scale, latent_norm=pr.latent_norm,
+                             eps_latent=pr.eps_latent, out_norm=pr.out_norm, eps_out=pr.eps_out, res_tau=pr.res_tau,
+                             res_floor=pr.res_floor)
 
     stream = torch.cuda.current_stream()
 
@@ -176,7 +181,12 @@ def main():
         torch.cuda.synchronize()
         wall = time.perf_counter() - t_start
         stages = {}
-        ran = [s for s in moe.STAGES if s != "in_norm" or pr.in_norm != "none"]
+        skip = set()
+        if pr.in_norm == "none":
+            skip.add("in_norm")
+        if pr.out_norm == "none" and pr.res_gate != "muse":
+            skip.add("resgate")  # the linear gate runs in the up-projection's epilogue
+        ran = [s for s in moe.STAGES if s not in skip]
         for s in ran:
             v = [sum(e.elapsed_ms(s) or 0.0 for e in row) for row in evs]
             if any(v):
@@ -318,6 +328,18 @@ def main():
                                                  "MXFP4 weights, 4 chunks of T=8192, input norm %s" % p4.in_norm)
         del W4
         torch.cuda.empty_cache()
+
+    # ---- the Muse sublayer around the same layer ----
+    if not args.no_extra:
+        result["muse"] = {}
+        for name, steps, label in (("m1", args.steps, "decode T=64"), ("m2", 5, "prefill T=8192")):
+            pm = synthetic.PRESETS[name]
+            gv = {k: to_dev(v) for k, v in synthetic.gains(pm).items()}
+            gm = {"router_bias": gv.get("bias"), "gamma_in": gv.get("gamma_in"), "gamma_expert": gv.get("gamma_ex"),
+                  "res_gate": gv.get("gate"), "gamma_latent": gv.get("gamma_lat"), "gamma_out": gv.get("gamma_out")}
+            result["muse"][name] = report(pm, run_workload(pm, steps, 2, gd=gm),
+                                          "Muse sublayer (sigmoid router + bias, C_pre, output norm, alpha/beta "
+                                          "gate), " + label)
 
     # ---- CPU oracle baseline on a bounded sample of the decode workload ----
     if not args.no_cpu_baseline:

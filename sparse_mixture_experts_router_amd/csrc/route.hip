@@ -545,19 +545,23 @@ __global__ __launch_bounds__(256) void combine_kernel(const uint16_t *__restrict
 // overwritten element by element by the thread that read it.
 // ---------------------------------------------------------------------------
 
-template <bool NORM>
+template <bool NORM, int J>
 __global__ __launch_bounds__(256) void resgate_rows_kernel(const uint16_t *__restrict__ S,
                                                            const float *__restrict__ ssq, int nparts, float eps,
                                                            const uint16_t *__restrict__ x,
                                                            const float *__restrict__ g, int res, float tau,
-                                                           float floor_, int64_t T, int64_t d, float *out,
-                                                           float *__restrict__ ydbg) {
+                                                           float floor_, int64_t T, int64_t d, int rows,
+                                                           float *out, float *__restrict__ ydbg) {
+    // workgroup b: column slice b % nslices (256 * J chunks of 8 values), rows (b / nslices) * rows + [0, rows)
     __shared__ float lds4[4];
     const int64_t nch = d / 8;
-    float ca[kNormMaxChunks][8], cb[kNormMaxChunks][8];
+    const int nslices = (int)((nch + 256 * J - 1) / (256 * J));
+    const int slice = blockIdx.x % nslices;
+    const int64_t row0 = (int64_t)(blockIdx.x / nslices) * rows;
+    float ca[J][8], cb[J][8];
 #pragma unroll
-    for (int j = 0; j < kNormMaxChunks; ++j) {
-        const int64_t c = threadIdx.x + 256 * j;
+    for (int j = 0; j < J; ++j) {
+        const int64_t c = (int64_t)slice * 256 * J + threadIdx.x + 256 * j;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             float a = 0.f, b = 1.f;
@@ -577,8 +581,8 @@ __global__ __launch_bounds__(256) void resgate_rows_kernel(const uint16_t *__res
             cb[j][i] = b;
         }
     }
-    const int64_t r1 = min<int64_t>(T, (int64_t)(blockIdx.x + 1) * kNormRows);
-    for (int64_t row = (int64_t)blockIdx.x * kNormRows; row < r1; ++row) {
+    const int64_t r1 = min<int64_t>(T, row0 + rows);
+    for (int64_t row = row0; row < r1; ++row) {
         float inv = 1.f;
         if constexpr (NORM) {
             float sq = 0.f;
@@ -587,8 +591,8 @@ __global__ __launch_bounds__(256) void resgate_rows_kernel(const uint16_t *__res
             inv = 1.0f / sqrtf(sq / (float)d + eps);
         }
 #pragma unroll
-        for (int j = 0; j < kNormMaxChunks; ++j) {
-            const int64_t c = threadIdx.x + 256 * j;
+        for (int j = 0; j < J; ++j) {
+            const int64_t c = (int64_t)slice * 256 * J + threadIdx.x + 256 * j;
             if (c >= nch) continue;
             float bv[8];
             if constexpr (NORM) {
@@ -742,7 +746,8 @@ template <int IT>
 static hipError_t run_rmsnorm(const uint16_t *x, const float *gamma, uint16_t *u, int64_t T, int64_t d, float eps,
                               int mode, hipStream_t s) {
     if (T <= 0) return hipSuccess;
-    if (d / 8 <= 256 * kNormMaxChunks)
+    // eight rows per workgroup once that still gives 256 or more workgroups
+    if (d / 8 <= 256 * kNormMaxChunks && T >= 256 * kNormRows)
         rmsnorm_rows_kernel<IT><<<(unsigned)((T + kNormRows - 1) / kNormRows), 256, 0, s>>>(x, gamma, u, T, d, eps,
                                                                                              mode);
     else
@@ -796,11 +801,26 @@ hipError_t launch_resgate(const uint16_t *S, const float *ssq, int nparts, float
                           float *ydbg, hipStream_t s) {
     if (T <= 0) return hipSuccess;
     if (d % 8 || d / 8 > 256 * kNormMaxChunks) return hipErrorInvalidValue;
-    const unsigned grid = (unsigned)((T + kNormRows - 1) / kNormRows);
-    if (S)
-        resgate_rows_kernel<true><<<grid, 256, 0, s>>>(S, ssq, nparts, eps, x, g, res, tau, floor_, T, d, out, ydbg);
-    else
-        resgate_rows_kernel<false><<<grid, 256, 0, s>>>(S, ssq, nparts, eps, x, g, res, tau, floor_, T, d, out, ydbg);
+    // Large batches: a workgroup takes kNormRows whole rows (gate coefficients
+    // computed once for eight rows).  Small batches: one row and a 2048-value
+    // slice each, so a decode batch still spreads over the chip.
+    if (T >= 2048) {
+        const unsigned grid = (unsigned)((T + kNormRows - 1) / kNormRows);
+        if (S)
+            resgate_rows_kernel<true, kNormMaxChunks><<<grid, 256, 0, s>>>(S, ssq, nparts, eps, x, g, res, tau,
+                                                                           floor_, T, d, kNormRows, out, ydbg);
+        else
+            resgate_rows_kernel<false, kNormMaxChunks><<<grid, 256, 0, s>>>(S, ssq, nparts, eps, x, g, res, tau,
+                                                                            floor_, T, d, kNormRows, out, ydbg);
+    } else {
+        const unsigned grid = (unsigned)(T * ((d / 8 + 255) / 256));
+        if (S)
+            resgate_rows_kernel<true, 1><<<grid, 256, 0, s>>>(S, ssq, nparts, eps, x, g, res, tau, floor_, T, d, 1,
+                                                              out, ydbg);
+        else
+            resgate_rows_kernel<false, 1><<<grid, 256, 0, s>>>(S, ssq, nparts, eps, x, g, res, tau, floor_, T, d, 1,
+                                                               out, ydbg);
+    }
     return hipGetLastError();
 }
 

@@ -153,7 +153,7 @@ class Preset:
     eps_expert: float = 1e-6
     layer_seed: int = 1
     input_seed: int = 1
-    router_bias: str = "none"      # "none" | "zipf" | "normal" (N(0, 0.05) correction bias)
+    router_bias: str = "none"      # "none" | "zipf" | "normal" | "normal_wide" (correction biases, see gains())
     chunks: int = 1
     w_std: float = 0.02            # latent layers; c0 uses 1/sqrt(fan_in)
     bias_in_weights: int = 0
@@ -301,8 +301,15 @@ def gains(p: Preset) -> dict:
         out["gamma_out"] = normal_f32(s, "gamma_out", p.d, 0.02)
     if p.router_bias == "zipf":
         out["bias"] = zipf_bias(p.n)
-    elif p.router_bias == "normal":
-        out["bias"] = normal_f32(s, "router_bias", p.n, 0.05)
+    elif p.router_bias in ("normal", "normal_wide"):
+        # A correction bias for sigmoid scores.  "normal" (std 0.002) is of the
+        # order of the gaps between a token's top sigmoid scores at the full
+        # shape: it changes the expert set of ~30% of the tokens while the
+        # load stays about as balanced as without it (the bias exists to
+        # balance load).  "normal_wide" (std 0.05) swamps those gaps: a few
+        # experts take most tokens (a skewed-load stress case).
+        std = 0.002 if p.router_bias == "normal" else 0.05
+        out["bias"] = normal_f32(s, "router_bias", p.n, std)
     return out
 
 

@@ -83,6 +83,7 @@ def test_muse_small_prefill_shape(weights):
     dict(res_gate="muse", out_norm="none"),                           # alpha/beta on the raw branch
     dict(res_gate="none", out_norm="centered"),                       # output-scaled output norm
     dict(res_gate="linear", out_norm="none", latent_norm="none"),     # sigmoid router on the fused path
+    dict(router_bias="normal_wide"),                                  # a bias that swamps the score gaps
     dict(router_fn="softmax", router_bias="zipf", latent_norm="centered", out_norm="none", res_gate="linear"),
 ])
 @pytest.mark.parametrize("T", [77, 300])
