@@ -266,52 +266,31 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 // Large-tile kernel (many rows per expert; dense projections at large T)
 // ---------------------------------------------------------------------------
 //
-// Tile 256 (A rows) x 256 (B rows), 256 threads as 2 x 2 waves of 128 x 128,
-// each a 4 x 4 grid of 32 x 32 x 16 MFMA blocks (one wave per SIMD keeps this
-// MFMA shape close to its peak issue rate; the 16 x 16 x 32 shape would need
-// two waves per SIMD).  K advances in pairs of 64: a pair buffer holds the A
-// and B rows of one pair as 128-byte rows, and two buffers alternate.
-// Operands move global -> LDS with direct-to-LDS loads (global_load_lds): a
-// wave instruction fills 8 rows x 128 bytes of LDS in lane order, so each lane
-// fetches the global chunk that belongs at its XOR-swizzled LDS slot, and
-// every L2 request is a whole 128-byte row segment.  A pair runs as two 32-K
-// sub-steps.  Fragments are double-buffered in registers: the MFMAs of one
-// sub-step overlap the LDS reads of the next, and the loads of pair p+2 are
-// spread between the MFMAs of pair p's second sub-step; the only barrier of a
-// pair sits in front of it.
-// When the MFMA type differs from the stored weights (bf16 weights with fp16
-// activations, or MXFP4), each wave converts the share of a pair's B that its
-// own loads brought in, in LDS, before the barrier that publishes the pair
-// (bf16 -> fp16 in place; MXFP4 codes and block scales -> the activation type
-// into the B operand area), so MFMA operands always come straight from LDS.
+// Output tiles of 32 x 32 x 16 MFMA blocks, one wave per SIMD (four waves;
+// eight for the wide mode): with one wave per SIMD this MFMA shape issues
+// close to its peak rate, the 16 x 16 x 32 shape would need two.  K advances
+// in pairs of 64: a K pair of A (activation) or B (weight) rows sits in LDS
+// as 128-byte rows.  Operands move global -> LDS with buffer loads straight
+// into LDS: a wave instruction fills 8 rows x 128 bytes in lane order, so
+// each lane fetches the global chunk that belongs at its XOR-swizzled LDS
+// slot and every L2 request is a whole 128-byte row segment.  A double-
+// buffers and B rotates through three slots (the weight ring below); MXFP4
+// slots hold codes and scale words that are dequantised in registers as the
+// fragments are read, and bf16 weights under fp16 activations are converted
+// per fragment in registers.  A pair runs as two 32-K sub-steps with
+// fragments double-buffered in registers: the MFMAs of one overlap the LDS
+// reads of the next, the loads of later pairs are spread between the MFMAs,
+// and the only barrier of a pair sits in front of it.
 // The MFMA operands are swapped (B first), so a lane's accumulator registers
 // hold runs of four adjacent output columns of one row: epilogue stores are 8
 // or 16 bytes wide.  EPI_SWIGLU tiles hold 128 gate rows then the 128 matching
 // up rows; a wave's gate column blocks pair with its up column blocks.
 // Rows past the tile's valid rows load a clamped valid A row; their results
-// are never stored.  The half-height variant (HM) serves grouped tiles of at
-// most 128 rows (an expert's remainder): its four waves share the 128 A rows
-// and each takes 64 of the 256 B rows, so no wave idles on empty rows.
+// are never stored.
 
 constexpr int kBigBM = kTileBM, kBigBN = kTileBN, kBigBK = 64;  // K per pair
 static_assert(kBigBM == 256 && kBigBN == 256, "the wave layout below assumes 256x256 tiles");
 constexpr int kBigRow = kBigBK * 2;                             // bytes per LDS row (128)
-constexpr int kBigOpBytes = kBigBM * kBigRow;                   // A area, or B area in the MFMA type: 32 KiB
-constexpr int kBigMxCodeOff = 2 * kBigOpBytes;                  // MXFP4: 256 rows x 32 bytes of codes,
-constexpr int kBigMxScaleOff = kBigMxCodeOff + kBigBN * 32;     // then 256 scale words
-constexpr int kBigPairBytes = kBigMxScaleOff + kBigBN * 4;      // 73 KiB; two buffers = 146 KiB
-
-__shared__ __attribute__((aligned(16))) uint8_t big_lds0[kBigPairBytes];
-__shared__ __attribute__((aligned(16))) uint8_t big_lds1[kBigPairBytes];
-
-// Separate LDS objects per buffer let the compiler see that a read of one
-// buffer does not depend on the loads still landing in the other.
-template <int P>
-__device__ __forceinline__ uint8_t *big_buf() {
-    if constexpr (P == 0) return big_lds0;
-    else return big_lds1;
-}
-
 #define MOE_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
 // 128-byte rows (64 x 16-bit): 16-byte chunk c of row r lives at chunk
@@ -338,10 +317,7 @@ template <int TM> struct BigTile {
     static constexpr int NA = BM / (8 * WAVES);                     // A loads (8 rows) per wave per pair
     static constexpr int NBL = BN / (8 * WAVES);                    // bf16 B loads per wave per pair
     static constexpr int NBC = BN / 128;                            // MXFP4 code loads per wave per pair
-    static constexpr int BOFF = (TM >= 2 ? 320 : 256) * kBigRow;    // MXFP4 buffers: byte offset of the B area
     static constexpr int BPW = BN / WAVES;                          // B rows loaded by one wave
-    template <bool MX> static constexpr int kPerPair = NA + (MX ? NBC + 1 : NBL);
-    static_assert(TM == 3 || BOFF + BN * kBigRow <= kBigMxCodeOff, "A and B areas must end before the MXFP4 area");
 };
 
 // Load addresses: a wave-uniform base plus a 32-bit byte offset per lane, so
@@ -368,89 +344,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t ring_rsrc(const void *ptr) {
 // for a pure weight stream on this chip).
 constexpr int kStreamPolicy = 2;  // nt
 
-// Direct-to-LDS loads of K pair pr into buffer P.
-template <int P, bool MX, int TM>
-__device__ __forceinline__ void big_issue(const BigCtx &c, int pr, int wave) {
-    using S = BigTile<TM>;
-    uint8_t *buf = big_buf<P>();
-    const uint8_t *Ak = c.A + (int64_t)pr * kBigRow;
-#pragma unroll
-    for (int i = 0; i < S::NA; ++i)
-        __builtin_amdgcn_global_load_lds(Ak + c.aoff[i], MOE_LDS(buf + (wave * S::NA + i) * 1024), 16, 0, 0);
-    if constexpr (MX) {
-        const uint8_t *Bk = c.B + (int64_t)pr * 32;
-#pragma unroll
-        for (int i = 0; i < S::NBC; ++i)
-            __builtin_amdgcn_global_load_lds(Bk + c.boff[i], MOE_LDS(buf + kBigMxCodeOff + (wave * S::NBC + i) * 1024),
-                                             16, 0, kStreamPolicy);
-        // the 4-byte-aligned word holding the scale bytes of K-tiles 2pr, 2pr+1
-        __builtin_amdgcn_global_load_lds(c.bsc + (int64_t)((2 * pr) & ~3) + c.boff[2],
-                                         MOE_LDS(buf + kBigMxScaleOff + wave * 256), 4, 0, 0);
-    } else {
-        uint8_t *bb = buf + S::BOFF;
-        const uint8_t *Bk = c.B + (int64_t)pr * kBigRow;
-#pragma unroll
-        for (int i = 0; i < S::NBL; ++i)
-            __builtin_amdgcn_global_load_lds(Bk + c.boff[i], MOE_LDS(bb + (wave * S::NBL + i) * 1024), 16, 0,
-                                             kStreamPolicy);
-    }
-}
-
-// MXFP4 weights are dequantised in LDS, once per wave share; bf16 weights
-// with fp16 activations are converted per fragment in registers, between
-// the MFMAs.
-template <bool MX, int AT> constexpr bool kBigConvert = MX;
+// bf16 weights under fp16 activations are converted per fragment in
+// registers, between the MFMAs.
 template <bool MX, int AT> constexpr bool kBigRegConvert = !MX && AT == ACT_F16;
-
-// Dequantise the MXFP4 codes that this wave's own loads put into buffer P
-// (pair pr): the 64 codes of each of the wave's B rows times the block scales
-// of K-tiles 2pr and 2pr+1 -> eight swizzled chunks of the B operand area.
-// With 64 rows per wave a lane does a whole row; with 32 rows (TM 2) the two
-// half-waves split a row's chunks.
-template <int P, int TM, int AT>
-__device__ __forceinline__ void big_convert(int pr, int wave, int lane) {
-    using S = BigTile<TM>;
-    uint8_t *buf = big_buf<P>();
-    uint8_t *bb = buf + S::BOFF;
-    constexpr int SPLIT = 64 / S::BPW;                   // lanes per row: 1 or 2
-    const int li = lane % S::BPW, part = lane / S::BPW;  // part: which chunks of the row
-    const int r = wave * S::BPW + li;
-    const uint32_t sw = *(const uint32_t *)(buf + kBigMxScaleOff + (wave * 64 + li) * 4);
-    const uint32_t s0 = (sw >> (8 * ((2 * pr) & 3))) & 255u, s1 = (sw >> (8 * ((2 * pr + 1) & 3))) & 255u;
-#pragma unroll
-    for (int h = 0; h < 2; ++h) {
-        if (SPLIT == 2 && h != part) continue;
-        const uint4 cw = *(const uint4 *)(buf + kBigMxCodeOff + r * 32 + h * 16);
-        const uint32_t sc = h ? s1 : s0;
-        *(uint4 *)(bb + bswz(r, 4 * h + 0)) = mxfp4x8_to_act<AT>(cw.x, sc);
-        *(uint4 *)(bb + bswz(r, 4 * h + 1)) = mxfp4x8_to_act<AT>(cw.y, sc);
-        *(uint4 *)(bb + bswz(r, 4 * h + 2)) = mxfp4x8_to_act<AT>(cw.z, sc);
-        *(uint4 *)(bb + bswz(r, 4 * h + 3)) = mxfp4x8_to_act<AT>(cw.w, sc);
-    }
-}
-
-// Fragments of sub-step HS (K 32*HS .. +31 of the pair in buffer P) for the
-// 32x32x16 MFMA: lane (lr = l%32, lh = l/32) reads row lr of each 32-row
-// block at K half h, i.e. logical chunk 4*HS + 2h + lh.
-// fa[2m + h]: A rows arow0 + 32m + lr; fb[2c + h]: B rows bcol[c] + lr.
-template <int P, int HS, int TM, bool CVT>
-__device__ __forceinline__ void big_read(uint4 (&fa)[2 * BigTile<TM>::MB], uint4 (&fb)[2 * BigTile<TM>::NBK],
-                                         const int (&bcol)[BigTile<TM>::NBK], int arow0, int lr, int lh) {
-    using S = BigTile<TM>;
-    const uint8_t *buf = big_buf<P>();
-    const uint8_t *bb = buf + S::BOFF;
-#pragma unroll
-    for (int c = 0; c < S::NBK; ++c)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) {
-            const uint4 v = *(const uint4 *)(bb + bswz(bcol[c] + lr, 4 * HS + 2 * h + lh));
-            fb[2 * c + h] = CVT ? bf16x8_to_f16x8(v) : v;
-        }
-#pragma unroll
-    for (int m = 0; m < S::MB; ++m)
-#pragma unroll
-        for (int h = 0; h < 2; ++h) fa[2 * m + h] = *(const uint4 *)(buf + bswz(arow0 + m * 32 + lr, 4 * HS + 2 * h + lh));
-}
 
 // The MFMAs of one sub-step, K half by K half, so two MFMAs on one
 // accumulator are MB * NBK instructions apart.
@@ -471,52 +367,6 @@ __device__ __forceinline__ void big_mma(floatx16_t (&acc)[BigTile<TM>::MB][BigTi
 // and 15:14, expcnt 6:4, lgkmcnt 11:8.
 constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
 constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
-
-// Pair pr (buffer P) in two sub-steps.  On entry the wave holds the
-// fragments of sub-step 2pr (f0), buffer P is complete everywhere, and the
-// loads of pair pr+1 (buffer P^1) are in flight.
-//   first:  read sub-step 2pr+1 (buffer P) into f1; MFMAs on f0.
-//   second: wait for the own loads of pair pr+1, dequantise them if needed,
-//           barrier (pair pr+1 complete everywhere, every read of buffer P
-//           done), loads of pair pr+2 into buffer P (clamped to the last pair
-//           near the end: those loads are never read), read sub-step 2pr+2
-//           (buffer P^1) into f0, MFMAs on f1 with the loads and reads spread
-//           between them.
-template <int P, bool MX, int AT, int TM>
-__device__ __forceinline__ void big_pair(const BigCtx &c, floatx16_t (&acc)[BigTile<TM>::MB][BigTile<TM>::NBK],
-                                         uint4 (&fa0)[2 * BigTile<TM>::MB], uint4 (&fb0)[2 * BigTile<TM>::NBK],
-                                         uint4 (&fa1)[2 * BigTile<TM>::MB], uint4 (&fb1)[2 * BigTile<TM>::NBK],
-                                         const int (&bcol)[BigTile<TM>::NBK], int pr, int npair, int wave, int arow0,
-                                         int lane) {
-    using S = BigTile<TM>;
-    constexpr bool CVT = kBigRegConvert<MX, AT>;
-    const int lr = lane & 31, lh = lane >> 5;
-    big_read<P, 1, TM, CVT>(fa1, fb1, bcol, arow0, lr, lh);
-    big_mma<AT, TM>(acc, fa0, fb0);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
-    if constexpr (kBigConvert<MX, AT>) big_convert<P ^ 1, TM, AT>(pr + 1, wave, lane);
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-    __builtin_amdgcn_s_barrier();
-    __builtin_amdgcn_sched_barrier(0);
-    big_issue<P, MX, TM>(c, min(pr + 2, npair - 1), wave);
-    big_read<P ^ 1, 0, TM, CVT>(fa0, fb0, bcol, arow0, lr, lh);
-    big_mma<AT, TM>(acc, fa1, fb1);
-    constexpr int NL = S::template kPerPair<MX>, NR = 2 * (S::MB + S::NBK), NM = 2 * S::MB * S::NBK;
-#pragma unroll
-    for (int i = 0; i < NL; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // direct-to-LDS load
-    }
-#pragma unroll
-    for (int i = 0; i < NR; ++i) {
-        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-        __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-    }
-    __builtin_amdgcn_sched_group_barrier(0x008, NM - NL - NR > 0 ? NM - NL - NR : 0, 0);
-    __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-}
 
 // ---------------------------------------------------------------------------
 // bf16 weights: a three-slot weight ring.  Every weight byte comes from HBM
@@ -643,8 +493,10 @@ __device__ __forceinline__ void ring_read_mx(uint4 (&fa)[2 * BigTile<TM>::MB], u
             fa[2 * m + h] = *(const uint4 *)(ab + bswz(arow0 + m * 32 + lr, 4 * HS + 2 * lh + h));
 }
 
-// Fragments of sub-step HS from activation slot SA and weight slot SB (the
-// same lane mapping as big_read).
+// Fragments of sub-step HS from activation slot SA and weight slot SB:
+// lane (lr = l % 32, lh = l / 32) reads row lr of each 32-row block at
+// logical chunks 4 * HS + 2h + lh (fa[2m + h]: A rows arow0 + 32m + lr;
+// fb[2c + h]: B rows bcol[c] + lr).
 template <int TM, int SA, int SB, int HS, bool CVT>
 __device__ __forceinline__ void ring_read(uint4 (&fa)[2 * BigTile<TM>::MB], uint4 (&fb)[2 * BigTile<TM>::NBK],
                                           const int (&bcol)[BigTile<TM>::NBK], int arow0, int lr, int lh) {
