@@ -286,8 +286,8 @@ def main():
             "stage_ms": {k: round(v, 4) for k, v in r2["stages"].items()},
             # at ~256 rows per expert GEMM1 does ~240 FLOP per byte it must move, below the chip's
             # 2.5 PFLOP/s / 8 TB/s = 312 FLOP/B balance: HBM bounds it (2.3 ms vs 1.8 ms of MFMA)
-            "roofline": {"kernel": "gemm_big_kernel, grouped GEMM1 + SwiGLU (full-tile and tall-tile launches, "
-                                   "timed together by the stage's HIP events)",
+            "roofline": {"kernel": "gemm_big_kernel + gemm_wide_kernel, grouped GEMM1 + SwiGLU (full-tile and "
+                                   "wide-tile launches, timed together by the stage's HIP events)",
                          "bound": "hbm", "achieved": round(by2["gemm1"] / (g1 * 1e-3) / 1e9, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(by2["gemm1"] / (g1 * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
