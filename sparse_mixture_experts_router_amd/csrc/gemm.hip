@@ -294,10 +294,16 @@ constexpr int kBigRow = kBigBK * 2;                             // bytes per LDS
 #define MOE_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
 // 128-byte rows (64 x 16-bit): 16-byte chunk c of row r lives at chunk
-// c ^ ((r >> 1) & 3), so the 8 rows a ds_read_b128 phase serves at one
-// logical chunk hit 8 distinct 16-byte bank groups.
+// c ^ swz(r).  A fragment read takes one logical chunk of 32 consecutive
+// rows (lanes 0-31) and the next chunk of the same rows (lanes 32-63).  Any
+// 8 consecutive rows from a multiple of 8 get 8 distinct XOR terms, and of
+// 16 rows from a multiple of 16 the even ones get 8 distinct terms and so do
+// the odd ones, so a phase of 8 lanes over 128 bytes of banks and a phase of
+// 16 lanes over 256 bytes both touch every 16-byte bank group once.
+__host__ __device__ constexpr int swz(int r) { return (r & 7) ^ ((r >> 3) & 1); }
+
 __device__ __forceinline__ int bswz(int row, int chunk) {
-    return row * kBigRow + ((chunk ^ ((row >> 1) & 3)) << 4);
+    return row * kBigRow + ((chunk ^ swz(row)) << 4);
 }
 
 // Tile modes: TM 0 = full (256 A rows x 256 B rows; 2 x 2 waves of 128 x 128),
@@ -763,9 +769,11 @@ __device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, i
     const int ks = (EPI == EPI_F32 && !MX && !GROUPED && a.ksplit > 1) ? a.ksplit : 1;
     const int64_t kn = K / ks, k0 = (int64_t)ksl * kn;  // this item's K slice
     const int npair = (int)(kn / kBigBK);  // a multiple of 8
-    // Direct-load lane mapping of 128-byte rows: lane l fills row 8q + (l >> 3),
-    // physical chunk l & 7, i.e. logical chunk (l & 7) ^ ((l >> 4) & 3).
-    const int drow = lane >> 3, dchunk = (lane & 7) ^ ((lane >> 4) & 3);
+    // Direct-load lane mapping of 128-byte rows: load q of a wave fills LDS
+    // rows 8q .. 8q + 7, lane l row 8q + (l >> 3) at physical chunk l & 7,
+    // i.e. logical chunk (l & 7) ^ swz(8q + (l >> 3)).
+    const int drow = lane >> 3;
+    auto dchunk = [&](int ldsrow) { return (lane & 7) ^ swz(ldsrow); };
     const int64_t brow0 = GROUPED ? (int64_t)rt.e * a.b_group_rows : 0;
 
     // Tile B rows of this wave's column blocks.  SWIGLU: the tile's first BN/2
@@ -784,10 +792,11 @@ __device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, i
     c.A = (const uint8_t *)a.A + k0 * 2;
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-        const int row = min(wave * (NA * 8) + i * 8 + drow, rt.mcount - 1);
+        const int lrow = wave * (NA * 8) + i * 8 + drow;  // LDS row; the source row is clamped to a valid one
+        const int row = min(lrow, rt.mcount - 1);
         const int64_t p = rt.p0 + row;
         const int64_t arow = a.a_gather ? (int64_t)a.a_gather[p] : p;
-        c.aoff[i] = (uint32_t)((arow * a.lda + dchunk * 8) * 2);
+        c.aoff[i] = (uint32_t)((arow * a.lda + dchunk(lrow) * 8) * 2);
     }
 #pragma unroll
     for (int i = NA; i < 12; ++i) c.aoff[i] = 0;
@@ -814,7 +823,9 @@ __device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, i
         c.B = (const uint8_t *)((const uint16_t *)a.B + bfirst * K + k0);
 #pragma unroll
         for (int i = 0; i < 8; ++i)
-            c.boff[i] = i < S::NBL ? (uint32_t)((brel(wave * S::BPW + i * 8 + drow) * K + dchunk * 8) * 2) : 0;
+            c.boff[i] = i < S::NBL ? (uint32_t)((brel(wave * S::BPW + i * 8 + drow) * K +
+                                                 dchunk(wave * S::BPW + i * 8 + drow) * 8) * 2)
+                                   : 0;
         c.bsc = nullptr;
         c.ra = ring_rsrc(c.A);
         c.rb = ring_rsrc(c.B);
