@@ -229,7 +229,11 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
             // Epilogue: lane holds rows 4*lg + q (q = 0..3) of each row block, column li.
 #pragma unroll
             for (int m = 0; m < MB; ++m) {
-                float rowsq[4] = {0.f, 0.f, 0.f, 0.f};
+                float rowsq[NB][4];  // EPI_NORM: sums of squares per 16-column block and row
+#pragma unroll
+                for (int c = 0; c < NB; ++c)
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) rowsq[c][q] = 0.f;
 #pragma unroll
                 for (int q = 0; q < 4; ++q) {
                     int row = m * 16 + lg * 4 + q;
@@ -244,17 +248,19 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
                         for (int c = 0; c < NB; ++c) {
                             int64_t n = (nb * NB + c) * 16 + li;
-                            if (ok) rowsq[q] += store_elem<EPI, OT>(a, p, n, acc[m][c][q]);
+                            if (ok) rowsq[c][q] += store_elem<EPI, OT>(a, p, n, acc[m][c][q]);
                         }
                     }
                 }
                 if constexpr (EPI == EPI_NORM) {
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        float v = sum16(rowsq[q]);
-                        int row = m * 16 + lg * 4 + q;
-                        if (li == 0 && row < rt.mcount) a.ssq[(rt.p0 + row) * a.nparts + nb] = v;
-                    }
+                    for (int c = 0; c < NB; ++c)
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) {
+                            float v = sum16(rowsq[c][q]);
+                            int row = m * 16 + lg * 4 + q;
+                            if (li == 0 && row < rt.mcount) a.ssq[(rt.p0 + row) * a.nparts + nb * NB + c] = v;
+                        }
                 }
             }
         }
@@ -1110,23 +1116,23 @@ hipError_t launch_gemm1(const GemmArgs &a, int path, bool mx, int at, hipStream_
 hipError_t launch_gemm2(const GemmArgs &a, int path, bool mx, int at, bool norm, hipStream_t s) {
     if (at == ACT_F16_W16) {
         if (mx) return hipErrorInvalidValue;
-        if (norm) return run_path<EPI_NORM, 1, false, true, ACT_F16_W16, ACT_BF16>(a, path, s);
-        return run_path<EPI_ACT, 1, false, true, ACT_F16_W16, ACT_BF16>(a, path, s);
+        if (norm) return run_path<EPI_NORM, 2, false, true, ACT_F16_W16, ACT_BF16>(a, path, s);
+        return run_path<EPI_ACT, 2, false, true, ACT_F16_W16, ACT_BF16>(a, path, s);
     }
     if (norm) {
         if (mx) {
-            if (at == ACT_F16) return run_path<EPI_NORM, 1, true, true, ACT_F16, ACT_BF16>(a, path, s);
-            return run_path<EPI_NORM, 1, true, true, ACT_BF16, ACT_BF16>(a, path, s);
+            if (at == ACT_F16) return run_path<EPI_NORM, 2, true, true, ACT_F16, ACT_BF16>(a, path, s);
+            return run_path<EPI_NORM, 2, true, true, ACT_BF16, ACT_BF16>(a, path, s);
         }
-        if (at == ACT_F16) return run_path<EPI_NORM, 1, false, true, ACT_F16, ACT_BF16>(a, path, s);
-        return run_path<EPI_NORM, 1, false, true, ACT_BF16, ACT_BF16>(a, path, s);
+        if (at == ACT_F16) return run_path<EPI_NORM, 2, false, true, ACT_F16, ACT_BF16>(a, path, s);
+        return run_path<EPI_NORM, 2, false, true, ACT_BF16, ACT_BF16>(a, path, s);
     }
     if (mx) {
-        if (at == ACT_F16) return run_path<EPI_ACT, 1, true, true, ACT_F16, ACT_BF16>(a, path, s);
-        return run_path<EPI_ACT, 1, true, true, ACT_BF16, ACT_BF16>(a, path, s);
+        if (at == ACT_F16) return run_path<EPI_ACT, 2, true, true, ACT_F16, ACT_BF16>(a, path, s);
+        return run_path<EPI_ACT, 2, true, true, ACT_BF16, ACT_BF16>(a, path, s);
     }
-    if (at == ACT_F16) return run_path<EPI_ACT, 1, false, true, ACT_F16, ACT_BF16>(a, path, s);
-    return run_path<EPI_ACT, 1, false, true, ACT_BF16, ACT_BF16>(a, path, s);
+    if (at == ACT_F16) return run_path<EPI_ACT, 2, false, true, ACT_F16, ACT_BF16>(a, path, s);
+    return run_path<EPI_ACT, 2, false, true, ACT_BF16, ACT_BF16>(a, path, s);
 }
 
 template <int EPI>
