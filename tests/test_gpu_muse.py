@@ -161,3 +161,21 @@ def test_sigmoid_router_saturation_and_underflow_fp32():
     assert list(gi[2]) == [3, 1, 0]
     s = np.array([0.9, 0.75, 0.5])
     np.testing.assert_allclose(gw[2], 2.0 * s / s.sum(), rtol=1e-6)
+
+
+@pytest.mark.parametrize("T,n,k", [(1, 32, 4), (40, 16, 16), (40, 256, 16)])
+def test_muse_degenerate_shapes(T, n, k):
+    # a single token; every expert selected (weights = all sigmoids / their sum); the widest router
+    # (256 experts) with the largest top-k (16)
+    run_and_compare(muse_case("muse_T%d_n%d_k%d" % (T, n, k), T=T, n=n, k=k))
+
+
+def test_muse_empty_batch_enqueues_nothing():
+    p = muse_case("muse_empty", T=0)
+    layer = DeviceLayer(p)
+    out = torch.empty((0, p.d), dtype=torch.float32, device="cuda")
+    x = torch.empty((0, p.d), dtype=torch.int16, device="cuda")
+    dv = layer.dev
+    moe.moe_layer_forward(desc_of(p, 0), x, dv["router_w"], dv["down_w"], dv["w1"], dv["w2"], dv["up_w"],
+                          layer.gains(), out)
+    torch.cuda.synchronize()
