@@ -69,7 +69,9 @@ enum {
 /*
  * Layer descriptor (host memory, read during the call only).
  *   T            tokens (rows of x); 0 is valid, enqueues nothing and
- *                accepts NULL tensor and workspace pointers
+ *                accepts NULL tensor and workspace pointers.  The latent
+ *                path takes batches with T * d_latent * 2 < 2^31 (the
+ *                latent z below 2 GiB; split larger batches)
  *   d_model      width d of x and out
  *   d_latent     latent width L of the expert space; 0 = experts read u
  *   n_experts    n (1..256); top_k: k (1..min(n,16))

@@ -81,18 +81,33 @@ __device__ __forceinline__ float sum16(float v) {
     return v;
 }
 
+#define MOE_LDS(p) ((__attribute__((address_space(3))) void *)(p))
+
+// Cache policy of the weight loads: every weight block is read once, and
+// the non-temporal (nt) policy moves them measurably faster (7.0 vs 6.2 TB/s
+// for a pure weight stream on this chip).
+constexpr int kStreamPolicy = 2;  // nt
+
+// Waits go through the s_waitcnt builtin (not inline asm) so the compiler's
+// own wait insertion knows of them.  gfx9 s_waitcnt fields: vmcnt bits 3:0
+// and 15:14, expcnt 6:4, lgkmcnt 11:8.
+constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
+constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
+
 // ---------------------------------------------------------------------------
 // Streaming kernel (small row counts per expert: weight-bandwidth bound)
 // ---------------------------------------------------------------------------
 //
 // Work item = (row tile, column block).  A column block is NB blocks of 16 B
 // rows (EPI_SWIGLU: NB = 2, the gate rows j0.. and the up rows F + j0..).
-// The 4 waves of the workgroup split K in four contiguous quarters.  Every
-// 128-wide K group is one lane-group-permuted MFMA quartet: lane group
-// g = lane/16 owns k in [32g, 32g+32) of the group and feeds 8 of them to
-// each of 4 MFMAs, so a lane reads 64 contiguous bytes of a bf16 B row (or
-// one whole 32-element MXFP4 block: 16 code bytes and its scale) and the
-// same 64 bytes of its A row.  Partial sums of the waves meet in LDS and
+// The 4 waves of the workgroup split K in four contiguous quarters.  Dense
+// items and MXFP4 weights load straight into registers: every 128-wide K
+// group is one lane-group-permuted MFMA quartet, lane group g = lane/16
+// owning k in [32g, 32g+32) of the group and feeding 8 of them to each of 4
+// MFMAs, so a lane reads 64 contiguous bytes of a bf16 B row (or one whole
+// 32-element MXFP4 block: 16 code bytes and its scale) and the same 64
+// bytes of its A row.  Grouped items on bf16/fp16 weights stage A and B
+// through LDS instead (below).  Partial sums of the waves meet in LDS and
 // wave 0 applies the epilogue.
 
 template <int MB, int NB>
@@ -133,13 +148,112 @@ __device__ __forceinline__ void stream_load(StreamFrag<MB, NB> &f, const uint8_t
     }
 }
 
+// Grouped items on bf16/fp16 weights stream their operands through LDS: a
+// buffer load of 64 lanes x 16 bytes straight into LDS fills 8 rows x 128
+// bytes of one 64-wide K group (whole cache lines; weights with the
+// non-temporal policy: a probe of this form streams at 7.0 TB/s against 6.2
+// for register loads in the lane pattern above).  Each wave keeps its K
+// groups in three slots (each its own LDS object), a slot holding the
+// group's A rows (16) and its 16-row B blocks.  Three slots of 4 waves x 3
+// blocks x 2 KB leave room for two workgroups per CU, so one covers the
+// other's start and end of an item.  In a block, row r keeps logical chunk
+// q (8 values) at chunk q ^ f(r), f(r) = (r >> 1) ^ 4 (r & 1): a fragment
+// read (rows 0..15 at one logical chunk) then hits distinct 16-byte bank
+// groups in every 8-lane and 16-lane phase.
+constexpr int kStrmKG = 64;                            // K per group
+constexpr int kStrmRow = kStrmKG * 2;                  // bytes per block row (128)
+constexpr int kStrmBlock = 16 * kStrmRow;              // bytes per 16-row block (2 KB)
+constexpr int kStrmLoads = kStrmBlock / 1024;          // loads per block (2)
+constexpr int kStrmWaveBytes = 3 * kStrmBlock;         // A block + 2 B blocks
+constexpr int kStrmSlotBytes = 4 * kStrmWaveBytes;     // 4 waves
+__shared__ __attribute__((aligned(16))) uint8_t strm_s0[kStrmSlotBytes];
+__shared__ __attribute__((aligned(16))) uint8_t strm_s1[kStrmSlotBytes];
+__shared__ __attribute__((aligned(16))) uint8_t strm_s2[kStrmSlotBytes];
+
+__device__ __forceinline__ int strm_swz(int r) { return (r >> 1) ^ ((r & 1) << 2); }
+
+template <int S>
+__device__ __forceinline__ uint8_t *strm_slot() {
+    if constexpr (S == 0) return strm_s0;
+    else if constexpr (S == 1) return strm_s1;
+    else return strm_s2;
+}
+
+// Per-item state of an LDS-streamed item: buffer descriptors of A (rows
+// gathered: per-row lane offsets from the buffer start) and of the first
+// row of each B block (rows consecutive); the lane's byte offsets of load i
+// of a block (rows 8i + lane / 8) in aoff[i] and boff[i]; the byte offsets
+// (within a slot) of its fragment reads in roff[s].
+struct StrmCtx {
+    __amdgpu_buffer_rsrc_t ra, rb0, rb1;
+    uint32_t aoff[kStrmLoads], boff[kStrmLoads], roff[kStrmKG / 32];
+};
+
+// A pointer the whole wave holds, moved to scalar registers (descriptors
+// built from it then stay scalar).  Both halves are taken as unsigned: the
+// builtin returns int, and a widened int would carry bit 31 of the low half
+// into the high half.
+__device__ __forceinline__ void *uniform_ptr(const void *p) {
+    const uint64_t v = (uint64_t)p;
+    const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    return (void *)(((uint64_t)hi << 32) | lo);
+}
+
+// Loads of the K group at element kk into slot S (this wave's area).
+template <int NB, int S>
+__device__ __forceinline__ void strm_issue(const StrmCtx &c, int wave, int64_t kk) {
+    // each access is one address step from its slot object, which keeps the
+    // compiler's per-object tracking of these loads (and with it the freedom
+    // to read other slots while they are in flight)
+    const int w0 = wave * kStrmWaveBytes;
+#pragma unroll
+    for (int i = 0; i < kStrmLoads; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.ra, MOE_LDS(strm_slot<S>() + (w0 + i * 1024)), 16, c.aoff[i],
+                                                 (int)(kk * 2), 0, 0);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int i = 0; i < kStrmLoads; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(b == 0 ? c.rb0 : c.rb1,
+                                                     MOE_LDS(strm_slot<S>() + (w0 + (1 + b) * kStrmBlock + i * 1024)),
+                                                     16, c.boff[i], (int)(kk * 2), 0, kStreamPolicy);
+}
+
+// One K group of an LDS-streamed item, slot S = g % 3.  On entry groups g
+// and g+1 are in flight, issued in that order; the step waits for group g
+// (all but the loads of group g+1), issues group g+2 into slot (S+2) % 3
+// (clamped to the last group: clamped loads are never read), reads group g
+// and runs its MFMAs.
+template <int NB, int AT, int S>
+__device__ __forceinline__ void strm_step(floatx4_t (&acc)[1][NB], const StrmCtx &c, int64_t kbeg, int g, int ng,
+                                          int wave) {
+    constexpr int NS = kStrmKG / 32;  // MFMA K steps per group
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm((1 + NB) * kStrmLoads));
+    __builtin_amdgcn_sched_barrier(0);
+    strm_issue<NB, (S + 2) % 3>(c, wave, kbeg + kStrmKG * (int64_t)min(g + 2, ng - 1));
+    uint4 fa[NS], fb[NB][NS];
+#pragma unroll
+    for (int s = 0; s < NS; ++s) fa[s] = *(const uint4 *)(strm_slot<S>() + c.roff[s]);
+#pragma unroll
+    for (int b = 0; b < NB; ++b)
+#pragma unroll
+        for (int s = 0; s < NS; ++s)
+            fb[b][s] = weight_bf16_as<AT>(*(const uint4 *)(strm_slot<S>() + c.roff[s] + (1 + b) * kStrmBlock));
+#pragma unroll
+    for (int s = 0; s < NS; ++s)
+#pragma unroll
+        for (int b = 0; b < NB; ++b) acc[0][b] = mfma16x16x32<AT>(fa[s], fb[b][s], acc[0][b]);
+}
+
 template <int MB, int NB, int EPI, bool MX, bool GROUPED, int AT, int OT>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
     constexpr int BM = 16 * MB;
     __shared__ floatx4_t red[3][MB][NB][64];
 
     const int lane = threadIdx.x & 63;
-    const int wave = threadIdx.x >> 6;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int li = lane & 15;  // row (A) / column (B) within a 16-block
     const int lg = lane >> 4;  // k group of 32 within a 128-wide K group
 
@@ -151,6 +265,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
     const int ntiles = GROUPED ? *a.ntiles : (int)((a.M + BM - 1) / BM);
     const int64_t items = (int64_t)ntiles * nblocks;
 
+    // grouped items on bf16/fp16 weights stream their weights through LDS
+    constexpr bool kDma = !MX && GROUPED && MB == 1 && NB <= 2;
     for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
         const int t = (int)(item / nblocks);
         const int64_t nb = item - (int64_t)t * nblocks;
@@ -180,7 +296,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
         const uint16_t *aptr[MB];
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
-            int row = m * 16 + li;
+            // DMA items: rows past the tile's valid rows read its last valid row (their
+            // results are never stored), so every load goes out and the wait counts hold
+            int row = kDma ? min(m * 16 + li, rt.mcount - 1) : m * 16 + li;
             if (row < rt.mcount) {
                 int64_t p = rt.p0 + row;
                 int64_t arow = a.a_gather ? (int64_t)a.a_gather[p] : p;
@@ -196,18 +314,73 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
             for (int c = 0; c < NB; ++c) acc[m][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-        StreamFrag<MB, NB> cur, nxt;
-        stream_load<MB, NB, MX, AT>(cur, bptr, bscale, aptr, kbeg);
-        for (int64_t kk = kbeg; kk < kend; kk += 128) {
-            if (kk + 128 < kend) stream_load<MB, NB, MX, AT>(nxt, bptr, bscale, aptr, kk + 128);
+        if constexpr (kDma) {
+            StrmCtx c;
+            // gathered A rows are addressed from the buffer start (the layer keeps that
+            // buffer below 2 GiB), contiguous ones from the tile's first row
+            const uint16_t *abase = a.a_gather ? a.A : a.A + rt.p0 * a.lda;
+            c.ra = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(abase), 0, 0x7fffffff, 0x00020000);
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
+            for (int b = 0; b < NB; ++b) {
+                int64_t r0;
+                if constexpr (EPI == EPI_SWIGLU)
+                    r0 = brow0 + (b == 0 ? 0 : a.N) + nb * 16;
+                else
+                    r0 = brow0 + (nb * NB + b) * 16;
+                const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr((const uint8_t *)a.B + r0 * K * 2),
+                                                                    0, 0x7fffffff, 0x00020000);
+                if (b == 0) c.rb0 = rsrc;
+                else c.rb1 = rsrc;
+            }
+            // load i of a block fills rows r = 8i + lane / 8; physical chunk lane % 8
+            // holds logical chunk (lane % 8) ^ f(r)
 #pragma unroll
-                for (int m = 0; m < MB; ++m)
+            for (int i = 0; i < kStrmLoads; ++i) {
+                const int r = 8 * i + (lane >> 3);
+                const int chunk = ((lane & 7) ^ strm_swz(r)) << 4;
+                const int rr = min(r, rt.mcount - 1);  // rows past the valid ones read the last
+                const int64_t arow = a.a_gather ? (int64_t)a.a_gather[rt.p0 + rr] : rr;
+                c.aoff[i] = (uint32_t)(arow * a.lda * 2 + chunk);
+                c.boff[i] = (uint32_t)(r * K * 2 + chunk);
+            }
+            // fragment reads: row li of the wave's blocks, logical chunk 2 lg + s.  Each
+            // offset is an opaque value, so every read is one short address step from
+            // its slot object (the compiler then knows which slot a read touches)
 #pragma unroll
-                    for (int c = 0; c < NB; ++c)
-                        acc[m][c] = mfma16x16x32<AT>(cur.a[m][s], cur.b[c][s], acc[m][c]);
-            cur = nxt;
+            for (int s = 0; s < kStrmKG / 32; ++s) {
+                c.roff[s] = (uint32_t)(wave * kStrmWaveBytes + li * kStrmRow +
+                                       ((((kStrmKG / 32) * lg + s) ^ strm_swz(li)) << 4));
+                asm("" : "+v"(c.roff[s]));
+            }
+            const int ng = (int)(kq / kStrmKG);
+            strm_issue<NB, 0>(c, wave, kbeg);
+            strm_issue<NB, 1>(c, wave, kbeg + kStrmKG * (int64_t)min(1, ng - 1));
+            int g = 0;
+            for (; g + 3 <= ng; g += 3) {
+                strm_step<NB, AT, 0>(acc, c, kbeg, g, ng, wave);
+                strm_step<NB, AT, 1>(acc, c, kbeg, g + 1, ng, wave);
+                strm_step<NB, AT, 2>(acc, c, kbeg, g + 2, ng, wave);
+            }
+            if (g < ng) {
+                strm_step<NB, AT, 0>(acc, c, kbeg, g, ng, wave);
+                if (g + 1 < ng) strm_step<NB, AT, 1>(acc, c, kbeg, g + 1, ng, wave);
+            }
+            // the clamped tail loads land before the slots are reused
+            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+        } else {
+            StreamFrag<MB, NB> cur, nxt;
+            stream_load<MB, NB, MX, AT>(cur, bptr, bscale, aptr, kbeg);
+            for (int64_t kk = kbeg; kk < kend; kk += 128) {
+                if (kk + 128 < kend) stream_load<MB, NB, MX, AT>(nxt, bptr, bscale, aptr, kk + 128);
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int m = 0; m < MB; ++m)
+#pragma unroll
+                        for (int c = 0; c < NB; ++c)
+                            acc[m][c] = mfma16x16x32<AT>(cur.a[m][s], cur.b[c][s], acc[m][c]);
+                cur = nxt;
+            }
         }
 
         // Cross-wave reduction, fixed order: wave0 + wave1 + wave2 + wave3.
@@ -297,7 +470,6 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 constexpr int kBigBM = kTileBM, kBigBN = kTileBN, kBigBK = 64;  // K per pair
 static_assert(kBigBM == 256 && kBigBN == 256, "the wave layout below assumes 256x256 tiles");
 constexpr int kBigRow = kBigBK * 2;                             // bytes per LDS row (128)
-#define MOE_LDS(p) ((__attribute__((address_space(3))) void *)(p))
 
 // 128-byte rows (64 x 16-bit): 16-byte chunk c of row r lives at chunk
 // c ^ swz(r).  A fragment read takes one logical chunk of 32 consecutive
@@ -351,10 +523,6 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t ring_rsrc(const void *ptr) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(ptr), 0, 0x7fffffff, 0x00020000);
 }
 
-// Cache policy of the weight loads: every weight block is read once, and
-// the non-temporal (nt) policy moves them measurably faster (7.0 vs 6.2 TB/s
-// for a pure weight stream on this chip).
-constexpr int kStreamPolicy = 2;  // nt
 
 // bf16 weights under fp16 activations are converted per fragment in
 // registers, between the MFMAs.
@@ -374,11 +542,6 @@ __device__ __forceinline__ void big_mma(floatx16_t (&acc)[BigTile<TM>::MB][BigTi
             for (int c = 0; c < S::NBK; ++c) acc[m][c] = mfma32x32x16<AT>(fb[2 * c + h], fa[2 * m + h], acc[m][c]);
 }
 
-// Waits go through the s_waitcnt builtin (not inline asm) so the compiler's
-// own wait insertion knows of them.  gfx9 s_waitcnt fields: vmcnt bits 3:0
-// and 15:14, expcnt 6:4, lgkmcnt 11:8.
-constexpr int waitcnt_vm(int n) { return (n & 15) | ((n >> 4) << 14) | (7 << 4) | (15 << 8); }
-constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 
 // ---------------------------------------------------------------------------
 // bf16 weights: a three-slot weight ring.  Every weight byte comes from HBM

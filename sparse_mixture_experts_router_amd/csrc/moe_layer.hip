@@ -146,6 +146,8 @@ int check_desc(const moe_desc *d) {
     if (d->weight_dtype == MOE_DT_F16 && d->interm_dtype == MOE_DT_BF16) return MOE_ERR_UNSUPPORTED;
     if (d->d_latent == 0 || d->expert_kind != MOE_EXPERT_SWIGLU3) return MOE_ERR_UNSUPPORTED;
     if (d->d_model % 512 || d->d_latent % 512 || d->d_ff % 512 || d->n_experts % 16) return MOE_ERR_UNSUPPORTED;
+    // the expert GEMMs address the latent rows they gather with 32-bit offsets
+    if (d->T * d->d_latent * 2 >= ((int64_t)1 << 31)) return MOE_ERR_UNSUPPORTED;
     // the latent pre-norm is the output-scaled form; the output norm and the
     // residual-gate kernel hold a row of at most 8192 values per workgroup
     if (d->latent_norm == MOE_NORM_INPUT_SCALED) return MOE_ERR_UNSUPPORTED;

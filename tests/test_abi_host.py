@@ -71,12 +71,19 @@ def test_workspace_grows_with_T_and_is_aligned():
     ("d_latent", 0, moe.MOE_ERR_UNSUPPORTED),
     ("weight_dtype", 0, moe.MOE_ERR_UNSUPPORTED),
     ("n_experts", 250, moe.MOE_ERR_UNSUPPORTED),
+    ("T", (1 << 30) // 4096, moe.MOE_ERR_UNSUPPORTED),   # latent z of 2 GiB: past 32-bit row offsets
 ])
 def test_validation_errors(field, value, code):
     d = desc_of(synthetic.PRESETS["c1"])
     setattr(d, field, value)
     assert moe.moe_validate(d) == code
     assert moe.moe_workspace_bytes(d) == 0
+
+
+def test_largest_batch_of_the_latent_path_validates():
+    d = desc_of(synthetic.PRESETS["c1"])
+    d.T = (1 << 30) // 4096 - 1
+    assert moe.moe_validate(d) == moe.MOE_OK
 
 
 def test_forward_rejects_before_any_launch():
