@@ -163,23 +163,51 @@ def main():
         ws = torch.empty(moe.moe_workspace_bytes(desc), dtype=torch.uint8, device=dev)
         counts = torch.empty(pr.n, dtype=torch.int32, device=dev)
 
-        def fwd(c, dbg=None):
+        def fwd(c, dbg=None, s=None):
             moe.moe_layer_forward(desc, xs[c], Wd["router_w"], Wd["down_w"], Wd["w1"], Wd["w2"], Wd["up_w"], gd,
-                                  out, workspace=ws, dbg=dbg, stream=stream)
+                                  out, workspace=ws, dbg=dbg, stream=s or stream)
+
+        def timed(step):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for _ in range(steps):
+                step()
+            torch.cuda.synchronize()
+            return (time.perf_counter() - t0) * 1e3 / steps
+
+        def eager_step():
+            for c in range(pr.chunks):
+                fwd(c)
 
         fwd(0, {"expert_counts": counts})
         torch.cuda.synchronize()
         for _ in range(warmup):
+            eager_step()
+        eager_ms = timed(eager_step)
+        # the same step as one HIP graph (the forward launches kernels only: no
+        # allocation, no memset), reported beside the plain calls
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        with torch.cuda.stream(side):
             for c in range(pr.chunks):
-                fwd(c)
+                fwd(c, s=side)
+        stream.wait_stream(side)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            cap = torch.cuda.current_stream()
+            for c in range(pr.chunks):
+                fwd(c, s=cap)
+        for _ in range(warmup):
+            graph.replay()
+        graph_ms = timed(graph.replay)
+        # per-stage times in a separate eager pass (the stage events add gaps of their own)
         evs = [[moe.StageEvents() for _ in range(pr.chunks)] for _ in range(steps)]
         torch.cuda.synchronize()
-        t_start = time.perf_counter()
         for i in range(steps):
             for c in range(pr.chunks):
                 fwd(c, {"stage_events": evs[i][c].address})
         torch.cuda.synchronize()
-        wall = time.perf_counter() - t_start
         stages = {}
         skip = set()
         if pr.in_norm == "none":
@@ -194,8 +222,9 @@ def main():
         for row in evs:
             for e in row:
                 e.close()
-        return {"T": T * pr.chunks, "ms": wall * 1e3 / steps, "stages": stages, "counts": counts.cpu().numpy(),
-                "x": x_host, "fwd": fwd}
+        del graph
+        return {"T": T * pr.chunks, "ms": eager_ms, "graph_ms": graph_ms, "stages": stages,
+                "counts": counts.cpu().numpy(), "x": x_host, "fwd": fwd}
 
     def flushed_ms(r, steps):
         """Median event-timed ms of one call after writing 1 GiB of scratch, so no weight, router or
@@ -228,8 +257,8 @@ def main():
     tok_s = p.chunk_T / (r["ms"] * 1e-3)
     g1_ms = r["stages"]["gemm1"]
     g1_gbs = by["gemm1"] / (g1_ms * 1e-3) / 1e9
-    log("decode T=%d: %.3f ms/step, %.0f tok/s, layer %.0f GB/s; stages %s" % (
-        p.chunk_T, r["ms"], tok_s, by["total"] / (r["ms"] * 1e-3) / 1e9,
+    log("decode T=%d: %.3f ms/step (as a HIP graph %.3f), %.0f tok/s, layer %.0f GB/s; stages %s" % (
+        p.chunk_T, r["ms"], r["graph_ms"], tok_s, by["total"] / (r["ms"] * 1e-3) / 1e9,
         {k: round(v, 4) for k, v in r["stages"].items()}))
 
     result = {
@@ -251,6 +280,7 @@ def main():
                    "touched_experts": by["touched"], "layer_bytes": by["total"],
                    "layer_GBps": round(by["total"] / (r["ms"] * 1e-3) / 1e9, 1),
                    "layer_frac_hbm": round(by["total"] / (r["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                   "graph_ms_per_step": round(r["graph_ms"], 4),
                    "stage_ms": {k: round(v, 4) for k, v in r["stages"].items()}},
         "roofline": {"kernel": "gemm_stream_kernel (grouped GEMM1 + SwiGLU)", "bound": "hbm",
                      "achieved": round(g1_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
@@ -281,7 +311,8 @@ def main():
             p2.chunk_T, r2["ms"], p2.chunk_T / (r2["ms"] * 1e-3), tf, {k: round(v, 4) for k, v in r2["stages"].items()}))
         result["secondary"] = {
             "workload": "latent MoE layer, prefill T=8192", "value": round(p2.chunk_T / (r2["ms"] * 1e-3), 1),
-            "unit": "tokens/s", "ms_per_step": round(r2["ms"], 4), "steps": args.prefill_steps,
+            "unit": "tokens/s", "ms_per_step": round(r2["ms"], 4), "graph_ms_per_step": round(r2["graph_ms"], 4),
+            "steps": args.prefill_steps,
             "layer_TFLOPs": round(tf, 1), "layer_frac_mfma": round(tf / BF16_PEAK_TFLOPS, 4),
             "stage_ms": {k: round(v, 4) for k, v in r2["stages"].items()},
             # at ~256 rows per expert GEMM1 does ~240 FLOP per byte it must move, below the chip's
@@ -302,6 +333,7 @@ def main():
         flx, byx = layer_flops(pr), layer_bytes(pr, rr["counts"])
         toks = pr.chunk_T * pr.chunks
         d = {"workload": label, "tokens_per_s": round(toks / (rr["ms"] * 1e-3), 1), "ms_per_step": round(rr["ms"], 4),
+             "graph_ms_per_step": round(rr["graph_ms"], 4),
              "TFLOPs": round(flx["total"] / (rr["ms"] * 1e-3) / 1e12, 1),
              "frac_mfma": round(flx["total"] / (rr["ms"] * 1e-3) / 1e12 / BF16_PEAK_TFLOPS, 4),
              "weight_and_io_GBps": round(byx["total"] * pr.chunks / (rr["ms"] * 1e-3) / 1e9, 1),

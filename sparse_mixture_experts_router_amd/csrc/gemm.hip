@@ -220,19 +220,20 @@ __device__ __forceinline__ void strm_issue(const StrmCtx &c, int wave, int64_t k
                                                      16, c.boff[i], (int)(kk * 2), 0, kStreamPolicy);
 }
 
-// One K group of an LDS-streamed item, slot S = g % 3.  On entry groups g
-// and g+1 are in flight, issued in that order; the step waits for group g
-// (all but the loads of group g+1), issues group g+2 into slot (S+2) % 3
-// (clamped to the last group: clamped loads are never read), reads group g
-// and runs its MFMAs.
-template <int NB, int AT, int S>
-__device__ __forceinline__ void strm_step(floatx4_t (&acc)[1][NB], const StrmCtx &c, int64_t kbeg, int g, int ng,
+// One K group g of an LDS-streamed item, slot S = g % 3.  On entry group g
+// and (when g + 1 < ng) group g+1 are in flight, issued in that order.  The
+// step waits for group g: all but the loads of group g+1 (NEXT), or for
+// everything (last group); with ISSUE it then loads group g+2 into slot
+// (S+2) % 3; it reads group g and runs its MFMAs.  Slot (S+2) % 3 last held
+// group g-1, whose reads finished in the previous step.
+template <int NB, int AT, int S, bool ISSUE, bool NEXT>
+__device__ __forceinline__ void strm_step(floatx4_t (&acc)[1][NB], const StrmCtx &c, int64_t kbeg, int g,
                                           int wave) {
     constexpr int NS = kStrmKG / 32;  // MFMA K steps per group
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm((1 + NB) * kStrmLoads));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(NEXT ? (1 + NB) * kStrmLoads : 0));
     __builtin_amdgcn_sched_barrier(0);
-    strm_issue<NB, (S + 2) % 3>(c, wave, kbeg + kStrmKG * (int64_t)min(g + 2, ng - 1));
+    if constexpr (ISSUE) strm_issue<NB, (S + 2) % 3>(c, wave, kbeg + kStrmKG * (int64_t)(g + 2));
     uint4 fa[NS], fb[NB][NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) fa[s] = *(const uint4 *)(strm_slot<S>() + c.roff[s]);
@@ -247,6 +248,40 @@ __device__ __forceinline__ void strm_step(floatx4_t (&acc)[1][NB], const StrmCtx
         for (int b = 0; b < NB; ++b) acc[0][b] = mfma16x16x32<AT>(fa[s], fb[b][s], acc[0][b]);
 }
 
+// The K loop of an LDS-streamed item over ng >= 2 groups from kbeg (K a
+// multiple of 512): every group is loaded exactly once.  Steady state in
+// triples (each step issues the group two ahead), then the last 2..4 groups
+// with the issues and waits that remain.
+template <int NB, int AT>
+__device__ __forceinline__ void strm_loop(floatx4_t (&acc)[1][NB], const StrmCtx &c, int64_t kbeg, int ng,
+                                          int wave) {
+    strm_issue<NB, 0>(c, wave, kbeg);
+    strm_issue<NB, 1>(c, wave, kbeg + kStrmKG);
+    int g = 0;
+    for (; g + 5 <= ng; g += 3) {
+        strm_step<NB, AT, 0, true, true>(acc, c, kbeg, g, wave);
+        strm_step<NB, AT, 1, true, true>(acc, c, kbeg, g + 1, wave);
+        strm_step<NB, AT, 2, true, true>(acc, c, kbeg, g + 2, wave);
+    }
+    switch (ng - g) {
+    case 4:
+        strm_step<NB, AT, 0, true, true>(acc, c, kbeg, g, wave);
+        strm_step<NB, AT, 1, true, true>(acc, c, kbeg, g + 1, wave);
+        strm_step<NB, AT, 2, false, true>(acc, c, kbeg, g + 2, wave);
+        strm_step<NB, AT, 0, false, false>(acc, c, kbeg, g + 3, wave);
+        break;
+    case 3:
+        strm_step<NB, AT, 0, true, true>(acc, c, kbeg, g, wave);
+        strm_step<NB, AT, 1, false, true>(acc, c, kbeg, g + 1, wave);
+        strm_step<NB, AT, 2, false, false>(acc, c, kbeg, g + 2, wave);
+        break;
+    default:  // 2
+        strm_step<NB, AT, 0, false, true>(acc, c, kbeg, g, wave);
+        strm_step<NB, AT, 1, false, false>(acc, c, kbeg, g + 1, wave);
+        break;
+    }
+}
+
 template <int MB, int NB, int EPI, bool MX, bool GROUPED, int AT, int OT>
 __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
     constexpr int BM = 16 * MB;
@@ -258,18 +293,23 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
     const int lg = lane >> 4;  // k group of 32 within a 128-wide K group
 
     const int64_t K = a.K;
-    const int64_t kq = K / 4;            // K range of one wave
-    const int64_t kbeg = wave * kq;
-    const int64_t kend = kbeg + kq;
+    // dense fp32 outputs may split K into ks slices: slice s of an item adds
+    // its partial sums into plane s of C ([ks][M][ldc])
+    const int ks = (EPI == EPI_F32 && !MX && !GROUPED && a.ksplit > 1) ? a.ksplit : 1;
+    const int64_t kq = K / ks / 4;       // K range of one wave
     const int64_t nblocks = (EPI == EPI_SWIGLU) ? a.N / 16 : a.N / (16 * NB);
     const int ntiles = GROUPED ? *a.ntiles : (int)((a.M + BM - 1) / BM);
-    const int64_t items = (int64_t)ntiles * nblocks;
+    const int64_t items = (int64_t)ntiles * nblocks * ks;
 
     // grouped items on bf16/fp16 weights stream their weights through LDS
     constexpr bool kDma = !MX && GROUPED && MB == 1 && NB <= 2;
     for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
-        const int t = (int)(item / nblocks);
-        const int64_t nb = item - (int64_t)t * nblocks;
+        const int ksl = (int)(item % ks);
+        const int64_t tb = item / ks;
+        const int t = (int)(tb / nblocks);
+        const int64_t nb = tb - (int64_t)t * nblocks;
+        const int64_t kbeg = (ksl * 4 + wave) * kq;
+        const int64_t kend = kbeg + kq;
         RowTile rt;
         load_tile(a, GROUPED, BM, t, rt);  // mcount > 0 for every listed tile
 
@@ -352,21 +392,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
                                        ((((kStrmKG / 32) * lg + s) ^ strm_swz(li)) << 4));
                 asm("" : "+v"(c.roff[s]));
             }
-            const int ng = (int)(kq / kStrmKG);
-            strm_issue<NB, 0>(c, wave, kbeg);
-            strm_issue<NB, 1>(c, wave, kbeg + kStrmKG * (int64_t)min(1, ng - 1));
-            int g = 0;
-            for (; g + 3 <= ng; g += 3) {
-                strm_step<NB, AT, 0>(acc, c, kbeg, g, ng, wave);
-                strm_step<NB, AT, 1>(acc, c, kbeg, g + 1, ng, wave);
-                strm_step<NB, AT, 2>(acc, c, kbeg, g + 2, ng, wave);
-            }
-            if (g < ng) {
-                strm_step<NB, AT, 0>(acc, c, kbeg, g, ng, wave);
-                if (g + 1 < ng) strm_step<NB, AT, 1>(acc, c, kbeg, g + 1, ng, wave);
-            }
-            // the clamped tail loads land before the slots are reused
-            __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+            strm_loop<NB, AT>(acc, c, kbeg, (int)(kq / kStrmKG), wave);
         } else {
             StreamFrag<MB, NB> cur, nxt;
             stream_load<MB, NB, MX, AT>(cur, bptr, bscale, aptr, kbeg);
@@ -421,7 +447,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
                         for (int c = 0; c < NB; ++c) {
                             int64_t n = (nb * NB + c) * 16 + li;
-                            if (ok) rowsq[c][q] += store_elem<EPI, OT>(a, p, n, acc[m][c][q]);
+                            if (ok) rowsq[c][q] += store_elem<EPI, OT>(a, p + ksl * a.M, n, acc[m][c][q]);
                         }
                     }
                 }
@@ -1209,8 +1235,12 @@ template <int MB, int NB, int EPI, bool MX, bool GROUPED, int AT, int OT>
 static hipError_t run_stream(const GemmArgs &a, hipStream_t s) {
     const int64_t nblocks = (EPI == EPI_SWIGLU) ? a.N / 16 : a.N / (16 * NB);
     const int64_t tiles = GROUPED ? a.max_tiles : (a.M + 16 * MB - 1) / (16 * MB);
-    const int64_t items = tiles * nblocks;
+    const int64_t items = tiles * nblocks * (EPI == EPI_F32 && !MX && !GROUPED && a.ksplit > 1 ? a.ksplit : 1);
     if (items <= 0) return hipSuccess;
+    // each wave's K range holds whole 128-wide groups (register path) and at
+    // least two 64-wide groups (LDS path)
+    const int ks = (EPI == EPI_F32 && !MX && !GROUPED && a.ksplit > 1) ? a.ksplit : 1;
+    if (a.K % (512 * ks)) return hipErrorInvalidValue;
     const int grid = (int)(items < kStreamGrid ? items : kStreamGrid);
     gemm_stream_kernel<MB, NB, EPI, MX, GROUPED, AT, OT><<<grid, 256, 0, s>>>(a);
     return hipGetLastError();

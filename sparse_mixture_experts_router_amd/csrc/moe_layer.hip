@@ -57,10 +57,14 @@ int64_t tall_tile_cap(int64_t n) { return n; }  // at most one per expert
 // in slice order.  Small batches (streaming kernel) are not sliced.
 int router_splits(const moe_desc *d) {
     if (d->act_dtype != MOE_DT_BF16 || d->router_dtype != MOE_DT_BF16) return 1;
-    if (d->T <= 128 || d->n_experts % kTileBN) return 1;
-    const int64_t items = (d->T + kTileBM - 1) / kTileBM;
+    // items of the kernel dense_path() picks: 256-row tiles (one column block
+    // of 256 experts), or 64-row x 16-expert streaming items; K slices of a
+    // multiple of 512 until about one (tiles) or two (streaming) workgroups a CU
+    const bool tiled = d->T > 128 && d->n_experts % kTileBN == 0;
+    const int64_t items = tiled ? (d->T + kTileBM - 1) / kTileBM : ((d->T + 63) / 64) * (d->n_experts / 16);
+    const int64_t target = tiled ? 256 : 512;
     int ks = 1;
-    while (items * ks * 2 <= 256 && d->d_model % (ks * 2 * 512) == 0) ks *= 2;
+    while (items * ks * 2 <= target && d->d_model % (ks * 2 * 512) == 0) ks *= 2;
     return ks;
 }
 

@@ -172,12 +172,29 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
     float sc[4], hv[4];
     const float *lr = logits + t * n;
     const int64_t plane = T * n;
+    // plane sums: the loads of four planes go out together, the additions
+    // stay in plane order
+    float ls[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) ls[r] = lane + 64 * r < n ? lr[lane + 64 * r] : 0.f;
+    for (int q = 1; q < ks; q += 4) {
+        float v[4][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                v[j][r] = (q + j < ks && lane + 64 * r < n) ? lr[(q + j) * plane + lane + 64 * r] : 0.f;
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 4; ++r)
+                if (q + j < ks) ls[r] += v[j][r];
+    }
 #pragma unroll
     for (int r = 0; r < 4; ++r) {
         int e = lane + 64 * r;
         if (e < n) {
-            float l = lr[e];
-            for (int q = 1; q < ks; ++q) l += lr[q * plane + e];
+            const float l = ls[r];
             if (lout) lout[t * n + e] = l;
             if (fn == kRouterSigmoid) {
                 const float sg = 1.0f / (1.0f + expf(-(l * out_mult)));
