@@ -200,15 +200,16 @@ __device__ __forceinline__ void *uniform_ptr(const void *p) {
     return (void *)(((uint64_t)hi << 32) | lo);
 }
 
-// Loads of the K group at element kk into slot S (this wave's area).
-template <int NB, int S>
+// Loads of the K group at element kk into slot S (this wave's area): NA
+// loads of 8 A rows each (1: rows 0..7 only), then the NB weight blocks.
+template <int NB, int NA, int S>
 __device__ __forceinline__ void strm_issue(const StrmCtx &c, int wave, int64_t kk) {
     // each access is one address step from its slot object, which keeps the
     // compiler's per-object tracking of these loads (and with it the freedom
     // to read other slots while they are in flight)
     const int w0 = wave * kStrmWaveBytes;
 #pragma unroll
-    for (int i = 0; i < kStrmLoads; ++i)
+    for (int i = 0; i < NA; ++i)
         __builtin_amdgcn_raw_ptr_buffer_load_lds(c.ra, MOE_LDS(strm_slot<S>() + (w0 + i * 1024)), 16, c.aoff[i],
                                                  (int)(kk * 2), 0, 0);
 #pragma unroll
@@ -226,14 +227,14 @@ __device__ __forceinline__ void strm_issue(const StrmCtx &c, int wave, int64_t k
 // everything (last group); with ISSUE it then loads group g+2 into slot
 // (S+2) % 3; it reads group g and runs its MFMAs.  Slot (S+2) % 3 last held
 // group g-1, whose reads finished in the previous step.
-template <int NB, int AT, int S, bool ISSUE, bool NEXT>
+template <int NB, int NA, int AT, int S, bool ISSUE, bool NEXT>
 __device__ __forceinline__ void strm_step(floatx4_t (&acc)[1][NB], const StrmCtx &c, int64_t kbeg, int g,
                                           int wave) {
     constexpr int NS = kStrmKG / 32;  // MFMA K steps per group
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(NEXT ? (1 + NB) * kStrmLoads : 0));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(NEXT ? NA + NB * kStrmLoads : 0));
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (ISSUE) strm_issue<NB, (S + 2) % 3>(c, wave, kbeg + kStrmKG * (int64_t)(g + 2));
+    if constexpr (ISSUE) strm_issue<NB, NA, (S + 2) % 3>(c, wave, kbeg + kStrmKG * (int64_t)(g + 2));
     uint4 fa[NS], fb[NB][NS];
 #pragma unroll
     for (int s = 0; s < NS; ++s) fa[s] = *(const uint4 *)(strm_slot<S>() + c.roff[s]);
@@ -252,32 +253,32 @@ __device__ __forceinline__ void strm_step(floatx4_t (&acc)[1][NB], const StrmCtx
 // multiple of 512): every group is loaded exactly once.  Steady state in
 // triples (each step issues the group two ahead), then the last 2..4 groups
 // with the issues and waits that remain.
-template <int NB, int AT>
+template <int NB, int NA, int AT>
 __device__ __forceinline__ void strm_loop(floatx4_t (&acc)[1][NB], const StrmCtx &c, int64_t kbeg, int ng,
                                           int wave) {
-    strm_issue<NB, 0>(c, wave, kbeg);
-    strm_issue<NB, 1>(c, wave, kbeg + kStrmKG);
+    strm_issue<NB, NA, 0>(c, wave, kbeg);
+    strm_issue<NB, NA, 1>(c, wave, kbeg + kStrmKG);
     int g = 0;
     for (; g + 5 <= ng; g += 3) {
-        strm_step<NB, AT, 0, true, true>(acc, c, kbeg, g, wave);
-        strm_step<NB, AT, 1, true, true>(acc, c, kbeg, g + 1, wave);
-        strm_step<NB, AT, 2, true, true>(acc, c, kbeg, g + 2, wave);
+        strm_step<NB, NA, AT, 0, true, true>(acc, c, kbeg, g, wave);
+        strm_step<NB, NA, AT, 1, true, true>(acc, c, kbeg, g + 1, wave);
+        strm_step<NB, NA, AT, 2, true, true>(acc, c, kbeg, g + 2, wave);
     }
     switch (ng - g) {
     case 4:
-        strm_step<NB, AT, 0, true, true>(acc, c, kbeg, g, wave);
-        strm_step<NB, AT, 1, true, true>(acc, c, kbeg, g + 1, wave);
-        strm_step<NB, AT, 2, false, true>(acc, c, kbeg, g + 2, wave);
-        strm_step<NB, AT, 0, false, false>(acc, c, kbeg, g + 3, wave);
+        strm_step<NB, NA, AT, 0, true, true>(acc, c, kbeg, g, wave);
+        strm_step<NB, NA, AT, 1, true, true>(acc, c, kbeg, g + 1, wave);
+        strm_step<NB, NA, AT, 2, false, true>(acc, c, kbeg, g + 2, wave);
+        strm_step<NB, NA, AT, 0, false, false>(acc, c, kbeg, g + 3, wave);
         break;
     case 3:
-        strm_step<NB, AT, 0, true, true>(acc, c, kbeg, g, wave);
-        strm_step<NB, AT, 1, false, true>(acc, c, kbeg, g + 1, wave);
-        strm_step<NB, AT, 2, false, false>(acc, c, kbeg, g + 2, wave);
+        strm_step<NB, NA, AT, 0, true, true>(acc, c, kbeg, g, wave);
+        strm_step<NB, NA, AT, 1, false, true>(acc, c, kbeg, g + 1, wave);
+        strm_step<NB, NA, AT, 2, false, false>(acc, c, kbeg, g + 2, wave);
         break;
     default:  // 2
-        strm_step<NB, AT, 0, false, true>(acc, c, kbeg, g, wave);
-        strm_step<NB, AT, 1, false, false>(acc, c, kbeg, g + 1, wave);
+        strm_step<NB, NA, AT, 0, false, true>(acc, c, kbeg, g, wave);
+        strm_step<NB, NA, AT, 1, false, false>(acc, c, kbeg, g + 1, wave);
         break;
     }
 }
@@ -392,7 +393,10 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
                                        ((((kStrmKG / 32) * lg + s) ^ strm_swz(li)) << 4));
                 asm("" : "+v"(c.roff[s]));
             }
-            strm_loop<NB, AT>(acc, c, kbeg, (int)(kq / kStrmKG), wave);
+            // tiles of up to 8 rows (most of them at decode) load one A row block:
+            // fragment rows 8..15 then hold stale data, and their results are never stored
+            if (rt.mcount <= 8) strm_loop<NB, 1, AT>(acc, c, kbeg, (int)(kq / kStrmKG), wave);
+            else strm_loop<NB, 2, AT>(acc, c, kbeg, (int)(kq / kStrmKG), wave);
         } else {
             StreamFrag<MB, NB> cur, nxt;
             stream_load<MB, NB, MX, AT>(cur, bptr, bscale, aptr, kbeg);
