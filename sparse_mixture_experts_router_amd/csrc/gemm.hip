@@ -148,45 +148,46 @@ __device__ __forceinline__ void stream_load(StreamFrag<MB, NB> &f, const uint8_t
     }
 }
 
-// Grouped items on bf16/fp16 weights stream their operands through LDS: a
-// buffer load of 64 lanes x 16 bytes straight into LDS fills 8 rows x 128
-// bytes of one 64-wide K group (whole cache lines; weights with the
-// non-temporal policy: a probe of this form streams at 7.0 TB/s against 6.2
-// for register loads in the lane pattern above).  Each wave keeps its K
-// groups in three slots (each its own LDS object), a slot holding the
-// group's A rows (16) and its 16-row B blocks.  Three slots of 4 waves x 3
-// blocks x 2 KB leave room for two workgroups per CU, so one covers the
-// other's start and end of an item.  In a block, row r keeps logical chunk
-// q (8 values) at chunk q ^ f(r), f(r) = (r >> 1) ^ 4 (r & 1): a fragment
-// read (rows 0..15 at one logical chunk) then hits distinct 16-byte bank
-// groups in every 8-lane and 16-lane phase.
+// Items on bf16/fp16 weights (grouped 16-row tiles, dense 64-row tiles)
+// stream their operands through LDS: a buffer load of 64 lanes x 16 bytes
+// straight into LDS fills 8 rows x 128 bytes of one 64-wide K group (whole
+// cache lines; weights with the non-temporal policy: a probe of this form
+// streams at 7.0 TB/s against 6.2 for register loads in the lane pattern
+// above, and reads L2-resident rows at 80-130 GB/s per CU against 36 for
+// register loads).  Each wave keeps its K groups in three slots (each its
+// own LDS object), a slot holding the group's MB 16-row A blocks and its NB
+// 16-row B blocks.  Grouped slots (4 waves x 3 blocks x 2 KB) leave room
+// for two workgroups per CU, so one covers the other's start and end of an
+// item.  In a block, row r keeps logical chunk q (8 values) at chunk
+// q ^ f(r), f(r) = (r >> 1) ^ 4 (r & 1): a fragment read (rows 0..15 at one
+// logical chunk) then hits distinct 16-byte bank groups in every 8-lane and
+// 16-lane phase.
 constexpr int kStrmKG = 64;                            // K per group
 constexpr int kStrmRow = kStrmKG * 2;                  // bytes per block row (128)
 constexpr int kStrmBlock = 16 * kStrmRow;              // bytes per 16-row block (2 KB)
 constexpr int kStrmLoads = kStrmBlock / 1024;          // loads per block (2)
-constexpr int kStrmWaveBytes = 3 * kStrmBlock;         // A block + 2 B blocks
-constexpr int kStrmSlotBytes = 4 * kStrmWaveBytes;     // 4 waves
-__shared__ __attribute__((aligned(16))) uint8_t strm_s0[kStrmSlotBytes];
-__shared__ __attribute__((aligned(16))) uint8_t strm_s1[kStrmSlotBytes];
-__shared__ __attribute__((aligned(16))) uint8_t strm_s2[kStrmSlotBytes];
+
+template <int MB, int NB>
+constexpr int strm_wave_bytes() { return (MB + NB) * kStrmBlock; }
 
 __device__ __forceinline__ int strm_swz(int r) { return (r >> 1) ^ ((r & 1) << 2); }
 
-template <int S>
+// Slot S of a kernel whose waves hold MB A and NB B blocks per group.
+template <int MB, int NB, int S>
 __device__ __forceinline__ uint8_t *strm_slot() {
-    if constexpr (S == 0) return strm_s0;
-    else if constexpr (S == 1) return strm_s1;
-    else return strm_s2;
+    __shared__ __attribute__((aligned(16))) uint8_t slot[4 * strm_wave_bytes<MB, NB>()];
+    return slot;
 }
 
 // Per-item state of an LDS-streamed item: buffer descriptors of A (rows
 // gathered: per-row lane offsets from the buffer start) and of the first
-// row of each B block (rows consecutive); the lane's byte offsets of load i
-// of a block (rows 8i + lane / 8) in aoff[i] and boff[i]; the byte offsets
-// (within a slot) of its fragment reads in roff[s].
+// row of each B block (rows consecutive); the lane's byte offsets of A load
+// i (rows 8i + lane / 8) in aoff[i] and of B load i of a block in boff[i];
+// the byte offsets (within a slot) of its fragment reads in roff[s].
+constexpr int kStrmMaxMB = 4;  // A blocks per wave: 1 (grouped) or 4 (dense)
 struct StrmCtx {
     __amdgpu_buffer_rsrc_t ra, rb0, rb1;
-    uint32_t aoff[kStrmLoads], boff[kStrmLoads], roff[kStrmKG / 32];
+    uint32_t aoff[2 * kStrmMaxMB], boff[kStrmLoads], roff[kStrmKG / 32];
 };
 
 // A pointer the whole wave holds, moved to scalar registers (descriptors
@@ -201,24 +202,26 @@ __device__ __forceinline__ void *uniform_ptr(const void *p) {
 }
 
 // Loads of the K group at element kk into slot S (this wave's area): NA
-// loads of 8 A rows each (1: rows 0..7 only), then the NB weight blocks.
-template <int NB, int NA, int S>
+// loads of 8 A rows each (fewer than 2 MB: the tile's rows fit in them),
+// then the NB weight blocks.
+template <int MB, int NB, int NA, int S>
 __device__ __forceinline__ void strm_issue(const StrmCtx &c, int wave, int64_t kk) {
     // each access is one address step from its slot object, which keeps the
     // compiler's per-object tracking of these loads (and with it the freedom
     // to read other slots while they are in flight)
-    const int w0 = wave * kStrmWaveBytes;
+    uint8_t *const slot = strm_slot<MB, NB, S>();
+    const int w0 = wave * strm_wave_bytes<MB, NB>();
 #pragma unroll
     for (int i = 0; i < NA; ++i)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.ra, MOE_LDS(strm_slot<S>() + (w0 + i * 1024)), 16, c.aoff[i],
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.ra, MOE_LDS(slot + (w0 + i * 1024)), 16, c.aoff[i],
                                                  (int)(kk * 2), 0, 0);
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int i = 0; i < kStrmLoads; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(b == 0 ? c.rb0 : c.rb1,
-                                                     MOE_LDS(strm_slot<S>() + (w0 + (1 + b) * kStrmBlock + i * 1024)),
-                                                     16, c.boff[i], (int)(kk * 2), 0, kStreamPolicy);
+                                                     MOE_LDS(slot + (w0 + (MB + b) * kStrmBlock + i * 1024)), 16,
+                                                     c.boff[i], (int)(kk * 2), 0, kStreamPolicy);
 }
 
 // One K group g of an LDS-streamed item, slot S = g % 3.  On entry group g
@@ -227,58 +230,63 @@ __device__ __forceinline__ void strm_issue(const StrmCtx &c, int wave, int64_t k
 // everything (last group); with ISSUE it then loads group g+2 into slot
 // (S+2) % 3; it reads group g and runs its MFMAs.  Slot (S+2) % 3 last held
 // group g-1, whose reads finished in the previous step.
-template <int NB, int NA, int AT, int S, bool ISSUE, bool NEXT>
-__device__ __forceinline__ void strm_step(floatx4_t (&acc)[1][NB], const StrmCtx &c, int64_t kbeg, int g,
+template <int MB, int NB, int NA, int AT, int S, bool ISSUE, bool NEXT>
+__device__ __forceinline__ void strm_step(floatx4_t (&acc)[MB][NB], const StrmCtx &c, int64_t kbeg, int g,
                                           int wave) {
     constexpr int NS = kStrmKG / 32;  // MFMA K steps per group
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(NEXT ? NA + NB * kStrmLoads : 0));
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (ISSUE) strm_issue<NB, NA, (S + 2) % 3>(c, wave, kbeg + kStrmKG * (int64_t)(g + 2));
-    uint4 fa[NS], fb[NB][NS];
+    if constexpr (ISSUE) strm_issue<MB, NB, NA, (S + 2) % 3>(c, wave, kbeg + kStrmKG * (int64_t)(g + 2));
+    const uint8_t *const slot = strm_slot<MB, NB, S>();
+    uint4 fa[MB][NS], fb[NB][NS];
 #pragma unroll
-    for (int s = 0; s < NS; ++s) fa[s] = *(const uint4 *)(strm_slot<S>() + c.roff[s]);
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int s = 0; s < NS; ++s) fa[m][s] = *(const uint4 *)(slot + c.roff[s] + m * kStrmBlock);
 #pragma unroll
     for (int b = 0; b < NB; ++b)
 #pragma unroll
         for (int s = 0; s < NS; ++s)
-            fb[b][s] = weight_bf16_as<AT>(*(const uint4 *)(strm_slot<S>() + c.roff[s] + (1 + b) * kStrmBlock));
+            fb[b][s] = weight_bf16_as<AT>(*(const uint4 *)(slot + c.roff[s] + (MB + b) * kStrmBlock));
 #pragma unroll
     for (int s = 0; s < NS; ++s)
 #pragma unroll
-        for (int b = 0; b < NB; ++b) acc[0][b] = mfma16x16x32<AT>(fa[s], fb[b][s], acc[0][b]);
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int b = 0; b < NB; ++b) acc[m][b] = mfma16x16x32<AT>(fa[m][s], fb[b][s], acc[m][b]);
 }
 
 // The K loop of an LDS-streamed item over ng >= 2 groups from kbeg (K a
 // multiple of 512): every group is loaded exactly once.  Steady state in
 // triples (each step issues the group two ahead), then the last 2..4 groups
 // with the issues and waits that remain.
-template <int NB, int NA, int AT>
-__device__ __forceinline__ void strm_loop(floatx4_t (&acc)[1][NB], const StrmCtx &c, int64_t kbeg, int ng,
+template <int MB, int NB, int NA, int AT>
+__device__ __forceinline__ void strm_loop(floatx4_t (&acc)[MB][NB], const StrmCtx &c, int64_t kbeg, int ng,
                                           int wave) {
-    strm_issue<NB, NA, 0>(c, wave, kbeg);
-    strm_issue<NB, NA, 1>(c, wave, kbeg + kStrmKG);
+    strm_issue<MB, NB, NA, 0>(c, wave, kbeg);
+    strm_issue<MB, NB, NA, 1>(c, wave, kbeg + kStrmKG);
     int g = 0;
     for (; g + 5 <= ng; g += 3) {
-        strm_step<NB, NA, AT, 0, true, true>(acc, c, kbeg, g, wave);
-        strm_step<NB, NA, AT, 1, true, true>(acc, c, kbeg, g + 1, wave);
-        strm_step<NB, NA, AT, 2, true, true>(acc, c, kbeg, g + 2, wave);
+        strm_step<MB, NB, NA, AT, 0, true, true>(acc, c, kbeg, g, wave);
+        strm_step<MB, NB, NA, AT, 1, true, true>(acc, c, kbeg, g + 1, wave);
+        strm_step<MB, NB, NA, AT, 2, true, true>(acc, c, kbeg, g + 2, wave);
     }
     switch (ng - g) {
     case 4:
-        strm_step<NB, NA, AT, 0, true, true>(acc, c, kbeg, g, wave);
-        strm_step<NB, NA, AT, 1, true, true>(acc, c, kbeg, g + 1, wave);
-        strm_step<NB, NA, AT, 2, false, true>(acc, c, kbeg, g + 2, wave);
-        strm_step<NB, NA, AT, 0, false, false>(acc, c, kbeg, g + 3, wave);
+        strm_step<MB, NB, NA, AT, 0, true, true>(acc, c, kbeg, g, wave);
+        strm_step<MB, NB, NA, AT, 1, true, true>(acc, c, kbeg, g + 1, wave);
+        strm_step<MB, NB, NA, AT, 2, false, true>(acc, c, kbeg, g + 2, wave);
+        strm_step<MB, NB, NA, AT, 0, false, false>(acc, c, kbeg, g + 3, wave);
         break;
     case 3:
-        strm_step<NB, NA, AT, 0, true, true>(acc, c, kbeg, g, wave);
-        strm_step<NB, NA, AT, 1, false, true>(acc, c, kbeg, g + 1, wave);
-        strm_step<NB, NA, AT, 2, false, false>(acc, c, kbeg, g + 2, wave);
+        strm_step<MB, NB, NA, AT, 0, true, true>(acc, c, kbeg, g, wave);
+        strm_step<MB, NB, NA, AT, 1, false, true>(acc, c, kbeg, g + 1, wave);
+        strm_step<MB, NB, NA, AT, 2, false, false>(acc, c, kbeg, g + 2, wave);
         break;
     default:  // 2
-        strm_step<NB, NA, AT, 0, false, true>(acc, c, kbeg, g, wave);
-        strm_step<NB, NA, AT, 1, false, false>(acc, c, kbeg, g + 1, wave);
+        strm_step<MB, NB, NA, AT, 0, false, true>(acc, c, kbeg, g, wave);
+        strm_step<MB, NB, NA, AT, 1, false, false>(acc, c, kbeg, g + 1, wave);
         break;
     }
 }
@@ -303,7 +311,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
     const int64_t items = (int64_t)ntiles * nblocks * ks;
 
     // grouped items on bf16/fp16 weights stream their weights through LDS
-    constexpr bool kDma = !MX && GROUPED && MB == 1 && NB <= 2;
+    constexpr bool kDma = !MX && NB <= 2 && (GROUPED ? MB == 1 : MB == 4);
     for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
         const int ksl = (int)(item % ks);
         const int64_t tb = item / ks;
@@ -356,6 +364,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
             for (int c = 0; c < NB; ++c) acc[m][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
         if constexpr (kDma) {
+            static_assert(MB <= kStrmMaxMB, "A blocks per wave");
             StrmCtx c;
             // gathered A rows are addressed from the buffer start (the layer keeps that
             // buffer below 2 GiB), contiguous ones from the tile's first row
@@ -373,30 +382,35 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
                 if (b == 0) c.rb0 = rsrc;
                 else c.rb1 = rsrc;
             }
-            // load i of a block fills rows r = 8i + lane / 8; physical chunk lane % 8
-            // holds logical chunk (lane % 8) ^ f(r)
+            // load i fills rows r = 8i + lane / 8 of the A blocks (of a B block for
+            // i < 2); physical chunk lane % 8 holds logical chunk (lane % 8) ^ f(r % 16)
 #pragma unroll
-            for (int i = 0; i < kStrmLoads; ++i) {
+            for (int i = 0; i < 2 * MB; ++i) {
                 const int r = 8 * i + (lane >> 3);
-                const int chunk = ((lane & 7) ^ strm_swz(r)) << 4;
+                const int chunk = ((lane & 7) ^ strm_swz(r & 15)) << 4;
                 const int rr = min(r, rt.mcount - 1);  // rows past the valid ones read the last
                 const int64_t arow = a.a_gather ? (int64_t)a.a_gather[rt.p0 + rr] : rr;
                 c.aoff[i] = (uint32_t)(arow * a.lda * 2 + chunk);
-                c.boff[i] = (uint32_t)(r * K * 2 + chunk);
+                if (i < kStrmLoads) c.boff[i] = (uint32_t)(r * K * 2 + chunk);
             }
             // fragment reads: row li of the wave's blocks, logical chunk 2 lg + s.  Each
             // offset is an opaque value, so every read is one short address step from
             // its slot object (the compiler then knows which slot a read touches)
 #pragma unroll
             for (int s = 0; s < kStrmKG / 32; ++s) {
-                c.roff[s] = (uint32_t)(wave * kStrmWaveBytes + li * kStrmRow +
+                c.roff[s] = (uint32_t)(wave * strm_wave_bytes<MB, NB>() + li * kStrmRow +
                                        ((((kStrmKG / 32) * lg + s) ^ strm_swz(li)) << 4));
                 asm("" : "+v"(c.roff[s]));
             }
-            // tiles of up to 8 rows (most of them at decode) load one A row block:
-            // fragment rows 8..15 then hold stale data, and their results are never stored
-            if (rt.mcount <= 8) strm_loop<NB, 1, AT>(acc, c, kbeg, (int)(kq / kStrmKG), wave);
-            else strm_loop<NB, 2, AT>(acc, c, kbeg, (int)(kq / kStrmKG), wave);
+            const int ng = (int)(kq / kStrmKG);
+            if constexpr (MB == 1) {
+                // tiles of up to 8 rows (most of them at decode) load one A row block:
+                // fragment rows 8..15 then hold stale data, and their results are never stored
+                if (rt.mcount <= 8) strm_loop<MB, NB, 1, AT>(acc, c, kbeg, ng, wave);
+                else strm_loop<MB, NB, 2, AT>(acc, c, kbeg, ng, wave);
+            } else {
+                strm_loop<MB, NB, 2 * MB, AT>(acc, c, kbeg, ng, wave);
+            }
         } else {
             StreamFrag<MB, NB> cur, nxt;
             stream_load<MB, NB, MX, AT>(cur, bptr, bscale, aptr, kbeg);

@@ -808,6 +808,7 @@ hipError_t launch_permute(const int32_t *idx, int64_t T, int k, int n, int32_t *
 
 hipError_t launch_combine(const uint16_t *S, const float *ssq, const int32_t *pos, const float *w, int64_t T,
                           int64_t L, int nparts, float eps, int k, int ot, uint16_t *m, hipStream_t s) {
+    if (k < 1 || k > 16 || L % 8) return hipErrorInvalidValue;  // coef[] and prow[] hold 16 slots
     if (ot == ACT_F16) combine_kernel<ACT_F16><<<(unsigned)T, 256, 0, s>>>(S, ssq, pos, w, L, nparts, eps, k, m);
     else combine_kernel<ACT_BF16><<<(unsigned)T, 256, 0, s>>>(S, ssq, pos, w, L, nparts, eps, k, m);
     return hipGetLastError();
