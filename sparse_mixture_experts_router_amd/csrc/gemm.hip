@@ -1002,13 +1002,16 @@ __device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, i
     }
 
     BigCtx c;
-    c.A = (const uint8_t *)a.A + k0 * 2;
+    // The loads take 32-bit lane offsets from the A base: gathered rows count
+    // from the buffer start (the layer keeps the gathered latent rows below
+    // 2 GiB), contiguous rows from the tile's first row, so a batch whose rows
+    // span more than 2 GiB (GEMM2's T k rows) still addresses every row.
+    c.A = (const uint8_t *)uniform_ptr(a.a_gather ? a.A : a.A + rt.p0 * a.lda) + k0 * 2;
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
         const int lrow = wave * (NA * 8) + i * 8 + drow;  // LDS row; the source row is clamped to a valid one
         const int row = min(lrow, rt.mcount - 1);
-        const int64_t p = rt.p0 + row;
-        const int64_t arow = a.a_gather ? (int64_t)a.a_gather[p] : p;
+        const int64_t arow = a.a_gather ? (int64_t)a.a_gather[rt.p0 + row] : row;
         c.aoff[i] = (uint32_t)((arow * a.lda + dchunk(lrow) * 8) * 2);
     }
 #pragma unroll

@@ -76,6 +76,23 @@ def test_small_skewed_mixed_tiles():
     assert counts.max() > 32 and (counts <= 32).any()
 
 
+def test_batch_rows_past_2gib():
+    # T * k * d_ff * 2 bytes of expert activations exceed 2 GiB: the tile kernels address GEMM2's rows from
+    # each tile's first row (32-bit lane offsets), so slots whose rows sit past 2 GiB of that buffer are
+    # computed like the first ones; checked on tokens with such slots, and a few others
+    p = small_case("rows_past_2gib", T=131072, d=512, L=512, F=2048, n=16, k=8)
+    assert p.T * p.k * p.F * 2 > 2 ** 31
+    layer = DeviceLayer(p)
+    x = synthetic.inputs(p)
+    gpu = run(layer, x, stages=False)
+    far = np.flatnonzero((gpu["pos"].astype(np.int64) * p.F * 2 >= 2 ** 31).any(axis=1))
+    assert far.size > 1000
+    rng = np.random.default_rng(7)
+    tok = np.unique(np.concatenate([rng.choice(far, 12, replace=False), rng.choice(p.T, 4, replace=False),
+                                    [0, p.T - 1]]))
+    compare(p, layer.host, x, gpu, tokens=tok, route_tokens=synthetic.sample_tokens(p.T, 2048, seed=8))
+
+
 def test_single_token_and_top1():
     run_and_compare(small_case("t1", T=1))
     run_and_compare(small_case("top1", T=50, k=1))
