@@ -234,8 +234,13 @@ template <int MB, int NB, int NA, int AT, int S, bool ISSUE, bool NEXT>
 __device__ __forceinline__ void strm_step(floatx4_t (&acc)[MB][NB], const StrmCtx &c, int64_t kbeg, int g,
                                           int wave) {
     constexpr int NS = kStrmKG / 32;  // MFMA K steps per group
+    // Loads of group g+1 left in flight: grouped items count one A load for
+    // either A-block count, since the previous item may have issued this
+    // item's first groups under the other count as far as the compiler can
+    // tell (waiting for one more load of group g+1 costs nothing measurable).
+    constexpr int kLeft = (MB == 1 ? 1 : NA) + NB * kStrmLoads;
     __builtin_amdgcn_sched_barrier(0);
-    __builtin_amdgcn_s_waitcnt(waitcnt_vm(NEXT ? NA + NB * kStrmLoads : 0));
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(NEXT ? kLeft : 0));
     __builtin_amdgcn_sched_barrier(0);
     if constexpr (ISSUE) strm_issue<MB, NB, NA, (S + 2) % 3>(c, wave, kbeg + kStrmKG * (int64_t)(g + 2));
     const uint8_t *const slot = strm_slot<MB, NB, S>();
@@ -258,14 +263,19 @@ __device__ __forceinline__ void strm_step(floatx4_t (&acc)[MB][NB], const StrmCt
 }
 
 // The K loop of an LDS-streamed item over ng >= 2 groups from kbeg (K a
-// multiple of 512): every group is loaded exactly once.  Steady state in
-// triples (each step issues the group two ahead), then the last 2..4 groups
-// with the issues and waits that remain.
-template <int MB, int NB, int NA, int AT>
-__device__ __forceinline__ void strm_loop(floatx4_t (&acc)[MB][NB], const StrmCtx &c, int64_t kbeg, int ng,
-                                          int wave) {
+// multiple of 512): every group is loaded exactly once.  strm_first issues
+// groups 0 and 1; strm_steps then runs the steady state in triples (each
+// step issues the group two ahead) and the last 2..4 groups with the issues
+// and waits that remain.
+template <int MB, int NB, int NA>
+__device__ __forceinline__ void strm_first(const StrmCtx &c, int wave, int64_t kbeg) {
     strm_issue<MB, NB, NA, 0>(c, wave, kbeg);
     strm_issue<MB, NB, NA, 1>(c, wave, kbeg + kStrmKG);
+}
+
+template <int MB, int NB, int NA, int AT>
+__device__ __forceinline__ void strm_steps(floatx4_t (&acc)[MB][NB], const StrmCtx &c, int64_t kbeg, int ng,
+                                           int wave) {
     int g = 0;
     for (; g + 5 <= ng; g += 3) {
         strm_step<MB, NB, NA, AT, 0, true, true>(acc, c, kbeg, g, wave);
@@ -312,121 +322,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 
     // grouped items on bf16/fp16 weights stream their weights through LDS
     constexpr bool kDma = !MX && NB <= 2 && (GROUPED ? MB == 1 : MB == 4);
-    for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
-        const int ksl = (int)(item % ks);
-        const int64_t tb = item / ks;
-        const int t = (int)(tb / nblocks);
-        const int64_t nb = tb - (int64_t)t * nblocks;
-        const int64_t kbeg = (ksl * 4 + wave) * kq;
-        const int64_t kend = kbeg + kq;
-        RowTile rt;
-        load_tile(a, GROUPED, BM, t, rt);  // mcount > 0 for every listed tile
-
-        // B row pointers (lane's row li of each 16-row block) and A row pointers.
-        const uint8_t *bptr[NB];
-        const uint8_t *bscale[NB];
-        int64_t brow0 = GROUPED ? (int64_t)rt.e * a.b_group_rows : 0;
-#pragma unroll
-        for (int c = 0; c < NB; ++c) {
-            int64_t r;
-            if constexpr (EPI == EPI_SWIGLU)
-                r = brow0 + (c == 0 ? 0 : a.N) + nb * 16 + li;
-            else
-                r = brow0 + (nb * NB + c) * 16 + li;
-            if constexpr (MX) {
-                // lane group lg reads its 32-element block of each 128-wide group
-                bptr[c] = (const uint8_t *)a.B + r * (K / 2) + (lg * 32) / 2;
-                bscale[c] = (const uint8_t *)a.B + a.b_rows_total * (K / 2) + r * (K / 32) + lg;
-            } else {
-                bptr[c] = (const uint8_t *)a.B + (r * K + lg * 32) * 2;
-                bscale[c] = nullptr;
-            }
-        }
-        const uint16_t *aptr[MB];
-#pragma unroll
-        for (int m = 0; m < MB; ++m) {
-            // DMA items: rows past the tile's valid rows read its last valid row (their
-            // results are never stored), so every load goes out and the wait counts hold
-            int row = kDma ? min(m * 16 + li, rt.mcount - 1) : m * 16 + li;
-            if (row < rt.mcount) {
-                int64_t p = rt.p0 + row;
-                int64_t arow = a.a_gather ? (int64_t)a.a_gather[p] : p;
-                aptr[m] = a.A + arow * a.lda + lg * 32;
-            } else {
-                aptr[m] = nullptr;
-            }
-        }
-
-        floatx4_t acc[MB][NB];
-#pragma unroll
-        for (int m = 0; m < MB; ++m)
-#pragma unroll
-            for (int c = 0; c < NB; ++c) acc[m][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
-
-        if constexpr (kDma) {
-            static_assert(MB <= kStrmMaxMB, "A blocks per wave");
-            StrmCtx c;
-            // gathered A rows are addressed from the buffer start (the layer keeps that
-            // buffer below 2 GiB), contiguous ones from the tile's first row
-            const uint16_t *abase = a.a_gather ? a.A : a.A + rt.p0 * a.lda;
-            c.ra = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(abase), 0, 0x7fffffff, 0x00020000);
-#pragma unroll
-            for (int b = 0; b < NB; ++b) {
-                int64_t r0;
-                if constexpr (EPI == EPI_SWIGLU)
-                    r0 = brow0 + (b == 0 ? 0 : a.N) + nb * 16;
-                else
-                    r0 = brow0 + (nb * NB + b) * 16;
-                const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr((const uint8_t *)a.B + r0 * K * 2),
-                                                                    0, 0x7fffffff, 0x00020000);
-                if (b == 0) c.rb0 = rsrc;
-                else c.rb1 = rsrc;
-            }
-            // load i fills rows r = 8i + lane / 8 of the A blocks (of a B block for
-            // i < 2); physical chunk lane % 8 holds logical chunk (lane % 8) ^ f(r % 16)
-#pragma unroll
-            for (int i = 0; i < 2 * MB; ++i) {
-                const int r = 8 * i + (lane >> 3);
-                const int chunk = ((lane & 7) ^ strm_swz(r & 15)) << 4;
-                const int rr = min(r, rt.mcount - 1);  // rows past the valid ones read the last
-                const int64_t arow = a.a_gather ? (int64_t)a.a_gather[rt.p0 + rr] : rr;
-                c.aoff[i] = (uint32_t)(arow * a.lda * 2 + chunk);
-                if (i < kStrmLoads) c.boff[i] = (uint32_t)(r * K * 2 + chunk);
-            }
-            // fragment reads: row li of the wave's blocks, logical chunk 2 lg + s.  Each
-            // offset is an opaque value, so every read is one short address step from
-            // its slot object (the compiler then knows which slot a read touches)
-#pragma unroll
-            for (int s = 0; s < kStrmKG / 32; ++s) {
-                c.roff[s] = (uint32_t)(wave * strm_wave_bytes<MB, NB>() + li * kStrmRow +
-                                       ((((kStrmKG / 32) * lg + s) ^ strm_swz(li)) << 4));
-                asm("" : "+v"(c.roff[s]));
-            }
-            const int ng = (int)(kq / kStrmKG);
-            if constexpr (MB == 1) {
-                // tiles of up to 8 rows (most of them at decode) load one A row block:
-                // fragment rows 8..15 then hold stale data, and their results are never stored
-                if (rt.mcount <= 8) strm_loop<MB, NB, 1, AT>(acc, c, kbeg, ng, wave);
-                else strm_loop<MB, NB, 2, AT>(acc, c, kbeg, ng, wave);
-            } else {
-                strm_loop<MB, NB, 2 * MB, AT>(acc, c, kbeg, ng, wave);
-            }
-        } else {
-            StreamFrag<MB, NB> cur, nxt;
-            stream_load<MB, NB, MX, AT>(cur, bptr, bscale, aptr, kbeg);
-            for (int64_t kk = kbeg; kk < kend; kk += 128) {
-                if (kk + 128 < kend) stream_load<MB, NB, MX, AT>(nxt, bptr, bscale, aptr, kk + 128);
-#pragma unroll
-                for (int s = 0; s < 4; ++s)
-#pragma unroll
-                    for (int m = 0; m < MB; ++m)
-#pragma unroll
-                        for (int c = 0; c < NB; ++c)
-                            acc[m][c] = mfma16x16x32<AT>(cur.a[m][s], cur.b[c][s], acc[m][c]);
-                cur = nxt;
-            }
-        }
-
+    // Cross-wave reduction and epilogue of one item (acc: this wave's partial sums).
+    auto finish = [&](const RowTile &rt, int64_t nb, int ksl, floatx4_t (&acc)[MB][NB]) {
         // Cross-wave reduction, fixed order: wave0 + wave1 + wave2 + wave3.
         if (wave > 0) {
 #pragma unroll
@@ -482,6 +379,176 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
             }
         }
         __syncthreads();  // red[] is reused by the next item
+    };
+
+    if constexpr (kDma) {
+        // LDS-streamed items run software-pipelined over the workgroup's items:
+        // the first two K groups of the next item go out before this item's
+        // reduction and epilogue, so they are in flight while those run.
+        static_assert(MB <= kStrmMaxMB, "A blocks per wave");
+        int64_t item = blockIdx.x;
+        if (item >= items) return;
+        // Lane-only offsets.  Load i fills rows r = 8i + lane / 8 (of the A blocks;
+        // of a B block for i < 2); physical chunk lane % 8 holds logical chunk
+        // (lane % 8) ^ f(r % 16).  Fragment reads take row li of the wave's blocks
+        // at logical chunk 2 lg + s; each read offset is an opaque value, so every
+        // read is one short address step from its slot object (the compiler then
+        // knows which slot a read touches).
+        StrmCtx c;
+#pragma unroll
+        for (int i = 0; i < kStrmLoads; ++i) {
+            const int r = 8 * i + (lane >> 3);
+            c.boff[i] = (uint32_t)(r * K * 2 + (((lane & 7) ^ strm_swz(r & 15)) << 4));
+        }
+#pragma unroll
+        for (int s = 0; s < kStrmKG / 32; ++s) {
+            c.roff[s] = (uint32_t)(wave * strm_wave_bytes<MB, NB>() + li * kStrmRow +
+                                   ((((kStrmKG / 32) * lg + s) ^ strm_swz(li)) << 4));
+            asm("" : "+v"(c.roff[s]));
+        }
+        struct Item {
+            RowTile rt;
+            int64_t nb, kbeg;
+            int ksl;
+        };
+        // tile entry, descriptors and A offsets of item it
+        auto setup = [&](int64_t it, Item &I) {
+            I.ksl = (int)(it % ks);
+            const int64_t tb = it / ks;
+            const int t = (int)(tb / nblocks);
+            I.nb = tb - (int64_t)t * nblocks;
+            I.kbeg = (I.ksl * 4 + wave) * kq;
+            load_tile(a, GROUPED, BM, t, I.rt);  // mcount > 0 for every listed tile
+            // gathered A rows are addressed from the buffer start (the layer keeps that
+            // buffer below 2 GiB), contiguous ones from the tile's first row
+            const uint16_t *abase = a.a_gather ? a.A : a.A + I.rt.p0 * a.lda;
+            c.ra = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr(abase), 0, 0x7fffffff, 0x00020000);
+#pragma unroll
+            for (int i = 0; i < 2 * MB; ++i) {
+                const int r = 8 * i + (lane >> 3);
+                const int rr = min(r, I.rt.mcount - 1);  // rows past the valid ones read the last
+                const int64_t arow = a.a_gather ? (int64_t)a.a_gather[I.rt.p0 + rr] : rr;
+                c.aoff[i] = (uint32_t)(arow * a.lda * 2 + (((lane & 7) ^ strm_swz(r & 15)) << 4));
+            }
+            const int64_t brow0 = GROUPED ? (int64_t)I.rt.e * a.b_group_rows : 0;
+#pragma unroll
+            for (int b = 0; b < NB; ++b) {
+                int64_t r0;
+                if constexpr (EPI == EPI_SWIGLU)
+                    r0 = brow0 + (b == 0 ? 0 : a.N) + I.nb * 16;
+                else
+                    r0 = brow0 + (I.nb * NB + b) * 16;
+                const auto rsrc = __builtin_amdgcn_make_buffer_rsrc(uniform_ptr((const uint8_t *)a.B + r0 * K * 2),
+                                                                    0, 0x7fffffff, 0x00020000);
+                if (b == 0) c.rb0 = rsrc;
+                else c.rb1 = rsrc;
+            }
+        };
+        // Tiles of up to 8 rows (most of them at decode) load one A row block per
+        // group: fragment rows 8..15 then hold stale data, and their results are
+        // never stored.
+        auto first = [&](const Item &I) {
+            if constexpr (MB == 1) {
+                if (I.rt.mcount <= 8) strm_first<MB, NB, 1>(c, wave, I.kbeg);
+                else strm_first<MB, NB, 2>(c, wave, I.kbeg);
+            } else {
+                strm_first<MB, NB, 2 * MB>(c, wave, I.kbeg);
+            }
+        };
+        const int ng = (int)(kq / kStrmKG);
+        Item cur;
+        setup(item, cur);
+        first(cur);
+        for (;;) {
+            floatx4_t acc[MB][NB];
+#pragma unroll
+            for (int m = 0; m < MB; ++m)
+#pragma unroll
+                for (int b = 0; b < NB; ++b) acc[m][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+            if constexpr (MB == 1) {
+                if (cur.rt.mcount <= 8) strm_steps<MB, NB, 1, AT>(acc, c, cur.kbeg, ng, wave);
+                else strm_steps<MB, NB, 2, AT>(acc, c, cur.kbeg, ng, wave);
+            } else {
+                strm_steps<MB, NB, 2 * MB, AT>(acc, c, cur.kbeg, ng, wave);
+            }
+            // every load of this item has landed and every slot read is done
+            const int64_t nx = item + gridDim.x;
+            Item nxt;
+            if (nx < items) {
+                setup(nx, nxt);
+                first(nxt);
+            }
+            finish(cur.rt, cur.nb, cur.ksl, acc);
+            if (nx >= items) break;
+            item = nx;
+            cur = nxt;
+        }
+        return;
+    }
+    for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
+        const int ksl = (int)(item % ks);
+        const int64_t tb = item / ks;
+        const int t = (int)(tb / nblocks);
+        const int64_t nb = tb - (int64_t)t * nblocks;
+        const int64_t kbeg = (ksl * 4 + wave) * kq;
+        const int64_t kend = kbeg + kq;
+        RowTile rt;
+        load_tile(a, GROUPED, BM, t, rt);  // mcount > 0 for every listed tile
+
+        // B row pointers (lane's row li of each 16-row block) and A row pointers.
+        const uint8_t *bptr[NB];
+        const uint8_t *bscale[NB];
+        int64_t brow0 = GROUPED ? (int64_t)rt.e * a.b_group_rows : 0;
+#pragma unroll
+        for (int c = 0; c < NB; ++c) {
+            int64_t r;
+            if constexpr (EPI == EPI_SWIGLU)
+                r = brow0 + (c == 0 ? 0 : a.N) + nb * 16 + li;
+            else
+                r = brow0 + (nb * NB + c) * 16 + li;
+            if constexpr (MX) {
+                // lane group lg reads its 32-element block of each 128-wide group
+                bptr[c] = (const uint8_t *)a.B + r * (K / 2) + (lg * 32) / 2;
+                bscale[c] = (const uint8_t *)a.B + a.b_rows_total * (K / 2) + r * (K / 32) + lg;
+            } else {
+                bptr[c] = (const uint8_t *)a.B + (r * K + lg * 32) * 2;
+                bscale[c] = nullptr;
+            }
+        }
+        const uint16_t *aptr[MB];
+#pragma unroll
+        for (int m = 0; m < MB; ++m) {
+            const int row = m * 16 + li;
+            if (row < rt.mcount) {
+                int64_t p = rt.p0 + row;
+                int64_t arow = a.a_gather ? (int64_t)a.a_gather[p] : p;
+                aptr[m] = a.A + arow * a.lda + lg * 32;
+            } else {
+                aptr[m] = nullptr;
+            }
+        }
+
+        floatx4_t acc[MB][NB];
+#pragma unroll
+        for (int m = 0; m < MB; ++m)
+#pragma unroll
+            for (int c = 0; c < NB; ++c) acc[m][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+        StreamFrag<MB, NB> cur, nxt;
+        stream_load<MB, NB, MX, AT>(cur, bptr, bscale, aptr, kbeg);
+        for (int64_t kk = kbeg; kk < kend; kk += 128) {
+            if (kk + 128 < kend) stream_load<MB, NB, MX, AT>(nxt, bptr, bscale, aptr, kk + 128);
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+#pragma unroll
+                for (int m = 0; m < MB; ++m)
+#pragma unroll
+                    for (int c = 0; c < NB; ++c)
+                        acc[m][c] = mfma16x16x32<AT>(cur.a[m][s], cur.b[c][s], acc[m][c]);
+            cur = nxt;
+        }
+
+        finish(rt, nb, ksl, acc);
     }
 }
 
