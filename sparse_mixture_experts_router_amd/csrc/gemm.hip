@@ -100,15 +100,14 @@ constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 //
 // Work item = (row tile, column block).  A column block is NB blocks of 16 B
 // rows (EPI_SWIGLU: NB = 2, the gate rows j0.. and the up rows F + j0..).
-// The 4 waves of the workgroup split K in four contiguous quarters.  Dense
-// items and MXFP4 weights load straight into registers: every 128-wide K
-// group is one lane-group-permuted MFMA quartet, lane group g = lane/16
-// owning k in [32g, 32g+32) of the group and feeding 8 of them to each of 4
-// MFMAs, so a lane reads 64 contiguous bytes of a bf16 B row (or one whole
-// 32-element MXFP4 block: 16 code bytes and its scale) and the same 64
-// bytes of its A row.  Grouped items on bf16/fp16 weights stage A and B
-// through LDS instead (below).  Partial sums of the waves meet in LDS and
-// wave 0 applies the epilogue.
+// The 4 waves of the workgroup split K in four contiguous quarters.  Items
+// on bf16/fp16 weights (grouped 16-row and dense 64-row tiles) stage A and B
+// through LDS (below).  Items on MXFP4 weights load straight into registers:
+// every 128-wide K group is one lane-group-permuted MFMA quartet, lane group
+// g = lane/16 owning k in [32g, 32g+32) of the group and feeding 8 of them
+// to each of 4 MFMAs, so a lane reads one whole 32-element MXFP4 block (16
+// code bytes and its scale) and the same 64 bytes of its A row.  Partial
+// sums of the waves meet in LDS and wave 0 applies the epilogue.
 
 template <int MB, int NB>
 struct StreamFrag {
@@ -320,7 +319,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
     const int ntiles = GROUPED ? *a.ntiles : (int)((a.M + BM - 1) / BM);
     const int64_t items = (int64_t)ntiles * nblocks * ks;
 
-    // grouped items on bf16/fp16 weights stream their weights through LDS
+    // items on bf16/fp16 weights stream A and B through LDS
     constexpr bool kDma = !MX && NB <= 2 && (GROUPED ? MB == 1 : MB == 4);
     // Cross-wave reduction and epilogue of one item (acc: this wave's partial sums).
     auto finish = [&](const RowTile &rt, int64_t nb, int ksl, floatx4_t (&acc)[MB][NB]) {
