@@ -76,6 +76,18 @@ def test_small_skewed_mixed_tiles():
     assert counts.max() > 32 and (counts <= 32).any()
 
 
+def test_stream_items_pipelined_across_tiles():
+    # ~19 tokens per expert over 256 experts: every expert streamed as a full 16-row tile plus a short
+    # one, and more items than the streaming grid, so each workgroup runs several items back to back
+    # (the next item's first loads go out under the previous item's epilogue) over tiles of both sizes
+    p = small_case("stream_pipelined", T=600, n=256, k=8)
+    res, gpu = run_and_compare(p, tokens=synthetic.sample_tokens(p.T, 200, seed=9))
+    counts = gpu["expert_counts"]
+    # (an average of <= 32 rows per expert streams every expert, whatever its count)
+    assert -(-p.T * p.k // p.n) <= 32
+    assert (counts > 16).sum() > 100 and ((counts % 16) <= 8).sum() > 50
+
+
 def test_batch_rows_past_2gib():
     # T * k * d_ff * 2 bytes of expert activations exceed 2 GiB: the tile kernels address GEMM2's rows from
     # each tile's first row (32-bit lane offsets), so slots whose rows sit past 2 GiB of that buffer are
