@@ -26,6 +26,8 @@ enum Epi : int {
 struct TileEntry {  // one M-tile of a grouped GEMM: expert e, rows m0 .. of its segment
     int32_t e;
     int32_t m0;
+    int32_t p0;      // its first permuted row: the expert's offset + m0
+    int32_t mcount;  // its valid rows (1 .. the list's tile height)
 };
 
 struct GemmArgs {

@@ -35,11 +35,10 @@ struct RowTile {
 
 __device__ __forceinline__ bool load_tile(const GemmArgs &a, bool grouped, int bm, int t, RowTile &rt) {
     if (grouped) {
-        TileEntry te = a.tiles[t];
-        int c = a.counts[te.e];
+        const TileEntry te = a.tiles[t];  // rows and count precomputed with the list
         rt.e = te.e;
-        rt.p0 = (int64_t)a.offsets[te.e] + te.m0;
-        rt.mcount = min(bm, c - te.m0);
+        rt.p0 = te.p0;
+        rt.mcount = te.mcount;
     } else {
         rt.e = 0;
         rt.p0 = (int64_t)t * bm;
@@ -410,14 +409,27 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
             int64_t nb, kbeg;
             int ksl;
         };
-        // tile entry, descriptors and A offsets of item it
-        auto setup = [&](int64_t it, Item &I) {
+        // the tile of item it and, for grouped items, its list entry
+        auto tile_of = [&](int64_t it) { return (int)(it / ks / nblocks); };
+        auto entry_of = [&](int64_t it) {
+            TileEntry te{};
+            if constexpr (GROUPED) te = a.tiles[tile_of(it)];
+            return te;
+        };
+        // row tile, descriptors and A offsets of item it (te: its list entry)
+        auto setup = [&](int64_t it, Item &I, const TileEntry &te) {
             I.ksl = (int)(it % ks);
             const int64_t tb = it / ks;
             const int t = (int)(tb / nblocks);
             I.nb = tb - (int64_t)t * nblocks;
             I.kbeg = (I.ksl * 4 + wave) * kq;
-            load_tile(a, GROUPED, BM, t, I.rt);  // mcount > 0 for every listed tile
+            if constexpr (GROUPED) {
+                I.rt.e = te.e;
+                I.rt.p0 = te.p0;
+                I.rt.mcount = te.mcount;  // > 0 for every listed tile
+            } else {
+                load_tile(a, false, BM, t, I.rt);
+            }
             // gathered A rows are addressed from the buffer start (the layer keeps that
             // buffer below 2 GiB), contiguous ones from the tile's first row
             const uint16_t *abase = a.a_gather ? a.A : a.A + I.rt.p0 * a.lda;
@@ -456,9 +468,12 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
         };
         const int ng = (int)(kq / kStrmKG);
         Item cur;
-        setup(item, cur);
+        setup(item, cur, entry_of(item));
         first(cur);
         for (;;) {
+            // the next item's list entry goes out now, under this item's K loop
+            const int64_t nx = item + gridDim.x;
+            const TileEntry te_nx = nx < items ? entry_of(nx) : TileEntry{};
             floatx4_t acc[MB][NB];
 #pragma unroll
             for (int m = 0; m < MB; ++m)
@@ -471,10 +486,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
                 strm_steps<MB, NB, 2 * MB, AT>(acc, c, cur.kbeg, ng, wave);
             }
             // every load of this item has landed and every slot read is done
-            const int64_t nx = item + gridDim.x;
             Item nxt;
             if (nx < items) {
-                setup(nx, nxt);
+                setup(nx, nxt, te_nx);
                 first(nxt);
             }
             finish(cur.rt, cur.nb, cur.ksl, acc);

@@ -349,14 +349,16 @@ __device__ void publish_counts(const int *cnt, int *off, int *ts, int *tb, int *
         const int c = cnt[tid];
         counts[tid] = c;
         offsets[tid] = off[tid];
+        const int o = off[tid];
+        auto entry = [&](int m0, int bm) { return TileEntry{tid, m0, o + m0, min(bm, c - m0)}; };
         if (tiles_small)
-            for (int q = 0; q < ts[tid + 1] - ts[tid]; ++q) tiles_small[ts[tid] + q] = TileEntry{tid, q * kSmallBM};
+            for (int q = 0; q < ts[tid + 1] - ts[tid]; ++q) tiles_small[ts[tid] + q] = entry(q * kSmallBM, kSmallBM);
         if (tiles_big)
-            for (int q = 0; q < tb[tid + 1] - tb[tid]; ++q) tiles_big[tb[tid] + q] = TileEntry{tid, q * kTileBM};
+            for (int q = 0; q < tb[tid + 1] - tb[tid]; ++q) tiles_big[tb[tid] + q] = entry(q * kTileBM, kTileBM);
         // a half-height tile holds either the whole expert or its remainder after the full tiles
         if (tiles_half && th[tid + 1] > th[tid])
-            tiles_half[th[tid]] = TileEntry{tid, c <= kHalfBM ? 0 : (c / kTileBM) * kTileBM};
-        if (tiles_tall && tt[tid + 1] > tt[tid]) tiles_tall[tt[tid]] = TileEntry{tid, 0};
+            tiles_half[th[tid]] = entry(c <= kHalfBM ? 0 : (c / kTileBM) * kTileBM, kHalfBM);
+        if (tiles_tall && tt[tid + 1] > tt[tid]) tiles_tall[tt[tid]] = entry(0, kTallBM);
     }
     if (tid == 0) {
         offsets[n] = off[n];
