@@ -1057,7 +1057,6 @@ __device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, i
     const int wn = TM == 1 ? wave : TM == 3 ? wave & 3 : wave & 1;
     const int arow0 = wm * 32 * MB;       // first A row of this wave's row blocks
     lane = opaque(lane);
-    const int lr = lane & 31, lh = lane >> 5;
     const int64_t K = a.K;                // B row length
     const int ks = (EPI == EPI_F32 && !MX && !GROUPED && a.ksplit > 1) ? a.ksplit : 1;
     const int64_t kn = K / ks, k0 = (int64_t)ksl * kn;  // this item's K slice
