@@ -248,7 +248,10 @@ size_t moe_workspace_bytes(const moe_desc *desc);
  *   workspace  device scratch of at least moe_workspace_bytes(desc) bytes,
  *              256-byte aligned; contents on entry are ignored
  *   dbg        optional inspection outputs (NULL for none)
- * Returns MOE_OK once everything is enqueued on `stream`.
+ * Returns MOE_OK once everything is enqueued on `stream`.  Without dbg the
+ * call enqueues kernels only (no allocation, memset, copy or wait), so it may
+ * be captured into a HIP graph; the replays reuse the captured pointers and
+ * the workspace, so calls that overlap on one workspace race.
  */
 int moe_layer_forward(const moe_desc *desc, const void *x, const void *router_w, const void *down_w,
                       const void *expert_w1, const void *expert_w2, const void *up_w,
