@@ -68,6 +68,17 @@ def recorded_traffic(name: str):
     return rec["traffic_bytes"]
 
 
+def cpu_model() -> str:
+    """The host CPU's model name (from /proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
 def csrc_hash() -> str:
     """Digest of the kernel sources (all of csrc/, in name order)."""
     import glob
@@ -136,10 +147,6 @@ def main():
     log("layer generated in %.1f s" % (time.time() - t0))
     W = {k: to_dev(v) for k, v in host.items()}
     wfmt = args.weight_format
-    if wfmt == "f16":
-        for key in ("w1", "w2", "up_w"):  # in place, once, outside every timed region
-            moe.moe_convert_bf16_to_f16(W[key], W[key], W[key].numel())
-        torch.cuda.synchronize()
     gains = {"router_bias": None, "gamma_in": None, "gamma_expert": W["gamma_ex"], "res_gate": W["gate"]}
 
     def make_desc(T, pr, wf):
@@ -242,6 +249,33 @@ def main():
         del scratch
         return float(np.median(ms))
 
+    def to_f16_format():
+        # expert_w1, expert_w2 and up_w converted in place, once, outside every timed region
+        for key in ("w1", "w2", "up_w"):
+            moe.moe_convert_bf16_to_f16(W[key], W[key], W[key].numel())
+        torch.cuda.synchronize()
+
+    # The bf16 checkpoint as given (no conversion), decode and prefill, before the fp16 format is made
+    bf16_ckpt = None
+    if wfmt == "f16" and not args.no_extra and not args.only_prefill:
+        rb = run_workload(p, args.steps, args.warmup, wf="bf16")
+        bf16_ckpt = {"decode_T64": {"ms_per_step": round(rb["ms"], 4),
+                                    "tokens_per_s": round(p.chunk_T / (rb["ms"] * 1e-3), 1),
+                                    "stage_ms": {k: round(v, 4) for k, v in rb["stages"].items()}}}
+        log("bf16 checkpoint, decode T=%d: %.3f ms/step" % (p.chunk_T, rb["ms"]))
+        if not args.no_prefill:
+            pc = synthetic.PRESETS["c2"]
+            rb2 = run_workload(pc, 3, 1, wf="bf16")
+            bf16_ckpt["prefill_T8192"] = {
+                "ms_per_step": round(rb2["ms"], 4), "tokens_per_s": round(pc.chunk_T / (rb2["ms"] * 1e-3), 1),
+                "TFLOPs": round(layer_flops(pc)["total"] / (rb2["ms"] * 1e-3) / 1e12, 1),
+                "stage_ms": {k: round(v, 4) for k, v in rb2["stages"].items()}}
+            log("bf16 checkpoint, prefill T=%d: %.3f ms/step" % (pc.chunk_T, rb2["ms"]))
+        bf16_ckpt["note"] = ("expert_w1, expert_w2 and up_w read as bf16 and converted to fp16 per fragment "
+                             "inside the GEMMs; same results bit for bit as the fp16 weight format")
+    if wfmt == "f16":
+        to_f16_format()
+
     if args.only_prefill:
         p2 = synthetic.PRESETS["c2"]
         r2 = run_workload(p2, args.prefill_steps, 2)
@@ -272,7 +306,8 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": ("fp16 MFMA operands (bf16 checkpoint weights stored as fp16, value-exact), fp32 accumulate"
+        "dtype": ("fp16 MFMA operands (bf16 checkpoint weights stored as fp16: exact for magnitudes in "
+                  "[2^-17, 65504], smaller ones round to fp16 subnormals), fp32 accumulate"
                   if wfmt == "f16" else "bf16 weights, fp16 activations, fp32 accumulate"),
         "data": "synthetic (seeded Philox normals, random-init weights of the 816B-A42B layer shape)",
         "config": {"workload": "latent MoE layer, decode T=64", "T": p.chunk_T, "d_model": p.d, "d_latent": p.L,
@@ -289,6 +324,8 @@ def main():
                      "bytes_per_launch": by["gemm1"], "avg_launch_ms": round(g1_ms, 4)},
     }
 
+    if bf16_ckpt:
+        result["bf16_checkpoint"] = bf16_ckpt
     if not args.no_extra:
         fm = flushed_ms(r, args.steps)
         result["decode_cache_flushed"] = {
@@ -388,11 +425,31 @@ def main():
             el += time.perf_counter() - t1
             passes += 1
             m += len(toks)
-        cores = int(os.environ.get("OMP_NUM_THREADS", os.cpu_count() or 1))
+        cores = oracle.threads()
         result["cpu_baseline"] = {"value": round(m / el, 3), "unit": "tokens/s", "cores": cores, "kind": "oracle",
+                                  "cpu_model": cpu_model(),
                                   "sample": "%d passes over the T=%d decode batch (%d token rows), fp64 oracle, "
                                             "%.1f s" % (passes, p.chunk_T, m, el)}
         log("cpu oracle: %d token rows in %.1f s on %d threads" % (m, el, cores))
+        if not args.no_prefill:
+            # the prefill batch: routing (router, top-k, weights) of all its tokens, and the whole layer on a
+            # seeded sample of them (exact per token: rows are independent)
+            p2 = synthetic.PRESETS["c2"]
+            x2 = synthetic.inputs(p2)
+            t2 = dict(host, x=x2)
+            t1 = time.perf_counter()
+            oracle.forward(p2.cfg(), t2, want_outputs=False)
+            el_r = time.perf_counter() - t1
+            sub = synthetic.sample_tokens(p2.T, 256, seed=77)
+            t1 = time.perf_counter()
+            oracle.forward(p2.cfg(), t2, tokens=sub)
+            el_f = time.perf_counter() - t1
+            result["cpu_baseline"]["prefill_T8192"] = {
+                "routing_tokens_per_s": round(p2.T / el_r, 1), "layer_tokens_per_s": round(len(sub) / el_f, 3),
+                "sample": "routing of all %d tokens (%.1f s); the whole layer on %d seeded tokens (%.1f s)" % (
+                    p2.T, el_r, len(sub), el_f)}
+            log("cpu oracle, prefill batch: routing %d tokens in %.1f s, layer on %d tokens in %.1f s" % (
+                p2.T, el_r, len(sub), el_f))
 
     print(json.dumps(result))
 

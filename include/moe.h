@@ -33,6 +33,11 @@
  *     asynchronously and no call synchronises with the host;
  *   - the descriptor is validated on the host before any launch; on error
  *     nothing is enqueued and a negative moe_status is returned;
+ *   - MOE_ERR_HIP is the one status returned after launching began: a HIP
+ *     launch or event call of the chain failed, the kernels before it may
+ *     have been enqueued, and every output is undefined.  An error left
+ *     pending by an earlier, unrelated HIP call on the calling thread is
+ *     cleared when an entry point starts and is not reported by it;
  *   - inputs are assumed finite; there are no device-side checks.
  */
 #ifndef MOE_MI355X_H
@@ -207,7 +212,12 @@ typedef struct {
  *   stage_events  NULL or an array of 2*MOE_NUM_STAGES hipEvent_t created
  *                 by the caller; stage s records [2s] before and [2s+1]
  *                 after its kernels on `stream` (skipped stages record
- *                 nothing) */
+ *                 nothing)
+ *   logits   [T][n] fp32   the router logits the selection used (the K
+ *                          slices of the router GEMM already added, in
+ *                          slice order)
+ *   u        [T][d] act_dtype  the branch input the router and the
+ *                          down-projection read: x, or its input norm */
 typedef struct {
     int32_t *topk_idx;
     float *topk_w;
@@ -223,17 +233,31 @@ typedef struct {
     float *ssq;
     void *m;
     void **stage_events;
+    float *logits;
+    void *u;
 } moe_debug;
 
 /* Human-readable text of a moe_status (static storage). */
 const char *moe_error_string(int status);
 
 /* Host-only check of a descriptor: MOE_OK, MOE_ERR_INVALID_ARG or
- * MOE_ERR_UNSUPPORTED.  Needs no GPU. */
+ * MOE_ERR_UNSUPPORTED.  Needs no GPU.  What it checks is the shape of the
+ * layer y = sum_i G(x)_i E_i(x) with a top-k gate over n experts
+ * (bobbyburns.tech "816 billion parameters, and only 42 billion show up
+ * for each token", "The math": "Setup" and "The gate": 1 <= k <= n) and of
+ * the latent SwiGLU experts with their norms and residual gate (flozi.net
+ * "Muse Spark Open: Norm-Preserving Gates Are Not a Norm Guarantee",
+ * "Latent experts: normalization happens before the weighted sum"), plus
+ * the size limits stated with moe_desc. */
 int moe_validate(const moe_desc *desc);
 
 /* Device workspace bytes moe_layer_forward needs for this descriptor
- * (0 if the descriptor is invalid).  Host-only; needs no GPU. */
+ * (0 if the descriptor is invalid).  Host-only; needs no GPU.  It holds
+ * the layer's intermediates between its stages (the sections cited for
+ * moe_validate): the router logits, the kept experts and weights, the
+ * permutation of the (token, slot) pairs, the latent z, the SwiGLU
+ * outputs and normalised expert outputs of the k selected experts of
+ * every token, and the weighted sum m. */
 size_t moe_workspace_bytes(const moe_desc *desc);
 
 /*
@@ -279,7 +303,12 @@ int moe_router_topk(const moe_desc *desc, const void *u, const void *router_w, c
                     size_t workspace_bytes, void *stream);
 
 /*
- * Permutation stage alone: from topk_idx [T][k] (values in [0, n)) writes
+ * Permutation stage alone.  It realises the sparse evaluation of
+ * bobbyburns.tech "816 billion parameters, and only 42 billion show up for
+ * each token", "The math" -> "Setup": an expert whose gate value is 0 is
+ * never evaluated, so the (token, slot) pairs are grouped by the expert
+ * they selected and each expert runs on its own rows only.
+ * From topk_idx [T][k] (values in [0, n)) writes
  *   counts [n], offsets [n+1]  tokens per expert, exclusive prefix sum
  *   perm_tok, perm_slot [T*k]  pairs sorted by (expert, token): within
  *                              expert e's segment [offsets[e], offsets[e+1])

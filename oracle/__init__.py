@@ -67,8 +67,10 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        build()  # compiles only when the library is missing or older than its source
-        _lib = ctypes.CDLL(_LIB)
+        path = os.environ.get("MOE_ORACLE_LIB")  # a separately built copy (e.g. a sanitizer build)
+        if not path:
+            path = build()  # compiles only when the library is missing or older than its source
+        _lib = ctypes.CDLL(path)
         vp, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
         _lib.orc_forward.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Tensors), vp, i64, vp, i32,
                                      vp, vp, vp, vp, vp, vp, vp]
@@ -86,7 +88,14 @@ def lib():
         _lib.orc_router_scores.argtypes = [ctypes.POINTER(_Desc), vp, vp, vp, vp]
         _lib.orc_router_weights.argtypes = [ctypes.POINTER(_Desc), vp, vp, i64, vp]
         _lib.orc_muse_gate_coeffs.argtypes = [dbl, dbl, dbl, vp, vp]
+        _lib.orc_threads.restype = ctypes.c_int
+        _lib.orc_branch_input.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Tensors), vp, i64, vp]
     return _lib
+
+
+def threads() -> int:
+    """Threads the oracle's parallel loops run on."""
+    return int(lib().orc_threads())
 
 
 def _p(a):
@@ -163,6 +172,19 @@ def forward(cfg: dict, t: dict, tokens=None, forced=None, dense: bool = False, m
     assert rc == 0
     res["tokens"] = tok
     return res
+
+
+def branch_input(cfg: dict, t: dict, tokens=None) -> np.ndarray:
+    """The branch input u of rows `tokens` (all rows if None): x, or its
+    input norm rounded to the input dtype, as float64 [ntok][d]."""
+    desc = make_desc(cfg)
+    x = np.ascontiguousarray(t["x"])
+    tok = np.arange(x.shape[0], dtype=np.int64) if tokens is None else _c(tokens, np.int64)
+    g = None if t.get("gamma_in") is None else _c(t["gamma_in"], np.float32)
+    tens = _Tensors(x=_p(x), gamma_in=_p(g))
+    out = np.zeros((tok.shape[0], cfg["d"]), np.float64)
+    lib().orc_branch_input(ctypes.byref(desc), ctypes.byref(tens), _p(tok), tok.shape[0], _p(out))
+    return out
 
 
 def router_scores(cfg: dict, logits, bias=None):

@@ -43,6 +43,9 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 
 enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_MXFP4 = 2, ORC_F16 = 3 };
 enum { ORC_NORM_NONE = 0, ORC_NORM_CENTERED = 1, ORC_NORM_INPUT_SCALED = 2 };
@@ -562,3 +565,24 @@ void orc_decode_matrix(const void *base, int32_t dt, int64_t rows, int64_t K, do
 
 double orc_round_bf16(double v) { return round_to_bf16(v); }
 double orc_round_f16(double v) { return round_to_f16(v); }
+
+/* The branch input u (x, or its input norm in the input dtype) of tokens
+ * tok[0..ntok), as the forward pass computes it: out [ntok][d]. */
+void orc_branch_input(const orc_desc *d, const orc_tensors *w, const int64_t *tok, int64_t ntok, double *out) {
+    double *h = (double *)malloc(sizeof(double) * (size_t)d->d);
+    for (int64_t q = 0; q < ntok; ++q) branch_input(d, w, tok[q], h, out + q * d->d);
+    free(h);
+}
+
+/* Threads of the oracle's parallel row loops (the OpenMP team size; 1 without OpenMP). */
+int orc_threads(void) {
+    int n = 1;
+#ifdef _OPENMP
+#pragma omp parallel
+    {
+#pragma omp single
+        n = omp_get_num_threads();
+    }
+#endif
+    return n;
+}

@@ -56,7 +56,7 @@ class moe_debug(ctypes.Structure):
                 ("expert_offsets", ctypes.c_void_p), ("perm_tok", ctypes.c_void_p), ("perm_slot", ctypes.c_void_p),
                 ("y", ctypes.c_void_p), ("pos", ctypes.c_void_p), ("z", ctypes.c_void_p), ("act", ctypes.c_void_p),
                 ("S", ctypes.c_void_p), ("ssq", ctypes.c_void_p), ("m", ctypes.c_void_p),
-                ("stage_events", ctypes.c_void_p)]
+                ("stage_events", ctypes.c_void_p), ("logits", ctypes.c_void_p), ("u", ctypes.c_void_p)]
 
 
 _lib = None
@@ -147,6 +147,26 @@ def _stream(stream):
     return stream.cuda_stream
 
 
+def _scratch(nbytes: int, device, stream):
+    """A uint8 device buffer for a call enqueued on `stream`.  It comes from
+    torch's caching allocator on the current stream; when the call goes to
+    another torch stream the buffer is recorded on that stream, so the
+    allocator does not hand its memory out again before the call's kernels
+    are done.  A raw stream handle other than the current stream cannot be
+    recorded: such calls must pass their own buffer."""
+    import torch
+    buf = torch.empty(max(nbytes, 1), dtype=torch.uint8, device=device)
+    if stream is not None:
+        cur = torch.cuda.current_stream(device)
+        if isinstance(stream, int):
+            if stream != cur.cuda_stream:
+                raise ValueError("a call on a raw stream handle other than torch's current stream needs an "
+                                 "explicit workspace")
+        elif stream != cur:
+            buf.record_stream(stream)
+    return buf
+
+
 def _wbytes(desc: moe_desc, rows: int, K: int) -> int:
     if desc.weight_dtype == DT["mxfp4"]:
         return rows * K // 2 + rows * K // 32
@@ -161,7 +181,8 @@ def moe_layer_forward(desc: moe_desc, x, router_w, down_w, expert_w1, expert_w2,
     gamma_expert, res_gate, gamma_latent, gamma_out (absent = NULL).  dbg:
     dict of device tensors under the moe_debug field names, plus optionally
     "stage_events" (an int address of 2 * len(STAGES) hipEvent_t).  workspace: uint8 device tensor of at least
-    moe_workspace_bytes(desc) bytes (allocated here when None).
+    moe_workspace_bytes(desc) bytes (allocated here when None, and then kept
+    from reuse until the call's kernels on `stream` are done).
     """
     import torch
     T, d, L, n, k, F = desc.T, desc.d_model, desc.d_latent, desc.n_experts, desc.top_k, desc.d_ff
@@ -171,7 +192,7 @@ def moe_layer_forward(desc: moe_desc, x, router_w, down_w, expert_w1, expert_w2,
     rows1 = n * (2 * F if desc.expert_kind == KIND["swiglu3"] else F)
     need = moe_workspace_bytes(desc)
     if workspace is None:
-        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=x.device)
+        workspace = _scratch(need, x.device, stream)
     g = moe_gains()
     for nm in GAINS:
         v = (gains or {}).get(nm)
@@ -198,9 +219,8 @@ def moe_layer_forward(desc: moe_desc, x, router_w, down_w, expert_w1, expert_w2,
 
 def moe_router_topk(desc: moe_desc, u, router_w, router_bias, topk_idx, topk_w, logits=None, workspace=None,
                     stream=None):
-    import torch
     if logits is None and workspace is None:
-        workspace = torch.empty(max(moe_router_workspace_bytes(desc), 1), dtype=torch.uint8, device=u.device)
+        workspace = _scratch(moe_router_workspace_bytes(desc), u.device, stream)
     rc = lib().moe_router_topk(ctypes.byref(desc), _ptr(u, "u"), _ptr(router_w, "router_w"),
                                _ptr(router_bias, "router_bias"), _ptr(topk_idx, "topk_idx"), _ptr(topk_w, "topk_w"),
                                _ptr(logits, "logits"), _ptr(workspace, "workspace"),

@@ -249,7 +249,7 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
 
     MOE_TRY_RC(ev.begin(MOE_STAGE_TOPK));
     MOE_TRY(launch_topk(logits, router_splits(d), gains ? gains->router_bias : nullptr, T, (int)n, (int)k,
-                        d->bias_in_weights, router_fn_of(d), idx, wts, nullptr, s));
+                        d->bias_in_weights, router_fn_of(d), idx, wts, dbg ? dbg->logits : nullptr, s));
     MOE_TRY_RC(ev.end(MOE_STAGE_TOPK));
 
     // Experts with up to small_max tokens are streamed (weight-bandwidth
@@ -426,6 +426,7 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
         if (dbg->ssq && ssq)
             MOE_TRY(hipMemcpyAsync(dbg->ssq, ssq, (size_t)TK * (Lw / 16) * 4, hipMemcpyDeviceToDevice, s));
         if (dbg->m) MOE_TRY(hipMemcpyAsync(dbg->m, m, (size_t)T * Lw * 2, hipMemcpyDeviceToDevice, s));
+        if (dbg->u) MOE_TRY(hipMemcpyAsync(dbg->u, u, (size_t)T * D * 2, hipMemcpyDeviceToDevice, s));
     }
     return MOE_OK;
 }
@@ -447,7 +448,7 @@ int forward_f32(const moe_desc *d, const void *x, const void *router_w, const vo
     MOE_TRY_RC(ev.end(MOE_STAGE_ROUTER));
     MOE_TRY_RC(ev.begin(MOE_STAGE_TOPK));
     MOE_TRY(launch_topk(logits, 1, gains ? gains->router_bias : nullptr, T, (int)n, (int)k, d->bias_in_weights,
-                        router_fn_of(d), idx, wts, nullptr, s));
+                        router_fn_of(d), idx, wts, dbg ? dbg->logits : nullptr, s));
     MOE_TRY_RC(ev.end(MOE_STAGE_TOPK));
     MOE_TRY_RC(ev.begin(MOE_STAGE_PERMUTE));
     MOE_TRY(launch_permute(idx, T, (int)k, (int)n, counts, offsets, perm_tok, perm_slot, pos, nullptr, nullptr,
@@ -474,9 +475,14 @@ int forward_f32(const moe_desc *d, const void *x, const void *router_w, const vo
         if (dbg->perm_tok) MOE_TRY(hipMemcpyAsync(dbg->perm_tok, perm_tok, TK * 4, hipMemcpyDeviceToDevice, s));
         if (dbg->perm_slot) MOE_TRY(hipMemcpyAsync(dbg->perm_slot, perm_slot, TK * 4, hipMemcpyDeviceToDevice, s));
         if (dbg->pos) MOE_TRY(hipMemcpyAsync(dbg->pos, pos, TK * 4, hipMemcpyDeviceToDevice, s));
+        if (dbg->u) MOE_TRY(hipMemcpyAsync(dbg->u, x, (size_t)T * D * 4, hipMemcpyDeviceToDevice, s));
     }
     return MOE_OK;
 }
+
+// Clears an error left pending by an earlier HIP call of the calling thread,
+// so the launchers' hipGetLastError reports their own launches only.
+inline void clear_stale_error() { (void)hipGetLastError(); }
 
 }  // namespace
 
@@ -513,8 +519,8 @@ int moe_layer_forward(const moe_desc *d, const void *x, const void *router_w, co
     Layout L = make_layout(d);
     if (workspace_bytes < L.total) return MOE_ERR_WORKSPACE_TOO_SMALL;
     if (!workspace || ((uintptr_t)workspace & 255)) return MOE_ERR_INVALID_ARG;
-    if (d->T == 0) return MOE_OK;
     hipStream_t s = as_stream(stream);
+    clear_stale_error();
     if (d->act_dtype == MOE_DT_BF16)
         return forward_bf16(d, x, router_w, down_w, expert_w1, expert_w2, up_w, gains, out, (uint8_t *)workspace, L,
                             dbg, s);
@@ -545,6 +551,7 @@ int moe_router_topk(const moe_desc *d, const void *u, const void *router_w, cons
     }
     if (d->T == 0) return MOE_OK;
     hipStream_t s = as_stream(stream);
+    clear_stale_error();
     if (d->router_dtype == MOE_DT_F32) {
         MOE_TRY(launch_router_f32((const float *)u, (const float *)router_w, d->T, (int)d->n_experts, d->d_model, lg,
                                   s));
@@ -572,6 +579,7 @@ int moe_permute(int64_t T, int64_t k, int64_t n, const int32_t *topk_idx, int32_
     if (T < 0 || k < 1 || n < 1 || n > 256 || k > n || T * k >= ((int64_t)1 << 31)) return MOE_ERR_INVALID_ARG;
     if (!topk_idx || !counts || !offsets || !perm_tok || !perm_slot || !pos) return MOE_ERR_INVALID_ARG;
     hipStream_t s = as_stream(stream);
+    clear_stale_error();
     MOE_TRY(launch_permute(topk_idx, T, (int)k, (int)n, counts, offsets, perm_tok, perm_slot, pos, nullptr, nullptr,
                            nullptr, nullptr, nullptr, 0, nullptr, s));
     return MOE_OK;
@@ -582,12 +590,14 @@ int moe_convert_bf16_to_f16(const void *src, void *dst, int64_t count, void *str
         return MOE_ERR_INVALID_ARG;
     const uintptr_t a = (uintptr_t)src, b = (uintptr_t)dst, bytes = (uintptr_t)count * 2;
     if (a != b && a < b + bytes && b < a + bytes) return MOE_ERR_INVALID_ARG;  // partial overlap
+    clear_stale_error();
     MOE_TRY(launch_bf16_to_f16(src, dst, count, as_stream(stream)));
     return MOE_OK;
 }
 
 int moe_hbm_copy(void *dst, const void *src, size_t bytes, void *stream) {
     if ((bytes & 15) || (bytes && (!dst || !src)) || (((uintptr_t)dst | (uintptr_t)src) & 15)) return MOE_ERR_INVALID_ARG;
+    clear_stale_error();
     MOE_TRY(launch_copy16(src, dst, (int64_t)bytes, as_stream(stream)));
     return MOE_OK;
 }

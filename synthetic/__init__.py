@@ -12,6 +12,7 @@ Workloads (the shapes and distributions of the pages' model):
   c3   same layer, T=16384, Zipf(1.2) selection bias 1.5*ln(rank weight)
   c4c  same layer with MXFP4 weights, 4 chunks of 8192, centered input norm
   c4i  as c4c with the input-scaled input norm
+  m1/m2  the Muse sublayer around the c1 layer at T=64 / T=8192
 """
 from __future__ import annotations
 
@@ -43,8 +44,10 @@ _lib = None
 def lib():
     global _lib
     if _lib is None:
-        build()  # compiles only when the library is missing or older than its source
-        _lib = ctypes.CDLL(_LIB)
+        path = os.environ.get("MOE_SYNTH_LIB")  # a separately built copy (e.g. a sanitizer build)
+        if not path:
+            path = build()  # compiles only when the library is missing or older than its source
+        _lib = ctypes.CDLL(path)
         vp, u64, i64, f32, cp = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int64, ctypes.c_float, ctypes.c_char_p
         _lib.synth_philox4x32_10.argtypes = [vp, vp, vp]
         _lib.synth_key.argtypes = [u64, cp, vp]

@@ -186,3 +186,28 @@ def test_convert_rejects_before_any_launch():
     assert lib.moe_convert_bf16_to_f16(None, b, 8, None) == bad
     assert lib.moe_convert_bf16_to_f16(a, ctypes.c_void_p(4096 + 16), 64, None) == bad  # partial overlap
     assert lib.moe_convert_bf16_to_f16(None, None, 0, None) == moe.MOE_OK       # nothing to do
+
+
+def test_binding_structs_match_the_header(tmp_path):
+    # sizeof and every field offset of the three C structs, compiled from include/moe.h,
+    # against the ctypes structures the binding passes
+    structs = {"moe_desc": moe.moe_desc, "moe_gains": moe.moe_gains, "moe_debug": moe.moe_debug}
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "moe.h"', "int main(void) {"]
+    for sn, cls in structs.items():
+        lines.append('printf("%s sizeof %%zu\\n", sizeof(%s));' % (sn, sn))
+        for fn, _ in cls._fields_:
+            lines.append('printf("%s %s %%zu\\n", offsetof(%s, %s));' % (sn, fn, sn, fn))
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    import subprocess
+    subprocess.check_call(["gcc", "-std=c11", "-I", os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    got = {}
+    for line in subprocess.check_output([str(exe)], text=True).splitlines():
+        sn, fn, v = line.split()
+        got[(sn, fn)] = int(v)
+    for sn, cls in structs.items():
+        assert got[(sn, "sizeof")] == ctypes.sizeof(cls), sn
+        for fn, _ in cls._fields_:
+            assert got[(sn, fn)] == getattr(cls, fn).offset, (sn, fn)
