@@ -27,7 +27,9 @@
  * Conventions for every entry point:
  *   - all tensor pointers are DEVICE pointers (hipMalloc'd or from a
  *     framework allocator) owned by the caller; the library allocates
- *     nothing, keeps no global mutable state and is re-entrant;
+ *     nothing and is re-entrant; its only global state is the static
+ *     scratch of moe_layer_forward_static and that array's per-device
+ *     address, looked up once per device;
  *   - all matrices are row-major with the reduction dimension contiguous;
  *   - `stream` is a hipStream_t (NULL = default stream); work is enqueued
  *     asynchronously and no call synchronises with the host;
@@ -55,7 +57,9 @@ typedef enum {
     MOE_ERR_INVALID_ARG = -1,          /* malformed descriptor or NULL required pointer */
     MOE_ERR_UNSUPPORTED = -2,          /* well-formed, but a combination this build does not run */
     MOE_ERR_WORKSPACE_TOO_SMALL = -3,  /* workspace_bytes < moe_workspace_bytes(desc) */
-    MOE_ERR_HIP = -4                   /* a HIP launch or event call failed */
+    MOE_ERR_HIP = -4,                  /* a HIP launch or event call failed */
+    MOE_ERR_STATIC_SCRATCH_TOO_SMALL = -5  /* moe_layer_forward_static: the batch needs more workspace
+                                              than MOE_STATIC_SCRATCH_BYTES */
 } moe_status;
 
 enum { MOE_DT_F32 = 0, MOE_DT_BF16 = 1, MOE_DT_MXFP4 = 2, MOE_DT_F16 = 3 };
@@ -281,6 +285,34 @@ int moe_layer_forward(const moe_desc *desc, const void *x, const void *router_w,
                       const void *expert_w1, const void *expert_w2, const void *up_w,
                       const moe_gains *gains, void *out, void *workspace, size_t workspace_bytes,
                       moe_debug *dbg, void *stream);
+
+/*
+ * moe_layer_forward without a caller workspace and without any allocation,
+ * for callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc).  The
+ * workspace is a static device array of MOE_STATIC_SCRATCH_BYTES inside the
+ * library: each device the library runs on holds its own copy from the first
+ * call on it until the process ends.  Arguments, outputs and results are
+ * those of moe_layer_forward (the same kernels run); the current HIP device
+ * must be the one `stream` belongs to.
+ *   - returns MOE_ERR_STATIC_SCRATCH_TOO_SMALL, before any launch, when
+ *     moe_workspace_bytes(desc) > MOE_STATIC_SCRATCH_BYTES (at the
+ *     816B-A42B layer shape: batches of more than 389 tokens, or 324 with
+ *     the branch output norm);
+ *   - calls no hipMalloc, hipFree or other allocating routine; the first
+ *     call on a device looks up that device's copy of the array
+ *     (hipGetSymbolAddress) and caches its address;
+ *   - the forward reads no workspace byte before writing it, so nothing is
+ *     cleared between calls; the array keeps the last call's intermediates;
+ *   - every call on one device shares that device's array: calls that
+ *     overlap on one device (concurrent streams, or threads enqueueing
+ *     before the previous call's kernels have finished on another stream)
+ *     race.  Calls enqueued on one stream are ordered and safe.
+ */
+#define MOE_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+int moe_layer_forward_static(const moe_desc *desc, const void *x, const void *router_w, const void *down_w,
+                             const void *expert_w1, const void *expert_w2, const void *up_w,
+                             const moe_gains *gains, void *out, moe_debug *dbg, void *stream);
 
 /*
  * Router stage alone: fp32 logits l = u W_r^T, then desc->router_fn:

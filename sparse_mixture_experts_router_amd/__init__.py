@@ -6,7 +6,7 @@ layer runs in that library's HIP kernels; this module only checks tensors and
 passes device pointers.  There is no fallback: if the library is missing the
 import of any entry point raises.
 
-Names follow the C ABI: ``moe_layer_forward``, ``moe_workspace_bytes``,
+Names follow the C ABI: ``moe_layer_forward``, ``moe_layer_forward_static``, ``moe_workspace_bytes``,
 ``moe_validate``, ``moe_error_string``, ``moe_router_topk``,
 ``moe_router_workspace_bytes``, ``moe_permute``, ``moe_convert_bf16_to_f16``,
 ``moe_hbm_copy``.
@@ -20,6 +20,8 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmoe_mi355x.so")
 
 MOE_OK, MOE_ERR_INVALID_ARG, MOE_ERR_UNSUPPORTED, MOE_ERR_WORKSPACE_TOO_SMALL, MOE_ERR_HIP = 0, -1, -2, -3, -4
+MOE_ERR_STATIC_SCRATCH_TOO_SMALL = -5
+MOE_STATIC_SCRATCH_BYTES = 64 << 20  # the static scratch of moe_layer_forward_static (include/moe.h)
 DT = {"f32": 0, "bf16": 1, "mxfp4": 2, "f16": 3}
 NORM = {"none": 0, "centered": 1, "input_scaled": 2}
 KIND = {"relu2": 0, "swiglu3": 1}
@@ -78,6 +80,8 @@ def lib() -> ctypes.CDLL:
         L.moe_workspace_bytes.restype = sz
         L.moe_layer_forward.argtypes = [ctypes.POINTER(moe_desc), vp, vp, vp, vp, vp, vp, ctypes.POINTER(moe_gains),
                                         vp, vp, sz, ctypes.POINTER(moe_debug), vp]
+        L.moe_layer_forward_static.argtypes = [ctypes.POINTER(moe_desc), vp, vp, vp, vp, vp, vp,
+                                               ctypes.POINTER(moe_gains), vp, ctypes.POINTER(moe_debug), vp]
         L.moe_router_workspace_bytes.argtypes = [ctypes.POINTER(moe_desc)]
         L.moe_router_workspace_bytes.restype = sz
         L.moe_router_topk.argtypes = [ctypes.POINTER(moe_desc), vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -88,7 +92,7 @@ def lib() -> ctypes.CDLL:
     return _lib
 
 
-EXPORTED = ["moe_error_string", "moe_validate", "moe_workspace_bytes", "moe_layer_forward",
+EXPORTED = ["moe_error_string", "moe_validate", "moe_workspace_bytes", "moe_layer_forward", "moe_layer_forward_static",
             "moe_router_workspace_bytes", "moe_router_topk", "moe_permute", "moe_convert_bf16_to_f16", "moe_hbm_copy"]
 
 
@@ -214,6 +218,38 @@ def moe_layer_forward(desc: moe_desc, x, router_w, down_w, expert_w1, expert_w2,
         _stream(stream))
     if rc != MOE_OK:
         raise MoeError(rc, "moe_layer_forward")
+    return out
+
+
+def moe_layer_forward_static(desc: moe_desc, x, router_w, down_w, expert_w1, expert_w2, up_w, gains: dict | None,
+                             out, dbg: dict | None = None, stream=None):
+    """moe_layer_forward on the library's static scratch: no workspace and
+    no allocation (batches up to MOE_STATIC_SCRATCH_BYTES of workspace)."""
+    import torch
+    T, d, L, n, F = desc.T, desc.d_model, desc.d_latent, desc.n_experts, desc.d_ff
+    ab = 4 if desc.act_dtype == DT["f32"] else 2
+    rb = 4 if desc.router_dtype == DT["f32"] else 2
+    Din = L if L else d
+    rows1 = n * (2 * F if desc.expert_kind == KIND["swiglu3"] else F)
+    g = moe_gains()
+    for nm in GAINS:
+        v = (gains or {}).get(nm)
+        if v is not None and v.dtype != torch.float32:
+            raise ValueError("gain %s must be float32" % nm)
+        setattr(g, nm, _ptr(v, nm))
+    dd = None
+    if dbg:
+        dd = moe_debug()
+        for nm, _ in moe_debug._fields_:
+            v = dbg.get(nm)
+            setattr(dd, nm, _ptr(v, nm) if nm != "stage_events" else v)
+    rc = lib().moe_layer_forward_static(
+        ctypes.byref(desc), _ptr(x, "x", T * d * ab), _ptr(router_w, "router_w", n * d * rb),
+        _ptr(down_w, "down_w", _wbytes(desc, L, d) if L else None), _ptr(expert_w1, "expert_w1", _wbytes(desc, rows1, Din)),
+        _ptr(expert_w2, "expert_w2", _wbytes(desc, n * Din, F)), _ptr(up_w, "up_w", _wbytes(desc, d, L) if L else None),
+        ctypes.byref(g), _ptr(out, "out", T * d * 4), ctypes.byref(dd) if dd else None, _stream(stream))
+    if rc != MOE_OK:
+        raise MoeError(rc, "moe_layer_forward_static")
     return out
 
 

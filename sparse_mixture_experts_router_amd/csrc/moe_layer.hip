@@ -19,6 +19,8 @@
 #include <math.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "../../include/moe.h"
 #include "gemm.h"
 #include "route.h"
@@ -486,6 +488,40 @@ inline void clear_stale_error() { (void)hipGetLastError(); }
 
 }  // namespace
 
+// ---------------------------------------------------------------------------
+// Static scratch of moe_layer_forward_static: the workspace of callers that
+// cannot allocate.  Every device the library runs on holds its own copy
+// until the process ends.  Host code never uses the name `scratch` as an
+// address (on the host it names a stand-in, not device memory): the device
+// address comes from hipGetSymbolAddress, once per device, with that device
+// current, and is kept in static_scratch_ptr.
+// ---------------------------------------------------------------------------
+static_assert(MOE_STATIC_SCRATCH_BYTES % 256 == 0, "whole 256-byte units");
+__device__ __align__(256) uint8_t scratch[MOE_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's copy of `scratch`.
+int static_scratch_ptr(void **out) {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess) return MOE_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return MOE_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (!g_scratch_ptr[dev]) {
+        void *ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess || !ptr) return MOE_ERR_HIP;
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return MOE_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char *moe_error_string(int status) {
@@ -495,6 +531,7 @@ const char *moe_error_string(int status) {
         case MOE_ERR_UNSUPPORTED: return "unsupported configuration";
         case MOE_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
         case MOE_ERR_HIP: return "HIP error";
+        case MOE_ERR_STATIC_SCRATCH_TOO_SMALL: return "batch needs more than the static scratch";
     }
     return "unknown status";
 }
@@ -525,6 +562,22 @@ int moe_layer_forward(const moe_desc *d, const void *x, const void *router_w, co
         return forward_bf16(d, x, router_w, down_w, expert_w1, expert_w2, up_w, gains, out, (uint8_t *)workspace, L,
                             dbg, s);
     return forward_f32(d, x, router_w, expert_w1, expert_w2, gains, out, (uint8_t *)workspace, L, dbg, s);
+}
+
+int moe_layer_forward_static(const moe_desc *d, const void *x, const void *router_w, const void *down_w,
+                             const void *expert_w1, const void *expert_w2, const void *up_w,
+                             const moe_gains *gains, void *out, moe_debug *dbg, void *stream) {
+    int rc = check_desc(d);
+    if (rc != MOE_OK) return rc;
+    if (d->T == 0) return MOE_OK;
+    const size_t need = make_layout(d).total;
+    if (need > MOE_STATIC_SCRATCH_BYTES) return MOE_ERR_STATIC_SCRATCH_TOO_SMALL;
+    void *ws = nullptr;
+    clear_stale_error();
+    rc = static_scratch_ptr(&ws);
+    if (rc != MOE_OK) return rc;
+    return moe_layer_forward(d, x, router_w, down_w, expert_w1, expert_w2, up_w, gains, out, ws,
+                             MOE_STATIC_SCRATCH_BYTES, dbg, stream);
 }
 
 size_t moe_router_workspace_bytes(const moe_desc *d) {
