@@ -18,17 +18,18 @@ _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "moe_oracle.c")
 _LIB = os.path.join(_HERE, "libmoe_oracle.so")
 
-F32, BF16, MXFP4, F16 = 0, 1, 2, 3
+F32, BF16, MXFP4, F16, MXFP8 = 0, 1, 2, 3, 4
 NORM_NONE, NORM_CENTERED, NORM_INPUT_SCALED = 0, 1, 2
 RELU, SWIGLU = 0, 1
 RES_NONE, RES_LINEAR, RES_MUSE = 0, 1, 2
 ROUTER_SOFTMAX, ROUTER_SIGMOID = 0, 1
 
-_DT = {"f32": F32, "bf16": BF16, "mxfp4": MXFP4, "f16": F16}
+_DT = {"f32": F32, "bf16": BF16, "mxfp4": MXFP4, "f16": F16, "mxfp8": MXFP8}
 _NORM = {"none": NORM_NONE, "centered": NORM_CENTERED, "input_scaled": NORM_INPUT_SCALED}
 _KIND = {"relu2": RELU, "swiglu3": SWIGLU}
 _RES = {"none": RES_NONE, "linear": RES_LINEAR, "muse": RES_MUSE}
 _ROUTER = {"softmax": ROUTER_SOFTMAX, "sigmoid": ROUTER_SIGMOID}
+_AQ = {"none": 0, "mxfp8": 1}
 
 
 def build(force: bool = False) -> str:
@@ -52,7 +53,7 @@ class _Desc(ctypes.Structure):
                 ("router_fn", ctypes.c_int32), ("out_mult", ctypes.c_double), ("rsf", ctypes.c_double),
                 ("lat_norm", ctypes.c_int32), ("out_norm", ctypes.c_int32),
                 ("eps_lat", ctypes.c_double), ("eps_out", ctypes.c_double),
-                ("tau", ctypes.c_double), ("floor_", ctypes.c_double)]
+                ("tau", ctypes.c_double), ("floor_", ctypes.c_double), ("act_quant", ctypes.c_int32)]
 
 
 class _Tensors(ctypes.Structure):
@@ -90,6 +91,7 @@ def lib():
         _lib.orc_muse_gate_coeffs.argtypes = [dbl, dbl, dbl, vp, vp]
         _lib.orc_threads.restype = ctypes.c_int
         _lib.orc_branch_input.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Tensors), vp, i64, vp]
+        _lib.orc_mxfp8_quantize.argtypes = [vp, i64, vp]
     return _lib
 
 
@@ -111,7 +113,8 @@ def make_desc(cfg: dict, mirror: bool = False) -> _Desc:
     expert_norm, res_gate, eps_in, eps_expert, bias_in_weights; optional
     router_fn ("softmax"), out_mult (1), routed_scale (1), latent_norm
     ("none"), out_norm ("none"), eps_latent, eps_out (1e-5), res_tau (0.3),
-    res_floor (1e-3)."""
+    res_floor (1e-3), act_quant ("none" | "mxfp8": the expert GEMMs read
+    MXFP8 activations)."""
     return _Desc(d=cfg["d"], L=cfg["L"], n=cfg["n"], k=cfg["k"], F=cfg["F"],
                  kind=_KIND[cfg["kind"]], act=_DT[cfg["act"]], wdt=_DT[cfg["weights"]],
                  rdt=_DT[cfg["router_w"]], in_norm=_NORM[cfg["in_norm"]],
@@ -123,7 +126,7 @@ def make_desc(cfg: dict, mirror: bool = False) -> _Desc:
                  rsf=float(cfg.get("routed_scale", 1.0)), lat_norm=_NORM[cfg.get("latent_norm", "none")],
                  out_norm=_NORM[cfg.get("out_norm", "none")], eps_lat=float(cfg.get("eps_latent", 1e-5)),
                  eps_out=float(cfg.get("eps_out", 1e-5)), tau=float(cfg.get("res_tau", 0.3)),
-                 floor_=float(cfg.get("res_floor", 1e-3)))
+                 floor_=float(cfg.get("res_floor", 1e-3)), act_quant=_AQ[cfg.get("act_quant", "none")])
 
 
 _KEEP = []
@@ -185,6 +188,18 @@ def branch_input(cfg: dict, t: dict, tokens=None) -> np.ndarray:
     out = np.zeros((tok.shape[0], cfg["d"]), np.float64)
     lib().orc_branch_input(ctypes.byref(desc), ctypes.byref(tens), _p(tok), tok.shape[0], _p(out))
     return out
+
+
+def mxfp8_quantize(v):
+    """MXFP8 (E4M3 elements, one power-of-two scale per 32 consecutive
+    values of the last axis): (dequantized values, scale exponents X)."""
+    v = np.array(v, np.float64, copy=True)
+    shape = v.shape
+    assert shape[-1] % 32 == 0
+    flat = np.ascontiguousarray(v.reshape(-1))
+    X = np.zeros(flat.size // 32, np.int32)
+    lib().orc_mxfp8_quantize(_p(flat), flat.size, _p(X))
+    return flat.reshape(shape), X.reshape(shape[:-1] + (shape[-1] // 32,))
 
 
 def router_scores(cfg: dict, logits, bias=None):

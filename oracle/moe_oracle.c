@@ -30,6 +30,11 @@
  *  - a norm returns its input dtype ([Gates], serving section), and the
  *    input-scaled norm rounds the scaled vector to the input dtype before
  *    its reduction ([Gates], normalization-orders section);
+ *  - with act_quant = MXFP8 (a mode of this build, not of the pages) the
+ *    inputs of the two expert GEMMs (the latent z and the SwiGLU output)
+ *    are the stored intermediates (rounded to the intermediate dtype)
+ *    quantized to MXFP8 per OCP MX v1.0, since that is what those GEMMs
+ *    multiply in that mode;
  *  - optional "mirror" mode additionally rounds the latent z, the SwiGLU
  *    output and the mixture m to an intermediate dtype (bf16 or fp16), the
  *    way a device stores them between GEMMs (a diagnostic, not a bar).
@@ -47,11 +52,12 @@
 #include <omp.h>
 #endif
 
-enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_MXFP4 = 2, ORC_F16 = 3 };
+enum { ORC_F32 = 0, ORC_BF16 = 1, ORC_MXFP4 = 2, ORC_F16 = 3, ORC_MXFP8 = 4 };
 enum { ORC_NORM_NONE = 0, ORC_NORM_CENTERED = 1, ORC_NORM_INPUT_SCALED = 2 };
 enum { ORC_RELU = 0, ORC_SWIGLU = 1 };
 enum { ORC_RES_NONE = 0, ORC_RES_LINEAR = 1, ORC_RES_MUSE = 2 };
 enum { ORC_ROUTER_SOFTMAX = 0, ORC_ROUTER_SIGMOID = 1 };
+enum { ORC_AQ_NONE = 0, ORC_AQ_MXFP8 = 1 };
 
 typedef struct {
     int64_t d, L, n, k, F; /* L == 0: no latent projection, experts read u directly */
@@ -74,6 +80,8 @@ typedef struct {
     int32_t out_norm;      /* norm of the branch output P_up m (the FFN output norm) */
     double eps_lat, eps_out;
     double tau, floor_;    /* ORC_RES_MUSE: temperature and floor of the residual gate */
+    int32_t act_quant;     /* ORC_AQ_MXFP8: the expert GEMMs read MXFP8 activations (the latent z and
+                              the SwiGLU output, stored in the intermediate dtype, then quantized) */
 } orc_desc;
 
 typedef struct {
@@ -159,9 +167,87 @@ static double e2m1_value(unsigned code) {
 /* E8M0 scale = 2^(E-127). */
 static double e8m0_value(unsigned E) { return ldexp(1.0, (int)E - 127); }
 
+/* ------------------------------------------------------------------ */
+/* MXFP8 activations (OCP Microscaling Formats (MX) v1.0, MXFP8 with   */
+/* E4M3 elements).  A block of 32 consecutive values along the         */
+/* reduction dimension shares one power-of-two scale 2^X, with         */
+/* X = floor(log2(max |v|)) - 8 (8 is the largest exponent of an E4M3  */
+/* element); each value becomes v / 2^X rounded to the nearest E4M3    */
+/* value, ties to even, a magnitude beyond the largest finite E4M3     */
+/* value (448) clamped to it.  An all-zero block keeps the smallest    */
+/* scale (E8M0 code 0) and zero elements.                              */
+/* ------------------------------------------------------------------ */
+
+/* Nearest E4M3 value to v (ties to even), clamped to [-448, 448].  E4M3
+ * has 3 mantissa bits, normal exponents -6..8 and subnormals of spacing
+ * 2^-9. */
+static double round_to_e4m3(double v) {
+    if (v == 0.0 || isnan(v)) return v;
+    double a = fabs(v);
+    if (a >= 448.0) return copysign(448.0, v);
+    int e;
+    frexp(a, &e);            /* a in [2^(e-1), 2^e) */
+    int ex = e - 1;
+    if (ex < -6) ex = -6;    /* below the normal range the spacing is fixed */
+    double q = ldexp(1.0, ex - 3);
+    double r = a / q, fl = floor(r), diff = r - fl, res;
+    if (diff > 0.5) res = fl + 1.0;
+    else if (diff < 0.5) res = fl;
+    else res = (fmod(fl, 2.0) == 0.0) ? fl : fl + 1.0;
+    res *= q;
+    if (res > 448.0) res = 448.0;
+    return copysign(res, v);
+}
+
+/* One MX block of n (<= 32) values quantized in place to its dequantized
+ * values q_i * 2^X; returns X (-127 for an all-zero block). */
+static int mxfp8_block(double *v, int64_t n) {
+    double amax = 0.0;
+    for (int64_t i = 0; i < n; ++i) if (fabs(v[i]) > amax) amax = fabs(v[i]);
+    if (amax == 0.0) {
+        for (int64_t i = 0; i < n; ++i) v[i] = 0.0;
+        return -127;
+    }
+    int e;
+    frexp(amax, &e);         /* floor(log2(amax)) = e - 1 */
+    int X = e - 1 - 8;
+    if (X < -127) X = -127;
+    if (X > 127) X = 127;
+    double sc = ldexp(1.0, X);
+    for (int64_t i = 0; i < n; ++i) v[i] = round_to_e4m3(v[i] / sc) * sc;
+    return X;
+}
+
+/* v[0..n) (n a multiple of 32) quantized block by block to MXFP8, in place;
+ * X[b] (may be NULL) receives the scale exponent of block b. */
+void orc_mxfp8_quantize(double *v, int64_t n, int32_t *X) {
+    for (int64_t b = 0; b * 32 < n; ++b) {
+        int x = mxfp8_block(v + b * 32, 32);
+        if (X) X[b] = x;
+    }
+}
+
+/* The value an expert GEMM reads under MXFP8 activations: the stored
+ * intermediate (rounded to the intermediate dtype), then quantized. */
+static void quantize_activations(const orc_desc *d, double *v, int64_t n) {
+    if (d->act_quant != ORC_AQ_MXFP8) return;
+    for (int64_t i = 0; i < n; ++i) v[i] = round_act(d->interm, v[i]);
+    orc_mxfp8_quantize(v, n, NULL);
+}
+
+/* OCP FP8 E4M3 element: (-1)^s * 2^(E-7) * (1 + m/8) for E in 1..15, (-1)^s *
+ * 2^-6 * m/8 for E = 0; S.1111.111 is NaN (there are no infinities). */
+static double e4m3_value(unsigned code) {
+    unsigned s = (code >> 7) & 1u, E = (code >> 3) & 15u, m = code & 7u;
+    if (E == 15 && m == 7) return NAN;
+    double mag = (E == 0) ? ldexp((double)m / 8.0, -6) : ldexp(1.0 + (double)m / 8.0, (int)E - 7);
+    return s ? -mag : mag;
+}
+
 /* Row r (of a [rows][K] matrix) decoded to doubles.  MXFP4 matrices are one
  * buffer: packed nibbles [rows][K/2] (low nibble = even element), then E8M0
- * scales [rows][K/32]. */
+ * scales [rows][K/32]; MXFP8 matrices: E4M3 codes [rows][K], then E8M0 scales
+ * [rows][K/32]. */
 static void load_row(const void *base, int dt, int64_t rows, int64_t K, int64_t r, double *out) {
     if (dt == ORC_F32) {
         const float *p = (const float *)base + r * K;
@@ -169,6 +255,10 @@ static void load_row(const void *base, int dt, int64_t rows, int64_t K, int64_t 
     } else if (dt == ORC_BF16) {
         const uint16_t *p = (const uint16_t *)base + r * K;
         for (int64_t c = 0; c < K; ++c) out[c] = bf16_bits_to_double(p[c]);
+    } else if (dt == ORC_MXFP8) {
+        const uint8_t *cd = (const uint8_t *)base + r * K;
+        const uint8_t *sc = (const uint8_t *)base + rows * K + r * (K / 32);
+        for (int64_t c = 0; c < K; ++c) out[c] = e4m3_value(cd[c]) * e8m0_value(sc[c / 32]);
     } else {
         const uint8_t *nib = (const uint8_t *)base + r * (K / 2);
         const uint8_t *sc = (const uint8_t *)base + rows * (K / 2) + r * (K / 32);
@@ -411,6 +501,7 @@ static void expert(const orc_desc *d, const orc_tensors *w, int64_t e, const dou
             a[i] = silu * up[i];
             if (d->mirror) a[i] = round_act(d->interm, a[i]);
         }
+        quantize_activations(d, a, F);
         free(g);
         free(up);
     } else {
@@ -485,6 +576,7 @@ int orc_forward(const orc_desc *d, const orc_tensors *w, const int64_t *tok, int
                 memcpy(z, zn, sizeof(double) * (size_t)L);
                 if (d->mirror) for (int64_t i = 0; i < L; ++i) z[i] = round_act(d->interm, z[i]);
             }
+            quantize_activations(d, z, L);
         } else {
             memcpy(z, u, sizeof(double) * (size_t)D);
         }

@@ -208,8 +208,9 @@ def test_identical_experts_make_routing_irrelevant():
 # Brute force: an independent numpy evaluation of the whole layer
 # ---------------------------------------------------------------------------
 
-def _numpy_layer(cfg, t, act_round):
-    """Plain numpy matmuls over all experts with the dense gate vector."""
+def _numpy_layer(cfg, t, act_round, aq=None):
+    """Plain numpy matmuls over all experts with the dense gate vector.
+    aq (optional): the quantizer applied to the inputs of the expert GEMMs."""
     x = t["x"].astype(np.float64)
     T = x.shape[0]
     if cfg["in_norm"] == "centered":
@@ -241,6 +242,8 @@ def _numpy_layer(cfg, t, act_round):
     if cfg.get("latent_norm", "none") == "centered":
         z = (1 + t["gamma_lat"].astype(np.float64)) * z / np.sqrt((z * z).mean(1, keepdims=True)
                                                                  + cfg["eps_latent"])
+    if aq is not None:
+        z = aq(z)
     m = np.zeros_like(z)
     for e in range(n):
         W1 = t["w1"][e].astype(np.float64)
@@ -249,6 +252,8 @@ def _numpy_layer(cfg, t, act_round):
             a = gg * scipy.special.expit(gg) * vv
         else:
             a = np.maximum(z @ W1.T, 0)
+        if aq is not None:
+            a = aq(a)
         o = a @ t["w2"][e].astype(np.float64).T
         if cfg["expert_norm"] == "input_scaled":
             s = act_round((1 + t["gamma_ex"].astype(np.float64)) * o)
@@ -614,3 +619,142 @@ def test_bruteforce_muse_bf16_small_layer():
     G, y, out = _numpy_layer(cfg, tf, bf)
     np.testing.assert_allclose(r["y"], y, rtol=1e-9, atol=1e-12)
     np.testing.assert_allclose(r["out"], out, rtol=1e-9, atol=1e-12)
+
+
+# ---------------------------------------------------------------------------
+# MXFP8 activations (OCP MX v1.0: E4M3 elements, one power-of-two scale per
+# 32 values along K, X = floor(log2 amax) - 8, round to nearest even,
+# magnitudes past 448 clamped)
+# ---------------------------------------------------------------------------
+
+def _e4m3_library(v):
+    """torch's float8_e4m3fn conversion (round to nearest even; it returns
+    NaN past 464 instead of clamping, so clamp first)."""
+    v = np.clip(np.asarray(v, np.float64), -448.0, 448.0)
+    return torch.from_numpy(v).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+
+
+def test_mxfp8_element_grid_is_e4m3():
+    # a dense sweep of one block scale: the distinct outputs are exactly the 127 non-negative finite
+    # E4M3 values (the OCP FP8 E4M3 format has 8 per binade from 2^-6 to 2^8, subnormals of 2^-9)
+    v = np.linspace(0, 448, 32 * 20000)
+    v[::32] = 448.0  # every block's max is 448: X = floor(log2 448) - 8 = 0
+    q, X = oracle.mxfp8_quantize(v)
+    assert (X == 0).all()
+    vals = np.unique(q)
+    assert len(vals) == 127 and vals[0] == 0 and vals[1] == 2.0 ** -9 and vals[-1] == 448.0
+    for e in range(-6, 9):
+        inb = vals[(vals >= 2.0 ** e) & (vals < 2.0 ** (e + 1))]
+        assert len(inb) == (7 if e == 8 else 8)
+
+
+def test_mxfp8_matches_library_rounding_and_ties():
+    rng = np.random.default_rng(3)
+    # random values whose block max is 448 (scale 1), midpoints of the E4M3 grid included
+    v = rng.uniform(-448, 448, (2000, 32))
+    v[:, 0] = 448.0
+    mids = np.array([1 + 1 / 16, 1.1875, 2.0 ** -9 * 1.5, 2.0 ** -9 * 0.5, 300.0, 272.0, 304.0, -1.0625])
+    v[:8, 1:1 + len(mids)] = mids
+    q, X = oracle.mxfp8_quantize(v)
+    assert (X == 0).all()
+    np.testing.assert_array_equal(q, _e4m3_library(v))
+    # ties go to the even mantissa: 1 + 1/16 -> 1, 1.1875 -> 1.25, 1.5 * 2^-9 -> 2^-8, 0.5 * 2^-9 -> 0
+    np.testing.assert_array_equal(q[0, 1:6], [1.0, 1.25, 2.0 ** -8, 0.0, 288.0])
+
+
+def test_mxfp8_shared_scale_closed_form():
+    rng = np.random.default_rng(4)
+    v = rng.standard_normal((500, 64)) * np.exp2(rng.integers(-20, 12, (500, 1)))
+    q, X = oracle.mxfp8_quantize(v)
+    blocks = v.reshape(500, 2, 32)
+    amax = np.abs(blocks).max(axis=2)
+    m, e = np.frexp(amax)          # amax = m * 2^e, m in [0.5, 1): floor(log2 amax) = e - 1
+    np.testing.assert_array_equal(X, e - 1 - 8)
+    # the element values are the library's E4M3 rounding of v / 2^X, and the block max lands in [256, 448]
+    sc = np.exp2(X.astype(np.float64))[:, :, None]
+    ref = _e4m3_library(blocks / sc) * sc
+    np.testing.assert_array_equal(q.reshape(500, 2, 32), ref)
+    qm = np.abs(q.reshape(500, 2, 32)).max(axis=2) / sc[:, :, 0]
+    assert ((qm >= 256) & (qm <= 448)).all()
+    # below 448 * 2^X an element moves by at most half an E4M3 spacing (2^-4 of its magnitude, or half the
+    # subnormal spacing 2^(X-10)); at or past it, it clamps to 448 * 2^X
+    Xe = np.exp2(X.repeat(32, axis=1).astype(np.float64))
+    inside = np.abs(v) < 448 * Xe
+    assert (np.abs(q - v)[inside] <= np.maximum(np.abs(v) * 2.0 ** -4, Xe * 2.0 ** -10)[inside]).all()
+    np.testing.assert_array_equal(np.abs(q)[~inside], 448 * Xe[~inside])
+
+
+def test_mxfp8_zero_block_and_idempotence():
+    v = np.zeros((3, 32))
+    v[1, 5] = -3.0
+    q, X = oracle.mxfp8_quantize(v)
+    assert X[0, 0] == -127 and (q[0] == 0).all()
+    assert X[1, 0] == 1 - 8 and q[1, 5] == -3.0 and (np.delete(q[1], 5) == 0).all()
+    rng = np.random.default_rng(5)
+    w = rng.standard_normal((100, 96))
+    q1, X1 = oracle.mxfp8_quantize(w)
+    q2, X2 = oracle.mxfp8_quantize(q1)   # already on the grid: unchanged
+    np.testing.assert_array_equal(q1, q2)
+    np.testing.assert_array_equal(X1, X2)
+
+
+def _mx_act(interm):
+    """An independent statement of the activation quantizer: the stored
+    intermediate (torch's fp16 or bf16 rounding), then the library's E4M3
+    rounding on the shared scale of each 32-block."""
+    tdt = torch.float16 if interm == "f16" else torch.bfloat16
+
+    def q(a):
+        a = torch.from_numpy(np.asarray(a, np.float64)).to(tdt).to(torch.float64).numpy()
+        b = a.reshape(a.shape[:-1] + (a.shape[-1] // 32, 32))
+        amax = np.abs(b).max(axis=-1, keepdims=True)
+        e = np.frexp(np.where(amax > 0, amax, 1.0))[1]
+        sc = np.exp2((e - 1 - 8).astype(np.float64))
+        out = np.where(amax > 0, _e4m3_library(b / sc) * sc, 0.0)
+        return out.reshape(a.shape)
+    return q
+
+
+@pytest.mark.parametrize("interm", ["f16", "bf16"])
+def test_bruteforce_mxfp8_activation_layer(interm):
+    # the quantized-activation mode through the whole layer against the numpy brute force with the
+    # quantizer applied where the expert GEMMs read: the latent z and the SwiGLU output
+    p = synthetic.small(T=7, d=128, L=64, F=64, n=8, k=2, weights="mxfp4")
+    t = dict(synthetic.layer_params(p), x=synthetic.inputs(p))
+    cfg = dict(p.cfg(), act_quant="mxfp8", interm=interm)
+    r = oracle.forward(cfg, t)
+    tf = {kk: (synthetic.bf16_to_f32(v) if v.dtype == np.uint16 else v) for kk, v in t.items()}
+    for key, rows, K in (("down_w", p.L, p.d), ("up_w", p.d, p.L), ("w1", p.n * 2 * p.F, p.L),
+                         ("w2", p.n * p.L, p.F)):
+        dec = oracle.decode_matrix(t[key], "mxfp4", rows, K)
+        tf[key] = dec.reshape((p.n, 2 * p.F, p.L) if key == "w1" else (p.n, p.L, p.F) if key == "w2" else (rows, K))
+    bf = lambda v: torch.from_numpy(np.asarray(v, np.float64)).to(torch.bfloat16).to(torch.float64).numpy()
+    G, y, out = _numpy_layer(cfg, tf, bf, aq=_mx_act(interm))
+    np.testing.assert_allclose(r["y"], y, rtol=1e-9, atol=1e-12)
+    np.testing.assert_allclose(r["out"], out, rtol=1e-9, atol=1e-12)
+    # the quantization is not a no-op: without it the layer differs
+    r0 = oracle.forward(dict(cfg, act_quant="none"), t)
+    assert np.abs(r0["y"] - r["y"]).max() > 1e-3 * np.abs(r["y"]).max()
+
+
+@pytest.mark.parametrize("E", [127, 120, 131])
+def test_mxfp8_decode_exhaustive(E):
+    # every E4M3 code against the library's float8_e4m3fn value, times the block scale 2^(E-127)
+    codes = np.arange(256, dtype=np.uint8)
+    buf = np.concatenate([codes, np.full(256 // 32, E, np.uint8)])
+    got = oracle.decode_matrix(buf, "mxfp8", 1, 256)[0]
+    ref = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).to(torch.float64).numpy() * 2.0 ** (E - 127)
+    nan = np.isnan(ref)
+    assert nan.sum() == 2 and np.isnan(got[nan]).all()
+    np.testing.assert_array_equal(got[~nan], ref[~nan])
+
+
+def test_mxfp8_quantize_then_decode_round_trip():
+    # codes made from the quantizer's own values (library encoding) decode back to them exactly
+    rng = np.random.default_rng(6)
+    v = rng.standard_normal((3, 64)) * np.exp2(rng.integers(-10, 10, (3, 1)))
+    q, X = oracle.mxfp8_quantize(v)
+    sc = np.exp2(X.repeat(32, axis=1).astype(np.float64))
+    codes = torch.from_numpy(q / sc).to(torch.float8_e4m3fn).view(torch.uint8).numpy().reshape(-1)
+    buf = np.concatenate([codes, (X + 127).astype(np.uint8).reshape(-1)])
+    np.testing.assert_array_equal(oracle.decode_matrix(buf, "mxfp8", 3, 64), q)
