@@ -27,6 +27,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E
 BF16_PEAK_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+FP8_PEAK_TFLOPS = 5000.0     # MI355X dense fp8 MFMA (fp8 x fp4 runs at the fp8 rate)
 
 
 def log(*a):
@@ -52,7 +53,8 @@ def layer_flops(p) -> dict:
     """FLOPs of one pass over all chunks of preset p."""
     T = p.chunk_T * p.chunks
     per_tok = 2 * p.d * p.n + 2 * p.d * p.L + p.k * (2 * p.L * 2 * p.F + 2 * p.F * p.L) + 2 * p.L * p.d
-    return {"total": T * per_tok, "gemm1": T * p.k * 2 * p.L * 2 * p.F}
+    return {"total": T * per_tok, "gemm1": T * p.k * 2 * p.L * 2 * p.F,
+            "experts": T * p.k * (2 * p.L * 2 * p.F + 2 * p.F * p.L)}
 
 
 def recorded_traffic(name: str):
@@ -66,6 +68,20 @@ def recorded_traffic(name: str):
     if csrc_hash() != rec.get("source_sha256_16"):
         return None
     return rec["traffic_bytes"]
+
+
+def recorded_mfma_counters(workload: str):
+    """Per-kernel MFMA-busy share, clock and TFLOP/s of the prefill GEMMs from
+    the committed rocprofv3 counter record, or None when the kernel sources
+    changed since the counters were taken."""
+    path = os.path.join(ROOT, "profiles", "prefill_T8192_mfma_counters.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    if csrc_hash() != rec.get("source_sha256_16"):
+        return None
+    return {r["role"]: {"mfma_busy": r["mfma_busy"], "clock_GHz": r["clock_GHz"], "TFLOPs": r["TFLOPs"]}
+            for r in rec[workload]}
 
 
 def cpu_model() -> str:
@@ -97,7 +113,9 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--prefill-steps", type=int, default=10)
     ap.add_argument("--no-prefill", action="store_true")
-    ap.add_argument("--only-prefill", action="store_true", help="skip the decode workload (profiling runs)")
+    ap.add_argument("--only-prefill", action="store_true", help="only the prefill workload (profiling runs)")
+    ap.add_argument("--only", default=None, metavar="PRESET",
+                    help="only the named workload preset (c2, c3, c4c, c4i, c4q, m1, m2), for profiling runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the cache-flushed decode timing and the skewed (T=16384) and MXFP4 (4 x 8192) workloads")
@@ -155,7 +173,7 @@ def main():
                              eps_in=pr.eps_in, eps_expert=pr.eps_expert, interm=pr.interm, router_fn=pr.router_fn,
                              out_mult=pr.out_mult, routed_scale=pr.routed_scale, latent_norm=pr.latent_norm,
                              eps_latent=pr.eps_latent, out_norm=pr.out_norm, eps_out=pr.eps_out, res_tau=pr.res_tau,
-                             res_floor=pr.res_floor)
+                             res_floor=pr.res_floor, act_quant=pr.act_quant)
 
     stream = torch.cuda.current_stream()
 
@@ -257,7 +275,9 @@ def main():
 
     # The bf16 checkpoint as given (no conversion), decode and prefill, before the fp16 format is made
     bf16_ckpt = None
-    if wfmt == "f16" and not args.no_extra and not args.only_prefill:
+    if args.only_prefill:
+        args.only = "c2"
+    if wfmt == "f16" and not args.no_extra and not args.only:
         rb = run_workload(p, args.steps, args.warmup, wf="bf16")
         bf16_ckpt = {"decode_T64": {"ms_per_step": round(rb["ms"], 4),
                                     "tokens_per_s": round(p.chunk_T / (rb["ms"] * 1e-3), 1),
@@ -276,12 +296,24 @@ def main():
     if wfmt == "f16":
         to_f16_format()
 
-    if args.only_prefill:
-        p2 = synthetic.PRESETS["c2"]
-        r2 = run_workload(p2, args.prefill_steps, 2)
-        tf = layer_flops(p2)["total"] / (r2["ms"] * 1e-3) / 1e12
-        log("prefill T=%d: %.3f ms/step, %.1f TFLOP/s; stages %s" % (
-            p2.chunk_T, r2["ms"], tf, {k: round(v, 4) for k, v in r2["stages"].items()}))
+    def preset_gains(pr, dev_w):
+        gv = {k: to_dev(v) for k, v in synthetic.gains(pr).items()}
+        return {"router_bias": gv.get("bias"), "gamma_in": gv.get("gamma_in"), "gamma_expert": gv.get("gamma_ex"),
+                "res_gate": gv.get("gate"), "gamma_latent": gv.get("gamma_lat"), "gamma_out": gv.get("gamma_out")}
+
+    if args.only:
+        # one workload alone (profiling runs): the preset's weight format and parameter vectors
+        po = synthetic.PRESETS[args.only]
+        Wo, wfo = W, wfmt
+        if po.weights == "mxfp4":
+            W.clear()  # the bf16 layer is not needed: free its 24 GB first
+            torch.cuda.empty_cache()
+            Wo = {k: to_dev(v) for k, v in synthetic.layer_params(po).items()}
+            wfo = "mxfp4"
+        ro = run_workload(po, args.prefill_steps, 2, Wd=Wo, gd=preset_gains(po, Wo), wf=wfo)
+        tf = layer_flops(po)["total"] / (ro["ms"] * 1e-3) / 1e12
+        log("%s (T=%d x %d): %.3f ms/step, %.1f TFLOP/s; stages %s" % (
+            args.only, po.chunk_T, po.chunks, ro["ms"], tf, {k: round(v, 4) for k, v in ro["stages"].items()}))
         return
 
     # ---- decode (headline) ----
@@ -363,7 +395,8 @@ def main():
                          "traffic": recorded_traffic("prefill_T8192_gemm1_traffic.json"),
                          "mfma_view": {"flops": fl2["gemm1"], "achieved_TFLOPs": round(g1_tf, 1),
                                        "peak_TFLOPs": BF16_PEAK_TFLOPS,
-                                       "frac": round(g1_tf / BF16_PEAK_TFLOPS, 4)}}}
+                                       "frac": round(g1_tf / BF16_PEAK_TFLOPS, 4),
+                                       "counters": recorded_mfma_counters("c2")}}}
 
     # ---- the skewed and MXFP4 workloads ----
     def report(pr, rr, label):
@@ -395,6 +428,17 @@ def main():
             g4 = {"router_bias": None, "gamma_in": W4["gamma_in"], "gamma_expert": W4["gamma_ex"], "res_gate": W4["gate"]}
             result["mxfp4"][p4.in_norm] = report(p4, run_workload(p4, 3, 1, Wd=W4, gd=g4, wf="mxfp4"),
                                                  "MXFP4 weights, 4 chunks of T=8192, input norm %s" % p4.in_norm)
+        # the same workload with MXFP8 activations at the expert GEMMs (the scaled fp8 x fp4 MFMA)
+        p4 = synthetic.PRESETS["c4q"]
+        g4 = {"router_bias": None, "gamma_in": W4["gamma_in"], "gamma_expert": W4["gamma_ex"], "res_gate": W4["gate"]}
+        rq = report(p4, run_workload(p4, 3, 1, Wd=W4, gd=g4, wf="mxfp4"),
+                    "MXFP4 weights and MXFP8 expert-GEMM activations, 4 chunks of T=8192, input norm centered")
+        flq = layer_flops(p4)
+        rq["frac_fp8_mfma"] = round(rq["TFLOPs"] / FP8_PEAK_TFLOPS, 4)
+        rq["note"] = ("TFLOPs and frac_mfma count every FLOP of the layer against the bf16 peak; the expert GEMMs "
+                      "(%.0f%% of the FLOPs) run on the fp8 x fp4 MFMA, whose dense peak is %.0f TFLOP/s" % (
+                          100.0 * flq["experts"] / flq["total"], FP8_PEAK_TFLOPS))
+        result["mxfp4"]["mxfp8_activations"] = rq
         del W4
         torch.cuda.empty_cache()
 

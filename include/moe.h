@@ -67,6 +67,7 @@ enum { MOE_NORM_NONE = 0, MOE_NORM_CENTERED = 1, MOE_NORM_INPUT_SCALED = 2 };
 enum { MOE_EXPERT_RELU2 = 0, MOE_EXPERT_SWIGLU3 = 1 };
 enum { MOE_RES_NONE = 0, MOE_RES_LINEAR = 1, MOE_RES_MUSE = 2 };
 enum { MOE_ROUTER_SOFTMAX = 0, MOE_ROUTER_SIGMOID = 1 };
+enum { MOE_AQ_NONE = 0, MOE_AQ_MXFP8 = 1 };
 
 /* Number of timed stages; stage s is bracketed by stage_events[2s], [2s+1]. */
 enum {
@@ -148,6 +149,17 @@ enum {
  *                path only.
  *   res_tau, res_floor  MOE_RES_MUSE temperature (> 0; the page's default
  *                is 0.3) and floor (>= 0; 1e-3 on the page)
+ *   act_quant    MOE_AQ_NONE (0), or MOE_AQ_MXFP8: the two expert GEMMs read
+ *                MXFP8 activations (OCP MX v1.0: E4M3 elements, one E8M0
+ *                scale 2^X per 32 consecutive values along K, X =
+ *                floor(log2 max|v|) - 8, round to nearest even, magnitudes
+ *                past 448 clamped), quantized from the stored latent z and
+ *                the stored SwiGLU output (interm_dtype); with MXFP4 weights
+ *                they run on the scaled fp8 x fp4 MFMA.  The router, the
+ *                projections, norms and combine keep their precision.
+ *                Needs weight_dtype MOE_DT_MXFP4 (the quantized-activation
+ *                path of a 4-bit checkpoint, hefu.hk "Welcome Muse Spark
+ *                Open", "Mixture of Experts Architecture").
  */
 typedef struct {
     int64_t T;
@@ -176,6 +188,7 @@ typedef struct {
     float eps_out;
     float res_tau;
     float res_floor;
+    int32_t act_quant;
 } moe_desc;
 
 /* FP32 parameter vectors (device pointers; NULL where the stage is off).
@@ -221,7 +234,11 @@ typedef struct {
  *                          slices of the router GEMM already added, in
  *                          slice order)
  *   u        [T][d] act_dtype  the branch input the router and the
- *                          down-projection read: x, or its input norm */
+ *                          down-projection read: x, or its input norm
+ *   zq, actq (act_quant = MXFP8) the MXFP8 forms of z [T][L] and of the
+ *                          SwiGLU output [T*k][F] (perm order), each one
+ *                          buffer: E4M3 codes [rows][K], then E8M0 scales
+ *                          [rows][K/32] */
 typedef struct {
     int32_t *topk_idx;
     float *topk_w;
@@ -239,6 +256,8 @@ typedef struct {
     void **stage_events;
     float *logits;
     void *u;
+    void *zq;
+    void *actq;
 } moe_debug;
 
 /* Human-readable text of a moe_status (static storage). */

@@ -74,7 +74,7 @@ def lib():
         _lib = ctypes.CDLL(path)
         vp, i64, i32, dbl = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int32, ctypes.c_double
         _lib.orc_forward.argtypes = [ctypes.POINTER(_Desc), ctypes.POINTER(_Tensors), vp, i64, vp, i32,
-                                     vp, vp, vp, vp, vp, vp, vp]
+                                     vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp]
         _lib.orc_permute.argtypes = [vp, i64, i64, i64, vp, vp, vp, vp, vp]
         _lib.orc_rms_centered.argtypes = [vp, vp, i64, dbl, vp]
         _lib.orc_rms_input_scaled.argtypes = [vp, vp, i64, dbl, ctypes.c_int, vp]
@@ -133,7 +133,8 @@ _KEEP = []
 
 
 def forward(cfg: dict, t: dict, tokens=None, forced=None, dense: bool = False, mirror: bool = False,
-            want_outputs: bool = True) -> dict:
+            want_outputs: bool = True, want_z: bool = False, forced_z=None, want_a: bool = False,
+            forced_a=None) -> dict:
     """Run the oracle on host arrays.
 
     t: dict with numpy arrays (raw stored forms: uint16 bf16 bits, float32,
@@ -141,6 +142,10 @@ def forward(cfg: dict, t: dict, tokens=None, forced=None, dense: bool = False, m
     optional float32 bias, gamma_in, gamma_ex, gate, gamma_lat, gamma_out.
     tokens: int64 array of token ids (None: all T rows of x).
     forced: int32 [ntok][k] expert ids (None: route).
+    forced_z: float64 [ntok][Dx] expert-space inputs to use (None: compute).
+    want_z: also return z, the expert-space input the experts read.
+    forced_a: float64 [ntok][k][F] hidden activations of the selected experts
+    to use (None: compute); want_a: also return a, the ones the experts read.
     Outputs: logits, idx, w, margin; with want_outputs also y (the branch
     output entering the residual gate), out, and ypre (the branch output
     before the output norm).
@@ -169,9 +174,17 @@ def forward(cfg: dict, t: dict, tokens=None, forced=None, dense: bool = False, m
         res["out"] = np.zeros((ntok, d), np.float64)
         res["ypre"] = np.zeros((ntok, d), np.float64)
     fz = None if forced is None else _c(forced, np.int32)
+    Dx = cfg["L"] if cfg["L"] else cfg["d"]
+    if want_z:
+        res["z"] = np.zeros((ntok, Dx), np.float64)
+    fzz = None if forced_z is None else _c(forced_z, np.float64)
+    if want_a:
+        res["a"] = np.zeros((ntok, k, cfg["F"]), np.float64)
+    faa = None if forced_a is None else _c(forced_a, np.float64)
     rc = lib().orc_forward(ctypes.byref(desc), ctypes.byref(tens), _p(tok), ntok, _p(fz), int(dense),
                            _p(res.get("y")), _p(res.get("out")), _p(res["logits"]), _p(res["idx"]),
-                           _p(res["w"]), _p(res["margin"]), _p(res.get("ypre")))
+                           _p(res["w"]), _p(res["margin"]), _p(res.get("ypre")), _p(res.get("z")), _p(fzz),
+                           _p(res.get("a")), _p(faa))
     assert rc == 0
     res["tokens"] = tok
     return res

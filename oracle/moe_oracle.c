@@ -484,13 +484,19 @@ void orc_muse_gate_coeffs(double g, double tau, double floor_, double *alpha, do
 }
 
 /* Expert e applied to its input v (z for SwiGLU experts, u for ReLU
- * experts); o receives the expert output (length = L, or d without latent). */
-static void expert(const orc_desc *d, const orc_tensors *w, int64_t e, const double *v, double *o) {
+ * experts); o receives the expert output (length = L, or d without latent).
+ * aout (may be NULL) receives the hidden activation a the second matrix
+ * reads; a_given (may be NULL) is used as that activation instead of
+ * computing it. */
+static void expert(const orc_desc *d, const orc_tensors *w, int64_t e, const double *v, double *o, double *aout,
+                   const double *a_given) {
     int64_t F = d->F;
     int64_t Kin = d->L ? d->L : d->d;   /* expert input width */
     int64_t Dout = Kin;                  /* expert output width */
     double *a = (double *)malloc(sizeof(double) * (size_t)F);
-    if (d->kind == ORC_SWIGLU) {
+    if (a_given) {
+        memcpy(a, a_given, sizeof(double) * (size_t)F);
+    } else if (d->kind == ORC_SWIGLU) {
         double *g = (double *)malloc(sizeof(double) * (size_t)F);
         double *up = (double *)malloc(sizeof(double) * (size_t)F);
         int64_t rows1 = d->n * 2 * F;
@@ -511,6 +517,7 @@ static void expert(const orc_desc *d, const orc_tensors *w, int64_t e, const dou
             if (d->mirror) a[i] = round_act(d->interm, a[i]);
         }
     }
+    if (aout) memcpy(aout, a, sizeof(double) * (size_t)F);
     matvec(w->w2, d->wdt, d->n * Dout, F, e * Dout, Dout, a, o);
     free(a);
 }
@@ -536,13 +543,23 @@ static void expert_norm(const orc_desc *d, const orc_tensors *w, const double *o
  *   idx   [ntok][k]  selected experts, selection order
  *   wts   [ntok][k]  their gate weights
  *   margin[ntok]     k-th minus (k+1)-th selection score
+ *   zout  [ntok][Dx] the expert-space input the experts read (the latent z
+ *                    after the optional pre-norm and activation quantizer)
  * forced: [ntok][k] expert ids to use instead of the top-k (NULL: route).
+ * forced_z: [ntok][Dx] expert-space inputs to use instead of computing them
+ *        (NULL: compute), e.g. a device's quantized latent, the way forced
+ *        evaluates a token on given experts.
+ *   aout  [ntok][k][F] the hidden activation each selected expert's second
+ *                    matrix reads (after the activation quantizer)
+ * forced_a: [ntok][k][F] hidden activations to use instead of computing them
+ *        (NULL: compute; not with dense).
  * dense: 1 evaluates every expert and sums G_e * N(E_e) over all n experts
  *        with the dense gate vector (zeros included): the brute-force form.
  */
 int orc_forward(const orc_desc *d, const orc_tensors *w, const int64_t *tok, int64_t ntok,
                 const int32_t *forced, int32_t dense, double *y, double *out, float *logits,
-                int32_t *idx, double *wts, double *margin, double *ypre) {
+                int32_t *idx, double *wts, double *margin, double *ypre, double *zout,
+                const double *forced_z, double *aout, const double *forced_a) {
     int64_t D = d->d, L = d->L, k = d->k, n = d->n;
     int64_t Dx = L ? L : D; /* width of the expert space */
     double *h = (double *)malloc(sizeof(double) * (size_t)D);
@@ -565,9 +582,11 @@ int orc_forward(const orc_desc *d, const orc_tensors *w, const int64_t *tok, int
         if (idx) memcpy(idx + q * k, sel, sizeof(int32_t) * (size_t)k);
         if (wts) memcpy(wts + q * k, wt, sizeof(double) * (size_t)k);
         if (margin) margin[q] = mg;
-        if (!y && !out && !ypre) continue;
-        /* expert-space input */
-        if (L) {
+        if (!y && !out && !ypre && !zout && !aout) continue;
+        /* expert-space input (or the given one) */
+        if (forced_z) {
+            memcpy(z, forced_z + q * Dx, sizeof(double) * (size_t)Dx);
+        } else if (L) {
             matvec(w->down_w, d->wdt, L, D, 0, L, u, z);
             if (d->mirror) for (int64_t i = 0; i < L; ++i) z[i] = round_act(d->interm, z[i]);
             if (d->lat_norm != ORC_NORM_NONE) {
@@ -580,18 +599,20 @@ int orc_forward(const orc_desc *d, const orc_tensors *w, const int64_t *tok, int
         } else {
             memcpy(z, u, sizeof(double) * (size_t)D);
         }
+        if (zout) memcpy(zout + q * Dx, z, sizeof(double) * (size_t)Dx);
         for (int64_t i = 0; i < Dx; ++i) m[i] = 0.0;
         if (dense) {
             for (int64_t e = 0; e < n; ++e) G[e] = 0.0;
             for (int64_t j = 0; j < k; ++j) G[sel[j]] = wt[j];
             for (int64_t e = 0; e < n; ++e) {
-                expert(d, w, e, z, o);
+                expert(d, w, e, z, o, NULL, NULL);
                 expert_norm(d, w, o, Dx, nr);
                 for (int64_t i = 0; i < Dx; ++i) m[i] += G[e] * nr[i];
             }
         } else {
             for (int64_t j = 0; j < k; ++j) {
-                expert(d, w, sel[j], z, o);
+                expert(d, w, sel[j], z, o, aout ? aout + (q * k + j) * d->F : NULL,
+                       forced_a ? forced_a + (q * k + j) * d->F : NULL);
                 expert_norm(d, w, o, Dx, nr);
                 for (int64_t i = 0; i < Dx; ++i) m[i] += wt[j] * nr[i];
             }

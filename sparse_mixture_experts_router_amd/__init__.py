@@ -27,6 +27,7 @@ NORM = {"none": 0, "centered": 1, "input_scaled": 2}
 KIND = {"relu2": 0, "swiglu3": 1}
 RES = {"none": 0, "linear": 1, "muse": 2}
 ROUTER = {"softmax": 0, "sigmoid": 1}
+ACT_QUANT = {"none": 0, "mxfp8": 1}
 STAGES = ["in_norm", "router", "topk", "permute", "down", "gemm1", "gemm2", "combine", "up", "resgate"]
 GAINS = ("router_bias", "gamma_in", "gamma_expert", "res_gate", "gamma_latent", "gamma_out")
 
@@ -46,7 +47,8 @@ class moe_desc(ctypes.Structure):
                 ("eps_expert", ctypes.c_float), ("interm_dtype", ctypes.c_int32), ("router_fn", ctypes.c_int32),
                 ("router_out_mult", ctypes.c_float), ("routed_scale", ctypes.c_float),
                 ("latent_norm", ctypes.c_int32), ("eps_latent", ctypes.c_float), ("out_norm", ctypes.c_int32),
-                ("eps_out", ctypes.c_float), ("res_tau", ctypes.c_float), ("res_floor", ctypes.c_float)]
+                ("eps_out", ctypes.c_float), ("res_tau", ctypes.c_float), ("res_floor", ctypes.c_float),
+                ("act_quant", ctypes.c_int32)]
 
 
 class moe_gains(ctypes.Structure):
@@ -58,7 +60,8 @@ class moe_debug(ctypes.Structure):
                 ("expert_offsets", ctypes.c_void_p), ("perm_tok", ctypes.c_void_p), ("perm_slot", ctypes.c_void_p),
                 ("y", ctypes.c_void_p), ("pos", ctypes.c_void_p), ("z", ctypes.c_void_p), ("act", ctypes.c_void_p),
                 ("S", ctypes.c_void_p), ("ssq", ctypes.c_void_p), ("m", ctypes.c_void_p),
-                ("stage_events", ctypes.c_void_p), ("logits", ctypes.c_void_p), ("u", ctypes.c_void_p)]
+                ("stage_events", ctypes.c_void_p), ("logits", ctypes.c_void_p), ("u", ctypes.c_void_p),
+                ("zq", ctypes.c_void_p), ("actq", ctypes.c_void_p)]
 
 
 _lib = None
@@ -100,7 +103,7 @@ def make_desc(T, d_model, d_latent, n_experts, top_k, d_ff, expert_kind="swiglu3
               weights="bf16", in_norm="none", expert_norm="none", res_gate="none", bias_in_weights=0,
               eps_in=1e-5, eps_expert=1e-6, interm="f16", router_fn="softmax", out_mult=1.0, routed_scale=1.0,
               latent_norm="none", eps_latent=1e-5, out_norm="none", eps_out=1e-5, res_tau=0.3,
-              res_floor=1e-3) -> moe_desc:
+              res_floor=1e-3, act_quant="none") -> moe_desc:
     return moe_desc(T=T, d_model=d_model, d_latent=d_latent, n_experts=n_experts, top_k=top_k, d_ff=d_ff,
                     expert_kind=KIND[expert_kind], act_dtype=DT[act], router_dtype=DT[router],
                     weight_dtype=DT[weights], in_norm=NORM[in_norm], expert_norm=NORM[expert_norm],
@@ -108,7 +111,7 @@ def make_desc(T, d_model, d_latent, n_experts, top_k, d_ff, expert_kind="swiglu3
                     eps_expert=eps_expert, interm_dtype=DT[interm], router_fn=ROUTER[router_fn],
                     router_out_mult=out_mult, routed_scale=routed_scale, latent_norm=NORM[latent_norm],
                     eps_latent=eps_latent, out_norm=NORM[out_norm], eps_out=eps_out, res_tau=res_tau,
-                    res_floor=res_floor)
+                    res_floor=res_floor, act_quant=ACT_QUANT[act_quant])
 
 
 def moe_error_string(code: int) -> str:

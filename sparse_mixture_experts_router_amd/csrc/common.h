@@ -34,10 +34,11 @@ __device__ __forceinline__ bf16x8_t as_bf16x8(uint4 v) { return __builtin_bit_ca
 // D(16x16, fp32) += A(16x32) * B(32x16), bf16 or fp16 inputs.
 // Lane l supplies A[l%16][8*(l/16) .. +8) and B[8*(l/16) .. +8)[l%16]
 // (any permutation of k shared by A and B gives the same sum) and receives
-// D[4*(l/16) + r][l%16] in element r.
+// D[4*(l/16) + r][l%16] in element r.  ACT_Q8 operands are decoded to bf16
+// before they reach an MFMA of this shape.
 template <int AT>
 __device__ __forceinline__ floatx4_t mfma16x16x32(uint4 a, uint4 b, floatx4_t c) {
-    if constexpr (AT != ACT_BF16)
+    if constexpr (AT != ACT_BF16 && AT != ACT_Q8)
         return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, a), __builtin_bit_cast(f16x8_t, b),
                                                       c, 0, 0, 0);
     else
@@ -97,7 +98,7 @@ __device__ __forceinline__ uint4 weight_bf16_as(uint4 v) {
 // bf16 or fp16 (exact whenever the product is representable).
 template <int AT>
 __device__ __forceinline__ uint4 mxfp4x8_to_act(uint32_t codes, uint32_t e8m0) {
-    static_assert(AT == ACT_BF16 || AT == ACT_F16, "MXFP4 weights are decoded to bf16 or fp16");
+    static_assert(AT == ACT_BF16 || AT == ACT_F16 || AT == ACT_Q8, "MXFP4 weights are decoded to bf16 or fp16");
     float scale = e8m0 ? __uint_as_float(e8m0 << 23) : __uint_as_float(0x00400000u);
     uint4 r;
     if constexpr (AT == ACT_F16) {
@@ -112,6 +113,57 @@ __device__ __forceinline__ uint4 mxfp4x8_to_act(uint32_t codes, uint32_t e8m0) {
         r.w = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(codes, scale, 3));
     }
     return r;
+}
+
+// ---------------------------------------------------------------------------
+// MXFP8 activations (OCP Microscaling Formats (MX) v1.0, MXFP8 with E4M3
+// elements): 32 consecutive values along K share one E8M0 scale 2^X.
+// ---------------------------------------------------------------------------
+
+// E4M3 code of w (an exact fp32 value, |w| < 2^9): nearest E4M3 value, ties
+// to even, magnitudes from 448 (the largest finite E4M3 value) up clamped to
+// 448.  Normal results (|w| >= 2^-6) keep the top 3 mantissa bits after a
+// round-to-nearest-even carry on the fp32 bits (a carry into the exponent is
+// the next binade); below 2^-6 the E4M3 values are the multiples of 2^-9, so
+// the code is w * 2^9 rounded to an integer (8 is the code of 2^-6).
+__device__ __forceinline__ uint32_t e4m3_code(float w) {
+    const uint32_t b = __float_as_uint(w);
+    const uint32_t sgn = (b >> 24) & 0x80u;
+    const uint32_t a = b & 0x7fffffffu;
+    uint32_t c;
+    if (a >= 0x43e00000u) c = 0x7eu;  // 448
+    else if (a >= 0x3c800000u) c = ((a + 0x7ffffu + ((a >> 20) & 1u)) >> 20) - ((127u - 7u) << 3);
+    else c = (uint32_t)__builtin_rintf(__uint_as_float(a) * 512.0f);
+    return sgn | c;
+}
+
+// The shared exponent of a block from its largest magnitude: X =
+// floor(log2 amax) - 8, clamped to [-127, 127]; returned as the E8M0 code
+// X + 127 (0 for an all-zero block).  amax is a finite fp32 value.
+__device__ __forceinline__ uint32_t mx8_scale_code(float amax) {
+    const uint32_t e = __float_as_uint(amax) >> 23;  // biased exponent (amax >= 0)
+    if (e == 0) return 0u;                           // zero (or an fp32 subnormal): the smallest scale
+    const int x = (int)e - 127 - 8;
+    return (uint32_t)(x < -127 ? 0 : x + 127);
+}
+
+// 2^-X for an E8M0 code X + 127 in 0..246 (the codes the quantizer makes:
+// X <= 119 for a finite fp32 block maximum), a normal fp32 value.
+__device__ __forceinline__ float mx8_inv_scale(uint32_t code) { return __uint_as_float((254u - code) << 23); }
+
+// 2^(E-127) as an fp32 value (E = 0 gives the subnormal 2^-127).
+__device__ __forceinline__ float e8m0_value(uint32_t e8m0) {
+    return e8m0 ? __uint_as_float(e8m0 << 23) : __uint_as_float(0x00400000u);
+}
+
+// Sixteen E4M3 codes (one uint4, lowest byte first) times 2^(E-127) -> sixteen
+// bf16 (two uint4), exact: an E4M3 value has 4 significant bits.
+__device__ __forceinline__ void mxfp8x16_to_bf16(uint4 codes, uint32_t e8m0, uint4 &lo, uint4 &hi) {
+    const float sc = e8m0_value(e8m0);
+#define MOE_CV8(w, upper) __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((w), sc, (upper)))
+    lo = make_uint4(MOE_CV8(codes.x, false), MOE_CV8(codes.x, true), MOE_CV8(codes.y, false), MOE_CV8(codes.y, true));
+    hi = make_uint4(MOE_CV8(codes.z, false), MOE_CV8(codes.z, true), MOE_CV8(codes.w, false), MOE_CV8(codes.w, true));
+#undef MOE_CV8
 }
 
 // silu(t) = t / (1 + e^-t): `silu` with the accurate exponential and an

@@ -12,8 +12,11 @@ namespace moe {
 // Operand types of an MFMA GEMM (template parameter AT) and storage types of
 // activations (OT): bf16 activations with bf16 weights; fp16 activations
 // with bf16 or MXFP4 weights converted to fp16 as they are read; fp16
-// activations with weights already stored as fp16 (AT only).
-enum ActType : int { ACT_BF16 = 0, ACT_F16 = 1, ACT_F16_W16 = 2 };
+// activations with weights already stored as fp16 (AT only); MXFP8
+// activations (E4M3 codes with one E8M0 scale per 32 along K) with MXFP4
+// weights (AT only): the scaled fp8 x fp4 MFMA on large tiles, both operands
+// decoded to bf16 (exactly) on the streaming kernel.
+enum ActType : int { ACT_BF16 = 0, ACT_F16 = 1, ACT_F16_W16 = 2, ACT_Q8 = 3 };
 
 enum Epi : int {
     EPI_F32 = 0,     // C[p][n] = acc (fp32)
@@ -63,6 +66,11 @@ struct GemmArgs {
     // equal slices (each a multiple of 512), slice s adding its partial sums
     // into plane s of C ([ksplit][M][ldc]); 0 or 1 = no split
     int32_t ksplit;
+    // ACT_Q8: the A rows as E4M3 codes [rows][K] (row stride K bytes) and their
+    // E8M0 scales [rows][K/32], row-indexed like A (gathered through a_gather
+    // or contiguous); A itself is not read
+    const uint8_t *A8;
+    const uint8_t *A8s;
 };
 
 constexpr int kTileBM = 256;      // rows per tile of the large-tile kernel (and of its grouped lists)
@@ -82,6 +90,14 @@ hipError_t launch_down_gemm(const GemmArgs &a, int path, bool mx, int ot, hipStr
 hipError_t launch_gemm1(const GemmArgs &a, int path, bool mx, int at, hipStream_t s);
 // Expert GEMM2: grouped, A = act in `at`; EPI_NORM (bf16 S + partial sums) or EPI_ACT with bf16 S.
 hipError_t launch_gemm2(const GemmArgs &a, int path, bool mx, int at, bool norm, hipStream_t s);
+// Expert GEMM1 + SwiGLU and GEMM2 on MXFP8 activations (A8, A8s) and MXFP4
+// weights; GEMM1's output in `ot` (ACT_F16 / ACT_BF16), GEMM2's as launch_gemm2.
+hipError_t launch_gemm1_q8(const GemmArgs &a, int path, int ot, hipStream_t s);
+hipError_t launch_gemm2_q8(const GemmArgs &a, int path, bool norm, hipStream_t s);
+// MXFP8 quantization of 16-bit activation rows (ACT_BF16 or ACT_F16 storage
+// `it`): x [rows][K] (K % 32 == 0) -> E4M3 codes q [rows][K], then E8M0 scales
+// [rows][K/32] at q + rows * K (one buffer, the layout of an MXFP4 matrix).
+hipError_t launch_mxfp8_rows(const uint16_t *x, int64_t rows, int64_t K, int it, uint8_t *q, hipStream_t s);
 // Up-projection: dense, A = m in `at`; epi = EPI_RESID, EPI_F32, or EPI_NORM
 // (bf16 (1 + gamma) y and per-16-column sums of squares for the output norm).
 hipError_t launch_up_gemm(const GemmArgs &a, int path, bool mx, int at, int epi, hipStream_t s);

@@ -117,6 +117,7 @@ struct StreamFrag {
 template <int MB, int NB, bool MX, int AT>
 __device__ __forceinline__ void stream_load(StreamFrag<MB, NB> &f, const uint8_t *const bptr[NB],
                                             const uint8_t *const bscale[NB], const uint16_t *const aptr[MB],
+                                            const uint8_t *const a8ptr[MB], const uint8_t *const a8scale[MB],
                                             int64_t kk) {
 #pragma unroll
     for (int c = 0; c < NB; ++c) {
@@ -135,7 +136,18 @@ __device__ __forceinline__ void stream_load(StreamFrag<MB, NB> &f, const uint8_t
     }
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
-        if (aptr[m]) {
+        if constexpr (AT == ACT_Q8) {
+            // 32 E4M3 codes of the lane's block and its scale, decoded to bf16
+            if (a8ptr[m]) {
+                const uint4 *p = (const uint4 *)(a8ptr[m] + kk);
+                const uint32_t sc = a8scale[m][kk >> 5];
+                mxfp8x16_to_bf16(p[0], sc, f.a[m][0], f.a[m][1]);
+                mxfp8x16_to_bf16(p[1], sc, f.a[m][2], f.a[m][3]);
+            } else {
+#pragma unroll
+                for (int s = 0; s < 4; ++s) f.a[m][s] = make_uint4(0, 0, 0, 0);
+            }
+        } else if (aptr[m]) {
             const uint4 *p = (const uint4 *)(aptr[m] + kk);
 #pragma unroll
             for (int s = 0; s < 4; ++s) f.a[m][s] = p[s];
@@ -529,15 +541,24 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
             }
         }
         const uint16_t *aptr[MB];
+        const uint8_t *a8ptr[MB], *a8scale[MB];
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
             const int row = m * 16 + li;
             if (row < rt.mcount) {
                 int64_t p = rt.p0 + row;
                 int64_t arow = a.a_gather ? (int64_t)a.a_gather[p] : p;
-                aptr[m] = a.A + arow * a.lda + lg * 32;
+                if constexpr (AT == ACT_Q8) {
+                    aptr[m] = nullptr;
+                    a8ptr[m] = a.A8 + arow * K + lg * 32;
+                    a8scale[m] = a.A8s + arow * (K / 32) + lg;
+                } else {
+                    aptr[m] = a.A + arow * a.lda + lg * 32;
+                    a8ptr[m] = a8scale[m] = nullptr;
+                }
             } else {
                 aptr[m] = nullptr;
+                a8ptr[m] = a8scale[m] = nullptr;
             }
         }
 
@@ -548,9 +569,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
             for (int c = 0; c < NB; ++c) acc[m][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
         StreamFrag<MB, NB> cur, nxt;
-        stream_load<MB, NB, MX, AT>(cur, bptr, bscale, aptr, kbeg);
+        stream_load<MB, NB, MX, AT>(cur, bptr, bscale, aptr, a8ptr, a8scale, kbeg);
         for (int64_t kk = kbeg; kk < kend; kk += 128) {
-            if (kk + 128 < kend) stream_load<MB, NB, MX, AT>(nxt, bptr, bscale, aptr, kk + 128);
+            if (kk + 128 < kend) stream_load<MB, NB, MX, AT>(nxt, bptr, bscale, aptr, a8ptr, a8scale, kk + 128);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -1274,6 +1295,349 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs &a, const RowTile &r
     }
 }
 
+// ---------------------------------------------------------------------------
+// Large tiles on MXFP8 activations x MXFP4 weights (ACT_Q8): the scaled MFMA
+// v_mfma_scale_f32_32x32x64_f8f6f4 with operand a = 32 weight rows of E2M1
+// codes and operand b = 32 activation rows of E4M3 codes (the swap keeps the
+// accumulator layout, and so the epilogues, of the bf16 tiles); each lane
+// gives 32 consecutive K values of one row of each operand and the E8M0 scale
+// of that 32-block.  The products are exact and accumulate in fp32, so the
+// tile computes what the bf16 tiles compute on the dequantised values, up to
+// the order of the fp32 sums.
+//
+// K advances in steps of 128: a step of an activation row is 128 E4M3 bytes
+// (an LDS row like a bf16 K pair, same swizzle and DMA pattern), a step of a
+// weight row 64 bytes of E2M1 codes, and each row's four E8M0 scale bytes of
+// the step are one 32-bit word.  Activations double-buffer, weights cycle
+// through three slots (the ring of the bf16 tiles); every slot holds its
+// rows' scale words after the codes, padded to whole 64-row loads so every
+// wave issues the same loads.  A step runs as two 64-K sub-steps, the reads
+// of one overlapping the MFMAs of the other.
+// ---------------------------------------------------------------------------
+
+constexpr int kQ8BK = 128;      // K per step
+constexpr int kQ8BRow = 64;     // bytes of a weight row per step (E2M1 codes)
+
+// 64-byte weight rows: 16-byte chunk c of row r lives at chunk c ^ q8_bswz(r).
+// A fragment read takes one chunk of 32 consecutive rows (lanes 0-31) and the
+// next chunk of the same rows (lanes 32-63); of any 8 consecutive rows from a
+// multiple of 8 the even and the odd ones get 4 distinct terms each, and of
+// any 16 rows from a multiple of 16 the rows of one residue mod 4 do, so an
+// 8-lane phase over 128 bytes of banks and a 16-lane phase over 256 bytes
+// both touch every 16-byte bank group once.
+__host__ __device__ constexpr int q8_bswz(int r) { return ((r >> 1) & 3) ^ ((r >> 3) & 1); }
+
+template <int TM> struct Q8Tile {
+    using B = BigTile<TM>;
+    static_assert(TM <= 2, "MXFP8 tiles: full, half, tall");
+    static constexpr int NA = B::BM / 32;                 // activation code loads (8 rows) per wave per step
+    static constexpr int NAS = (B::BM + 255) / 256;       // activation scale loads (64 rows) per wave per step
+    static constexpr int NBL = B::BN / 64;                // weight code loads (16 rows) per wave per step
+    static constexpr int NBX = NBL + 1;                   // weight-side loads per wave per step (codes + scales)
+    static constexpr int ASZ = B::BM * kBigRow + NAS * 1024;   // activation slot: codes, then scale words
+    static constexpr int BSZ = B::BN * kQ8BRow + 1024;          // weight slot: codes, then scale words
+};
+
+#define MOE_Q8_SLOTS(TM)                                                                          \
+    __shared__ __attribute__((aligned(16))) uint8_t q8##TM##_a0[Q8Tile<TM>::ASZ];                \
+    __shared__ __attribute__((aligned(16))) uint8_t q8##TM##_a1[Q8Tile<TM>::ASZ];                \
+    __shared__ __attribute__((aligned(16))) uint8_t q8##TM##_b0[Q8Tile<TM>::BSZ];                \
+    __shared__ __attribute__((aligned(16))) uint8_t q8##TM##_b1[Q8Tile<TM>::BSZ];                \
+    __shared__ __attribute__((aligned(16))) uint8_t q8##TM##_b2[Q8Tile<TM>::BSZ];
+MOE_Q8_SLOTS(0)  // full: 2 x 33 KiB + 3 x 17 KiB
+MOE_Q8_SLOTS(1)  // half: 2 x 17 KiB + 3 x 17 KiB
+MOE_Q8_SLOTS(2)  // tall: 2 x 42 KiB + 3 x 9 KiB
+#undef MOE_Q8_SLOTS
+
+template <int TM, int S>
+__device__ __forceinline__ uint8_t *q8_a() {
+    static_assert(S == 0 || S == 1, "two activation slots");
+    if constexpr (TM == 0) return S ? q80_a1 : q80_a0;
+    else if constexpr (TM == 1) return S ? q81_a1 : q81_a0;
+    else return S ? q82_a1 : q82_a0;
+}
+
+template <int TM, int S>
+__device__ __forceinline__ uint8_t *q8_b() {
+    static_assert(S >= 0 && S < kRingB, "weight slot");
+    if constexpr (TM == 0) return S == 0 ? q80_b0 : S == 1 ? q80_b1 : q80_b2;
+    else if constexpr (TM == 1) return S == 0 ? q81_b0 : S == 1 ? q81_b1 : q81_b2;
+    else return S == 0 ? q82_b0 : S == 1 ? q82_b1 : q82_b2;
+}
+
+// Load state of a tile: descriptors of the activation codes, activation
+// scales, weight codes and weight scales, and the lane's 32-bit offsets
+// (at step 0) of each of its loads.
+struct Q8Ctx {
+    __amdgpu_buffer_rsrc_t ra, ras, rb, rbs;
+    uint32_t aoff[10], asoff[2], boff[4], bsoff;
+};
+
+template <int TM, int S>
+__device__ __forceinline__ void q8_issue_a(const Q8Ctx &c, int st, int wave) {
+    using Q = Q8Tile<TM>;
+    uint8_t *buf = q8_a<TM, S>();
+#pragma unroll
+    for (int i = 0; i < Q::NA; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.ra, MOE_LDS(buf + (wave * Q::NA + i) * 1024), 16, c.aoff[i],
+                                                 st * kQ8BK, 0, 0);
+#pragma unroll
+    for (int i = 0; i < Q::NAS; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.ras, MOE_LDS(buf + BigTile<TM>::BM * kBigRow + (wave + 4 * i) * 256),
+                                                 4, c.asoff[i], st * 4, 0, 0);
+}
+
+template <int TM, int S>
+__device__ __forceinline__ void q8_issue_b(const Q8Ctx &c, int st, int wave) {
+    using Q = Q8Tile<TM>;
+    uint8_t *buf = q8_b<TM, S>();
+#pragma unroll
+    for (int i = 0; i < Q::NBL; ++i)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rb, MOE_LDS(buf + (wave * Q::NBL + i) * 1024), 16, c.boff[i],
+                                                 st * kQ8BRow, 0, kStreamPolicy);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(c.rbs, MOE_LDS(buf + BigTile<TM>::BN * kQ8BRow + wave * 256), 4, c.bsoff,
+                                             st * 4, 0, 0);
+}
+
+typedef int int32x8_t __attribute__((ext_vector_type(8)));
+
+// Fragments of sub-step HS (K 64 HS .. 64 HS + 63 of the step).  The scaled
+// MFMA takes an E2M1 operand as 32 consecutive K values per lane (lane half
+// lh: the 32-block lh of the 64) and an E4M3 operand as two runs of 16 (lane
+// half lh: K 16 lh .. +15 of block 0, then of block 1), and applies to row i
+// of block b the scale held by lane i + 32 b (checked on the chip with a
+// one-wave probe).  So a lane reads weight rows bcol[c] + lr at chunk 2 HS +
+// lh of the 64-byte row and activation rows arow0 + 32m + lr at chunks
+// 4 HS + lh and 4 HS + 2 + lh of the 128-byte row, and gives the scales of
+// block lh of the sub-step.
+template <int TM, int SA, int SB, int HS>
+__device__ __forceinline__ void q8_read(int32x8_t (&fa)[BigTile<TM>::MB], int32x8_t (&fb)[BigTile<TM>::NBK],
+                                        const int (&bcol)[BigTile<TM>::NBK], int arow0, int lr, int lh) {
+    using T = BigTile<TM>;
+    const uint8_t *ab = q8_a<TM, SA>();
+    const uint8_t *bb = q8_b<TM, SB>();
+#pragma unroll
+    for (int c = 0; c < T::NBK; ++c) {
+        const int row = bcol[c] + lr;
+        const uint4 v = *(const uint4 *)(bb + row * kQ8BRow + (((2 * HS + lh) ^ q8_bswz(row)) << 4));
+        fb[c] = int32x8_t{(int)v.x, (int)v.y, (int)v.z, (int)v.w, 0, 0, 0, 0};
+    }
+#pragma unroll
+    for (int m = 0; m < T::MB; ++m) {
+        const int row = arow0 + m * 32 + lr;
+        const uint4 v0 = *(const uint4 *)(ab + bswz(row, 4 * HS + lh));
+        const uint4 v1 = *(const uint4 *)(ab + bswz(row, 4 * HS + 2 + lh));
+        fa[m] = int32x8_t{(int)v0.x, (int)v0.y, (int)v0.z, (int)v0.w, (int)v1.x, (int)v1.y, (int)v1.z, (int)v1.w};
+    }
+}
+
+// The scale words of a step: activation rows arow0 + 32m + lr, weight rows bcol[c] + lr.
+template <int TM, int SA, int SB>
+__device__ __forceinline__ void q8_read_scales(uint32_t (&sa)[BigTile<TM>::MB], uint32_t (&sb)[BigTile<TM>::NBK],
+                                               const int (&bcol)[BigTile<TM>::NBK], int arow0, int lr) {
+    using T = BigTile<TM>;
+    const uint8_t *ab = q8_a<TM, SA>() + T::BM * kBigRow;
+    const uint8_t *bb = q8_b<TM, SB>() + T::BN * kQ8BRow;
+#pragma unroll
+    for (int m = 0; m < T::MB; ++m) sa[m] = *(const uint32_t *)(ab + (arow0 + m * 32 + lr) * 4);
+#pragma unroll
+    for (int c = 0; c < T::NBK; ++c) sb[c] = *(const uint32_t *)(bb + (bcol[c] + lr) * 4);
+}
+
+// The scaled MFMAs of sub-step HS: the lane's scale byte of its 32-block is
+// byte 2 HS + lh of the row's word (moved to byte 0: op_sel 0).
+template <int TM, int HS>
+__device__ __forceinline__ void q8_mma(floatx16_t (&acc)[BigTile<TM>::MB][BigTile<TM>::NBK],
+                                       const int32x8_t (&fa)[BigTile<TM>::MB], const int32x8_t (&fb)[BigTile<TM>::NBK],
+                                       const uint32_t (&sa)[BigTile<TM>::MB], const uint32_t (&sb)[BigTile<TM>::NBK],
+                                       int lh) {
+    using T = BigTile<TM>;
+    const int sh = 8 * (2 * HS + lh);
+#pragma unroll
+    for (int m = 0; m < T::MB; ++m)
+#pragma unroll
+        for (int c = 0; c < T::NBK; ++c)
+            acc[m][c] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(fb[c], fa[m], acc[m][c], 4, 0, 0,
+                                                                         (int)(sb[c] >> sh), 0, (int)(sa[m] >> sh));
+}
+
+// Step st with activations in slot SA = st % 2 and weights in SB = st % 3.
+// On entry f0 holds sub-step 0 of step st and s0 its scale words; A(st+1),
+// B(st+1), B(st+2) are in flight, issued in the order B(st+1), A(st+1),
+// B(st+2).  Reads sub-step 1 into f1 under the MFMAs of sub-step 0, waits for
+// its own A(st+1), B(st+1) (all but the last NBX loads), passes the barrier,
+// issues A(st+2) into SA and B(st+3) into SB (clamped to the last step:
+// clamped loads are never read), reads sub-step 0 and the scales of step
+// st+1 into f0, s1 under the MFMAs of sub-step 1, then hands s1 over to s0.
+template <int TM, int SA, int SB>
+__device__ __forceinline__ void q8_step(const Q8Ctx &c, floatx16_t (&acc)[BigTile<TM>::MB][BigTile<TM>::NBK],
+                                        int32x8_t (&fa0)[BigTile<TM>::MB], int32x8_t (&fb0)[BigTile<TM>::NBK],
+                                        int32x8_t (&fa1)[BigTile<TM>::MB], int32x8_t (&fb1)[BigTile<TM>::NBK],
+                                        uint32_t (&sa0)[BigTile<TM>::MB], uint32_t (&sb0)[BigTile<TM>::NBK],
+                                        const int (&bcol)[BigTile<TM>::NBK], int st, int nstep, int wave, int arow0,
+                                        int lane) {
+    using T = BigTile<TM>;
+    using Q = Q8Tile<TM>;
+    const int lr = lane & 31, lh = lane >> 5;
+    q8_read<TM, SA, SB, 1>(fa1, fb1, bcol, arow0, lr, lh);
+    q8_mma<TM, 0>(acc, fa0, fb0, sa0, sb0, lh);
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(Q::NBX));
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    q8_issue_a<TM, SA>(c, min(st + 2, nstep - 1), wave);
+    q8_issue_b<TM, SB>(c, min(st + 3, nstep - 1), wave);
+    uint32_t sa1[T::MB], sb1[T::NBK];
+    q8_read<TM, SA ^ 1, (SB + 1) % kRingB, 0>(fa0, fb0, bcol, arow0, lr, lh);
+    q8_read_scales<TM, SA ^ 1, (SB + 1) % kRingB>(sa1, sb1, bcol, arow0, lr);
+    q8_mma<TM, 1>(acc, fa1, fb1, sa0, sb0, lh);
+    // the LDS reads spread over the first half of the sub-step's MFMAs, the
+    // loads over the second half
+    constexpr int NL = Q::NA + Q::NAS + Q::NBX, NR = 2 * T::MB + T::NBK + T::MB + T::NBK, NM = T::MB * T::NBK;
+    constexpr int H1 = NM / 2, H2 = NM - NM / 2;
+    constexpr int RPM = (NR + H1 - 1) / H1, LPM = (NL + H2 - 1) / H2;
+#pragma unroll
+    for (int i = 0; i < H1; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);    // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x100, RPM, 0);  // LDS reads
+    }
+#pragma unroll
+    for (int i = 0; i < H2; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+        __builtin_amdgcn_sched_group_barrier(0x020, LPM, 0);  // direct-to-LDS loads
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+#pragma unroll
+    for (int m = 0; m < T::MB; ++m) sa0[m] = sa1[m];
+#pragma unroll
+    for (int cc = 0; cc < T::NBK; ++cc) sb0[cc] = sb1[cc];
+}
+
+// The K loop: prologue, steps in groups of six (one turn of both slot
+// cycles), and a tail of 0, 2 or 4 steps (nstep is a multiple of 4).
+template <int TM>
+__device__ __forceinline__ void q8_kloop(const Q8Ctx &c, floatx16_t (&acc)[BigTile<TM>::MB][BigTile<TM>::NBK],
+                                         const int (&bcol)[BigTile<TM>::NBK], int nstep, int wave, int arow0,
+                                         int lane) {
+    using T = BigTile<TM>;
+    using Q = Q8Tile<TM>;
+    const int lr = lane & 31, lh = lane >> 5;
+    q8_issue_a<TM, 0>(c, 0, wave);
+    q8_issue_b<TM, 0>(c, 0, wave);
+    q8_issue_b<TM, 1>(c, 1, wave);
+    q8_issue_a<TM, 1>(c, 1, wave);
+    q8_issue_b<TM, 2>(c, 2, wave);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(2 * Q::NBX + Q::NA + Q::NAS));  // A(0) and B(0) landed
+    __builtin_amdgcn_s_barrier();
+    int32x8_t fa0[T::MB], fb0[T::NBK], fa1[T::MB], fb1[T::NBK];
+    uint32_t sa0[T::MB], sb0[T::NBK];
+    q8_read<TM, 0, 0, 0>(fa0, fb0, bcol, arow0, lr, lh);
+    q8_read_scales<TM, 0, 0>(sa0, sb0, bcol, arow0, lr);
+    __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+    int st = 0;
+    for (; st + 6 <= nstep; st += 6) {
+        q8_step<TM, 0, 0>(c, acc, fa0, fb0, fa1, fb1, sa0, sb0, bcol, st + 0, nstep, wave, arow0, lane);
+        q8_step<TM, 1, 1>(c, acc, fa0, fb0, fa1, fb1, sa0, sb0, bcol, st + 1, nstep, wave, arow0, lane);
+        q8_step<TM, 0, 2>(c, acc, fa0, fb0, fa1, fb1, sa0, sb0, bcol, st + 2, nstep, wave, arow0, lane);
+        q8_step<TM, 1, 0>(c, acc, fa0, fb0, fa1, fb1, sa0, sb0, bcol, st + 3, nstep, wave, arow0, lane);
+        q8_step<TM, 0, 1>(c, acc, fa0, fb0, fa1, fb1, sa0, sb0, bcol, st + 4, nstep, wave, arow0, lane);
+        q8_step<TM, 1, 2>(c, acc, fa0, fb0, fa1, fb1, sa0, sb0, bcol, st + 5, nstep, wave, arow0, lane);
+    }
+    if (st + 2 <= nstep) {
+        q8_step<TM, 0, 0>(c, acc, fa0, fb0, fa1, fb1, sa0, sb0, bcol, st + 0, nstep, wave, arow0, lane);
+        q8_step<TM, 1, 1>(c, acc, fa0, fb0, fa1, fb1, sa0, sb0, bcol, st + 1, nstep, wave, arow0, lane);
+        if (st + 4 <= nstep) {
+            q8_step<TM, 0, 2>(c, acc, fa0, fb0, fa1, fb1, sa0, sb0, bcol, st + 2, nstep, wave, arow0, lane);
+            q8_step<TM, 1, 0>(c, acc, fa0, fb0, fa1, fb1, sa0, sb0, bcol, st + 3, nstep, wave, arow0, lane);
+        }
+    }
+}
+
+// One output tile (row tile rt, column block nb) of a grouped GEMM on MXFP8
+// activations and MXFP4 weights, in mode TM.
+template <int EPI, bool GROUPED, int OT, int TM>
+__device__ __forceinline__ void q8_item(const GemmArgs &a, const RowTile &rt, int64_t nb, int wave, int lane) {
+    using S = BigTile<TM>;
+    using Q = Q8Tile<TM>;
+    constexpr int MB = S::MB, NBK = S::NBK;
+    constexpr int WCOLS = 32 * NBK;
+    const int wm = TM == 1 ? 0 : wave >> 1;
+    const int wn = TM == 1 ? wave : wave & 1;
+    const int arow0 = wm * 32 * MB;
+    lane = opaque(lane);
+    const int64_t K = a.K;
+    const int nstep = (int)(K / kQ8BK);  // a multiple of 4
+    const int64_t brow0 = GROUPED ? (int64_t)rt.e * a.b_group_rows : 0;
+    int bcol[NBK];
+#pragma unroll
+    for (int c = 0; c < NBK; ++c) {
+        if constexpr (EPI == EPI_SWIGLU)
+            bcol[c] = (c < NBK / 2) ? wn * (WCOLS / 2) + c * 32 : S::BN / 2 + wn * (WCOLS / 2) + (c - NBK / 2) * 32;
+        else
+            bcol[c] = wn * WCOLS + c * 32;
+    }
+    Q8Ctx c;
+    // activation codes: load i of a wave fills LDS rows 8(wave NA + i) + lane / 8, at physical chunk
+    // lane % 8 of the row's logical chunk (lane % 8) ^ swz(row); rows past the valid ones read the last
+    // valid row (their results are never stored); gathered rows count from the buffer start,
+    // contiguous ones from the tile's first row
+    const uint8_t *a8 = (const uint8_t *)uniform_ptr(a.a_gather ? a.A8 : a.A8 + rt.p0 * K);
+    const uint8_t *a8s = (const uint8_t *)uniform_ptr(a.a_gather ? a.A8s : a.A8s + rt.p0 * (K / 32));
+    auto arow_of = [&](int row) -> int64_t {
+        const int r = min(row, rt.mcount - 1);
+        return a.a_gather ? (int64_t)a.a_gather[rt.p0 + r] : (int64_t)r;
+    };
+#pragma unroll
+    for (int i = 0; i < 10; ++i) {
+        if (i < Q::NA) {
+            const int lrow = (wave * Q::NA + i) * 8 + (lane >> 3);
+            c.aoff[i] = (uint32_t)(arow_of(lrow) * K + (((lane & 7) ^ swz(lrow)) << 4));
+        } else {
+            c.aoff[i] = 0;
+        }
+    }
+    // activation scale words: load i of a wave fills rows 64 (wave + 4 i) + lane (rows past BM: padding)
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+        c.asoff[i] = i < Q::NAS ? (uint32_t)(arow_of(64 * (wave + 4 * i) + lane) * (K / 32)) : 0;
+    // weight codes: load i of a wave fills rows 16 (wave NBL + i) + lane / 4 at physical chunk lane % 4 of
+    // logical chunk (lane % 4) ^ q8_bswz(row); SWIGLU rows past BN/2 are the matching up rows
+    const int64_t bfirst = brow0 + ((EPI == EPI_SWIGLU) ? nb * (S::BN / 2) : nb * S::BN);
+    const int64_t upskip = (EPI == EPI_SWIGLU) ? a.N - S::BN / 2 : 0;
+    auto brel = [&](int row) -> int64_t { return row + (row >= S::BN / 2 ? upskip : 0); };
+    const uint8_t *bcodes = (const uint8_t *)uniform_ptr((const uint8_t *)a.B + bfirst * (K / 2));
+    const uint8_t *bscale = (const uint8_t *)uniform_ptr((const uint8_t *)a.B + a.b_rows_total * (K / 2) +
+                                                         bfirst * (K / 32));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        if (i < Q::NBL) {
+            const int row = (wave * Q::NBL + i) * 16 + (lane >> 2);
+            c.boff[i] = (uint32_t)(brel(row) * (K / 2) + (((lane & 3) ^ q8_bswz(row)) << 4));
+        } else {
+            c.boff[i] = 0;
+        }
+    }
+    c.bsoff = (uint32_t)(brel(min(wave * 64 + lane, S::BN - 1)) * (K / 32));
+    c.ra = ring_rsrc(a8);
+    c.ras = ring_rsrc(a8s);
+    c.rb = ring_rsrc(bcodes);
+    c.rbs = ring_rsrc(bscale);
+
+    floatx16_t acc[MB][NBK];
+#pragma unroll
+    for (int m = 0; m < MB; ++m)
+#pragma unroll
+        for (int cc = 0; cc < NBK; ++cc)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[m][cc][r] = 0.f;
+    q8_kloop<TM>(c, acc, bcol, nstep, wave, arow0, lane);
+    __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
+    __builtin_amdgcn_s_barrier();
+    big_epilogue<EPI, OT, TM>(a, rt, nb, acc, bcol, arow0, opaque(lane), 0);
+}
+
 constexpr int kXcds = 8;  // workgroup b runs on XCD b % 8 (round-robin dispatch, checked on the chip)
 
 // Grouped launches (one tile mode each): tile t runs on XCD t % 8 and its
@@ -1295,7 +1659,8 @@ __device__ __forceinline__ void big_kernel_body(const GemmArgs &a) {
             RowTile rt;
             load_tile(a, true, BigTile<TM>::BM, t, rt);
             uniform_tile(rt);
-            big_item<EPI, MX, GROUPED, AT, OT, TM>(a, rt, nb, 0, wave, lane);
+            if constexpr (AT == ACT_Q8) q8_item<EPI, GROUPED, OT, TM>(a, rt, nb, wave, lane);
+            else big_item<EPI, MX, GROUPED, AT, OT, TM>(a, rt, nb, 0, wave, lane);
         }
     } else {
         const int ntiles = (int)((a.M + BigTile<TM>::BM - 1) / BigTile<TM>::BM);
@@ -1426,6 +1791,16 @@ hipError_t launch_gemm2(const GemmArgs &a, int path, bool mx, int at, bool norm,
     }
     if (at == ACT_F16) return run_path<EPI_ACT, 2, false, true, ACT_F16, ACT_BF16>(a, path, s);
     return run_path<EPI_ACT, 2, false, true, ACT_BF16, ACT_BF16>(a, path, s);
+}
+
+hipError_t launch_gemm1_q8(const GemmArgs &a, int path, int ot, hipStream_t s) {
+    if (ot == ACT_F16) return run_path<EPI_SWIGLU, 2, true, true, ACT_Q8, ACT_F16>(a, path, s);
+    return run_path<EPI_SWIGLU, 2, true, true, ACT_Q8, ACT_BF16>(a, path, s);
+}
+
+hipError_t launch_gemm2_q8(const GemmArgs &a, int path, bool norm, hipStream_t s) {
+    if (norm) return run_path<EPI_NORM, 2, true, true, ACT_Q8, ACT_BF16>(a, path, s);
+    return run_path<EPI_ACT, 2, true, true, ACT_Q8, ACT_BF16>(a, path, s);
 }
 
 template <int EPI>

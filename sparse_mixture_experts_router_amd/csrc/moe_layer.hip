@@ -42,7 +42,7 @@ struct Carve {
 
 struct Layout {
     size_t u, logits, idx, w, counts, offsets, perm_tok, perm_slot, pos, ntiles, tiles_small, tiles_big, tiles_half;
-    size_t tiles_tall, perm_scratch, z, act, S, ssq, m, S_out, ssq_out;
+    size_t tiles_tall, perm_scratch, z, act, S, ssq, m, S_out, ssq_out, zq, actq;
     int64_t max_small, max_big, max_half, max_tall;
     size_t total;
 };
@@ -105,6 +105,9 @@ Layout make_layout(const moe_desc *d) {
     const bool onorm = bf && d->out_norm != MOE_NORM_NONE;
     L.S_out = onorm ? c.take((size_t)T * d->d_model * 2) : 0;
     L.ssq_out = onorm ? c.take((size_t)T * (d->d_model / 16) * 4) : 0;
+    const bool q8 = bf && d->act_quant == MOE_AQ_MXFP8;
+    L.zq = q8 ? c.take((size_t)T * d->d_latent * 33 / 32) : 0;
+    L.actq = q8 ? c.take((size_t)TK * d->d_ff * 33 / 32) : 0;
     L.total = c.total;
     return L;
 }
@@ -137,6 +140,7 @@ int check_desc(const moe_desc *d) {
     if (d->interm_dtype != MOE_DT_F32 && d->interm_dtype != MOE_DT_BF16 && d->interm_dtype != MOE_DT_F16)
         return MOE_ERR_INVALID_ARG;
     if (d->T * d->top_k >= ((int64_t)1 << 31) || d->T >= ((int64_t)1 << 31)) return MOE_ERR_INVALID_ARG;
+    if (d->act_quant != MOE_AQ_NONE && d->act_quant != MOE_AQ_MXFP8) return MOE_ERR_INVALID_ARG;
     if (d->expert_kind == MOE_EXPERT_RELU2 && d->d_latent != 0) return MOE_ERR_INVALID_ARG;
     if (d->act_dtype == MOE_DT_F32) {
         // fp32 path: the small Shazeer layer shape (no latent, no norms).
@@ -144,8 +148,11 @@ int check_desc(const moe_desc *d) {
         if (d->d_latent != 0 || d->in_norm != MOE_NORM_NONE || d->expert_norm != MOE_NORM_NONE)
             return MOE_ERR_UNSUPPORTED;
         if (d->out_norm != MOE_NORM_NONE || d->res_gate == MOE_RES_MUSE) return MOE_ERR_UNSUPPORTED;
+        if (d->act_quant != MOE_AQ_NONE) return MOE_ERR_UNSUPPORTED;
         return MOE_OK;
     }
+    // quantized activations: the scaled fp8 x fp4 MFMA path of MXFP4 weights
+    if (d->act_quant == MOE_AQ_MXFP8 && d->weight_dtype != MOE_DT_MXFP4) return MOE_ERR_UNSUPPORTED;
     // bf16 path: latent SwiGLU layer on MFMA tiles.
     if (d->router_dtype != MOE_DT_BF16 || d->weight_dtype == MOE_DT_F32) return MOE_ERR_UNSUPPORTED;
     // fp16 weights feed the fp16 GEMMs directly: only with fp16 intermediates
@@ -281,7 +288,17 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
     }
     if (d->latent_norm != MOE_NORM_NONE)  // z = C_pre(z), in place, in the intermediate type
         MOE_TRY(launch_rmsnorm(z, gains ? gains->gamma_latent : nullptr, z, T, Lw, d->eps_latent, 1, at, s));
+    // MXFP8 activations: the expert GEMMs read the quantized z
+    const bool q8 = d->act_quant == MOE_AQ_MXFP8;
+    uint8_t *zq = q8 ? ws + L.zq : nullptr, *actq = q8 ? ws + L.actq : nullptr;
+    if (q8) MOE_TRY(launch_mxfp8_rows(z, T, Lw, at, zq, s));
     MOE_TRY_RC(ev.end(MOE_STAGE_DOWN));
+    auto gemm1 = [&](const GemmArgs &g, int path) {
+        return q8 ? launch_gemm1_q8(g, path, at, s) : launch_gemm1(g, path, mx, wat, s);
+    };
+    auto gemm2 = [&](const GemmArgs &g, int path, bool norm) {
+        return q8 ? launch_gemm2_q8(g, path, norm, s) : launch_gemm2(g, path, mx, wat, norm, s);
+    };
 
     auto grouped = [&](GemmArgs &g) {
         g.counts = counts;
@@ -301,25 +318,29 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
         g.K = Lw;
         g.C = act;
         g.ldc = F;
+        g.A8 = zq;
+        g.A8s = q8 ? zq + (size_t)T * Lw : nullptr;
         grouped(g);
         g.tiles = tiles_small;
         g.ntiles = ntiles;
         g.max_tiles = (int32_t)L.max_small;
-        MOE_TRY(launch_gemm1(g, PATH_STREAM, mx, wat, s));
+        MOE_TRY(gemm1(g, PATH_STREAM));
         if (any_big) {
             g.tiles = tiles_big;
             g.ntiles = ntiles + 1;
             g.max_tiles = (int32_t)L.max_big;
-            MOE_TRY(launch_gemm1(g, PATH_TILE, mx, wat, s));
+            MOE_TRY(gemm1(g, PATH_TILE));
             g.tiles = tiles_half;
             g.ntiles = ntiles + 2;
             g.max_tiles = (int32_t)L.max_half;
-            MOE_TRY(launch_gemm1(g, PATH_HALF, mx, wat, s));
+            MOE_TRY(gemm1(g, PATH_HALF));
             g.tiles = tiles_tall;
             g.ntiles = ntiles + 3;
             g.max_tiles = (int32_t)L.max_tall;
-            MOE_TRY(launch_gemm1(g, PATH_TALL, mx, wat, s));
+            MOE_TRY(gemm1(g, PATH_TALL));
         }
+        // MXFP8 activations: GEMM2 reads the quantized SwiGLU output
+        if (q8) MOE_TRY(launch_mxfp8_rows(act, TK, F, at, actq, s));
     }
     MOE_TRY_RC(ev.end(MOE_STAGE_GEMM1));
 
@@ -341,24 +362,26 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
         g.ssq = ssq;
         g.nparts = (int32_t)(Lw / 16);
         g.norm_round = d->expert_norm == MOE_NORM_INPUT_SCALED ? 1 : 0;
+        g.A8 = actq;
+        g.A8s = q8 ? actq + (size_t)TK * F : nullptr;
         grouped(g);
         g.tiles = tiles_small;
         g.ntiles = ntiles;
         g.max_tiles = (int32_t)L.max_small;
-        MOE_TRY(launch_gemm2(g, PATH_STREAM, mx, wat, norm2, s));
+        MOE_TRY(gemm2(g, PATH_STREAM, norm2));
         if (any_big) {
             g.tiles = tiles_big;
             g.ntiles = ntiles + 1;
             g.max_tiles = (int32_t)L.max_big;
-            MOE_TRY(launch_gemm2(g, PATH_TILE, mx, wat, norm2, s));
+            MOE_TRY(gemm2(g, PATH_TILE, norm2));
             g.tiles = tiles_half;
             g.ntiles = ntiles + 2;
             g.max_tiles = (int32_t)L.max_half;
-            MOE_TRY(launch_gemm2(g, PATH_HALF, mx, wat, norm2, s));
+            MOE_TRY(gemm2(g, PATH_HALF, norm2));
             g.tiles = tiles_tall;
             g.ntiles = ntiles + 3;
             g.max_tiles = (int32_t)L.max_tall;
-            MOE_TRY(launch_gemm2(g, PATH_TALL, mx, wat, norm2, s));
+            MOE_TRY(gemm2(g, PATH_TALL, norm2));
         }
     }
     MOE_TRY_RC(ev.end(MOE_STAGE_GEMM2));
@@ -429,6 +452,10 @@ int forward_bf16(const moe_desc *d, const void *x, const void *router_w, const v
             MOE_TRY(hipMemcpyAsync(dbg->ssq, ssq, (size_t)TK * (Lw / 16) * 4, hipMemcpyDeviceToDevice, s));
         if (dbg->m) MOE_TRY(hipMemcpyAsync(dbg->m, m, (size_t)T * Lw * 2, hipMemcpyDeviceToDevice, s));
         if (dbg->u) MOE_TRY(hipMemcpyAsync(dbg->u, u, (size_t)T * D * 2, hipMemcpyDeviceToDevice, s));
+        if (dbg->zq && q8)
+            MOE_TRY(hipMemcpyAsync(dbg->zq, zq, (size_t)T * Lw * 33 / 32, hipMemcpyDeviceToDevice, s));
+        if (dbg->actq && q8)
+            MOE_TRY(hipMemcpyAsync(dbg->actq, actq, (size_t)TK * F * 33 / 32, hipMemcpyDeviceToDevice, s));
     }
     return MOE_OK;
 }

@@ -742,6 +742,60 @@ __global__ __launch_bounds__(256) void bf16_to_f16_kernel(const uint4 *__restric
 // Launchers
 // ---------------------------------------------------------------------------
 
+// ---------------------------------------------------------------------------
+// MXFP8 quantization of activation rows (OCP Microscaling Formats (MX) v1.0,
+// MXFP8 E4M3): one thread per block of 32 consecutive values of a row.  The
+// block's largest magnitude sets the shared scale 2^X, X = floor(log2 amax)
+// - 8; every value becomes the E4M3 code of v * 2^-X (exact scaling of an
+// exact fp32 value, then round to nearest even, clamped to 448).  Codes go
+// to q [rows][K] and the E8M0 scale codes X + 127 to q + rows * K.
+// ---------------------------------------------------------------------------
+template <int IT>
+__global__ __launch_bounds__(256) void mxfp8_rows_kernel(const uint16_t *__restrict__ x, int64_t nblk,
+                                                         uint8_t *__restrict__ codes, uint8_t *__restrict__ scales) {
+    for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblk; b += (int64_t)gridDim.x * 256) {
+        const uint4 *src = (const uint4 *)(x + b * 32);
+        uint4 raw[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) raw[i] = src[i];
+        float v[32];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t w[4] = {raw[i].x, raw[i].y, raw[i].z, raw[i].w};
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                v[8 * i + 2 * j] = act_to_f32<IT>((uint16_t)(w[j] & 0xffffu));
+                v[8 * i + 2 * j + 1] = act_to_f32<IT>((uint16_t)(w[j] >> 16));
+            }
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int i = 0; i < 32; ++i) amax = fmaxf(amax, fabsf(v[i]));
+        const uint32_t sc = mx8_scale_code(amax);
+        const float inv = mx8_inv_scale(sc);
+        uint32_t packed[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            packed[i] = e4m3_code(v[4 * i] * inv) | (e4m3_code(v[4 * i + 1] * inv) << 8) |
+                        (e4m3_code(v[4 * i + 2] * inv) << 16) | (e4m3_code(v[4 * i + 3] * inv) << 24);
+        uint4 *dst = (uint4 *)(codes + b * 32);
+        dst[0] = make_uint4(packed[0], packed[1], packed[2], packed[3]);
+        dst[1] = make_uint4(packed[4], packed[5], packed[6], packed[7]);
+        scales[b] = (uint8_t)sc;
+    }
+}
+
+hipError_t launch_mxfp8_rows(const uint16_t *x, int64_t rows, int64_t K, int it, uint8_t *q, hipStream_t s) {
+    const int64_t nblk = rows * (K / 32);
+    if (nblk <= 0) return hipSuccess;
+    if (K % 32) return hipErrorInvalidValue;
+    const int64_t want = (nblk + 255) / 256;
+    const int grid = (int)(want < 8192 ? want : 8192);
+    if (it == ACT_F16) mxfp8_rows_kernel<ACT_F16><<<grid, 256, 0, s>>>(x, nblk, q, q + rows * K);
+    else mxfp8_rows_kernel<ACT_BF16><<<grid, 256, 0, s>>>(x, nblk, q, q + rows * K);
+    return hipGetLastError();
+}
+
 hipError_t launch_bf16_to_f16(const void *src, void *dst, int64_t count, hipStream_t s) {
     const int64_t n8 = count / 8;
     if (n8 <= 0) return hipSuccess;

@@ -12,6 +12,7 @@ Workloads (the shapes and distributions of the pages' model):
   c3   same layer, T=16384, Zipf(1.2) selection bias 1.5*ln(rank weight)
   c4c  same layer with MXFP4 weights, 4 chunks of 8192, centered input norm
   c4i  as c4c with the input-scaled input norm
+  c4q  as c4c with MXFP8 activations at the two expert GEMMs
   m1/m2  the Muse sublayer around the c1 layer at T=64 / T=8192
 """
 from __future__ import annotations
@@ -170,6 +171,7 @@ class Preset:
     eps_out: float = 1e-5
     res_tau: float = 0.3           # Muse residual gate temperature and floor
     res_floor: float = 1e-3
+    act_quant: str = "none"        # "none" | "mxfp8": the expert GEMMs read MXFP8 activations
 
     @property
     def chunk_T(self) -> int:
@@ -209,6 +211,9 @@ def muse(name: str = "muse", T: int = 8192, input_seed: int = 5, **kw) -> Preset
 
 PRESETS["m1"] = muse("m1", 64, 6)      # decode batch
 PRESETS["m2"] = muse("m2", 8192, 5)    # prefill batch
+# the c4 workload (MXFP4 weights, centered input norm, 4 chunks of 8192) with MXFP8 activations at the
+# expert GEMMs (the scaled fp8 x fp4 MFMA)
+PRESETS["c4q"] = dataclasses.replace(PRESETS["c4c"], name="c4q", act_quant="mxfp8")
 
 
 def small(name: str = "small", T: int = 77, d: int = 512, L: int = 256, F: int = 256, n: int = 16,

@@ -36,4 +36,5 @@ def preset_desc(p, T=None):
                          res_gate=p.res_gate, bias_in_weights=p.bias_in_weights, eps_in=p.eps_in,
                          eps_expert=p.eps_expert, interm=p.interm, router_fn=p.router_fn, out_mult=p.out_mult,
                          routed_scale=p.routed_scale, latent_norm=p.latent_norm, eps_latent=p.eps_latent,
-                         out_norm=p.out_norm, eps_out=p.eps_out, res_tau=p.res_tau, res_floor=p.res_floor)
+                         out_norm=p.out_norm, eps_out=p.eps_out, res_tau=p.res_tau, res_floor=p.res_floor,
+                         act_quant=p.act_quant)

@@ -74,6 +74,9 @@ def run(layer: DeviceLayer, x: np.ndarray, dbg: bool = True, workspace=None, sta
                       "S": torch.empty((TK, p.L), dtype=torch.int16, device="cuda"),
                       "ssq": torch.empty((TK, p.L // 16), dtype=torch.float32, device="cuda"),
                       "m": torch.empty((T, p.L), dtype=torch.int16, device="cuda")})
+            if p.act_quant == "mxfp8":
+                D.update({"zq": torch.empty(T * p.L * 33 // 32, dtype=torch.uint8, device="cuda"),
+                          "actq": torch.empty(TK * p.F * 33 // 32, dtype=torch.uint8, device="cuda")})
     dv = layer.dev
     moe.moe_layer_forward(desc, xd, dv["router_w"], dv.get("down_w"), dv["w1"], dv["w2"], dv.get("up_w"),
                           layer.gains(), out, workspace=workspace, dbg=D)
@@ -289,14 +292,39 @@ def compare(p: synthetic.Preset, host: dict, x: np.ndarray, gpu: dict, tokens=No
     gidx = gpu["topk_idx"][tok]
     refs = {}
     ndf = min(len(tok), DATAFLOW_TOKENS)  # the diagnostic dataflow mode runs on a prefix of the sample
+    q8 = p.act_quant == "mxfp8" and "zq" in gpu
+    if q8:
+        # the device's quantized expert inputs of the compared tokens: z, and the hidden activation of every
+        # selected expert in slot order (row pos[t, j] of the permuted buffer)
+        zq_dev = oracle.decode_matrix(gpu["zq"], "mxfp8", T, p.L)[tok]
+        TK, F_ = T * p.k, p.F
+        prow = gpu["pos"][tok].reshape(-1)
+        abuf = np.concatenate([gpu["actq"][:TK * F_].reshape(TK, F_)[prow].reshape(-1),
+                               gpu["actq"][TK * F_:].reshape(TK, F_ // 32)[prow].reshape(-1)])
+        aq_dev = oracle.decode_matrix(abuf, "mxfp8", len(prow), F_).reshape(len(tok), p.k, F_)
+    nzf = 0
     for mode, mirror, tt in (("exact", False, tok), ("dataflow", True, tok[:ndf])):
-        r = oracle.forward(cfg, t, tokens=tt, mirror=mirror)
+        r = oracle.forward(cfg, t, tokens=tt, mirror=mirror, want_z=q8, want_a=q8)
         y_ref, out_ref, ypre = r["y"].copy(), r["out"].copy(), r["ypre"].copy()
-        diff = np.flatnonzero(~(gidx[:len(tt)] == r["idx"]).all(axis=1))
-        if diff.size:
-            rf = oracle.forward(cfg, t, tokens=tt[diff], forced=gidx[diff], mirror=mirror)
-            y_ref[diff], out_ref[diff], ypre[diff] = rf["y"], rf["out"], rf["ypre"]
-        refs[mode] = (y_ref, out_ref, diff.size, ypre)
+        nt = len(tt)
+        diff = ~(gidx[:nt] == r["idx"]).all(axis=1)
+        qdiff = np.zeros(nt, bool)
+        if q8:
+            # A token whose quantized expert inputs differ from the oracle's is evaluated on the device's, as
+            # a near-tie token is on the device's experts: an E4M3 code (or a block's shared scale) decided on
+            # either side of a rounding point by a one-ulp difference of the stored value, from fp32 against
+            # fp64 sums, from a flip of u, or within the scaled MFMA's own error bound.
+            qdiff = ~(zq_dev[:nt] == r["z"]).all(axis=1) | ~(aq_dev[:nt] == r["a"]).all(axis=(1, 2))
+        redo = np.flatnonzero(diff | qdiff)
+        if mode == "exact" and q8:
+            unforced = np.abs(gpu["out"][tt] - r["out"]).max() / np.sqrt(np.mean(r["y"] ** 2))
+        if redo.size:
+            rf = oracle.forward(cfg, t, tokens=tt[redo], forced=gidx[redo], mirror=mirror,
+                                forced_z=zq_dev[redo] if q8 else None, forced_a=aq_dev[redo] if q8 else None)
+            y_ref[redo], out_ref[redo], ypre[redo] = rf["y"], rf["out"], rf["ypre"]
+        if mode == "exact":
+            nzf = int(qdiff.sum())
+        refs[mode] = (y_ref, out_ref, int(diff.sum()), ypre)
     y_ex, out_ex, nforced, ypre = refs["exact"]
     y_df, out_df, _, ypre_df = refs["dataflow"]
     rms = float(np.sqrt(np.mean(y_ex ** 2)))
@@ -310,12 +338,21 @@ def compare(p: synthetic.Preset, host: dict, x: np.ndarray, gpu: dict, tokens=No
     e_out_df = float(np.maximum(np.abs(gpu["out"][tok[:ndf]] - out_df) - allow_out_df, 0).max()) / rms
     e_y_df = float(np.maximum(np.abs(gpu["y"][tok[:ndf]] - y_df) - allow_y_df, 0).max()) / rms
     beyond = float((dout > tol * rms).mean())
+    if q8:
+        say("%s: %d of %d tokens evaluated on the device's quantized expert inputs (an MXFP8 code differs); "
+            "without that, max|dout|/rms = %.3g (reported)" % (label, nzf, len(tok), unforced))
     say("%s: routed=%d (excluded %d) compared=%d forced=%d rms(y)=%.4g | exact: max|dout|/rms=%.3g (tol %.0e) "
         "max|dy|/rms=%.3g | bf16-dataflow: max|dout|/rms=%.3g max|dy|/rms=%.3g (tol %.0e)%s" % (
             label, len(rtok), excluded, len(tok), nforced, rms, e_out, tol, e_y, e_out_df, e_y_df, tol_df,
             " | output-norm flips: raw max|dout|/rms=%.3g, beyond tol %.4f%%" % (float(dout.max()) / rms,
                                                                            100 * beyond)
             if p.out_norm != "none" else ""))
+    if e_out > tol:
+        worst = np.argsort(-np.maximum(dout - allow_out, 0).max(axis=1))[:5]
+        for w_ in worst:
+            say("  worst token %d: max|dout|/rms %.3g, experts %s" % (
+                tok[w_], float(np.maximum(dout[w_] - allow_out if np.ndim(allow_out) < 2 else dout[w_] - allow_out[w_],
+                                          0).max()) / rms, gidx[w_].tolist()))
     assert e_out <= tol, "%s out error %.3g * RMS(y) > %.0e" % (label, e_out, tol)
     assert beyond <= FLIP_OUT_FRACTION, "%s: %.3g of the outputs beyond the tolerance" % (label, beyond)
     if kind == "f32":
@@ -385,18 +422,34 @@ def weight_rows(host: dict, key: str, fmt: str, rows_total: int, K: int, row0: i
     return bf16f(flat) if flat.dtype == np.uint16 else flat.astype(np.float64)
 
 
-def _flips(name, got, ref, label, ulp=ulp_bf16, floor=None):
+# The scaled fp8 x fp4 MFMA (MXFP8 activations on the large tiles) does not
+# sum its products in full fp32: a one-wave probe of the instruction on
+# random E4M3/E2M1 operands and scales put its error at up to 2^-11.6 of the
+# largest product of the 64-deep instruction and 2.4e-4 of the sum of the
+# products' magnitudes.  Its GEMM outputs are therefore allowed, on top of
+# the rounding of the stored value, 2^-11 times the sum of |a_k b_k| over K.
+MX8_MFMA_REL = 2.0 ** -11
+
+
+def _flips(name, got, ref, label, ulp=ulp_bf16, floor=None, extra=None):
     """got vs ref: equal except one-ulp flips; `floor` (per row) admits the
-    absolute error of an fp32 sum where the result nearly cancels."""
+    absolute error of an fp32 sum where the result nearly cancels; `extra`
+    (per element) an error bound of the arithmetic that produced got."""
     d = np.abs(got - ref)
     lim = 1.01 * ulp(ref)
     if floor is not None:
         lim = np.maximum(lim, floor[:, None])
+    if extra is not None:
+        lim = lim + extra
     bad = d > lim
     frac = float((d > 0).mean())
     say("  stage %-4s %s: differing %.4f%%, beyond 1 ulp %d" % (name, label, 100 * frac, int(bad.sum())))
+    for r_, c_ in list(zip(*np.nonzero(bad)))[:6]:
+        say("    row %d col %d: device %.9g reference %.9g |d| %.3g limit %.3g" % (
+            r_, c_, got[r_, c_], ref[r_, c_], d[r_, c_], lim[r_, c_]))
     assert not bad.any(), "%s stage %s: %d elements beyond one bf16 ulp" % (label, name, int(bad.sum()))
-    assert frac <= FLIP_FRACTION, "%s stage %s: %.3g of elements differ" % (label, name, frac)
+    if extra is None:  # with an arithmetic error bound, the element-wise bound is the check
+        assert frac <= FLIP_FRACTION, "%s stage %s: %.3g of elements differ" % (label, name, frac)
 
 
 def check_stages(p: synthetic.Preset, host: dict, x: np.ndarray, gpu: dict, tokens, label: str = ""):
@@ -451,20 +504,58 @@ def check_stages(p: synthetic.Preset, host: dict, x: np.ndarray, gpu: dict, toke
     ptok = gpu["perm_tok"]
     actg = dec(gpu["act"][rows])
     Sg = bf16f(gpu["S"][rows])
+    act_in = actg  # what GEMM2 multiplies
+    if p.act_quant == "mxfp8":
+        # the quantized z and SwiGLU output: bit for bit the oracle's quantizer applied to the device's own
+        # stored values (the same inputs: a decision taken in the same precision on both sides)
+        T = gpu["z"].shape[0]
+        TK = gpu["act"].shape[0]
+        zq = oracle.decode_matrix(gpu["zq"], "mxfp8", T, L)
+        zq_ref, zX = oracle.mxfp8_quantize(zfull)
+        np.testing.assert_array_equal(zq, zq_ref, err_msg=label + " stage zq (values)")
+        np.testing.assert_array_equal(gpu["zq"][T * L:].reshape(T, L // 32).astype(np.int32),
+                                      np.maximum(zX + 127, 0), err_msg=label + " stage zq (scales)")
+        ascales = gpu["actq"][TK * F:].reshape(TK, F // 32).astype(np.int32)
+        acodes = gpu["actq"][:TK * F].reshape(TK, F)
+        # every row up to 16384 rows; beyond, a seeded sample of 16384 rows and the checked tokens' rows
+        arows = np.arange(TK) if TK <= 16384 else np.unique(np.concatenate([
+            np.random.default_rng(3).choice(TK, 16384, replace=False), rows]))
+        for a in range(0, len(arows), 8192):
+            r_ = arows[a:a + 8192]
+            buf = np.concatenate([acodes[r_].reshape(-1), gpu["actq"][TK * F:].reshape(TK, F // 32)[r_].reshape(-1)])
+            got = oracle.decode_matrix(buf, "mxfp8", len(r_), F)
+            ref, aX = oracle.mxfp8_quantize(dec(gpu["act"][r_]))
+            np.testing.assert_array_equal(got, ref, err_msg=label + " stage actq (values)")
+            np.testing.assert_array_equal(ascales[r_], np.maximum(aX + 127, 0), err_msg=label + " stage actq (scales)")
+        say("  stage zq/actq %s: MXFP8 codes and scales of %d + %d rows bit-exact" % (label, T, len(arows)))
+        zfull = zq
+        abuf = np.concatenate([gpu["actq"][:TK * F].reshape(TK, F)[rows].reshape(-1),
+                               gpu["actq"][TK * F:].reshape(TK, F // 32)[rows].reshape(-1)])
+        act_in = oracle.decode_matrix(abuf, "mxfp8", len(rows), F)
     act_ref = np.zeros_like(actg)
     o_ref = np.zeros_like(Sg)
+    q8 = p.act_quant == "mxfp8"
+    act_err = np.zeros_like(actg) if q8 else None  # the scaled MFMA's bound, carried through SwiGLU
+    o_err = np.zeros_like(Sg) if q8 else None
     for e in np.unique(eid):
         sel = np.flatnonzero(eid == e)
         W1 = weight_rows(host, "w1", fmt, n * 2 * F, L, e * 2 * F, 2 * F)
         zin = zfull[ptok[rows[sel]]]
         g_, v_ = zin @ W1[:F].T, zin @ W1[F:].T
-        act_ref[sel] = g_ / (1 + np.exp(-g_)) * v_
+        sg = 1 / (1 + np.exp(-g_))
+        act_ref[sel] = g_ * sg * v_
         W2 = weight_rows(host, "w2", fmt, n * L, F, e * L, L)
-        o_ref[sel] = actg[sel] @ W2.T
-    _flips("act", actg, rnd(act_ref), label, ulp, rowfloor(act_ref))
+        o_ref[sel] = act_in[sel] @ W2.T
+        if q8:
+            dg = MX8_MFMA_REL * (np.abs(zin) @ np.abs(W1[:F]).T)
+            dv = MX8_MFMA_REL * (np.abs(zin) @ np.abs(W1[F:]).T)
+            dsilu = sg * (1 + g_ * (1 - sg))  # d silu / dg
+            act_err[sel] = np.abs(dsilu * v_) * dg + np.abs(g_ * sg) * dv + dg * dv
+            o_err[sel] = MX8_MFMA_REL * (np.abs(act_in[sel]) @ np.abs(W2).T)
+    _flips("act", actg, rnd(act_ref), label, ulp, rowfloor(act_ref), act_err)
     gam = 1.0 + (host["gamma_ex"].astype(np.float64) if "gamma_ex" in host else 0.0)
     S_ref = round_bf16(gam * o_ref)
-    _flips("S", Sg, S_ref, label, ulp_bf16, rowfloor(gam * o_ref))
+    _flips("S", Sg, S_ref, label, ulp_bf16, rowfloor(gam * o_ref), None if o_err is None else np.abs(gam) * o_err)
     if p.expert_norm != "none":
         sq = (Sg if p.expert_norm == "input_scaled" else o_ref) ** 2
         ssq_ref = sq.reshape(len(rows), L // 16, 16).sum(2)

@@ -158,7 +158,7 @@ def test_muse_forward_needs_its_gate_vector():
     rc = lib.moe_layer_forward(ctypes.byref(d), fake, fake, fake, fake, fake, fake, ctypes.byref(g), fake, fake,
                                1 << 40, None, None)
     assert rc == moe.MOE_ERR_INVALID_ARG
-    assert ctypes.sizeof(moe.moe_desc) == 128 and ctypes.sizeof(moe.moe_gains) == 48
+    assert ctypes.sizeof(moe.moe_desc) == 136 and ctypes.sizeof(moe.moe_gains) == 48
 
 
 def test_error_strings():
@@ -211,3 +211,17 @@ def test_binding_structs_match_the_header(tmp_path):
         assert got[(sn, "sizeof")] == ctypes.sizeof(cls), sn
         for fn, _ in cls._fields_:
             assert got[(sn, fn)] == getattr(cls, fn).offset, (sn, fn)
+
+
+def test_mxfp8_activations_need_mxfp4_weights():
+    p = dataclasses.replace(synthetic.PRESETS["c4q"], name="q8_bf16w", weights="bf16")
+    assert moe.moe_validate(desc_of(p)) == moe.MOE_ERR_UNSUPPORTED
+    assert moe.moe_validate(desc_of(synthetic.PRESETS["c4q"])) == moe.MOE_OK
+    d = desc_of(synthetic.PRESETS["c4q"])
+    d.act_quant = 2
+    assert moe.moe_validate(d) == moe.MOE_ERR_INVALID_ARG
+    # the quantized forms of z and of the SwiGLU output: 33/32 bytes per value each
+    a, b = moe.moe_workspace_bytes(desc_of(synthetic.PRESETS["c4q"])), moe.moe_workspace_bytes(
+        desc_of(synthetic.PRESETS["c4c"]))
+    p = synthetic.PRESETS["c4q"]
+    assert a - b >= p.chunk_T * (p.L + p.k * p.F) * 33 // 32

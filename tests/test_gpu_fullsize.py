@@ -151,3 +151,21 @@ def test_muse_sublayer_full_size(name, layer_host, bf16_layer):
         compare(p, lay.host, x, gpu, tokens=synthetic.sample_tokens(p.T, OUT_SAMPLE, seed=72), label=name)
         st = synthetic.sample_tokens(p.T, 4, seed=74)
     check_stages(p, lay.host, x, gpu, st, label=name)
+
+
+def test_c4q_mxfp8_activations(layer_host, bf16_layer):
+    # the c4 workload's first chunk with MXFP8 activations at the expert GEMMs (the scaled fp8 x fp4 MFMA
+    # on the tiled experts), graded against the oracle with the same quantizer (MXFP4 bar)
+    p = synthetic.PRESETS["c4q"]
+    lay = preset_layer(p, layer_host, bf16_layer)
+    x = synthetic.inputs(p, chunk=0)
+    gpu = run(lay, x)
+    tok = synthetic.sample_tokens(p.chunk_T, OUT_SAMPLE, seed=80)
+    check_stages(p, lay.host, x, gpu, tok[:3], label="c4q chunk 0")
+    compare(p, lay.host, x, gpu, tokens=tok, label="c4q chunk 0")
+    import oracle
+    t = dict(lay.host, x=x)
+    r0 = oracle.forward(dict(p.cfg(), act_quant="none"), t, tokens=tok[:64])
+    rms = float(np.sqrt(np.mean(r0["y"] ** 2)))
+    say("c4q: max|dout| against the unquantized oracle %.3g * RMS(y) (reported)" % (
+        float(np.abs(gpu["out"][tok[:64]] - r0["out"]).max()) / rms))

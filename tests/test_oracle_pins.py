@@ -758,3 +758,28 @@ def test_mxfp8_quantize_then_decode_round_trip():
     codes = torch.from_numpy(q / sc).to(torch.float8_e4m3fn).view(torch.uint8).numpy().reshape(-1)
     buf = np.concatenate([codes, (X + 127).astype(np.uint8).reshape(-1)])
     np.testing.assert_array_equal(oracle.decode_matrix(buf, "mxfp8", 3, 64), q)
+
+
+def test_forced_expert_input():
+    # the expert-space input given instead of computed: its own z reproduces the forward exactly; z = 0 gives
+    # SwiGLU(0) = 0 in every expert, so the branch output is 0 and out = x (the linear gate)
+    p = synthetic.small(T=5, d=64, L=32, F=32, n=8, k=2, weights="mxfp4")
+    t = dict(synthetic.layer_params(p), x=synthetic.inputs(p))
+    for aq in ("none", "mxfp8"):
+        cfg = dict(p.cfg(), act_quant=aq)
+        r = oracle.forward(cfg, t, want_z=True)
+        r2 = oracle.forward(cfg, t, forced_z=r["z"])
+        np.testing.assert_array_equal(r2["out"], r["out"])
+        r0 = oracle.forward(cfg, t, forced_z=np.zeros_like(r["z"]))
+        assert (r0["y"] == 0).all()
+        np.testing.assert_array_equal(r0["out"], synthetic.bf16_to_f32(t["x"]).astype(np.float64))
+    # under MXFP8 the z the experts read is on the E4M3 grid of its blocks
+    zq, _ = oracle.mxfp8_quantize(r["z"])
+    np.testing.assert_array_equal(zq, r["z"])
+    # the hidden activations given instead of computed: its own reproduce the forward; zeros give o = 0 in
+    # every selected expert, so again y = 0
+    ra = oracle.forward(cfg, t, want_a=True)
+    aq, _ = oracle.mxfp8_quantize(ra["a"])
+    np.testing.assert_array_equal(aq, ra["a"])
+    np.testing.assert_array_equal(oracle.forward(cfg, t, forced_a=ra["a"])["out"], ra["out"])
+    assert (oracle.forward(cfg, t, forced_a=np.zeros_like(ra["a"]))["y"] == 0).all()
