@@ -256,15 +256,26 @@ static void load_row(const void *base, int dt, int64_t rows, int64_t K, int64_t 
         const uint16_t *p = (const uint16_t *)base + r * K;
         for (int64_t c = 0; c < K; ++c) out[c] = bf16_bits_to_double(p[c]);
     } else if (dt == ORC_MXFP8) {
+        /* the element values by code, from the definition above (a lookup, not a new formula) */
+        double val[256];
+        for (unsigned q = 0; q < 256; ++q) val[q] = e4m3_value(q);
         const uint8_t *cd = (const uint8_t *)base + r * K;
         const uint8_t *sc = (const uint8_t *)base + rows * K + r * (K / 32);
-        for (int64_t c = 0; c < K; ++c) out[c] = e4m3_value(cd[c]) * e8m0_value(sc[c / 32]);
+        for (int64_t b = 0; b < K / 32; ++b) {
+            const double scale = e8m0_value(sc[b]);
+            for (int64_t c = 32 * b; c < 32 * b + 32; ++c) out[c] = val[cd[c]] * scale;
+        }
     } else {
+        double val[16];
+        for (unsigned q = 0; q < 16; ++q) val[q] = e2m1_value(q);
         const uint8_t *nib = (const uint8_t *)base + r * (K / 2);
         const uint8_t *sc = (const uint8_t *)base + rows * (K / 2) + r * (K / 32);
-        for (int64_t c = 0; c < K; ++c) {
-            unsigned code = (nib[c / 2] >> (4 * (c & 1))) & 15u;
-            out[c] = e2m1_value(code) * e8m0_value(sc[c / 32]);
+        for (int64_t b = 0; b < K / 32; ++b) {
+            const double scale = e8m0_value(sc[b]);
+            for (int64_t c = 32 * b; c < 32 * b + 32; ++c) {
+                unsigned code = (nib[c / 2] >> (4 * (c & 1))) & 15u;
+                out[c] = val[code] * scale;
+            }
         }
     }
 }
