@@ -107,7 +107,7 @@ def gate_weight_atol(p) -> float:
     return 1e-3 if (p.act == "bf16" and p.in_norm != "none") else 2e-5
 
 
-def check_router_stage(p, host, gpu, label=""):
+def check_router_stage(p, host, gpu, label="", known=None):
     """Router and top-k stage on every token of the batch, each against the
     oracle applied to the device's own stage input:
       logits: the oracle's router (fp64 dot products rounded to fp32) on the
@@ -119,14 +119,21 @@ def check_router_stage(p, host, gpu, label=""):
               apart) on tokens whose k-th/(k+1)-th gap is >= 1e-6, in order
               where every adjacent gap of the top k+1 is;
       weights: the oracle's weights of the device's own logits and experts,
-              to 2e-6 (times the routed scale)."""
+              to 2e-6 (times the routed scale).
+    known: optional (logits, same) — the oracle's logits of every token from
+    its own u, and which tokens' device u equals that u bit for bit; those
+    logits are reused instead of routing the same input again."""
     cfg = dict(oracle_cfg(p), in_norm="none")
     u = gpu["u"]
     lg = gpu["logits"]
     T = lg.shape[0]
     ref = np.empty_like(lg)
-    for a in range(0, T, 2048):  # oracle router on the device's branch input, in row blocks
-        rows = np.arange(a, min(T, a + 2048))
+    todo = np.arange(T)
+    if known is not None:
+        ref[known[1]] = known[0][known[1]]
+        todo = np.flatnonzero(~known[1])
+    for a in range(0, len(todo), 2048):  # oracle router on the device's branch input, in row blocks
+        rows = todo[a:a + 2048]
         ref[rows] = oracle.forward(cfg, dict(host, x=u), tokens=rows, want_outputs=False)["logits"]
     dl = float(np.abs(lg - ref).max())
     sel, H = oracle.router_scores(cfg, lg, host.get("bias"))
@@ -155,7 +162,7 @@ def check_router_stage(p, host, gpu, label=""):
     assert dw <= 2e-6 * max(1.0, abs(p.routed_scale)), "%s gate weights %.3g" % (label, dw)
 
 
-def check_input_norm(p, host, x, gpu, label=""):
+def check_input_norm(p, host, x, gpu, label="", u_orc=None):
     """The device's u = input norm of x on every token against the oracle's
     (fp64, rounded to bf16): equal except one-ulp flips on <= 0.5% of the
     elements (an fp32 and an fp64 value straddling a bf16 rounding
@@ -170,7 +177,7 @@ def check_input_norm(p, host, x, gpu, label=""):
     t = dict(host, x=x)
     for a in range(0, T, 1024):
         rows = np.arange(a, min(T, a + 1024))
-        ur = oracle.branch_input(oracle_cfg(p), t, rows)
+        ur = oracle.branch_input(oracle_cfg(p), t, rows) if u_orc is None else u_orc[rows]
         d = np.abs(bf16f(gpu["u"][rows]) - ur)
         nflip += int((d > 0).sum())
         nbad += int((d > (2.01 if p.in_norm == "input_scaled" else 1.01) * ulp_bf16(ur)).sum())
@@ -180,7 +187,7 @@ def check_input_norm(p, host, x, gpu, label=""):
     assert frac <= FLIP_FRACTION, "%s input norm: %.3g of elements differ" % (label, frac)
 
 
-def check_routing(p, host, x, gpu, tokens, label=""):
+def check_routing(p, host, x, gpu, tokens, label="", u_orc=None):
     """Routing of rows `tokens`: expert sets bit-exact where the oracle's
     k-th/(k+1)-th score margin is >= 1e-4, order bit-exact where every
     adjacent gap of the top k+1 scores is >= 1e-4; gate weights to 2e-5.
@@ -200,7 +207,8 @@ def check_routing(p, host, x, gpu, tokens, label=""):
         wtol = 2e-5  # tokens whose u differs are graded on the device's u instead
         for a in range(0, len(tokens), 1024):
             rows = np.asarray(tokens)[a:a + 1024]
-            same_u[a:a + 1024] = (bf16f(gpu["u"][rows]) == oracle.branch_input(oracle_cfg(p), t, rows)).all(axis=1)
+            uo = oracle.branch_input(oracle_cfg(p), t, rows) if u_orc is None else u_orc[rows]
+            same_u[a:a + 1024] = (bf16f(gpu["u"][rows]) == uo).all(axis=1)
         say("  routing %s: %d tokens whose device u has a one-ulp flip are graded on the device's u" % (
             label, int((~same_u).sum())))
         clean &= same_u
@@ -217,7 +225,7 @@ def check_routing(p, host, x, gpu, tokens, label=""):
     same = (gidx == r["idx"]).all(axis=1) & same_u
     np.testing.assert_allclose(gpu["topk_w"][tokens][same], r["w"][same], rtol=0, atol=wtol,
                                err_msg=label + " gate weights")
-    return int((~clean).sum())
+    return int((~clean).sum()), r["logits"], same_u
 
 
 # The oracle's bf16-dataflow mode (z, the SwiGLU output and m rounded to
@@ -229,7 +237,7 @@ def check_routing(p, host, x, gpu, tokens, label=""):
 # of the bf16 rounding noise itself.  The per-stage checks below (check_stages)
 # are the tight ones.
 TOL_DATAFLOW = {"f32": 1e-5, "bf16": 2e-2, "mxfp4": 5e-2}
-DATAFLOW_TOKENS = 64
+DATAFLOW_TOKENS = 32
 
 # The FFN output norm stores s = bf16((1 + gamma) y) (the input-scaled form
 # rounds it there by definition; the output-scaled form is stored that way
@@ -283,10 +291,19 @@ def compare(p: synthetic.Preset, host: dict, x: np.ndarray, gpu: dict, tokens=No
         for k_ in ("down_w", "w1", "w2", "up_w"):
             if k_ + "@" + weights_key in host:
                 t[k_] = host[k_ + "@" + weights_key]
-    excluded = check_routing(p, t, x, gpu, rtok, label)
+    u_orc = None
+    if p.in_norm != "none" and p.act == "bf16" and "u" in gpu:
+        u_orc = oracle.branch_input(oracle_cfg(p), dict(t, x=x))  # every row, once
+    excluded, r_logits, same_u = check_routing(p, t, x, gpu, rtok, label, u_orc)
     if "logits" in gpu and "u" in gpu:
-        check_router_stage(p, t, gpu, label)
-        check_input_norm(p, t, x, gpu, label)
+        known = None
+        if len(rtok) == T and (rtok == np.arange(T)).all():  # the oracle's logits of every token, from its u
+            if p.in_norm == "none":
+                known = (r_logits, (gpu["u"] == x).all(axis=1))
+            elif p.act == "bf16":
+                known = (r_logits, same_u)
+        check_router_stage(p, t, gpu, label, known)
+        check_input_norm(p, t, x, gpu, label, u_orc)
     t["x"] = x
     cfg = oracle_cfg(p)
     gidx = gpu["topk_idx"][tok]
