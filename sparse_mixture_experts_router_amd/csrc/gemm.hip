@@ -609,8 +609,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 // hold runs of four adjacent output columns of one row: epilogue stores are 8
 // or 16 bytes wide.  EPI_SWIGLU tiles hold 128 gate rows then the 128 matching
 // up rows; a wave's gate column blocks pair with its up column blocks.
-// Rows past the tile's valid rows load a clamped valid A row; their results
-// are never stored.
+// Rows past the tile's valid rows load zeros (an offset beyond the buffer
+// descriptor's range); their results are never stored.
 
 constexpr int kBigBM = kTileBM, kBigBN = kTileBN, kBigBK = 64;  // K per pair
 static_assert(kBigBM == 256 && kBigBN == 256, "the wave layout below assumes 256x256 tiles");
@@ -661,12 +661,19 @@ struct BigCtx {
     __amdgpu_buffer_rsrc_t rs;      // ring, MXFP4: descriptor of the tile's scale rows
 };
 
-// A raw buffer descriptor over ptr (stride 0, no range limit in practice):
-// buffer loads take the per-lane 32-bit offset in a VGPR and the pair offset
-// in an SGPR, so the compiler cannot fold them into per-lane 64-bit addresses.
+// A raw buffer descriptor over ptr (stride 0, 2^31 - 1 bytes): buffer loads
+// take the per-lane 32-bit offset in a VGPR and the pair offset in an SGPR,
+// so the compiler cannot fold them into per-lane 64-bit addresses.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t ring_rsrc(const void *ptr) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(ptr), 0, 0x7fffffff, 0x00020000);
 }
+
+// The lane offset of an A row past the tile's valid rows: beyond the
+// descriptor's range, so the buffer load returns zeros (into LDS) without
+// touching memory.  Those rows' results are never stored; zero operands make
+// their MFMAs cheap in power, and the chip's clock follows the power the
+// MFMAs draw on these GEMMs.
+constexpr uint32_t kPadRowOffset = 0x80000000u;
 
 
 // bf16 weights under fp16 activations are converted per fragment in
@@ -1109,10 +1116,10 @@ __device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, i
     c.A = (const uint8_t *)uniform_ptr(a.a_gather ? a.A : a.A + rt.p0 * a.lda) + k0 * 2;
 #pragma unroll
     for (int i = 0; i < NA; ++i) {
-        const int lrow = wave * (NA * 8) + i * 8 + drow;  // LDS row; the source row is clamped to a valid one
+        const int lrow = wave * (NA * 8) + i * 8 + drow;  // LDS row; rows past the valid ones load zeros
         const int row = min(lrow, rt.mcount - 1);
         const int64_t arow = a.a_gather ? (int64_t)a.a_gather[rt.p0 + row] : row;
-        c.aoff[i] = (uint32_t)((arow * a.lda + dchunk(lrow) * 8) * 2);
+        c.aoff[i] = lrow < rt.mcount ? (uint32_t)((arow * a.lda + dchunk(lrow) * 8) * 2) : kPadRowOffset;
     }
 #pragma unroll
     for (int i = NA; i < 12; ++i) c.aoff[i] = 0;
@@ -1580,9 +1587,9 @@ __device__ __forceinline__ void q8_item(const GemmArgs &a, const RowTile &rt, in
     }
     Q8Ctx c;
     // activation codes: load i of a wave fills LDS rows 8(wave NA + i) + lane / 8, at physical chunk
-    // lane % 8 of the row's logical chunk (lane % 8) ^ swz(row); rows past the valid ones read the last
-    // valid row (their results are never stored); gathered rows count from the buffer start,
-    // contiguous ones from the tile's first row
+    // lane % 8 of the row's logical chunk (lane % 8) ^ swz(row); rows past the valid ones load zeros
+    // (their results are never stored); gathered rows count from the buffer start, contiguous ones
+    // from the tile's first row
     const uint8_t *a8 = (const uint8_t *)uniform_ptr(a.a_gather ? a.A8 : a.A8 + rt.p0 * K);
     const uint8_t *a8s = (const uint8_t *)uniform_ptr(a.a_gather ? a.A8s : a.A8s + rt.p0 * (K / 32));
     auto arow_of = [&](int row) -> int64_t {
@@ -1592,8 +1599,9 @@ __device__ __forceinline__ void q8_item(const GemmArgs &a, const RowTile &rt, in
 #pragma unroll
     for (int i = 0; i < 10; ++i) {
         if (i < Q::NA) {
-            const int lrow = (wave * Q::NA + i) * 8 + (lane >> 3);
-            c.aoff[i] = (uint32_t)(arow_of(lrow) * K + (((lane & 7) ^ swz(lrow)) << 4));
+            const int lrow = (wave * Q::NA + i) * 8 + (lane >> 3);  // rows past the valid ones load zero codes
+            c.aoff[i] = lrow < rt.mcount ? (uint32_t)(arow_of(lrow) * K + (((lane & 7) ^ swz(lrow)) << 4))
+                                         : kPadRowOffset;
         } else {
             c.aoff[i] = 0;
         }
