@@ -901,7 +901,7 @@ __device__ __forceinline__ void ring_pair(const BigCtx &c, floatx16_t (&acc)[Big
 // waits for its own loads of pair pr+1, passes the barrier (pair pr+1
 // complete everywhere, every read of slot S done) and issues pair pr+2 into
 // slot S (clamped to the last pair: clamped loads are never read).
-template <int TM, int S, int HS, int H, bool CVT>
+template <int TM, int S, int HS, int H, bool CVT, int MV>
 __device__ __forceinline__ void wide_read(uint4 (&fa)[BigTile<TM>::MB], uint4 (&fb)[BigTile<TM>::NBK],
                                           const int (&bcol)[BigTile<TM>::NBK], int arow0, int lr, int lh) {
     using T = BigTile<TM>;
@@ -913,7 +913,7 @@ __device__ __forceinline__ void wide_read(uint4 (&fa)[BigTile<TM>::MB], uint4 (&
         fb[c] = CVT ? bf16x8_to_f16x8(v) : v;
     }
 #pragma unroll
-    for (int m = 0; m < T::MB; ++m) fa[m] = *(const uint4 *)(ab + bswz(arow0 + m * 32 + lr, 4 * HS + 2 * H + lh));
+    for (int m = 0; m < MV; ++m) fa[m] = *(const uint4 *)(ab + bswz(arow0 + m * 32 + lr, 4 * HS + 2 * H + lh));
 }
 
 // Quarters are software-pipelined across two fragment buffers: the reads
@@ -922,11 +922,11 @@ __device__ __forceinline__ void wide_read(uint4 (&fa)[BigTile<TM>::MB], uint4 (&
 // pair pr+1 and passes the barrier (pair pr+1 complete everywhere, every
 // read of slot S done); the loads of pair pr+2 into slot S and the reads of
 // quarter 0 of pair pr+1 then go out between the last quarter's MFMAs.
-template <int TM, int AT>
+template <int TM, int AT, int MV>
 __device__ __forceinline__ void wide_mma(floatx16_t (&acc)[BigTile<TM>::MB][BigTile<TM>::NBK],
                                          const uint4 (&fa)[BigTile<TM>::MB], const uint4 (&fb)[BigTile<TM>::NBK]) {
 #pragma unroll
-    for (int m = 0; m < BigTile<TM>::MB; ++m)
+    for (int m = 0; m < MV; ++m)
 #pragma unroll
         for (int c = 0; c < BigTile<TM>::NBK; ++c) acc[m][c] = mfma32x32x16<AT>(fb[c], fa[m], acc[m][c]);
 }
@@ -948,7 +948,7 @@ __device__ __forceinline__ void wide_interleave() {
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
 }
 
-template <int TM, int AT, int S>
+template <int TM, int AT, int S, int MV>
 __device__ __forceinline__ void wide_pair(const BigCtx &c, floatx16_t (&acc)[BigTile<TM>::MB][BigTile<TM>::NBK],
                                           uint4 (&qa0)[BigTile<TM>::MB], uint4 (&qb0)[BigTile<TM>::NBK],
                                           uint4 (&qa1)[BigTile<TM>::MB], uint4 (&qb1)[BigTile<TM>::NBK],
@@ -956,27 +956,29 @@ __device__ __forceinline__ void wide_pair(const BigCtx &c, floatx16_t (&acc)[Big
                                           int arow0, int lr, int lh) {
     using T = BigTile<TM>;
     constexpr bool CVT = kBigRegConvert<false, AT>;
-    constexpr int NR = T::MB + T::NBK, NM = T::MB * T::NBK;
-    wide_read<TM, S, 0, 1, CVT>(qa1, qb1, bcol, arow0, lr, lh);
-    wide_mma<TM, AT>(acc, qa0, qb0);
+    constexpr int NR = MV + T::NBK, NM = MV * T::NBK;
+    wide_read<TM, S, 0, 1, CVT, MV>(qa1, qb1, bcol, arow0, lr, lh);
+    wide_mma<TM, AT, MV>(acc, qa0, qb0);
     wide_interleave<0, NR, NM>();
-    wide_read<TM, S, 1, 0, CVT>(qa0, qb0, bcol, arow0, lr, lh);
-    wide_mma<TM, AT>(acc, qa1, qb1);
+    wide_read<TM, S, 1, 0, CVT, MV>(qa0, qb0, bcol, arow0, lr, lh);
+    wide_mma<TM, AT, MV>(acc, qa1, qb1);
     wide_interleave<0, NR, NM>();
-    wide_read<TM, S, 1, 1, CVT>(qa1, qb1, bcol, arow0, lr, lh);
-    wide_mma<TM, AT>(acc, qa0, qb0);
+    wide_read<TM, S, 1, 1, CVT, MV>(qa1, qb1, bcol, arow0, lr, lh);
+    wide_mma<TM, AT, MV>(acc, qa0, qb0);
     wide_interleave<0, NR, NM>();
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();
     __builtin_amdgcn_sched_barrier(0);
     ring_issue_a<TM, S>(c, min(pr + 2, npair - 1), wave);
     ring_issue_b<TM, S>(c, min(pr + 2, npair - 1), wave);
-    wide_read<TM, S ^ 1, 0, 0, CVT>(qa0, qb0, bcol, arow0, lr, lh);
-    wide_mma<TM, AT>(acc, qa1, qb1);
+    wide_read<TM, S ^ 1, 0, 0, CVT, MV>(qa0, qb0, bcol, arow0, lr, lh);
+    wide_mma<TM, AT, MV>(acc, qa1, qb1);
     wide_interleave<T::NA + T::NBL, NR, NM>();
 }
 
-template <int TM, int AT>
+// MV: the wave's 32-row blocks that hold valid rows (the others are padding:
+// their fragments are not read and their MFMAs not issued).
+template <int TM, int AT, int MV>
 __device__ __forceinline__ void wide_kloop(const BigCtx &c, floatx16_t (&acc)[BigTile<TM>::MB][BigTile<TM>::NBK],
                                            const int (&bcol)[BigTile<TM>::NBK], int npair, int wave, int arow0,
                                            int lane) {
@@ -989,11 +991,11 @@ __device__ __forceinline__ void wide_kloop(const BigCtx &c, floatx16_t (&acc)[Bi
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(T::NA + T::NBL));  // A(0) and B(0) landed
     __builtin_amdgcn_s_barrier();
     uint4 qa0[T::MB], qb0[T::NBK], qa1[T::MB], qb1[T::NBK];
-    wide_read<TM, 0, 0, 0, kBigRegConvert<false, AT>>(qa0, qb0, bcol, arow0, lr, lh);
+    wide_read<TM, 0, 0, 0, kBigRegConvert<false, AT>, MV>(qa0, qb0, bcol, arow0, lr, lh);
     __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
     for (int pr = 0; pr < npair; pr += 2) {
-        wide_pair<TM, AT, 0>(c, acc, qa0, qb0, qa1, qb1, bcol, pr, npair, wave, arow0, lr, lh);
-        wide_pair<TM, AT, 1>(c, acc, qa0, qb0, qa1, qb1, bcol, pr + 1, npair, wave, arow0, lr, lh);
+        wide_pair<TM, AT, 0, MV>(c, acc, qa0, qb0, qa1, qb1, bcol, pr, npair, wave, arow0, lr, lh);
+        wide_pair<TM, AT, 1, MV>(c, acc, qa0, qb0, qa1, qb1, bcol, pr + 1, npair, wave, arow0, lr, lh);
     }
 }
 
@@ -1162,8 +1164,15 @@ __device__ __forceinline__ void big_item(const GemmArgs &a, const RowTile &rt, i
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[m][cc][r] = 0.f;
 
-    if constexpr (TM == 3) wide_kloop<TM, AT>(c, acc, bcol, npair, wave, arow0, lane);
-    else ring_kloop<TM, AT, MX>(c, acc, bcol, npair, wave, arow0, lane);
+    if constexpr (TM == 3) {
+        // A wide tile holds 257..320 rows, so the second row of waves has 97..160 of them: its last
+        // 32-row block is often all padding, and skipping it frees a tenth of its SIMD's MFMA time
+        // (each SIMD runs one wave of each row).
+        if (rt.mcount - arow0 > 32 * (MB - 1)) wide_kloop<TM, AT, MB>(c, acc, bcol, npair, wave, arow0, lane);
+        else wide_kloop<TM, AT, MB - 1>(c, acc, bcol, npair, wave, arow0, lane);
+    } else {
+        ring_kloop<TM, AT, MX>(c, acc, bcol, npair, wave, arow0, lane);
+    }
     // Drain the clamped tail loads before the buffers are refilled.
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(0));
     __builtin_amdgcn_s_barrier();
@@ -1226,6 +1235,14 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs &a, const RowTile &r
             // (the residual and the output have different types)
             asm volatile("" ::: "memory");
             load_resid(m);
+        }
+        // The residual and norm epilogues: the block's accumulators stay in
+        // their AGPRs up to here, so the VGPR copies the arithmetic needs are
+        // made one row block at a time (copied all at once after the K loop,
+        // they spilled).  The wide mode keeps its accumulators in VGPRs.
+        if constexpr ((EPI == EPI_RESID || EPI == EPI_NORM) && TM != 3) {
+#pragma unroll
+            for (int cc = 0; cc < NBK; ++cc) asm volatile("" : "+a"(acc[m][cc]));
         }
         if constexpr (EPI == EPI_SWIGLU) {
 #pragma unroll
