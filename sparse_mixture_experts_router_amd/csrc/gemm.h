@@ -102,4 +102,15 @@ hipError_t launch_mxfp8_rows(const uint16_t *x, int64_t rows, int64_t K, int it,
 // (bf16 (1 + gamma) y and per-16-column sums of squares for the output norm).
 hipError_t launch_up_gemm(const GemmArgs &a, int path, bool mx, int at, int epi, hipStream_t s);
 
+// Dense projection of a few rows (at most 128) on half-height tiles (128 x
+// 256) with K cut into a.ksplit >= 2 slices of a multiple of 512: slice s
+// stores its partial sums into fp32 plane s of C ([ksplit][M][ldc], ldc = N).
+// A in `at`, bf16 or fp16 weights.  launch_split_reduce finishes the sums.
+hipError_t launch_dense_split(const GemmArgs &a, int at, hipStream_t s);
+// Sums the ks planes [ks][M][N] (fp32, in slice order) and applies the
+// epilogue: EPI_RESID: C[p][n] = x[p][n] + gate[n] * sum (fp32), y[p][n] =
+// sum when y != NULL; EPI_F32: C[p][n] = sum.  N a multiple of 4.
+hipError_t launch_split_reduce(const float *planes, int ks, int64_t M, int64_t N, int epi, void *C,
+                               const uint16_t *resid, const float *gate, float *y, hipStream_t s);
+
 }  // namespace moe

@@ -1849,4 +1849,62 @@ hipError_t launch_up_gemm(const GemmArgs &a, int path, bool mx, int at, int epi,
     return hipErrorInvalidValue;
 }
 
+// A batch of a few rows reads every activation row once per item: on the
+// streaming kernel (16 weight rows an item) the activation bytes are four
+// times the weight bytes at 64 rows, and a fp32 epilogue of 512 items holds
+// two per CU.  A half-height tile takes 256 weight rows against the batch's
+// rows, and K slices give every CU one tile.
+hipError_t launch_dense_split(const GemmArgs &a, int at, hipStream_t s) {
+    if (a.ksplit < 2 || a.M > BigTile<1>::BM || a.N % BigTile<1>::BN || a.K % (512 * (int64_t)a.ksplit) ||
+        a.ldc != a.N)
+        return hipErrorInvalidValue;
+    if (at == ACT_F16_W16) return run_tile<EPI_F32, false, false, ACT_F16_W16, ACT_BF16, 1>(a, s);
+    if (at == ACT_F16) return run_tile<EPI_F32, false, false, ACT_F16, ACT_BF16, 1>(a, s);
+    return run_tile<EPI_F32, false, false, ACT_BF16, ACT_BF16, 1>(a, s);
+}
+
+// One thread per four adjacent outputs: the planes are added in slice order.
+template <int EPI>
+__global__ __launch_bounds__(256) void split_reduce_kernel(const float *planes, int ks, int64_t M, int64_t N,
+                                                           void *C, const uint16_t *resid, const float *gate,
+                                                           float *y) {
+    const int64_t e = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 4;  // element p * N + n
+    const int64_t plane = M * N;
+    if (e >= plane) return;
+    floatx4_t v = *(const floatx4_t *)(planes + e);
+    for (int sl = 1; sl < ks; ++sl) {
+        const floatx4_t w = *(const floatx4_t *)(planes + sl * plane + e);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] += w[q];
+    }
+    if constexpr (EPI == EPI_RESID) {
+        const uint2 hx = *(const uint2 *)(resid + e);
+        const float4 gt = *(const float4 *)(gate + e % N);
+        floatx4_t o;
+        o[0] = bf16_to_f32((uint16_t)hx.x) + gt.x * v[0];
+        o[1] = bf16_to_f32((uint16_t)(hx.x >> 16)) + gt.y * v[1];
+        o[2] = bf16_to_f32((uint16_t)hx.y) + gt.z * v[2];
+        o[3] = bf16_to_f32((uint16_t)(hx.y >> 16)) + gt.w * v[3];
+        *(floatx4_t *)((float *)C + e) = o;
+        if (y) *(floatx4_t *)(y + e) = v;
+    } else {
+        *(floatx4_t *)((float *)C + e) = v;
+    }
+}
+
+hipError_t launch_split_reduce(const float *planes, int ks, int64_t M, int64_t N, int epi, void *C,
+                               const uint16_t *resid, const float *gate, float *y, hipStream_t s) {
+    if (ks < 1 || N % 4 || M < 0) return hipErrorInvalidValue;
+    const int64_t groups = M * N / 4;
+    if (groups == 0) return hipSuccess;
+    const int grid = (int)((groups + 255) / 256);
+    if (epi == EPI_RESID)
+        split_reduce_kernel<EPI_RESID><<<grid, 256, 0, s>>>(planes, ks, M, N, C, resid, gate, y);
+    else if (epi == EPI_F32)
+        split_reduce_kernel<EPI_F32><<<grid, 256, 0, s>>>(planes, ks, M, N, C, resid, gate, y);
+    else
+        return hipErrorInvalidValue;
+    return hipGetLastError();
+}
+
 }  // namespace moe

@@ -68,6 +68,21 @@ def test_small_prefill_shape(weights):
     run_and_compare(p, tokens=tok)
 
 
+@pytest.mark.parametrize("T,res_gate", [(32, "linear"), (77, "linear"), (128, "linear"), (100, "none")])
+def test_up_projection_k_sliced(T, res_gate):
+    # 32..128 rows: the up-projection on half-height tiles whose 4 K slices of 512 store fp32 planes
+    # that a second kernel adds in slice order before the residual (or plain) epilogue
+    p = small_case("up_split_T%d_%s" % (T, res_gate), T=T, d=2048, L=2048, F=512, n=32, k=4,
+                   res_gate=res_gate)
+    layer = DeviceLayer(p)
+    _, gpu = run_and_compare(p, layer=layer)
+    if T == 77:
+        # the fp16 weight format through the same slices: bitwise the bf16 format's results
+        got = run(f16_weight_layer(layer), synthetic.inputs(p))
+        for key in gpu:
+            np.testing.assert_array_equal(got[key], gpu[key], err_msg=key)
+
+
 def test_small_skewed_mixed_tiles():
     # a Zipf selection bias: hot experts on the tiled kernel, cold ones streamed, some empty
     p = small_case("small_skew", T=700, n=32, k=4, router_bias="zipf")
