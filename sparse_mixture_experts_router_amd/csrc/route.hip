@@ -282,21 +282,40 @@ __global__ __launch_bounds__(256) void topk_kernel(const float *__restrict__ log
 constexpr int kPermThreads = 1024;
 constexpr int kPermWords = kPermThreads / 32;
 
-__device__ __forceinline__ void scan256_excl(int *a, int n) {  // in-place exclusive scan, a[n] = total
-    // Hillis-Steele on n <= 256 entries by the first 256 threads.
-    const int tid = threadIdx.x;
-    int v = (tid < n) ? a[tid] : 0;
-    __syncthreads();
-    for (int off = 1; off < 256; off <<= 1) {
-        int add = (tid < 256 && tid >= off && tid < n) ? a[tid - off] : 0;
-        __syncthreads();
-        if (tid < n) a[tid] += add;
-        __syncthreads();
+// In-place exclusive scans of five LDS arrays of n <= 256 entries each
+// (a[n] = the total) by the first 256 threads: prefix sums inside each wave
+// with shuffles, then the totals of the waves before it (three workgroup
+// barriers in all).  Every thread of the workgroup must call it.
+__device__ __forceinline__ void scan256_excl5(int *a0, int *a1, int *a2, int *a3, int *a4, int n) {
+    __shared__ int wtot[4][5];
+    int *const a[5] = {a0, a1, a2, a3, a4};
+    const int tid = threadIdx.x, lane = tid & 63, wv = tid >> 6;
+    int v[5], inc[5];
+#pragma unroll
+    for (int j = 0; j < 5; ++j) v[j] = (tid < n) ? a[j][tid] : 0;
+    __syncthreads();  // every read before the in-place writes
+#pragma unroll
+    for (int j = 0; j < 5; ++j) {
+        inc[j] = v[j];
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const int up = __shfl_up(inc[j], o, 64);
+            if (lane >= o) inc[j] += up;
+        }
     }
-    int incl = (tid < n) ? a[tid] : 0;
+    if (tid < 256 && lane == 63)
+#pragma unroll
+        for (int j = 0; j < 5; ++j) wtot[wv][j] = inc[j];
     __syncthreads();
-    if (tid < n) a[tid] = incl - v;
-    if (tid == n - 1) a[n] = incl;
+    if (tid < n) {
+#pragma unroll
+        for (int j = 0; j < 5; ++j) {
+            int incl = inc[j];
+            for (int w = 0; w < wv; ++w) incl += wtot[w][j];
+            a[j][tid] = incl - v[j];
+            if (tid == n - 1) a[j][n] = incl;
+        }
+    }
     __syncthreads();
 }
 
@@ -340,11 +359,7 @@ __device__ void publish_counts(const int *cnt, int *off, int *ts, int *tb, int *
         th[tid] = nh;
         tt[tid] = nt;
     }
-    scan256_excl(off, n);
-    scan256_excl(ts, n);
-    scan256_excl(tb, n);
-    scan256_excl(th, n);
-    scan256_excl(tt, n);
+    scan256_excl5(off, ts, tb, th, tt, n);
     if (tid < n) {
         const int c = cnt[tid];
         counts[tid] = c;
@@ -438,8 +453,10 @@ __global__ __launch_bounds__(kChunkTok) void perm_count_kernel(const int32_t *__
     if (tid < n) wg_counts[(int64_t)blockIdx.x * n + tid] = cnt[tid];
 }
 
-// One workgroup: per-expert totals, the chunk bases wg_base[g][e] =
-// offsets[e] + sum_{g' < g} wg_counts[g'][e], offsets and tile lists.
+// One workgroup: per-expert totals, the chunk bases within each expert
+// wg_base[g][e] = sum_{g' < g} wg_counts[g'][e] (the scatter adds
+// offsets[e]), offsets and tile lists.  The counts are read eight chunks at
+// a time, so their loads overlap.
 __global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t *__restrict__ wg_counts, int G, int n,
                                                         int32_t *__restrict__ wg_base, int32_t *__restrict__ counts,
                                                         int32_t *__restrict__ offsets, TileEntry *tiles_small,
@@ -449,26 +466,28 @@ __global__ __launch_bounds__(256) void perm_scan_kernel(const int32_t *__restric
     const int tid = threadIdx.x;
     if (tid < n) {
         int run = 0;
-        for (int g = 0; g < G; ++g) {
-            const int c = wg_counts[(int64_t)g * n + tid];
-            wg_base[(int64_t)g * n + tid] = run;
-            run += c;
+        for (int g0 = 0; g0 < G; g0 += 8) {
+            int c[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) c[j] = g0 + j < G ? wg_counts[(int64_t)(g0 + j) * n + tid] : 0;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                if (g0 + j < G) wg_base[(int64_t)(g0 + j) * n + tid] = run;
+                run += c[j];
+            }
         }
         cnt[tid] = run;
     }
     __syncthreads();
     publish_counts(cnt, off, ts, tb, th, tt, n, small_max, counts, offsets, tiles_small, tiles_big, tiles_half,
                    tiles_tall, ntiles);
-    if (tid < n) {
-        const int o = off[tid];
-        for (int g = 0; g < G; ++g) wg_base[(int64_t)g * n + tid] += o;
-    }
 }
 
 // Stable scatter of one chunk: rank of token t among the chunk's tokens of
-// expert e from the LDS bitmap, plus the chunk's base for e.
+// expert e from the LDS bitmap, plus the chunk's base within e and e's offset.
 __global__ __launch_bounds__(kChunkTok) void perm_scatter_kernel(const int32_t *__restrict__ idx, int64_t T, int k,
                                                                 int n, const int32_t *__restrict__ wg_base,
+                                                                const int32_t *__restrict__ offsets,
                                                                 int32_t *__restrict__ perm_tok,
                                                                 int32_t *__restrict__ perm_slot,
                                                                 int32_t *__restrict__ pos) {
@@ -488,7 +507,7 @@ __global__ __launch_bounds__(kChunkTok) void perm_scatter_kernel(const int32_t *
             const int e = idx[t * k + j];
             int rank = __popc(mask[e][word] & ((1u << bit) - 1u));
             for (int q = 0; q < word; ++q) rank += __popc(mask[e][q]);
-            const int p = base[e] + rank;
+            const int p = offsets[e] + base[e] + rank;
             perm_tok[p] = (int32_t)t;
             perm_slot[p] = j;
             pos[t * k + j] = p;
@@ -858,7 +877,7 @@ hipError_t launch_permute(const int32_t *idx, int64_t T, int k, int n, int32_t *
     perm_count_kernel<<<G, kChunkTok, 0, s>>>(idx, T, k, n, wg_counts);
     perm_scan_kernel<<<1, 256, 0, s>>>(wg_counts, G, n, wg_base, counts, offsets, tiles_small, tiles_big, tiles_half,
                                        tiles_tall, ntiles, small_max);
-    perm_scatter_kernel<<<G, kChunkTok, 0, s>>>(idx, T, k, n, wg_base, perm_tok, perm_slot, pos);
+    perm_scatter_kernel<<<G, kChunkTok, 0, s>>>(idx, T, k, n, wg_base, offsets, perm_tok, perm_slot, pos);
     return hipGetLastError();
 }
 
