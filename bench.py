@@ -115,7 +115,7 @@ def main():
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--only-prefill", action="store_true", help="only the prefill workload (profiling runs)")
     ap.add_argument("--only", default=None, metavar="PRESET",
-                    help="only the named workload preset (c2, c3, c4c, c4i, c4q, m1, m2), for profiling runs")
+                    help="only the named workload preset (c1m, c2, c3, c4c, c4i, c4q, m1, m2), for profiling runs")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the cache-flushed decode timing and the skewed (T=16384) and MXFP4 (4 x 8192) workloads")
@@ -439,6 +439,20 @@ def main():
                       "(%.0f%% of the FLOPs) run on the fp8 x fp4 MFMA, whose dense peak is %.0f TFLOP/s" % (
                           100.0 * flq["experts"] / flq["total"], FP8_PEAK_TFLOPS))
         result["mxfp4"]["mxfp8_activations"] = rq
+        # the decode batch on the same MXFP4 weights
+        p1m = synthetic.PRESETS["c1m"]
+        g1m = {"router_bias": None, "gamma_in": None, "gamma_expert": W4["gamma_ex"], "res_gate": W4["gate"]}
+        r1m = run_workload(p1m, args.steps, args.warmup, Wd=W4, gd=g1m, wf="mxfp4")
+        by1m = layer_bytes(p1m, r1m["counts"])
+        result["mxfp4"]["decode_T64"] = {
+            "workload": "MXFP4 weights, decode T=64", "ms_per_step": round(r1m["ms"], 4),
+            "graph_ms_per_step": round(r1m["graph_ms"], 4),
+            "tokens_per_s": round(p1m.chunk_T / (r1m["ms"] * 1e-3), 1),
+            "layer_bytes": by1m["total"], "layer_GBps": round(by1m["total"] / (r1m["ms"] * 1e-3) / 1e9, 1),
+            "layer_frac_hbm": round(by1m["total"] / (r1m["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "touched_experts": by1m["touched"], "stage_ms": {k: round(v, 4) for k, v in r1m["stages"].items()}}
+        log("MXFP4 weights, decode T=64: %.3f ms/step, %.0f tok/s, layer %.0f GB/s" % (
+            r1m["ms"], p1m.chunk_T / (r1m["ms"] * 1e-3), by1m["total"] / (r1m["ms"] * 1e-3) / 1e9))
         del W4
         torch.cuda.empty_cache()
 

@@ -114,46 +114,72 @@ struct StreamFrag {
     uint4 a[MB][4];
 };
 
+// Register-path loads are split in two: stream_fetch issues a K group's loads
+// into raw registers (codes and scale bytes as stored), stream_decode turns
+// them into MFMA fragments.  The loop decodes a group only when it needs it,
+// with the next group's loads in flight: decoding right after issuing would
+// make every group wait for its own loads.
 template <int MB, int NB, bool MX, int AT>
-__device__ __forceinline__ void stream_load(StreamFrag<MB, NB> &f, const uint8_t *const bptr[NB],
-                                            const uint8_t *const bscale[NB], const uint16_t *const aptr[MB],
-                                            const uint8_t *const a8ptr[MB], const uint8_t *const a8scale[MB],
-                                            int64_t kk) {
+struct StreamRaw {
+    uint4 b[NB][MX ? 1 : 4];  // MXFP4: 32 E2M1 codes of the lane's block; else 4 x 8 values
+    uint32_t bs[MX ? NB : 1];  // MXFP4: the block's E8M0 scale byte
+    uint4 a[MB][AT == ACT_Q8 ? 2 : 4];  // MXFP8: 32 E4M3 codes; else 4 x 8 values
+    uint32_t as[AT == ACT_Q8 ? MB : 1];  // MXFP8: the block's E8M0 scale byte
+};
+
+template <int MB, int NB, bool MX, int AT>
+__device__ __forceinline__ void stream_fetch(StreamRaw<MB, NB, MX, AT> &r, const uint8_t *const bptr[NB],
+                                             const uint8_t *const bscale[NB], const uint16_t *const aptr[MB],
+                                             const uint8_t *const a8ptr[MB], const uint8_t *const a8scale[MB],
+                                             int64_t kk) {
 #pragma unroll
     for (int c = 0; c < NB; ++c) {
         if constexpr (MX) {
-            uint4 codes = *(const uint4 *)(bptr[c] + (kk >> 1));
-            uint32_t sc = bscale[c][kk >> 5];
-            f.b[c][0] = mxfp4x8_to_act<AT>(codes.x, sc);
-            f.b[c][1] = mxfp4x8_to_act<AT>(codes.y, sc);
-            f.b[c][2] = mxfp4x8_to_act<AT>(codes.z, sc);
-            f.b[c][3] = mxfp4x8_to_act<AT>(codes.w, sc);
+            r.b[c][0] = *(const uint4 *)(bptr[c] + (kk >> 1));
+            r.bs[c] = bscale[c][kk >> 5];
         } else {
             const uint4 *p = (const uint4 *)(bptr[c] + kk * 2);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) f.b[c][s] = weight_bf16_as<AT>(p[s]);
+            for (int s = 0; s < 4; ++s) r.b[c][s] = p[s];
         }
     }
 #pragma unroll
     for (int m = 0; m < MB; ++m) {
         if constexpr (AT == ACT_Q8) {
-            // 32 E4M3 codes of the lane's block and its scale, decoded to bf16
-            if (a8ptr[m]) {
-                const uint4 *p = (const uint4 *)(a8ptr[m] + kk);
-                const uint32_t sc = a8scale[m][kk >> 5];
-                mxfp8x16_to_bf16(p[0], sc, f.a[m][0], f.a[m][1]);
-                mxfp8x16_to_bf16(p[1], sc, f.a[m][2], f.a[m][3]);
-            } else {
-#pragma unroll
-                for (int s = 0; s < 4; ++s) f.a[m][s] = make_uint4(0, 0, 0, 0);
-            }
-        } else if (aptr[m]) {
+            const uint4 *p = (const uint4 *)(a8ptr[m] + kk);
+            r.a[m][0] = p[0];
+            r.a[m][1] = p[1];
+            r.as[m] = a8scale[m][kk >> 5];
+        } else {
             const uint4 *p = (const uint4 *)(aptr[m] + kk);
 #pragma unroll
-            for (int s = 0; s < 4; ++s) f.a[m][s] = p[s];
+            for (int s = 0; s < 4; ++s) r.a[m][s] = p[s];
+        }
+    }
+}
+
+template <int MB, int NB, bool MX, int AT>
+__device__ __forceinline__ void stream_decode(StreamFrag<MB, NB> &f, const StreamRaw<MB, NB, MX, AT> &r) {
+#pragma unroll
+    for (int c = 0; c < NB; ++c) {
+        if constexpr (MX) {
+            f.b[c][0] = mxfp4x8_to_act<AT>(r.b[c][0].x, r.bs[c]);
+            f.b[c][1] = mxfp4x8_to_act<AT>(r.b[c][0].y, r.bs[c]);
+            f.b[c][2] = mxfp4x8_to_act<AT>(r.b[c][0].z, r.bs[c]);
+            f.b[c][3] = mxfp4x8_to_act<AT>(r.b[c][0].w, r.bs[c]);
         } else {
 #pragma unroll
-            for (int s = 0; s < 4; ++s) f.a[m][s] = make_uint4(0, 0, 0, 0);
+            for (int s = 0; s < 4; ++s) f.b[c][s] = weight_bf16_as<AT>(r.b[c][s]);
+        }
+    }
+#pragma unroll
+    for (int m = 0; m < MB; ++m) {
+        if constexpr (AT == ACT_Q8) {
+            mxfp8x16_to_bf16(r.a[m][0], r.as[m], f.a[m][0], f.a[m][1]);
+            mxfp8x16_to_bf16(r.a[m][1], r.as[m], f.a[m][2], f.a[m][3]);
+        } else {
+#pragma unroll
+            for (int s = 0; s < 4; ++s) f.a[m][s] = r.a[m][s];
         }
     }
 }
@@ -544,20 +570,17 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
         const uint8_t *a8ptr[MB], *a8scale[MB];
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
-            const int row = m * 16 + li;
-            if (row < rt.mcount) {
-                int64_t p = rt.p0 + row;
-                int64_t arow = a.a_gather ? (int64_t)a.a_gather[p] : p;
-                if constexpr (AT == ACT_Q8) {
-                    aptr[m] = nullptr;
-                    a8ptr[m] = a.A8 + arow * K + lg * 32;
-                    a8scale[m] = a.A8s + arow * (K / 32) + lg;
-                } else {
-                    aptr[m] = a.A + arow * a.lda + lg * 32;
-                    a8ptr[m] = a8scale[m] = nullptr;
-                }
-            } else {
+            // rows past the tile's valid rows read its last valid row (their results are never stored), so
+            // every lane issues the same loads and the in-order wait counts stay exact
+            const int row = min(m * 16 + li, rt.mcount - 1);
+            int64_t p = rt.p0 + row;
+            int64_t arow = a.a_gather ? (int64_t)a.a_gather[p] : p;
+            if constexpr (AT == ACT_Q8) {
                 aptr[m] = nullptr;
+                a8ptr[m] = a.A8 + arow * K + lg * 32;
+                a8scale[m] = a.A8s + arow * (K / 32) + lg;
+            } else {
+                aptr[m] = a.A + arow * a.lda + lg * 32;
                 a8ptr[m] = a8scale[m] = nullptr;
             }
         }
@@ -568,10 +591,14 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
             for (int c = 0; c < NB; ++c) acc[m][c] = floatx4_t{0.f, 0.f, 0.f, 0.f};
 
-        StreamFrag<MB, NB> cur, nxt;
-        stream_load<MB, NB, MX, AT>(cur, bptr, bscale, aptr, a8ptr, a8scale, kbeg);
-        for (int64_t kk = kbeg; kk < kend; kk += 128) {
-            if (kk + 128 < kend) stream_load<MB, NB, MX, AT>(nxt, bptr, bscale, aptr, a8ptr, a8scale, kk + 128);
+        // Two groups in flight: the raw registers of groups g+1 and g+2 while group g's MFMAs run.  The
+        // two raw buffers alternate by position in an unrolled pair of groups, each refilled once its
+        // group's MFMAs have read it, so no buffer is copied (a copy of registers a load is still writing,
+        // or a load into registers an MFMA has yet to read, would wait for that load).
+        StreamRaw<MB, NB, MX, AT> r0, r1;
+        auto step = [&](StreamRaw<MB, NB, MX, AT> &r, int64_t kk) {
+            StreamFrag<MB, NB> cur;
+            stream_decode<MB, NB, MX, AT>(cur, r);
 #pragma unroll
             for (int s = 0; s < 4; ++s)
 #pragma unroll
@@ -579,8 +606,22 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
                     for (int c = 0; c < NB; ++c)
                         acc[m][c] = mfma16x16x32<AT>(cur.a[m][s], cur.b[c][s], acc[m][c]);
-            cur = nxt;
+            if (kk + 256 < kend) stream_fetch<MB, NB, MX, AT>(r, bptr, bscale, aptr, a8ptr, a8scale, kk + 256);
+            // a group's refill stays ahead of the next group's, so waiting for one buffer leaves the other's
+            // loads in flight (the counter is in order)
+            __builtin_amdgcn_sched_barrier(0);
+        };
+        stream_fetch<MB, NB, MX, AT>(r0, bptr, bscale, aptr, a8ptr, a8scale, kbeg);
+        if (kbeg + 128 < kend) stream_fetch<MB, NB, MX, AT>(r1, bptr, bscale, aptr, a8ptr, a8scale, kbeg + 128);
+        int64_t kk = kbeg;
+        for (; kk + 512 <= kend; kk += 256) {  // every refill in range: one path, exact waits
+            step(r0, kk);
+            step(r1, kk + 128);
         }
+        // the last 1..3 groups, already loaded or in flight
+        step(r0, kk);
+        if (kk + 128 < kend) step(r1, kk + 128);
+        if (kk + 256 < kend) step(r0, kk + 256);
 
         finish(rt, nb, ksl, acc);
     }

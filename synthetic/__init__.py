@@ -214,6 +214,8 @@ PRESETS["m2"] = muse("m2", 8192, 5)    # prefill batch
 # the c4 workload (MXFP4 weights, centered input norm, 4 chunks of 8192) with MXFP8 activations at the
 # expert GEMMs (the scaled fp8 x fp4 MFMA)
 PRESETS["c4q"] = dataclasses.replace(PRESETS["c4c"], name="c4q", act_quant="mxfp8")
+# the decode batch (c1) on the MXFP4 forms of the same weights: the 4-bit checkpoint at decode
+PRESETS["c1m"] = dataclasses.replace(PRESETS["c1"], name="c1m", weights="mxfp4")
 
 
 def small(name: str = "small", T: int = 77, d: int = 512, L: int = 256, F: int = 256, n: int = 16,

@@ -99,6 +99,17 @@ def test_c3_skewed_T16384(layer_host, bf16_layer):
     check_stages(p, lay.host, x, gpu, np.unique(np.concatenate([tok[:3], cold[:2]])), label="c3")
 
 
+def test_c1m_mxfp4_decode_T64(layer_host, bf16_layer):
+    # the decode batch on the MXFP4 weights (streaming kernel, codes dequantised in registers): every
+    # token's outputs against the oracle on the same dequantised bits
+    p = synthetic.PRESETS["c1m"]
+    lay = preset_layer(p, layer_host, bf16_layer)
+    x = synthetic.inputs(p)
+    gpu = run(lay, x)
+    compare(p, lay.host, x, gpu, label="c1m")
+    check_stages(p, lay.host, x, gpu, np.arange(4), label="c1m")
+
+
 @pytest.mark.parametrize("name", ["c4c", "c4i"])
 @pytest.mark.parametrize("which", ["first", "last"])
 def test_c4_mxfp4_chunks(name, which, layer_host, bf16_layer):
