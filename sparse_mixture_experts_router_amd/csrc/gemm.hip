@@ -1277,11 +1277,12 @@ __device__ __forceinline__ void big_epilogue(const GemmArgs &a, const RowTile &r
             asm volatile("" ::: "memory");
             load_resid(m);
         }
-        // The residual and norm epilogues: the block's accumulators stay in
-        // their AGPRs up to here, so the VGPR copies the arithmetic needs are
-        // made one row block at a time (copied all at once after the K loop,
-        // they spilled).  The wide mode keeps its accumulators in VGPRs.
-        if constexpr ((EPI == EPI_RESID || EPI == EPI_NORM) && TM != 3) {
+        // The residual, norm and 16-bit-store epilogues: the block's
+        // accumulators stay in their AGPRs up to here, so the VGPR copies the
+        // arithmetic needs are made one row block at a time (copied all at
+        // once after the K loop, they spilled).  The wide mode keeps its
+        // accumulators in VGPRs.
+        if constexpr (EPI != EPI_SWIGLU && EPI != EPI_F32 && TM != 3) {
 #pragma unroll
             for (int cc = 0; cc < NBK; ++cc) asm volatile("" : "+a"(acc[m][cc]));
         }
@@ -1706,10 +1707,25 @@ __device__ __forceinline__ void q8_item(const GemmArgs &a, const RowTile &rt, in
 
 constexpr int kXcds = 8;  // workgroup b runs on XCD b % 8 (round-robin dispatch, checked on the chip)
 
+// Dense launches: the items of a round (one per workgroup) are cut into one
+// chunk per XCD, and a chunk holds a few row tiles x several column blocks
+// (row bands of kDenseBand tiles, column-major inside a band), so an XCD's
+// L2 sees kDenseBand A row panels and nslot / kDenseBand B panels per round
+// instead of every row tile of the round.  Returns the item's (t, nb).
+constexpr int kDenseBand = 8;
+__host__ __device__ inline void dense_item(uint32_t L, uint32_t ntiles, uint32_t nblocks, uint32_t &t,
+                                           uint32_t &nb) {
+    const uint32_t band = L / (kDenseBand * nblocks);
+    const uint32_t rows = ntiles - band * kDenseBand < kDenseBand ? ntiles - band * kDenseBand : kDenseBand;
+    const uint32_t w = L - band * kDenseBand * nblocks;
+    nb = w / rows;
+    t = band * kDenseBand + w % rows;
+}
+
 // Grouped launches (one tile mode each): tile t runs on XCD t % 8 and its
 // column blocks are spread over that XCD's workgroups, so the tile's A rows
 // are fetched into the XCD's L2 once and every weight block of the expert
-// is read once.  Dense launches: tile-major order over all workgroups.
+// is read once.
 template <int EPI, bool MX, bool GROUPED, int AT, int OT, int TM>
 __device__ __forceinline__ void big_kernel_body(const GemmArgs &a) {
     const int lane = threadIdx.x & 63, wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
@@ -1732,13 +1748,32 @@ __device__ __forceinline__ void big_kernel_body(const GemmArgs &a) {
         const int ntiles = (int)((a.M + BigTile<TM>::BM - 1) / BigTile<TM>::BM);
         const int ks = (EPI == EPI_F32 && !MX && a.ksplit > 1) ? a.ksplit : 1;
         const int64_t items = (int64_t)ntiles * nblocks * ks;
-        for (int64_t item = blockIdx.x; item < items; item += gridDim.x) {
-            const int ksl = (int)(item % ks);
-            const int64_t tb = item / ks;
-            const int t = (int)(tb / nblocks);
-            const int64_t nb = tb - (int64_t)t * nblocks;
+        // The plain order (item b + round * grid on workgroup b) gives every
+        // XCD every row tile of a round once a round spans more than
+        // kDenseBand of them; below that it already gives an XCD kDenseBand
+        // rows or fewer.  K-sliced launches and grids of a partial XCD group
+        // keep the plain order.
+        const bool xmap = ks == 1 && gridDim.x % kXcds == 0 && (int64_t)gridDim.x > kDenseBand * nblocks;
+        const int xcd = blockIdx.x % kXcds, slot = blockIdx.x / kXcds, nslot = gridDim.x / kXcds;
+        for (int64_t r0 = 0; r0 < items; r0 += gridDim.x) {
+            // round r0 / grid: XCD x takes items r0 + x * nslot + slot, slot = 0 .. nslot - 1
+            const int64_t item = r0 + (xmap ? (int64_t)xcd * nslot + slot : (int64_t)blockIdx.x);
+            if (item >= items) continue;
+            int64_t t, nb;
+            int ksl = 0;
+            if (xmap) {
+                uint32_t t32, nb32;  // a dense launch has far fewer than 2^32 items
+                dense_item((uint32_t)item, (uint32_t)ntiles, (uint32_t)nblocks, t32, nb32);
+                t = t32;
+                nb = nb32;
+            } else {
+                ksl = (int)(item % ks);
+                const int64_t tb = item / ks;
+                t = tb / nblocks;
+                nb = tb - t * nblocks;
+            }
             RowTile rt;
-            load_tile(a, false, BigTile<TM>::BM, t, rt);
+            load_tile(a, false, BigTile<TM>::BM, (int)t, rt);
             big_item<EPI, MX, GROUPED, AT, OT, TM>(a, rt, nb, ksl, wave, lane);
         }
     }
