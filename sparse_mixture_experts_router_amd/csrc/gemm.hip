@@ -114,6 +114,13 @@ struct StreamFrag {
     uint4 a[MB][4];
 };
 
+// The lane offset of an A row past the tile's valid rows: beyond the range
+// of a raw buffer descriptor of 2^31 - 1 bytes, so the buffer load returns
+// zeros (into registers or LDS) without touching memory.  Those rows'
+// results are never stored; zero operands make their MFMAs cheap in power,
+// and the chip's clock follows the power the MFMAs draw on these GEMMs.
+constexpr uint32_t kPadRowOffset = 0x80000000u;
+
 // Register-path loads are split in two: stream_fetch issues a K group's loads
 // into raw registers (codes and scale bytes as stored), stream_decode turns
 // them into MFMA fragments.  The loop decodes a group only when it needs it,
@@ -127,9 +134,10 @@ struct StreamRaw {
     uint32_t as[AT == ACT_Q8 ? MB : 1];  // MXFP8: the block's E8M0 scale byte
 };
 
-template <int MB, int NB, bool MX, int AT>
+template <int MB, int NB, bool MX, int AT, bool ABUF>
 __device__ __forceinline__ void stream_fetch(StreamRaw<MB, NB, MX, AT> &r, const uint8_t *const bptr[NB],
                                              const uint8_t *const bscale[NB], const uint16_t *const aptr[MB],
+                                             __amdgpu_buffer_rsrc_t ra, const uint32_t (&aoff)[MB],
                                              const uint8_t *const a8ptr[MB], const uint8_t *const a8scale[MB],
                                              int64_t kk) {
 #pragma unroll
@@ -150,6 +158,12 @@ __device__ __forceinline__ void stream_fetch(StreamRaw<MB, NB, MX, AT> &r, const
             r.a[m][0] = p[0];
             r.a[m][1] = p[1];
             r.as[m] = a8scale[m][kk >> 5];
+        } else if constexpr (ABUF) {
+            // rows past the tile's valid rows have an offset out of range: zeros, no memory access
+#pragma unroll
+            for (int s = 0; s < 4; ++s)
+                r.a[m][s] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                          ra, aoff[m], (uint32_t)(kk * 2 + s * 16), 0));
         } else {
             const uint4 *p = (const uint4 *)(aptr[m] + kk);
 #pragma unroll
@@ -566,22 +580,36 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
                 bscale[c] = nullptr;
             }
         }
+        // A rows.  Grouped items (mostly a few valid rows of 16 at decode) read
+        // 16-bit rows through a buffer descriptor (gathered rows from the buffer
+        // start, which the layer keeps below 2 GiB; contiguous rows from the
+        // tile's first row), rows past the tile's valid rows at an out-of-range
+        // offset, so those lanes touch no memory.  Dense items and MXFP8 rows
+        // read through pointers, rows past the valid ones at the last valid row
+        // (their results are never stored).  Every lane issues the same loads,
+        // so the in-order wait counts stay exact.
+        const __amdgpu_buffer_rsrc_t ra = __builtin_amdgcn_make_buffer_rsrc(
+            uniform_ptr(a.a_gather ? a.A : a.A + rt.p0 * a.lda), 0, 0x7fffffff, 0x00020000);
+        uint32_t aoff[MB];
         const uint16_t *aptr[MB];
         const uint8_t *a8ptr[MB], *a8scale[MB];
 #pragma unroll
         for (int m = 0; m < MB; ++m) {
-            // rows past the tile's valid rows read its last valid row (their results are never stored), so
-            // every lane issues the same loads and the in-order wait counts stay exact
-            const int row = min(m * 16 + li, rt.mcount - 1);
+            const int lrow = m * 16 + li;
+            const int row = min(lrow, rt.mcount - 1);
             int64_t p = rt.p0 + row;
             int64_t arow = a.a_gather ? (int64_t)a.a_gather[p] : p;
+            aoff[m] = 0;
+            aptr[m] = nullptr;
+            a8ptr[m] = a8scale[m] = nullptr;
             if constexpr (AT == ACT_Q8) {
-                aptr[m] = nullptr;
                 a8ptr[m] = a.A8 + arow * K + lg * 32;
                 a8scale[m] = a.A8s + arow * (K / 32) + lg;
+            } else if constexpr (GROUPED) {
+                const int64_t lr = a.a_gather ? arow : row;
+                aoff[m] = lrow < rt.mcount ? (uint32_t)((lr * a.lda + lg * 32) * 2) : kPadRowOffset;
             } else {
                 aptr[m] = a.A + arow * a.lda + lg * 32;
-                a8ptr[m] = a8scale[m] = nullptr;
             }
         }
 
@@ -606,13 +634,15 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
                     for (int c = 0; c < NB; ++c)
                         acc[m][c] = mfma16x16x32<AT>(cur.a[m][s], cur.b[c][s], acc[m][c]);
-            if (kk + 256 < kend) stream_fetch<MB, NB, MX, AT>(r, bptr, bscale, aptr, a8ptr, a8scale, kk + 256);
+            if (kk + 256 < kend)
+                stream_fetch<MB, NB, MX, AT, GROUPED>(r, bptr, bscale, aptr, ra, aoff, a8ptr, a8scale, kk + 256);
             // a group's refill stays ahead of the next group's, so waiting for one buffer leaves the other's
             // loads in flight (the counter is in order)
             __builtin_amdgcn_sched_barrier(0);
         };
-        stream_fetch<MB, NB, MX, AT>(r0, bptr, bscale, aptr, a8ptr, a8scale, kbeg);
-        if (kbeg + 128 < kend) stream_fetch<MB, NB, MX, AT>(r1, bptr, bscale, aptr, a8ptr, a8scale, kbeg + 128);
+        stream_fetch<MB, NB, MX, AT, GROUPED>(r0, bptr, bscale, aptr, ra, aoff, a8ptr, a8scale, kbeg);
+        if (kbeg + 128 < kend)
+            stream_fetch<MB, NB, MX, AT, GROUPED>(r1, bptr, bscale, aptr, ra, aoff, a8ptr, a8scale, kbeg + 128);
         int64_t kk = kbeg;
         for (; kk + 512 <= kend; kk += 256) {  // every refill in range: one path, exact waits
             step(r0, kk);
@@ -708,13 +738,6 @@ struct BigCtx {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t ring_rsrc(const void *ptr) {
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(ptr), 0, 0x7fffffff, 0x00020000);
 }
-
-// The lane offset of an A row past the tile's valid rows: beyond the
-// descriptor's range, so the buffer load returns zeros (into LDS) without
-// touching memory.  Those rows' results are never stored; zero operands make
-// their MFMAs cheap in power, and the chip's clock follows the power the
-// MFMAs draw on these GEMMs.
-constexpr uint32_t kPadRowOffset = 0x80000000u;
 
 
 // bf16 weights under fp16 activations are converted per fragment in
