@@ -274,13 +274,25 @@ __device__ __forceinline__ void strm_issue(const StrmCtx &c, int wave, int64_t k
                                                      c.boff[i], (int)(kk * 2), 0, kStreamPolicy);
 }
 
+// The order of a wave's K groups within an item's K slice (four waves, kq
+// elements each): KO 1 = the wave's contiguous quarter, KO 4 = every fourth
+// group from group `wave`.  kbeg is the wave's first group (strm_kbeg).
+template <int KO>
+__device__ __forceinline__ int64_t strm_kbeg(int64_t slice0, int64_t kq, int wave) {
+    return KO == 4 ? slice0 + (int64_t)wave * kStrmKG : slice0 + wave * kq;
+}
+template <int KO>
+__device__ __forceinline__ int64_t strm_kpos(int64_t kbeg, int g) {
+    return kbeg + (int64_t)KO * kStrmKG * g;
+}
+
 // One K group g of an LDS-streamed item, slot S = g % 3.  On entry group g
 // and (when g + 1 < ng) group g+1 are in flight, issued in that order.  The
 // step waits for group g: all but the loads of group g+1 (NEXT), or for
 // everything (last group); with ISSUE it then loads group g+2 into slot
 // (S+2) % 3; it reads group g and runs its MFMAs.  Slot (S+2) % 3 last held
 // group g-1, whose reads finished in the previous step.
-template <int MB, int NB, int NA, int AT, int S, bool ISSUE, bool NEXT>
+template <int MB, int NB, int NA, int AT, int KO, int S, bool ISSUE, bool NEXT>
 __device__ __forceinline__ void strm_step(floatx4_t (&acc)[MB][NB], const StrmCtx &c, int64_t kbeg, int g,
                                           int wave) {
     constexpr int NS = kStrmKG / 32;  // MFMA K steps per group
@@ -292,7 +304,7 @@ __device__ __forceinline__ void strm_step(floatx4_t (&acc)[MB][NB], const StrmCt
     __builtin_amdgcn_sched_barrier(0);
     __builtin_amdgcn_s_waitcnt(waitcnt_vm(NEXT ? kLeft : 0));
     __builtin_amdgcn_sched_barrier(0);
-    if constexpr (ISSUE) strm_issue<MB, NB, NA, (S + 2) % 3>(c, wave, kbeg + kStrmKG * (int64_t)(g + 2));
+    if constexpr (ISSUE) strm_issue<MB, NB, NA, (S + 2) % 3>(c, wave, strm_kpos<KO>(kbeg, g + 2));
     const uint8_t *const slot = strm_slot<MB, NB, S>();
     uint4 fa[MB][NS], fb[NB][NS];
 #pragma unroll
@@ -317,36 +329,36 @@ __device__ __forceinline__ void strm_step(floatx4_t (&acc)[MB][NB], const StrmCt
 // groups 0 and 1; strm_steps then runs the steady state in triples (each
 // step issues the group two ahead) and the last 2..4 groups with the issues
 // and waits that remain.
-template <int MB, int NB, int NA>
+template <int MB, int NB, int NA, int KO>
 __device__ __forceinline__ void strm_first(const StrmCtx &c, int wave, int64_t kbeg) {
     strm_issue<MB, NB, NA, 0>(c, wave, kbeg);
-    strm_issue<MB, NB, NA, 1>(c, wave, kbeg + kStrmKG);
+    strm_issue<MB, NB, NA, 1>(c, wave, strm_kpos<KO>(kbeg, 1));
 }
 
-template <int MB, int NB, int NA, int AT>
+template <int MB, int NB, int NA, int AT, int KO>
 __device__ __forceinline__ void strm_steps(floatx4_t (&acc)[MB][NB], const StrmCtx &c, int64_t kbeg, int ng,
                                            int wave) {
     int g = 0;
     for (; g + 5 <= ng; g += 3) {
-        strm_step<MB, NB, NA, AT, 0, true, true>(acc, c, kbeg, g, wave);
-        strm_step<MB, NB, NA, AT, 1, true, true>(acc, c, kbeg, g + 1, wave);
-        strm_step<MB, NB, NA, AT, 2, true, true>(acc, c, kbeg, g + 2, wave);
+        strm_step<MB, NB, NA, AT, KO, 0, true, true>(acc, c, kbeg, g, wave);
+        strm_step<MB, NB, NA, AT, KO, 1, true, true>(acc, c, kbeg, g + 1, wave);
+        strm_step<MB, NB, NA, AT, KO, 2, true, true>(acc, c, kbeg, g + 2, wave);
     }
     switch (ng - g) {
     case 4:
-        strm_step<MB, NB, NA, AT, 0, true, true>(acc, c, kbeg, g, wave);
-        strm_step<MB, NB, NA, AT, 1, true, true>(acc, c, kbeg, g + 1, wave);
-        strm_step<MB, NB, NA, AT, 2, false, true>(acc, c, kbeg, g + 2, wave);
-        strm_step<MB, NB, NA, AT, 0, false, false>(acc, c, kbeg, g + 3, wave);
+        strm_step<MB, NB, NA, AT, KO, 0, true, true>(acc, c, kbeg, g, wave);
+        strm_step<MB, NB, NA, AT, KO, 1, true, true>(acc, c, kbeg, g + 1, wave);
+        strm_step<MB, NB, NA, AT, KO, 2, false, true>(acc, c, kbeg, g + 2, wave);
+        strm_step<MB, NB, NA, AT, KO, 0, false, false>(acc, c, kbeg, g + 3, wave);
         break;
     case 3:
-        strm_step<MB, NB, NA, AT, 0, true, true>(acc, c, kbeg, g, wave);
-        strm_step<MB, NB, NA, AT, 1, false, true>(acc, c, kbeg, g + 1, wave);
-        strm_step<MB, NB, NA, AT, 2, false, false>(acc, c, kbeg, g + 2, wave);
+        strm_step<MB, NB, NA, AT, KO, 0, true, true>(acc, c, kbeg, g, wave);
+        strm_step<MB, NB, NA, AT, KO, 1, false, true>(acc, c, kbeg, g + 1, wave);
+        strm_step<MB, NB, NA, AT, KO, 2, false, false>(acc, c, kbeg, g + 2, wave);
         break;
     default:  // 2
-        strm_step<MB, NB, NA, AT, 0, false, true>(acc, c, kbeg, g, wave);
-        strm_step<MB, NB, NA, AT, 1, false, false>(acc, c, kbeg, g + 1, wave);
+        strm_step<MB, NB, NA, AT, KO, 0, false, true>(acc, c, kbeg, g, wave);
+        strm_step<MB, NB, NA, AT, KO, 1, false, false>(acc, c, kbeg, g + 1, wave);
         break;
     }
 }
@@ -372,6 +384,14 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 
     // items on bf16/fp16 weights stream A and B through LDS
     constexpr bool kDma = !MX && NB <= 2 && (GROUPED ? MB == 1 : MB == 4);
+    // The order of each wave's K groups, chosen by measurement at decode: the
+    // four waves of a workgroup take every fourth group (so at any time they
+    // read adjacent groups of the same rows) on the LDS path for GEMM1 (6%
+    // faster than contiguous quarters) and the dense 16-bit projections (4%),
+    // and on the register path for both grouped GEMMs (3% and 2%); GEMM2 on
+    // the LDS path runs 12% slower that way and keeps contiguous quarters.
+    constexpr int KO = (EPI == EPI_SWIGLU || (!GROUPED && EPI != EPI_F32)) ? 4 : 1;  // LDS path: 4 or 1
+    constexpr int64_t kRegGS = GROUPED ? 512 : 128;  // register path: K stride of a wave's 128-wide groups
     // Cross-wave reduction and epilogue of one item (acc: this wave's partial sums).
     auto finish = [&](const RowTile &rt, int64_t nb, int ksl, floatx4_t (&acc)[MB][NB]) {
         // Cross-wave reduction, fixed order: wave0 + wave1 + wave2 + wave3.
@@ -474,7 +494,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
             const int64_t tb = it / ks;
             const int t = (int)(tb / nblocks);
             I.nb = tb - (int64_t)t * nblocks;
-            I.kbeg = (I.ksl * 4 + wave) * kq;
+            I.kbeg = strm_kbeg<KO>(I.ksl * 4 * kq, kq, wave);
             if constexpr (GROUPED) {
                 I.rt.e = te.e;
                 I.rt.p0 = te.p0;
@@ -512,10 +532,10 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
         // never stored.
         auto first = [&](const Item &I) {
             if constexpr (MB == 1) {
-                if (I.rt.mcount <= 8) strm_first<MB, NB, 1>(c, wave, I.kbeg);
-                else strm_first<MB, NB, 2>(c, wave, I.kbeg);
+                if (I.rt.mcount <= 8) strm_first<MB, NB, 1, KO>(c, wave, I.kbeg);
+                else strm_first<MB, NB, 2, KO>(c, wave, I.kbeg);
             } else {
-                strm_first<MB, NB, 2 * MB>(c, wave, I.kbeg);
+                strm_first<MB, NB, 2 * MB, KO>(c, wave, I.kbeg);
             }
         };
         const int ng = (int)(kq / kStrmKG);
@@ -532,10 +552,10 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
                 for (int b = 0; b < NB; ++b) acc[m][b] = floatx4_t{0.f, 0.f, 0.f, 0.f};
             if constexpr (MB == 1) {
-                if (cur.rt.mcount <= 8) strm_steps<MB, NB, 1, AT>(acc, c, cur.kbeg, ng, wave);
-                else strm_steps<MB, NB, 2, AT>(acc, c, cur.kbeg, ng, wave);
+                if (cur.rt.mcount <= 8) strm_steps<MB, NB, 1, AT, KO>(acc, c, cur.kbeg, ng, wave);
+                else strm_steps<MB, NB, 2, AT, KO>(acc, c, cur.kbeg, ng, wave);
             } else {
-                strm_steps<MB, NB, 2 * MB, AT>(acc, c, cur.kbeg, ng, wave);
+                strm_steps<MB, NB, 2 * MB, AT, KO>(acc, c, cur.kbeg, ng, wave);
             }
             // every load of this item has landed and every slot read is done
             Item nxt;
@@ -555,8 +575,11 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
         const int64_t tb = item / ks;
         const int t = (int)(tb / nblocks);
         const int64_t nb = tb - (int64_t)t * nblocks;
-        const int64_t kbeg = (ksl * 4 + wave) * kq;
-        const int64_t kend = kbeg + kq;
+        // the wave's 128-wide K groups: its contiguous quarter (gs = 128) or
+        // every fourth group from group `wave` (gs = 512)
+        constexpr int64_t gs = kRegGS;
+        const int64_t kbeg = gs == 128 ? (ksl * 4 + wave) * kq : ksl * 4 * kq + wave * 128;
+        const int64_t kend = kbeg + (kq / 128) * gs;
         RowTile rt;
         load_tile(a, GROUPED, BM, t, rt);  // mcount > 0 for every listed tile
 
@@ -634,24 +657,24 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
                     for (int c = 0; c < NB; ++c)
                         acc[m][c] = mfma16x16x32<AT>(cur.a[m][s], cur.b[c][s], acc[m][c]);
-            if (kk + 256 < kend)
-                stream_fetch<MB, NB, MX, AT, GROUPED>(r, bptr, bscale, aptr, ra, aoff, a8ptr, a8scale, kk + 256);
+            if (kk + 2 * gs < kend)
+                stream_fetch<MB, NB, MX, AT, GROUPED>(r, bptr, bscale, aptr, ra, aoff, a8ptr, a8scale, kk + 2 * gs);
             // a group's refill stays ahead of the next group's, so waiting for one buffer leaves the other's
             // loads in flight (the counter is in order)
             __builtin_amdgcn_sched_barrier(0);
         };
         stream_fetch<MB, NB, MX, AT, GROUPED>(r0, bptr, bscale, aptr, ra, aoff, a8ptr, a8scale, kbeg);
-        if (kbeg + 128 < kend)
-            stream_fetch<MB, NB, MX, AT, GROUPED>(r1, bptr, bscale, aptr, ra, aoff, a8ptr, a8scale, kbeg + 128);
+        if (kbeg + gs < kend)
+            stream_fetch<MB, NB, MX, AT, GROUPED>(r1, bptr, bscale, aptr, ra, aoff, a8ptr, a8scale, kbeg + gs);
         int64_t kk = kbeg;
-        for (; kk + 512 <= kend; kk += 256) {  // every refill in range: one path, exact waits
+        for (; kk + 4 * gs <= kend; kk += 2 * gs) {  // every refill in range: one path, exact waits
             step(r0, kk);
-            step(r1, kk + 128);
+            step(r1, kk + gs);
         }
         // the last 1..3 groups, already loaded or in flight
         step(r0, kk);
-        if (kk + 128 < kend) step(r1, kk + 128);
-        if (kk + 256 < kend) step(r0, kk + 256);
+        if (kk + gs < kend) step(r1, kk + gs);
+        if (kk + 2 * gs < kend) step(r0, kk + 2 * gs);
 
         finish(rt, nb, ksl, acc);
     }
