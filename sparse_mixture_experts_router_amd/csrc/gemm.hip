@@ -98,15 +98,18 @@ constexpr int kWaitLgkm0 = 15 | (3 << 14) | (7 << 4);
 // ---------------------------------------------------------------------------
 //
 // Work item = (row tile, column block).  A column block is NB blocks of 16 B
-// rows (EPI_SWIGLU: NB = 2, the gate rows j0.. and the up rows F + j0..).
-// The 4 waves of the workgroup split K in four contiguous quarters.  Items
-// on bf16/fp16 weights (grouped 16-row and dense 64-row tiles) stage A and B
-// through LDS (below).  Items on MXFP4 weights load straight into registers:
-// every 128-wide K group is one lane-group-permuted MFMA quartet, lane group
-// g = lane/16 owning k in [32g, 32g+32) of the group and feeding 8 of them
-// to each of 4 MFMAs, so a lane reads one whole 32-element MXFP4 block (16
-// code bytes and its scale) and the same 64 bytes of its A row.  Partial
-// sums of the waves meet in LDS and wave 0 applies the epilogue.
+// rows (EPI_SWIGLU: NB / 2 gate blocks of rows j0.. and the matching up
+// blocks of rows F + j0..).  The 4 waves of the workgroup split K between
+// them.  Items on bf16/fp16 weights (grouped 16-row and dense 64-row tiles)
+// stage A and B through LDS (below).  Items on MXFP4 weights load straight
+// into registers: every 128-wide K group is one lane-group-permuted MFMA
+// quartet, lane group g = lane/16 owning k in [32g, 32g+32) of the group and
+// feeding 8 of them to each of 4 MFMAs, so a lane reads one whole 32-element
+// MXFP4 block (16 code bytes; its scale comes from scale words, below) and
+// the same 64 bytes of its A row.  Grouped MXFP4 items hold four weight
+// blocks: the A loads, the same for every block of an item, then serve four
+// times 16 rows of codes (two blocks: 0.84 -> 0.75 ms for GEMM1 at decode).
+// Partial sums of the waves meet in LDS and wave 0 applies the epilogue.
 
 template <int MB, int NB>
 struct StreamFrag {
@@ -136,15 +139,14 @@ struct StreamRaw {
 
 template <int MB, int NB, bool MX, int AT, bool ABUF>
 __device__ __forceinline__ void stream_fetch(StreamRaw<MB, NB, MX, AT> &r, const uint8_t *const bptr[NB],
-                                             const uint8_t *const bscale[NB], const uint16_t *const aptr[MB],
+                                             const uint16_t *const aptr[MB],
                                              __amdgpu_buffer_rsrc_t ra, const uint32_t (&aoff)[MB],
                                              const uint8_t *const a8ptr[MB], const uint8_t *const a8scale[MB],
                                              int64_t kk) {
 #pragma unroll
     for (int c = 0; c < NB; ++c) {
         if constexpr (MX) {
-            r.b[c][0] = *(const uint4 *)(bptr[c] + (kk >> 1));
-            r.bs[c] = bscale[c][kk >> 5];
+            r.b[c][0] = *(const uint4 *)(bptr[c] + (kk >> 1));  // r.bs[c]: set by the caller (mx_scale)
         } else {
             const uint4 *p = (const uint4 *)(bptr[c] + kk * 2);
 #pragma unroll
@@ -170,6 +172,26 @@ __device__ __forceinline__ void stream_fetch(StreamRaw<MB, NB, MX, AT> &r, const
             for (int s = 0; s < 4; ++s) r.a[m][s] = p[s];
         }
     }
+}
+
+// MXFP4 scales on the register path.  A row keeps its E8M0 scales as K/32
+// consecutive bytes, so the 32-bit word at byte 4G holds the scales of the
+// four 32-element blocks of 128-wide group G, one per lane group.  Loaded
+// byte by byte per group, every scale load touches as many cache lines as the
+// group's code load (one per row) for a sixteenth of the bytes.  Instead a
+// lane (q, li) loads, for up to 16 groups j of the wave's K range, the word
+// of row li and group j into slot j / 4 when j % 4 == q, and a group's scale
+// is read from lane (j % 4, li) with a cross-lane permute, byte lg.
+constexpr int kMxWordGroups = 16;  // groups whose scale words the slots hold
+
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// (A vector indexed by the wave-uniform j / 4 stays in registers; selects
+// between loads of an array would be folded into a load through a selected
+// address, which keeps the array in scratch memory.)
+__device__ __forceinline__ uint32_t mx_scale(u32x4_t w, int j, int li, int lg) {
+    const uint32_t v = (uint32_t)__builtin_amdgcn_ds_bpermute((((j & 3) << 4) + li) << 2, (int)w[(j >> 2) & 3]);
+    return (v >> (8 * lg)) & 0xffu;
 }
 
 template <int MB, int NB, bool MX, int AT>
@@ -378,7 +400,9 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
     // its partial sums into plane s of C ([ks][M][ldc])
     const int ks = (EPI == EPI_F32 && !MX && !GROUPED && a.ksplit > 1) ? a.ksplit : 1;
     const int64_t kq = K / ks / 4;       // K range of one wave
-    const int64_t nblocks = (EPI == EPI_SWIGLU) ? a.N / 16 : a.N / (16 * NB);
+    // EPI_SWIGLU items hold kSwHalf gate blocks, then the matching up blocks
+    constexpr int kSwHalf = NB > 1 ? NB / 2 : 1;
+    const int64_t nblocks = (EPI == EPI_SWIGLU) ? a.N / (16 * kSwHalf) : a.N / (16 * NB);
     const int ntiles = GROUPED ? *a.ntiles : (int)((a.M + BM - 1) / BM);
     const int64_t items = (int64_t)ntiles * nblocks * ks;
 
@@ -424,10 +448,13 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
                     bool ok = row < rt.mcount;
                     int64_t p = rt.p0 + row;
                     if constexpr (EPI == EPI_SWIGLU) {
-                        if (ok) {
-                            float g = acc[m][0][q], u = acc[m][NB - 1][q];
-                            ((uint16_t *)a.C)[p * a.ldc + nb * 16 + li] = f32_to_act<OT>(silu_fast(g) * u);
-                        }
+#pragma unroll
+                        for (int c = 0; c < kSwHalf; ++c)
+                            if (ok) {
+                                float g = acc[m][c][q], u = acc[m][c + kSwHalf][q];
+                                ((uint16_t *)a.C)[p * a.ldc + (nb * kSwHalf + c) * 16 + li] =
+                                    f32_to_act<OT>(silu_fast(g) * u);
+                            }
                     } else {
 #pragma unroll
                         for (int c = 0; c < NB; ++c) {
@@ -585,22 +612,22 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 
         // B row pointers (lane's row li of each 16-row block) and A row pointers.
         const uint8_t *bptr[NB];
-        const uint8_t *bscale[NB];
+        const uint8_t *srow[NB];  // MXFP4: the row's scale bytes
         int64_t brow0 = GROUPED ? (int64_t)rt.e * a.b_group_rows : 0;
 #pragma unroll
         for (int c = 0; c < NB; ++c) {
             int64_t r;
             if constexpr (EPI == EPI_SWIGLU)
-                r = brow0 + (c == 0 ? 0 : a.N) + nb * 16 + li;
+                r = brow0 + (c < kSwHalf ? 0 : a.N) + (nb * kSwHalf + c % kSwHalf) * 16 + li;
             else
                 r = brow0 + (nb * NB + c) * 16 + li;
             if constexpr (MX) {
                 // lane group lg reads its 32-element block of each 128-wide group
                 bptr[c] = (const uint8_t *)a.B + r * (K / 2) + (lg * 32) / 2;
-                bscale[c] = (const uint8_t *)a.B + a.b_rows_total * (K / 2) + r * (K / 32) + lg;
+                srow[c] = (const uint8_t *)a.B + a.b_rows_total * (K / 2) + r * (K / 32);
             } else {
                 bptr[c] = (const uint8_t *)a.B + (r * K + lg * 32) * 2;
-                bscale[c] = nullptr;
+                srow[c] = nullptr;
             }
         }
         // A rows.  Grouped items (mostly a few valid rows of 16 at decode) read
@@ -645,36 +672,61 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
         // Two groups in flight: the raw registers of groups g+1 and g+2 while group g's MFMAs run.  The
         // two raw buffers alternate by position in an unrolled pair of groups, each refilled once its
         // group's MFMAs have read it, so no buffer is copied (a copy of registers a load is still writing,
-        // or a load into registers an MFMA has yet to read, would wait for that load).
+        // or a load into registers an MFMA has yet to read, would wait for that load).  MXFP4 items run
+        // the pipeline over chunks of up to kMxWordGroups groups, each after loading its scale words.
         StreamRaw<MB, NB, MX, AT> r0, r1;
-        auto step = [&](StreamRaw<MB, NB, MX, AT> &r, int64_t kk) {
-            StreamFrag<MB, NB> cur;
-            stream_decode<MB, NB, MX, AT>(cur, r);
+        for (int64_t kc = kbeg; kc < kend; kc += (MX ? kMxWordGroups * gs : kend - kbeg)) {
+            const int64_t kce = MX ? min(kend, kc + kMxWordGroups * gs) : kend;
+            u32x4_t sw[MX ? NB : 1];
+            if constexpr (MX) {
+                const int nw = (int)((kce - kc) / gs + 3) >> 2;  // words per lane (wave-uniform)
 #pragma unroll
-            for (int s = 0; s < 4; ++s)
+                for (int c = 0; c < NB; ++c)
 #pragma unroll
-                for (int m = 0; m < MB; ++m)
+                    for (int h = 0; h < 4; ++h) {
+                        const int64_t j = min((int64_t)(4 * h + lg), (kce - kc) / gs - 1);
+                        sw[c][h] = h < nw ? *(const uint32_t *)(srow[c] + (((kc + j * gs) >> 7) << 2)) : 0u;
+                    }
+            }
+            // the scales of the group at kn into the raw buffer o (its code loads may still be in flight)
+            auto scales = [&](StreamRaw<MB, NB, MX, AT> &o, int64_t kn) {
+                if constexpr (MX) {
+                    const int j = (int)((kn - kc) / gs);
 #pragma unroll
-                    for (int c = 0; c < NB; ++c)
-                        acc[m][c] = mfma16x16x32<AT>(cur.a[m][s], cur.b[c][s], acc[m][c]);
-            if (kk + 2 * gs < kend)
-                stream_fetch<MB, NB, MX, AT, GROUPED>(r, bptr, bscale, aptr, ra, aoff, a8ptr, a8scale, kk + 2 * gs);
-            // a group's refill stays ahead of the next group's, so waiting for one buffer leaves the other's
-            // loads in flight (the counter is in order)
-            __builtin_amdgcn_sched_barrier(0);
-        };
-        stream_fetch<MB, NB, MX, AT, GROUPED>(r0, bptr, bscale, aptr, ra, aoff, a8ptr, a8scale, kbeg);
-        if (kbeg + gs < kend)
-            stream_fetch<MB, NB, MX, AT, GROUPED>(r1, bptr, bscale, aptr, ra, aoff, a8ptr, a8scale, kbeg + gs);
-        int64_t kk = kbeg;
-        for (; kk + 4 * gs <= kend; kk += 2 * gs) {  // every refill in range: one path, exact waits
-            step(r0, kk);
-            step(r1, kk + gs);
+                    for (int c = 0; c < NB; ++c) o.bs[c] = mx_scale(sw[c], j, li, lg);
+                }
+            };
+            auto step = [&](StreamRaw<MB, NB, MX, AT> &r, StreamRaw<MB, NB, MX, AT> &o, int64_t kk) {
+                StreamFrag<MB, NB> cur;
+                stream_decode<MB, NB, MX, AT>(cur, r);
+#pragma unroll
+                for (int s = 0; s < 4; ++s)
+#pragma unroll
+                    for (int m = 0; m < MB; ++m)
+#pragma unroll
+                        for (int c = 0; c < NB; ++c)
+                            acc[m][c] = mfma16x16x32<AT>(cur.a[m][s], cur.b[c][s], acc[m][c]);
+                if (kk + 2 * gs < kce)
+                    stream_fetch<MB, NB, MX, AT, GROUPED>(r, bptr, aptr, ra, aoff, a8ptr, a8scale, kk + 2 * gs);
+                scales(o, kk + gs);  // the next group's, read while this group's MFMAs run
+                // a group's refill stays ahead of the next group's, so waiting for one buffer leaves the
+                // other's loads in flight (the counter is in order)
+                __builtin_amdgcn_sched_barrier(0);
+            };
+            stream_fetch<MB, NB, MX, AT, GROUPED>(r0, bptr, aptr, ra, aoff, a8ptr, a8scale, kc);
+            if (kc + gs < kce)
+                stream_fetch<MB, NB, MX, AT, GROUPED>(r1, bptr, aptr, ra, aoff, a8ptr, a8scale, kc + gs);
+            scales(r0, kc);
+            int64_t kk = kc;
+            for (; kk + 4 * gs <= kce; kk += 2 * gs) {  // every refill in range: one path, exact waits
+                step(r0, r1, kk);
+                step(r1, r0, kk + gs);
+            }
+            // the last 1..3 groups, already loaded or in flight
+            step(r0, r1, kk);
+            if (kk + gs < kce) step(r1, r0, kk + gs);
+            if (kk + 2 * gs < kce) step(r0, r1, kk + 2 * gs);
         }
-        // the last 1..3 groups, already loaded or in flight
-        step(r0, kk);
-        if (kk + gs < kend) step(r1, kk + gs);
-        if (kk + 2 * gs < kend) step(r0, kk + 2 * gs);
 
         finish(rt, nb, ksl, acc);
     }
@@ -1845,7 +1897,7 @@ constexpr int kBigGrid = 256;      // persistent grid cap of the large-tile kern
 
 template <int MB, int NB, int EPI, bool MX, bool GROUPED, int AT, int OT>
 static hipError_t run_stream(const GemmArgs &a, hipStream_t s) {
-    const int64_t nblocks = (EPI == EPI_SWIGLU) ? a.N / 16 : a.N / (16 * NB);
+    const int64_t nblocks = (EPI == EPI_SWIGLU) ? a.N / (16 * (NB > 1 ? NB / 2 : 1)) : a.N / (16 * NB);
     const int64_t tiles = GROUPED ? a.max_tiles : (a.M + 16 * MB - 1) / (16 * MB);
     const int64_t items = tiles * nblocks * (EPI == EPI_F32 && !MX && !GROUPED && a.ksplit > 1 ? a.ksplit : 1);
     if (items <= 0) return hipSuccess;
@@ -1888,7 +1940,9 @@ static hipError_t run_path(const GemmArgs &a, int path, hipStream_t s) {
             return hipErrorInvalidValue;
         }
     }
-    if constexpr (GROUPED) return run_stream<1, NB, EPI, MX, GROUPED, AT, OT>(a, s);
+    // MXFP4 weights on the register path: items of four 16-row weight blocks, so a lane's activation loads
+    // (the same per item) serve twice the weight bytes of two-block items
+    if constexpr (GROUPED) return run_stream<1, (MX && AT != ACT_Q8) ? 4 : NB, EPI, MX, GROUPED, AT, OT>(a, s);
     else return run_stream<4, NB, EPI, MX, GROUPED, AT, OT>(a, s);
 }
 

@@ -60,6 +60,13 @@ def test_small_decode_shape(weights, in_norm):
     run_and_compare(small_case("small_decode_%s_%s" % (weights, in_norm), weights=weights, in_norm=in_norm))
 
 
+def test_mxfp4_streaming_scale_chunks():
+    # MXFP4 streaming items hold the scale words of up to 16 of a wave's 128-wide K groups at a time: the
+    # down-projection (K = 8704: 17 groups per wave) and GEMM1 (K = 8704) run a chunk of 16 groups and a
+    # ragged chunk of one; GEMM2 (K = 512) has one group per wave
+    run_and_compare(small_case("mxfp4_scale_chunks", T=24, d=8704, L=8704, F=512, n=16, k=2, weights="mxfp4"))
+
+
 @pytest.mark.parametrize("weights", ["bf16", "mxfp4"])
 def test_small_prefill_shape(weights):
     # ~300 tokens per expert: tiled kernels for the dense and grouped GEMMs
