@@ -1943,7 +1943,10 @@ static hipError_t run_path(const GemmArgs &a, int path, hipStream_t s) {
     // MXFP4 weights on the register path: items of four 16-row weight blocks, so a lane's activation loads
     // (the same per item) serve twice the weight bytes of two-block items
     if constexpr (GROUPED) return run_stream<1, (MX && AT != ACT_Q8) ? 4 : NB, EPI, MX, GROUPED, AT, OT>(a, s);
-    else return run_stream<4, NB, EPI, MX, GROUPED, AT, OT>(a, s);
+    // Dense items re-read the batch's activation rows once per column block, which bounded the MXFP4
+    // projections at small T: items of 16 rows and four weight blocks read a quarter of those bytes (their
+    // weight rows, 4.25 bits a value, are re-read per 16-row tile from L2 instead); T=64: down 40 -> 24 us
+    else return run_stream<MX ? 1 : 4, MX ? 4 : NB, EPI, MX, GROUPED, AT, OT>(a, s);
 }
 
 hipError_t launch_router_gemm(const GemmArgs &a, int path, hipStream_t s) {
