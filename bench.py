@@ -106,6 +106,47 @@ def csrc_hash() -> str:
     return h.hexdigest()[:16]
 
 
+def vendor_gemm_reference(torch) -> None:
+    """Times the vendor GEMM library (torch.bmm / torch.mm) on the layer's GEMM shapes with N(0,1) operands (and
+    one with zeros), fp16 and bf16: the rate a library GEMM reaches on this chip and data, printed as one JSON line."""
+    dev = torch.device("cuda:0")
+    g = torch.Generator(device=dev)
+    g.manual_seed(0)
+    res = []
+
+    def timed(fn, flop, label, dt):
+        for _ in range(3):
+            fn()
+        torch.cuda.synchronize()
+        n = 10
+        t0 = time.perf_counter()
+        for _ in range(n):
+            fn()
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) * 1e3 / n
+        res.append({"shape": label, "dtype": dt, "ms": round(ms, 3), "TFLOPs": round(flop / (ms * 1e-3) / 1e12, 1)})
+        log(res[-1])
+
+    for dt in (torch.float16, torch.bfloat16):
+        name = "fp16" if dt == torch.float16 else "bf16"
+        a = torch.randn(256, 256, 4096, device=dev, dtype=dt, generator=g)
+        b = torch.randn(256, 4096, 8192, device=dev, dtype=dt, generator=g)
+        timed(lambda: torch.bmm(a, b), 2.0 * 256 * 256 * 4096 * 8192,
+              "256 experts x [256 x 4096] @ [4096 x 8192] (GEMM1's shape, every expert at 256 rows)", name)
+        del a, b
+        a = torch.randn(8192, 8192, device=dev, dtype=dt, generator=g)
+        b = torch.randn(8192, 4096, device=dev, dtype=dt, generator=g)
+        timed(lambda: torch.mm(a, b), 2.0 * 8192 * 8192 * 4096, "[8192 x 8192] @ [8192 x 4096] (down-projection)", name)
+        b = torch.randn(8192, 8192, device=dev, dtype=dt, generator=g)
+        timed(lambda: torch.mm(a, b), 2.0 * 8192 ** 3, "[8192 x 8192] @ [8192 x 8192], N(0,1) operands", name)
+        a.zero_()
+        b.zero_()
+        timed(lambda: torch.mm(a, b), 2.0 * 8192 ** 3, "[8192 x 8192] @ [8192 x 8192], zero operands", name)
+        del a, b
+        torch.cuda.empty_cache()
+    print(json.dumps({"vendor_gemm": res}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -125,6 +166,8 @@ def main():
     ap.add_argument("--cpu-seconds", type=float, default=15.0, help="target CPU time of the oracle baseline")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="MIB",
                     help="only run the library's plain 16-byte copy of MIB MiB (5 times), to calibrate HBM counters")
+    ap.add_argument("--vendor-gemm", action="store_true",
+                    help="only time the vendor GEMM library (torch) on the layer's GEMM shapes, as a reference rate")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path (--gpus %d requested)" % args.gpus,
@@ -150,6 +193,9 @@ def main():
         torch.cuda.synchronize()
         dt = (time.perf_counter() - t0) / 5
         print(json.dumps({"copy_bytes": n, "copy_GBps": round(2 * n / dt / 1e9, 1)}))
+        return
+    if args.vendor_gemm:
+        vendor_gemm_reference(torch)
         return
     moe.lib()  # fail loudly if the HIP library is missing
     dev = torch.device("cuda:0")
