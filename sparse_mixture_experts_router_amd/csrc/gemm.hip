@@ -417,7 +417,14 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
     constexpr int KO = (EPI == EPI_SWIGLU || (!GROUPED && EPI != EPI_F32)) ? 4 : 1;  // LDS path: 4 or 1
     constexpr int64_t kRegGS = GROUPED ? 512 : 128;  // register path: K stride of a wave's 128-wide groups
     // Cross-wave reduction and epilogue of one item (acc: this wave's partial sums).
-    auto finish = [&](const RowTile &rt, int64_t nb, int ksl, floatx4_t (&acc)[MB][NB]) {
+    // EPI_NORM: the gains 1 + gamma of a lane's column in each block, loaded when the item is set up (a load
+    // in the epilogue would hold the other waves at its barrier for a memory round trip per item)
+    auto gains_of = [&](int64_t nb, float (&gam)[NB]) {
+#pragma unroll
+        for (int c = 0; c < NB; ++c)
+            gam[c] = (EPI == EPI_NORM && a.gamma) ? 1.0f + a.gamma[(nb * NB + c) * 16 + li] : 1.0f;
+    };
+    auto finish = [&](const RowTile &rt, int64_t nb, int ksl, floatx4_t (&acc)[MB][NB], const float (&gam)[NB]) {
         // Cross-wave reduction, fixed order: wave0 + wave1 + wave2 + wave3.
         if (wave > 0) {
 #pragma unroll
@@ -459,7 +466,16 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
 #pragma unroll
                         for (int c = 0; c < NB; ++c) {
                             int64_t n = (nb * NB + c) * 16 + li;
-                            if (ok) rowsq[c][q] += store_elem<EPI, OT>(a, p + ksl * a.M, n, acc[m][c][q]);
+                            if constexpr (EPI == EPI_NORM) {
+                                if (ok) {
+                                    const uint16_t sv = f32_to_bf16(gam[c] * acc[m][c][q]);
+                                    ((uint16_t *)a.C)[p * a.ldc + n] = sv;
+                                    const float qv = a.norm_round ? bf16_to_f32(sv) : acc[m][c][q];
+                                    rowsq[c][q] += qv * qv;
+                                }
+                            } else {
+                                if (ok) rowsq[c][q] += store_elem<EPI, OT>(a, p + ksl * a.M, n, acc[m][c][q]);
+                            }
                         }
                     }
                 }
@@ -507,6 +523,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
             RowTile rt;
             int64_t nb, kbeg;
             int ksl;
+            float gam[NB];
         };
         // the tile of item it and, for grouped items, its list entry
         auto tile_of = [&](int64_t it) { return (int)(it / ks / nblocks); };
@@ -522,6 +539,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
             const int t = (int)(tb / nblocks);
             I.nb = tb - (int64_t)t * nblocks;
             I.kbeg = strm_kbeg<KO>(I.ksl * 4 * kq, kq, wave);
+            gains_of(I.nb, I.gam);
             if constexpr (GROUPED) {
                 I.rt.e = te.e;
                 I.rt.p0 = te.p0;
@@ -590,7 +608,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
                 setup(nx, nxt, te_nx);
                 first(nxt);
             }
-            finish(cur.rt, cur.nb, cur.ksl, acc);
+            finish(cur.rt, cur.nb, cur.ksl, acc, cur.gam);
             if (nx >= items) break;
             item = nx;
             cur = nxt;
@@ -609,6 +627,8 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
         const int64_t kend = kbeg + (kq / 128) * gs;
         RowTile rt;
         load_tile(a, GROUPED, BM, t, rt);  // mcount > 0 for every listed tile
+        float gam[NB];
+        gains_of(nb, gam);
 
         // B row pointers (lane's row li of each 16-row block) and A row pointers.
         const uint8_t *bptr[NB];
@@ -728,7 +748,7 @@ __global__ __launch_bounds__(256) void gemm_stream_kernel(GemmArgs a) {
             if (kk + 2 * gs < kce) step(r0, r1, kk + 2 * gs);
         }
 
-        finish(rt, nb, ksl, acc);
+        finish(rt, nb, ksl, acc, gam);
     }
 }
 
