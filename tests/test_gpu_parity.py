@@ -132,6 +132,17 @@ def test_single_token_and_top1():
     run_and_compare(small_case("top1", T=50, k=1))
 
 
+@pytest.mark.parametrize("T", [1, 16, 128])
+def test_mxfp4_batch_edges(T):
+    # MXFP4 dense projections take 16-row items of four weight blocks up to T = 128 (one row, one full tile,
+    # eight tiles); grouped items of four blocks on every expert
+    run_and_compare(small_case("mxfp4_T%d" % T, T=T, weights="mxfp4"))
+
+
+def test_mxfp4_k_equals_n():
+    run_and_compare(small_case("mxfp4_k_eq_n", T=40, n=16, k=16, weights="mxfp4"))
+
+
 def test_k_equals_n():
     run_and_compare(small_case("k_eq_n", T=40, n=16, k=16))
 
