@@ -496,7 +496,12 @@ def main():
             "tokens_per_s": round(p1m.chunk_T / (r1m["ms"] * 1e-3), 1),
             "layer_bytes": by1m["total"], "layer_GBps": round(by1m["total"] / (r1m["ms"] * 1e-3) / 1e9, 1),
             "layer_frac_hbm": round(by1m["total"] / (r1m["ms"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "touched_experts": by1m["touched"], "stage_ms": {k: round(v, 4) for k, v in r1m["stages"].items()}}
+            "touched_experts": by1m["touched"],
+            # the grouped GEMM1 on MXFP4 codes (4.25 bits a weight) and its scale words: algorithmic bytes over
+            # its event-timed stage
+            "gemm1_GBps": round(by1m["gemm1"] / (r1m["stages"]["gemm1"] * 1e-3) / 1e9, 1),
+            "gemm1_frac_hbm": round(by1m["gemm1"] / (r1m["stages"]["gemm1"] * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "stage_ms": {k: round(v, 4) for k, v in r1m["stages"].items()}}
         log("MXFP4 weights, decode T=64: %.3f ms/step, %.0f tok/s, layer %.0f GB/s" % (
             r1m["ms"], p1m.chunk_T / (r1m["ms"] * 1e-3), by1m["total"] / (r1m["ms"] * 1e-3) / 1e9))
         del W4
